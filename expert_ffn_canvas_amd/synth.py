@@ -1,0 +1,173 @@
+"""Seeded synthetic inputs for the MoE feed-forward layer.
+
+This module only draws and lays out inputs: it holds none of the layer's
+arithmetic, and both the GPU path and the CPU oracle consume what it returns.
+
+Workloads (sizes from the pages: 128 experts / 8 active, d_model 2816,
+expert d_ff 704, a 256-token canvas, a 2048-token prompt encoded together with
+the canvas, two canvases, 30 MoE layers):
+
+  canvas32   T=32,   fp32 hidden states, fp32 router weight, bf16 experts
+  canvas256  T=256,  all bf16, router bias -1.1*ln(e+1) (Zipf s=1.1 skew)
+  encode2304 T=2304, all bf16, no router bias
+  int4       T=256,  bf16 activations, int4-g128 experts (zero point 8)
+  stack30    T=512,  30 layers with their own bf16 weights, Zipf skew,
+             a N(0, 0.5) offset [T, D] added after each layer
+
+Draw order from one torch generator seeded with the workload's seed:
+x, then per layer: router weight, router gamma, expert-norm gamma, gate_up,
+down (then, for the stack, the offset of that layer). Normal draws are fp32
+and are rounded to bf16 (round-to-nearest-even) where the tensor is bf16.
+Gammas and the bias stay fp32 tensors; in the all-bf16 workloads their values
+are rounded to bf16-representable numbers. The generator runs on the device
+the tensors are made on, so values depend on (seed, device type); every check
+hands the oracle the exact tensors the GPU saw.
+"""
+from __future__ import annotations
+
+import math
+from dataclasses import dataclass, field
+
+import numpy as np
+import torch
+
+N_EXPERTS = 128
+TOP_K = 8
+D_MODEL = 2816
+D_FF = 704
+RMS_EPS = 1e-6
+GROUP = 128  # int4 group size along the input dimension
+
+
+@dataclass
+class Workload:
+    name: str
+    T: int
+    act: str            # "f32" | "bf16"
+    router_w: str       # "f32" | "bf16"
+    experts: str        # "bf16" | "i4g128"
+    bias: str | None    # None | "zipf"
+    seed: int
+    layers: int = 1
+    delta_std: float = 0.0
+    E: int = N_EXPERTS
+    K: int = TOP_K
+    D: int = D_MODEL
+    F: int = D_FF
+    extra: dict = field(default_factory=dict)
+
+
+WORKLOADS = {
+    "canvas32": Workload("canvas32", 32, "f32", "f32", "bf16", None, 0),
+    "canvas256": Workload("canvas256", 256, "bf16", "bf16", "bf16", "zipf", 1),
+    "encode2304": Workload("encode2304", 2304, "bf16", "bf16", "bf16", None, 2),
+    "int4": Workload("int4", 256, "bf16", "bf16", "i4g128", None, 3),
+    "stack30": Workload("stack30", 512, "bf16", "bf16", "bf16", "zipf", 4, layers=30, delta_std=0.5),
+}
+
+
+def _randn(shape, std, gen, device):
+    return torch.randn(shape, generator=gen, device=device, dtype=torch.float32) * std
+
+
+def _as_bf16_valued(t: torch.Tensor) -> torch.Tensor:
+    return t.to(torch.bfloat16).to(torch.float32)
+
+
+def zipf_bias(E: int, s: float = 1.1) -> torch.Tensor:
+    """Log of the unnormalised Zipf pmf over expert ids: b_e = -s * ln(e + 1)."""
+    return torch.tensor([-s * math.log(e + 1) for e in range(E)], dtype=torch.float32)
+
+
+def quantize_i4g128(w: torch.Tensor):
+    """Symmetric int4 codes with zero point 8, groups of 128 along the last dim.
+
+    w: fp32 [..., K]. Per (row, group): s = fp16(2 * amax / 15) and
+    q = clamp(round_half_even(w / s) + 8, 0, 15). The last group of a row holds
+    whatever remains when K is not a multiple of 128.
+    Returns (packed uint8 [..., ceil(K/2)] with even k in the low nibble,
+    scales as fp16 [..., ceil(K/128)]).
+    """
+    K = w.shape[-1]
+    G = (K + GROUP - 1) // GROUP
+    pad = G * GROUP - K
+    wp = torch.nn.functional.pad(w, (0, pad)) if pad else w
+    wg = wp.reshape(*w.shape[:-1], G, GROUP)
+    amax = wg.abs().amax(dim=-1)
+    s16 = (2.0 * amax / 15.0).clamp_min(1e-8).to(torch.float16)
+    q = torch.round(wg / s16.to(torch.float32).unsqueeze(-1)) + 8.0
+    q = q.clamp(0, 15).to(torch.uint8).reshape(*w.shape[:-1], G * GROUP)[..., :K]
+    if K % 2:
+        q = torch.nn.functional.pad(q, (0, 1))
+    packed = (q[..., 0::2] | (q[..., 1::2] << 4)).contiguous()
+    return packed, s16.contiguous()
+
+
+def make_layer_weights(wl: Workload, gen: torch.Generator, device) -> dict:
+    """Weights of one layer, drawn in the fixed order (router W, gammas, gate_up, down)."""
+    E, D, F = wl.E, wl.D, wl.F
+    w = {}
+    rw = _randn((E, D), 0.02, gen, device)
+    w["router_w"] = rw.to(torch.bfloat16) if wl.router_w == "bf16" else rw
+    g_r = _randn((D,), 0.1, gen, device)
+    g_e = _randn((D,), 0.1, gen, device)
+    if wl.act == "bf16":
+        g_r, g_e = _as_bf16_valued(g_r), _as_bf16_valued(g_e)
+    w["router_gamma"], w["ffn_gamma"] = g_r, g_e
+    if wl.bias == "zipf":
+        b = zipf_bias(E).to(device)
+        w["router_bias"] = _as_bf16_valued(b) if wl.act == "bf16" else b
+    else:
+        w["router_bias"] = None
+    gu = _randn((E, 2 * F, D), 0.02, gen, device)
+    if wl.experts == "i4g128":
+        w["q_gate_up"], w["s_gate_up"] = quantize_i4g128(gu)
+        del gu
+        dn = _randn((E, D, F), 0.02, gen, device)
+        w["q_down"], w["s_down"] = quantize_i4g128(dn)
+        del dn
+    else:
+        w["w_gate_up"] = gu.to(torch.bfloat16)
+        del gu
+        w["w_down"] = _randn((E, D, F), 0.02, gen, device).to(torch.bfloat16)
+    return w
+
+
+def make_inputs(wl: Workload, device="cpu", layers: int | None = None, T: int | None = None):
+    """Generate x and the weights of the first `layers` layers (default: all).
+
+    Returns dict(x, layers=[weights...], deltas=[...] for stacks).
+    """
+    gen = torch.Generator(device=device)
+    gen.manual_seed(wl.seed)
+    T = wl.T if T is None else T
+    x = _randn((T, wl.D), 1.0, gen, device)
+    x = x.to(torch.bfloat16) if wl.act == "bf16" else x
+    n_layers = wl.layers if layers is None else layers
+    out = {"x": x, "layers": [], "deltas": []}
+    for _ in range(n_layers):
+        out["layers"].append(make_layer_weights(wl, gen, device))
+        if wl.delta_std > 0:
+            d = _randn((T, wl.D), wl.delta_std, gen, device)
+            out["deltas"].append(d.to(torch.bfloat16) if wl.act == "bf16" else d)
+    return out
+
+
+def small_workload(name="tiny", T=16, E=6, K=2, D=128, F=64, act="bf16", router_w="bf16",
+                   experts="bf16", bias=None, seed=0) -> Workload:
+    """A shrunken workload with the same recipe, for tests the oracle finishes quickly."""
+    return Workload(name, T, act, router_w, experts, bias, seed, E=E, K=K, D=D, F=F)
+
+
+def to_numpy_bits(t: torch.Tensor | None):
+    """Host numpy view for the oracle: bf16 -> uint16 bits, fp16 -> uint16 bits, others as is."""
+    if t is None:
+        return None
+    t = t.detach().to("cpu").contiguous()
+    if t.dtype == torch.bfloat16 or t.dtype == torch.float16:
+        return t.view(torch.int16).numpy().view(np.uint16)
+    return t.numpy()
+
+
+def weights_to_numpy(w: dict) -> dict:
+    return {k: to_numpy_bits(v) for k, v in w.items()}
