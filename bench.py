@@ -1,0 +1,292 @@
+#!/usr/bin/env python3
+"""Benchmark of the MI355X MoE feed-forward layer (DiffusionGemma 26B-A4B shape).
+
+One step = one dg_moe_forward over one batch of T tokens: router, permutation, gate_up grouped GEMM,
+down grouped GEMM and combine, on inputs already resident in HBM. The default workload is one layer
+over a 256-token canvas, bf16, with the Zipf-skewed router bias; the weights rotate over several
+resident copies so that no cache holds them from one step to the next.
+
+Prints one JSON line: tokens/s, the roofline of the dominant kernel (gate_up, HBM-bound) measured with
+HIP events on the launch stream, and the CPU oracle timed on the host on a bounded sample.
+
+  python bench.py [--steps K] [--warmup W] [--workload canvas256|encode2304|int4|canvas32|stack30]
+"""
+import argparse
+import ctypes
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "MoE-layer tokens/s per canvas step (T=256, bf16) + % of HBM/MFMA roofline"
+HBM_PEAK_GBPS = 8000.0         # MI355X HBM3E
+BF16_PEAK_TFLOPS = 2500.0      # MI355X dense bf16 MFMA
+F16_PEAK_TFLOPS = 2500.0
+COUNTERS_FILE = os.path.join(ROOT, "profiles", "gate_up_counters.txt")
+KERNEL_NAMES = ("router", "permute", "gate_up", "down", "combine")
+
+
+class HipEvents:
+    """hipEvent_t through the HIP runtime the process already runs (torch's, same soname)."""
+
+    def __init__(self):
+        self.hip = ctypes.CDLL("libamdhip64.so.7")
+        self.hip.hipEventCreate.argtypes = [ctypes.POINTER(ctypes.c_void_p)]
+        self.hip.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p, ctypes.c_void_p]
+        self.hip.hipEventRecord.argtypes = [ctypes.c_void_p, ctypes.c_void_p]
+        self.hip.hipEventSynchronize.argtypes = [ctypes.c_void_p]
+        self.hip.hipEventDestroy.argtypes = [ctypes.c_void_p]
+
+    def create(self, n):
+        evs = []
+        for _ in range(n):
+            e = ctypes.c_void_p()
+            assert self.hip.hipEventCreate(ctypes.byref(e)) == 0
+            evs.append(e.value)
+        return evs
+
+    def record(self, ev, stream):
+        assert self.hip.hipEventRecord(ctypes.c_void_p(ev), ctypes.c_void_p(stream)) == 0
+
+    def elapsed_ms(self, a, b):
+        ms = ctypes.c_float()
+        assert self.hip.hipEventSynchronize(ctypes.c_void_p(b)) == 0
+        assert self.hip.hipEventElapsedTime(ctypes.byref(ms), ctypes.c_void_p(a), ctypes.c_void_p(b)) == 0
+        return ms.value
+
+    def destroy(self, evs):
+        for e in evs:
+            self.hip.hipEventDestroy(ctypes.c_void_p(e))
+
+
+def expert_bytes(wl):
+    D, F = wl.D, wl.F
+    if wl.experts == "i4g128":
+        gu = 2 * F * (D // 2) + 2 * F * (D // 128) * 2
+        dn = D * (F // 2) + D * ((F + 127) // 128) * 2
+    else:
+        gu = 2 * F * D * 2
+        dn = D * F * 2
+    return gu, dn
+
+
+def algorithmic(wl, T, touched):
+    """Bytes and FLOPs the method must move / compute for one forward (intermediates excluded)."""
+    D, F, E, K = wl.D, wl.F, wl.E, wl.K
+    act_b = 4 if wl.act == "f32" else 2
+    rw_b = 4 if wl.router_w == "f32" else 2
+    gu, dn = expert_bytes(wl)
+    layer_bytes = touched * (gu + dn) + E * D * rw_b + 2 * D * 4 + E * 4 + 2 * T * D * act_b
+    flops = T * K * 2 * 3 * D * F + T * 2 * E * D
+    # gate_up launch: weights of touched experts + expert input rows [T, D] + gated activations [K T, F]
+    gate_up_bytes = touched * gu + T * D * 2 + K * T * F * 2
+    return layer_bytes, flops, gate_up_bytes
+
+
+def kernel_sources_digest():
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "expert_ffn_canvas_amd", "csrc")
+    for name in ("gemm_bf16.hip", "dg_common.h", "launch.h"):
+        with open(os.path.join(csrc, name), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def read_traffic(workload):
+    """HBM bytes per gate_up launch from the committed rocprofv3 counter summary, if it was taken on the
+    current kernel source for this workload; else None."""
+    if not os.path.exists(COUNTERS_FILE):
+        return None
+    kv = {}
+    for line in open(COUNTERS_FILE):
+        if "=" in line and not line.startswith("#"):
+            k, v = line.split("=", 1)
+            kv[k.strip()] = v.strip()
+    if kv.get("source_digest") != kernel_sources_digest() or kv.get("workload") != workload:
+        return None
+    try:
+        return float(kv["traffic_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
+
+
+def cpu_baseline(wl, x, w, threads):
+    """The oracle, as it stands, on the whole batch of this workload (one step), on the host cores."""
+    import oracle
+    from expert_ffn_canvas_amd import synth
+
+    wn = synth.weights_to_numpy(w)
+    xn = synth.to_numpy_bits(x)
+    T = x.shape[0]
+    n_tok = T if T <= 256 else 256
+    tok = list(range(n_tok))
+    oracle.load()
+    t0 = time.perf_counter()
+    oracle.moe_forward(wn, xn, wl.K, synth.RMS_EPS, tokens=tok, n_threads=threads)
+    dt = time.perf_counter() - t0
+    return {"value": round(n_tok / dt, 3), "unit": "tokens/s", "cores": threads, "kind": "oracle",
+            "sample": f"{n_tok} tokens of the {wl.name} batch (T={T}), all {wl.K} slots each, one layer; "
+                      f"{dt:.2f} s wall"}
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--workload", default="canvas256")
+    ap.add_argument("--rotate", type=int, default=4, help="resident weight copies cycled through")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-profile", action="store_true", help="skip the per-kernel event pass")
+    args = ap.parse_args()
+
+    if args.gpus != 1:
+        print(json.dumps({"error": "this build runs on one GPU only; --gpus must be 1", "n_gpus": args.gpus}))
+        sys.exit(2)
+
+    import torch
+
+    from expert_ffn_canvas_amd import dgmoe, synth
+
+    wl = synth.WORKLOADS[args.workload]
+    dev = "cuda:0"
+    torch.cuda.set_device(0)
+    stream = torch.cuda.current_stream()
+    sp = stream.cuda_stream
+    act = torch.float32 if wl.act == "f32" else torch.bfloat16
+    T = wl.T
+    t_setup = time.perf_counter()
+    inp = synth.make_inputs(wl, device=dev)
+    x = inp["x"]
+
+    # handles: for a single layer, `rotate` copies of the weights; for the stack, its 30 layers
+    if wl.layers > 1:
+        sets = inp["layers"]
+        rotate = 1
+    else:
+        base = inp["layers"][0]
+        sets = [base] + [{k: (None if v is None else v.clone()) for k, v in base.items()}
+                         for _ in range(max(args.rotate, 1) - 1)]
+        rotate = len(sets)
+    layers = [dgmoe.MoELayer(w, max_tokens=T, act_dtype=act, top_k=wl.K) for w in sets]
+    out = torch.empty((T, wl.D), dtype=act, device=dev)
+    bufs = [torch.empty_like(x), torch.empty_like(x)]
+    deltas = inp["deltas"]
+
+    def step(i):
+        if wl.layers > 1:
+            # x stays the stack input; the layers ping-pong between two buffers
+            src = x
+            for l, layer in enumerate(layers):
+                dst = bufs[l % 2]
+                st = dgmoe.dg_moe_forward(layer.handle, src.data_ptr(), dst.data_ptr(), T,
+                                          deltas[l].data_ptr(), dgmoe.DG_FWD_ADD_INPUT, sp)
+                assert st == 0, dgmoe.dg_moe_last_error()
+                src = dst
+        else:
+            layer = layers[i % rotate]
+            st = dgmoe.dg_moe_forward(layer.handle, x.data_ptr(), out.data_ptr(), T, None, 0, sp)
+            assert st == 0, dgmoe.dg_moe_last_error()
+
+    # routing statistics of the benchmark batch (first layer)
+    dbg = layers[0].forward_debug(x)
+    torch.cuda.synchronize()
+    counts = dbg["counts"].cpu()
+    touched = int((counts > 0).sum())
+    max_load = int(counts.max())
+    print(f"[bench] {wl.name}: T={T} touched={touched} max_load={max_load} rotate={rotate} "
+          f"setup {time.perf_counter() - t_setup:.1f}s", file=sys.stderr, flush=True)
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+
+    ev = HipEvents()
+    e0, e1 = ev.create(2)
+    torch.cuda.synchronize()
+    w0 = time.perf_counter()
+    ev.record(e0, sp)
+    for i in range(args.steps):
+        step(i)
+    ev.record(e1, sp)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - w0
+    gpu_ms = ev.elapsed_ms(e0, e1)
+    ms_per_step = gpu_ms / args.steps
+    tokens_per_s = T * args.steps / (gpu_ms / 1e3)
+    print(f"[bench] timed {args.steps} steps: {ms_per_step * 1e3:.1f} us/step (wall {wall:.3f}s)",
+          file=sys.stderr, flush=True)
+
+    # per-kernel durations: a second pass with events between the kernels (single-layer workloads)
+    kern_us = None
+    n_prof = 0 if (args.no_profile or wl.layers > 1) else min(args.steps, 100)
+    if n_prof:
+        evs = ev.create(6 * n_prof)
+        for i in range(n_prof):
+            layer = layers[i % rotate]
+            st = dgmoe.dg_moe_forward_profiled(layer.handle, x.data_ptr(), out.data_ptr(), T, None, 0,
+                                               evs[6 * i:6 * i + 6], sp)
+            assert st == 0, dgmoe.dg_moe_last_error()
+        torch.cuda.synchronize()
+        tot = [0.0] * 5
+        for i in range(n_prof):
+            for k in range(5):
+                tot[k] += ev.elapsed_ms(evs[6 * i + k], evs[6 * i + k + 1])
+        kern_us = {name: round(tot[k] / n_prof * 1e3, 2) for k, name in enumerate(KERNEL_NAMES)}
+        ev.destroy(evs)
+    ev.destroy([e0, e1])
+
+    n_layers = wl.layers
+    layer_bytes, flops, gate_up_bytes = algorithmic(wl, T, touched)
+    step_s = ms_per_step / 1e3
+    layer_gbps = layer_bytes * n_layers / step_s / 1e9  # stack: touched of layer 0 as the estimate
+    peak_tflops = F16_PEAK_TFLOPS if wl.experts == "i4g128" else BF16_PEAK_TFLOPS
+    roofline = None
+    if kern_us:
+        gu_s = kern_us["gate_up"] / 1e6
+        ach = gate_up_bytes / gu_s / 1e9
+        traffic = read_traffic(wl.name)
+        roofline = {"bound": "hbm", "kernel": "gate_up", "achieved": round(ach, 1), "peak": HBM_PEAK_GBPS,
+                    "unit": "GB/s", "frac": round(ach / HBM_PEAK_GBPS, 4),
+                    "traffic": traffic, "alg_bytes_per_launch": gate_up_bytes,
+                    "avg_launch_us": kern_us["gate_up"]}
+
+    result = {
+        "metric": METRIC,
+        "value": round(tokens_per_s, 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "int4-g128 weights, f16 MFMA" if wl.experts == "i4g128" else "bf16",
+        "data": "synthetic",
+        "config": {"workload": wl.name, "T": T, "n_experts": wl.E, "top_k": wl.K, "d_model": wl.D,
+                   "d_ff": wl.F, "experts": wl.experts, "act": wl.act, "router_bias": wl.bias or "none",
+                   "layers": n_layers, "weight_copies_rotated": rotate},
+        "roofline": roofline,
+        "layer": {"alg_bytes": layer_bytes * n_layers, "alg_flops": flops * n_layers,
+                  "achieved_GBps": round(layer_gbps, 1), "hbm_frac": round(layer_gbps / HBM_PEAK_GBPS, 4),
+                  "mfma_frac": round(flops * n_layers / step_s / 1e12 / peak_tflops, 4),
+                  "touched_experts": touched, "max_expert_load": max_load},
+        "kernels_us": kern_us,
+        "cpu_baseline": None,
+    }
+    if not args.no_cpu_baseline:
+        threads = int(os.environ.get("OMP_NUM_THREADS", "0")) or os.cpu_count()
+        w_host = inp["layers"][0]
+        result["cpu_baseline"] = cpu_baseline(wl, x, w_host, threads)
+    for layer in layers:
+        layer.close()
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

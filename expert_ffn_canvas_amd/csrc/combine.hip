@@ -1,0 +1,65 @@
+// Weighted combine back to token order on gfx950:
+//   out[t] = sum_j y[row_of_slot[t k + j]]  (+ x[t]) (+ addend[t])
+// where each y row already carries its routing weight. The k slots are summed
+// in their routing order (logit descending), always in the same order, so the
+// result is bit-reproducible; the sum is fp32 and the output is rounded once
+// (round-to-nearest-even for bf16).
+#include "dg_common.h"
+#include "launch.h"
+
+namespace dg {
+
+namespace {
+
+constexpr int kThreads = 256;
+
+template <bool OUT_F32>
+__global__ __launch_bounds__(kThreads) void k_combine(CombineArgs a) {
+  const int t = blockIdx.x;
+  const int K = a.K, D = a.D;
+  int rows[8];
+#pragma unroll
+  for (int j = 0; j < 8; ++j) rows[j] = (j < K) ? a.row_of_slot[(size_t)t * K + j] : 0;
+  for (int c = threadIdx.x * 4; c < D; c += kThreads * 4) {
+    float4 s = *reinterpret_cast<const float4*>(a.y + (size_t)rows[0] * D + c);
+#pragma unroll
+    for (int j = 1; j < 8; ++j) {
+      if (j < K) {
+        const float4 v = *reinterpret_cast<const float4*>(a.y + (size_t)rows[j] * D + c);
+        s.x += v.x; s.y += v.y; s.z += v.z; s.w += v.w;
+      }
+    }
+    const void* extra[2] = {a.x, a.addend};
+#pragma unroll
+    for (int q = 0; q < 2; ++q) {
+      if (extra[q] == nullptr) continue;
+      if (OUT_F32) {
+        const float4 v = *reinterpret_cast<const float4*>(static_cast<const float*>(extra[q]) + (size_t)t * D + c);
+        s.x += v.x; s.y += v.y; s.z += v.z; s.w += v.w;
+      } else {
+        const uint2 v = *reinterpret_cast<const uint2*>(static_cast<const uint16_t*>(extra[q]) + (size_t)t * D + c);
+        s.x += bf16_lo(v.x); s.y += bf16_hi(v.x); s.z += bf16_lo(v.y); s.w += bf16_hi(v.y);
+      }
+    }
+    if (OUT_F32) {
+      *reinterpret_cast<float4*>(static_cast<float*>(a.out) + (size_t)t * D + c) = s;
+    } else {
+      uint2 o;
+      o.x = pack_bf16x2(s.x, s.y);
+      o.y = pack_bf16x2(s.z, s.w);
+      *reinterpret_cast<uint2*>(static_cast<uint16_t*>(a.out) + (size_t)t * D + c) = o;
+    }
+  }
+}
+
+}  // namespace
+
+hipError_t launch_combine(const CombineArgs& a, hipStream_t stream) {
+  if (a.act_f32)
+    k_combine<true><<<dim3(a.T), dim3(kThreads), 0, stream>>>(a);
+  else
+    k_combine<false><<<dim3(a.T), dim3(kThreads), 0, stream>>>(a);
+  return hipGetLastError();
+}
+
+}  // namespace dg

@@ -1,0 +1,433 @@
+// Host side of the C ABI in include/dg_moe.h: argument validation, the
+// workspace allocated once at create time, router-weight preparation, and the
+// asynchronous launch sequence of one forward:
+//
+//   router (norm, logits, top-k, weights, expert input)
+//   -> permutation (counts, offsets, tile list, stable scatter)
+//   -> gate_up grouped GEMM (+ GELU-tanh gating)
+//   -> down grouped GEMM (x routing weight)
+//   -> combine back to token order.
+//
+// Nothing in a forward allocates, synchronises or reads device data back.
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <new>
+#include <string>
+
+#include "dg_common.h"
+#include "dg_moe.h"
+#include "launch.h"
+
+namespace {
+
+thread_local std::string g_last_error;
+
+dg_status fail(dg_status s, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof(buf), fmt, ap);
+  va_end(ap);
+  g_last_error = buf;
+  return s;
+}
+
+dg_status ok() {
+  g_last_error.clear();
+  return DG_OK;
+}
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+size_t round_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
+
+size_t act_elem_bytes(int dt) { return dt == DG_F32 ? 4 : 2; }
+
+// Sub-buffer layout of the workspace (byte offsets from the base).
+struct Layout {
+  size_t h, topk_idx, topk_w, counts, offsets, tiles, n_tiles, sorted_token, row_w, row_of_slot, act, y;
+  size_t wr, gamma_r, bias, gamma_e;
+  size_t total;
+  int Epad, n_wplanes, max_tiles;
+};
+
+Layout plan(const dg_moe_config& c) {
+  Layout L{};
+  const size_t T = (size_t)c.max_tokens, D = (size_t)c.d_model, F = (size_t)c.d_ff;
+  const size_t E = (size_t)c.n_experts, K = (size_t)c.top_k;
+  L.Epad = (int)round_up(E, 16);
+  L.n_wplanes = (c.router_w_dtype == DG_F32) ? 3 : 1;
+  L.max_tiles = (int)(K * T / dg::kTileRows + E);
+  size_t off = 0;
+  auto take = [&](size_t bytes) {
+    const size_t at = off;
+    off = round_up(off + bytes, 256);
+    return at;
+  };
+  L.h = take(T * D * 2);
+  L.topk_idx = take(T * K * 4);
+  L.topk_w = take(T * K * 4);
+  L.counts = take(E * 4);
+  L.offsets = take((E + 1) * 4);
+  L.tiles = take((size_t)L.max_tiles * sizeof(dg::Tile));
+  L.n_tiles = take(4);
+  L.sorted_token = take(K * T * 4);
+  L.row_w = take(K * T * 4);
+  L.row_of_slot = take(K * T * 4);
+  L.act = take(K * T * F * 2);
+  L.y = take(K * T * D * 4);
+  L.wr = take((size_t)L.n_wplanes * L.Epad * D * 2);
+  L.gamma_r = take(D * 4);
+  L.bias = take(E * 4);
+  L.gamma_e = take(D * 4);
+  L.total = off;
+  return L;
+}
+
+dg_status check_config(const dg_moe_config* c) {
+  if (!c) return fail(DG_ERR_INVALID_ARG, "config is NULL");
+  if (c->struct_size != sizeof(dg_moe_config))
+    return fail(DG_ERR_INVALID_ARG, "config struct_size %u != %zu", c->struct_size, sizeof(dg_moe_config));
+  if (c->n_experts < 1 || c->n_experts > 256) return fail(DG_ERR_SHAPE, "n_experts %d not in [1, 256]", c->n_experts);
+  if (c->top_k < 1 || c->top_k > 8 || c->top_k > c->n_experts)
+    return fail(DG_ERR_SHAPE, "top_k %d not in [1, min(n_experts, 8)]", c->top_k);
+  if (c->d_model < 128 || c->d_model > 16384 || c->d_model % 128)
+    return fail(DG_ERR_SHAPE, "d_model %d must be a multiple of 128 in [128, 16384]", c->d_model);
+  if (c->d_ff < 64 || c->d_ff > 4096 || c->d_ff % 64)
+    return fail(DG_ERR_SHAPE, "d_ff %d must be a multiple of 64 in [64, 4096]", c->d_ff);
+  if (c->max_tokens < 1 || c->max_tokens > (1 << 20))
+    return fail(DG_ERR_SHAPE, "max_tokens %d not in [1, 2^20]", c->max_tokens);
+  if (!(c->rms_eps > 0.0f) || !std::isfinite(c->rms_eps)) return fail(DG_ERR_INVALID_ARG, "rms_eps must be finite and > 0");
+  if (c->act_dtype != DG_F32 && c->act_dtype != DG_BF16)
+    return fail(DG_ERR_DTYPE, "act_dtype %d: only DG_F32 or DG_BF16", c->act_dtype);
+  if (c->router_w_dtype != DG_F32 && c->router_w_dtype != DG_BF16)
+    return fail(DG_ERR_DTYPE, "router_w_dtype %d: only DG_F32 or DG_BF16", c->router_w_dtype);
+  if (c->expert_w_dtype != DG_BF16 && c->expert_w_dtype != DG_I4G128)
+    return fail(DG_ERR_DTYPE, "expert_w_dtype %d: only DG_BF16 or DG_I4G128", c->expert_w_dtype);
+  if (c->flags & ~DG_MOE_PACK_WEIGHTS) return fail(DG_ERR_INVALID_ARG, "unknown config flags 0x%x", c->flags);
+  return DG_OK;
+}
+
+}  // namespace
+
+struct dg_moe_s {
+  dg_moe_config cfg;
+  Layout L;
+  int device;
+  char* ws;           // workspace + prepared router parameters
+  void* packed;       // expert weights copied at create (pack mode), else null
+  const void* w_gate_up;
+  const void* w_down;
+  const uint16_t* s_gate_up;
+  const uint16_t* s_down;
+  bool has_bias;
+
+  template <typename P>
+  P* at(size_t off) const { return reinterpret_cast<P*>(ws + off); }
+};
+
+namespace {
+
+struct ExpertBytes {
+  size_t gu, dn, sgu, sdn;
+};
+
+ExpertBytes expert_bytes(const dg_moe_config& c) {
+  const size_t E = c.n_experts, D = c.d_model, F = c.d_ff;
+  ExpertBytes b{};
+  if (c.expert_w_dtype == DG_BF16) {
+    b.gu = E * 2 * F * D * 2;
+    b.dn = E * D * F * 2;
+  } else {
+    b.gu = E * 2 * F * (D / 2);
+    b.dn = E * D * (F / 2);
+    b.sgu = E * 2 * F * (D / 128) * 2;
+    b.sdn = E * D * ((F + 127) / 128) * 2;
+  }
+  return b;
+}
+
+dg_status hip_fail(hipError_t e, const char* what) {
+  return fail(DG_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+}  // namespace
+
+extern "C" {
+
+int32_t dg_moe_abi_version(void) { return DG_MOE_ABI_VERSION; }
+
+const char* dg_moe_status_string(dg_status s) {
+  switch (s) {
+    case DG_OK: return "ok";
+    case DG_ERR_INVALID_ARG: return "invalid argument";
+    case DG_ERR_SHAPE: return "unsupported shape";
+    case DG_ERR_DTYPE: return "unsupported dtype";
+    case DG_ERR_ALIGN: return "pointer not 16-byte aligned";
+    case DG_ERR_OOM: return "device out of memory";
+    case DG_ERR_HIP: return "HIP runtime error";
+    case DG_ERR_UNSUPPORTED: return "unsupported device";
+  }
+  return "unknown status";
+}
+
+const char* dg_moe_last_error(void) { return g_last_error.c_str(); }
+
+uint64_t dg_moe_workspace_bytes(const dg_moe_config* cfg) {
+  if (check_config(cfg) != DG_OK) return 0;
+  return (uint64_t)plan(*cfg).total;
+}
+
+dg_status dg_moe_create(const dg_moe_config* cfg, const dg_moe_weights* w, void* stream_v, dg_moe_handle* out) {
+  if (out) *out = nullptr;
+  dg_status st = check_config(cfg);
+  if (st != DG_OK) return st;
+  if (!w || !out) return fail(DG_ERR_INVALID_ARG, "weights or out is NULL");
+  const bool i4 = cfg->expert_w_dtype == DG_I4G128;
+  if (!w->router_w || !w->router_gamma || !w->ffn_gamma || !w->w_gate_up || !w->w_down)
+    return fail(DG_ERR_INVALID_ARG, "a required weight pointer is NULL");
+  if (i4 && (!w->s_gate_up || !w->s_down)) return fail(DG_ERR_INVALID_ARG, "int4 weights need both scale tensors");
+  const void* ptrs[] = {w->router_w, w->router_gamma, w->router_bias, w->ffn_gamma,
+                        w->w_gate_up, w->w_down, w->s_gate_up, w->s_down};
+  for (const void* p : ptrs)
+    if (p && !aligned16(p)) return fail(DG_ERR_ALIGN, "weight pointer %p is not 16-byte aligned", p);
+
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
+  hipDeviceProp_t prop;
+  e = hipGetDeviceProperties(&prop, dev);
+  if (e != hipSuccess) return hip_fail(e, "hipGetDeviceProperties");
+  if (std::strncmp(prop.gcnArchName, "gfx950", 6) != 0)
+    return fail(DG_ERR_UNSUPPORTED, "device %d is %s; this library is built for gfx950", dev, prop.gcnArchName);
+
+  dg_moe_s* hd = new (std::nothrow) dg_moe_s();
+  if (!hd) return fail(DG_ERR_OOM, "host allocation failed");
+  hd->cfg = *cfg;
+  hd->L = plan(*cfg);
+  hd->device = dev;
+  hipStream_t stream = static_cast<hipStream_t>(stream_v);
+
+  e = hipMalloc(reinterpret_cast<void**>(&hd->ws), hd->L.total);
+  if (e != hipSuccess) {
+    delete hd;
+    (void)hipGetLastError();
+    return fail(DG_ERR_OOM, "workspace of %zu bytes: %s", hd->L.total, hipGetErrorString(e));
+  }
+  const ExpertBytes eb = expert_bytes(*cfg);
+  if (cfg->flags & DG_MOE_PACK_WEIGHTS) {
+    const size_t total = round_up(eb.gu, 256) + round_up(eb.dn, 256) + round_up(eb.sgu, 256) + round_up(eb.sdn, 256);
+    e = hipMalloc(&hd->packed, total);
+    if (e != hipSuccess) {
+      (void)hipFree(hd->ws);
+      delete hd;
+      (void)hipGetLastError();
+      return fail(DG_ERR_OOM, "packed weights of %zu bytes: %s", total, hipGetErrorString(e));
+    }
+    char* p = static_cast<char*>(hd->packed);
+    hd->w_gate_up = p;
+    hd->w_down = p + round_up(eb.gu, 256);
+    hd->s_gate_up = i4 ? reinterpret_cast<const uint16_t*>(p + round_up(eb.gu, 256) + round_up(eb.dn, 256)) : nullptr;
+    hd->s_down = i4 ? reinterpret_cast<const uint16_t*>(p + round_up(eb.gu, 256) + round_up(eb.dn, 256) +
+                                                        round_up(eb.sgu, 256))
+                    : nullptr;
+    hipError_t c1 = hipMemcpyAsync(const_cast<void*>(hd->w_gate_up), w->w_gate_up, eb.gu, hipMemcpyDeviceToDevice, stream);
+    hipError_t c2 = hipMemcpyAsync(const_cast<void*>(hd->w_down), w->w_down, eb.dn, hipMemcpyDeviceToDevice, stream);
+    hipError_t c3 = hipSuccess, c4 = hipSuccess;
+    if (i4) {
+      c3 = hipMemcpyAsync(const_cast<uint16_t*>(hd->s_gate_up), w->s_gate_up, eb.sgu, hipMemcpyDeviceToDevice, stream);
+      c4 = hipMemcpyAsync(const_cast<uint16_t*>(hd->s_down), w->s_down, eb.sdn, hipMemcpyDeviceToDevice, stream);
+    }
+    if (c1 != hipSuccess || c2 != hipSuccess || c3 != hipSuccess || c4 != hipSuccess) {
+      dg_moe_destroy(hd);
+      return fail(DG_ERR_HIP, "copying expert weights failed");
+    }
+  } else {
+    hd->w_gate_up = w->w_gate_up;
+    hd->w_down = w->w_down;
+    hd->s_gate_up = w->s_gate_up;
+    hd->s_down = w->s_down;
+  }
+  hd->has_bias = w->router_bias != nullptr;
+  const size_t D = cfg->d_model, E = cfg->n_experts;
+  hipError_t c[4];
+  c[0] = hipMemcpyAsync(hd->ws + hd->L.gamma_r, w->router_gamma, D * 4, hipMemcpyDeviceToDevice, stream);
+  c[1] = hipMemcpyAsync(hd->ws + hd->L.gamma_e, w->ffn_gamma, D * 4, hipMemcpyDeviceToDevice, stream);
+  c[2] = hd->has_bias ? hipMemcpyAsync(hd->ws + hd->L.bias, w->router_bias, E * 4, hipMemcpyDeviceToDevice, stream)
+                      : hipSuccess;
+  c[3] = dg::launch_prep_router_w(w->router_w, cfg->router_w_dtype == DG_F32, (int)E, hd->L.Epad, (int)D,
+                                  hd->at<uint16_t>(hd->L.wr), stream);
+  for (hipError_t ci : c) {
+    if (ci != hipSuccess) {
+      dg_moe_destroy(hd);
+      return hip_fail(ci, "preparing router parameters");
+    }
+  }
+  e = hipStreamSynchronize(stream);
+  if (e != hipSuccess) {
+    dg_moe_destroy(hd);
+    return hip_fail(e, "create: stream synchronize");
+  }
+  *out = hd;
+  return ok();
+}
+
+static dg_status run_forward(dg_moe_handle hd, const void* x, void* out, int32_t T, const void* addend,
+                             uint32_t flags, const dg_moe_debug* dbg, void* const* events, void* stream_v) {
+  if (!hd) return fail(DG_ERR_INVALID_ARG, "handle is NULL");
+  if (flags & ~DG_FWD_ADD_INPUT) return fail(DG_ERR_INVALID_ARG, "unknown forward flags 0x%x", flags);
+  const dg_moe_config& c = hd->cfg;
+  if (T < 0 || T > c.max_tokens) return fail(DG_ERR_SHAPE, "T = %d not in [0, max_tokens = %d]", T, c.max_tokens);
+  if (T == 0) return ok();
+  if (!x || !out) return fail(DG_ERR_INVALID_ARG, "x or out is NULL");
+  if (!aligned16(x) || !aligned16(out) || (addend && !aligned16(addend)))
+    return fail(DG_ERR_ALIGN, "x, out and addend must be 16-byte aligned");
+  const size_t bytes = (size_t)T * c.d_model * act_elem_bytes(c.act_dtype);
+  auto overlap = [bytes](const void* p, const void* q) {
+    const char* a = static_cast<const char*>(p);
+    const char* b = static_cast<const char*>(q);
+    return a < b + bytes && b < a + bytes;
+  };
+  if (overlap(out, x) || (addend && overlap(out, addend)))
+    return fail(DG_ERR_INVALID_ARG, "out overlaps x or addend");
+
+  hipStream_t stream = static_cast<hipStream_t>(stream_v);
+  const Layout& L = hd->L;
+  const bool i4 = c.expert_w_dtype == DG_I4G128;
+  auto mark = [&](int i) -> hipError_t {
+    return events ? hipEventRecord(static_cast<hipEvent_t>(events[i]), stream) : hipSuccess;
+  };
+  if (mark(0) != hipSuccess) return fail(DG_ERR_HIP, "hipEventRecord");
+
+  dg::RouterArgs ra{};
+  ra.x = x;
+  ra.x_f32 = c.act_dtype == DG_F32;
+  ra.T = T;
+  ra.D = c.d_model;
+  ra.E = c.n_experts;
+  ra.Epad = L.Epad;
+  ra.K = c.top_k;
+  ra.wr = hd->at<uint16_t>(L.wr);
+  ra.n_wplanes = L.n_wplanes;
+  ra.gamma_r = hd->at<float>(L.gamma_r);
+  ra.bias = hd->has_bias ? hd->at<float>(L.bias) : nullptr;
+  ra.gamma_e = hd->at<float>(L.gamma_e);
+  ra.eps = c.rms_eps;
+  ra.h_f16 = i4 ? 1 : 0;
+  ra.h = hd->at<uint16_t>(L.h);
+  ra.topk_idx = hd->at<int32_t>(L.topk_idx);
+  ra.topk_w = hd->at<float>(L.topk_w);
+  hipError_t e = dg::launch_router(ra, stream);
+  if (e != hipSuccess) return hip_fail(e, "router launch");
+  if ((e = mark(1)) != hipSuccess) return hip_fail(e, "hipEventRecord");
+
+  dg::PermuteArgs pa{};
+  pa.topk_idx = ra.topk_idx;
+  pa.topk_w = ra.topk_w;
+  pa.T = T;
+  pa.K = c.top_k;
+  pa.E = c.n_experts;
+  pa.BM = dg::kTileRows;
+  pa.counts = hd->at<int32_t>(L.counts);
+  pa.offsets = hd->at<int32_t>(L.offsets);
+  pa.tiles = hd->at<dg::Tile>(L.tiles);
+  pa.n_tiles = hd->at<int32_t>(L.n_tiles);
+  pa.sorted_token = hd->at<int32_t>(L.sorted_token);
+  pa.row_w = hd->at<float>(L.row_w);
+  pa.row_of_slot = hd->at<int32_t>(L.row_of_slot);
+  e = dg::launch_permute(pa, stream);
+  if (e != hipSuccess) return hip_fail(e, "permute launch");
+  if ((e = mark(2)) != hipSuccess) return hip_fail(e, "hipEventRecord");
+
+  dg::GemmArgs ga{};
+  ga.tiles = pa.tiles;
+  ga.n_tiles = pa.n_tiles;
+  ga.max_tiles = (int)((size_t)c.top_k * T / dg::kTileRows + c.n_experts);
+  ga.sorted_token = pa.sorted_token;
+  ga.row_w = pa.row_w;
+  ga.h = ra.h;
+  ga.w_gate_up = hd->w_gate_up;
+  ga.w_down = hd->w_down;
+  ga.s_gate_up = hd->s_gate_up;
+  ga.s_down = hd->s_down;
+  ga.act = hd->at<uint16_t>(L.act);
+  ga.y = hd->at<float>(L.y);
+  ga.D = c.d_model;
+  ga.F = c.d_ff;
+  e = i4 ? dg::launch_gate_up_i4(ga, stream) : dg::launch_gate_up_bf16(ga, stream);
+  if (e != hipSuccess) return hip_fail(e, "gate_up launch");
+  if ((e = mark(3)) != hipSuccess) return hip_fail(e, "hipEventRecord");
+  e = i4 ? dg::launch_down_i4(ga, stream) : dg::launch_down_bf16(ga, stream);
+  if (e != hipSuccess) return hip_fail(e, "down launch");
+  if ((e = mark(4)) != hipSuccess) return hip_fail(e, "hipEventRecord");
+
+  dg::CombineArgs ca{};
+  ca.y = ga.y;
+  ca.row_of_slot = pa.row_of_slot;
+  ca.T = T;
+  ca.K = c.top_k;
+  ca.D = c.d_model;
+  ca.x = (flags & DG_FWD_ADD_INPUT) ? x : nullptr;
+  ca.addend = addend;
+  ca.out = out;
+  ca.act_f32 = c.act_dtype == DG_F32;
+  e = dg::launch_combine(ca, stream);
+  if (e != hipSuccess) return hip_fail(e, "combine launch");
+  if ((e = mark(5)) != hipSuccess) return hip_fail(e, "hipEventRecord");
+
+  if (dbg) {
+    const size_t tk = (size_t)T * c.top_k;
+    struct Cp {
+      void* dst;
+      size_t off;
+      size_t bytes;
+    } cps[] = {{dbg->topk_idx, L.topk_idx, tk * 4},
+               {dbg->topk_w, L.topk_w, tk * 4},
+               {dbg->counts, L.counts, (size_t)c.n_experts * 4},
+               {dbg->offsets, L.offsets, (size_t)(c.n_experts + 1) * 4},
+               {dbg->sorted_token, L.sorted_token, tk * 4},
+               {dbg->row_of_slot, L.row_of_slot, tk * 4}};
+    for (const Cp& cp : cps) {
+      if (!cp.dst) continue;
+      e = hipMemcpyAsync(cp.dst, hd->ws + cp.off, cp.bytes, hipMemcpyDeviceToDevice, stream);
+      if (e != hipSuccess) return hip_fail(e, "debug copy");
+    }
+  }
+  return ok();
+}
+
+dg_status dg_moe_forward(dg_moe_handle hd, const void* x, void* out, int32_t T, const void* addend, uint32_t flags,
+                         void* stream) {
+  return run_forward(hd, x, out, T, addend, flags, nullptr, nullptr, stream);
+}
+
+dg_status dg_moe_forward_profiled(dg_moe_handle hd, const void* x, void* out, int32_t T, const void* addend,
+                                  uint32_t flags, void* const* events, void* stream) {
+  if (!events) return fail(DG_ERR_INVALID_ARG, "events is NULL");
+  for (int i = 0; i < 6; ++i)
+    if (!events[i]) return fail(DG_ERR_INVALID_ARG, "events[%d] is NULL", i);
+  if (T <= 0) return fail(DG_ERR_SHAPE, "profiled forward needs T > 0");
+  return run_forward(hd, x, out, T, addend, flags, nullptr, events, stream);
+}
+
+dg_status dg_moe_forward_debug(dg_moe_handle hd, const void* x, void* out, int32_t T, const dg_moe_debug* dbg,
+                               void* stream) {
+  if (!dbg) return fail(DG_ERR_INVALID_ARG, "debug struct is NULL");
+  return run_forward(hd, x, out, T, nullptr, 0, dbg, nullptr, stream);
+}
+
+dg_status dg_moe_destroy(dg_moe_handle hd) {
+  if (!hd) return ok();
+  hipError_t e1 = hd->ws ? hipFree(hd->ws) : hipSuccess;
+  hipError_t e2 = hd->packed ? hipFree(hd->packed) : hipSuccess;
+  delete hd;
+  if (e1 != hipSuccess) return hip_fail(e1, "hipFree(workspace)");
+  if (e2 != hipSuccess) return hip_fail(e2, "hipFree(packed weights)");
+  return ok();
+}
+
+}  // extern "C"

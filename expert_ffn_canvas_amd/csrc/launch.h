@@ -1,0 +1,79 @@
+// Host-side launchers of the gfx950 kernels (one per kernel family). Each
+// enqueues work on `stream` and returns the launch status; none synchronises.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace dg {
+
+struct Tile;
+
+struct RouterArgs {
+  const void* x;        // [T, D] fp32 or bf16
+  int x_f32;
+  int T, D, E, Epad, K;
+  const uint16_t* wr;   // bf16 planes [n_wplanes][Epad][D]
+  int n_wplanes;        // 1 (bf16 router weight) or 3 (fp32 split exactly)
+  const float* gamma_r;
+  const float* bias;    // [E] or null
+  const float* gamma_e;
+  float eps;
+  int h_f16;            // expert input stored as fp16 (int4 experts) instead of bf16
+  uint16_t* h;          // [T, D]
+  int32_t* topk_idx;    // [T, K]
+  float* topk_w;        // [T, K]
+};
+hipError_t launch_router(const RouterArgs& a, hipStream_t stream);
+hipError_t launch_prep_router_w(const void* w, int w_f32, int E, int Epad, int D, uint16_t* planes,
+                                hipStream_t stream);
+
+struct PermuteArgs {
+  const int32_t* topk_idx;
+  const float* topk_w;
+  int T, K, E, BM;
+  int32_t* counts;        // [E]
+  int32_t* offsets;       // [E + 1]
+  Tile* tiles;            // [max_tiles]
+  int32_t* n_tiles;       // [1]
+  int32_t* sorted_token;  // [K T]
+  float* row_w;           // [K T]
+  int32_t* row_of_slot;   // [K T]
+};
+hipError_t launch_permute(const PermuteArgs& a, hipStream_t stream);
+
+struct GemmArgs {
+  const Tile* tiles;
+  const int32_t* n_tiles;
+  int max_tiles;
+  const int32_t* sorted_token;
+  const float* row_w;
+  const uint16_t* h;       // [T, D] expert input (bf16, or fp16 for int4 experts)
+  const void* w_gate_up;   // bf16 [E, 2F, D] or int4 bytes [E, 2F, D/2]
+  const void* w_down;      // bf16 [E, D, F] or int4 bytes [E, D, F/2]
+  const uint16_t* s_gate_up;
+  const uint16_t* s_down;
+  uint16_t* act;           // [K T, F] gelu_tanh(gate) * up, expert-sorted rows
+  float* y;                // [K T, D] w * down(act), expert-sorted rows
+  int D, F;
+};
+hipError_t launch_gate_up_bf16(const GemmArgs& a, hipStream_t stream);
+hipError_t launch_down_bf16(const GemmArgs& a, hipStream_t stream);
+hipError_t launch_gate_up_i4(const GemmArgs& a, hipStream_t stream);
+hipError_t launch_down_i4(const GemmArgs& a, hipStream_t stream);
+
+struct CombineArgs {
+  const float* y;
+  const int32_t* row_of_slot;
+  int T, K, D;
+  const void* x;       // residual to add, or null
+  const void* addend;  // extra addend, or null
+  void* out;
+  int act_f32;
+};
+hipError_t launch_combine(const CombineArgs& a, hipStream_t stream);
+
+// Largest number of rows one tile holds.
+constexpr int kTileRows = 128;
+
+}  // namespace dg

@@ -1,0 +1,225 @@
+"""ctypes binding of libdgmoe.so (include/dg_moe.h): argument marshalling only.
+
+The C entry points are exposed under their own names. `MoELayer` is a small
+convenience wrapper that keeps torch tensors (device memory) alive next to a
+handle; every step of the layer runs in the HIP library.
+
+Importing this module loads the library and fails loudly if it has not been
+built: there is no CPU fallback.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "libdgmoe.so")
+
+DG_F32, DG_BF16, DG_F16, DG_I4G128 = 0, 1, 2, 3
+DG_OK = 0
+DG_ERR_INVALID_ARG, DG_ERR_SHAPE, DG_ERR_DTYPE, DG_ERR_ALIGN = -1, -2, -3, -4
+DG_ERR_OOM, DG_ERR_HIP, DG_ERR_UNSUPPORTED = -5, -6, -7
+DG_MOE_PACK_WEIGHTS = 0x1
+DG_FWD_ADD_INPUT = 0x1
+ABI_VERSION = 1
+
+EXPORTED = ("dg_moe_create", "dg_moe_forward", "dg_moe_forward_debug", "dg_moe_forward_profiled", "dg_moe_destroy",
+            "dg_moe_status_string", "dg_moe_last_error", "dg_moe_abi_version", "dg_moe_workspace_bytes")
+
+
+class dg_moe_config(ctypes.Structure):
+    _fields_ = [("struct_size", ctypes.c_uint32), ("n_experts", ctypes.c_int32), ("top_k", ctypes.c_int32),
+                ("d_model", ctypes.c_int32), ("d_ff", ctypes.c_int32), ("max_tokens", ctypes.c_int32),
+                ("rms_eps", ctypes.c_float), ("act_dtype", ctypes.c_int32), ("router_w_dtype", ctypes.c_int32),
+                ("expert_w_dtype", ctypes.c_int32), ("flags", ctypes.c_uint32)]
+
+
+class dg_moe_weights(ctypes.Structure):
+    _fields_ = [("router_w", ctypes.c_void_p), ("router_gamma", ctypes.c_void_p), ("router_bias", ctypes.c_void_p),
+                ("ffn_gamma", ctypes.c_void_p), ("w_gate_up", ctypes.c_void_p), ("w_down", ctypes.c_void_p),
+                ("s_gate_up", ctypes.c_void_p), ("s_down", ctypes.c_void_p)]
+
+
+class dg_moe_debug(ctypes.Structure):
+    _fields_ = [("topk_idx", ctypes.c_void_p), ("topk_w", ctypes.c_void_p), ("counts", ctypes.c_void_p),
+                ("offsets", ctypes.c_void_p), ("sorted_token", ctypes.c_void_p), ("row_of_slot", ctypes.c_void_p)]
+
+
+def _load():
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(f"{LIB_PATH} is missing: build it with `python -m expert_ffn_canvas_amd.build` "
+                          "(there is no CPU fallback for the MoE layer)")
+    # Load torch first: its HIP runtime then owns the process, and the library (which needs the same
+    # soname, libamdhip64.so.7) binds to that one runtime, the one that made the caller's streams and memory.
+    import torch  # noqa: F401
+    lib = ctypes.CDLL(LIB_PATH)
+    vp, i32, u32 = ctypes.c_void_p, ctypes.c_int32, ctypes.c_uint32
+    lib.dg_moe_create.argtypes = [ctypes.POINTER(dg_moe_config), ctypes.POINTER(dg_moe_weights), vp,
+                                  ctypes.POINTER(vp)]
+    lib.dg_moe_create.restype = i32
+    lib.dg_moe_forward.argtypes = [vp, vp, vp, i32, vp, u32, vp]
+    lib.dg_moe_forward.restype = i32
+    lib.dg_moe_forward_debug.argtypes = [vp, vp, vp, i32, ctypes.POINTER(dg_moe_debug), vp]
+    lib.dg_moe_forward_debug.restype = i32
+    lib.dg_moe_forward_profiled.argtypes = [vp, vp, vp, i32, vp, u32, ctypes.POINTER(vp), vp]
+    lib.dg_moe_forward_profiled.restype = i32
+    lib.dg_moe_destroy.argtypes = [vp]
+    lib.dg_moe_destroy.restype = i32
+    lib.dg_moe_status_string.argtypes = [i32]
+    lib.dg_moe_status_string.restype = ctypes.c_char_p
+    lib.dg_moe_last_error.argtypes = []
+    lib.dg_moe_last_error.restype = ctypes.c_char_p
+    lib.dg_moe_abi_version.argtypes = []
+    lib.dg_moe_abi_version.restype = i32
+    lib.dg_moe_workspace_bytes.argtypes = [ctypes.POINTER(dg_moe_config)]
+    lib.dg_moe_workspace_bytes.restype = ctypes.c_uint64
+    if lib.dg_moe_abi_version() != ABI_VERSION:
+        raise ImportError("libdgmoe.so ABI version mismatch")
+    return lib
+
+
+_lib = _load()
+
+
+class DgMoeError(RuntimeError):
+    def __init__(self, status, where):
+        self.status = status
+        detail = _lib.dg_moe_last_error().decode()
+        super().__init__(f"{where}: {_lib.dg_moe_status_string(status).decode()} ({status}): {detail}")
+
+
+def _check(status, where):
+    if status != DG_OK:
+        raise DgMoeError(status, where)
+
+
+# --- the C entry points under their own names -------------------------------------------------------------
+
+def dg_moe_create(cfg: dg_moe_config, weights: dg_moe_weights, stream: int):
+    """Returns (status, handle)."""
+    h = ctypes.c_void_p()
+    st = _lib.dg_moe_create(ctypes.byref(cfg), ctypes.byref(weights), ctypes.c_void_p(stream), ctypes.byref(h))
+    return st, h
+
+
+def dg_moe_forward(handle, x: int, out: int, T: int, addend: int | None, flags: int, stream: int) -> int:
+    return _lib.dg_moe_forward(handle, x, out, T, addend, flags, ctypes.c_void_p(stream))
+
+
+def dg_moe_forward_debug(handle, x: int, out: int, T: int, dbg: dg_moe_debug, stream: int) -> int:
+    return _lib.dg_moe_forward_debug(handle, x, out, T, ctypes.byref(dbg), ctypes.c_void_p(stream))
+
+
+def dg_moe_forward_profiled(handle, x: int, out: int, T: int, addend: int | None, flags: int, events,
+                            stream: int) -> int:
+    """events: sequence of six hipEvent_t handles (ints)."""
+    arr = (ctypes.c_void_p * 6)(*events)
+    return _lib.dg_moe_forward_profiled(handle, x, out, T, addend, flags, arr, ctypes.c_void_p(stream))
+
+
+def dg_moe_destroy(handle) -> int:
+    return _lib.dg_moe_destroy(handle)
+
+
+def dg_moe_status_string(status: int) -> str:
+    return _lib.dg_moe_status_string(status).decode()
+
+
+def dg_moe_last_error() -> str:
+    return _lib.dg_moe_last_error().decode()
+
+
+def dg_moe_abi_version() -> int:
+    return _lib.dg_moe_abi_version()
+
+
+def dg_moe_workspace_bytes(cfg: dg_moe_config) -> int:
+    return _lib.dg_moe_workspace_bytes(ctypes.byref(cfg))
+
+
+def make_config(E=128, K=8, D=2816, F=704, max_tokens=256, eps=1e-6, act=DG_BF16, router_w=DG_BF16,
+                experts=DG_BF16, flags=0) -> dg_moe_config:
+    return dg_moe_config(ctypes.sizeof(dg_moe_config), E, K, D, F, max_tokens, eps, act, router_w, experts, flags)
+
+
+# --- torch convenience wrapper (device memory and streams only) -------------------------------------------
+
+def _ptr(t):
+    return None if t is None else t.data_ptr()
+
+
+def _dtype_code(t):
+    import torch
+    return {torch.float32: DG_F32, torch.bfloat16: DG_BF16, torch.float16: DG_F16}[t.dtype]
+
+
+class MoELayer:
+    """One MoE layer handle over device tensors in the synth weight-dict format."""
+
+    def __init__(self, weights: dict, max_tokens: int, act_dtype, top_k: int = 8, eps: float = 1e-6,
+                 pack: bool = False, stream=None):
+        import torch
+        self.w = weights  # keep the borrowed device tensors alive
+        rw = weights["router_w"]
+        i4 = "q_gate_up" in weights
+        E, D = rw.shape
+        gu = weights["q_gate_up"] if i4 else weights["w_gate_up"]
+        F = gu.shape[1] // 2
+        self.E, self.D, self.F = E, D, F
+        self.K = top_k
+        self.act_dtype = act_dtype
+        cfg = make_config(E=E, K=self.K, D=D, F=F, max_tokens=max_tokens, eps=eps, act=_dtype_code(
+            torch.empty((), dtype=act_dtype)), router_w=_dtype_code(rw), experts=DG_I4G128 if i4 else DG_BF16,
+            flags=DG_MOE_PACK_WEIGHTS if pack else 0)
+        wts = dg_moe_weights(
+            _ptr(rw), _ptr(weights["router_gamma"]), _ptr(weights.get("router_bias")), _ptr(weights["ffn_gamma"]),
+            _ptr(gu), _ptr(weights["q_down"] if i4 else weights["w_down"]),
+            _ptr(weights.get("s_gate_up")), _ptr(weights.get("s_down")))
+        self.stream = stream if stream is not None else torch.cuda.current_stream()
+        st, h = dg_moe_create(cfg, wts, self.stream.cuda_stream)
+        _check(st, "dg_moe_create")
+        self.handle = h
+        self.max_tokens = max_tokens
+
+    def forward(self, x, out=None, addend=None, add_input=False):
+        import torch
+        T = x.shape[0]
+        if out is None:
+            out = torch.empty((T, self.D), dtype=x.dtype, device=x.device)
+        st = dg_moe_forward(self.handle, _ptr(x), _ptr(out), T, _ptr(addend), DG_FWD_ADD_INPUT if add_input else 0,
+                            self.stream.cuda_stream)
+        _check(st, "dg_moe_forward")
+        return out
+
+    def forward_debug(self, x, out=None):
+        """Forward plus routing/permutation outputs (device tensors)."""
+        import torch
+        T = x.shape[0]
+        dev = x.device
+        if out is None:
+            out = torch.empty((T, self.D), dtype=x.dtype, device=dev)
+        r = dict(
+            topk_idx=torch.empty((T, self.K), dtype=torch.int32, device=dev),
+            topk_w=torch.empty((T, self.K), dtype=torch.float32, device=dev),
+            counts=torch.empty((self.E,), dtype=torch.int32, device=dev),
+            offsets=torch.empty((self.E + 1,), dtype=torch.int32, device=dev),
+            sorted_token=torch.empty((T * self.K,), dtype=torch.int32, device=dev),
+            row_of_slot=torch.empty((T * self.K,), dtype=torch.int32, device=dev),
+        )
+        dbg = dg_moe_debug(*(_ptr(r[k]) for k in ("topk_idx", "topk_w", "counts", "offsets", "sorted_token",
+                                                   "row_of_slot")))
+        st = dg_moe_forward_debug(self.handle, _ptr(x), _ptr(out), T, dbg, self.stream.cuda_stream)
+        _check(st, "dg_moe_forward_debug")
+        r["out"] = out
+        return r
+
+    def close(self):
+        if getattr(self, "handle", None):
+            _check(dg_moe_destroy(self.handle), "dg_moe_destroy")
+            self.handle = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass

@@ -1,0 +1,172 @@
+/*
+ * dg_moe.h - C ABI of the MI355X (gfx950) mixture-of-experts feed-forward layer
+ * of DiffusionGemma 26B-A4B.
+ *
+ * The layer (per token t, residual x_t of width d_model):
+ *
+ *   r_t      = 1 / sqrt(mean_d x_t[d]^2 + eps)
+ *   logits   = W_r (x_t r_t (1 + gamma_r)) + b                 router with its own norm
+ *   S_t      = the top_k largest logits (ties: lower expert id)
+ *   w_{t,e}  = softmax(logits)_e / sum_{e' in S_t} softmax(logits)_{e'}
+ *   h_t      = x_t r_t (1 + gamma_e)                           pre_feedforward_layernorm_2
+ *   FFN_e(h) = W_down[e] (gelu_tanh(W_gate[e] h) * (W_up[e] h))
+ *   MoE(x)_t = sum_{e in S_t} w_{t,e} FFN_e(h_t)
+ *
+ * Sources (page title, section):
+ *  - 128 experts with 8 active: Quant-Tuner PR "Add DiffusionGemma (Gemma-4 MoE
+ *    block-diffusion) support", Summary.
+ *  - Expert linears gate_proj/up_proj 2816->704 and down_proj 704->2816, no
+ *    bias, GELUTanh activation: auto-round PR "Add quantization support for
+ *    DiffusionGemma", transformers backend test log, expert module dumps.
+ *  - (1+gamma) RMSNorm pre_feedforward_layernorm_2 feeding only the fused 3D
+ *    gate_up projection; the router reading the raw residual through its own
+ *    norm: Quant-Tuner PR, "Answers to the motivating questions" (AWQ answer).
+ *  - int4, group size 128, symmetric: auto-round PR, quantization_config.
+ *
+ * Conventions for every entry point:
+ *  - All tensor pointers are DEVICE pointers (hipMalloc or torch CUDA memory),
+ *    row-major and densely packed; 16-byte aligned.
+ *  - `stream` is a hipStream_t passed as void*; NULL means the null stream.
+ *  - Every call returns a dg_status. Arguments are checked on the host before
+ *    anything is enqueued; on an error nothing is launched and
+ *    dg_moe_last_error() holds a message (thread-local). No C++ exception
+ *    crosses this boundary. Faults during asynchronous execution surface at
+ *    the caller's next synchronisation.
+ *  - The library never synchronises the device inside dg_moe_forward and never
+ *    reads device data back to the host there.
+ */
+#ifndef DG_MOE_H
+#define DG_MOE_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define DG_MOE_ABI_VERSION 1
+
+/* Element types. DG_I4G128: 4-bit codes q in [0,15] standing for (q - 8) * s,
+ * two codes per byte (even input index in the low nibble), with one fp16
+ * scale s per (output row, group of 128 consecutive inputs); the last group
+ * of a row holds whatever remains (64 inputs when the row is 704 long). */
+typedef enum dg_dtype { DG_F32 = 0, DG_BF16 = 1, DG_F16 = 2, DG_I4G128 = 3 } dg_dtype;
+
+typedef enum dg_status {
+  DG_OK = 0,
+  DG_ERR_INVALID_ARG = -1, /* null pointer, bad handle, bad flag            */
+  DG_ERR_SHAPE = -2,       /* a size out of the supported range            */
+  DG_ERR_DTYPE = -3,       /* unsupported element type or combination      */
+  DG_ERR_ALIGN = -4,       /* a pointer not 16-byte aligned                */
+  DG_ERR_OOM = -5,         /* device allocation failed in dg_moe_create    */
+  DG_ERR_HIP = -6,         /* a HIP runtime call or kernel launch failed   */
+  DG_ERR_UNSUPPORTED = -7  /* no GPU of the supported architecture         */
+} dg_status;
+
+/* dg_moe_config.flags */
+#define DG_MOE_PACK_WEIGHTS 0x1u /* copy the expert weights into handle-owned
+                                    memory at create (else borrow the caller's) */
+
+/* dg_moe_forward flags */
+#define DG_FWD_ADD_INPUT 0x1u /* out = x + MoE(x) (+ addend) */
+
+typedef struct dg_moe_config {
+  uint32_t struct_size;   /* = sizeof(dg_moe_config)                                  */
+  int32_t n_experts;      /* E, 1..256 (128 for the model)                             */
+  int32_t top_k;          /* k, 1..min(E, 8) (8 for the model)                         */
+  int32_t d_model;        /* D, multiple of 128, <= 16384 (2816)                       */
+  int32_t d_ff;           /* F, multiple of 64, <= 4096 (704)                          */
+  int32_t max_tokens;     /* largest T a forward may take; sizes the workspace         */
+  float rms_eps;          /* eps of both RMSNorms (> 0)                                */
+  int32_t act_dtype;      /* x / out / addend: DG_F32 or DG_BF16                       */
+  int32_t router_w_dtype; /* router weight: DG_F32 or DG_BF16                          */
+  int32_t expert_w_dtype; /* expert weights: DG_BF16 or DG_I4G128                      */
+  uint32_t flags;         /* DG_MOE_PACK_WEIGHTS                                       */
+} dg_moe_config;
+
+/* Weights of one layer; device pointers. */
+typedef struct dg_moe_weights {
+  const void* router_w;       /* [E, D] router_w_dtype                                      */
+  const float* router_gamma;  /* [D] fp32; the router norm multiplies by (1 + gamma)        */
+  const float* router_bias;   /* [E] fp32 added to the logits before the softmax, or NULL   */
+  const float* ffn_gamma;     /* [D] fp32; the expert-input norm multiplies by (1 + gamma)  */
+  const void* w_gate_up;      /* bf16 [E, 2F, D]: rows 0..F-1 gate, F..2F-1 up;
+                                 int4: uint8 [E, 2F, D/2]                                  */
+  const void* w_down;         /* bf16 [E, D, F]; int4: uint8 [E, D, F/2]                   */
+  const uint16_t* s_gate_up;  /* int4 only: fp16 [E, 2F, D/128]                            */
+  const uint16_t* s_down;     /* int4 only: fp16 [E, D, ceil(F/128)]                       */
+} dg_moe_weights;
+
+/* Optional routing outputs of dg_moe_forward_debug; any member may be NULL. */
+typedef struct dg_moe_debug {
+  int32_t* topk_idx;     /* [T, k] selected experts, by logit descending then id     */
+  float* topk_w;         /* [T, k] their renormalised softmax weights                */
+  int32_t* counts;       /* [E] tokens routed to each expert                         */
+  int32_t* offsets;      /* [E + 1] exclusive prefix sum of counts                   */
+  int32_t* sorted_token; /* [k T] token of each expert-sorted row (increasing token
+                            order inside an expert)                                  */
+  int32_t* row_of_slot;  /* [k T] expert-sorted row of slot (t, j)                   */
+} dg_moe_debug;
+
+typedef struct dg_moe_s* dg_moe_handle;
+
+/* Create a layer handle: validates the configuration, allocates the whole
+ * workspace for config->max_tokens (so dg_moe_forward never allocates), and
+ * prepares the router weight. In borrow mode (default) the expert weight
+ * pointers are kept and must stay valid and unmodified for the handle's
+ * lifetime; with DG_MOE_PACK_WEIGHTS they are copied. router_gamma,
+ * router_bias and ffn_gamma are always copied. Work is enqueued on `stream`
+ * and the call synchronises that stream before returning.
+ * Errors: DG_ERR_INVALID_ARG (null cfg/weights/out, wrong struct_size),
+ * DG_ERR_SHAPE, DG_ERR_DTYPE, DG_ERR_ALIGN, DG_ERR_OOM, DG_ERR_HIP,
+ * DG_ERR_UNSUPPORTED (current device is not gfx950). *out is set to NULL on
+ * any error. */
+dg_status dg_moe_create(const dg_moe_config* cfg, const dg_moe_weights* weights, void* stream,
+                        dg_moe_handle* out);
+
+/* out[T, D] (act_dtype) = MoE(x[T, D]) (+ x if DG_FWD_ADD_INPUT) (+ addend if not
+ * NULL), summed in fp32 and rounded once (round-to-nearest-even for bf16).
+ * Asynchronous on `stream`. T = 0 returns DG_OK and launches nothing.
+ * `out` must not overlap `x` or `addend`. One handle must not run two
+ * forwards at the same time (they share the workspace): use one handle per
+ * stream. Errors: DG_ERR_INVALID_ARG (null handle/x/out, unknown flag,
+ * out overlapping an input), DG_ERR_SHAPE (T < 0 or T > max_tokens),
+ * DG_ERR_ALIGN, DG_ERR_HIP (launch failure). */
+dg_status dg_moe_forward(dg_moe_handle h, const void* x, void* out, int32_t T, const void* addend,
+                         uint32_t flags, void* stream);
+
+/* dg_moe_forward plus copies of the routing and permutation (device memory,
+ * filled asynchronously on `stream`). For tests and inspection. */
+dg_status dg_moe_forward_debug(dg_moe_handle h, const void* x, void* out, int32_t T,
+                               const dg_moe_debug* dbg, void* stream);
+
+/* Measurement entry point: dg_moe_forward that also records six caller-created
+ * hipEvent_t (passed as void*) on `stream`: events[0] before the router,
+ * [1] before the permutation, [2] before the gate_up GEMM, [3] before the down
+ * GEMM, [4] before the combine and [5] after it, so that the caller can read
+ * each kernel's duration with hipEventElapsedTime. T must be > 0. */
+dg_status dg_moe_forward_profiled(dg_moe_handle h, const void* x, void* out, int32_t T, const void* addend,
+                                  uint32_t flags, void* const* events, void* stream);
+
+/* Release the handle and everything it allocated. NULL is a no-op. Not stream
+ * ordered: the caller makes sure no forward on it is still running. */
+dg_status dg_moe_destroy(dg_moe_handle h);
+
+/* Static text for a status code. */
+const char* dg_moe_status_string(dg_status s);
+
+/* Detail of the last non-OK status returned on this thread ("" if none). */
+const char* dg_moe_last_error(void);
+
+/* DG_MOE_ABI_VERSION of the loaded library. */
+int32_t dg_moe_abi_version(void);
+
+/* Bytes of device workspace a handle with this configuration allocates
+ * (excluding packed weights); 0 if the configuration is invalid. */
+uint64_t dg_moe_workspace_bytes(const dg_moe_config* cfg);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* DG_MOE_H */

@@ -62,18 +62,23 @@ inline float bf16_bits_to_float(uint16_t b) {
 // IEEE binary16 -> fp32, written from the format definition
 // (1 sign bit, 5 exponent bits with bias 15, 10 fraction bits).
 inline float half_bits_to_float(uint16_t h) {
-  const int sign = (h >> 15) & 1;
-  const int expo = (h >> 10) & 0x1f;
-  const int frac = h & 0x3ff;
-  double v;
+  const uint32_t sign = static_cast<uint32_t>(h >> 15) << 31;
+  const uint32_t expo = (h >> 10) & 0x1f;
+  const uint32_t frac = h & 0x3ff;
+  uint32_t u;
   if (expo == 0) {
-    v = std::ldexp(static_cast<double>(frac), -24);  // subnormal: frac * 2^-24
+    // zero or subnormal: frac * 2^-24, exact in fp32
+    float v = static_cast<float>(frac) * 5.9604644775390625e-8f;
+    std::memcpy(&u, &v, 4);
+    u |= sign;
   } else if (expo == 31) {
-    v = frac ? NAN : INFINITY;
+    u = sign | 0x7f800000u | (frac << 13);  // inf or NaN
   } else {
-    v = std::ldexp(1.0 + frac / 1024.0, expo - 15);
+    u = sign | ((expo - 15 + 127) << 23) | (frac << 13);
   }
-  return static_cast<float>(sign ? -v : v);
+  float f;
+  std::memcpy(&f, &u, 4);
+  return f;
 }
 
 // fp32 -> bf16 with round-to-nearest-even on the dropped 16 bits.

@@ -1,0 +1,108 @@
+"""The C ABI library on the host (no GPU needed): it loads, exports every entry point the header
+declares, and rejects bad arguments before touching a device."""
+import ctypes
+import os
+import re
+
+import pytest
+
+from expert_ffn_canvas_amd import dgmoe
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "dg_moe.h")
+
+
+def declared_functions():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(dg_moe_\w+)\s*\(", src)))
+
+
+def test_header_declares_the_entry_points():
+    names = declared_functions()
+    for n in ("dg_moe_create", "dg_moe_forward", "dg_moe_destroy"):
+        assert n in names
+    assert set(names) == set(dgmoe.EXPORTED)
+
+
+def test_library_exports_every_declared_symbol():
+    lib = ctypes.CDLL(dgmoe.LIB_PATH)
+    for name in declared_functions():
+        assert hasattr(lib, name), f"{name} not exported"
+
+
+def test_struct_layouts_match_the_header():
+    # dg_moe_config: 11 four-byte fields; dg_moe_weights: 8 pointers; dg_moe_debug: 6 pointers
+    assert ctypes.sizeof(dgmoe.dg_moe_config) == 44
+    assert ctypes.sizeof(dgmoe.dg_moe_weights) == 64
+    assert ctypes.sizeof(dgmoe.dg_moe_debug) == 48
+
+
+def test_version_and_status_strings():
+    assert dgmoe.dg_moe_abi_version() == 1
+    assert dgmoe.dg_moe_status_string(dgmoe.DG_OK) == "ok"
+    for st in range(-7, 0):
+        assert dgmoe.dg_moe_status_string(st) not in ("", "unknown status")
+    assert dgmoe.dg_moe_status_string(-99) == "unknown status"
+
+
+def test_workspace_bytes():
+    good = dgmoe.make_config(max_tokens=256)
+    ws = dgmoe.dg_moe_workspace_bytes(good)
+    # at least h, act and the fp32 per-slot outputs
+    T, K, D, F = 256, 8, 2816, 704
+    assert ws >= T * D * 2 + K * T * F * 2 + K * T * D * 4
+    assert dgmoe.dg_moe_workspace_bytes(dgmoe.make_config(D=100)) == 0
+
+
+def _weights(align=16):
+    base = 1 << 20
+    return dgmoe.dg_moe_weights(base, base + 1 * 4096, 0, base + 2 * 4096, base + 3 * 4096, base + 4 * 4096,
+                                0, 0) if align == 16 else \
+        dgmoe.dg_moe_weights(base + 8, base + 4096, 0, base + 2 * 4096, base + 3 * 4096, base + 4 * 4096, 0, 0)
+
+
+@pytest.mark.parametrize("field,value,status", [
+    ("n_experts", 0, dgmoe.DG_ERR_SHAPE),
+    ("n_experts", 300, dgmoe.DG_ERR_SHAPE),
+    ("top_k", 9, dgmoe.DG_ERR_SHAPE),
+    ("top_k", 0, dgmoe.DG_ERR_SHAPE),
+    ("d_model", 2800, dgmoe.DG_ERR_SHAPE),
+    ("d_ff", 700, dgmoe.DG_ERR_SHAPE),
+    ("max_tokens", 0, dgmoe.DG_ERR_SHAPE),
+    ("rms_eps", 0.0, dgmoe.DG_ERR_INVALID_ARG),
+    ("act_dtype", dgmoe.DG_F16, dgmoe.DG_ERR_DTYPE),
+    ("router_w_dtype", dgmoe.DG_I4G128, dgmoe.DG_ERR_DTYPE),
+    ("expert_w_dtype", dgmoe.DG_F32, dgmoe.DG_ERR_DTYPE),
+    ("flags", 0x80, dgmoe.DG_ERR_INVALID_ARG),
+    ("struct_size", 12, dgmoe.DG_ERR_INVALID_ARG),
+])
+def test_create_rejects_bad_config(field, value, status):
+    cfg = dgmoe.make_config()
+    setattr(cfg, field, value)
+    st, h = dgmoe.dg_moe_create(cfg, _weights(), 0)
+    assert st == status
+    assert not h.value
+    assert dgmoe.dg_moe_last_error() != ""
+
+
+def test_create_rejects_null_and_misaligned_weights():
+    cfg = dgmoe.make_config()
+    w = _weights()
+    w.w_down = None
+    st, _ = dgmoe.dg_moe_create(cfg, w, 0)
+    assert st == dgmoe.DG_ERR_INVALID_ARG
+    st, _ = dgmoe.dg_moe_create(cfg, _weights(align=8), 0)
+    assert st == dgmoe.DG_ERR_ALIGN
+    cfg4 = dgmoe.make_config(experts=dgmoe.DG_I4G128)
+    st, _ = dgmoe.dg_moe_create(cfg4, _weights(), 0)  # int4 without scales
+    assert st == dgmoe.DG_ERR_INVALID_ARG
+    h = ctypes.c_void_p()
+    assert dgmoe._lib.dg_moe_create(None, ctypes.byref(w), None, ctypes.byref(h)) == dgmoe.DG_ERR_INVALID_ARG
+
+
+def test_forward_and_destroy_with_null_handle():
+    assert dgmoe.dg_moe_forward(None, 16, 32, 4, None, 0, 0) == dgmoe.DG_ERR_INVALID_ARG
+    dbg = dgmoe.dg_moe_debug()
+    assert dgmoe.dg_moe_forward_debug(None, 16, 32, 4, dbg, 0) == dgmoe.DG_ERR_INVALID_ARG
+    assert dgmoe.dg_moe_destroy(None) == dgmoe.DG_OK

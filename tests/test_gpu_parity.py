@@ -1,0 +1,288 @@
+"""GPU parity of the HIP MoE layer against the CPU oracle, through the C ABI (MI355X only).
+
+Every case prints what it runs before touching the GPU, so a failing run names its case.
+"""
+import numpy as np
+import pytest
+import torch
+
+from expert_ffn_canvas_amd import synth
+from tests.conftest import gpu_available
+from tests.parity_util import OUT_TOL, host, layer_parity, oracle_weights, rel_max_err, to_f32
+
+pytestmark = pytest.mark.gpu
+
+if gpu_available():
+    from expert_ffn_canvas_amd import dgmoe
+    import oracle
+
+
+def _say(msg):
+    print(f"[case] {msg}", flush=True)
+
+
+def _layer(w, max_tokens, act, K=8, pack=False):
+    return dgmoe.MoELayer(w, max_tokens=max_tokens, act_dtype=act, top_k=K, pack=pack)
+
+
+def _act(wl):
+    return torch.float32 if wl.act == "f32" else torch.bfloat16
+
+
+@pytest.fixture(scope="module")
+def canvas256():
+    wl = synth.WORKLOADS["canvas256"]
+    inp = synth.make_inputs(wl, device="cuda")
+    w = inp["layers"][0]
+    return wl, inp["x"], w, oracle_weights(w)
+
+
+# ----------------------------------------------------------------------------- small shapes
+
+@pytest.mark.parametrize("E,K,D,F,T,act,rw", [
+    (6, 2, 128, 64, 37, "bf16", "bf16"),
+    (16, 4, 256, 128, 70, "f32", "f32"),
+    (40, 8, 384, 192, 129, "bf16", "f32"),
+])
+def test_small_shapes(E, K, D, F, T, act, rw):
+    _say(f"small E={E} K={K} D={D} F={F} T={T} act={act} router={rw}")
+    wl = synth.small_workload(T=T, E=E, K=K, D=D, F=F, act=act, router_w=rw, bias="zipf", seed=E + T)
+    inp = synth.make_inputs(wl, device="cuda")
+    w = inp["layers"][0]
+    layer = _layer(w, T, _act(wl), K=K)
+    r = layer_parity(layer, inp["x"], oracle_weights(w), K)
+    print(f"err {r['err']:.3e} near-ties {r['near_ties']}")
+
+
+def test_single_expert_closed_form():
+    _say("E=1 k=1 D=256 F=128 T=33")
+    wl = synth.small_workload(T=33, E=1, K=1, D=256, F=128, seed=5)
+    inp = synth.make_inputs(wl, device="cuda")
+    w = inp["layers"][0]
+    layer = _layer(w, 33, torch.bfloat16, K=1)
+    r = layer_parity(layer, inp["x"], oracle_weights(w), 1)
+    assert np.all(r["dbg"]["topk_w"].cpu().numpy() == 1.0)
+
+
+# ----------------------------------------------------------------------------- the five workloads
+
+def test_canvas32_fp32():
+    wl = synth.WORKLOADS["canvas32"]
+    _say(f"{wl.name} T={wl.T}")
+    inp = synth.make_inputs(wl, device="cuda")
+    w = inp["layers"][0]
+    layer = _layer(w, wl.T, torch.float32)
+    r = layer_parity(layer, inp["x"], oracle_weights(w), wl.K)
+    print(f"err {r['err']:.3e} near-ties {r['near_ties']}")
+
+
+def test_canvas256_zipf(canvas256):
+    wl, x, w, wn = canvas256
+    _say(f"{wl.name} T={wl.T}")
+    layer = _layer(w, wl.T, torch.bfloat16)
+    r = layer_parity(layer, x, wn, wl.K)
+    counts = r["dbg"]["counts"].cpu().numpy()
+    print(f"err {r['err']:.3e} near-ties {r['near_ties']} touched {int((counts > 0).sum())} max {counts.max()}")
+    assert (counts > 0).sum() < wl.E  # the skew leaves experts empty
+
+
+def test_encode2304_sampled():
+    wl = synth.WORKLOADS["encode2304"]
+    _say(f"{wl.name} T={wl.T}")
+    inp = synth.make_inputs(wl, device="cuda")
+    w = inp["layers"][0]
+    layer = _layer(w, wl.T, torch.bfloat16)
+    rng = np.random.default_rng(0)
+    tok = np.unique(np.concatenate([[0, 1, wl.T - 1], rng.choice(wl.T, 125, replace=False)]))
+    r = layer_parity(layer, inp["x"], oracle_weights(w), wl.K, tokens=tok)
+    print(f"err {r['err']:.3e} near-ties {r['near_ties']}")
+
+
+def test_int4_g128():
+    wl = synth.WORKLOADS["int4"]
+    _say(f"{wl.name} T={wl.T}")
+    inp = synth.make_inputs(wl, device="cuda")
+    w = inp["layers"][0]
+    layer = _layer(w, wl.T, torch.bfloat16)
+    rng = np.random.default_rng(1)
+    tok = np.unique(np.concatenate([[0, wl.T - 1], rng.choice(wl.T, 100, replace=False)]))
+    r = layer_parity(layer, inp["x"], oracle_weights(w), wl.K, tokens=tok)
+    print(f"err {r['err']:.3e} near-ties {r['near_ties']}")
+
+
+def test_int4_small_tail_group():
+    # d_ff = 192 = 128 + 64: the down projection's last scale group is 64 wide
+    _say("int4 small E=12 K=3 D=256 F=192 T=50")
+    wl = synth.small_workload(T=50, E=12, K=3, D=256, F=192, experts="i4g128", seed=8)
+    inp = synth.make_inputs(wl, device="cuda")
+    w = inp["layers"][0]
+    layer = _layer(w, 50, torch.bfloat16, K=3)
+    layer_parity(layer, inp["x"], oracle_weights(w), 3)
+
+
+# ----------------------------------------------------------------------------- edge cases
+
+@pytest.mark.parametrize("T", [1, 15, 17, 255, 257])
+def test_ragged_token_counts(canvas256, T):
+    wl, x, w, wn = canvas256
+    _say(f"ragged T={T}")
+    gen = torch.Generator(device="cuda").manual_seed(100 + T)
+    xt = torch.randn((T, wl.D), generator=gen, device="cuda").to(torch.bfloat16)
+    layer = _layer(w, 300, torch.bfloat16)
+    layer_parity(layer, xt, wn, wl.K)
+
+
+def test_zero_tokens_is_a_no_op(canvas256):
+    wl, x, w, wn = canvas256
+    _say("T=0")
+    layer = _layer(w, 16, torch.bfloat16)
+    out = torch.full((1, wl.D), 7.0, dtype=torch.bfloat16, device="cuda")
+    st = dgmoe.dg_moe_forward(layer.handle, x.data_ptr(), out.data_ptr(), 0, None, 0,
+                              torch.cuda.current_stream().cuda_stream)
+    assert st == dgmoe.DG_OK
+    torch.cuda.synchronize()
+    assert torch.all(out == 7.0)
+
+
+def test_all_tokens_forced_to_one_expert(canvas256):
+    # bias +30 on one expert: every token picks it first with weight ~1, it receives all T rows
+    # (three tiles), and most experts stay empty.
+    wl, x, w, wn = canvas256
+    T = 300
+    _say(f"forced expert 7, T={T}")
+    w2 = dict(w)
+    b = torch.zeros(wl.E, device="cuda")
+    b[7] = 30.0
+    w2["router_bias"] = b
+    gen = torch.Generator(device="cuda").manual_seed(7)
+    xt = torch.randn((T, wl.D), generator=gen, device="cuda").to(torch.bfloat16)
+    layer = _layer(w2, T, torch.bfloat16, K=1)
+    wn2 = dict(wn)
+    wn2["router_bias"] = host(b)
+    r = layer_parity(layer, xt, wn2, 1)
+    counts = r["dbg"]["counts"].cpu().numpy()
+    assert counts[7] == T and counts.sum() == T
+    # identity: with k = 1 the output is that expert's FFN of the normalised input
+    assert np.all(r["dbg"]["topk_w"].cpu().numpy() == 1.0)
+
+
+def test_identical_experts_any_routing():
+    # all experts share one weight set: the output is the dense FFN whatever the routing
+    _say("identical experts E=16 K=4 D=2816 F=704 T=96")
+    wl = synth.small_workload(T=96, E=16, K=4, D=2816, F=704, bias="zipf", seed=9)
+    inp = synth.make_inputs(wl, device="cuda")
+    w = inp["layers"][0]
+    w["w_gate_up"] = w["w_gate_up"][:1].expand(16, -1, -1).contiguous()
+    w["w_down"] = w["w_down"][:1].expand(16, -1, -1).contiguous()
+    layer = _layer(w, 96, torch.bfloat16, K=4)
+    out = to_f32(layer.forward(inp["x"]))
+    wn = oracle_weights(w)
+    xn = host(inp["x"])
+    # closed form: expert 0 alone, through the oracle's single-expert FFN on the normalised input
+    rt = oracle.route(xn, wn["router_w"], wn["router_gamma"], wn["router_bias"], 4, synth.RMS_EPS)
+    h = (xn.view(np.uint16).astype(np.uint32) << 16).view(np.float32).astype(np.float64) * rt["r"][:, None] \
+        * (1.0 + wn["ffn_gamma"].astype(np.float64))
+    ref = oracle.expert_ffn(wn, 0, h.astype(np.float32))
+    assert rel_max_err(out, ref) <= OUT_TOL
+
+
+def test_determinism(canvas256):
+    wl, x, w, wn = canvas256
+    _say("determinism")
+    layer = _layer(w, wl.T, torch.bfloat16)
+    a = layer.forward(x).clone()
+    b = layer.forward(x).clone()
+    torch.cuda.synchronize()
+    assert torch.equal(a.view(torch.int16), b.view(torch.int16))
+
+
+def test_fold_invariance_bit_exact(canvas256):
+    # moving a power-of-two scale from the expert norm into gate_up's input columns leaves the routing and
+    # (with exact powers of two) every product unchanged
+    wl, x, w, wn = canvas256
+    _say("fold invariance")
+    gen = torch.Generator(device="cuda").manual_seed(3)
+    g = torch.randint(-256, 256, (wl.D,), generator=gen, device="cuda").float() / 1024.0
+    s = torch.tensor([0.5, 1.0, 2.0], device="cuda")[torch.randint(0, 3, (wl.D,), generator=gen, device="cuda")]
+    w1 = dict(w)
+    w1["ffn_gamma"] = g
+    w2 = dict(w)
+    w2["ffn_gamma"] = (1.0 + g) / s - 1.0
+    w2["w_gate_up"] = (w["w_gate_up"].float() * s).to(torch.bfloat16)
+    l1 = _layer(w1, wl.T, torch.bfloat16)
+    l2 = _layer(w2, wl.T, torch.bfloat16)
+    d1 = l1.forward_debug(x)
+    d2 = l2.forward_debug(x)
+    torch.cuda.synchronize()
+    assert torch.equal(d1["topk_idx"], d2["topk_idx"])
+    assert torch.equal(d1["topk_w"], d2["topk_w"])
+    assert torch.equal(d1["out"].view(torch.int16), d2["out"].view(torch.int16))
+
+
+def test_pack_equals_borrow(canvas256):
+    wl, x, w, wn = canvas256
+    _say("pack vs borrow")
+    a = _layer(w, wl.T, torch.bfloat16).forward(x)
+    b = _layer(w, wl.T, torch.bfloat16, pack=True).forward(x)
+    torch.cuda.synchronize()
+    assert torch.equal(a.view(torch.int16), b.view(torch.int16))
+
+
+def test_residual_and_addend(canvas256):
+    wl, x, w, wn = canvas256
+    _say("residual + addend")
+    gen = torch.Generator(device="cuda").manual_seed(11)
+    add = (torch.randn(x.shape, generator=gen, device="cuda") * 0.5).to(torch.bfloat16)
+    layer = _layer(w, wl.T, torch.bfloat16)
+    moe = to_f32(layer.forward(x))
+    full = to_f32(layer.forward(x, addend=add, add_input=True))
+    tok = np.arange(0, wl.T, 4)
+    ref = oracle.moe_forward(wn, host(x), wl.K, synth.RMS_EPS, tokens=tok)["out"]
+    exact = ref + to_f32(x)[tok] + to_f32(add)[tok]
+    # bf16 rounding of the sum can move by one ulp of the sum when the MoE part differs within tolerance
+    ulp = np.abs(exact) * 2.0 ** -7
+    assert np.all(np.abs(full[tok] - exact) <= ulp + OUT_TOL * np.max(np.abs(ref)))
+    assert rel_max_err(moe[tok], ref) <= OUT_TOL
+
+
+def test_error_paths_on_device(canvas256):
+    wl, x, w, wn = canvas256
+    _say("error paths")
+    layer = _layer(w, 64, torch.bfloat16)
+    out = torch.empty((128, wl.D), dtype=torch.bfloat16, device="cuda")
+    sp = torch.cuda.current_stream().cuda_stream
+    assert dgmoe.dg_moe_forward(layer.handle, x.data_ptr(), out.data_ptr(), 65, None, 0, sp) == dgmoe.DG_ERR_SHAPE
+    assert "max_tokens" in dgmoe.dg_moe_last_error()
+    assert dgmoe.dg_moe_forward(layer.handle, x.data_ptr(), x.data_ptr(), 8, None, 0, sp) == dgmoe.DG_ERR_INVALID_ARG
+    assert dgmoe.dg_moe_forward(layer.handle, x.data_ptr(), out.data_ptr(), 8, None, 0x10, sp) == \
+        dgmoe.DG_ERR_INVALID_ARG
+    assert dgmoe.dg_moe_forward(layer.handle, x.data_ptr() + 2, out.data_ptr(), 8, None, 0, sp) == dgmoe.DG_ERR_ALIGN
+
+
+def test_stack30_teacher_forced():
+    # 30 layers with their own weights (45.7 GB of bf16 experts resident), T = 512 (two canvases):
+    # x_{l+1} = bf16(x_l + MoE_l(x_l) + delta_l). Each checked layer is compared on its own GPU input.
+    wl = synth.WORKLOADS["stack30"]
+    _say(f"{wl.name} T={wl.T} layers={wl.layers}")
+    inp = synth.make_inputs(wl, device="cuda")
+    layers = [_layer(w, wl.T, torch.bfloat16) for w in inp["layers"]]
+    xs = [inp["x"]]
+    for l in range(wl.layers):
+        xs.append(layers[l].forward(xs[l], addend=inp["deltas"][l], add_input=True))
+    torch.cuda.synchronize()
+    assert all(torch.isfinite(t.float()).all() for t in xs)
+    rng = np.random.default_rng(4)
+    for l in (0, 13, 29):
+        _say(f"{wl.name} layer {l}")
+        wn = oracle_weights(inp["layers"][l])
+        tok = np.unique(np.concatenate([[0, wl.T - 1], rng.choice(wl.T, 40, replace=False)]))
+        r = layer_parity(layers[l], xs[l], wn, wl.K, tokens=tok)
+        # the residual path of the same layer: bf16(x + MoE + delta) within one bf16 ulp of the sum
+        exact = r["ref"]["out"] + to_f32(xs[l])[tok] + to_f32(inp["deltas"][l])[tok]
+        got = to_f32(xs[l + 1])[tok]
+        ulp = np.abs(exact) * 2.0 ** -7
+        assert np.all(np.abs(got - exact) <= ulp + OUT_TOL * np.max(np.abs(r["ref"]["out"])))
+        print(f"layer {l}: err {r['err']:.3e} near-ties {r['near_ties']} "
+              f"touched {(r['dbg']['counts'].cpu().numpy() > 0).sum()}")
+    for layer in layers:
+        layer.close()
