@@ -13,14 +13,19 @@ namespace {
 
 constexpr int kThreads = 256;
 
+constexpr int kCols = kThreads * 4;  // columns per workgroup
+
+// Workgroup (t, chunk): token t, columns chunk * 1024 .. + 1023.
 template <bool OUT_F32>
 __global__ __launch_bounds__(kThreads) void k_combine(CombineArgs a) {
-  const int t = blockIdx.x;
   const int K = a.K, D = a.D;
+  const int n_chunk = (D + kCols - 1) / kCols;
+  const int t = blockIdx.x / n_chunk;
+  const int c = (blockIdx.x - t * n_chunk) * kCols + threadIdx.x * 4;
   int rows[8];
 #pragma unroll
   for (int j = 0; j < 8; ++j) rows[j] = (j < K) ? a.row_of_slot[(size_t)t * K + j] : 0;
-  for (int c = threadIdx.x * 4; c < D; c += kThreads * 4) {
+  if (c < D) {
     float4 s = *reinterpret_cast<const float4*>(a.y + (size_t)rows[0] * D + c);
 #pragma unroll
     for (int j = 1; j < 8; ++j) {
@@ -55,10 +60,11 @@ __global__ __launch_bounds__(kThreads) void k_combine(CombineArgs a) {
 }  // namespace
 
 hipError_t launch_combine(const CombineArgs& a, hipStream_t stream) {
+  const dim3 grid(a.T * ((a.D + kCols - 1) / kCols));
   if (a.act_f32)
-    k_combine<true><<<dim3(a.T), dim3(kThreads), 0, stream>>>(a);
+    k_combine<true><<<grid, dim3(kThreads), 0, stream>>>(a);
   else
-    k_combine<false><<<dim3(a.T), dim3(kThreads), 0, stream>>>(a);
+    k_combine<false><<<grid, dim3(kThreads), 0, stream>>>(a);
   return hipGetLastError();
 }
 

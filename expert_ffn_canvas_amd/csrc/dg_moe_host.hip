@@ -2,7 +2,7 @@
 // workspace allocated once at create time, router-weight preparation, and the
 // asynchronous launch sequence of one forward:
 //
-//   router (norm, logits, top-k, weights, expert input)
+//   router (norm + expert input, logits, top-k + weights)
 //   -> permutation (counts, offsets, tile list, stable scatter)
 //   -> gate_up grouped GEMM (+ GELU-tanh gating)
 //   -> down grouped GEMM (x routing weight)
@@ -49,19 +49,19 @@ size_t act_elem_bytes(int dt) { return dt == DG_F32 ? 4 : 2; }
 
 // Sub-buffer layout of the workspace (byte offsets from the base).
 struct Layout {
-  size_t h, topk_idx, topk_w, counts, offsets, tiles, n_tiles, sorted_token, row_w, row_of_slot, act, y;
+  size_t h, z, logits, topk_idx, topk_w, counts, offsets, tiles, qlen, sorted_token, row_w, row_of_slot, act, y;
   size_t wr, gamma_r, bias, gamma_e;
   size_t total;
-  int Epad, n_wplanes, max_tiles;
+  int Epad, n_wplanes, qmax;
 };
 
 Layout plan(const dg_moe_config& c) {
   Layout L{};
   const size_t T = (size_t)c.max_tokens, D = (size_t)c.d_model, F = (size_t)c.d_ff;
   const size_t E = (size_t)c.n_experts, K = (size_t)c.top_k;
-  L.Epad = (int)round_up(E, 16);
+  L.Epad = (int)round_up(E, 32);
   L.n_wplanes = (c.router_w_dtype == DG_F32) ? 3 : 1;
-  L.max_tiles = (int)(K * T / dg::kTileRows + E);
+  L.qmax = dg::max_queue_len((int)T, (int)K, (int)E);
   size_t off = 0;
   auto take = [&](size_t bytes) {
     const size_t at = off;
@@ -69,12 +69,14 @@ Layout plan(const dg_moe_config& c) {
     return at;
   };
   L.h = take(T * D * 2);
+  L.z = take(3 * T * D * 2);
+  L.logits = take(T * (size_t)L.Epad * 4);
   L.topk_idx = take(T * K * 4);
   L.topk_w = take(T * K * 4);
   L.counts = take(E * 4);
   L.offsets = take((E + 1) * 4);
-  L.tiles = take((size_t)L.max_tiles * sizeof(dg::Tile));
-  L.n_tiles = take(4);
+  L.tiles = take((size_t)L.qmax * dg::kQueues * sizeof(dg::Tile));
+  L.qlen = take(dg::kQueues * 4);
   L.sorted_token = take(K * T * 4);
   L.row_w = take(K * T * 4);
   L.row_of_slot = take(K * T * 4);
@@ -319,6 +321,8 @@ static dg_status run_forward(dg_moe_handle hd, const void* x, void* out, int32_t
   ra.eps = c.rms_eps;
   ra.h_f16 = i4 ? 1 : 0;
   ra.h = hd->at<uint16_t>(L.h);
+  ra.z = hd->at<uint16_t>(L.z);
+  ra.logits = hd->at<float>(L.logits);
   ra.topk_idx = hd->at<int32_t>(L.topk_idx);
   ra.topk_w = hd->at<float>(L.topk_w);
   hipError_t e = dg::launch_router(ra, stream);
@@ -331,11 +335,11 @@ static dg_status run_forward(dg_moe_handle hd, const void* x, void* out, int32_t
   pa.T = T;
   pa.K = c.top_k;
   pa.E = c.n_experts;
-  pa.BM = dg::kTileRows;
+  pa.qmax = dg::max_queue_len(T, c.top_k, c.n_experts);
   pa.counts = hd->at<int32_t>(L.counts);
   pa.offsets = hd->at<int32_t>(L.offsets);
   pa.tiles = hd->at<dg::Tile>(L.tiles);
-  pa.n_tiles = hd->at<int32_t>(L.n_tiles);
+  pa.qlen = hd->at<int32_t>(L.qlen);
   pa.sorted_token = hd->at<int32_t>(L.sorted_token);
   pa.row_w = hd->at<float>(L.row_w);
   pa.row_of_slot = hd->at<int32_t>(L.row_of_slot);
@@ -345,8 +349,8 @@ static dg_status run_forward(dg_moe_handle hd, const void* x, void* out, int32_t
 
   dg::GemmArgs ga{};
   ga.tiles = pa.tiles;
-  ga.n_tiles = pa.n_tiles;
-  ga.max_tiles = (int)((size_t)c.top_k * T / dg::kTileRows + c.n_experts);
+  ga.qlen = pa.qlen;
+  ga.qmax = pa.qmax;
   ga.sorted_token = pa.sorted_token;
   ga.row_w = pa.row_w;
   ga.h = ra.h;

@@ -1,8 +1,9 @@
 // Grouped expert GEMMs on gfx950 bf16 matrix cores (fp32 accumulation).
 //
-//  gate_up: for each tile (expert e, rows row0 .. row0+mc-1) and each block of
-//           64 d_ff features: g = h W_gate[e]^T, u = h W_up[e]^T over the full
-//           d_model, then act = gelu_tanh(g) * u (bf16).
+//  gate_up: for each tile (expert e, rows row0 .. row0+mc-1, mc <= 64) and
+//           each block of 64 d_ff features: g = h W_gate[e]^T and
+//           u = h W_up[e]^T over the full d_model, then act = gelu_tanh(g) * u
+//           (bf16).
 //  down:    for each tile and each block of 128 d_model outputs:
 //           y = row_w * (act W_down[e]^T) in fp32, one row per routed slot.
 //
@@ -14,12 +15,19 @@
 // names the fused 3D gate_up projection; the row order is this library's).
 //
 // Mapping: one workgroup = 4 waves = one (tile, column block). Each wave owns
-// 16 output columns of each operand it needs (gate+up, or two down tiles)
-// for every row of the tile, so every weight byte is read from HBM by exactly
-// one wave and goes straight from global memory into MFMA operand registers.
-// The tile's activation rows are shared by the 4 waves through LDS
-// (double-buffered along K). Weights for the next K step are loaded while the
-// current step's MFMAs run.
+// two 16-row weight panels (gate+up, or two down panels) for every row of the
+// tile, so every weight byte is read by exactly one wave and goes straight
+// from global memory into MFMA operand registers; the next K step of
+// the panels is in flight while the current one is multiplied (256-wide K steps). The tile's
+// activation rows are staged once per K step into LDS (double-buffered) and
+// shared by the four waves. The main loop is specialised on the number of
+// 16-row MFMA tiles the tile needs (1..4) and is branch-free inside (rows past
+// the tile re-read its last row), so the next step's loads stay in flight
+// across the current step's MFMAs.
+//
+// Work distribution: workgroup b takes queue b % 8 (its XCD) and, within it,
+// entry (b / 8) / NB and column block (b / 8) % NB; the permutation kernel
+// balanced the queues and put all tiles of one expert into one queue.
 #include "dg_common.h"
 #include "launch.h"
 
@@ -28,132 +36,220 @@ namespace dg {
 namespace {
 
 constexpr int kThreads = 256;
-constexpr int kKStep = 64;               // K per pipeline step
-constexpr int kPitch = kKStep + 8;       // LDS row pitch in 16-bit elements (144 B)
-constexpr int kBMT = kTileRows / 16;     // m-tiles per tile
-constexpr int kAPass = kTileRows / 32;   // 256 threads stage 32 rows x 64 K per pass
+constexpr int kKS = 128;                  // K per pipeline step (four MFMA K steps of 32)
+constexpr int kNS = kKS / 32;
+constexpr int kSegs = kKS / 8;            // 16-byte segments per staged row
+constexpr int kRowBytes = kKS * 2;
+constexpr int kDmaRows = 1024 / kRowBytes;  // rows one wave-wide 16-byte-per-lane transfer fills
+constexpr int kStageBytes = kTileRows * kRowBytes;
+constexpr int kBMT = kTileRows / 16;      // m-tiles per tile
+constexpr int kDmaInstr = kTileRows / (4 * kDmaRows);  // transfers per wave for a full tile
 
-// Stage rows [0, mc) of a tile's K step into LDS. Thread (row r = tid/8 + 32 p,
-// 16-byte segment tid % 8). `src[p]` is null for rows past mc.
-__device__ __forceinline__ void load_a(const uint16_t* const (&src)[kAPass], int k0, u32x4 (&ra)[kAPass]) {
-#pragma unroll
-  for (int p = 0; p < kAPass; ++p)
-    if (src[p]) ra[p] = *reinterpret_cast<const u32x4*>(src[p] + k0);
+struct Panels {
+  u32x4 b0[kNS], b1[kNS];
+};
+
+// vmcnt(n) with the other counters left alone (gfx9 encoding: vmcnt in bits
+// 3:0 and 15:14, expcnt 6:4, lgkmcnt 11:8).
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
 }
 
-__device__ __forceinline__ void store_a(uint16_t* lds, const uint16_t* const (&src)[kAPass], int tid,
-                                        const u32x4 (&ra)[kAPass]) {
+// Weight panels of one K step: NS sub-steps of 32.
+template <int NS>
+__device__ __forceinline__ void load_w(const uint16_t* w0, const uint16_t* w1, int k0, Panels& p) {
 #pragma unroll
-  for (int p = 0; p < kAPass; ++p)
-    if (src[p]) *reinterpret_cast<u32x4*>(lds + ((tid >> 3) + 32 * p) * kPitch + (tid & 7) * 8) = ra[p];
+  for (int s = 0; s < NS; ++s) {
+    p.b0[s] = *reinterpret_cast<const u32x4*>(w0 + k0 + 32 * s);
+    p.b1[s] = *reinterpret_cast<const u32x4*>(w1 + k0 + 32 * s);
+  }
 }
 
-__global__ __launch_bounds__(kThreads) void k_gate_up_bf16(GemmArgs a) {
-  __shared__ __attribute__((aligned(16))) uint16_t As[2][kTileRows * kPitch];
+// LDS byte address of a shared-memory pointer (the address-space cast to
+// the local address space; its value is the offset inside the workgroup's LDS).
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+  return static_cast<uint32_t>(reinterpret_cast<uintptr_t>((const __attribute__((address_space(3))) char*)p));
+}
+
+// One 16-byte-per-lane global -> LDS transfer (global_load_lds_dwordx4): lane l
+// writes LDS bytes lds_base + 16 l .. + 15. Issued from inline assembly so the
+// compiler does not treat every later LDS read as depending on it; completion
+// is awaited explicitly (vmcnt) before the workgroup barrier that publishes it.
+// No register is written, so nothing is left in flight in a register.
+// M0 is saved and restored around the transfer, so nothing the compiler keeps
+// in M0 is disturbed.
+__device__ __forceinline__ void lds_dma16(uint32_t lds_base, const void* gaddr) {
+  uint32_t saved;
+  asm volatile(
+      "s_mov_b32 %0, m0\n\t"
+      "s_mov_b32 m0, %1\n\t"
+      "s_nop 0\n\t"
+      "global_load_lds_dwordx4 %2, off\n\t"
+      "s_mov_b32 m0, %0"
+      : "=&s"(saved)
+      : "s"(lds_base), "v"(gaddr)
+      : "memory");
+}
+
+// Activation rows of one K step straight into LDS: instruction i of wave w
+// fills the kDmaRows rows starting at kDmaRows (w + 4 i); lane l lands in row
+// slot l / kSegs, 16-byte position l % kSegs and carries logical segment
+// position ^ (row % kSegs), an XOR swizzle that makes the MFMA reads
+// bank-conflict free. Segments past a short last step re-read a valid one.
+template <int NMT, int NSEG>
+__device__ __forceinline__ void dma_a(char* stage, const uint16_t* const (&rowp)[kDmaInstr], int k0, int wave,
+                                      int lane) {
+  const uint32_t base = __builtin_amdgcn_readfirstlane(lds_addr(stage) + wave * kDmaRows * kRowBytes);
+#pragma unroll
+  for (int i = 0; i < 16 * NMT / (4 * kDmaRows); ++i) {
+    const int r = kDmaRows * (wave + 4 * i) + lane / kSegs;
+    int sg = (lane % kSegs) ^ (r % kSegs);
+    if (NSEG < kSegs) sg = sg % NSEG;
+    lds_dma16(base + i * 4 * kDmaRows * kRowBytes, rowp[i] + k0 + sg * 8);
+  }
+}
+
+template <int NMT, int NS>
+__device__ __forceinline__ void mma_step(const char* stage, int lane, const Panels& p, f32x4 (&acc0)[kBMT],
+                                         f32x4 (&acc1)[kBMT]) {
+  const int g = lane >> 4, m = lane & 15;
+#pragma unroll
+  for (int s = 0; s < NS; ++s) {
+    const bf16x8 bb0 = as_bf16x8(p.b0[s]);
+    const bf16x8 bb1 = as_bf16x8(p.b1[s]);
+#pragma unroll
+    for (int mt = 0; mt < NMT; ++mt) {
+      const int r = mt * 16 + m;
+      const int pos = (s * 4 + g) ^ (r % kSegs);
+      const bf16x8 av = as_bf16x8(*reinterpret_cast<const u32x4*>(stage + r * kRowBytes + pos * 16));
+      acc0[mt] = mfma_bf16(av, bb0, acc0[mt]);
+      acc1[mt] = mfma_bf16(av, bb1, acc1[mt]);
+    }
+    // keep at most two sub-steps of activation fragments live at a time
+    if (s & 1) __builtin_amdgcn_sched_barrier(0);
+  }
+}
+
+// Workgroup barrier that does not wait for this wave's outstanding global
+// loads: the LDS-DMA writes the other waves are about to read are covered by
+// the explicit vmcnt wait before it. The empty asm statements stop the
+// compiler from moving memory operations across the barrier.
+__device__ __forceinline__ void lds_barrier() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
+// One step with NS sub-steps, issued after the previous one: DMA of the
+// activation rows into stage (it + 1) & 1, then the weight panels into `nxt`,
+// then the MFMAs of step `it` (NSP sub-steps) from `cur`.
+template <int NMT, int NS, int NSP>
+__device__ __forceinline__ void step(char* As, const uint16_t* const (&rowp)[kDmaInstr], const uint16_t* w0,
+                                     const uint16_t* w1, int k1, int it, int wave, int lane, const Panels& cur,
+                                     Panels& nxt, f32x4 (&acc0)[kBMT], f32x4 (&acc1)[kBMT]) {
+  dma_a<NMT, NS * 4>(As + ((it + 1) & 1) * kStageBytes, rowp, k1, wave, lane);
+  __builtin_amdgcn_sched_barrier(0);
+  load_w<NS>(w0, w1, k1, nxt);
+  __builtin_amdgcn_sched_barrier(0);
+  mma_step<NMT, NSP>(As + (it & 1) * kStageBytes, lane, cur, acc0, acc1);
+  wait_vmcnt<2 * NS>();  // this wave's DMA has landed; its weight loads may still fly
+  lds_barrier();
+}
+
+// The last full step `last` (panels in `cur`) and the short tail, if any.
+template <int NMT>
+__device__ __forceinline__ void finish(char* As, const uint16_t* const (&rowp)[kDmaInstr], const uint16_t* w0,
+                                       const uint16_t* w1, int nfull, int ntail, int wave, int lane,
+                                       const Panels& cur, Panels& nxt, f32x4 (&acc0)[kBMT], f32x4 (&acc1)[kBMT]) {
+  const int last = nfull - 1;
+  const int k1 = nfull * kKS;
+  char* tail_stage = As + (nfull & 1) * kStageBytes;
+  if (ntail == 0) {
+    mma_step<NMT, kNS>(As + (last & 1) * kStageBytes, lane, cur, acc0, acc1);
+  } else {  // one 64-wide step remains (K % 128 == 64)
+    step<NMT, 2, kNS>(As, rowp, w0, w1, k1, last, wave, lane, cur, nxt, acc0, acc1);
+    wait_vmcnt<0>();
+    mma_step<NMT, 2>(tail_stage, lane, nxt, acc0, acc1);
+  }
+}
+
+// The K loop of one tile with NMT 16-row MFMA tiles. K is a multiple of 64.
+// Two panel buffers alternate roles (the loop is unrolled by two) so that no
+// register copies are needed between steps.
+template <int NMT>
+__device__ __forceinline__ void k_loop(char* As, const uint16_t* const (&rowp)[kDmaInstr], const uint16_t* w0,
+                                       const uint16_t* w1, int K, int tid, f32x4 (&acc0)[kBMT],
+                                       f32x4 (&acc1)[kBMT]) {
+  const int lane = tid & 63, wave = tid >> 6;
+  const int nfull = K / kKS;
+  const int ntail = (K - nfull * kKS) / 32;  // 0, or 2 for a last 64-wide step (K is a multiple of 64)
+  Panels p0, p1;
+  if (nfull == 0) {
+    // K = 64: one short step only
+    dma_a<NMT, 8>(As, rowp, 0, wave, lane);
+    load_w<2>(w0, w1, 0, p0);
+    wait_vmcnt<0>();
+    lds_barrier();
+    mma_step<NMT, 2>(As, lane, p0, acc0, acc1);
+    return;
+  }
+  dma_a<NMT, kSegs>(As, rowp, 0, wave, lane);
+  __builtin_amdgcn_sched_barrier(0);
+  load_w<kNS>(w0, w1, 0, p0);
+  wait_vmcnt<2 * kNS>();
+  lds_barrier();
+  int it = 0;
+  for (; it + 2 < nfull; it += 2) {
+    step<NMT, kNS, kNS>(As, rowp, w0, w1, (it + 1) * kKS, it, wave, lane, p0, p1, acc0, acc1);
+    step<NMT, kNS, kNS>(As, rowp, w0, w1, (it + 2) * kKS, it + 1, wave, lane, p1, p0, acc0, acc1);
+  }
+  if (it + 2 == nfull) {
+    step<NMT, kNS, kNS>(As, rowp, w0, w1, (it + 1) * kKS, it, wave, lane, p0, p1, acc0, acc1);
+    finish<NMT>(As, rowp, w0, w1, nfull, ntail, wave, lane, p1, p0, acc0, acc1);
+  } else {
+    finish<NMT>(As, rowp, w0, w1, nfull, ntail, wave, lane, p0, p1, acc0, acc1);
+  }
+}
+
+// Three workgroups per CU (waves_per_eu 3): the register budget that keeps
+// two K steps of weight panels per wave in flight without spilling.
+template <bool GATE_UP>
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3, 3))) void k_gemm_bf16(GemmArgs a) {
+  __shared__ __attribute__((aligned(16))) char As[2 * kStageBytes];
   const int F = a.F, D = a.D;
-  const int NB = F / 64;
-  const int ti = blockIdx.x / NB;
-  const int fb = blockIdx.x - ti * NB;
-  if (ti >= *a.n_tiles) return;
-  const Tile tl = a.tiles[ti];
+  const int NB = GATE_UP ? F / 64 : D / 128;
+  const int K = GATE_UP ? D : F;
+  const int qx = blockIdx.x & (kQueues - 1);
+  const int j = blockIdx.x / kQueues;
+  const int q = j / NB;
+  const int nb = j - q * NB;
+  if (q >= a.qlen[qx]) return;
+  const Tile tl = a.tiles[(size_t)q * kQueues + qx];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int g = lane >> 4;
   const int nmt = (tl.mc + 15) >> 4;
 
-  const uint16_t* src[kAPass];
+  // source row of each DMA instruction of this lane (rows past the tile re-read
+  // its last row; their results are never stored)
+  const uint16_t* rowp[kDmaInstr];
 #pragma unroll
-  for (int p = 0; p < kAPass; ++p) {
-    const int r = (tid >> 3) + 32 * p;
-    src[p] = (r < tl.mc) ? a.h + (size_t)a.sorted_token[tl.row0 + r] * D + (tid & 7) * 8 : nullptr;
+  for (int i = 0; i < kDmaInstr; ++i) {
+    const int r = min(kDmaRows * (wave + 4 * i) + lane / kSegs, tl.mc - 1);
+    rowp[i] = GATE_UP ? a.h + (size_t)a.sorted_token[tl.row0 + r] * D : a.act + (size_t)(tl.row0 + r) * F;
   }
-  const int f = fb * 64 + wave * 16 + (lane & 15);
-  const uint16_t* wg = static_cast<const uint16_t*>(a.w_gate_up) + ((size_t)tl.e * 2 * F + f) * D + (lane >> 4) * 8;
-  const uint16_t* wu = wg + (size_t)F * D;
-
-  f32x4 accg[kBMT], accu[kBMT];
-#pragma unroll
-  for (int i = 0; i < kBMT; ++i) {
-    accg[i] = f32x4{0.f, 0.f, 0.f, 0.f};
-    accu[i] = f32x4{0.f, 0.f, 0.f, 0.f};
+  int col;  // gate_up: feature f; down: first output d
+  const uint16_t* w0;
+  const uint16_t* w1;
+  if (GATE_UP) {
+    col = nb * 64 + wave * 16 + (lane & 15);
+    w0 = static_cast<const uint16_t*>(a.w_gate_up) + ((size_t)tl.e * 2 * F + col) * D + g * 8;
+    w1 = w0 + (size_t)F * D;
+  } else {
+    col = nb * 128 + wave * 32 + (lane & 15);
+    w0 = static_cast<const uint16_t*>(a.w_down) + ((size_t)tl.e * D + col) * F + g * 8;
+    w1 = w0 + (size_t)16 * F;
   }
-
-  u32x4 ra[kAPass];
-  u32x4 wgc[2], wuc[2], wgn[2], wun[2];
-  load_a(src, 0, ra);
-  wgc[0] = *reinterpret_cast<const u32x4*>(wg);
-  wgc[1] = *reinterpret_cast<const u32x4*>(wg + 32);
-  wuc[0] = *reinterpret_cast<const u32x4*>(wu);
-  wuc[1] = *reinterpret_cast<const u32x4*>(wu + 32);
-  store_a(As[0], src, tid, ra);
-  __syncthreads();
-
-  const int nk = D / kKStep;
-  for (int it = 0; it < nk; ++it) {
-    const int cur = it & 1;
-    const bool more = it + 1 < nk;
-    if (more) {
-      const int k1 = (it + 1) * kKStep;
-      load_a(src, k1, ra);
-      wgn[0] = *reinterpret_cast<const u32x4*>(wg + k1);
-      wgn[1] = *reinterpret_cast<const u32x4*>(wg + k1 + 32);
-      wun[0] = *reinterpret_cast<const u32x4*>(wu + k1);
-      wun[1] = *reinterpret_cast<const u32x4*>(wu + k1 + 32);
-    }
-    const uint16_t* Ab = As[cur];
-#pragma unroll
-    for (int ks = 0; ks < 2; ++ks) {
-      const bf16x8 bg = as_bf16x8(wgc[ks]);
-      const bf16x8 bu = as_bf16x8(wuc[ks]);
-#pragma unroll
-      for (int mt = 0; mt < kBMT; ++mt) {
-        if (mt < nmt) {
-          const bf16x8 av = as_bf16x8(
-              *reinterpret_cast<const u32x4*>(Ab + (mt * 16 + (lane & 15)) * kPitch + ks * 32 + (lane >> 4) * 8));
-          accg[mt] = mfma_bf16(av, bg, accg[mt]);
-          accu[mt] = mfma_bf16(av, bu, accu[mt]);
-        }
-      }
-    }
-    if (more) {
-      store_a(As[cur ^ 1], src, tid, ra);
-      wgc[0] = wgn[0]; wgc[1] = wgn[1];
-      wuc[0] = wun[0]; wuc[1] = wun[1];
-    }
-    __syncthreads();
-  }
-
-  uint16_t* out = a.act + (size_t)tl.row0 * F + f;
-#pragma unroll
-  for (int mt = 0; mt < kBMT; ++mt) {
-    if (mt < nmt) {
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int r = mt * 16 + (lane >> 4) * 4 + i;
-        if (r < tl.mc) out[(size_t)r * F] = f32_to_bf16_bits(gelu_tanh(accg[mt][i]) * accu[mt][i]);
-      }
-    }
-  }
-}
-
-__global__ __launch_bounds__(kThreads) void k_down_bf16(GemmArgs a) {
-  __shared__ __attribute__((aligned(16))) uint16_t As[2][kTileRows * kPitch];
-  const int F = a.F, D = a.D;
-  const int NB = D / 128;
-  const int ti = blockIdx.x / NB;
-  const int nb = blockIdx.x - ti * NB;
-  if (ti >= *a.n_tiles) return;
-  const Tile tl = a.tiles[ti];
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int nmt = (tl.mc + 15) >> 4;
-
-  const uint16_t* src[kAPass];
-#pragma unroll
-  for (int p = 0; p < kAPass; ++p) {
-    const int r = (tid >> 3) + 32 * p;
-    src[p] = (r < tl.mc) ? a.act + (size_t)(tl.row0 + r) * F + (tid & 7) * 8 : nullptr;
-  }
-  const int d0 = nb * 128 + wave * 32 + (lane & 15);
-  const uint16_t* w0 = static_cast<const uint16_t*>(a.w_down) + ((size_t)tl.e * D + d0) * F + (lane >> 4) * 8;
-  const uint16_t* w1 = w0 + (size_t)16 * F;
 
   f32x4 acc0[kBMT], acc1[kBMT];
 #pragma unroll
@@ -161,50 +257,11 @@ __global__ __launch_bounds__(kThreads) void k_down_bf16(GemmArgs a) {
     acc0[i] = f32x4{0.f, 0.f, 0.f, 0.f};
     acc1[i] = f32x4{0.f, 0.f, 0.f, 0.f};
   }
-
-  u32x4 ra[kAPass];
-  u32x4 b0c[2], b1c[2], b0n[2], b1n[2];
-  load_a(src, 0, ra);
-  b0c[0] = *reinterpret_cast<const u32x4*>(w0);
-  b0c[1] = *reinterpret_cast<const u32x4*>(w0 + 32);
-  b1c[0] = *reinterpret_cast<const u32x4*>(w1);
-  b1c[1] = *reinterpret_cast<const u32x4*>(w1 + 32);
-  store_a(As[0], src, tid, ra);
-  __syncthreads();
-
-  const int nk = F / kKStep;
-  for (int it = 0; it < nk; ++it) {
-    const int cur = it & 1;
-    const bool more = it + 1 < nk;
-    if (more) {
-      const int k1 = (it + 1) * kKStep;
-      load_a(src, k1, ra);
-      b0n[0] = *reinterpret_cast<const u32x4*>(w0 + k1);
-      b0n[1] = *reinterpret_cast<const u32x4*>(w0 + k1 + 32);
-      b1n[0] = *reinterpret_cast<const u32x4*>(w1 + k1);
-      b1n[1] = *reinterpret_cast<const u32x4*>(w1 + k1 + 32);
-    }
-    const uint16_t* Ab = As[cur];
-#pragma unroll
-    for (int ks = 0; ks < 2; ++ks) {
-      const bf16x8 bb0 = as_bf16x8(b0c[ks]);
-      const bf16x8 bb1 = as_bf16x8(b1c[ks]);
-#pragma unroll
-      for (int mt = 0; mt < kBMT; ++mt) {
-        if (mt < nmt) {
-          const bf16x8 av = as_bf16x8(
-              *reinterpret_cast<const u32x4*>(Ab + (mt * 16 + (lane & 15)) * kPitch + ks * 32 + (lane >> 4) * 8));
-          acc0[mt] = mfma_bf16(av, bb0, acc0[mt]);
-          acc1[mt] = mfma_bf16(av, bb1, acc1[mt]);
-        }
-      }
-    }
-    if (more) {
-      store_a(As[cur ^ 1], src, tid, ra);
-      b0c[0] = b0n[0]; b0c[1] = b0n[1];
-      b1c[0] = b1n[0]; b1c[1] = b1n[1];
-    }
-    __syncthreads();
+  switch (nmt) {
+    case 1: k_loop<1>(As, rowp, w0, w1, K, tid, acc0, acc1); break;
+    case 2: k_loop<2>(As, rowp, w0, w1, K, tid, acc0, acc1); break;
+    case 3: k_loop<3>(As, rowp, w0, w1, K, tid, acc0, acc1); break;
+    default: k_loop<4>(As, rowp, w0, w1, K, tid, acc0, acc1); break;
   }
 
 #pragma unroll
@@ -212,12 +269,16 @@ __global__ __launch_bounds__(kThreads) void k_down_bf16(GemmArgs a) {
     if (mt < nmt) {
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        const int r = mt * 16 + (lane >> 4) * 4 + i;
+        const int r = mt * 16 + g * 4 + i;
         if (r < tl.mc) {
-          const float w = a.row_w[tl.row0 + r];
-          float* yr = a.y + (size_t)(tl.row0 + r) * D + d0;
-          yr[0] = w * acc0[mt][i];
-          yr[16] = w * acc1[mt][i];
+          if (GATE_UP) {
+            a.act[(size_t)(tl.row0 + r) * F + col] = f32_to_bf16_bits(gelu_tanh(acc0[mt][i]) * acc1[mt][i]);
+          } else {
+            const float w = a.row_w[tl.row0 + r];
+            float* yr = a.y + (size_t)(tl.row0 + r) * D + col;
+            yr[0] = w * acc0[mt][i];
+            yr[16] = w * acc1[mt][i];
+          }
         }
       }
     }
@@ -227,12 +288,12 @@ __global__ __launch_bounds__(kThreads) void k_down_bf16(GemmArgs a) {
 }  // namespace
 
 hipError_t launch_gate_up_bf16(const GemmArgs& a, hipStream_t stream) {
-  k_gate_up_bf16<<<dim3(a.max_tiles * (a.F / 64)), dim3(kThreads), 0, stream>>>(a);
+  k_gemm_bf16<true><<<dim3(kQueues * a.qmax * (a.F / 64)), dim3(kThreads), 0, stream>>>(a);
   return hipGetLastError();
 }
 
 hipError_t launch_down_bf16(const GemmArgs& a, hipStream_t stream) {
-  k_down_bf16<<<dim3(a.max_tiles * (a.D / 128)), dim3(kThreads), 0, stream>>>(a);
+  k_gemm_bf16<false><<<dim3(kQueues * a.qmax * (a.D / 128)), dim3(kThreads), 0, stream>>>(a);
   return hipGetLastError();
 }
 

@@ -14,6 +14,9 @@
 // activations (products exact in fp32); each group's partial sum is then
 // multiplied by its scale in fp32. So every weight enters as exactly (q - 8) s.
 //
+// Work distribution as in the bf16 kernels: workgroup b takes queue b % 8 (its
+// XCD), entry (b / 8) / NB and column block (b / 8) % NB.
+//
 // Lane layout: lane (n = l % 16, g = l / 16) loads 16 bytes = 32 codes of
 // row n covering inputs 32 g .. 32 g + 31 of a 128-input group; dword s of that
 // load feeds MFMA step s. Unpacking a dword with the mask 0x000F000F pairs
@@ -82,10 +85,12 @@ __global__ __launch_bounds__(kThreads) void k_gate_up_i4(GemmArgs a) {
   __shared__ __attribute__((aligned(16))) uint16_t As[2][kTileRows * kPitch];
   const int F = a.F, D = a.D;
   const int NB = F / 64;
-  const int ti = blockIdx.x / NB;
-  const int fb = blockIdx.x - ti * NB;
-  if (ti >= *a.n_tiles) return;
-  const Tile tl = a.tiles[ti];
+  const int qx = blockIdx.x & (kQueues - 1);
+  const int jq = blockIdx.x / kQueues;
+  const int q = jq / NB;
+  const int fb = jq - q * NB;
+  if (q >= a.qlen[qx]) return;
+  const Tile tl = a.tiles[(size_t)q * kQueues + qx];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int nmt = (tl.mc + 15) >> 4;
   const int seg = tid & 15;
@@ -185,10 +190,12 @@ __global__ __launch_bounds__(kThreads) void k_down_i4(GemmArgs a) {
   __shared__ __attribute__((aligned(16))) uint16_t As[2][kTileRows * kPitch];
   const int F = a.F, D = a.D;
   const int NB = D / 128;
-  const int ti = blockIdx.x / NB;
-  const int nb = blockIdx.x - ti * NB;
-  if (ti >= *a.n_tiles) return;
-  const Tile tl = a.tiles[ti];
+  const int qx = blockIdx.x & (kQueues - 1);
+  const int jq = blockIdx.x / kQueues;
+  const int q = jq / NB;
+  const int nb = jq - q * NB;
+  if (q >= a.qlen[qx]) return;
+  const Tile tl = a.tiles[(size_t)q * kQueues + qx];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int nmt = (tl.mc + 15) >> 4;
   const int seg = tid & 15;
@@ -294,12 +301,12 @@ __global__ __launch_bounds__(kThreads) void k_down_i4(GemmArgs a) {
 }  // namespace
 
 hipError_t launch_gate_up_i4(const GemmArgs& a, hipStream_t stream) {
-  k_gate_up_i4<<<dim3(a.max_tiles * (a.F / 64)), dim3(kThreads), 0, stream>>>(a);
+  k_gate_up_i4<<<dim3(kQueues * a.qmax * (a.F / 64)), dim3(kThreads), 0, stream>>>(a);
   return hipGetLastError();
 }
 
 hipError_t launch_down_i4(const GemmArgs& a, hipStream_t stream) {
-  k_down_i4<<<dim3(a.max_tiles * (a.D / 128)), dim3(kThreads), 0, stream>>>(a);
+  k_down_i4<<<dim3(kQueues * a.qmax * (a.D / 128)), dim3(kThreads), 0, stream>>>(a);
   return hipGetLastError();
 }
 

@@ -9,6 +9,18 @@ namespace dg {
 
 struct Tile;
 
+// Largest number of rows one tile holds (four 16-row MFMA tiles).
+constexpr int kTileRows = 64;
+// Tiles are spread over this many queues, one per XCD: queue x holds the
+// tiles that workgroups with blockIdx % kQueues == x process.
+constexpr int kQueues = 8;
+
+// Upper bound on the length of one tile queue for T tokens.
+inline int max_queue_len(int T, int K, int E) {
+  const int max_tiles = (K * T + kTileRows - 1) / kTileRows + E;
+  return (max_tiles + kQueues - 1) / kQueues + (T + kTileRows - 1) / kTileRows;
+}
+
 struct RouterArgs {
   const void* x;        // [T, D] fp32 or bf16
   int x_f32;
@@ -21,6 +33,8 @@ struct RouterArgs {
   float eps;
   int h_f16;            // expert input stored as fp16 (int4 experts) instead of bf16
   uint16_t* h;          // [T, D]
+  uint16_t* z;          // [3][T][D] bf16 planes of the normalised router input
+  float* logits;        // [T, Epad]
   int32_t* topk_idx;    // [T, K]
   float* topk_w;        // [T, K]
 };
@@ -31,11 +45,12 @@ hipError_t launch_prep_router_w(const void* w, int w_f32, int E, int Epad, int D
 struct PermuteArgs {
   const int32_t* topk_idx;
   const float* topk_w;
-  int T, K, E, BM;
+  int T, K, E;
+  int qmax;               // capacity of each tile queue
   int32_t* counts;        // [E]
   int32_t* offsets;       // [E + 1]
-  Tile* tiles;            // [max_tiles]
-  int32_t* n_tiles;       // [1]
+  Tile* tiles;            // [qmax][kQueues]: tile p of queue x at tiles[p * kQueues + x]
+  int32_t* qlen;          // [kQueues]
   int32_t* sorted_token;  // [K T]
   float* row_w;           // [K T]
   int32_t* row_of_slot;   // [K T]
@@ -44,8 +59,8 @@ hipError_t launch_permute(const PermuteArgs& a, hipStream_t stream);
 
 struct GemmArgs {
   const Tile* tiles;
-  const int32_t* n_tiles;
-  int max_tiles;
+  const int32_t* qlen;
+  int qmax;
   const int32_t* sorted_token;
   const float* row_w;
   const uint16_t* h;       // [T, D] expert input (bf16, or fp16 for int4 experts)
@@ -72,8 +87,5 @@ struct CombineArgs {
   int act_f32;
 };
 hipError_t launch_combine(const CombineArgs& a, hipStream_t stream);
-
-// Largest number of rows one tile holds.
-constexpr int kTileRows = 128;
 
 }  // namespace dg
