@@ -142,6 +142,9 @@ def main():
     ap.add_argument("--rotate", type=int, default=4, help="resident weight copies cycled through")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-profile", action="store_true", help="skip the per-kernel event pass")
+    ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
+                    help="also run a plain device copy of this many MiB (3 times), so that a counter run "
+                         "records HBM bytes for a transfer of known size")
     args = ap.parse_args()
 
     if args.gpus != 1:
@@ -285,6 +288,14 @@ def main():
         result["cpu_baseline"] = cpu_baseline(wl, x, w_host, threads)
     for layer in layers:
         layer.close()
+    if args.copy_calibration:
+        n = args.copy_calibration << 20
+        src = torch.empty(n, dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        result["copy_calibration_bytes"] = n
     print(json.dumps(result), flush=True)
 
 

@@ -2,7 +2,7 @@
 // workspace allocated once at create time, router-weight preparation, and the
 // asynchronous launch sequence of one forward:
 //
-//   router (norm + expert input, logits, top-k + weights)
+//   router (norm + expert input, then logits + top-k + weights)
 //   -> permutation (counts, offsets, tile list, stable scatter)
 //   -> gate_up grouped GEMM (+ GELU-tanh gating)
 //   -> down grouped GEMM (x routing weight)
@@ -49,7 +49,7 @@ size_t act_elem_bytes(int dt) { return dt == DG_F32 ? 4 : 2; }
 
 // Sub-buffer layout of the workspace (byte offsets from the base).
 struct Layout {
-  size_t h, z, logits, topk_idx, topk_w, counts, offsets, tiles, qlen, sorted_token, row_w, row_of_slot, act, y;
+  size_t h, z, logits, tile_count, topk_idx, topk_w, counts, offsets, tiles, qlen, sorted_token, row_w, row_of_slot, act, y;
   size_t wr, gamma_r, bias, gamma_e;
   size_t total;
   int Epad, n_wplanes, qmax;
@@ -71,6 +71,7 @@ Layout plan(const dg_moe_config& c) {
   L.h = take(T * D * 2);
   L.z = take(3 * T * D * 2);
   L.logits = take(T * (size_t)L.Epad * 4);
+  L.tile_count = take((T + 15) / 16 * 4);
   L.topk_idx = take(T * K * 4);
   L.topk_w = take(T * K * 4);
   L.counts = take(E * 4);
@@ -269,6 +270,11 @@ dg_status dg_moe_create(const dg_moe_config* cfg, const dg_moe_weights* w, void*
       return hip_fail(ci, "preparing router parameters");
     }
   }
+  e = hipMemsetAsync(hd->ws + hd->L.tile_count, 0, ((size_t)cfg->max_tokens + 15) / 16 * 4, stream);
+  if (e != hipSuccess) {
+    dg_moe_destroy(hd);
+    return hip_fail(e, "create: clearing the arrival counters");
+  }
   e = hipStreamSynchronize(stream);
   if (e != hipSuccess) {
     dg_moe_destroy(hd);
@@ -323,6 +329,7 @@ static dg_status run_forward(dg_moe_handle hd, const void* x, void* out, int32_t
   ra.h = hd->at<uint16_t>(L.h);
   ra.z = hd->at<uint16_t>(L.z);
   ra.logits = hd->at<float>(L.logits);
+  ra.tile_count = hd->at<int32_t>(L.tile_count);
   ra.topk_idx = hd->at<int32_t>(L.topk_idx);
   ra.topk_w = hd->at<float>(L.topk_w);
   hipError_t e = dg::launch_router(ra, stream);

@@ -35,7 +35,11 @@ namespace dg {
 
 namespace {
 
-constexpr int kThreads = 256;
+#ifndef DG_GEMM_WAVES
+#define DG_GEMM_WAVES 4
+#endif
+constexpr int kWaves = DG_GEMM_WAVES;    // waves per workgroup
+constexpr int kThreads = 64 * kWaves;
 constexpr int kKS = 128;                  // K per pipeline step (four MFMA K steps of 32)
 constexpr int kNS = kKS / 32;
 constexpr int kSegs = kKS / 8;            // 16-byte segments per staged row
@@ -43,7 +47,7 @@ constexpr int kRowBytes = kKS * 2;
 constexpr int kDmaRows = 1024 / kRowBytes;  // rows one wave-wide 16-byte-per-lane transfer fills
 constexpr int kStageBytes = kTileRows * kRowBytes;
 constexpr int kBMT = kTileRows / 16;      // m-tiles per tile
-constexpr int kDmaInstr = kTileRows / (4 * kDmaRows);  // transfers per wave for a full tile
+constexpr int kDmaInstr = kTileRows / (kWaves * kDmaRows);  // transfers per wave for a full tile
 
 struct Panels {
   u32x4 b0[kNS], b1[kNS];
@@ -93,7 +97,7 @@ __device__ __forceinline__ void lds_dma16(uint32_t lds_base, const void* gaddr) 
 }
 
 // Activation rows of one K step straight into LDS: instruction i of wave w
-// fills the kDmaRows rows starting at kDmaRows (w + 4 i); lane l lands in row
+// fills the kDmaRows rows starting at kDmaRows (w + kWaves i); lane l lands in row
 // slot l / kSegs, 16-byte position l % kSegs and carries logical segment
 // position ^ (row % kSegs), an XOR swizzle that makes the MFMA reads
 // bank-conflict free. Segments past a short last step re-read a valid one.
@@ -102,11 +106,11 @@ __device__ __forceinline__ void dma_a(char* stage, const uint16_t* const (&rowp)
                                       int lane) {
   const uint32_t base = __builtin_amdgcn_readfirstlane(lds_addr(stage) + wave * kDmaRows * kRowBytes);
 #pragma unroll
-  for (int i = 0; i < 16 * NMT / (4 * kDmaRows); ++i) {
-    const int r = kDmaRows * (wave + 4 * i) + lane / kSegs;
+  for (int i = 0; i < 16 * NMT / (kWaves * kDmaRows); ++i) {
+    const int r = kDmaRows * (wave + kWaves * i) + lane / kSegs;
     int sg = (lane % kSegs) ^ (r % kSegs);
     if (NSEG < kSegs) sg = sg % NSEG;
-    lds_dma16(base + i * 4 * kDmaRows * kRowBytes, rowp[i] + k0 + sg * 8);
+    lds_dma16(base + i * kWaves * kDmaRows * kRowBytes, rowp[i] + k0 + sg * 8);
   }
 }
 
@@ -218,7 +222,7 @@ template <bool GATE_UP>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3, 3))) void k_gemm_bf16(GemmArgs a) {
   __shared__ __attribute__((aligned(16))) char As[2 * kStageBytes];
   const int F = a.F, D = a.D;
-  const int NB = GATE_UP ? F / 64 : D / 128;
+  const int NB = GATE_UP ? F / (16 * kWaves) : D / (32 * kWaves);
   const int K = GATE_UP ? D : F;
   const int qx = blockIdx.x & (kQueues - 1);
   const int j = blockIdx.x / kQueues;
@@ -235,18 +239,18 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3, 3))
   const uint16_t* rowp[kDmaInstr];
 #pragma unroll
   for (int i = 0; i < kDmaInstr; ++i) {
-    const int r = min(kDmaRows * (wave + 4 * i) + lane / kSegs, tl.mc - 1);
+    const int r = min(kDmaRows * (wave + kWaves * i) + lane / kSegs, tl.mc - 1);
     rowp[i] = GATE_UP ? a.h + (size_t)a.sorted_token[tl.row0 + r] * D : a.act + (size_t)(tl.row0 + r) * F;
   }
   int col;  // gate_up: feature f; down: first output d
   const uint16_t* w0;
   const uint16_t* w1;
   if (GATE_UP) {
-    col = nb * 64 + wave * 16 + (lane & 15);
+    col = nb * 16 * kWaves + wave * 16 + (lane & 15);
     w0 = static_cast<const uint16_t*>(a.w_gate_up) + ((size_t)tl.e * 2 * F + col) * D + g * 8;
     w1 = w0 + (size_t)F * D;
   } else {
-    col = nb * 128 + wave * 32 + (lane & 15);
+    col = nb * 32 * kWaves + wave * 32 + (lane & 15);
     w0 = static_cast<const uint16_t*>(a.w_down) + ((size_t)tl.e * D + col) * F + g * 8;
     w1 = w0 + (size_t)16 * F;
   }
@@ -288,12 +292,12 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3, 3))
 }  // namespace
 
 hipError_t launch_gate_up_bf16(const GemmArgs& a, hipStream_t stream) {
-  k_gemm_bf16<true><<<dim3(kQueues * a.qmax * (a.F / 64)), dim3(kThreads), 0, stream>>>(a);
+  k_gemm_bf16<true><<<dim3(kQueues * a.qmax * (a.F / (16 * kWaves))), dim3(kThreads), 0, stream>>>(a);
   return hipGetLastError();
 }
 
 hipError_t launch_down_bf16(const GemmArgs& a, hipStream_t stream) {
-  k_gemm_bf16<false><<<dim3(kQueues * a.qmax * (a.D / 128)), dim3(kThreads), 0, stream>>>(a);
+  k_gemm_bf16<false><<<dim3(kQueues * a.qmax * (a.D / (32 * kWaves))), dim3(kThreads), 0, stream>>>(a);
   return hipGetLastError();
 }
 

@@ -35,6 +35,7 @@ struct RouterArgs {
   uint16_t* h;          // [T, D]
   uint16_t* z;          // [3][T][D] bf16 planes of the normalised router input
   float* logits;        // [T, Epad]
+  int32_t* tile_count;  // [ceil(T / 16)] arrival counters of the logits kernel, zero between forwards
   int32_t* topk_idx;    // [T, K]
   float* topk_w;        // [T, K]
 };

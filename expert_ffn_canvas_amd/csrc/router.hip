@@ -1,16 +1,15 @@
-// Router of the MoE layer on gfx950, in three short kernels:
-//
-//  norm:   per token, r = 1/sqrt(mean x^2 + eps); the expert input
+// Router of the MoE layer on gfx950, two kernels:
+//  norm:   per token r = 1/sqrt(mean x^2 + eps); the expert input
 //          h = x r (1 + gamma_e) (bf16, or fp16 for int4 experts); and the
 //          router input z = x r (1 + gamma_r) in fp32, stored as three exact
-//          bf16 planes z = z0 + z1 + z2 (each plane holds the next 8
-//          significant bits of the fp32 value).
-//  logits: [T, E] = z W_r^T on the bf16 matrix cores. Each bf16 x bf16
+//          bf16 planes z = z0 + z1 + z2 (each holds the next 8 significant
+//          bits of the fp32 value).
+//  router: logits = z W_r^T + b on the bf16 matrix cores (each bf16 x bf16
 //          product is exact in fp32 and the MFMA accumulates in fp32, so with
-//          z in three planes (and an fp32 router weight split the same way at
-//          create time) the logits have fp32 dot-product accuracy.
-//  top-k:  per token, the k largest logits + bias (ties: lower expert id),
-//          their softmax renormalised over the k, slots ordered by logit.
+//          z in three planes, and an fp32 router weight split the same way at
+//          create time, the logits have fp32 dot-product accuracy); then per
+//          token the k largest logits (ties: lower expert id) and their
+//          softmax renormalised over the k, slots ordered by logit.
 //
 // Sources: Quant-Tuner PR "Add DiffusionGemma (Gemma-4 MoE block-diffusion)
 // support", "Answers to the motivating questions" (the router reads the raw
@@ -23,36 +22,145 @@ namespace dg {
 
 namespace {
 
-constexpr int kTokTile = 16;       // tokens per logits workgroup (MFMA M)
-constexpr int kKChunk = 128;       // d_model columns staged per LDS round
+constexpr int kTokTile = 16;    // tokens per workgroup (MFMA M)
+constexpr int kKChunk = 128;    // d_model columns per chunk
+constexpr int kWaves = 8;       // waves per workgroup; wave h owns chunks h, h + 8, ...
 
-__device__ __forceinline__ void split3(float z, uint16_t& b0, uint16_t& b1, uint16_t& b2) {
-  b0 = f32_to_bf16_bits(z);
-  const float r1 = z - bf16_bits_to_f32(b0);
-  b1 = f32_to_bf16_bits(r1);
-  const float r2 = r1 - bf16_bits_to_f32(b1);
-  b2 = f32_to_bf16_bits(r2);
+// z = hi + mid + lo exactly: hi keeps the top 8 significant bits of z
+// (truncated), mid the next 8 of the remainder, and the last remainder has at
+// most 8 significant bits, so all three are exact bf16 values.
+__device__ __forceinline__ void split3(float z, float& hi, float& mid, float& lo) {
+  hi = __uint_as_float(__float_as_uint(z) & 0xffff0000u);
+  const float r1 = z - hi;
+  mid = __uint_as_float(__float_as_uint(r1) & 0xffff0000u);
+  lo = r1 - mid;
+}
+
+// Upper halves of two floats that are exact bf16 values -> packed bf16 pair.
+__device__ __forceinline__ uint32_t pack_hi(float a, float b) {
+  return (__float_as_uint(a) >> 16) | (__float_as_uint(b) & 0xffff0000u);
+}
+
+// x values (fp32 or bf16) of one 8-column piece.
+template <bool XF32>
+struct XPiece {
+  u32x4 v[XF32 ? 2 : 1];
+};
+
+template <bool XF32>
+__device__ __forceinline__ void load_piece(const void* x, size_t off, XPiece<XF32>& p) {
+  if constexpr (XF32) {
+    p.v[0] = *reinterpret_cast<const u32x4*>(static_cast<const float*>(x) + off);
+    p.v[1] = *reinterpret_cast<const u32x4*>(static_cast<const float*>(x) + off + 4);
+  } else {
+    p.v[0] = *reinterpret_cast<const u32x4*>(static_cast<const uint16_t*>(x) + off);
+  }
 }
 
 template <bool XF32>
-__device__ __forceinline__ void load8(const void* x, size_t off, float (&v)[8]) {
-  if (XF32) {
-    const float4 a = *reinterpret_cast<const float4*>(static_cast<const float*>(x) + off);
-    const float4 b = *reinterpret_cast<const float4*>(static_cast<const float*>(x) + off + 4);
-    v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w; v[4] = b.x; v[5] = b.y; v[6] = b.z; v[7] = b.w;
-  } else {
-    const u32x4 a = *reinterpret_cast<const u32x4*>(static_cast<const uint16_t*>(x) + off);
+__device__ __forceinline__ void piece_floats(const XPiece<XF32>& p, float (&f)[8]) {
+  if constexpr (XF32) {
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      v[2 * i] = bf16_lo(a[i]);
-      v[2 * i + 1] = bf16_hi(a[i]);
+      f[i] = __uint_as_float(p.v[0][i]);
+      f[4 + i] = __uint_as_float(p.v[1][i]);
+    }
+  } else {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      f[2 * i] = bf16_lo(p.v[0][i]);
+      f[2 * i + 1] = bf16_hi(p.v[0][i]);
     }
   }
 }
 
-// One workgroup of 256 threads per token; thread i owns the 8-column segments
-// i, i + 256, ... (up to 8 of them, d_model <= 16384). All x loads of a thread
-// are issued together, then one block reduction gives the RMS statistic.
+// Order-preserving map of a float to uint32 (larger float -> larger key).
+__device__ __forceinline__ uint32_t float_key(float v) {
+  const uint32_t b = __float_as_uint(v);
+  return (b & 0x80000000u) ? ~b : (b | 0x80000000u);
+}
+
+// Number of lanes of the wave for which `pred` holds.
+__device__ __forceinline__ int wave_count(bool pred) { return __popcll(__ballot(pred)); }
+
+// Top-k of one token from its logits row in LDS (one wave, E <= 256; lane l
+// holds experts l + 64 u). A radix select on the keys finds the k-th largest
+// key t (the largest t with at least k keys >= t); the experts above t are
+// taken, and of those equal to t the lowest ids fill the remaining places.
+// The k chosen experts are then ordered by (logit desc, id asc) and their
+// softmax over the k is summed in that order.
+__device__ __forceinline__ void topk_row(const float* lrow, int E, int K, int lane, float* sel_v, int* sel_i,
+                                         int32_t* idx_out, float* w_out) {
+  const int nu = (E + 63) >> 6;
+  float v[4];
+  uint32_t key[4];
+#pragma unroll
+  for (int u = 0; u < 4; ++u) {
+    const bool present = (u < nu) && (lane + 64 * u < E);
+    v[u] = present ? lrow[lane + 64 * u] : -INFINITY;
+    key[u] = present ? float_key(v[u]) : 0u;  // absent experts rank below every real one
+  }
+  uint32_t t = 0;
+  for (int b = 31; b >= 0; --b) {
+    const uint32_t cand = t | (1u << b);
+    int cnt = 0;
+#pragma unroll
+    for (int u = 0; u < 4; ++u)
+      if (u < nu) cnt += wave_count(key[u] >= cand);
+    if (cnt >= K) t = cand;
+  }
+  int above = 0;
+#pragma unroll
+  for (int u = 0; u < 4; ++u)
+    if (u < nu) above += wave_count(key[u] > t);
+  // keys equal to t in id order: experts l + 64 u come before l + 64 (u + 1)
+  int need = K - above;
+  bool sel[4];
+#pragma unroll
+  for (int u = 0; u < 4; ++u) {
+    const bool present = (u < nu) && (lane + 64 * u < E);
+    const bool eq = present && key[u] == t;
+    const uint64_t msk = __ballot(eq);
+    const int before = __popcll(msk & ((1ull << lane) - 1ull));
+    sel[u] = present && (key[u] > t || (eq && before < need));
+    need -= min(__popcll(msk), max(need, 0));
+  }
+  // order the chosen experts: rank = chosen ones with a larger key, or an equal key and a lower id
+  int rank[4] = {0, 0, 0, 0};
+#pragma unroll
+  for (int u2 = 0; u2 < 4; ++u2) {
+    if (u2 >= nu) break;
+    uint64_t msk = __ballot(sel[u2]);
+    while (msk) {
+      const int src = __ffsll((long long)msk) - 1;
+      msk &= msk - 1ull;
+      const uint32_t ks = __shfl(key[u2], src);
+      const int es = src + 64 * u2;
+#pragma unroll
+      for (int u = 0; u < 4; ++u) rank[u] += (ks > key[u]) || (ks == key[u] && es < lane + 64 * u);
+    }
+  }
+#pragma unroll
+  for (int u = 0; u < 4; ++u) {
+    if (sel[u]) {
+      sel_v[rank[u]] = v[u];
+      sel_i[rank[u]] = lane + 64 * u;
+    }
+  }
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
+  if (lane < K) {
+    const float vmax = sel_v[0];
+    float den = 0.0f;
+    for (int j = 0; j < K; ++j) den += __expf(sel_v[j] - vmax);
+    idx_out[lane] = sel_i[lane];
+    w_out[lane] = __expf(sel_v[lane] - vmax) / den;
+  }
+}
+
+// One workgroup of 256 threads per token; thread i owns the 8-column pieces
+// i, i + 256, ... (up to 8 of them: d_model <= 16384). All loads of a thread
+// (x and both gammas) are issued together, one block reduction gives r.
 template <bool XF32>
 __global__ __launch_bounds__(256) void k_norm(RouterArgs a) {
   __shared__ float wsum[4];
@@ -61,21 +169,30 @@ __global__ __launch_bounds__(256) void k_norm(RouterArgs a) {
   const int D = a.D;
   const int nseg = D / 8;
   const size_t row = (size_t)t * D;
-  float v[8][8];
+  XPiece<XF32> xp[8];
+  float4 gr[8][2], ge[8][2];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const int sg = tid + 256 * i;
+    if (sg < nseg) {
+      load_piece<XF32>(a.x, row + sg * 8, xp[i]);
+      gr[i][0] = *reinterpret_cast<const float4*>(a.gamma_r + sg * 8);
+      gr[i][1] = *reinterpret_cast<const float4*>(a.gamma_r + sg * 8 + 4);
+      ge[i][0] = *reinterpret_cast<const float4*>(a.gamma_e + sg * 8);
+      ge[i][1] = *reinterpret_cast<const float4*>(a.gamma_e + sg * 8 + 4);
+    }
+  }
   float ss = 0.0f;
 #pragma unroll
   for (int i = 0; i < 8; ++i) {
-    const int sg = tid + 256 * i;
-    if (sg < nseg) load8<XF32>(a.x, row + sg * 8, v[i]);
-  }
+    if (tid + 256 * i < nseg) {
+      float f[8];
+      piece_floats<XF32>(xp[i], f);
 #pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    const int sg = tid + 256 * i;
-    if (sg < nseg)
-#pragma unroll
-      for (int k = 0; k < 8; ++k) ss += v[i][k] * v[i][k];
+      for (int k = 0; k < 8; ++k) ss += f[k] * f[k];
+    }
   }
-  for (int m = 32; m >= 1; m >>= 1) ss += __shfl_xor(ss, m);
+  for (int msk = 32; msk >= 1; msk >>= 1) ss += __shfl_xor(ss, msk);
   if (lane == 0) wsum[wave] = ss;
   __syncthreads();
   const float tot = (wsum[0] + wsum[1]) + (wsum[2] + wsum[3]);
@@ -85,79 +202,58 @@ __global__ __launch_bounds__(256) void k_norm(RouterArgs a) {
   for (int i = 0; i < 8; ++i) {
     const int sg = tid + 256 * i;
     if (sg >= nseg) continue;
-    const int c = sg * 8;
-    const float4 gr0 = *reinterpret_cast<const float4*>(a.gamma_r + c);
-    const float4 gr1 = *reinterpret_cast<const float4*>(a.gamma_r + c + 4);
-    const float4 ge0 = *reinterpret_cast<const float4*>(a.gamma_e + c);
-    const float4 ge1 = *reinterpret_cast<const float4*>(a.gamma_e + c + 4);
-    const float gr[8] = {gr0.x, gr0.y, gr0.z, gr0.w, gr1.x, gr1.y, gr1.z, gr1.w};
-    const float ge[8] = {ge0.x, ge0.y, ge0.z, ge0.w, ge1.x, ge1.y, ge1.z, ge1.w};
-    uint16_t zb[3][8];
-    float hv[8];
+    float f[8];
+    piece_floats<XF32>(xp[i], f);
+    const float g1[8] = {gr[i][0].x, gr[i][0].y, gr[i][0].z, gr[i][0].w, gr[i][1].x, gr[i][1].y, gr[i][1].z, gr[i][1].w};
+    const float g2[8] = {ge[i][0].x, ge[i][0].y, ge[i][0].z, ge[i][0].w, ge[i][1].x, ge[i][1].y, ge[i][1].z, ge[i][1].w};
+    float zh[8], zm[8], zl[8], hv[8];
 #pragma unroll
     for (int k = 0; k < 8; ++k) {
-      const float xr = v[i][k] * r;
-      split3(xr * (1.0f + gr[k]), zb[0][k], zb[1][k], zb[2][k]);
-      hv[k] = xr * (1.0f + ge[k]);
+      const float xr = f[k] * r;
+      split3(xr * (1.0f + g1[k]), zh[k], zm[k], zl[k]);
+      hv[k] = xr * (1.0f + g2[k]);
     }
+    u32x4 o0, o1, o2, ho;
 #pragma unroll
-    for (int p = 0; p < 3; ++p) {
-      u32x4 o;
-#pragma unroll
-      for (int k = 0; k < 4; ++k) o[k] = (uint32_t)zb[p][2 * k] | ((uint32_t)zb[p][2 * k + 1] << 16);
-      *reinterpret_cast<u32x4*>(a.z + p * plane + row + c) = o;
-    }
-    u32x4 ho;
-#pragma unroll
-    for (int k = 0; k < 4; ++k)
+    for (int k = 0; k < 4; ++k) {
+      o0[k] = pack_hi(zh[2 * k], zh[2 * k + 1]);
+      o1[k] = pack_hi(zm[2 * k], zm[2 * k + 1]);
+      o2[k] = pack_hi(zl[2 * k], zl[2 * k + 1]);
       ho[k] = a.h_f16 ? pack_f16x2(hv[2 * k], hv[2 * k + 1]) : pack_bf16x2(hv[2 * k], hv[2 * k + 1]);
-    *reinterpret_cast<u32x4*>(a.h + row + c) = ho;
+    }
+    const size_t off = row + sg * 8;
+    *reinterpret_cast<u32x4*>(a.z + off) = o0;
+    *reinterpret_cast<u32x4*>(a.z + plane + off) = o1;
+    *reinterpret_cast<u32x4*>(a.z + 2 * plane + off) = o2;
+    *reinterpret_cast<u32x4*>(a.h + off) = ho;
   }
 }
 
-// Workgroup = 16 tokens x 16 experts, eight waves: wave h takes the 128-column
-// chunks h, h + 8, ... of d_model and the eight partial sums are added through
-// LDS in a fixed order. Both MFMA operands come straight from global memory
-// (the z planes and the router weight are L2-resident); a wave has its first
-// two chunks in flight before it multiplies the first.
-constexpr int kLogitWaves = 8;
-
+// Workgroup (token tile tt, expert tile et): 16 tokens x 16 experts, 8 waves;
+// wave h owns the 128-column chunks h, h + 8, ... of d_model. Lane
+// (m = l % 16, g = l / 16) loads, in each chunk, the 8-column pieces g, g + 4,
+// g + 8, g + 12 of token m's three z planes and of expert m's router weight:
+// the MFMA operand layouts. A wave issues the loads of up to kGroup chunks at
+// once, then multiplies. The eight partial sums are added through LDS in a
+// fixed order.
+// All expert tiles of a token tile run on one XCD (workgroup b runs on XCD
+// b % 8) and share its L2: each one publishes its logits with a counter and
+// the last to arrive ranks the full rows for the top-k.
 template <int NWP>
-struct ZChunk {
-  u32x4 z[4][3];
-  u32x4 w[4][NWP];
-};
-
-template <int NWP>
-__device__ __forceinline__ void load_chunk(const uint16_t* zr, size_t plane, const uint16_t* wrow, size_t wplane,
-                                           int c, ZChunk<NWP>& ch) {
-#pragma unroll
-  for (int kk = 0; kk < 4; ++kk) {
-    const int col = c * kKChunk + kk * 32;
-#pragma unroll
-    for (int p = 0; p < 3; ++p) ch.z[kk][p] = *reinterpret_cast<const u32x4*>(zr + p * plane + col);
-#pragma unroll
-    for (int p = 0; p < NWP; ++p) ch.w[kk][p] = *reinterpret_cast<const u32x4*>(wrow + p * wplane + col);
-  }
-}
-
-template <int NWP>
-__device__ __forceinline__ void mma_chunk(const ZChunk<NWP>& ch, f32x4& acc) {
-#pragma unroll
-  for (int kk = 0; kk < 4; ++kk)
-#pragma unroll
-    for (int zp = 0; zp < 3; ++zp)
-#pragma unroll
-      for (int p = 0; p < NWP; ++p) acc = mfma_bf16(as_bf16x8(ch.z[kk][zp]), as_bf16x8(ch.w[kk][p]), acc);
-}
-
-template <int NWP>
-__global__ __launch_bounds__(64 * kLogitWaves) void k_logits(RouterArgs a) {
-  __shared__ float part[kLogitWaves][kTokTile][17];
+__global__ __launch_bounds__(64 * kWaves) void k_logits(RouterArgs a) {
+  constexpr int kGroup = (NWP == 1) ? 3 : 1;
+  __shared__ float part[kWaves][kTokTile][17];
+  __shared__ float lrow[kTokTile][260];
+  __shared__ float sel_v[kWaves][8];
+  __shared__ int sel_i[kWaves][8];
+  __shared__ int is_last;
   const int tid = threadIdx.x, lane = tid & 63, kh = tid >> 6;
   const int n_et = a.Epad / 16;
-  const int tt = blockIdx.x / n_et;
-  const int et = blockIdx.x - tt * n_et;
+  const int n_tt = (a.T + kTokTile - 1) / kTokTile;
+  const int xq = blockIdx.x % kQueues, jq = blockIdx.x / kQueues;
+  const int tt = xq + kQueues * (jq / n_et);
+  const int et = jq % n_et;
+  if (tt >= n_tt) return;
   const int t0 = tt * kTokTile;
   const int D = a.D;
   const int m = lane & 15, g = lane >> 4;
@@ -167,77 +263,79 @@ __global__ __launch_bounds__(64 * kLogitWaves) void k_logits(RouterArgs a) {
   const uint16_t* zr = a.z + (size_t)t * D + g * 8;
   const uint16_t* wrow = a.wr + (size_t)(et * 16 + m) * D + g * 8;
   const int nc = D / kKChunk;
-  const int n_my = (nc - kh + kLogitWaves - 1) / kLogitWaves;  // chunks kh, kh + 8, ...
+  const int n_my = (nc - kh + kWaves - 1) / kWaves;  // chunks kh, kh + 8, ...
 
   f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
-  ZChunk<NWP> cur, nxt;
-  if (n_my > 0) {
-    load_chunk<NWP>(zr, plane, wrow, wplane, kh, cur);
-    for (int i = 0; i + 1 < n_my; ++i) {
-      load_chunk<NWP>(zr, plane, wrow, wplane, kh + kLogitWaves * (i + 1), nxt);
-      __builtin_amdgcn_sched_barrier(0);
-      mma_chunk<NWP>(cur, acc);
-      cur = nxt;
+  for (int c0 = 0; c0 < n_my; c0 += kGroup) {
+    u32x4 zb[kGroup][4][3], wb[kGroup][4][NWP];
+#pragma unroll
+    for (int q = 0; q < kGroup; ++q) {
+      if (c0 + q < n_my) {
+        const int col = (kh + kWaves * (c0 + q)) * kKChunk;
+#pragma unroll
+        for (int kk = 0; kk < 4; ++kk) {
+#pragma unroll
+          for (int p = 0; p < 3; ++p) zb[q][kk][p] = *reinterpret_cast<const u32x4*>(zr + p * plane + col + kk * 32);
+#pragma unroll
+          for (int p = 0; p < NWP; ++p) wb[q][kk][p] = *reinterpret_cast<const u32x4*>(wrow + p * wplane + col + kk * 32);
+        }
+      }
     }
-    mma_chunk<NWP>(cur, acc);
+#pragma unroll
+    for (int q = 0; q < kGroup; ++q) {
+      if (c0 + q < n_my) {
+#pragma unroll
+        for (int kk = 0; kk < 4; ++kk)
+#pragma unroll
+          for (int zp = 0; zp < 3; ++zp)
+#pragma unroll
+            for (int p = 0; p < NWP; ++p) acc = mfma_bf16(as_bf16x8(zb[q][kk][zp]), as_bf16x8(wb[q][kk][p]), acc);
+      }
+    }
   }
 #pragma unroll
   for (int i = 0; i < 4; ++i) part[kh][g * 4 + i][m] = acc[i];
   __syncthreads();
-  // [16 tokens x 16 experts]; the eight partial sums in a fixed order
+  // [16 tokens x 16 experts] (+ bias); the eight partial sums in a fixed order
   if (tid < kTokTile * 16) {
     const int mm = tid >> 4, n = tid & 15;
     float sum = part[0][mm][n];
 #pragma unroll
-    for (int w = 1; w < kLogitWaves; ++w) sum += part[w][mm][n];
-    if (t0 + mm < a.T) a.logits[(size_t)(t0 + mm) * a.Epad + et * 16 + n] = sum;
+    for (int w = 1; w < kWaves; ++w) sum += part[w][mm][n];
+    const int e = et * 16 + n;
+    if (a.bias != nullptr && e < a.E) sum += a.bias[e];
+    if (t0 + mm < a.T) a.logits[(size_t)(t0 + mm) * a.Epad + e] = sum;
   }
-}
-
-// One wave per token: k rounds of a wave-wide argmax over (logit desc, id asc).
-__global__ __launch_bounds__(256) void k_topk(RouterArgs a) {
-  const int lane = threadIdx.x & 63;
-  const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
-  if (t >= a.T) return;
-  const int E = a.E, K = a.K;
-  float v[4];
-  bool taken[4];
-#pragma unroll
-  for (int u = 0; u < 4; ++u) {
-    const int e = lane + 64 * u;
-    float l = -INFINITY;
-    if (e < E) l = a.logits[(size_t)t * a.Epad + e] + (a.bias ? a.bias[e] : 0.0f);
-    v[u] = (l == l) ? l : -INFINITY;  // a NaN logit ranks last, so k valid ids are always chosen
-    taken[u] = (e >= E);
+  // publish: every thread's stores have reached L2 before the counter moves
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();
+  if (tid == 0) {
+    const int old = atomicAdd(&a.tile_count[tt], 1);
+    is_last = (old == n_et - 1);
+    if (is_last) a.tile_count[tt] = 0;  // ready for the next forward
   }
-  float my_v = -INFINITY, vmax = 0.0f;
-  int my_i = 0;
-  for (int j = 0; j < K; ++j) {
-    float bv = -INFINITY;
-    int bi = 0x7fffffff;
+  __syncthreads();
+  if (!is_last) return;
+  // Last expert tile of this token tile: gather the full logit rows. They come
+  // from this XCD's L2 (every writer ran on this XCD and waited for its
+  // stores); no workgroup on this CU read these rows earlier in the launch, so
+  // its L1 holds no stale copy.
+  for (int i = tid; i < kTokTile * (a.Epad / 4); i += 64 * kWaves) {
+    const int mm = i / (a.Epad / 4), c4 = i - mm * (a.Epad / 4);
+    float4 l = make_float4(-INFINITY, -INFINITY, -INFINITY, -INFINITY);
+    if (t0 + mm < a.T) l = *reinterpret_cast<const float4*>(&a.logits[(size_t)(t0 + mm) * a.Epad + 4 * c4]);
+    const float lv[4] = {l.x, l.y, l.z, l.w};
 #pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      const int e = lane + 64 * u;
-      if (!taken[u] && (v[u] > bv || (v[u] == bv && e < bi))) { bv = v[u]; bi = e; }
-    }
-    for (int m = 32; m >= 1; m >>= 1) {
-      const float ov = __shfl_xor(bv, m);
-      const int oi = __shfl_xor(bi, m);
-      if (ov > bv || (ov == bv && oi < bi)) { bv = ov; bi = oi; }
-    }
-    if (j == 0) vmax = bv;
-    if (lane == j) { my_v = bv; my_i = bi; }
-#pragma unroll
-    for (int u = 0; u < 4; ++u)
-      if (bi == lane + 64 * u) taken[u] = true;
+    for (int q = 0; q < 4; ++q)  // a NaN logit ranks last, so k valid ids are always chosen
+      lrow[mm][4 * c4 + q] = (lv[q] == lv[q]) ? lv[q] : -INFINITY;
   }
-  // softmax over the k selected logits (equal to the full softmax renormalised over them)
-  const float ex = (lane < K) ? __expf(my_v - vmax) : 0.0f;
-  float den = ex;
-  for (int m = 32; m >= 1; m >>= 1) den += __shfl_xor(den, m);
-  if (lane < K) {
-    a.topk_idx[(size_t)t * K + lane] = my_i;
-    a.topk_w[(size_t)t * K + lane] = ex / den;
+  __syncthreads();
+  for (int q = 0; q < kTokTile / kWaves; ++q) {
+    const int mm = kh * (kTokTile / kWaves) + q;
+    if (t0 + mm < a.T)
+      topk_row(lrow[mm], a.E, a.K, lane, sel_v[kh], sel_i[kh], a.topk_idx + (size_t)(t0 + mm) * a.K,
+               a.topk_w + (size_t)(t0 + mm) * a.K);
+    __builtin_amdgcn_wave_barrier();
   }
 }
 
@@ -250,11 +348,11 @@ __global__ void k_prep_router_w(const void* __restrict__ w, int w_f32, int E, in
     const int e = (int)(i / D);
     if (w_f32) {
       const float v = (e < E) ? static_cast<const float*>(w)[i] : 0.0f;
-      uint16_t b0, b1, b2;
+      float b0, b1, b2;
       split3(v, b0, b1, b2);
-      planes[i] = b0;
-      planes[n + i] = b1;
-      planes[2 * n + i] = b2;
+      planes[i] = (uint16_t)(__float_as_uint(b0) >> 16);
+      planes[n + i] = (uint16_t)(__float_as_uint(b1) >> 16);
+      planes[2 * n + i] = (uint16_t)(__float_as_uint(b2) >> 16);
     } else {
       planes[i] = (e < E) ? static_cast<const uint16_t*>(w)[i] : (uint16_t)0;
     }
@@ -264,21 +362,18 @@ __global__ void k_prep_router_w(const void* __restrict__ w, int w_f32, int E, in
 }  // namespace
 
 hipError_t launch_router(const RouterArgs& a, hipStream_t stream) {
-  const dim3 blk(256);
   if (a.x_f32)
-    k_norm<true><<<dim3(a.T), blk, 0, stream>>>(a);
+    k_norm<true><<<dim3(a.T), dim3(256), 0, stream>>>(a);
   else
-    k_norm<false><<<dim3(a.T), blk, 0, stream>>>(a);
+    k_norm<false><<<dim3(a.T), dim3(256), 0, stream>>>(a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  const dim3 lg(((a.T + kTokTile - 1) / kTokTile) * (a.Epad / 16));
+  const int n_tt = (a.T + kTokTile - 1) / kTokTile;
+  const dim3 grid(kQueues * ((n_tt + kQueues - 1) / kQueues) * (a.Epad / 16));
   if (a.n_wplanes == 3)
-    k_logits<3><<<lg, dim3(64 * kLogitWaves), 0, stream>>>(a);
+    k_logits<3><<<grid, dim3(64 * kWaves), 0, stream>>>(a);
   else
-    k_logits<1><<<lg, dim3(64 * kLogitWaves), 0, stream>>>(a);
-  e = hipGetLastError();
-  if (e != hipSuccess) return e;
-  k_topk<<<dim3((a.T + 3) / 4), blk, 0, stream>>>(a);
+    k_logits<1><<<grid, dim3(64 * kWaves), 0, stream>>>(a);
   return hipGetLastError();
 }
 
