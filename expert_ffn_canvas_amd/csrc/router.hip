@@ -80,81 +80,80 @@ __device__ __forceinline__ uint32_t float_key(float v) {
   return (b & 0x80000000u) ? ~b : (b | 0x80000000u);
 }
 
-// Number of lanes of the wave for which `pred` holds.
-__device__ __forceinline__ int wave_count(bool pred) { return __popcll(__ballot(pred)); }
+// Bits 0..31 (lanes 0..31) or 32..63 (lanes 32..63) of a wave-wide mask: the
+// half-wave of the calling lane.
+__device__ __forceinline__ uint32_t half_mask(uint64_t m, bool hi_half) {
+  return hi_half ? (uint32_t)(m >> 32) : (uint32_t)m;
+}
 
-// Top-k of one token from its logits row in LDS (one wave, E <= 256; lane l
-// holds experts l + 64 u). A radix select on the keys finds the k-th largest
-// key t (the largest t with at least k keys >= t); the experts above t are
-// taken, and of those equal to t the lowest ids fill the remaining places.
-// The k chosen experts are then ordered by (logit desc, id asc) and their
-// softmax over the k is summed in that order.
-__device__ __forceinline__ void topk_row(const float* lrow, int E, int K, int lane, float* sel_v, int* sel_i,
-                                         int32_t* idx_out, float* w_out) {
-  const int nu = (E + 63) >> 6;
-  float v[4];
-  uint32_t key[4];
+// Top-k of two tokens per wave, one per half-wave; lane j of a half holds the
+// logits of experts j + 32 u (u < NU, E <= 32 NU), read from `row`.
+// A radix select on order-preserving keys finds the k-th largest key kt (the
+// largest value with at least k keys >= it). The experts above kt are taken,
+// and of those equal to kt the lowest ids fill the remaining places. The k
+// chosen are compacted in id order into cv/ci (LDS, 8 entries per half);
+// then lane p < k of the half ranks entry p by (logit desc, id asc) and
+// writes it to that slot, with its softmax over the k (exponentials summed in
+// id order).
+template <int NU>
+__device__ __forceinline__ void topk_half(const float* row, bool active, int E, int K, int lane, float* cv,
+                                          int* ci, int32_t* idx_out, float* w_out) {
+  const bool hi_half = lane >= 32;
+  const int j = lane & 31;
+  const uint32_t lt = (1u << j) - 1u;
+  float v[NU];
+  uint32_t key[NU];
 #pragma unroll
-  for (int u = 0; u < 4; ++u) {
-    const bool present = (u < nu) && (lane + 64 * u < E);
-    v[u] = present ? lrow[lane + 64 * u] : -INFINITY;
-    key[u] = present ? float_key(v[u]) : 0u;  // absent experts rank below every real one
+  for (int u = 0; u < NU; ++u) {
+    const int e = j + 32 * u;
+    float l = -INFINITY;
+    if (active && e < E) l = row[e];
+    v[u] = (l == l) ? l : -INFINITY;  // a NaN logit ranks last
+    key[u] = (active && e < E) ? float_key(v[u]) : 0u;  // absent experts rank below every real one
   }
-  uint32_t t = 0;
+  uint32_t kt = 0;
   for (int b = 31; b >= 0; --b) {
-    const uint32_t cand = t | (1u << b);
-    int cnt = 0;
+    const uint32_t cand = kt | (1u << b);
+    int c = 0;
 #pragma unroll
-    for (int u = 0; u < 4; ++u)
-      if (u < nu) cnt += wave_count(key[u] >= cand);
-    if (cnt >= K) t = cand;
+    for (int u = 0; u < NU; ++u) c += __popc(half_mask(__ballot(key[u] >= cand), hi_half));
+    kt = (c >= K) ? cand : kt;
   }
   int above = 0;
 #pragma unroll
-  for (int u = 0; u < 4; ++u)
-    if (u < nu) above += wave_count(key[u] > t);
-  // keys equal to t in id order: experts l + 64 u come before l + 64 (u + 1)
+  for (int u = 0; u < NU; ++u) above += __popc(half_mask(__ballot(key[u] > kt), hi_half));
   int need = K - above;
-  bool sel[4];
+  int base = 0;
 #pragma unroll
-  for (int u = 0; u < 4; ++u) {
-    const bool present = (u < nu) && (lane + 64 * u < E);
-    const bool eq = present && key[u] == t;
-    const uint64_t msk = __ballot(eq);
-    const int before = __popcll(msk & ((1ull << lane) - 1ull));
-    sel[u] = present && (key[u] > t || (eq && before < need));
-    need -= min(__popcll(msk), max(need, 0));
-  }
-  // order the chosen experts: rank = chosen ones with a larger key, or an equal key and a lower id
-  int rank[4] = {0, 0, 0, 0};
-#pragma unroll
-  for (int u2 = 0; u2 < 4; ++u2) {
-    if (u2 >= nu) break;
-    uint64_t msk = __ballot(sel[u2]);
-    while (msk) {
-      const int src = __ffsll((long long)msk) - 1;
-      msk &= msk - 1ull;
-      const uint32_t ks = __shfl(key[u2], src);
-      const int es = src + 64 * u2;
-#pragma unroll
-      for (int u = 0; u < 4; ++u) rank[u] += (ks > key[u]) || (ks == key[u] && es < lane + 64 * u);
+  for (int u = 0; u < NU; ++u) {
+    const bool eq = key[u] == kt;
+    const uint32_t me = half_mask(__ballot(eq), hi_half);
+    const bool sel = key[u] > kt || (eq && __popc(me & lt) < need);
+    need -= min(__popc(me), max(need, 0));
+    const uint32_t ms = half_mask(__ballot(sel), hi_half);
+    if (sel) {
+      const int p = base + __popc(ms & lt);
+      cv[p] = v[u];
+      ci[p] = j + 32 * u;
     }
-  }
-#pragma unroll
-  for (int u = 0; u < 4; ++u) {
-    if (sel[u]) {
-      sel_v[rank[u]] = v[u];
-      sel_i[rank[u]] = lane + 64 * u;
-    }
+    base += __popc(ms);
   }
   __builtin_amdgcn_wave_barrier();
   __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
-  if (lane < K) {
-    const float vmax = sel_v[0];
+  if (active && j < K) {
+    const float vp = cv[j];
+    const int ip = ci[j];
+    float vmax = -INFINITY;
+    int rank = 0;
+    for (int q = 0; q < K; ++q) {
+      const float vq = cv[q];
+      vmax = fmaxf(vmax, vq);
+      rank += (vq > vp) || (vq == vp && ci[q] < ip);
+    }
     float den = 0.0f;
-    for (int j = 0; j < K; ++j) den += __expf(sel_v[j] - vmax);
-    idx_out[lane] = sel_i[lane];
-    w_out[lane] = __expf(sel_v[lane] - vmax) / den;
+    for (int q = 0; q < K; ++q) den += __expf(cv[q] - vmax);
+    idx_out[rank] = ip;
+    w_out[rank] = __expf(vp - vmax) / den;
   }
 }
 
@@ -233,21 +232,22 @@ __global__ __launch_bounds__(256) void k_norm(RouterArgs a) {
 // wave h owns the 128-column chunks h, h + 8, ... of d_model. Lane
 // (m = l % 16, g = l / 16) loads, in each chunk, the 8-column pieces g, g + 4,
 // g + 8, g + 12 of token m's three z planes and of expert m's router weight:
-// the MFMA operand layouts. A wave issues the loads of up to kGroup chunks at
-// once, then multiplies. The eight partial sums are added through LDS in a
-// fixed order.
+// the MFMA operand layouts. A wave issues the loads of kGroup chunks at once
+// (a chunk past its last is re-read and multiplied by a zero weight, so the
+// loop has no branches), then multiplies. The eight partial sums are added
+// through LDS in a fixed order.
 // All expert tiles of a token tile run on one XCD (workgroup b runs on XCD
 // b % 8) and share its L2: each one publishes its logits with a counter and
-// the last to arrive ranks the full rows for the top-k.
-template <int NWP>
+// the last to arrive selects the top-k of the 16 rows.
+template <int NWP, int NU>
 __global__ __launch_bounds__(64 * kWaves) void k_logits(RouterArgs a) {
-  constexpr int kGroup = (NWP == 1) ? 3 : 1;
+  constexpr int kGroup = (NWP == 1) ? 3 : 2;
   __shared__ float part[kWaves][kTokTile][17];
-  __shared__ float lrow[kTokTile][260];
-  __shared__ float sel_v[kWaves][8];
-  __shared__ int sel_i[kWaves][8];
+  __shared__ float cv[kWaves][2][8];
+  __shared__ int ci[kWaves][2][8];
   __shared__ int is_last;
-  const int tid = threadIdx.x, lane = tid & 63, kh = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int kh = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int n_et = a.Epad / 16;
   const int n_tt = (a.T + kTokTile - 1) / kTokTile;
   const int xq = blockIdx.x % kQueues, jq = blockIdx.x / kQueues;
@@ -256,6 +256,12 @@ __global__ __launch_bounds__(64 * kWaves) void k_logits(RouterArgs a) {
   if (tt >= n_tt) return;
   const int t0 = tt * kTokTile;
   const int D = a.D;
+  // bias of this thread's output column, fetched before the long loads
+  float bias_v = 0.0f;
+  {
+    const int e = et * 16 + (tid & 15);
+    if (tid < kTokTile * 16 && a.bias != nullptr && e < a.E) bias_v = a.bias[e];
+  }
   const int m = lane & 15, g = lane >> 4;
   const int t = min(t0 + m, a.T - 1);  // rows past T re-read the last token; never stored
   const size_t plane = (size_t)a.T * D;
@@ -270,27 +276,31 @@ __global__ __launch_bounds__(64 * kWaves) void k_logits(RouterArgs a) {
     u32x4 zb[kGroup][4][3], wb[kGroup][4][NWP];
 #pragma unroll
     for (int q = 0; q < kGroup; ++q) {
-      if (c0 + q < n_my) {
-        const int col = (kh + kWaves * (c0 + q)) * kKChunk;
+      const int col = (kh + kWaves * min(c0 + q, n_my - 1)) * kKChunk;
 #pragma unroll
-        for (int kk = 0; kk < 4; ++kk) {
+      for (int kk = 0; kk < 4; ++kk) {
 #pragma unroll
-          for (int p = 0; p < 3; ++p) zb[q][kk][p] = *reinterpret_cast<const u32x4*>(zr + p * plane + col + kk * 32);
+        for (int p = 0; p < 3; ++p) zb[q][kk][p] = *reinterpret_cast<const u32x4*>(zr + p * plane + col + kk * 32);
 #pragma unroll
-          for (int p = 0; p < NWP; ++p) wb[q][kk][p] = *reinterpret_cast<const u32x4*>(wrow + p * wplane + col + kk * 32);
-        }
+        for (int p = 0; p < NWP; ++p) wb[q][kk][p] = *reinterpret_cast<const u32x4*>(wrow + p * wplane + col + kk * 32);
       }
     }
+    // keep every load of the group ahead of the first multiply: one memory
+    // round trip per group instead of one per operand
+    __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int q = 0; q < kGroup; ++q) {
-      if (c0 + q < n_my) {
+      const uint32_t keep = (c0 + q < n_my) ? 0xffffffffu : 0u;
 #pragma unroll
-        for (int kk = 0; kk < 4; ++kk)
+      for (int kk = 0; kk < 4; ++kk)
 #pragma unroll
-          for (int zp = 0; zp < 3; ++zp)
+        for (int p = 0; p < NWP; ++p) {
+          u32x4 w = wb[q][kk][p];
 #pragma unroll
-            for (int p = 0; p < NWP; ++p) acc = mfma_bf16(as_bf16x8(zb[q][kk][zp]), as_bf16x8(wb[q][kk][p]), acc);
-      }
+          for (int i = 0; i < 4; ++i) w[i] &= keep;
+#pragma unroll
+          for (int zp = 0; zp < 3; ++zp) acc = mfma_bf16(as_bf16x8(zb[q][kk][zp]), as_bf16x8(w), acc);
+        }
     }
   }
 #pragma unroll
@@ -302,9 +312,8 @@ __global__ __launch_bounds__(64 * kWaves) void k_logits(RouterArgs a) {
     float sum = part[0][mm][n];
 #pragma unroll
     for (int w = 1; w < kWaves; ++w) sum += part[w][mm][n];
-    const int e = et * 16 + n;
-    if (a.bias != nullptr && e < a.E) sum += a.bias[e];
-    if (t0 + mm < a.T) a.logits[(size_t)(t0 + mm) * a.Epad + e] = sum;
+    sum += bias_v;
+    if (t0 + mm < a.T) a.logits[(size_t)(t0 + mm) * a.Epad + et * 16 + n] = sum;
   }
   // publish: every thread's stores have reached L2 before the counter moves
   __builtin_amdgcn_s_waitcnt(0);
@@ -316,27 +325,17 @@ __global__ __launch_bounds__(64 * kWaves) void k_logits(RouterArgs a) {
   }
   __syncthreads();
   if (!is_last) return;
-  // Last expert tile of this token tile: gather the full logit rows. They come
-  // from this XCD's L2 (every writer ran on this XCD and waited for its
-  // stores); no workgroup on this CU read these rows earlier in the launch, so
-  // its L1 holds no stale copy.
-  for (int i = tid; i < kTokTile * (a.Epad / 4); i += 64 * kWaves) {
-    const int mm = i / (a.Epad / 4), c4 = i - mm * (a.Epad / 4);
-    float4 l = make_float4(-INFINITY, -INFINITY, -INFINITY, -INFINITY);
-    if (t0 + mm < a.T) l = *reinterpret_cast<const float4*>(&a.logits[(size_t)(t0 + mm) * a.Epad + 4 * c4]);
-    const float lv[4] = {l.x, l.y, l.z, l.w};
-#pragma unroll
-    for (int q = 0; q < 4; ++q)  // a NaN logit ranks last, so k valid ids are always chosen
-      lrow[mm][4 * c4 + q] = (lv[q] == lv[q]) ? lv[q] : -INFINITY;
-  }
-  __syncthreads();
-  for (int q = 0; q < kTokTile / kWaves; ++q) {
-    const int mm = kh * (kTokTile / kWaves) + q;
-    if (t0 + mm < a.T)
-      topk_row(lrow[mm], a.E, a.K, lane, sel_v[kh], sel_i[kh], a.topk_idx + (size_t)(t0 + mm) * a.K,
-               a.topk_w + (size_t)(t0 + mm) * a.K);
-    __builtin_amdgcn_wave_barrier();
-  }
+  // Last expert tile of this token tile: the full logit rows come from this
+  // XCD's L2 (every writer ran on this XCD and waited for its stores); no
+  // workgroup on this CU read these rows earlier in the launch, so its L1
+  // holds no stale copy. Wave h takes tokens t0 + 2h (lanes 0..31) and
+  // t0 + 2h + 1 (lanes 32..63).
+  const int half = lane >> 5;
+  const int tk = t0 + 2 * kh + half;
+  const bool active = tk < a.T;
+  const size_t trow = (size_t)min(tk, a.T - 1);
+  topk_half<NU>(a.logits + trow * a.Epad, active, a.E, a.K, lane, cv[kh][half], ci[kh][half],
+                a.topk_idx + trow * a.K, a.topk_w + trow * a.K);
 }
 
 // Create-time: router weight [E, D] (fp32 or bf16) -> bf16 planes [P][Epad][D],
@@ -370,10 +369,19 @@ hipError_t launch_router(const RouterArgs& a, hipStream_t stream) {
   if (e != hipSuccess) return e;
   const int n_tt = (a.T + kTokTile - 1) / kTokTile;
   const dim3 grid(kQueues * ((n_tt + kQueues - 1) / kQueues) * (a.Epad / 16));
-  if (a.n_wplanes == 3)
-    k_logits<3><<<grid, dim3(64 * kWaves), 0, stream>>>(a);
-  else
-    k_logits<1><<<grid, dim3(64 * kWaves), 0, stream>>>(a);
+  const dim3 block(64 * kWaves);
+  const int nu = a.Epad / 32;  // 1 .. 8
+  if (a.n_wplanes == 3) {
+    if (nu <= 1) k_logits<3, 1><<<grid, block, 0, stream>>>(a);
+    else if (nu <= 2) k_logits<3, 2><<<grid, block, 0, stream>>>(a);
+    else if (nu <= 4) k_logits<3, 4><<<grid, block, 0, stream>>>(a);
+    else k_logits<3, 8><<<grid, block, 0, stream>>>(a);
+  } else {
+    if (nu <= 1) k_logits<1, 1><<<grid, block, 0, stream>>>(a);
+    else if (nu <= 2) k_logits<1, 2><<<grid, block, 0, stream>>>(a);
+    else if (nu <= 4) k_logits<1, 4><<<grid, block, 0, stream>>>(a);
+    else k_logits<1, 8><<<grid, block, 0, stream>>>(a);
+  }
   return hipGetLastError();
 }
 
