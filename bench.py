@@ -4,7 +4,8 @@
 One step = one dg_moe_forward over one batch of T tokens: router, permutation, gate_up grouped GEMM,
 down grouped GEMM and combine, on inputs already resident in HBM. The default workload is one layer
 over a 256-token canvas, bf16, with the Zipf-skewed router bias; the weights rotate over several
-resident copies so that no cache holds them from one step to the next.
+resident copies so that no cache holds them from one step to the next. The expert weights are packed at
+create into the GEMMs' fragment order (--borrow reads them in place, row-major).
 
 Prints one JSON line: tokens/s, the roofline of the dominant kernel (gate_up, HBM-bound) measured with
 HIP events on the launch stream, and the CPU oracle timed on the host on a bounded sample.
@@ -142,6 +143,8 @@ def main():
     ap.add_argument("--rotate", type=int, default=4, help="resident weight copies cycled through")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-profile", action="store_true", help="skip the per-kernel event pass")
+    ap.add_argument("--borrow", action="store_true",
+                    help="borrow the expert weights in their row-major layout instead of packing them at create")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="also run a plain device copy of this many MiB (3 times), so that a counter run "
                          "records HBM bytes for a transfer of known size")
@@ -175,7 +178,7 @@ def main():
         sets = [base] + [{k: (None if v is None else v.clone()) for k, v in base.items()}
                          for _ in range(max(args.rotate, 1) - 1)]
         rotate = len(sets)
-    layers = [dgmoe.MoELayer(w, max_tokens=T, act_dtype=act, top_k=wl.K) for w in sets]
+    layers = [dgmoe.MoELayer(w, max_tokens=T, act_dtype=act, top_k=wl.K, pack=not args.borrow) for w in sets]
     out = torch.empty((T, wl.D), dtype=act, device=dev)
     bufs = [torch.empty_like(x), torch.empty_like(x)]
     deltas = inp["deltas"]
@@ -273,7 +276,8 @@ def main():
         "data": "synthetic",
         "config": {"workload": wl.name, "T": T, "n_experts": wl.E, "top_k": wl.K, "d_model": wl.D,
                    "d_ff": wl.F, "experts": wl.experts, "act": wl.act, "router_bias": wl.bias or "none",
-                   "layers": n_layers, "weight_copies_rotated": rotate},
+                   "layers": n_layers, "weight_copies_rotated": rotate,
+                   "expert_weights": "borrowed row-major" if args.borrow else "packed at create"},
         "roofline": roofline,
         "layer": {"alg_bytes": layer_bytes * n_layers, "alg_flops": flops * n_layers,
                   "achieved_GBps": round(layer_gbps, 1), "hbm_frac": round(layer_gbps / HBM_PEAK_GBPS, 4),

@@ -123,6 +123,7 @@ struct dg_moe_s {
   int device;
   char* ws;           // workspace + prepared router parameters
   void* packed;       // expert weights copied at create (pack mode), else null
+  int w_packed = 0;   // bf16 weights in the panel-fragment layout
   const void* w_gate_up;
   const void* w_down;
   const uint16_t* s_gate_up;
@@ -238,9 +239,19 @@ dg_status dg_moe_create(const dg_moe_config* cfg, const dg_moe_weights* w, void*
     hd->s_down = i4 ? reinterpret_cast<const uint16_t*>(p + round_up(eb.gu, 256) + round_up(eb.dn, 256) +
                                                         round_up(eb.sgu, 256))
                     : nullptr;
-    hipError_t c1 = hipMemcpyAsync(const_cast<void*>(hd->w_gate_up), w->w_gate_up, eb.gu, hipMemcpyDeviceToDevice, stream);
-    hipError_t c2 = hipMemcpyAsync(const_cast<void*>(hd->w_down), w->w_down, eb.dn, hipMemcpyDeviceToDevice, stream);
-    hipError_t c3 = hipSuccess, c4 = hipSuccess;
+    hipError_t c1, c2, c3 = hipSuccess, c4 = hipSuccess;
+    if (i4) {
+      c1 = hipMemcpyAsync(const_cast<void*>(hd->w_gate_up), w->w_gate_up, eb.gu, hipMemcpyDeviceToDevice, stream);
+      c2 = hipMemcpyAsync(const_cast<void*>(hd->w_down), w->w_down, eb.dn, hipMemcpyDeviceToDevice, stream);
+    } else {  // bf16: MFMA fragment order, 1 KB per wave-wide read
+      c1 = dg::launch_pack_panels(static_cast<const uint16_t*>(w->w_gate_up),
+                                  static_cast<uint16_t*>(const_cast<void*>(hd->w_gate_up)), cfg->n_experts,
+                                  2 * cfg->d_ff, cfg->d_model, stream);
+      c2 = dg::launch_pack_panels(static_cast<const uint16_t*>(w->w_down),
+                                  static_cast<uint16_t*>(const_cast<void*>(hd->w_down)), cfg->n_experts,
+                                  cfg->d_model, cfg->d_ff, stream);
+      hd->w_packed = 1;
+    }
     if (i4) {
       c3 = hipMemcpyAsync(const_cast<uint16_t*>(hd->s_gate_up), w->s_gate_up, eb.sgu, hipMemcpyDeviceToDevice, stream);
       c4 = hipMemcpyAsync(const_cast<uint16_t*>(hd->s_down), w->s_down, eb.sdn, hipMemcpyDeviceToDevice, stream);
@@ -363,6 +374,7 @@ static dg_status run_forward(dg_moe_handle hd, const void* x, void* out, int32_t
   ga.h = ra.h;
   ga.w_gate_up = hd->w_gate_up;
   ga.w_down = hd->w_down;
+  ga.w_packed = hd->w_packed;
   ga.s_gate_up = hd->s_gate_up;
   ga.s_down = hd->s_down;
   ga.act = hd->at<uint16_t>(L.act);

@@ -60,13 +60,21 @@ __device__ __forceinline__ void wait_vmcnt() {
   __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
 }
 
+// Element offset of column k (a multiple of 32) inside a lane's weight
+// stream: row-major rows advance one element per column; the packed panel
+// layout advances one 1 KB block (512 elements) per 32 columns.
+template <bool PK>
+__device__ __forceinline__ int koff(int k) {
+  return PK ? 16 * k : k;
+}
+
 // Weight panels of one K step: NS sub-steps of 32.
-template <int NS>
+template <bool PK, int NS>
 __device__ __forceinline__ void load_w(const uint16_t* w0, const uint16_t* w1, int k0, Panels& p) {
 #pragma unroll
   for (int s = 0; s < NS; ++s) {
-    p.b0[s] = *reinterpret_cast<const u32x4*>(w0 + k0 + 32 * s);
-    p.b1[s] = *reinterpret_cast<const u32x4*>(w1 + k0 + 32 * s);
+    p.b0[s] = *reinterpret_cast<const u32x4*>(w0 + koff<PK>(k0 + 32 * s));
+    p.b1[s] = *reinterpret_cast<const u32x4*>(w1 + koff<PK>(k0 + 32 * s));
   }
 }
 
@@ -148,13 +156,13 @@ __device__ __forceinline__ void lds_barrier() {
 // One step with NS sub-steps, issued after the previous one: DMA of the
 // activation rows into stage (it + 1) & 1, then the weight panels into `nxt`,
 // then the MFMAs of step `it` (NSP sub-steps) from `cur`.
-template <int NMT, int NS, int NSP>
+template <bool PK, int NMT, int NS, int NSP>
 __device__ __forceinline__ void step(char* As, const uint16_t* const (&rowp)[kDmaInstr], const uint16_t* w0,
                                      const uint16_t* w1, int k1, int it, int wave, int lane, const Panels& cur,
                                      Panels& nxt, f32x4 (&acc0)[kBMT], f32x4 (&acc1)[kBMT]) {
   dma_a<NMT, NS * 4>(As + ((it + 1) & 1) * kStageBytes, rowp, k1, wave, lane);
   __builtin_amdgcn_sched_barrier(0);
-  load_w<NS>(w0, w1, k1, nxt);
+  load_w<PK, NS>(w0, w1, k1, nxt);
   __builtin_amdgcn_sched_barrier(0);
   mma_step<NMT, NSP>(As + (it & 1) * kStageBytes, lane, cur, acc0, acc1);
   wait_vmcnt<2 * NS>();  // this wave's DMA has landed; its weight loads may still fly
@@ -162,7 +170,7 @@ __device__ __forceinline__ void step(char* As, const uint16_t* const (&rowp)[kDm
 }
 
 // The last full step `last` (panels in `cur`) and the short tail, if any.
-template <int NMT>
+template <bool PK, int NMT>
 __device__ __forceinline__ void finish(char* As, const uint16_t* const (&rowp)[kDmaInstr], const uint16_t* w0,
                                        const uint16_t* w1, int nfull, int ntail, int wave, int lane,
                                        const Panels& cur, Panels& nxt, f32x4 (&acc0)[kBMT], f32x4 (&acc1)[kBMT]) {
@@ -172,7 +180,7 @@ __device__ __forceinline__ void finish(char* As, const uint16_t* const (&rowp)[k
   if (ntail == 0) {
     mma_step<NMT, kNS>(As + (last & 1) * kStageBytes, lane, cur, acc0, acc1);
   } else {  // one 64-wide step remains (K % 128 == 64)
-    step<NMT, 2, kNS>(As, rowp, w0, w1, k1, last, wave, lane, cur, nxt, acc0, acc1);
+    step<PK, NMT, 2, kNS>(As, rowp, w0, w1, k1, last, wave, lane, cur, nxt, acc0, acc1);
     wait_vmcnt<0>();
     mma_step<NMT, 2>(tail_stage, lane, nxt, acc0, acc1);
   }
@@ -181,7 +189,7 @@ __device__ __forceinline__ void finish(char* As, const uint16_t* const (&rowp)[k
 // The K loop of one tile with NMT 16-row MFMA tiles. K is a multiple of 64.
 // Two panel buffers alternate roles (the loop is unrolled by two) so that no
 // register copies are needed between steps.
-template <int NMT>
+template <bool PK, int NMT>
 __device__ __forceinline__ void k_loop(char* As, const uint16_t* const (&rowp)[kDmaInstr], const uint16_t* w0,
                                        const uint16_t* w1, int K, int tid, f32x4 (&acc0)[kBMT],
                                        f32x4 (&acc1)[kBMT]) {
@@ -192,7 +200,7 @@ __device__ __forceinline__ void k_loop(char* As, const uint16_t* const (&rowp)[k
   if (nfull == 0) {
     // K = 64: one short step only
     dma_a<NMT, 8>(As, rowp, 0, wave, lane);
-    load_w<2>(w0, w1, 0, p0);
+    load_w<PK, 2>(w0, w1, 0, p0);
     wait_vmcnt<0>();
     lds_barrier();
     mma_step<NMT, 2>(As, lane, p0, acc0, acc1);
@@ -200,25 +208,25 @@ __device__ __forceinline__ void k_loop(char* As, const uint16_t* const (&rowp)[k
   }
   dma_a<NMT, kSegs>(As, rowp, 0, wave, lane);
   __builtin_amdgcn_sched_barrier(0);
-  load_w<kNS>(w0, w1, 0, p0);
+  load_w<PK, kNS>(w0, w1, 0, p0);
   wait_vmcnt<2 * kNS>();
   lds_barrier();
   int it = 0;
   for (; it + 2 < nfull; it += 2) {
-    step<NMT, kNS, kNS>(As, rowp, w0, w1, (it + 1) * kKS, it, wave, lane, p0, p1, acc0, acc1);
-    step<NMT, kNS, kNS>(As, rowp, w0, w1, (it + 2) * kKS, it + 1, wave, lane, p1, p0, acc0, acc1);
+    step<PK, NMT, kNS, kNS>(As, rowp, w0, w1, (it + 1) * kKS, it, wave, lane, p0, p1, acc0, acc1);
+    step<PK, NMT, kNS, kNS>(As, rowp, w0, w1, (it + 2) * kKS, it + 1, wave, lane, p1, p0, acc0, acc1);
   }
   if (it + 2 == nfull) {
-    step<NMT, kNS, kNS>(As, rowp, w0, w1, (it + 1) * kKS, it, wave, lane, p0, p1, acc0, acc1);
-    finish<NMT>(As, rowp, w0, w1, nfull, ntail, wave, lane, p1, p0, acc0, acc1);
+    step<PK, NMT, kNS, kNS>(As, rowp, w0, w1, (it + 1) * kKS, it, wave, lane, p0, p1, acc0, acc1);
+    finish<PK, NMT>(As, rowp, w0, w1, nfull, ntail, wave, lane, p1, p0, acc0, acc1);
   } else {
-    finish<NMT>(As, rowp, w0, w1, nfull, ntail, wave, lane, p0, p1, acc0, acc1);
+    finish<PK, NMT>(As, rowp, w0, w1, nfull, ntail, wave, lane, p0, p1, acc0, acc1);
   }
 }
 
 // Three workgroups per CU (waves_per_eu 3): the register budget that keeps
 // two K steps of weight panels per wave in flight without spilling.
-template <bool GATE_UP>
+template <bool GATE_UP, bool PK>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3, 3))) void k_gemm_bf16(GemmArgs a) {
   __shared__ __attribute__((aligned(16))) char As[2 * kStageBytes];
   const int F = a.F, D = a.D;
@@ -247,12 +255,26 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3, 3))
   const uint16_t* w1;
   if (GATE_UP) {
     col = nb * 16 * kWaves + wave * 16 + (lane & 15);
-    w0 = static_cast<const uint16_t*>(a.w_gate_up) + ((size_t)tl.e * 2 * F + col) * D + g * 8;
-    w1 = w0 + (size_t)F * D;
+    const uint16_t* W = static_cast<const uint16_t*>(a.w_gate_up);
+    if (PK) {  // gate panel nb * kWaves + wave, up panel F / 16 later
+      const int p = nb * kWaves + wave;
+      w0 = W + ((size_t)tl.e * (2 * F / 16) + p) * (size_t)(D / 32) * 512 + lane * 8;
+      w1 = w0 + (size_t)(F / 16) * (D / 32) * 512;
+    } else {
+      w0 = W + ((size_t)tl.e * 2 * F + col) * D + g * 8;
+      w1 = w0 + (size_t)F * D;
+    }
   } else {
     col = nb * 32 * kWaves + wave * 32 + (lane & 15);
-    w0 = static_cast<const uint16_t*>(a.w_down) + ((size_t)tl.e * D + col) * F + g * 8;
-    w1 = w0 + (size_t)16 * F;
+    const uint16_t* W = static_cast<const uint16_t*>(a.w_down);
+    if (PK) {  // panels 2 (nb * kWaves + wave) and the next
+      const int p = 2 * (nb * kWaves + wave);
+      w0 = W + ((size_t)tl.e * (D / 16) + p) * (size_t)(F / 32) * 512 + lane * 8;
+      w1 = w0 + (size_t)(F / 32) * 512;
+    } else {
+      w0 = W + ((size_t)tl.e * D + col) * F + g * 8;
+      w1 = w0 + (size_t)16 * F;
+    }
   }
 
   f32x4 acc0[kBMT], acc1[kBMT];
@@ -262,10 +284,10 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3, 3))
     acc1[i] = f32x4{0.f, 0.f, 0.f, 0.f};
   }
   switch (nmt) {
-    case 1: k_loop<1>(As, rowp, w0, w1, K, tid, acc0, acc1); break;
-    case 2: k_loop<2>(As, rowp, w0, w1, K, tid, acc0, acc1); break;
-    case 3: k_loop<3>(As, rowp, w0, w1, K, tid, acc0, acc1); break;
-    default: k_loop<4>(As, rowp, w0, w1, K, tid, acc0, acc1); break;
+    case 1: k_loop<PK, 1>(As, rowp, w0, w1, K, tid, acc0, acc1); break;
+    case 2: k_loop<PK, 2>(As, rowp, w0, w1, K, tid, acc0, acc1); break;
+    case 3: k_loop<PK, 3>(As, rowp, w0, w1, K, tid, acc0, acc1); break;
+    default: k_loop<PK, 4>(As, rowp, w0, w1, K, tid, acc0, acc1); break;
   }
 
 #pragma unroll
@@ -289,15 +311,43 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3, 3))
   }
 }
 
+// One workgroup per block of 64 lanes x 16 bytes: block b = (e, p, s).
+__global__ __launch_bounds__(256) void k_pack_panels(const uint16_t* __restrict__ src, uint16_t* __restrict__ dst,
+                                                     int E, int R, int K) {
+  const int nks = K / 32, np = R / 16;
+  const size_t nblk = (size_t)E * np * nks;
+  const int lane = threadIdx.x & 63;
+  for (size_t b = (size_t)blockIdx.x * 4 + (threadIdx.x >> 6); b < nblk; b += (size_t)gridDim.x * 4) {
+    const int s = (int)(b % nks);
+    const size_t ep = b / nks;  // e * np + p
+    const size_t row = ep * 16 + (lane & 15);
+    const int k = 32 * s + 8 * (lane >> 4);
+    *reinterpret_cast<u32x4*>(dst + b * 512 + lane * 8) = *reinterpret_cast<const u32x4*>(src + row * K + k);
+  }
+}
+
 }  // namespace
 
+hipError_t launch_pack_panels(const uint16_t* src, uint16_t* dst, int E, int R, int K, hipStream_t stream) {
+  k_pack_panels<<<dim3(4096), dim3(256), 0, stream>>>(src, dst, E, R, K);
+  return hipGetLastError();
+}
+
 hipError_t launch_gate_up_bf16(const GemmArgs& a, hipStream_t stream) {
-  k_gemm_bf16<true><<<dim3(kQueues * a.qmax * (a.F / (16 * kWaves))), dim3(kThreads), 0, stream>>>(a);
+  const dim3 grid(kQueues * a.qmax * (a.F / (16 * kWaves)));
+  if (a.w_packed)
+    k_gemm_bf16<true, true><<<grid, dim3(kThreads), 0, stream>>>(a);
+  else
+    k_gemm_bf16<true, false><<<grid, dim3(kThreads), 0, stream>>>(a);
   return hipGetLastError();
 }
 
 hipError_t launch_down_bf16(const GemmArgs& a, hipStream_t stream) {
-  k_gemm_bf16<false><<<dim3(kQueues * a.qmax * (a.D / (32 * kWaves))), dim3(kThreads), 0, stream>>>(a);
+  const dim3 grid(kQueues * a.qmax * (a.D / (32 * kWaves)));
+  if (a.w_packed)
+    k_gemm_bf16<false, true><<<grid, dim3(kThreads), 0, stream>>>(a);
+  else
+    k_gemm_bf16<false, false><<<grid, dim3(kThreads), 0, stream>>>(a);
   return hipGetLastError();
 }
 

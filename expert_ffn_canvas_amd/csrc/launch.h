@@ -72,7 +72,14 @@ struct GemmArgs {
   uint16_t* act;           // [K T, F] gelu_tanh(gate) * up, expert-sorted rows
   float* y;                // [K T, D] w * down(act), expert-sorted rows
   int D, F;
+  int w_packed;            // bf16 weights in the panel-fragment layout of launch_pack_panels
 };
+// Create-time relayout of bf16 expert weights [E][R][K] (R % 16 == 0,
+// K % 32 == 0) into MFMA fragment order: 1 KB block (e, p, s) holds, at lane
+// l = n + 16 g, the 8 values W[e][16 p + n][32 s + 8 g .. + 7]; blocks are
+// ordered e-major, then p, then s. A wave reading one B-operand fragment of a
+// 16-row panel then reads 1 KB contiguously.
+hipError_t launch_pack_panels(const uint16_t* src, uint16_t* dst, int E, int R, int K, hipStream_t stream);
 hipError_t launch_gate_up_bf16(const GemmArgs& a, hipStream_t stream);
 hipError_t launch_down_bf16(const GemmArgs& a, hipStream_t stream);
 hipError_t launch_gate_up_i4(const GemmArgs& a, hipStream_t stream);

@@ -65,7 +65,9 @@ typedef enum dg_status {
 
 /* dg_moe_config.flags */
 #define DG_MOE_PACK_WEIGHTS 0x1u /* copy the expert weights into handle-owned
-                                    memory at create (else borrow the caller's) */
+                                    memory at create (else borrow the caller's);
+                                    bf16 experts are rearranged into the matrix-core
+                                    fragment order, which the GEMMs stream faster */
 
 /* dg_moe_forward flags */
 #define DG_FWD_ADD_INPUT 0x1u /* out = x + MoE(x) (+ addend) */
@@ -114,7 +116,9 @@ typedef struct dg_moe_s* dg_moe_handle;
  * workspace for config->max_tokens (so dg_moe_forward never allocates), and
  * prepares the router weight. In borrow mode (default) the expert weight
  * pointers are kept and must stay valid and unmodified for the handle's
- * lifetime; with DG_MOE_PACK_WEIGHTS they are copied. router_gamma,
+ * lifetime; with DG_MOE_PACK_WEIGHTS they are copied (bf16 experts in
+ * 16-row panels of 1 KB fragment blocks; int4 experts as given), after which
+ * the caller's expert buffers are no longer read. router_gamma,
  * router_bias and ffn_gamma are always copied. Work is enqueued on `stream`
  * and the call synchronises that stream before returning.
  * Errors: DG_ERR_INVALID_ARG (null cfg/weights/out, wrong struct_size),

@@ -44,12 +44,13 @@ def canvas256():
     (16, 4, 256, 128, 70, "f32", "f32"),
     (40, 8, 384, 192, 129, "bf16", "f32"),
 ])
-def test_small_shapes(E, K, D, F, T, act, rw):
-    _say(f"small E={E} K={K} D={D} F={F} T={T} act={act} router={rw}")
+@pytest.mark.parametrize("pack", [False, True], ids=["borrow", "pack"])
+def test_small_shapes(E, K, D, F, T, act, rw, pack):
+    _say(f"small E={E} K={K} D={D} F={F} T={T} act={act} router={rw} pack={pack}")
     wl = synth.small_workload(T=T, E=E, K=K, D=D, F=F, act=act, router_w=rw, bias="zipf", seed=E + T)
     inp = synth.make_inputs(wl, device="cuda")
     w = inp["layers"][0]
-    layer = _layer(w, T, _act(wl), K=K)
+    layer = _layer(w, T, _act(wl), K=K, pack=pack)
     r = layer_parity(layer, inp["x"], oracle_weights(w), K)
     print(f"err {r['err']:.3e} near-ties {r['near_ties']}")
 
