@@ -28,7 +28,7 @@ HBM_PEAK_GBPS = 8000.0         # MI355X HBM3E
 BF16_PEAK_TFLOPS = 2500.0      # MI355X dense bf16 MFMA
 F16_PEAK_TFLOPS = 2500.0
 COUNTERS_FILE = os.path.join(ROOT, "profiles", "gate_up_counters.txt")
-KERNEL_NAMES = ("router", "permute", "gate_up", "down", "combine")
+KERNEL_NAMES = ("norm", "logits_topk", "permute", "gate_up", "down", "combine")
 
 
 class HipEvents:
@@ -231,17 +231,18 @@ def main():
     kern_us = None
     n_prof = 0 if (args.no_profile or wl.layers > 1) else min(args.steps, 100)
     if n_prof:
-        evs = ev.create(6 * n_prof)
+        nk = len(KERNEL_NAMES)
+        evs = ev.create(2 * nk * n_prof)
         for i in range(n_prof):
             layer = layers[i % rotate]
             st = dgmoe.dg_moe_forward_profiled(layer.handle, x.data_ptr(), out.data_ptr(), T, None, 0,
-                                               evs[6 * i:6 * i + 6], sp)
+                                               evs[2 * nk * i:2 * nk * (i + 1)], sp)
             assert st == 0, dgmoe.dg_moe_last_error()
         torch.cuda.synchronize()
-        tot = [0.0] * 5
+        tot = [0.0] * nk
         for i in range(n_prof):
-            for k in range(5):
-                tot[k] += ev.elapsed_ms(evs[6 * i + k], evs[6 * i + k + 1])
+            for k in range(nk):
+                tot[k] += ev.elapsed_ms(evs[2 * nk * i + 2 * k], evs[2 * nk * i + 2 * k + 1])
         kern_us = {name: round(tot[k] / n_prof * 1e3, 2) for k, name in enumerate(KERNEL_NAMES)}
         ev.destroy(evs)
     ev.destroy([e0, e1])

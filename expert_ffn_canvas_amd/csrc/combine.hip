@@ -59,13 +59,9 @@ __global__ __launch_bounds__(kThreads) void k_combine(CombineArgs a) {
 
 }  // namespace
 
-hipError_t launch_combine(const CombineArgs& a, hipStream_t stream) {
+hipError_t launch_combine(const CombineArgs& a, hipStream_t stream, const KernelEvents* ev) {
   const dim3 grid(a.T * ((a.D + kCols - 1) / kCols));
-  if (a.act_f32)
-    k_combine<true><<<grid, dim3(kThreads), 0, stream>>>(a);
-  else
-    k_combine<false><<<grid, dim3(kThreads), 0, stream>>>(a);
-  return hipGetLastError();
+  return launch_kernel(a.act_f32 ? k_combine<true> : k_combine<false>, grid, dim3(kThreads), stream, ev, a);
 }
 
 }  // namespace dg

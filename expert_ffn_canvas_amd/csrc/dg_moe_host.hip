@@ -317,10 +317,14 @@ static dg_status run_forward(dg_moe_handle hd, const void* x, void* out, int32_t
   hipStream_t stream = static_cast<hipStream_t>(stream_v);
   const Layout& L = hd->L;
   const bool i4 = c.expert_w_dtype == DG_I4G128;
-  auto mark = [&](int i) -> hipError_t {
-    return events ? hipEventRecord(static_cast<hipEvent_t>(events[i]), stream) : hipSuccess;
-  };
-  if (mark(0) != hipSuccess) return fail(DG_ERR_HIP, "hipEventRecord");
+  // per-kernel start/stop events: norm, logits, permute, gate_up, down, combine
+  dg::KernelEvents kev[6];
+  if (events)
+    for (int i = 0; i < 6; ++i) {
+      kev[i].start = static_cast<hipEvent_t>(events[2 * i]);
+      kev[i].stop = static_cast<hipEvent_t>(events[2 * i + 1]);
+    }
+  auto ev = [&](int i) -> const dg::KernelEvents* { return events ? &kev[i] : nullptr; };
 
   dg::RouterArgs ra{};
   ra.x = x;
@@ -343,9 +347,8 @@ static dg_status run_forward(dg_moe_handle hd, const void* x, void* out, int32_t
   ra.tile_count = hd->at<int32_t>(L.tile_count);
   ra.topk_idx = hd->at<int32_t>(L.topk_idx);
   ra.topk_w = hd->at<float>(L.topk_w);
-  hipError_t e = dg::launch_router(ra, stream);
+  hipError_t e = dg::launch_router(ra, stream, ev(0));
   if (e != hipSuccess) return hip_fail(e, "router launch");
-  if ((e = mark(1)) != hipSuccess) return hip_fail(e, "hipEventRecord");
 
   dg::PermuteArgs pa{};
   pa.topk_idx = ra.topk_idx;
@@ -361,9 +364,8 @@ static dg_status run_forward(dg_moe_handle hd, const void* x, void* out, int32_t
   pa.sorted_token = hd->at<int32_t>(L.sorted_token);
   pa.row_w = hd->at<float>(L.row_w);
   pa.row_of_slot = hd->at<int32_t>(L.row_of_slot);
-  e = dg::launch_permute(pa, stream);
+  e = dg::launch_permute(pa, stream, ev(2));
   if (e != hipSuccess) return hip_fail(e, "permute launch");
-  if ((e = mark(2)) != hipSuccess) return hip_fail(e, "hipEventRecord");
 
   dg::GemmArgs ga{};
   ga.tiles = pa.tiles;
@@ -381,12 +383,10 @@ static dg_status run_forward(dg_moe_handle hd, const void* x, void* out, int32_t
   ga.y = hd->at<float>(L.y);
   ga.D = c.d_model;
   ga.F = c.d_ff;
-  e = i4 ? dg::launch_gate_up_i4(ga, stream) : dg::launch_gate_up_bf16(ga, stream);
+  e = i4 ? dg::launch_gate_up_i4(ga, stream, ev(3)) : dg::launch_gate_up_bf16(ga, stream, ev(3));
   if (e != hipSuccess) return hip_fail(e, "gate_up launch");
-  if ((e = mark(3)) != hipSuccess) return hip_fail(e, "hipEventRecord");
-  e = i4 ? dg::launch_down_i4(ga, stream) : dg::launch_down_bf16(ga, stream);
+  e = i4 ? dg::launch_down_i4(ga, stream, ev(4)) : dg::launch_down_bf16(ga, stream, ev(4));
   if (e != hipSuccess) return hip_fail(e, "down launch");
-  if ((e = mark(4)) != hipSuccess) return hip_fail(e, "hipEventRecord");
 
   dg::CombineArgs ca{};
   ca.y = ga.y;
@@ -398,9 +398,8 @@ static dg_status run_forward(dg_moe_handle hd, const void* x, void* out, int32_t
   ca.addend = addend;
   ca.out = out;
   ca.act_f32 = c.act_dtype == DG_F32;
-  e = dg::launch_combine(ca, stream);
+  e = dg::launch_combine(ca, stream, ev(5));
   if (e != hipSuccess) return hip_fail(e, "combine launch");
-  if ((e = mark(5)) != hipSuccess) return hip_fail(e, "hipEventRecord");
 
   if (dbg) {
     const size_t tk = (size_t)T * c.top_k;
@@ -431,7 +430,7 @@ dg_status dg_moe_forward(dg_moe_handle hd, const void* x, void* out, int32_t T, 
 dg_status dg_moe_forward_profiled(dg_moe_handle hd, const void* x, void* out, int32_t T, const void* addend,
                                   uint32_t flags, void* const* events, void* stream) {
   if (!events) return fail(DG_ERR_INVALID_ARG, "events is NULL");
-  for (int i = 0; i < 6; ++i)
+  for (int i = 0; i < 12; ++i)
     if (!events[i]) return fail(DG_ERR_INVALID_ARG, "events[%d] is NULL", i);
   if (T <= 0) return fail(DG_ERR_SHAPE, "profiled forward needs T > 0");
   return run_forward(hd, x, out, T, addend, flags, nullptr, events, stream);

@@ -333,22 +333,16 @@ hipError_t launch_pack_panels(const uint16_t* src, uint16_t* dst, int E, int R, 
   return hipGetLastError();
 }
 
-hipError_t launch_gate_up_bf16(const GemmArgs& a, hipStream_t stream) {
+hipError_t launch_gate_up_bf16(const GemmArgs& a, hipStream_t stream, const KernelEvents* ev) {
   const dim3 grid(kQueues * a.qmax * (a.F / (16 * kWaves)));
-  if (a.w_packed)
-    k_gemm_bf16<true, true><<<grid, dim3(kThreads), 0, stream>>>(a);
-  else
-    k_gemm_bf16<true, false><<<grid, dim3(kThreads), 0, stream>>>(a);
-  return hipGetLastError();
+  return launch_kernel(a.w_packed ? k_gemm_bf16<true, true> : k_gemm_bf16<true, false>, grid, dim3(kThreads), stream,
+                       ev, a);
 }
 
-hipError_t launch_down_bf16(const GemmArgs& a, hipStream_t stream) {
+hipError_t launch_down_bf16(const GemmArgs& a, hipStream_t stream, const KernelEvents* ev) {
   const dim3 grid(kQueues * a.qmax * (a.D / (32 * kWaves)));
-  if (a.w_packed)
-    k_gemm_bf16<false, true><<<grid, dim3(kThreads), 0, stream>>>(a);
-  else
-    k_gemm_bf16<false, false><<<grid, dim3(kThreads), 0, stream>>>(a);
-  return hipGetLastError();
+  return launch_kernel(a.w_packed ? k_gemm_bf16<false, true> : k_gemm_bf16<false, false>, grid, dim3(kThreads),
+                       stream, ev, a);
 }
 
 }  // namespace dg

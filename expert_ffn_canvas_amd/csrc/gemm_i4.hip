@@ -300,14 +300,12 @@ __global__ __launch_bounds__(kThreads) void k_down_i4(GemmArgs a) {
 
 }  // namespace
 
-hipError_t launch_gate_up_i4(const GemmArgs& a, hipStream_t stream) {
-  k_gate_up_i4<<<dim3(kQueues * a.qmax * (a.F / 64)), dim3(kThreads), 0, stream>>>(a);
-  return hipGetLastError();
+hipError_t launch_gate_up_i4(const GemmArgs& a, hipStream_t stream, const KernelEvents* ev) {
+  return launch_kernel(k_gate_up_i4, dim3(kQueues * a.qmax * (a.F / 64)), dim3(kThreads), stream, ev, a);
 }
 
-hipError_t launch_down_i4(const GemmArgs& a, hipStream_t stream) {
-  k_down_i4<<<dim3(kQueues * a.qmax * (a.D / 128)), dim3(kThreads), 0, stream>>>(a);
-  return hipGetLastError();
+hipError_t launch_down_i4(const GemmArgs& a, hipStream_t stream, const KernelEvents* ev) {
+  return launch_kernel(k_down_i4, dim3(kQueues * a.qmax * (a.D / 128)), dim3(kThreads), stream, ev, a);
 }
 
 }  // namespace dg

@@ -2,10 +2,26 @@
 // enqueues work on `stream` and returns the launch status; none synchronises.
 #pragma once
 
+#include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
 namespace dg {
+
+// Optional start/stop events of one kernel, stamped by the dispatch itself
+// (hipExtLaunchKernel), so they time exactly that kernel.
+struct KernelEvents {
+  hipEvent_t start = nullptr, stop = nullptr;
+};
+
+// Launch of a kernel that takes one argument struct, with optional events.
+template <typename Arg>
+inline hipError_t launch_kernel(void (*kernel)(Arg), dim3 grid, dim3 block, hipStream_t stream,
+                                const KernelEvents* ev, const Arg& arg) {
+  void* args[1] = {const_cast<Arg*>(&arg)};
+  return hipExtLaunchKernel(reinterpret_cast<const void*>(kernel), grid, block, args, 0, stream,
+                            ev ? ev->start : nullptr, ev ? ev->stop : nullptr, 0);
+}
 
 struct Tile;
 
@@ -39,7 +55,8 @@ struct RouterArgs {
   int32_t* topk_idx;    // [T, K]
   float* topk_w;        // [T, K]
 };
-hipError_t launch_router(const RouterArgs& a, hipStream_t stream);
+// ev: null, or the events of the norm and the logits kernels (two entries).
+hipError_t launch_router(const RouterArgs& a, hipStream_t stream, const KernelEvents* ev);
 hipError_t launch_prep_router_w(const void* w, int w_f32, int E, int Epad, int D, uint16_t* planes,
                                 hipStream_t stream);
 
@@ -56,7 +73,7 @@ struct PermuteArgs {
   float* row_w;           // [K T]
   int32_t* row_of_slot;   // [K T]
 };
-hipError_t launch_permute(const PermuteArgs& a, hipStream_t stream);
+hipError_t launch_permute(const PermuteArgs& a, hipStream_t stream, const KernelEvents* ev);
 
 struct GemmArgs {
   const Tile* tiles;
@@ -80,10 +97,10 @@ struct GemmArgs {
 // ordered e-major, then p, then s. A wave reading one B-operand fragment of a
 // 16-row panel then reads 1 KB contiguously.
 hipError_t launch_pack_panels(const uint16_t* src, uint16_t* dst, int E, int R, int K, hipStream_t stream);
-hipError_t launch_gate_up_bf16(const GemmArgs& a, hipStream_t stream);
-hipError_t launch_down_bf16(const GemmArgs& a, hipStream_t stream);
-hipError_t launch_gate_up_i4(const GemmArgs& a, hipStream_t stream);
-hipError_t launch_down_i4(const GemmArgs& a, hipStream_t stream);
+hipError_t launch_gate_up_bf16(const GemmArgs& a, hipStream_t stream, const KernelEvents* ev);
+hipError_t launch_down_bf16(const GemmArgs& a, hipStream_t stream, const KernelEvents* ev);
+hipError_t launch_gate_up_i4(const GemmArgs& a, hipStream_t stream, const KernelEvents* ev);
+hipError_t launch_down_i4(const GemmArgs& a, hipStream_t stream, const KernelEvents* ev);
 
 struct CombineArgs {
   const float* y;
@@ -94,6 +111,6 @@ struct CombineArgs {
   void* out;
   int act_f32;
 };
-hipError_t launch_combine(const CombineArgs& a, hipStream_t stream);
+hipError_t launch_combine(const CombineArgs& a, hipStream_t stream, const KernelEvents* ev);
 
 }  // namespace dg

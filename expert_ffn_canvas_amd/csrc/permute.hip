@@ -193,9 +193,8 @@ __global__ __launch_bounds__(kThreads) void k_permute(PermuteArgs a) {
 
 }  // namespace
 
-hipError_t launch_permute(const PermuteArgs& a, hipStream_t stream) {
-  k_permute<<<dim3(1), dim3(kThreads), 0, stream>>>(a);
-  return hipGetLastError();
+hipError_t launch_permute(const PermuteArgs& a, hipStream_t stream, const KernelEvents* ev) {
+  return launch_kernel(k_permute, dim3(1), dim3(kThreads), stream, ev, a);
 }
 
 }  // namespace dg

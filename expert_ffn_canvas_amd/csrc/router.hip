@@ -360,29 +360,19 @@ __global__ void k_prep_router_w(const void* __restrict__ w, int w_f32, int E, in
 
 }  // namespace
 
-hipError_t launch_router(const RouterArgs& a, hipStream_t stream) {
-  if (a.x_f32)
-    k_norm<true><<<dim3(a.T), dim3(256), 0, stream>>>(a);
-  else
-    k_norm<false><<<dim3(a.T), dim3(256), 0, stream>>>(a);
-  hipError_t e = hipGetLastError();
+hipError_t launch_router(const RouterArgs& a, hipStream_t stream, const KernelEvents* ev) {
+  hipError_t e = launch_kernel(a.x_f32 ? k_norm<true> : k_norm<false>, dim3(a.T), dim3(256), stream,
+                               ev ? &ev[0] : nullptr, a);
   if (e != hipSuccess) return e;
   const int n_tt = (a.T + kTokTile - 1) / kTokTile;
   const dim3 grid(kQueues * ((n_tt + kQueues - 1) / kQueues) * (a.Epad / 16));
-  const dim3 block(64 * kWaves);
   const int nu = a.Epad / 32;  // 1 .. 8
-  if (a.n_wplanes == 3) {
-    if (nu <= 1) k_logits<3, 1><<<grid, block, 0, stream>>>(a);
-    else if (nu <= 2) k_logits<3, 2><<<grid, block, 0, stream>>>(a);
-    else if (nu <= 4) k_logits<3, 4><<<grid, block, 0, stream>>>(a);
-    else k_logits<3, 8><<<grid, block, 0, stream>>>(a);
-  } else {
-    if (nu <= 1) k_logits<1, 1><<<grid, block, 0, stream>>>(a);
-    else if (nu <= 2) k_logits<1, 2><<<grid, block, 0, stream>>>(a);
-    else if (nu <= 4) k_logits<1, 4><<<grid, block, 0, stream>>>(a);
-    else k_logits<1, 8><<<grid, block, 0, stream>>>(a);
-  }
-  return hipGetLastError();
+  void (*k)(RouterArgs);
+  if (a.n_wplanes == 3)
+    k = nu <= 1 ? k_logits<3, 1> : nu <= 2 ? k_logits<3, 2> : nu <= 4 ? k_logits<3, 4> : k_logits<3, 8>;
+  else
+    k = nu <= 1 ? k_logits<1, 1> : nu <= 2 ? k_logits<1, 2> : nu <= 4 ? k_logits<1, 4> : k_logits<1, 8>;
+  return launch_kernel(k, grid, dim3(64 * kWaves), stream, ev ? &ev[1] : nullptr, a);
 }
 
 hipError_t launch_prep_router_w(const void* w, int w_f32, int E, int Epad, int D, uint16_t* planes,

@@ -112,8 +112,10 @@ def dg_moe_forward_debug(handle, x: int, out: int, T: int, dbg: dg_moe_debug, st
 
 def dg_moe_forward_profiled(handle, x: int, out: int, T: int, addend: int | None, flags: int, events,
                             stream: int) -> int:
-    """events: sequence of six hipEvent_t handles (ints)."""
-    arr = (ctypes.c_void_p * 6)(*events)
+    """events: sequence of twelve hipEvent_t handles (ints): start/stop of each of the six kernels."""
+    if len(events) != 12:
+        raise ValueError("dg_moe_forward_profiled takes 12 events")
+    arr = (ctypes.c_void_p * 12)(*events)
     return _lib.dg_moe_forward_profiled(handle, x, out, T, addend, flags, arr, ctypes.c_void_p(stream))
 
 

@@ -144,11 +144,14 @@ dg_status dg_moe_forward(dg_moe_handle h, const void* x, void* out, int32_t T, c
 dg_status dg_moe_forward_debug(dg_moe_handle h, const void* x, void* out, int32_t T,
                                const dg_moe_debug* dbg, void* stream);
 
-/* Measurement entry point: dg_moe_forward that also records six caller-created
- * hipEvent_t (passed as void*) on `stream`: events[0] before the router,
- * [1] before the permutation, [2] before the gate_up GEMM, [3] before the down
- * GEMM, [4] before the combine and [5] after it, so that the caller can read
- * each kernel's duration with hipEventElapsedTime. T must be > 0. */
+/* Measurement entry point: dg_moe_forward whose six kernel launches also
+ * stamp twelve caller-created hipEvent_t (passed as void*): events[2 i] at the
+ * start and events[2 i + 1] at the end of kernel i, in launch order: the
+ * norm, the router logits / top-k, the permutation, the gate_up GEMM, the down
+ * GEMM and the combine. The events are recorded by the kernel dispatches
+ * themselves (hipExtLaunchKernel), so hipEventElapsedTime(events[2 i],
+ * events[2 i + 1]) is that kernel's own duration. T must be > 0; every event
+ * must be non-NULL (else DG_ERR_INVALID_ARG, nothing launched). */
 dg_status dg_moe_forward_profiled(dg_moe_handle h, const void* x, void* out, int32_t T, const void* addend,
                                   uint32_t flags, void* const* events, void* stream);
 

@@ -287,3 +287,40 @@ def test_stack30_teacher_forced():
               f"touched {(r['dbg']['counts'].cpu().numpy() > 0).sum()}")
     for layer in layers:
         layer.close()
+
+
+def test_profiled_forward_times_each_kernel(canvas256):
+    import ctypes
+    wl, x, w, wn = canvas256
+    _say("profiled forward: 12 dispatch-stamped events")
+    hip = ctypes.CDLL("libamdhip64.so.7")
+    hip.hipEventCreate.argtypes = [ctypes.POINTER(ctypes.c_void_p)]
+    hip.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p, ctypes.c_void_p]
+    hip.hipEventDestroy.argtypes = [ctypes.c_void_p]
+    evs = []
+    for _ in range(12):
+        e = ctypes.c_void_p()
+        assert hip.hipEventCreate(ctypes.byref(e)) == 0
+        evs.append(e.value)
+    layer = _layer(w, wl.T, torch.bfloat16)
+    out = torch.empty_like(x)
+    sp = torch.cuda.current_stream().cuda_stream
+    ref = layer.forward(x)
+    st = dgmoe.dg_moe_forward_profiled(layer.handle, x.data_ptr(), out.data_ptr(), wl.T, None, 0, evs, sp)
+    assert st == 0, dgmoe.dg_moe_last_error()
+    torch.cuda.synchronize()
+    assert torch.equal(out.view(torch.int16), ref.view(torch.int16))
+    ms = []
+    for k in range(6):
+        t = ctypes.c_float()
+        assert hip.hipEventElapsedTime(ctypes.byref(t), evs[2 * k], evs[2 * k + 1]) == 0
+        ms.append(t.value)
+    print("kernel ms", [round(v, 4) for v in ms])
+    assert all(v > 0 for v in ms)
+    # a NULL event is rejected before anything is launched
+    bad = list(evs)
+    bad[7] = None
+    assert dgmoe.dg_moe_forward_profiled(layer.handle, x.data_ptr(), out.data_ptr(), wl.T, None, 0, bad, sp) == \
+        dgmoe.DG_ERR_INVALID_ARG
+    for e in evs:
+        hip.hipEventDestroy(e)
