@@ -12,13 +12,14 @@ typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
-// One routed tile of an expert: rows row0 .. row0+mc-1 of the expert-sorted
-// order, all belonging to expert e.
+// One task of a grouped GEMM: rows row0 .. row0+mc-1 of the expert-sorted
+// order (all routed to expert e, mc <= 64) times column block nb of that
+// expert's weight.
 struct Tile {
   int e;
   int row0;
   int mc;
-  int pad;
+  int nb;
 };
 
 constexpr int kWave = 64;

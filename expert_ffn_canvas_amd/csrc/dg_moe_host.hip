@@ -49,10 +49,11 @@ size_t act_elem_bytes(int dt) { return dt == DG_F32 ? 4 : 2; }
 
 // Sub-buffer layout of the workspace (byte offsets from the base).
 struct Layout {
-  size_t h, z, logits, tile_count, topk_idx, topk_w, counts, offsets, tiles, qlen, sorted_token, row_w, row_of_slot, act, y;
+  size_t h, z, logits, tile_count, topk_idx, topk_w, counts, offsets, tasks[2], qlen, sorted_token, row_w, row_of_slot, act,
+      y;
   size_t wr, gamma_r, bias, gamma_e;
   size_t total;
-  int Epad, n_wplanes, qmax;
+  int Epad, n_wplanes, nb[2], qmax[2];  // per GEMM (gate_up, down): column blocks, queue capacity
 };
 
 Layout plan(const dg_moe_config& c) {
@@ -61,7 +62,9 @@ Layout plan(const dg_moe_config& c) {
   const size_t E = (size_t)c.n_experts, K = (size_t)c.top_k;
   L.Epad = (int)round_up(E, 32);
   L.n_wplanes = (c.router_w_dtype == DG_F32) ? 3 : 1;
-  L.qmax = dg::max_queue_len((int)T, (int)K, (int)E);
+  L.nb[0] = dg::gate_up_blocks((int)F);
+  L.nb[1] = dg::down_blocks((int)D);
+  for (int g = 0; g < 2; ++g) L.qmax[g] = dg::max_queue_len((int)T, (int)K, (int)E, L.nb[g]);
   size_t off = 0;
   auto take = [&](size_t bytes) {
     const size_t at = off;
@@ -76,8 +79,8 @@ Layout plan(const dg_moe_config& c) {
   L.topk_w = take(T * K * 4);
   L.counts = take(E * 4);
   L.offsets = take((E + 1) * 4);
-  L.tiles = take((size_t)L.qmax * dg::kQueues * sizeof(dg::Tile));
-  L.qlen = take(dg::kQueues * 4);
+  for (int g = 0; g < 2; ++g) L.tasks[g] = take((size_t)L.qmax[g] * dg::kQueues * sizeof(dg::Tile));
+  L.qlen = take(2 * dg::kQueues * 4);
   L.sorted_token = take(K * T * 4);
   L.row_w = take(K * T * 4);
   L.row_of_slot = take(K * T * 4);
@@ -356,10 +359,13 @@ static dg_status run_forward(dg_moe_handle hd, const void* x, void* out, int32_t
   pa.T = T;
   pa.K = c.top_k;
   pa.E = c.n_experts;
-  pa.qmax = dg::max_queue_len(T, c.top_k, c.n_experts);
+  for (int g = 0; g < 2; ++g) {
+    pa.nb[g] = L.nb[g];
+    pa.qmax[g] = dg::max_queue_len(T, c.top_k, c.n_experts, L.nb[g]);
+    pa.tasks[g] = hd->at<dg::Tile>(L.tasks[g]);
+  }
   pa.counts = hd->at<int32_t>(L.counts);
   pa.offsets = hd->at<int32_t>(L.offsets);
-  pa.tiles = hd->at<dg::Tile>(L.tiles);
   pa.qlen = hd->at<int32_t>(L.qlen);
   pa.sorted_token = hd->at<int32_t>(L.sorted_token);
   pa.row_w = hd->at<float>(L.row_w);
@@ -368,9 +374,9 @@ static dg_status run_forward(dg_moe_handle hd, const void* x, void* out, int32_t
   if (e != hipSuccess) return hip_fail(e, "permute launch");
 
   dg::GemmArgs ga{};
-  ga.tiles = pa.tiles;
+  ga.tiles = pa.tasks[0];
   ga.qlen = pa.qlen;
-  ga.qmax = pa.qmax;
+  ga.qmax = pa.qmax[0];
   ga.sorted_token = pa.sorted_token;
   ga.row_w = pa.row_w;
   ga.h = ra.h;
@@ -385,6 +391,9 @@ static dg_status run_forward(dg_moe_handle hd, const void* x, void* out, int32_t
   ga.F = c.d_ff;
   e = i4 ? dg::launch_gate_up_i4(ga, stream, ev(3)) : dg::launch_gate_up_bf16(ga, stream, ev(3));
   if (e != hipSuccess) return hip_fail(e, "gate_up launch");
+  ga.tiles = pa.tasks[1];
+  ga.qlen = pa.qlen + dg::kQueues;
+  ga.qmax = pa.qmax[1];
   e = i4 ? dg::launch_down_i4(ga, stream, ev(4)) : dg::launch_down_bf16(ga, stream, ev(4));
   if (e != hipSuccess) return hip_fail(e, "down launch");
 

@@ -25,9 +25,9 @@
 // the tile re-read its last row), so the next step's loads stay in flight
 // across the current step's MFMAs.
 //
-// Work distribution: workgroup b takes queue b % 8 (its XCD) and, within it,
-// entry (b / 8) / NB and column block (b / 8) % NB; the permutation kernel
-// balanced the queues and put all tiles of one expert into one queue.
+// Work distribution: workgroup b takes task b / 8 of queue b % 8 (its XCD); the
+// permutation kernel balanced the queues and put the tiles that share a
+// weight block into one queue, next to each other.
 #include "dg_common.h"
 #include "launch.h"
 
@@ -230,14 +230,12 @@ template <bool GATE_UP, bool PK>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3, 3))) void k_gemm_bf16(GemmArgs a) {
   __shared__ __attribute__((aligned(16))) char As[2 * kStageBytes];
   const int F = a.F, D = a.D;
-  const int NB = GATE_UP ? F / (16 * kWaves) : D / (32 * kWaves);
   const int K = GATE_UP ? D : F;
   const int qx = blockIdx.x & (kQueues - 1);
   const int j = blockIdx.x / kQueues;
-  const int q = j / NB;
-  const int nb = j - q * NB;
-  if (q >= a.qlen[qx]) return;
-  const Tile tl = a.tiles[(size_t)q * kQueues + qx];
+  if (j >= a.qlen[qx]) return;
+  const Tile tl = a.tiles[(size_t)j * kQueues + qx];
+  const int nb = tl.nb;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int g = lane >> 4;
   const int nmt = (tl.mc + 15) >> 4;
@@ -334,13 +332,13 @@ hipError_t launch_pack_panels(const uint16_t* src, uint16_t* dst, int E, int R, 
 }
 
 hipError_t launch_gate_up_bf16(const GemmArgs& a, hipStream_t stream, const KernelEvents* ev) {
-  const dim3 grid(kQueues * a.qmax * (a.F / (16 * kWaves)));
+  const dim3 grid(kQueues * a.qmax);
   return launch_kernel(a.w_packed ? k_gemm_bf16<true, true> : k_gemm_bf16<true, false>, grid, dim3(kThreads), stream,
                        ev, a);
 }
 
 hipError_t launch_down_bf16(const GemmArgs& a, hipStream_t stream, const KernelEvents* ev) {
-  const dim3 grid(kQueues * a.qmax * (a.D / (32 * kWaves)));
+  const dim3 grid(kQueues * a.qmax);
   return launch_kernel(a.w_packed ? k_gemm_bf16<false, true> : k_gemm_bf16<false, false>, grid, dim3(kThreads),
                        stream, ev, a);
 }

@@ -15,7 +15,7 @@
 // multiplied by its scale in fp32. So every weight enters as exactly (q - 8) s.
 //
 // Work distribution as in the bf16 kernels: workgroup b takes queue b % 8 (its
-// XCD), entry (b / 8) / NB and column block (b / 8) % NB.
+// XCD), task b / 8 of that queue (a tile and a column block).
 //
 // Lane layout: lane (n = l % 16, g = l / 16) loads 16 bytes = 32 codes of
 // row n covering inputs 32 g .. 32 g + 31 of a 128-input group; dword s of that
@@ -84,13 +84,11 @@ __device__ __forceinline__ void store_a(uint16_t* lds, const uint16_t* const (&s
 __global__ __launch_bounds__(kThreads) void k_gate_up_i4(GemmArgs a) {
   __shared__ __attribute__((aligned(16))) uint16_t As[2][kTileRows * kPitch];
   const int F = a.F, D = a.D;
-  const int NB = F / 64;
   const int qx = blockIdx.x & (kQueues - 1);
   const int jq = blockIdx.x / kQueues;
-  const int q = jq / NB;
-  const int fb = jq - q * NB;
-  if (q >= a.qlen[qx]) return;
-  const Tile tl = a.tiles[(size_t)q * kQueues + qx];
+  if (jq >= a.qlen[qx]) return;
+  const Tile tl = a.tiles[(size_t)jq * kQueues + qx];
+  const int fb = tl.nb;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int nmt = (tl.mc + 15) >> 4;
   const int seg = tid & 15;
@@ -189,13 +187,11 @@ __global__ __launch_bounds__(kThreads) void k_gate_up_i4(GemmArgs a) {
 __global__ __launch_bounds__(kThreads) void k_down_i4(GemmArgs a) {
   __shared__ __attribute__((aligned(16))) uint16_t As[2][kTileRows * kPitch];
   const int F = a.F, D = a.D;
-  const int NB = D / 128;
   const int qx = blockIdx.x & (kQueues - 1);
   const int jq = blockIdx.x / kQueues;
-  const int q = jq / NB;
-  const int nb = jq - q * NB;
-  if (q >= a.qlen[qx]) return;
-  const Tile tl = a.tiles[(size_t)q * kQueues + qx];
+  if (jq >= a.qlen[qx]) return;
+  const Tile tl = a.tiles[(size_t)jq * kQueues + qx];
+  const int nb = tl.nb;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int nmt = (tl.mc + 15) >> 4;
   const int seg = tid & 15;
@@ -301,11 +297,11 @@ __global__ __launch_bounds__(kThreads) void k_down_i4(GemmArgs a) {
 }  // namespace
 
 hipError_t launch_gate_up_i4(const GemmArgs& a, hipStream_t stream, const KernelEvents* ev) {
-  return launch_kernel(k_gate_up_i4, dim3(kQueues * a.qmax * (a.F / 64)), dim3(kThreads), stream, ev, a);
+  return launch_kernel(k_gate_up_i4, dim3(kQueues * a.qmax), dim3(kThreads), stream, ev, a);
 }
 
 hipError_t launch_down_i4(const GemmArgs& a, hipStream_t stream, const KernelEvents* ev) {
-  return launch_kernel(k_down_i4, dim3(kQueues * a.qmax * (a.D / 128)), dim3(kThreads), stream, ev, a);
+  return launch_kernel(k_down_i4, dim3(kQueues * a.qmax), dim3(kThreads), stream, ev, a);
 }
 
 }  // namespace dg

@@ -27,15 +27,23 @@ struct Tile;
 
 // Largest number of rows one tile holds (four 16-row MFMA tiles).
 constexpr int kTileRows = 64;
-// Tiles are spread over this many queues, one per XCD: queue x holds the
-// tiles that workgroups with blockIdx % kQueues == x process.
+// GEMM tasks are spread over this many queues, one per XCD: queue x holds the
+// tasks that workgroups with blockIdx % kQueues == x process.
 constexpr int kQueues = 8;
 
-// Upper bound on the length of one tile queue for T tokens.
-inline int max_queue_len(int T, int K, int E) {
-  const int max_tiles = (K * T + kTileRows - 1) / kTileRows + E;
-  return (max_tiles + kQueues - 1) / kQueues + (T + kTileRows - 1) / kTileRows;
+// Upper bound on the length of one task queue of a GEMM with NB column blocks
+// for T tokens: the tasks are dealt round robin in units of non-increasing
+// size, so no queue exceeds the mean by more than the largest unit (an
+// expert's tile count, at most ceil(T / 64)).
+inline int max_queue_len(int T, int K, int E, int NB) {
+  const long max_tiles = ((long)K * T + kTileRows - 1) / kTileRows + E;
+  return (int)(((long)NB * max_tiles + kQueues - 1) / kQueues + (T + kTileRows - 1) / kTileRows);
 }
+
+// Column blocks of the two GEMMs: gate_up tasks cover 64 features (their gate
+// and up rows), down tasks 128 outputs.
+inline int gate_up_blocks(int F) { return F / 64; }
+inline int down_blocks(int D) { return D / 128; }
 
 struct RouterArgs {
   const void* x;        // [T, D] fp32 or bf16
@@ -64,11 +72,12 @@ struct PermuteArgs {
   const int32_t* topk_idx;
   const float* topk_w;
   int T, K, E;
-  int qmax;               // capacity of each tile queue
+  int nb[2];              // column blocks of gate_up and down
+  int qmax[2];            // capacity of each queue of gate_up and down
   int32_t* counts;        // [E]
   int32_t* offsets;       // [E + 1]
-  Tile* tiles;            // [qmax][kQueues]: tile p of queue x at tiles[p * kQueues + x]
-  int32_t* qlen;          // [kQueues]
+  Tile* tasks[2];         // [qmax][kQueues] each: task p of queue x at tasks[p * kQueues + x]
+  int32_t* qlen;          // [2][kQueues]
   int32_t* sorted_token;  // [K T]
   float* row_w;           // [K T]
   int32_t* row_of_slot;   // [K T]
@@ -76,9 +85,9 @@ struct PermuteArgs {
 hipError_t launch_permute(const PermuteArgs& a, hipStream_t stream, const KernelEvents* ev);
 
 struct GemmArgs {
-  const Tile* tiles;
-  const int32_t* qlen;
-  int qmax;
+  const Tile* tiles;       // this GEMM's task queues
+  const int32_t* qlen;     // [kQueues] their lengths
+  int qmax;                // their capacity
   const int32_t* sorted_token;
   const float* row_w;
   const uint16_t* h;       // [T, D] expert input (bf16, or fp16 for int4 experts)

@@ -2,12 +2,15 @@
 //  * counts[e]: tokens routed to expert e (their sum is k T);
 //  * offsets: exclusive prefix sum of counts (the rows of expert e are
 //    offsets[e] .. offsets[e+1]-1 in expert-sorted order);
-//  * tiles: each expert's rows cut into ceil(count / 64) tiles of near-equal
-//    size. Experts are ranked by count (descending, ties to the lower id) and
-//    dealt to the 8 per-XCD queues in snake order (0..7, 7..0, ...), all tiles
-//    of one expert into one queue, so every queue gets a similar share of the
-//    weight bytes and the tiles of a split expert run on one XCD, where they
-//    share that XCD's L2;
+//  * the task queues of the two grouped GEMMs. Each expert's rows are cut
+//    into ceil(count / 64) tiles of near-equal size; a task is one tile times
+//    one column block of the expert's weight. Units (expert, column block),
+//    each holding all tiles of that expert for that block, are ranked by
+//    expert (count descending, ties to the lower id), then block, and dealt
+//    round robin to the 8 per-XCD queues. So the tiles that read the same
+//    weight block run together on one XCD and share its L2, and since the
+//    unit sizes never grow along the deal, every queue holds the mean load
+//    to within one unit;
 //  * the stable scatter: the rows of expert e hold its tokens in increasing
 //    token order; sorted_token[row], row_w[row] (that slot's routing weight)
 //    and row_of_slot[t k + j].
@@ -27,10 +30,8 @@ constexpr int kThreads = 1024;
 constexpr int kMaxE = 256;
 constexpr int kWords = kThreads / 32;  // bitmap words per expert for one chunk of tokens
 
-__device__ __forceinline__ int snake_queue(int r) {
-  const int k = r / kQueues, p = r - k * kQueues;
-  return (k & 1) ? (kQueues - 1 - p) : p;
-}
+// Number of v in [0, m) with v % kQueues == x (m >= 0, 0 <= x < kQueues).
+__device__ __forceinline__ int n_mod(int m, int x) { return m > x ? (m - x + kQueues - 1) / kQueues : 0; }
 
 __global__ __launch_bounds__(kThreads) void k_permute(PermuteArgs a) {
   __shared__ int cnt[kMaxE];
@@ -40,6 +41,7 @@ __global__ __launch_bounds__(kThreads) void k_permute(PermuteArgs a) {
   __shared__ int ntile[kMaxE];
   __shared__ int ctot[kMaxE];
   __shared__ int wsum[kMaxE / 64];
+  __shared__ int pq[2][kQueues][kMaxE + 1];  // per GEMM and queue: load of the ranks before r
   __shared__ uint32_t bits[kMaxE * kWords];
   __shared__ uint16_t pre[kMaxE * kWords];
 
@@ -111,36 +113,60 @@ __global__ __launch_bounds__(kThreads) void k_permute(PermuteArgs a) {
   }
   __syncthreads();
 
-  // --- deal the experts to the queues and write their tiles
-  if (tid < E) {
-    const int e = order[tid];  // thread tid handles the expert of rank tid
-    const int r = tid;
-    const int x = snake_queue(r);
-    int qoff = 0;
-    for (int k = 0; k < r / kQueues; ++k) {
-      const int rr = k * kQueues + ((k & 1) ? (kQueues - 1 - x) : x);
-      qoff += ntile[order[rr]];
+  // --- per GEMM g and queue x, the load that the units of experts ranked
+  // before r put into x: wave w = 8 g + x scans 4 ranks per lane. Expert rank
+  // r owns units r NB .. r NB + NB - 1; unit u goes to queue u % 8 and holds
+  // ntile tasks.
+  {
+    const int g = wave >> 3, x = wave & 7;
+    const int NB = a.nb[g];
+    int v[4], run = 0;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int r = 4 * lane + i;
+      v[i] = (r < E) ? ntile[order[r]] * (n_mod((r + 1) * NB, x) - n_mod(r * NB, x)) : 0;
+      run += v[i];
     }
-    const int ce = cnt[e], nt = ntile[e];
-    for (int i = 0; i < nt; ++i) {
-      const int lo = (ce * i) / nt, hi = (ce * (i + 1)) / nt;
-      if (qoff + i < a.qmax) {
+    int incl = run;
+    for (int d = 1; d < 64; d <<= 1) {
+      const int o = __shfl_up(incl, d);
+      if (lane >= d) incl += o;
+    }
+    int before = incl - run;
+    if (lane == 0) pq[g][x][0] = 0;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      before += v[i];
+      pq[g][x][4 * lane + i + 1] = before;  // load of ranks 0 .. 4 lane + i
+    }
+  }
+  __syncthreads();
+  if (tid < 2 * kQueues) {
+    const int g = tid / kQueues, x = tid % kQueues;
+    a.qlen[tid] = min(pq[g][x][E], a.qmax[g]);
+  }
+  // --- the tasks of every unit
+#pragma unroll
+  for (int g = 0; g < 2; ++g) {
+    const int NB = a.nb[g];
+    for (int u = tid; u < E * NB; u += kThreads) {
+      const int r = u / NB, nb = u - r * NB;
+      const int e = order[r], nt = ntile[e];
+      if (nt == 0) continue;
+      const int x = u % kQueues;
+      const int qoff = pq[g][x][r] + nt * (n_mod(u, x) - n_mod(r * NB, x));
+      const int ce = cnt[e];
+      for (int i = 0; i < nt; ++i) {
+        if (qoff + i >= a.qmax[g]) break;
+        const int lo = (ce * i) / nt, hi = (ce * (i + 1)) / nt;
         Tile tl;
         tl.e = e;
         tl.row0 = base[e] + lo;
         tl.mc = hi - lo;
-        tl.pad = 0;
-        a.tiles[(size_t)(qoff + i) * kQueues + x] = tl;
+        tl.nb = nb;
+        a.tasks[g][(size_t)(qoff + i) * kQueues + x] = tl;
       }
     }
-  }
-  if (tid < kQueues) {
-    int len = 0;
-    for (int k = 0; k * kQueues < E; ++k) {
-      const int rr = k * kQueues + ((k & 1) ? (kQueues - 1 - tid) : tid);
-      if (rr < E) len += ntile[order[rr]];
-    }
-    a.qlen[tid] = min(len, a.qmax);
   }
 
   // --- stable scatter, kThreads tokens at a time
