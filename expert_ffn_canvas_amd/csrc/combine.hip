@@ -1,9 +1,10 @@
 // Weighted combine back to token order on gfx950:
-//   out[t] = sum_j y[row_of_slot[t k + j]]  (+ x[t]) (+ addend[t])
-// where each y row already carries its routing weight. The k slots are summed
-// in their routing order (logit descending), always in the same order, so the
-// result is bit-reproducible; the sum is fp32 and the output is rounded once
-// (round-to-nearest-even for bf16).
+//   out[t] = sum_j w[t, j] y[row_of_slot[t k + j]]  (+ x[t]) (+ addend[t])
+// with w the routing weights and y the expert outputs of the slots. The k
+// slots are accumulated (fused multiply-add, fp32) in their routing order
+// (logit descending), always in the same order, so the result is
+// bit-reproducible; the output is rounded once (round-to-nearest-even for
+// bf16).
 #include "dg_common.h"
 #include "launch.h"
 
@@ -23,15 +24,23 @@ __global__ __launch_bounds__(kThreads) void k_combine(CombineArgs a) {
   const int t = blockIdx.x / n_chunk;
   const int c = (blockIdx.x - t * n_chunk) * kCols + threadIdx.x * 4;
   int rows[8];
+  float w[8];
 #pragma unroll
-  for (int j = 0; j < 8; ++j) rows[j] = (j < K) ? a.row_of_slot[(size_t)t * K + j] : 0;
+  for (int j = 0; j < 8; ++j) {
+    rows[j] = (j < K) ? a.row_of_slot[(size_t)t * K + j] : 0;
+    w[j] = (j < K) ? a.topk_w[(size_t)t * K + j] : 0.0f;
+  }
   if (c < D) {
-    float4 s = *reinterpret_cast<const float4*>(a.y + (size_t)rows[0] * D + c);
+    const float4 v0 = *reinterpret_cast<const float4*>(a.y + (size_t)rows[0] * D + c);
+    float4 s = make_float4(w[0] * v0.x, w[0] * v0.y, w[0] * v0.z, w[0] * v0.w);
 #pragma unroll
     for (int j = 1; j < 8; ++j) {
       if (j < K) {
         const float4 v = *reinterpret_cast<const float4*>(a.y + (size_t)rows[j] * D + c);
-        s.x += v.x; s.y += v.y; s.z += v.z; s.w += v.w;
+        s.x = fmaf(w[j], v.x, s.x);
+        s.y = fmaf(w[j], v.y, s.y);
+        s.z = fmaf(w[j], v.z, s.z);
+        s.w = fmaf(w[j], v.w, s.w);
       }
     }
     const void* extra[2] = {a.x, a.addend};

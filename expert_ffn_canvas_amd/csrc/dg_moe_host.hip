@@ -49,7 +49,7 @@ size_t act_elem_bytes(int dt) { return dt == DG_F32 ? 4 : 2; }
 
 // Sub-buffer layout of the workspace (byte offsets from the base).
 struct Layout {
-  size_t h, z, logits, tile_count, topk_idx, topk_w, counts, offsets, tasks[2], qlen, sorted_token, row_w, row_of_slot, act,
+  size_t h, z, logits, tile_count, topk_idx, topk_w, counts, offsets, tasks[2], qlen, sorted_slot, row_of_slot, act,
       y;
   size_t wr, gamma_r, bias, gamma_e;
   size_t total;
@@ -81,8 +81,7 @@ Layout plan(const dg_moe_config& c) {
   L.offsets = take((E + 1) * 4);
   for (int g = 0; g < 2; ++g) L.tasks[g] = take((size_t)L.qmax[g] * dg::kQueues * sizeof(dg::Tile));
   L.qlen = take(2 * dg::kQueues * 4);
-  L.sorted_token = take(K * T * 4);
-  L.row_w = take(K * T * 4);
+  L.sorted_slot = take(K * T * 4);
   L.row_of_slot = take(K * T * 4);
   L.act = take(K * T * F * 2);
   L.y = take(K * T * D * 4);
@@ -355,7 +354,6 @@ static dg_status run_forward(dg_moe_handle hd, const void* x, void* out, int32_t
 
   dg::PermuteArgs pa{};
   pa.topk_idx = ra.topk_idx;
-  pa.topk_w = ra.topk_w;
   pa.T = T;
   pa.K = c.top_k;
   pa.E = c.n_experts;
@@ -367,8 +365,7 @@ static dg_status run_forward(dg_moe_handle hd, const void* x, void* out, int32_t
   pa.counts = hd->at<int32_t>(L.counts);
   pa.offsets = hd->at<int32_t>(L.offsets);
   pa.qlen = hd->at<int32_t>(L.qlen);
-  pa.sorted_token = hd->at<int32_t>(L.sorted_token);
-  pa.row_w = hd->at<float>(L.row_w);
+  pa.sorted_slot = hd->at<int32_t>(L.sorted_slot);
   pa.row_of_slot = hd->at<int32_t>(L.row_of_slot);
   e = dg::launch_permute(pa, stream, ev(2));
   if (e != hipSuccess) return hip_fail(e, "permute launch");
@@ -377,8 +374,8 @@ static dg_status run_forward(dg_moe_handle hd, const void* x, void* out, int32_t
   ga.tiles = pa.tasks[0];
   ga.qlen = pa.qlen;
   ga.qmax = pa.qmax[0];
-  ga.sorted_token = pa.sorted_token;
-  ga.row_w = pa.row_w;
+  ga.sorted_slot = pa.sorted_slot;
+  ga.K = c.top_k;
   ga.h = ra.h;
   ga.w_gate_up = hd->w_gate_up;
   ga.w_down = hd->w_down;
@@ -399,6 +396,7 @@ static dg_status run_forward(dg_moe_handle hd, const void* x, void* out, int32_t
 
   dg::CombineArgs ca{};
   ca.y = ga.y;
+  ca.topk_w = ra.topk_w;
   ca.row_of_slot = pa.row_of_slot;
   ca.T = T;
   ca.K = c.top_k;
@@ -420,7 +418,7 @@ static dg_status run_forward(dg_moe_handle hd, const void* x, void* out, int32_t
                {dbg->topk_w, L.topk_w, tk * 4},
                {dbg->counts, L.counts, (size_t)c.n_experts * 4},
                {dbg->offsets, L.offsets, (size_t)(c.n_experts + 1) * 4},
-               {dbg->sorted_token, L.sorted_token, tk * 4},
+               {dbg->sorted_slot, L.sorted_slot, tk * 4},
                {dbg->row_of_slot, L.row_of_slot, tk * 4}};
     for (const Cp& cp : cps) {
       if (!cp.dst) continue;

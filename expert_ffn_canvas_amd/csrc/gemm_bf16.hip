@@ -5,7 +5,8 @@
 //           u = h W_up[e]^T over the full d_model, then act = gelu_tanh(g) * u
 //           (bf16).
 //  down:    for each tile and each block of 128 d_model outputs:
-//           y = row_w * (act W_down[e]^T) in fp32, one row per routed slot.
+//           y = act W_down[e]^T in fp32, one row per routed slot (the combine
+//           applies the routing weights).
 //
 // Shapes (auto-round PR "Add quantization support for DiffusionGemma",
 // transformers backend test log, expert module dump): gate_proj and up_proj
@@ -246,7 +247,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3, 3))
 #pragma unroll
   for (int i = 0; i < kDmaInstr; ++i) {
     const int r = min(kDmaRows * (wave + kWaves * i) + lane / kSegs, tl.mc - 1);
-    rowp[i] = GATE_UP ? a.h + (size_t)a.sorted_token[tl.row0 + r] * D : a.act + (size_t)(tl.row0 + r) * F;
+    rowp[i] = GATE_UP ? a.h + (size_t)(a.sorted_slot[tl.row0 + r] / a.K) * D : a.act + (size_t)(tl.row0 + r) * F;
   }
   int col;  // gate_up: feature f; down: first output d
   const uint16_t* w0;
@@ -298,10 +299,9 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3, 3))
           if (GATE_UP) {
             a.act[(size_t)(tl.row0 + r) * F + col] = f32_to_bf16_bits(gelu_tanh(acc0[mt][i]) * acc1[mt][i]);
           } else {
-            const float w = a.row_w[tl.row0 + r];
             float* yr = a.y + (size_t)(tl.row0 + r) * D + col;
-            yr[0] = w * acc0[mt][i];
-            yr[16] = w * acc1[mt][i];
+            yr[0] = acc0[mt][i];
+            yr[16] = acc1[mt][i];
           }
         }
       }

@@ -97,7 +97,7 @@ __global__ __launch_bounds__(kThreads) void k_gate_up_i4(GemmArgs a) {
 #pragma unroll
   for (int p = 0; p < kAPass; ++p) {
     const int r = (tid >> 4) + 16 * p;
-    src[p] = (r < tl.mc) ? a.h + (size_t)a.sorted_token[tl.row0 + r] * D + seg * 8 : nullptr;
+    src[p] = (r < tl.mc) ? a.h + (size_t)(a.sorted_slot[tl.row0 + r] / a.K) * D + seg * 8 : nullptr;
   }
   const int G = D / kSlab;
   const int f = fb * 64 + wave * 16 + (lane & 15);
@@ -284,10 +284,9 @@ __global__ __launch_bounds__(kThreads) void k_down_i4(GemmArgs a) {
       for (int i = 0; i < 4; ++i) {
         const int r = mt * 16 + g * 4 + i;
         if (r < tl.mc) {
-          const float w = a.row_w[tl.row0 + r];
           float* yr = a.y + (size_t)(tl.row0 + r) * D + d0;
-          yr[0] = w * acc0[mt][i];
-          yr[16] = w * acc1[mt][i];
+          yr[0] = acc0[mt][i];
+          yr[16] = acc1[mt][i];
         }
       }
     }

@@ -70,7 +70,6 @@ hipError_t launch_prep_router_w(const void* w, int w_f32, int E, int Epad, int D
 
 struct PermuteArgs {
   const int32_t* topk_idx;
-  const float* topk_w;
   int T, K, E;
   int nb[2];              // column blocks of gate_up and down
   int qmax[2];            // capacity of each queue of gate_up and down
@@ -78,8 +77,7 @@ struct PermuteArgs {
   int32_t* offsets;       // [E + 1]
   Tile* tasks[2];         // [qmax][kQueues] each: task p of queue x at tasks[p * kQueues + x]
   int32_t* qlen;          // [2][kQueues]
-  int32_t* sorted_token;  // [K T]
-  float* row_w;           // [K T]
+  int32_t* sorted_slot;   // [K T] slot t K + j of each expert-sorted row
   int32_t* row_of_slot;   // [K T]
 };
 hipError_t launch_permute(const PermuteArgs& a, hipStream_t stream, const KernelEvents* ev);
@@ -88,15 +86,15 @@ struct GemmArgs {
   const Tile* tiles;       // this GEMM's task queues
   const int32_t* qlen;     // [kQueues] their lengths
   int qmax;                // their capacity
-  const int32_t* sorted_token;
-  const float* row_w;
+  const int32_t* sorted_slot;  // [K T] slot t K + j of each expert-sorted row
+  int K;
   const uint16_t* h;       // [T, D] expert input (bf16, or fp16 for int4 experts)
   const void* w_gate_up;   // bf16 [E, 2F, D] or int4 bytes [E, 2F, D/2]
   const void* w_down;      // bf16 [E, D, F] or int4 bytes [E, D, F/2]
   const uint16_t* s_gate_up;
   const uint16_t* s_down;
   uint16_t* act;           // [K T, F] gelu_tanh(gate) * up, expert-sorted rows
-  float* y;                // [K T, D] w * down(act), expert-sorted rows
+  float* y;                // [K T, D] down(act), expert-sorted rows
   int D, F;
   int w_packed;            // bf16 weights in the panel-fragment layout of launch_pack_panels
 };
@@ -112,7 +110,8 @@ hipError_t launch_gate_up_i4(const GemmArgs& a, hipStream_t stream, const Kernel
 hipError_t launch_down_i4(const GemmArgs& a, hipStream_t stream, const KernelEvents* ev);
 
 struct CombineArgs {
-  const float* y;
+  const float* y;              // [K T, D] expert outputs, expert-sorted rows
+  const float* topk_w;         // [T, K] routing weights
   const int32_t* row_of_slot;
   int T, K, D;
   const void* x;       // residual to add, or null

@@ -11,10 +11,16 @@
 //    weight block run together on one XCD and share its L2, and since the
 //    unit sizes never grow along the deal, every queue holds the mean load
 //    to within one unit;
-//  * the stable scatter: the rows of expert e hold its tokens in increasing
-//    token order; sorted_token[row], row_w[row] (that slot's routing weight)
-//    and row_of_slot[t k + j].
+//  * the stable scatter: the rows of expert e hold its slots in increasing
+//    token order; sorted_slot[row] = t k + j (token t, slot j) and
+//    row_of_slot[t k + j] = row.
 // Everything stays on the device; the host never reads the counts back.
+//
+// One workgroup issues every store of this kernel, and a store instruction
+// whose 64 lanes hit 64 different cache lines costs 64 line transactions, so
+// the layout of the writes is what bounds it: the task lists are written by
+// position (each lane finds which unit covers its position), and the sorted
+// slots are ranked into LDS and written out in order when they fit.
 //
 // Source of the per-expert token counts: Quant-Tuner PR "Add DiffusionGemma
 // (Gemma-4 MoE block-diffusion) support", "Answers to the motivating
@@ -27,11 +33,25 @@ namespace dg {
 namespace {
 
 constexpr int kThreads = 1024;
+constexpr int kWavesP = kThreads / 64;
 constexpr int kMaxE = 256;
-constexpr int kWords = kThreads / 32;  // bitmap words per expert for one chunk of tokens
+constexpr int kStage = 20480;  // sorted slots staged in LDS (k T up to this many)
 
 // Number of v in [0, m) with v % kQueues == x (m >= 0, 0 <= x < kQueues).
 __device__ __forceinline__ int n_mod(int m, int x) { return m > x ? (m - x + kQueues - 1) / kQueues : 0; }
+
+// The k expert ids of token t (k <= 8; ids past k are 0).
+__device__ __forceinline__ void load_ids(const int32_t* idx, int t, int K, int (&e)[8]) {
+  if (K == 8) {
+    const int4 a = *reinterpret_cast<const int4*>(idx + (size_t)t * 8);
+    const int4 b = *reinterpret_cast<const int4*>(idx + (size_t)t * 8 + 4);
+    e[0] = a.x; e[1] = a.y; e[2] = a.z; e[3] = a.w;
+    e[4] = b.x; e[5] = b.y; e[6] = b.z; e[7] = b.w;
+  } else {
+#pragma unroll
+    for (int j = 0; j < 8; ++j) e[j] = (j < K) ? idx[(size_t)t * K + j] : 0;
+  }
+}
 
 __global__ __launch_bounds__(kThreads) void k_permute(PermuteArgs a) {
   __shared__ int cnt[kMaxE];
@@ -39,27 +59,19 @@ __global__ __launch_bounds__(kThreads) void k_permute(PermuteArgs a) {
   __shared__ int cursor[kMaxE];
   __shared__ int order[kMaxE];
   __shared__ int ntile[kMaxE];
-  __shared__ int ctot[kMaxE];
   __shared__ int wsum[kMaxE / 64];
-  __shared__ int pq[2][kQueues][kMaxE + 1];  // per GEMM and queue: load of the ranks before r
-  __shared__ uint32_t bits[kMaxE * kWords];
-  __shared__ uint16_t pre[kMaxE * kWords];
+  __shared__ int pq[2][kQueues][kMaxE + 1];   // per GEMM and queue: load of the ranks before r
+  __shared__ uint64_t masks[kWavesP][kMaxE];  // per wave and expert: lanes whose token has it
+  __shared__ int wpre[kWavesP][kMaxE];        // first row of (wave, expert) in the chunk
+  __shared__ int stage[kStage];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int E = a.E, K = a.K, T = a.T;
+  const bool staged = (size_t)K * T <= (size_t)kStage;
 
   // the first chunk of tokens is loaded once and kept for the scatter
-  int e[8];
-  float w[8];
-  {
-    const int t = tid;
-#pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      const bool v = (t < T) && (j < K);
-      e[j] = v ? a.topk_idx[(size_t)t * K + j] : 0;
-      w[j] = v ? a.topk_w[(size_t)t * K + j] : 0.0f;
-    }
-  }
+  int ids[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+  if (tid < T) load_ids(a.topk_idx, tid, K, ids);
 
   // --- histogram
   if (tid < kMaxE) cnt[tid] = 0;
@@ -67,12 +79,11 @@ __global__ __launch_bounds__(kThreads) void k_permute(PermuteArgs a) {
   if (tid < T) {
 #pragma unroll
     for (int j = 0; j < 8; ++j)
-      if (j < K) atomicAdd(&cnt[e[j]], 1);
+      if (j < K) atomicAdd(&cnt[ids[j]], 1);
   }
   for (int t = tid + kThreads; t < T; t += kThreads) {
     int ee[8];
-#pragma unroll
-    for (int j = 0; j < 8; ++j) ee[j] = (j < K) ? a.topk_idx[(size_t)t * K + j] : 0;
+    load_ids(a.topk_idx, t, K, ee);
 #pragma unroll
     for (int j = 0; j < 8; ++j)
       if (j < K) atomicAdd(&cnt[ee[j]], 1);
@@ -101,15 +112,30 @@ __global__ __launch_bounds__(kThreads) void k_permute(PermuteArgs a) {
       a.offsets[tid] = excl;
       a.counts[tid] = c;
       if (tid == E - 1) a.offsets[E] = excl + c;
-      // rank by (count desc, id asc)
-      int r = 0;
-      for (int e2 = 0; e2 < E; ++e2) {
-        const int c2 = cnt[e2];
-        r += (c2 > c) || (c2 == c && e2 < tid);
-      }
-      order[r] = tid;
       ntile[tid] = (c + kTileRows - 1) / kTileRows;
     }
+  }
+  // --- rank of expert e by (count desc, id asc): four lanes per expert; lane
+  // q reads the counts 16 i + 4 q .. + 3 (consecutive lanes, consecutive
+  // banks) and compares against them
+  {
+    const int e = tid >> 2, q = tid & 3;
+    const int ce = (e < E) ? cnt[e] : 0;
+    int r = 0;
+#pragma unroll
+    for (int i = 0; i < kMaxE / 16; ++i) {
+      if (16 * i >= E) break;
+      const int4 c4 = *reinterpret_cast<const int4*>(&cnt[16 * i + 4 * q]);
+      const int cc[4] = {c4.x, c4.y, c4.z, c4.w};
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        const int e2 = 16 * i + 4 * q + k;
+        r += (e2 < E) && ((cc[k] > ce) || (cc[k] == ce && e2 < e));
+      }
+    }
+    r += __shfl_xor(r, 1);
+    r += __shfl_xor(r, 2);
+    if (q == 0 && e < E) order[r] = e;
   }
   __syncthreads();
 
@@ -127,12 +153,12 @@ __global__ __launch_bounds__(kThreads) void k_permute(PermuteArgs a) {
       v[i] = (r < E) ? ntile[order[r]] * (n_mod((r + 1) * NB, x) - n_mod(r * NB, x)) : 0;
       run += v[i];
     }
-    int incl = run;
+    int incl2 = run;
     for (int d = 1; d < 64; d <<= 1) {
-      const int o = __shfl_up(incl, d);
-      if (lane >= d) incl += o;
+      const int o = __shfl_up(incl2, d);
+      if (lane >= d) incl2 += o;
     }
-    int before = incl - run;
+    int before = incl2 - run;
     if (lane == 0) pq[g][x][0] = 0;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
@@ -145,75 +171,113 @@ __global__ __launch_bounds__(kThreads) void k_permute(PermuteArgs a) {
     const int g = tid / kQueues, x = tid % kQueues;
     a.qlen[tid] = min(pq[g][x][E], a.qmax[g]);
   }
-  // --- the tasks of every unit
+
+  // --- the tasks, one lane per queue position: position p of queue x is
+  // tasks[8 p + x], so consecutive lanes write consecutive entries. The lane
+  // needs the expert rank r whose units cover p: a table of the rank at every
+  // position, built in the (not yet used) staging memory by one lane per
+  // (queue, rank), when the queues fit in it; else a binary search on the
+  // queue's prefix. Then it finds the unit and the tile inside it.
 #pragma unroll
   for (int g = 0; g < 2; ++g) {
     const int NB = a.nb[g];
-    for (int u = tid; u < E * NB; u += kThreads) {
-      const int r = u / NB, nb = u - r * NB;
-      const int e = order[r], nt = ntile[e];
-      if (nt == 0) continue;
-      const int x = u % kQueues;
-      const int qoff = pq[g][x][r] + nt * (n_mod(u, x) - n_mod(r * NB, x));
-      const int ce = cnt[e];
-      for (int i = 0; i < nt; ++i) {
-        if (qoff + i >= a.qmax[g]) break;
-        const int lo = (ce * i) / nt, hi = (ce * (i + 1)) / nt;
-        Tile tl;
-        tl.e = e;
-        tl.row0 = base[e] + lo;
-        tl.mc = hi - lo;
-        tl.nb = nb;
-        a.tasks[g][(size_t)(qoff + i) * kQueues + x] = tl;
+    int longest = 0;
+#pragma unroll
+    for (int x = 0; x < kQueues; ++x) longest = max(longest, min(pq[g][x][E], a.qmax[g]));
+    const bool table = kQueues * longest <= kStage;
+    if (table) {
+      for (int i = tid; i < kQueues * E; i += kThreads) {
+        const int x = i / E, r = i - x * E;
+        const int p1 = min(pq[g][x][r + 1], longest);
+        for (int p = pq[g][x][r]; p < p1; ++p) stage[kQueues * p + x] = r;
       }
+      __syncthreads();
     }
+    for (int pl = tid; pl < kQueues * longest; pl += kThreads) {
+      const int x = pl % kQueues, p = pl / kQueues;
+      const int* pre = pq[g][x];
+      if (p >= min(pre[E], a.qmax[g])) continue;
+      int r;
+      if (table) {
+        r = stage[pl];
+      } else {
+        int lo = 0, hi = E;  // pre[lo] <= p < pre[hi]
+        while (hi - lo > 1) {
+          const int mid = (lo + hi) >> 1;
+          if (pre[mid] <= p) lo = mid; else hi = mid;
+        }
+        r = lo;
+      }
+      const int e = order[r], nt = ntile[e];
+      const int local = p - pre[r];
+      const int m = local / nt, i = local - m * nt;
+      const int nb0 = (x - (r * NB) % kQueues + kQueues) % kQueues;
+      const int ce = cnt[e];
+      Tile tl;
+      tl.e = e;
+      tl.row0 = base[e] + (ce * i) / nt;
+      tl.mc = (ce * (i + 1)) / nt - (ce * i) / nt;
+      tl.nb = nb0 + kQueues * m;
+      a.tasks[g][pl] = tl;
+    }
+    __syncthreads();  // the table is rebuilt for the next GEMM / reused by the scatter
   }
 
-  // --- stable scatter, kThreads tokens at a time
+  // --- stable scatter, kThreads tokens at a time: lane masks per (wave,
+  // expert) give each slot its rank among the chunk's earlier tokens
+  const uint64_t below = (1ull << lane) - 1ull;
   for (int c0 = 0; c0 < T; c0 += kThreads) {
     const int t = c0 + tid;
-    if (c0 > 0) {
-#pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        const bool v = (t < T) && (j < K);
-        e[j] = v ? a.topk_idx[(size_t)t * K + j] : 0;
-        w[j] = v ? a.topk_w[(size_t)t * K + j] : 0.0f;
-      }
-    }
-    for (int i = tid; i < E * kWords; i += kThreads) bits[i] = 0u;
-    __syncthreads();
-    const uint32_t my_bit = 1u << (tid & 31);
-    const int my_word = tid >> 5;
+    if (c0 > 0 && t < T) load_ids(a.topk_idx, t, K, ids);
+    for (int i = lane; i < E; i += 64) masks[wave][i] = 0ull;
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
     if (t < T) {
 #pragma unroll
       for (int j = 0; j < 8; ++j)
-        if (j < K) atomicOr(&bits[e[j] * kWords + my_word], my_bit);
+        if (j < K) atomicOr(reinterpret_cast<unsigned long long*>(&masks[wave][ids[j]]), 1ull << lane);
     }
     __syncthreads();
     if (tid < E) {
-      int run = 0;
-      for (int i = 0; i < kWords; ++i) {
-        pre[tid * kWords + i] = (uint16_t)run;
-        run += __popc(bits[tid * kWords + i]);
+      int run = cursor[tid];
+#pragma unroll
+      for (int w = 0; w < kWavesP; ++w) {
+        wpre[w][tid] = run;
+        run += __popcll(masks[w][tid]);
       }
-      ctot[tid] = run;
+      cursor[tid] = run;
     }
     __syncthreads();
     if (t < T) {
+      int rows[8];
 #pragma unroll
       for (int j = 0; j < 8; ++j) {
         if (j < K) {
-          const int rank = pre[e[j] * kWords + my_word] + __popc(bits[e[j] * kWords + my_word] & (my_bit - 1u));
-          const int row = cursor[e[j]] + rank;
-          a.sorted_token[row] = t;
-          a.row_w[row] = w[j];
-          a.row_of_slot[(size_t)t * K + j] = row;
+          const int ej = ids[j];
+          rows[j] = wpre[wave][ej] + __popcll(masks[wave][ej] & below);
+          const int slot = t * K + j;
+          if (staged)
+            stage[rows[j]] = slot;
+          else
+            a.sorted_slot[rows[j]] = slot;
+        } else {
+          rows[j] = 0;
         }
+      }
+      if (K == 8) {
+        *reinterpret_cast<int4*>(a.row_of_slot + (size_t)t * 8) = make_int4(rows[0], rows[1], rows[2], rows[3]);
+        *reinterpret_cast<int4*>(a.row_of_slot + (size_t)t * 8 + 4) = make_int4(rows[4], rows[5], rows[6], rows[7]);
+      } else {
+#pragma unroll
+        for (int j = 0; j < 8; ++j)
+          if (j < K) a.row_of_slot[(size_t)t * K + j] = rows[j];
       }
     }
     __syncthreads();
-    if (tid < E) cursor[tid] += ctot[tid];
-    __syncthreads();
+  }
+  if (staged) {
+    const int n = K * T;
+    for (int i = tid; i < n; i += kThreads) a.sorted_slot[i] = stage[i];
   }
 }
 

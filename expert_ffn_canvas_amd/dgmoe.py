@@ -42,7 +42,7 @@ class dg_moe_weights(ctypes.Structure):
 
 class dg_moe_debug(ctypes.Structure):
     _fields_ = [("topk_idx", ctypes.c_void_p), ("topk_w", ctypes.c_void_p), ("counts", ctypes.c_void_p),
-                ("offsets", ctypes.c_void_p), ("sorted_token", ctypes.c_void_p), ("row_of_slot", ctypes.c_void_p)]
+                ("offsets", ctypes.c_void_p), ("sorted_slot", ctypes.c_void_p), ("row_of_slot", ctypes.c_void_p)]
 
 
 def _load():
@@ -205,10 +205,10 @@ class MoELayer:
             topk_w=torch.empty((T, self.K), dtype=torch.float32, device=dev),
             counts=torch.empty((self.E,), dtype=torch.int32, device=dev),
             offsets=torch.empty((self.E + 1,), dtype=torch.int32, device=dev),
-            sorted_token=torch.empty((T * self.K,), dtype=torch.int32, device=dev),
+            sorted_slot=torch.empty((T * self.K,), dtype=torch.int32, device=dev),
             row_of_slot=torch.empty((T * self.K,), dtype=torch.int32, device=dev),
         )
-        dbg = dg_moe_debug(*(_ptr(r[k]) for k in ("topk_idx", "topk_w", "counts", "offsets", "sorted_token",
+        dbg = dg_moe_debug(*(_ptr(r[k]) for k in ("topk_idx", "topk_w", "counts", "offsets", "sorted_slot",
                                                    "row_of_slot")))
         st = dg_moe_forward_debug(self.handle, _ptr(x), _ptr(out), T, dbg, self.stream.cuda_stream)
         _check(st, "dg_moe_forward_debug")

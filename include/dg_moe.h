@@ -105,8 +105,8 @@ typedef struct dg_moe_debug {
   float* topk_w;         /* [T, k] their renormalised softmax weights                */
   int32_t* counts;       /* [E] tokens routed to each expert                         */
   int32_t* offsets;      /* [E + 1] exclusive prefix sum of counts                   */
-  int32_t* sorted_token; /* [k T] token of each expert-sorted row (increasing token
-                            order inside an expert)                                  */
+  int32_t* sorted_slot;  /* [k T] slot t k + j of each expert-sorted row (increasing
+                            token order inside an expert)                            */
   int32_t* row_of_slot;  /* [k T] expert-sorted row of slot (t, j)                   */
 } dg_moe_debug;
 

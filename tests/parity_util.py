@@ -67,8 +67,14 @@ def check_permutation(dbg, K, E, T):
     pm = oracle.permute(idx, E)
     assert np.array_equal(dbg["counts"].cpu().numpy(), pm["counts"])
     assert np.array_equal(dbg["offsets"].cpu().numpy(), pm["offsets"])
-    assert np.array_equal(dbg["sorted_token"].cpu().numpy(), pm["sorted_token"])
-    assert np.array_equal(dbg["row_of_slot"].cpu().numpy(), pm["row_of_slot"])
+    slot = dbg["sorted_slot"].cpu().numpy()
+    assert np.array_equal(slot // K, pm["sorted_token"])
+    row_of_slot = dbg["row_of_slot"].cpu().numpy()
+    assert np.array_equal(row_of_slot, pm["row_of_slot"])
+    # the slot of each row routes to that row's expert, and gather after scatter is the identity
+    row_expert = np.repeat(np.arange(E), pm["counts"])
+    assert np.array_equal(idx.ravel()[slot], row_expert)
+    assert np.array_equal(row_of_slot[slot], np.arange(K * T))
     assert int(pm["counts"].sum()) == K * T
 
 
