@@ -1,6 +1,6 @@
 // Weighted combine back to token order on gfx950:
 //   out[t] = sum_j w[t, j] y[row_of_slot[t k + j]]  (+ x[t]) (+ addend[t])
-// with w the routing weights and y the expert outputs of the slots. The k
+// with w the routing weights and y the expert outputs of the slots (bf16). The k
 // slots are accumulated (fused multiply-add, fp32) in their routing order
 // (logit descending), always in the same order, so the result is
 // bit-reproducible; the output is rounded once (round-to-nearest-even for
@@ -31,16 +31,19 @@ __global__ __launch_bounds__(kThreads) void k_combine(CombineArgs a) {
     w[j] = (j < K) ? a.topk_w[(size_t)t * K + j] : 0.0f;
   }
   if (c < D) {
-    const float4 v0 = *reinterpret_cast<const float4*>(a.y + (size_t)rows[0] * D + c);
-    float4 s = make_float4(w[0] * v0.x, w[0] * v0.y, w[0] * v0.z, w[0] * v0.w);
+    uint2 yv[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j)
+      if (j < K) yv[j] = *reinterpret_cast<const uint2*>(a.y + (size_t)rows[j] * D + c);
+    float4 s = make_float4(w[0] * bf16_lo(yv[0].x), w[0] * bf16_hi(yv[0].x), w[0] * bf16_lo(yv[0].y),
+                           w[0] * bf16_hi(yv[0].y));
 #pragma unroll
     for (int j = 1; j < 8; ++j) {
       if (j < K) {
-        const float4 v = *reinterpret_cast<const float4*>(a.y + (size_t)rows[j] * D + c);
-        s.x = fmaf(w[j], v.x, s.x);
-        s.y = fmaf(w[j], v.y, s.y);
-        s.z = fmaf(w[j], v.z, s.z);
-        s.w = fmaf(w[j], v.w, s.w);
+        s.x = fmaf(w[j], bf16_lo(yv[j].x), s.x);
+        s.y = fmaf(w[j], bf16_hi(yv[j].x), s.y);
+        s.z = fmaf(w[j], bf16_lo(yv[j].y), s.z);
+        s.w = fmaf(w[j], bf16_hi(yv[j].y), s.w);
       }
     }
     const void* extra[2] = {a.x, a.addend};

@@ -84,7 +84,7 @@ Layout plan(const dg_moe_config& c) {
   L.sorted_slot = take(K * T * 4);
   L.row_of_slot = take(K * T * 4);
   L.act = take(K * T * F * 2);
-  L.y = take(K * T * D * 4);
+  L.y = take(K * T * D * 2);
   L.wr = take((size_t)L.n_wplanes * L.Epad * D * 2);
   L.gamma_r = take(D * 4);
   L.bias = take(E * 4);
@@ -383,7 +383,7 @@ static dg_status run_forward(dg_moe_handle hd, const void* x, void* out, int32_t
   ga.s_gate_up = hd->s_gate_up;
   ga.s_down = hd->s_down;
   ga.act = hd->at<uint16_t>(L.act);
-  ga.y = hd->at<float>(L.y);
+  ga.y = hd->at<uint16_t>(L.y);
   ga.D = c.d_model;
   ga.F = c.d_ff;
   e = i4 ? dg::launch_gate_up_i4(ga, stream, ev(3)) : dg::launch_gate_up_bf16(ga, stream, ev(3));

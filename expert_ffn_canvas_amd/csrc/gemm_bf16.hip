@@ -5,8 +5,8 @@
 //           u = h W_up[e]^T over the full d_model, then act = gelu_tanh(g) * u
 //           (bf16).
 //  down:    for each tile and each block of 128 d_model outputs:
-//           y = act W_down[e]^T in fp32, one row per routed slot (the combine
-//           applies the routing weights).
+//           y = act W_down[e]^T (fp32 sums, stored as bf16), one row per routed
+//           slot (the combine applies the routing weights).
 //
 // Shapes (auto-round PR "Add quantization support for DiffusionGemma",
 // transformers backend test log, expert module dump): gate_proj and up_proj
@@ -299,9 +299,9 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3, 3))
           if (GATE_UP) {
             a.act[(size_t)(tl.row0 + r) * F + col] = f32_to_bf16_bits(gelu_tanh(acc0[mt][i]) * acc1[mt][i]);
           } else {
-            float* yr = a.y + (size_t)(tl.row0 + r) * D + col;
-            yr[0] = acc0[mt][i];
-            yr[16] = acc1[mt][i];
+            uint16_t* yr = a.y + (size_t)(tl.row0 + r) * D + col;
+            yr[0] = f32_to_bf16_bits(acc0[mt][i]);
+            yr[16] = f32_to_bf16_bits(acc1[mt][i]);
           }
         }
       }

@@ -284,9 +284,9 @@ __global__ __launch_bounds__(kThreads) void k_down_i4(GemmArgs a) {
       for (int i = 0; i < 4; ++i) {
         const int r = mt * 16 + g * 4 + i;
         if (r < tl.mc) {
-          float* yr = a.y + (size_t)(tl.row0 + r) * D + d0;
-          yr[0] = acc0[mt][i];
-          yr[16] = acc1[mt][i];
+          uint16_t* yr = a.y + (size_t)(tl.row0 + r) * D + d0;
+          yr[0] = f32_to_bf16_bits(acc0[mt][i]);
+          yr[16] = f32_to_bf16_bits(acc1[mt][i]);
         }
       }
     }

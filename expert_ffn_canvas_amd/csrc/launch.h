@@ -94,7 +94,7 @@ struct GemmArgs {
   const uint16_t* s_gate_up;
   const uint16_t* s_down;
   uint16_t* act;           // [K T, F] gelu_tanh(gate) * up, expert-sorted rows
-  float* y;                // [K T, D] down(act), expert-sorted rows
+  uint16_t* y;             // [K T, D] bf16 down(act), expert-sorted rows
   int D, F;
   int w_packed;            // bf16 weights in the panel-fragment layout of launch_pack_panels
 };
@@ -110,7 +110,7 @@ hipError_t launch_gate_up_i4(const GemmArgs& a, hipStream_t stream, const Kernel
 hipError_t launch_down_i4(const GemmArgs& a, hipStream_t stream, const KernelEvents* ev);
 
 struct CombineArgs {
-  const float* y;              // [K T, D] expert outputs, expert-sorted rows
+  const uint16_t* y;           // [K T, D] bf16 expert outputs, expert-sorted rows
   const float* topk_w;         // [T, K] routing weights
   const int32_t* row_of_slot;
   int T, K, D;
