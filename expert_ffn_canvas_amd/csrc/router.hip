@@ -158,9 +158,9 @@ __device__ __forceinline__ void topk_half(const float* row, bool active, int E, 
 }
 
 // One workgroup of 256 threads per token; thread i owns the 8-column pieces
-// i, i + 256, ... (up to 8 of them: d_model <= 16384). All loads of a thread
-// (x and both gammas) are issued together, one block reduction gives r.
-template <bool XF32>
+// i, i + 256, ... (up to NP of them: d_model <= 2048 NP). All loads of a
+// thread (x and both gammas) are issued together, one block reduction gives r.
+template <bool XF32, int NP>
 __global__ __launch_bounds__(256) void k_norm(RouterArgs a) {
   __shared__ float wsum[4];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -168,10 +168,10 @@ __global__ __launch_bounds__(256) void k_norm(RouterArgs a) {
   const int D = a.D;
   const int nseg = D / 8;
   const size_t row = (size_t)t * D;
-  XPiece<XF32> xp[8];
-  float4 gr[8][2], ge[8][2];
+  XPiece<XF32> xp[NP];
+  float4 gr[NP][2], ge[NP][2];
 #pragma unroll
-  for (int i = 0; i < 8; ++i) {
+  for (int i = 0; i < NP; ++i) {
     const int sg = tid + 256 * i;
     if (sg < nseg) {
       load_piece<XF32>(a.x, row + sg * 8, xp[i]);
@@ -183,7 +183,7 @@ __global__ __launch_bounds__(256) void k_norm(RouterArgs a) {
   }
   float ss = 0.0f;
 #pragma unroll
-  for (int i = 0; i < 8; ++i) {
+  for (int i = 0; i < NP; ++i) {
     if (tid + 256 * i < nseg) {
       float f[8];
       piece_floats<XF32>(xp[i], f);
@@ -198,7 +198,7 @@ __global__ __launch_bounds__(256) void k_norm(RouterArgs a) {
   const float r = 1.0f / sqrtf(tot / (float)D + a.eps);
   const size_t plane = (size_t)a.T * D;
 #pragma unroll
-  for (int i = 0; i < 8; ++i) {
+  for (int i = 0; i < NP; ++i) {
     const int sg = tid + 256 * i;
     if (sg >= nseg) continue;
     float f[8];
@@ -239,9 +239,13 @@ __global__ __launch_bounds__(256) void k_norm(RouterArgs a) {
 // All expert tiles of a token tile run on one XCD (workgroup b runs on XCD
 // b % 8) and share its L2: each one publishes its logits with a counter and
 // the last to arrive selects the top-k of the 16 rows.
-template <int NWP, int NU>
+// GROUPS: chunks whose loads a wave keeps in flight at once. Three (two for
+// fp32 router weights) take one round trip per wave at d_model <= 3072 but
+// hold about 200 registers, so one workgroup fits a CU; one group lets two
+// workgroups share a CU, which pays when there are many token tiles.
+template <int NWP, int NU, bool WIDE>
 __global__ __launch_bounds__(64 * kWaves) void k_logits(RouterArgs a) {
-  constexpr int kGroup = (NWP == 1) ? 3 : 2;
+  constexpr int kGroup = !WIDE ? 1 : (NWP == 1) ? 3 : 2;
   __shared__ float part[kWaves][kTokTile][17];
   __shared__ float cv[kWaves][2][8];
   __shared__ int ci[kWaves][2][8];
@@ -361,17 +365,27 @@ __global__ void k_prep_router_w(const void* __restrict__ w, int w_f32, int E, in
 }  // namespace
 
 hipError_t launch_router(const RouterArgs& a, hipStream_t stream, const KernelEvents* ev) {
-  hipError_t e = launch_kernel(a.x_f32 ? k_norm<true> : k_norm<false>, dim3(a.T), dim3(256), stream,
-                               ev ? &ev[0] : nullptr, a);
+  void (*kn)(RouterArgs);
+  if (a.D <= 2048 * 2)
+    kn = a.x_f32 ? k_norm<true, 2> : k_norm<false, 2>;
+  else
+    kn = a.x_f32 ? k_norm<true, 8> : k_norm<false, 8>;
+  hipError_t e = launch_kernel(kn, dim3(a.T), dim3(256), stream, ev ? &ev[0] : nullptr, a);
   if (e != hipSuccess) return e;
   const int n_tt = (a.T + kTokTile - 1) / kTokTile;
-  const dim3 grid(kQueues * ((n_tt + kQueues - 1) / kQueues) * (a.Epad / 16));
+  const int n_et = a.Epad / 16;
+  const dim3 grid(kQueues * ((n_tt + kQueues - 1) / kQueues) * n_et);
+  // more workgroups than CUs: the narrow variant keeps two per CU
+  const bool wide = (size_t)n_tt * n_et <= 256;
   const int nu = a.Epad / 32;  // 1 .. 8
   void (*k)(RouterArgs);
+#define DG_LOGITS(NWP, W) \
+  (nu <= 1 ? k_logits<NWP, 1, W> : nu <= 2 ? k_logits<NWP, 2, W> : nu <= 4 ? k_logits<NWP, 4, W> : k_logits<NWP, 8, W>)
   if (a.n_wplanes == 3)
-    k = nu <= 1 ? k_logits<3, 1> : nu <= 2 ? k_logits<3, 2> : nu <= 4 ? k_logits<3, 4> : k_logits<3, 8>;
+    k = wide ? DG_LOGITS(3, true) : DG_LOGITS(3, false);
   else
-    k = nu <= 1 ? k_logits<1, 1> : nu <= 2 ? k_logits<1, 2> : nu <= 4 ? k_logits<1, 4> : k_logits<1, 8>;
+    k = wide ? DG_LOGITS(1, true) : DG_LOGITS(1, false);
+#undef DG_LOGITS
   return launch_kernel(k, grid, dim3(64 * kWaves), stream, ev ? &ev[1] : nullptr, a);
 }
 
