@@ -224,8 +224,13 @@ dg_status dg_moe_create(const dg_moe_config* cfg, const dg_moe_weights* w, void*
     (void)hipGetLastError();
     return fail(DG_ERR_OOM, "workspace of %zu bytes: %s", hd->L.total, hipGetErrorString(e));
   }
-  const ExpertBytes eb = expert_bytes(*cfg);
+  ExpertBytes eb = expert_bytes(*cfg);
   if (cfg->flags & DG_MOE_PACK_WEIGHTS) {
+    if (i4) {  // packed int4 codes: a full 128-input group per (row, group), the short last one padded
+      const size_t E = cfg->n_experts, D = cfg->d_model, F = cfg->d_ff;
+      eb.gu = E * 2 * F * ((D + 127) / 128) * 64;
+      eb.dn = E * D * ((F + 127) / 128) * 64;
+    }
     const size_t total = round_up(eb.gu, 256) + round_up(eb.dn, 256) + round_up(eb.sgu, 256) + round_up(eb.sdn, 256);
     e = hipMalloc(&hd->packed, total);
     if (e != hipSuccess) {
@@ -242,9 +247,15 @@ dg_status dg_moe_create(const dg_moe_config* cfg, const dg_moe_weights* w, void*
                                                         round_up(eb.sgu, 256))
                     : nullptr;
     hipError_t c1, c2, c3 = hipSuccess, c4 = hipSuccess;
-    if (i4) {
-      c1 = hipMemcpyAsync(const_cast<void*>(hd->w_gate_up), w->w_gate_up, eb.gu, hipMemcpyDeviceToDevice, stream);
-      c2 = hipMemcpyAsync(const_cast<void*>(hd->w_down), w->w_down, eb.dn, hipMemcpyDeviceToDevice, stream);
+    if (i4) {  // int4: codes and scales in fragment order
+      c1 = dg::launch_pack_i4(static_cast<const uint8_t*>(w->w_gate_up), w->s_gate_up,
+                              static_cast<uint8_t*>(const_cast<void*>(hd->w_gate_up)),
+                              const_cast<uint16_t*>(hd->s_gate_up), cfg->n_experts, 2 * cfg->d_ff, cfg->d_model,
+                              stream);
+      c2 = dg::launch_pack_i4(static_cast<const uint8_t*>(w->w_down), w->s_down,
+                              static_cast<uint8_t*>(const_cast<void*>(hd->w_down)), const_cast<uint16_t*>(hd->s_down),
+                              cfg->n_experts, cfg->d_model, cfg->d_ff, stream);
+      hd->w_packed = 1;
     } else {  // bf16: MFMA fragment order, 1 KB per wave-wide read
       c1 = dg::launch_pack_panels(static_cast<const uint16_t*>(w->w_gate_up),
                                   static_cast<uint16_t*>(const_cast<void*>(hd->w_gate_up)), cfg->n_experts,
@@ -253,10 +264,6 @@ dg_status dg_moe_create(const dg_moe_config* cfg, const dg_moe_weights* w, void*
                                   static_cast<uint16_t*>(const_cast<void*>(hd->w_down)), cfg->n_experts,
                                   cfg->d_model, cfg->d_ff, stream);
       hd->w_packed = 1;
-    }
-    if (i4) {
-      c3 = hipMemcpyAsync(const_cast<uint16_t*>(hd->s_gate_up), w->s_gate_up, eb.sgu, hipMemcpyDeviceToDevice, stream);
-      c4 = hipMemcpyAsync(const_cast<uint16_t*>(hd->s_down), w->s_down, eb.sdn, hipMemcpyDeviceToDevice, stream);
     }
     if (c1 != hipSuccess || c2 != hipSuccess || c3 != hipSuccess || c4 != hipSuccess) {
       dg_moe_destroy(hd);

@@ -1,0 +1,88 @@
+// Building blocks shared by the grouped GEMM kernels on gfx950: tile
+// constants, explicit vmcnt waits, the global -> LDS DMA of activation rows
+// with its XOR swizzle, and the LDS-only workgroup barrier.
+#pragma once
+
+#include "dg_common.h"
+#include "launch.h"
+
+namespace dg {
+namespace gemm {
+
+#ifndef DG_GEMM_WAVES
+#define DG_GEMM_WAVES 4
+#endif
+constexpr int kWaves = DG_GEMM_WAVES;    // waves per workgroup
+constexpr int kThreads = 64 * kWaves;
+constexpr int kKS = 128;                  // K per pipeline step (four MFMA K steps of 32)
+constexpr int kNS = kKS / 32;
+constexpr int kSegs = kKS / 8;            // 16-byte segments per staged row
+constexpr int kRowBytes = kKS * 2;
+constexpr int kDmaRows = 1024 / kRowBytes;  // rows one wave-wide 16-byte-per-lane transfer fills
+constexpr int kStageBytes = kTileRows * kRowBytes;
+constexpr int kBMT = kTileRows / 16;      // m-tiles per tile
+constexpr int kDmaInstr = kTileRows / (kWaves * kDmaRows);  // transfers per wave for a full tile
+
+// vmcnt(n) with the other counters left alone (gfx9 encoding: vmcnt in bits
+// 3:0 and 15:14, expcnt 6:4, lgkmcnt 11:8).
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+}
+
+// LDS byte address of a shared-memory pointer (the address-space cast to
+// the local address space; its value is the offset inside the workgroup's LDS).
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+  return static_cast<uint32_t>(reinterpret_cast<uintptr_t>((const __attribute__((address_space(3))) char*)p));
+}
+
+// One 16-byte-per-lane global -> LDS transfer (global_load_lds_dwordx4): lane l
+// writes LDS bytes lds_base + 16 l .. + 15. Issued from inline assembly so the
+// compiler does not treat every later LDS read as depending on it; completion
+// is awaited explicitly (vmcnt) before the workgroup barrier that publishes it.
+// No register is written, so nothing is left in flight in a register.
+// M0 is saved and restored around the transfer, so nothing the compiler keeps
+// in M0 is disturbed.
+__device__ __forceinline__ void lds_dma16(uint32_t lds_base, const void* gaddr) {
+  uint32_t saved;
+  asm volatile(
+      "s_mov_b32 %0, m0\n\t"
+      "s_mov_b32 m0, %1\n\t"
+      "s_nop 0\n\t"
+      "global_load_lds_dwordx4 %2, off\n\t"
+      "s_mov_b32 m0, %0"
+      : "=&s"(saved)
+      : "s"(lds_base), "v"(gaddr)
+      : "memory");
+}
+
+// Activation rows of one K step straight into LDS: instruction i of wave w
+// fills the kDmaRows rows starting at kDmaRows (w + kWaves i); lane l lands in row
+// slot l / kSegs, 16-byte position l % kSegs and carries logical segment
+// position ^ (row % kSegs), an XOR swizzle that makes the MFMA reads
+// bank-conflict free. Segments past a short last step re-read a valid one.
+template <int NMT, int NSEG>
+__device__ __forceinline__ void dma_a(char* stage, const uint16_t* const (&rowp)[kDmaInstr], int k0, int wave,
+                                      int lane) {
+  const uint32_t base = __builtin_amdgcn_readfirstlane(lds_addr(stage) + wave * kDmaRows * kRowBytes);
+#pragma unroll
+  for (int i = 0; i < 16 * NMT / (kWaves * kDmaRows); ++i) {
+    const int r = kDmaRows * (wave + kWaves * i) + lane / kSegs;
+    int sg = (lane % kSegs) ^ (r % kSegs);
+    if (NSEG < kSegs) sg = sg % NSEG;
+    lds_dma16(base + i * kWaves * kDmaRows * kRowBytes, rowp[i] + k0 + sg * 8);
+  }
+}
+
+// Workgroup barrier that does not wait for this wave's outstanding global
+// loads: the LDS-DMA writes the other waves are about to read are covered by
+// the explicit vmcnt wait before it. The empty asm statements stop the
+// compiler from moving memory operations across the barrier.
+__device__ __forceinline__ void lds_barrier() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
+}  // namespace gemm
+}  // namespace dg

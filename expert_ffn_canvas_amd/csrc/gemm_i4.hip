@@ -23,16 +23,17 @@
 // codes (0,4), (1,5), (2,6), (3,7); the activations are stored into LDS in the
 // same order so that both MFMA operands agree on which k each element is.
 #include "dg_common.h"
+#include "gemm_common.h"
 #include "launch.h"
 
 namespace dg {
 
 namespace {
 
-constexpr int kThreads = 256;
+using namespace gemm;  // kThreads (256), kBMT (4), the DMA and wait helpers
+
 constexpr int kSlab = 128;              // inputs per scale group = K per step
 constexpr int kPitch = kSlab + 8;       // LDS row pitch in fp16 elements
-constexpr int kBMT = kTileRows / 16;
 constexpr int kAPass = kTileRows / 16;  // 256 threads stage 16 rows x 128 K per pass
 
 // 8 activations (a0..a7) -> order a0 a4 a1 a5 a2 a6 a3 a7.
@@ -293,13 +294,274 @@ __global__ __launch_bounds__(kThreads) void k_down_i4(GemmArgs a) {
   }
 }
 
+// ---------------------------------------------------------------------------
+// Packed layout (create-time): codes in MFMA fragment order, 1 KB block per
+// (expert e, 16-row panel p, group gi); lane l = n + 16 g of the block holds
+// 16 bytes for row 16 p + n: dword s carries the 8 codes of inputs
+// 128 gi + 32 s + 8 g .. + 7, nibble-ordered so that the exact widening below
+// yields them in natural order (nibble i holds input 2 i for i < 4 and
+// input 2 (i - 4) + 1 for i >= 4). Inputs past K (the short last group) get
+// code 8, which stands for 0. Scales: 16 fp16 per (e, p, gi), row order.
+// So a wave reads one weight fragment as 1 KB contiguous, and the activation
+// fragments are exactly the bf16 kernels' (same LDS layout and DMA).
+
+// 8 codes of the packed order -> 8 fp16 values (q - 8) in natural order.
+__device__ __forceinline__ f16x8 dequant8n(uint32_t v) {
+  const f16x2 bias = f16x2{(_Float16)-1032.0f, (_Float16)-1032.0f};
+  const f16x2 p0 = __builtin_bit_cast(f16x2, (v & 0x000F000Fu) | 0x64006400u) + bias;          // k0 k1
+  const f16x2 p1 = __builtin_bit_cast(f16x2, ((v >> 4) & 0x000F000Fu) | 0x64006400u) + bias;   // k2 k3
+  const f16x2 p2 = __builtin_bit_cast(f16x2, ((v >> 8) & 0x000F000Fu) | 0x64006400u) + bias;   // k4 k5
+  const f16x2 p3 = __builtin_bit_cast(f16x2, ((v >> 12) & 0x000F000Fu) | 0x64006400u) + bias;  // k6 k7
+  f16x8 r;
+  r[0] = p0[0]; r[1] = p0[1]; r[2] = p1[0]; r[3] = p1[1];
+  r[4] = p2[0]; r[5] = p2[1]; r[6] = p3[0]; r[7] = p3[1];
+  return r;
+}
+
+// One thread per (block, lane).
+__global__ __launch_bounds__(256) void k_pack_i4(const uint8_t* __restrict__ codes, const uint16_t* __restrict__ scales,
+                                                 uint8_t* __restrict__ pcodes, uint16_t* __restrict__ pscales, int E,
+                                                 int R, int K) {
+  const int G = (K + 127) / 128, NP = R / 16;
+  const size_t nblk = (size_t)E * NP * G;
+  const int lane = threadIdx.x & 63;
+  const int n = lane & 15, g = lane >> 4;
+  for (size_t b = (size_t)blockIdx.x * 4 + (threadIdx.x >> 6); b < nblk; b += (size_t)gridDim.x * 4) {
+    const int gi = (int)(b % G);
+    const size_t ep = b / G;  // e * NP + p
+    const size_t row = (ep / NP) * R + (ep % NP) * 16 + n;
+    const uint8_t* src = codes + row * (K / 2);
+    u32x4 o;
+#pragma unroll
+    for (int s = 0; s < 4; ++s) {
+      uint32_t c[8];
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        const int k = 128 * gi + 32 * s + 8 * g + j;
+        c[j] = (k < K) ? ((src[k >> 1] >> ((k & 1) * 4)) & 0xFu) : 8u;
+      }
+      o[s] = c[0] | (c[2] << 4) | (c[4] << 8) | (c[6] << 12) | (c[1] << 16) | (c[3] << 20) | (c[5] << 24) |
+             (c[7] << 28);
+    }
+    *reinterpret_cast<u32x4*>(pcodes + (b * 64 + lane) * 16) = o;
+    if (g == 0) pscales[b * 16 + n] = scales[row * G + gi];
+  }
+}
+
+// Weights of one group for this lane: codes of both panels and their scales.
+struct WGroup {
+  u32x4 c0, c1;
+  uint16_t s0, s1;
+};
+
+__device__ __forceinline__ void load_wg(const uint8_t* c0, const uint8_t* c1, const uint16_t* s0, const uint16_t* s1,
+                                        int gi, WGroup& w) {
+  w.c0 = *reinterpret_cast<const u32x4*>(c0 + (size_t)gi * 1024);
+  w.c1 = *reinterpret_cast<const u32x4*>(c1 + (size_t)gi * 1024);
+  w.s0 = s0[gi * 16];
+  w.s1 = s1[gi * 16];
+}
+
+// One group's MFMAs: partial sums over the 128 inputs in t, then scaled into acc.
+template <int NMT>
+__device__ __forceinline__ void mma_i4(const char* stage, int lane, const WGroup& w, f32x4 (&acc0)[kBMT],
+                                       f32x4 (&acc1)[kBMT]) {
+  const int g = lane >> 4, m = lane & 15;
+  f32x4 t0[kBMT], t1[kBMT];
+#pragma unroll
+  for (int mt = 0; mt < NMT; ++mt) {
+    t0[mt] = f32x4{0.f, 0.f, 0.f, 0.f};
+    t1[mt] = f32x4{0.f, 0.f, 0.f, 0.f};
+  }
+#pragma unroll
+  for (int s = 0; s < kNS; ++s) {
+    const f16x8 b0 = dequant8n(w.c0[s]);
+    const f16x8 b1 = dequant8n(w.c1[s]);
+#pragma unroll
+    for (int mt = 0; mt < NMT; ++mt) {
+      const int r = mt * 16 + m;
+      const int pos = (s * 4 + g) ^ (r % kSegs);
+      const f16x8 av = as_f16x8(*reinterpret_cast<const u32x4*>(stage + r * kRowBytes + pos * 16));
+      t0[mt] = mfma_f16(av, b0, t0[mt]);
+      t1[mt] = mfma_f16(av, b1, t1[mt]);
+    }
+    __builtin_amdgcn_sched_barrier(0);  // widen one sub-step's codes at a time
+  }
+  const float f0 = (float)__builtin_bit_cast(_Float16, w.s0), f1 = (float)__builtin_bit_cast(_Float16, w.s1);
+#pragma unroll
+  for (int mt = 0; mt < NMT; ++mt)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      acc0[mt][i] = fmaf(f0, t0[mt][i], acc0[mt][i]);
+      acc1[mt][i] = fmaf(f1, t1[mt][i], acc1[mt][i]);
+    }
+}
+
+constexpr int kDepthI4 = 3;  // LDS stages and weight buffers; step i + 2 is issued during step i
+
+template <int NMT>
+__device__ __forceinline__ void issue_i4(char* As, const uint16_t* const (&rowp)[kDmaInstr], const uint8_t* c0,
+                                         const uint8_t* c1, const uint16_t* s0, const uint16_t* s1, int j, int K,
+                                         int wave, int lane, WGroup& w) {
+  char* st = As + (j % kDepthI4) * kStageBytes;
+  const int k0 = j * kKS;
+  if (k0 + kKS <= K)
+    dma_a<NMT, kSegs>(st, rowp, k0, wave, lane);
+  else
+    dma_a<NMT, kSegs / 2>(st, rowp, k0, wave, lane);
+  __builtin_amdgcn_sched_barrier(0);
+  load_wg(c0, c1, s0, s1, j, w);
+  __builtin_amdgcn_sched_barrier(0);
+}
+
+// Step i: wait until step i's transfers have landed (those of step i + 1,
+// NMT DMA transfers and 4 weight loads, may still fly; WAIT = 0 for the last
+// step), publish, issue step i + 2, multiply step i.
+template <int NMT, bool ISSUE, int WAIT>
+__device__ __forceinline__ void step_i4(char* As, const uint16_t* const (&rowp)[kDmaInstr], const uint8_t* c0,
+                                        const uint8_t* c1, const uint16_t* s0, const uint16_t* s1, int i, int K,
+                                        int wave, int lane, const WGroup& wb, WGroup& wn2, f32x4 (&acc0)[kBMT],
+                                        f32x4 (&acc1)[kBMT]) {
+  wait_vmcnt<WAIT>();
+  lds_barrier();
+  if (ISSUE) issue_i4<NMT>(As, rowp, c0, c1, s0, s1, i + 2, K, wave, lane, wn2);
+  mma_i4<NMT>(As + (i % kDepthI4) * kStageBytes, lane, wb, acc0, acc1);
+}
+
+// The group loop: unrolled by three (one weight buffer per position), the last
+// two to four groups written out so that every wait count is exact.
+template <int NMT>
+__device__ __forceinline__ void loop_i4(char* As, const uint16_t* const (&rowp)[kDmaInstr], const uint8_t* c0,
+                                        const uint8_t* c1, const uint16_t* s0, const uint16_t* s1, int K, int tid,
+                                        f32x4 (&acc0)[kBMT], f32x4 (&acc1)[kBMT]) {
+  constexpr int kW = NMT + 4;
+  const int lane = tid & 63, wave = tid >> 6;
+  const int n = (K + kKS - 1) / kKS;
+  WGroup w0, w1, w2;
+  issue_i4<NMT>(As, rowp, c0, c1, s0, s1, 0, K, wave, lane, w0);
+  if (n == 1) {
+    step_i4<NMT, false, 0>(As, rowp, c0, c1, s0, s1, 0, K, wave, lane, w0, w2, acc0, acc1);
+    return;
+  }
+  issue_i4<NMT>(As, rowp, c0, c1, s0, s1, 1, K, wave, lane, w1);
+  int i = 0;
+  for (; i + 5 <= n; i += 3) {
+    step_i4<NMT, true, kW>(As, rowp, c0, c1, s0, s1, i, K, wave, lane, w0, w2, acc0, acc1);
+    step_i4<NMT, true, kW>(As, rowp, c0, c1, s0, s1, i + 1, K, wave, lane, w1, w0, acc0, acc1);
+    step_i4<NMT, true, kW>(As, rowp, c0, c1, s0, s1, i + 2, K, wave, lane, w2, w1, acc0, acc1);
+  }
+  switch (n - i) {
+    case 2:
+      step_i4<NMT, false, kW>(As, rowp, c0, c1, s0, s1, i, K, wave, lane, w0, w2, acc0, acc1);
+      step_i4<NMT, false, 0>(As, rowp, c0, c1, s0, s1, i + 1, K, wave, lane, w1, w0, acc0, acc1);
+      break;
+    case 3:
+      step_i4<NMT, true, kW>(As, rowp, c0, c1, s0, s1, i, K, wave, lane, w0, w2, acc0, acc1);
+      step_i4<NMT, false, kW>(As, rowp, c0, c1, s0, s1, i + 1, K, wave, lane, w1, w0, acc0, acc1);
+      step_i4<NMT, false, 0>(As, rowp, c0, c1, s0, s1, i + 2, K, wave, lane, w2, w1, acc0, acc1);
+      break;
+    default:  // 4
+      step_i4<NMT, true, kW>(As, rowp, c0, c1, s0, s1, i, K, wave, lane, w0, w2, acc0, acc1);
+      step_i4<NMT, true, kW>(As, rowp, c0, c1, s0, s1, i + 1, K, wave, lane, w1, w0, acc0, acc1);
+      step_i4<NMT, false, kW>(As, rowp, c0, c1, s0, s1, i + 2, K, wave, lane, w2, w1, acc0, acc1);
+      step_i4<NMT, false, 0>(As, rowp, c0, c1, s0, s1, i + 3, K, wave, lane, w0, w2, acc0, acc1);
+      break;
+  }
+}
+
+// Packed-weight grouped GEMMs: the bf16 kernels' mapping and activation path,
+// int4 weights widened exactly to fp16 in registers. gate_up writes the gated
+// activation as fp16, down its fp32 sums as bf16.
+template <bool GATE_UP>
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))) void k_gemm_i4p(GemmArgs a) {
+  __shared__ __attribute__((aligned(16))) char As[kDepthI4 * kStageBytes];
+  const int F = a.F, D = a.D;
+  const int K = GATE_UP ? D : F;
+  const int G = (K + kKS - 1) / kKS;
+  const int qx = blockIdx.x & (kQueues - 1);
+  const int j = blockIdx.x / kQueues;
+  if (j >= a.qlen[qx]) return;
+  const Tile tl = a.tiles[(size_t)j * kQueues + qx];
+  const int nb = tl.nb;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int g = lane >> 4;
+  const int nmt = (tl.mc + 15) >> 4;
+
+  const uint16_t* rowp[kDmaInstr];
+#pragma unroll
+  for (int i = 0; i < kDmaInstr; ++i) {
+    const int r = min(kDmaRows * (wave + kWaves * i) + lane / kSegs, tl.mc - 1);
+    rowp[i] = GATE_UP ? a.h + (size_t)(a.sorted_slot[tl.row0 + r] / a.K) * D : a.act + (size_t)(tl.row0 + r) * F;
+  }
+  int col, p0, p1, NP;
+  if (GATE_UP) {
+    col = nb * 16 * kWaves + wave * 16 + (lane & 15);
+    NP = 2 * F / 16;
+    p0 = nb * kWaves + wave;
+    p1 = p0 + F / 16;
+  } else {
+    col = nb * 32 * kWaves + wave * 32 + (lane & 15);
+    NP = D / 16;
+    p0 = 2 * (nb * kWaves + wave);
+    p1 = p0 + 1;
+  }
+  const uint8_t* C = static_cast<const uint8_t*>(GATE_UP ? a.w_gate_up : a.w_down);
+  const uint16_t* S = GATE_UP ? a.s_gate_up : a.s_down;
+  const size_t b0 = ((size_t)tl.e * NP + p0) * G, b1 = ((size_t)tl.e * NP + p1) * G;
+  const uint8_t* c0 = C + b0 * 1024 + lane * 16;
+  const uint8_t* c1 = C + b1 * 1024 + lane * 16;
+  const uint16_t* s0 = S + b0 * 16 + (lane & 15);
+  const uint16_t* s1 = S + b1 * 16 + (lane & 15);
+
+  f32x4 acc0[kBMT], acc1[kBMT];
+#pragma unroll
+  for (int i = 0; i < kBMT; ++i) {
+    acc0[i] = f32x4{0.f, 0.f, 0.f, 0.f};
+    acc1[i] = f32x4{0.f, 0.f, 0.f, 0.f};
+  }
+  switch (nmt) {
+    case 1: loop_i4<1>(As, rowp, c0, c1, s0, s1, K, tid, acc0, acc1); break;
+    case 2: loop_i4<2>(As, rowp, c0, c1, s0, s1, K, tid, acc0, acc1); break;
+    case 3: loop_i4<3>(As, rowp, c0, c1, s0, s1, K, tid, acc0, acc1); break;
+    default: loop_i4<4>(As, rowp, c0, c1, s0, s1, K, tid, acc0, acc1); break;
+  }
+
+#pragma unroll
+  for (int mt = 0; mt < kBMT; ++mt) {
+    if (mt < nmt) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int r = mt * 16 + g * 4 + i;
+        if (r < tl.mc) {
+          if (GATE_UP) {
+            const _Float16 v = (_Float16)(gelu_tanh(acc0[mt][i]) * acc1[mt][i]);
+            a.act[(size_t)(tl.row0 + r) * F + col] = __builtin_bit_cast(uint16_t, v);
+          } else {
+            uint16_t* yr = a.y + (size_t)(tl.row0 + r) * D + col;
+            yr[0] = f32_to_bf16_bits(acc0[mt][i]);
+            yr[16] = f32_to_bf16_bits(acc1[mt][i]);
+          }
+        }
+      }
+    }
+  }
+}
+
 }  // namespace
 
+hipError_t launch_pack_i4(const uint8_t* codes, const uint16_t* scales, uint8_t* pcodes, uint16_t* pscales, int E,
+                          int R, int K, hipStream_t stream) {
+  k_pack_i4<<<dim3(4096), dim3(256), 0, stream>>>(codes, scales, pcodes, pscales, E, R, K);
+  return hipGetLastError();
+}
+
 hipError_t launch_gate_up_i4(const GemmArgs& a, hipStream_t stream, const KernelEvents* ev) {
+  if (a.w_packed) return launch_kernel(k_gemm_i4p<true>, dim3(kQueues * a.qmax), dim3(kThreads), stream, ev, a);
   return launch_kernel(k_gate_up_i4, dim3(kQueues * a.qmax), dim3(kThreads), stream, ev, a);
 }
 
 hipError_t launch_down_i4(const GemmArgs& a, hipStream_t stream, const KernelEvents* ev) {
+  if (a.w_packed) return launch_kernel(k_gemm_i4p<false>, dim3(kQueues * a.qmax), dim3(kThreads), stream, ev, a);
   return launch_kernel(k_down_i4, dim3(kQueues * a.qmax), dim3(kThreads), stream, ev, a);
 }
 

@@ -96,7 +96,7 @@ struct GemmArgs {
   uint16_t* act;           // [K T, F] gelu_tanh(gate) * up, expert-sorted rows
   uint16_t* y;             // [K T, D] bf16 down(act), expert-sorted rows
   int D, F;
-  int w_packed;            // bf16 weights in the panel-fragment layout of launch_pack_panels
+  int w_packed;            // weights in the fragment layout of launch_pack_panels / launch_pack_i4
 };
 // Create-time relayout of bf16 expert weights [E][R][K] (R % 16 == 0,
 // K % 32 == 0) into MFMA fragment order: 1 KB block (e, p, s) holds, at lane
@@ -106,6 +106,12 @@ struct GemmArgs {
 hipError_t launch_pack_panels(const uint16_t* src, uint16_t* dst, int E, int R, int K, hipStream_t stream);
 hipError_t launch_gate_up_bf16(const GemmArgs& a, hipStream_t stream, const KernelEvents* ev);
 hipError_t launch_down_bf16(const GemmArgs& a, hipStream_t stream, const KernelEvents* ev);
+// Create-time relayout of int4-g128 expert weights (codes [E][R][K/2], scales
+// [E][R][ceil(K/128)]) into fragment order: 1 KB of codes and 16 scales per
+// (expert, 16-row panel, 128-input group), the short last group padded with
+// code 8 (zero).
+hipError_t launch_pack_i4(const uint8_t* codes, const uint16_t* scales, uint8_t* pcodes, uint16_t* pscales, int E,
+                          int R, int K, hipStream_t stream);
 hipError_t launch_gate_up_i4(const GemmArgs& a, hipStream_t stream, const KernelEvents* ev);
 hipError_t launch_down_i4(const GemmArgs& a, hipStream_t stream, const KernelEvents* ev);
 

@@ -102,26 +102,30 @@ def test_encode2304_sampled():
     print(f"err {r['err']:.3e} near-ties {r['near_ties']}")
 
 
-def test_int4_g128():
+@pytest.mark.parametrize("pack", [False, True], ids=["borrow", "pack"])
+def test_int4_g128(pack):
     wl = synth.WORKLOADS["int4"]
-    _say(f"{wl.name} T={wl.T}")
+    _say(f"{wl.name} T={wl.T} pack={pack}")
     inp = synth.make_inputs(wl, device="cuda")
     w = inp["layers"][0]
-    layer = _layer(w, wl.T, torch.bfloat16)
+    layer = _layer(w, wl.T, torch.bfloat16, pack=pack)
     rng = np.random.default_rng(1)
     tok = np.unique(np.concatenate([[0, wl.T - 1], rng.choice(wl.T, 100, replace=False)]))
     r = layer_parity(layer, inp["x"], oracle_weights(w), wl.K, tokens=tok)
     print(f"err {r['err']:.3e} near-ties {r['near_ties']}")
 
 
-def test_int4_small_tail_group():
-    # d_ff = 192 = 128 + 64: the down projection's last scale group is 64 wide
-    _say("int4 small E=12 K=3 D=256 F=192 T=50")
-    wl = synth.small_workload(T=50, E=12, K=3, D=256, F=192, experts="i4g128", seed=8)
+@pytest.mark.parametrize("E,K,T", [(12, 3, 50), (8, 4, 200)])
+@pytest.mark.parametrize("pack", [False, True], ids=["borrow", "pack"])
+def test_int4_small_tail_group(E, K, T, pack):
+    # d_ff = 192 = 128 + 64: the down projection's last scale group is 64 wide;
+    # T = 200 on 8 experts fills tiles of up to 64 rows
+    _say(f"int4 small E={E} K={K} D=256 F=192 T={T} pack={pack}")
+    wl = synth.small_workload(T=T, E=E, K=K, D=256, F=192, experts="i4g128", seed=8 + T)
     inp = synth.make_inputs(wl, device="cuda")
     w = inp["layers"][0]
-    layer = _layer(w, 50, torch.bfloat16, K=3)
-    layer_parity(layer, inp["x"], oracle_weights(w), 3)
+    layer = _layer(w, T, torch.bfloat16, K=K, pack=pack)
+    layer_parity(layer, inp["x"], oracle_weights(w), K)
 
 
 # ----------------------------------------------------------------------------- edge cases
