@@ -305,13 +305,19 @@ __global__ __launch_bounds__(kThreads) void k_down_i4(GemmArgs a) {
 // So a wave reads one weight fragment as 1 KB contiguous, and the activation
 // fragments are exactly the bf16 kernels' (same LDS layout and DMA).
 
+// (a & mask) | 0x64006400 in one three-input bitwise operation (truth table
+// 0xEA: (A & B) | C).
+__device__ __forceinline__ uint32_t nib_pair(uint32_t a) {
+  return __builtin_amdgcn_bitop3_b32(a, 0x000F000Fu, 0x64006400u, 0xEA);
+}
+
 // 8 codes of the packed order -> 8 fp16 values (q - 8) in natural order.
 __device__ __forceinline__ f16x8 dequant8n(uint32_t v) {
   const f16x2 bias = f16x2{(_Float16)-1032.0f, (_Float16)-1032.0f};
-  const f16x2 p0 = __builtin_bit_cast(f16x2, (v & 0x000F000Fu) | 0x64006400u) + bias;          // k0 k1
-  const f16x2 p1 = __builtin_bit_cast(f16x2, ((v >> 4) & 0x000F000Fu) | 0x64006400u) + bias;   // k2 k3
-  const f16x2 p2 = __builtin_bit_cast(f16x2, ((v >> 8) & 0x000F000Fu) | 0x64006400u) + bias;   // k4 k5
-  const f16x2 p3 = __builtin_bit_cast(f16x2, ((v >> 12) & 0x000F000Fu) | 0x64006400u) + bias;  // k6 k7
+  const f16x2 p0 = __builtin_bit_cast(f16x2, nib_pair(v)) + bias;        // k0 k1
+  const f16x2 p1 = __builtin_bit_cast(f16x2, nib_pair(v >> 4)) + bias;   // k2 k3
+  const f16x2 p2 = __builtin_bit_cast(f16x2, nib_pair(v >> 8)) + bias;   // k4 k5
+  const f16x2 p3 = __builtin_bit_cast(f16x2, nib_pair(v >> 12)) + bias;  // k6 k7
   f16x8 r;
   r[0] = p0[0]; r[1] = p0[1]; r[2] = p1[0]; r[3] = p1[1];
   r[4] = p2[0]; r[5] = p2[1]; r[6] = p3[0]; r[7] = p3[1];
