@@ -91,7 +91,7 @@ def algorithmic(wl, T, touched):
 def kernel_sources_digest():
     h = hashlib.sha256()
     csrc = os.path.join(ROOT, "expert_ffn_canvas_amd", "csrc")
-    for name in ("gemm_bf16.hip", "dg_common.h", "launch.h"):
+    for name in ("gemm_bf16.hip", "gemm_common.h", "dg_common.h", "launch.h"):
         with open(os.path.join(csrc, name), "rb") as f:
             h.update(f.read())
     return h.hexdigest()[:16]
