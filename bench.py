@@ -244,6 +244,8 @@ def main():
             for k in range(nk):
                 tot[k] += ev.elapsed_ms(evs[2 * nk * i + 2 * k], evs[2 * nk * i + 2 * k + 1])
         kern_us = {name: round(tot[k] / n_prof * 1e3, 2) for k, name in enumerate(KERNEL_NAMES)}
+        if layers[0].expert_norm_folded:  # no norm kernel ran: its events bracket nothing
+            kern_us["norm"] = 0.0
         ev.destroy(evs)
     ev.destroy([e0, e1])
 

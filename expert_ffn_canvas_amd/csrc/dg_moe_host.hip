@@ -2,7 +2,8 @@
 // workspace allocated once at create time, router-weight preparation, and the
 // asynchronous launch sequence of one forward:
 //
-//   router (norm + expert input, then logits + top-k + weights)
+//   router (the expert input where it is materialised, then r + logits +
+//   top-k + weights)
 //   -> permutation (counts, offsets, tile list, stable scatter)
 //   -> gate_up grouped GEMM (+ GELU-tanh gating)
 //   -> down grouped GEMM (x routing weight)
@@ -49,19 +50,27 @@ size_t act_elem_bytes(int dt) { return dt == DG_F32 ? 4 : 2; }
 
 // Sub-buffer layout of the workspace (byte offsets from the base).
 struct Layout {
-  size_t h, z, logits, tile_count, topk_idx, topk_w, counts, offsets, tasks[2], qlen, sorted_slot, row_of_slot, act,
+  size_t h, rnorm, logits, tile_count, topk_idx, topk_w, counts, offsets, tasks[2], qlen, sorted_slot, row_of_slot, act,
       y;
-  size_t wr, gamma_r, bias, gamma_e;
+  size_t wr, bias, gamma_e;
   size_t total;
-  int Epad, n_wplanes, nb[2], qmax[2];  // per GEMM (gate_up, down): column blocks, queue capacity
+  int Epad, nb[2], qmax[2];  // per GEMM (gate_up, down): column blocks, queue capacity
+  // bf16 activations with packed bf16 experts: (1 + gamma_e) is folded into
+  // the packed gate_up weight, the gate_up GEMM reads x and scales its sums by
+  // r, and the expert input h is never materialised
+  bool fold;
 };
+
+bool folds_expert_norm(const dg_moe_config& c) {
+  return (c.flags & DG_MOE_PACK_WEIGHTS) && c.expert_w_dtype == DG_BF16 && c.act_dtype == DG_BF16;
+}
 
 Layout plan(const dg_moe_config& c) {
   Layout L{};
   const size_t T = (size_t)c.max_tokens, D = (size_t)c.d_model, F = (size_t)c.d_ff;
   const size_t E = (size_t)c.n_experts, K = (size_t)c.top_k;
   L.Epad = (int)round_up(E, 32);
-  L.n_wplanes = (c.router_w_dtype == DG_F32) ? 3 : 1;
+  L.fold = folds_expert_norm(c);
   L.nb[0] = dg::gate_up_blocks((int)F);
   L.nb[1] = dg::down_blocks((int)D);
   for (int g = 0; g < 2; ++g) L.qmax[g] = dg::max_queue_len((int)T, (int)K, (int)E, L.nb[g]);
@@ -71,8 +80,8 @@ Layout plan(const dg_moe_config& c) {
     off = round_up(off + bytes, 256);
     return at;
   };
-  L.h = take(T * D * 2);
-  L.z = take(3 * T * D * 2);
+  L.h = take(L.fold ? 0 : T * D * 2);
+  L.rnorm = take(T * 4);
   L.logits = take(T * (size_t)L.Epad * 4);
   L.tile_count = take((T + 15) / 16 * 4);
   L.topk_idx = take(T * K * 4);
@@ -85,8 +94,7 @@ Layout plan(const dg_moe_config& c) {
   L.row_of_slot = take(K * T * 4);
   L.act = take(K * T * F * 2);
   L.y = take(K * T * D * 2);
-  L.wr = take((size_t)L.n_wplanes * L.Epad * D * 2);
-  L.gamma_r = take(D * 4);
+  L.wr = take(3 * (size_t)L.Epad * D * 2);
   L.bias = take(E * 4);
   L.gamma_e = take(D * 4);
   L.total = off;
@@ -259,10 +267,10 @@ dg_status dg_moe_create(const dg_moe_config* cfg, const dg_moe_weights* w, void*
     } else {  // bf16: MFMA fragment order, 1 KB per wave-wide read
       c1 = dg::launch_pack_panels(static_cast<const uint16_t*>(w->w_gate_up),
                                   static_cast<uint16_t*>(const_cast<void*>(hd->w_gate_up)), cfg->n_experts,
-                                  2 * cfg->d_ff, cfg->d_model, stream);
+                                  2 * cfg->d_ff, cfg->d_model, hd->L.fold ? w->ffn_gamma : nullptr, stream);
       c2 = dg::launch_pack_panels(static_cast<const uint16_t*>(w->w_down),
                                   static_cast<uint16_t*>(const_cast<void*>(hd->w_down)), cfg->n_experts,
-                                  cfg->d_model, cfg->d_ff, stream);
+                                  cfg->d_model, cfg->d_ff, nullptr, stream);
       hd->w_packed = 1;
     }
     if (c1 != hipSuccess || c2 != hipSuccess || c3 != hipSuccess || c4 != hipSuccess) {
@@ -277,13 +285,12 @@ dg_status dg_moe_create(const dg_moe_config* cfg, const dg_moe_weights* w, void*
   }
   hd->has_bias = w->router_bias != nullptr;
   const size_t D = cfg->d_model, E = cfg->n_experts;
-  hipError_t c[4];
-  c[0] = hipMemcpyAsync(hd->ws + hd->L.gamma_r, w->router_gamma, D * 4, hipMemcpyDeviceToDevice, stream);
-  c[1] = hipMemcpyAsync(hd->ws + hd->L.gamma_e, w->ffn_gamma, D * 4, hipMemcpyDeviceToDevice, stream);
-  c[2] = hd->has_bias ? hipMemcpyAsync(hd->ws + hd->L.bias, w->router_bias, E * 4, hipMemcpyDeviceToDevice, stream)
+  hipError_t c[3];
+  c[0] = hipMemcpyAsync(hd->ws + hd->L.gamma_e, w->ffn_gamma, D * 4, hipMemcpyDeviceToDevice, stream);
+  c[1] = hd->has_bias ? hipMemcpyAsync(hd->ws + hd->L.bias, w->router_bias, E * 4, hipMemcpyDeviceToDevice, stream)
                       : hipSuccess;
-  c[3] = dg::launch_prep_router_w(w->router_w, cfg->router_w_dtype == DG_F32, (int)E, hd->L.Epad, (int)D,
-                                  hd->at<uint16_t>(hd->L.wr), stream);
+  c[2] = dg::launch_prep_router_w(w->router_w, cfg->router_w_dtype == DG_F32, w->router_gamma, (int)E, hd->L.Epad,
+                                  (int)D, hd->at<uint16_t>(hd->L.wr), stream);
   for (hipError_t ci : c) {
     if (ci != hipSuccess) {
       dg_moe_destroy(hd);
@@ -344,19 +351,25 @@ static dg_status run_forward(dg_moe_handle hd, const void* x, void* out, int32_t
   ra.Epad = L.Epad;
   ra.K = c.top_k;
   ra.wr = hd->at<uint16_t>(L.wr);
-  ra.n_wplanes = L.n_wplanes;
-  ra.gamma_r = hd->at<float>(L.gamma_r);
   ra.bias = hd->has_bias ? hd->at<float>(L.bias) : nullptr;
   ra.gamma_e = hd->at<float>(L.gamma_e);
   ra.eps = c.rms_eps;
   ra.h_f16 = i4 ? 1 : 0;
-  ra.h = hd->at<uint16_t>(L.h);
-  ra.z = hd->at<uint16_t>(L.z);
+  ra.h = L.fold ? nullptr : hd->at<uint16_t>(L.h);
+  ra.rnorm = hd->at<float>(L.rnorm);
   ra.logits = hd->at<float>(L.logits);
   ra.tile_count = hd->at<int32_t>(L.tile_count);
   ra.topk_idx = hd->at<int32_t>(L.topk_idx);
   ra.topk_w = hd->at<float>(L.topk_w);
-  hipError_t e = dg::launch_router(ra, stream, ev(0));
+  hipError_t e = hipSuccess;
+  if (!L.fold) {
+    e = dg::launch_norm(ra, stream, ev(0));
+  } else if (events) {  // no norm kernel: its two events mark the same point
+    e = hipEventRecord(kev[0].start, stream);
+    if (e == hipSuccess) e = hipEventRecord(kev[0].stop, stream);
+  }
+  if (e != hipSuccess) return hip_fail(e, "norm launch");
+  e = dg::launch_logits(ra, stream, ev(1));
   if (e != hipSuccess) return hip_fail(e, "router launch");
 
   dg::PermuteArgs pa{};
@@ -383,7 +396,8 @@ static dg_status run_forward(dg_moe_handle hd, const void* x, void* out, int32_t
   ga.qmax = pa.qmax[0];
   ga.sorted_slot = pa.sorted_slot;
   ga.K = c.top_k;
-  ga.h = ra.h;
+  ga.h = L.fold ? static_cast<const uint16_t*>(x) : ra.h;
+  ga.rnorm = L.fold ? ra.rnorm : nullptr;
   ga.w_gate_up = hd->w_gate_up;
   ga.w_down = hd->w_down;
   ga.w_packed = hd->w_packed;

@@ -3,7 +3,10 @@
 //  gate_up: for each tile (expert e, rows row0 .. row0+mc-1, mc <= 64) and
 //           each block of 64 d_ff features: g = h W_gate[e]^T and
 //           u = h W_up[e]^T over the full d_model, then act = gelu_tanh(g) * u
-//           (bf16).
+//           (bf16). Where the expert input is not materialised, the rows are
+//           the raw x, the packed weight holds W diag(1 + gamma_e), and g and
+//           u are scaled by each token's r: the same h W^T, with the norm
+//           applied on the other side of the product.
 //  down:    for each tile and each block of 128 d_model outputs:
 //           y = act W_down[e]^T (fp32 sums, stored as bf16), one row per routed
 //           slot (the combine applies the routing weights).
@@ -158,6 +161,7 @@ __device__ __forceinline__ void k_loop(char* As, const uint16_t* const (&rowp)[k
 template <bool GATE_UP, bool PK>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3, 3))) void k_gemm_bf16(GemmArgs a) {
   __shared__ __attribute__((aligned(16))) char As[2 * kStageBytes];
+  __shared__ float rrow[kTileRows];  // gate_up: r of each row's token, or 1
   const int F = a.F, D = a.D;
   const int K = GATE_UP ? D : F;
   const int qx = blockIdx.x & (kQueues - 1);
@@ -168,6 +172,11 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3, 3))
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int g = lane >> 4;
   const int nmt = (tl.mc + 15) >> 4;
+  if (GATE_UP) {
+    if (tid < kTileRows)
+      rrow[tid] = (a.rnorm != nullptr && tid < tl.mc) ? a.rnorm[a.sorted_slot[tl.row0 + tid] / a.K] : 1.0f;
+    __syncthreads();
+  }
 
   // source row of each DMA instruction of this lane (rows past the tile re-read
   // its last row; their results are never stored)
@@ -225,7 +234,9 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3, 3))
         const int r = mt * 16 + g * 4 + i;
         if (r < tl.mc) {
           if (GATE_UP) {
-            a.act[(size_t)(tl.row0 + r) * F + col] = f32_to_bf16_bits(gelu_tanh(acc0[mt][i]) * acc1[mt][i]);
+            const float rr = rrow[r];
+            a.act[(size_t)(tl.row0 + r) * F + col] =
+                f32_to_bf16_bits(gelu_tanh(acc0[mt][i] * rr) * (acc1[mt][i] * rr));
           } else {
             uint16_t* yr = a.y + (size_t)(tl.row0 + r) * D + col;
             yr[0] = f32_to_bf16_bits(acc0[mt][i]);
@@ -237,9 +248,10 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3, 3))
   }
 }
 
-// One workgroup per block of 64 lanes x 16 bytes: block b = (e, p, s).
+// One wave per block of 64 lanes x 16 bytes: block b = (e, p, s). With
+// `gamma`, value k is scaled by (1 + gamma[k]) and rounded to bf16.
 __global__ __launch_bounds__(256) void k_pack_panels(const uint16_t* __restrict__ src, uint16_t* __restrict__ dst,
-                                                     int E, int R, int K) {
+                                                     int E, int R, int K, const float* __restrict__ gamma) {
   const int nks = K / 32, np = R / 16;
   const size_t nblk = (size_t)E * np * nks;
   const int lane = threadIdx.x & 63;
@@ -248,14 +260,21 @@ __global__ __launch_bounds__(256) void k_pack_panels(const uint16_t* __restrict_
     const size_t ep = b / nks;  // e * np + p
     const size_t row = ep * 16 + (lane & 15);
     const int k = 32 * s + 8 * (lane >> 4);
-    *reinterpret_cast<u32x4*>(dst + b * 512 + lane * 8) = *reinterpret_cast<const u32x4*>(src + row * K + k);
+    u32x4 v = *reinterpret_cast<const u32x4*>(src + row * K + k);
+    if (gamma != nullptr) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        v[i] = pack_bf16x2(bf16_lo(v[i]) * (1.0f + gamma[k + 2 * i]), bf16_hi(v[i]) * (1.0f + gamma[k + 2 * i + 1]));
+    }
+    *reinterpret_cast<u32x4*>(dst + b * 512 + lane * 8) = v;
   }
 }
 
 }  // namespace
 
-hipError_t launch_pack_panels(const uint16_t* src, uint16_t* dst, int E, int R, int K, hipStream_t stream) {
-  k_pack_panels<<<dim3(4096), dim3(256), 0, stream>>>(src, dst, E, R, K);
+hipError_t launch_pack_panels(const uint16_t* src, uint16_t* dst, int E, int R, int K, const float* gamma,
+                              hipStream_t stream) {
+  k_pack_panels<<<dim3(4096), dim3(256), 0, stream>>>(src, dst, E, R, K, gamma);
   return hipGetLastError();
 }
 

@@ -49,24 +49,25 @@ struct RouterArgs {
   const void* x;        // [T, D] fp32 or bf16
   int x_f32;
   int T, D, E, Epad, K;
-  const uint16_t* wr;   // bf16 planes [n_wplanes][Epad][D]
-  int n_wplanes;        // 1 (bf16 router weight) or 3 (fp32 split exactly)
-  const float* gamma_r;
+  const uint16_t* wr;   // W' = W_r diag(1 + gamma_r): three exact bf16 planes [3][Epad][D], fragment order
   const float* bias;    // [E] or null
   const float* gamma_e;
   float eps;
   int h_f16;            // expert input stored as fp16 (int4 experts) instead of bf16
-  uint16_t* h;          // [T, D]
-  uint16_t* z;          // [3][T][D] bf16 planes of the normalised router input
+  uint16_t* h;          // [T, D] expert input (norm kernel only)
+  float* rnorm;         // [T] r = 1/sqrt(mean x^2 + eps) of each token
   float* logits;        // [T, Epad]
   int32_t* tile_count;  // [ceil(T / 16)] arrival counters of the logits kernel, zero between forwards
   int32_t* topk_idx;    // [T, K]
   float* topk_w;        // [T, K]
 };
-// ev: null, or the events of the norm and the logits kernels (two entries).
-hipError_t launch_router(const RouterArgs& a, hipStream_t stream, const KernelEvents* ev);
-hipError_t launch_prep_router_w(const void* w, int w_f32, int E, int Epad, int D, uint16_t* planes,
-                                hipStream_t stream);
+// h = x r (1 + gamma_e).
+hipError_t launch_norm(const RouterArgs& a, hipStream_t stream, const KernelEvents* ev);
+// r, logits, top-k and the routing weights.
+hipError_t launch_logits(const RouterArgs& a, hipStream_t stream, const KernelEvents* ev);
+// Create time: W' planes from the router weight (fp32 or bf16 [E, D]) and gamma_r [D].
+hipError_t launch_prep_router_w(const void* w, int w_f32, const float* gamma_r, int E, int Epad, int D,
+                                uint16_t* planes, hipStream_t stream);
 
 struct PermuteArgs {
   const int32_t* topk_idx;
@@ -88,7 +89,9 @@ struct GemmArgs {
   int qmax;                // their capacity
   const int32_t* sorted_slot;  // [K T] slot t K + j of each expert-sorted row
   int K;
-  const uint16_t* h;       // [T, D] expert input (bf16, or fp16 for int4 experts)
+  const uint16_t* h;       // [T, D] expert input (bf16, or fp16 for int4 experts); the raw x when rnorm is set
+  const float* rnorm;      // [T] r of each token when h is the raw x and (1 + gamma_e) is folded into
+                           // w_gate_up: the gate and up sums are scaled by it; else null
   const void* w_gate_up;   // bf16 [E, 2F, D] or int4 bytes [E, 2F, D/2]
   const void* w_down;      // bf16 [E, D, F] or int4 bytes [E, D, F/2]
   const uint16_t* s_gate_up;
@@ -102,8 +105,10 @@ struct GemmArgs {
 // K % 32 == 0) into MFMA fragment order: 1 KB block (e, p, s) holds, at lane
 // l = n + 16 g, the 8 values W[e][16 p + n][32 s + 8 g .. + 7]; blocks are
 // ordered e-major, then p, then s. A wave reading one B-operand fragment of a
-// 16-row panel then reads 1 KB contiguously.
-hipError_t launch_pack_panels(const uint16_t* src, uint16_t* dst, int E, int R, int K, hipStream_t stream);
+// 16-row panel then reads 1 KB contiguously. With `gamma` ([K] fp32) each value
+// is first multiplied by (1 + gamma[k]) and rounded to bf16 (nearest even).
+hipError_t launch_pack_panels(const uint16_t* src, uint16_t* dst, int E, int R, int K, const float* gamma,
+                              hipStream_t stream);
 hipError_t launch_gate_up_bf16(const GemmArgs& a, hipStream_t stream, const KernelEvents* ev);
 hipError_t launch_down_bf16(const GemmArgs& a, hipStream_t stream, const KernelEvents* ev);
 // Create-time relayout of int4-g128 expert weights (codes [E][R][K/2], scales

@@ -1,30 +1,35 @@
-// Router of the MoE layer on gfx950, two kernels:
-//  norm:   per token r = 1/sqrt(mean x^2 + eps); the expert input
-//          h = x r (1 + gamma_e) (bf16, or fp16 for int4 experts); and the
-//          router input z = x r (1 + gamma_r) in fp32, stored as three exact
-//          bf16 planes z = z0 + z1 + z2 (each holds the next 8 significant
-//          bits of the fp32 value).
-//  router: logits = z W_r^T + b on the bf16 matrix cores (each bf16 x bf16
-//          product is exact in fp32 and the MFMA accumulates in fp32, so with
-//          z in three planes, and an fp32 router weight split the same way at
-//          create time, the logits have fp32 dot-product accuracy); then per
-//          token the k largest logits (ties: lower expert id) and their
-//          softmax renormalised over the k, slots ordered by logit.
+// Router of the MoE layer on gfx950.
+//
+//  logits + top-k (one kernel): per token r = 1/sqrt(mean_d x^2 + eps) and
+//          logits = r (W' x) + b with W' = W_r diag(1 + gamma_r), the router
+//          norm's scale folded into the router weight at create time. W' is
+//          kept in fp32 precision as three exact bf16 planes
+//          (W' = W0 + W1 + W2, each plane the next 8 significant bits), so
+//          the products on the bf16 matrix cores are exact and accumulate in
+//          fp32: the logits have fp32 dot-product accuracy. Then per token the
+//          k largest logits (ties: lower expert id), in that order, with their
+//          softmax renormalised over the k.
+//  norm:   only where the expert input has to be materialised (fp32
+//          activations, int4 experts, borrowed weights): r again and
+//          h = x r (1 + gamma_e), bf16 (fp16 for int4 experts). Otherwise the
+//          gate_up GEMM reads x itself, with (1 + gamma_e) folded into its
+//          packed weight and r applied to its sums.
 //
 // Sources: Quant-Tuner PR "Add DiffusionGemma (Gemma-4 MoE block-diffusion)
 // support", "Answers to the motivating questions" (the router reads the raw
 // residual through its own norm; pre_feedforward_layernorm_2 with the (1+gamma)
 // convention feeds the fused gate_up); 128 experts / 8 active from its Summary.
 #include "dg_common.h"
+#include "gemm_common.h"
 #include "launch.h"
 
 namespace dg {
 
 namespace {
 
-constexpr int kTokTile = 16;    // tokens per workgroup (MFMA M)
-constexpr int kKChunk = 128;    // d_model columns per chunk
-constexpr int kWaves = 8;       // waves per workgroup; wave h owns chunks h, h + 8, ...
+constexpr int kKChunk = 128;  // d_model columns per chunk
+constexpr int kWaves = 8;     // waves per workgroup; wave h owns chunks h, h + 8, ...
+constexpr int kChunkRowBytes = kKChunk * 2;
 
 // z = hi + mid + lo exactly: hi keeps the top 8 significant bits of z
 // (truncated), mid the next 8 of the remainder, and the last remainder has at
@@ -41,283 +46,289 @@ __device__ __forceinline__ uint32_t pack_hi(float a, float b) {
   return (__float_as_uint(a) >> 16) | (__float_as_uint(b) & 0xffff0000u);
 }
 
-// x values (fp32 or bf16) of one 8-column piece.
-template <bool XF32>
-struct XPiece {
-  u32x4 v[XF32 ? 2 : 1];
-};
-
-template <bool XF32>
-__device__ __forceinline__ void load_piece(const void* x, size_t off, XPiece<XF32>& p) {
-  if constexpr (XF32) {
-    p.v[0] = *reinterpret_cast<const u32x4*>(static_cast<const float*>(x) + off);
-    p.v[1] = *reinterpret_cast<const u32x4*>(static_cast<const float*>(x) + off + 4);
-  } else {
-    p.v[0] = *reinterpret_cast<const u32x4*>(static_cast<const uint16_t*>(x) + off);
-  }
-}
-
-template <bool XF32>
-__device__ __forceinline__ void piece_floats(const XPiece<XF32>& p, float (&f)[8]) {
-  if constexpr (XF32) {
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      f[i] = __uint_as_float(p.v[0][i]);
-      f[4 + i] = __uint_as_float(p.v[1][i]);
-    }
-  } else {
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      f[2 * i] = bf16_lo(p.v[0][i]);
-      f[2 * i + 1] = bf16_hi(p.v[0][i]);
-    }
-  }
-}
-
-// Order-preserving map of a float to uint32 (larger float -> larger key).
+// Order-preserving map of a float to uint32 (larger float -> larger key) and back.
 __device__ __forceinline__ uint32_t float_key(float v) {
   const uint32_t b = __float_as_uint(v);
   return (b & 0x80000000u) ? ~b : (b | 0x80000000u);
 }
-
-// Bits 0..31 (lanes 0..31) or 32..63 (lanes 32..63) of a wave-wide mask: the
-// half-wave of the calling lane.
-__device__ __forceinline__ uint32_t half_mask(uint64_t m, bool hi_half) {
-  return hi_half ? (uint32_t)(m >> 32) : (uint32_t)m;
+__device__ __forceinline__ float key_float(uint32_t k) {
+  return __uint_as_float((k & 0x80000000u) ? (k & 0x7fffffffu) : ~k);
 }
 
-// Top-k of two tokens per wave, one per half-wave; lane j of a half holds the
-// logits of experts j + 32 u (u < NU, E <= 32 NU), read from `row`.
-// A radix select on order-preserving keys finds the k-th largest key kt (the
-// largest value with at least k keys >= it). The experts above kt are taken,
-// and of those equal to kt the lowest ids fill the remaining places. The k
-// chosen are compacted in id order into cv/ci (LDS, 8 entries per half);
-// then lane p < k of the half ranks entry p by (logit desc, id asc) and
-// writes it to that slot, with its softmax over the k (exponentials summed in
-// id order).
+template <int CTRL>
+__device__ __forceinline__ uint32_t dpp(uint32_t v) {
+  return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, CTRL, 0xf, 0xf, false);
+}
+// DPP patterns inside a 16-lane row: swap neighbours, swap pairs, mirror
+// each half row, mirror the row. After all four every lane has combined all
+// sixteen.
+constexpr int kDppXor1 = 0xb1, kDppXor2 = 0x4e, kDppHalfMirror = 0x141, kDppMirror = 0x140;
+
+// Keep the larger (key, -id) of this lane's and the partner lane's.
+template <int CTRL>
+__device__ __forceinline__ void argmax_step(uint32_t& key, uint32_t& id) {
+  const uint32_t ok = dpp<CTRL>(key), oi = dpp<CTRL>(id);
+  const bool take = ok > key || (ok == key && oi < id);
+  key = take ? ok : key;
+  id = take ? oi : id;
+}
+
+template <int CTRL>
+__device__ __forceinline__ float add_step(float v) {
+  return v + __uint_as_float(dpp<CTRL>(__float_as_uint(v)));
+}
+
+// Top-k of one token per 16-lane row: lane j holds the logits of experts
+// j + 16 u (u < NU, E <= 16 NU), read from `row`. Round q takes the largest
+// remaining (logit, lowest id) of the row and removes it, so the k rounds
+// produce the selection in slot order (logit descending, ties by id). Lane
+// q < k keeps round q's pick and writes slot q with its softmax over the k
+// (the shift by the largest logit cancels in the renormalisation). A NaN
+// logit ranks below every number; experts >= E are never picked.
 template <int NU>
-__device__ __forceinline__ void topk_half(const float* row, bool active, int E, int K, int lane, float* cv,
-                                          int* ci, int32_t* idx_out, float* w_out) {
-  const bool hi_half = lane >= 32;
-  const int j = lane & 31;
-  const uint32_t lt = (1u << j) - 1u;
-  float v[NU];
+__device__ __forceinline__ void topk_row(const float* row, bool active, int E, int K, int j, int32_t* idx_out,
+                                         float* w_out) {
+  // all NU loads issued at once (a clamped index instead of a guarded load,
+  // which would wait for each load in turn), masked afterwards
+  float lv[NU];
+#pragma unroll
+  for (int u = 0; u < NU; ++u) lv[u] = row[min(j + 16 * u, E - 1)];
   uint32_t key[NU];
 #pragma unroll
   for (int u = 0; u < NU; ++u) {
-    const int e = j + 32 * u;
-    float l = -INFINITY;
-    if (active && e < E) l = row[e];
-    v[u] = (l == l) ? l : -INFINITY;  // a NaN logit ranks last
-    key[u] = (active && e < E) ? float_key(v[u]) : 0u;  // absent experts rank below every real one
+    const float l = (lv[u] == lv[u]) ? lv[u] : -INFINITY;
+    key[u] = (j + 16 * u < E) ? float_key(l) : 0u;  // every real expert's key is > 0
   }
-  uint32_t kt = 0;
-  for (int b = 31; b >= 0; --b) {
-    const uint32_t cand = kt | (1u << b);
-    int c = 0;
+  uint32_t my_key = 0, my_id = 0, top = 0;
+  for (int q = 0; q < K; ++q) {
+    uint32_t bk = key[0], bi = (uint32_t)j;
 #pragma unroll
-    for (int u = 0; u < NU; ++u) c += __popc(half_mask(__ballot(key[u] >= cand), hi_half));
-    kt = (c >= K) ? cand : kt;
-  }
-  int above = 0;
-#pragma unroll
-  for (int u = 0; u < NU; ++u) above += __popc(half_mask(__ballot(key[u] > kt), hi_half));
-  int need = K - above;
-  int base = 0;
-#pragma unroll
-  for (int u = 0; u < NU; ++u) {
-    const bool eq = key[u] == kt;
-    const uint32_t me = half_mask(__ballot(eq), hi_half);
-    const bool sel = key[u] > kt || (eq && __popc(me & lt) < need);
-    need -= min(__popc(me), max(need, 0));
-    const uint32_t ms = half_mask(__ballot(sel), hi_half);
-    if (sel) {
-      const int p = base + __popc(ms & lt);
-      cv[p] = v[u];
-      ci[p] = j + 32 * u;
+    for (int u = 1; u < NU; ++u) {
+      const bool gt = key[u] > bk;  // strict: on equal keys the lower id stays
+      bk = gt ? key[u] : bk;
+      bi = gt ? (uint32_t)(j + 16 * u) : bi;
     }
-    base += __popc(ms);
+    argmax_step<kDppXor1>(bk, bi);
+    argmax_step<kDppXor2>(bk, bi);
+    argmax_step<kDppHalfMirror>(bk, bi);
+    argmax_step<kDppMirror>(bk, bi);
+    top = (q == 0) ? bk : top;
+    if (j == q) {
+      my_key = bk;
+      my_id = bi;
+    }
+    const bool own = (int)(bi & 15u) == j;
+#pragma unroll
+    for (int u = 0; u < NU; ++u) key[u] = (own && (int)(bi >> 4) == u) ? 0u : key[u];
   }
-  __builtin_amdgcn_wave_barrier();
-  __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
+  const float ex = (j < K) ? __expf(key_float(my_key) - key_float(top)) : 0.0f;
+  float den = add_step<kDppXor1>(ex);
+  den = add_step<kDppXor2>(den);
+  den = add_step<kDppHalfMirror>(den);
+  den = add_step<kDppMirror>(den);
   if (active && j < K) {
-    const float vp = cv[j];
-    const int ip = ci[j];
-    float vmax = -INFINITY;
-    int rank = 0;
-    for (int q = 0; q < K; ++q) {
-      const float vq = cv[q];
-      vmax = fmaxf(vmax, vq);
-      rank += (vq > vp) || (vq == vp && ci[q] < ip);
-    }
-    float den = 0.0f;
-    for (int q = 0; q < K; ++q) den += __expf(cv[q] - vmax);
-    idx_out[rank] = ip;
-    w_out[rank] = __expf(vp - vmax) / den;
+    idx_out[j] = (int32_t)my_id;
+    w_out[j] = ex / den;
   }
 }
 
-// One workgroup of 256 threads per token; thread i owns the 8-column pieces
-// i, i + 256, ... (up to NP of them: d_model <= 2048 NP). All loads of a
-// thread (x and both gammas) are issued together, one block reduction gives r.
-template <bool XF32, int NP>
-__global__ __launch_bounds__(256) void k_norm(RouterArgs a) {
-  __shared__ float wsum[4];
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int t = blockIdx.x;
-  const int D = a.D;
-  const int nseg = D / 8;
-  const size_t row = (size_t)t * D;
-  XPiece<XF32> xp[NP];
-  float4 gr[NP][2], ge[NP][2];
+// bf16 x values of one MFMA operand (8 consecutive columns) -> sum of squares.
+__device__ __forceinline__ float sumsq8(const u32x4& v) {
+  float s = 0.0f;
 #pragma unroll
-  for (int i = 0; i < NP; ++i) {
-    const int sg = tid + 256 * i;
-    if (sg < nseg) {
-      load_piece<XF32>(a.x, row + sg * 8, xp[i]);
-      gr[i][0] = *reinterpret_cast<const float4*>(a.gamma_r + sg * 8);
-      gr[i][1] = *reinterpret_cast<const float4*>(a.gamma_r + sg * 8 + 4);
-      ge[i][0] = *reinterpret_cast<const float4*>(a.gamma_e + sg * 8);
-      ge[i][1] = *reinterpret_cast<const float4*>(a.gamma_e + sg * 8 + 4);
-    }
+  for (int i = 0; i < 4; ++i) {
+    s = fmaf(bf16_lo(v[i]), bf16_lo(v[i]), s);
+    s = fmaf(bf16_hi(v[i]), bf16_hi(v[i]), s);
   }
-  float ss = 0.0f;
-#pragma unroll
-  for (int i = 0; i < NP; ++i) {
-    if (tid + 256 * i < nseg) {
-      float f[8];
-      piece_floats<XF32>(xp[i], f);
-#pragma unroll
-      for (int k = 0; k < 8; ++k) ss += f[k] * f[k];
-    }
-  }
-  for (int msk = 32; msk >= 1; msk >>= 1) ss += __shfl_xor(ss, msk);
-  if (lane == 0) wsum[wave] = ss;
-  __syncthreads();
-  const float tot = (wsum[0] + wsum[1]) + (wsum[2] + wsum[3]);
-  const float r = 1.0f / sqrtf(tot / (float)D + a.eps);
-  const size_t plane = (size_t)a.T * D;
-#pragma unroll
-  for (int i = 0; i < NP; ++i) {
-    const int sg = tid + 256 * i;
-    if (sg >= nseg) continue;
-    float f[8];
-    piece_floats<XF32>(xp[i], f);
-    const float g1[8] = {gr[i][0].x, gr[i][0].y, gr[i][0].z, gr[i][0].w, gr[i][1].x, gr[i][1].y, gr[i][1].z, gr[i][1].w};
-    const float g2[8] = {ge[i][0].x, ge[i][0].y, ge[i][0].z, ge[i][0].w, ge[i][1].x, ge[i][1].y, ge[i][1].z, ge[i][1].w};
-    float zh[8], zm[8], zl[8], hv[8];
-#pragma unroll
-    for (int k = 0; k < 8; ++k) {
-      const float xr = f[k] * r;
-      split3(xr * (1.0f + g1[k]), zh[k], zm[k], zl[k]);
-      hv[k] = xr * (1.0f + g2[k]);
-    }
-    u32x4 o0, o1, o2, ho;
-#pragma unroll
-    for (int k = 0; k < 4; ++k) {
-      o0[k] = pack_hi(zh[2 * k], zh[2 * k + 1]);
-      o1[k] = pack_hi(zm[2 * k], zm[2 * k + 1]);
-      o2[k] = pack_hi(zl[2 * k], zl[2 * k + 1]);
-      ho[k] = a.h_f16 ? pack_f16x2(hv[2 * k], hv[2 * k + 1]) : pack_bf16x2(hv[2 * k], hv[2 * k + 1]);
-    }
-    const size_t off = row + sg * 8;
-    *reinterpret_cast<u32x4*>(a.z + off) = o0;
-    *reinterpret_cast<u32x4*>(a.z + plane + off) = o1;
-    *reinterpret_cast<u32x4*>(a.z + 2 * plane + off) = o2;
-    *reinterpret_cast<u32x4*>(a.h + off) = ho;
-  }
+  return s;
 }
 
-// Workgroup (token tile tt, expert tile et): 16 tokens x 16 experts, 8 waves;
-// wave h owns the 128-column chunks h, h + 8, ... of d_model. Lane
-// (m = l % 16, g = l / 16) loads, in each chunk, the 8-column pieces g, g + 4,
-// g + 8, g + 12 of token m's three z planes and of expert m's router weight:
-// the MFMA operand layouts. A wave issues the loads of kGroup chunks at once
-// (a chunk past its last is re-read and multiplied by a zero weight, so the
-// loop has no branches), then multiplies. The eight partial sums are added
-// through LDS in a fixed order.
+// Workgroup (token tile tt, expert tile et): 16 MT tokens x 16 experts, 8
+// waves; wave h owns the 128-column chunks h, h + 8, ... of d_model and keeps
+// G of them in flight. Per chunk, bf16 x rows are copied into the wave's own
+// LDS slot by full-line transfers (row r's 16-byte segment s at position
+// s ^ (r % 16)), and lane (m = l % 16, g = l / 16) reads token m's 8-column
+// pieces from there in the MFMA operand layout; fp32 x is loaded in that
+// layout directly and split into three exact bf16 planes in registers. W'
+// is stored in fragment order, so every weight read is 1 KB contiguous per
+// wave. A chunk past the wave's last re-reads its last one with a zero
+// weight and no share of the sum of squares, so the loop has no branches.
+// The partial sums (three accumulators per m-tile, one per W' plane, and
+// the sums of squares) are added through LDS in a fixed order; every expert
+// tile of a token tile computes the same r bit for bit.
 // All expert tiles of a token tile run on one XCD (workgroup b runs on XCD
-// b % 8) and share its L2: each one publishes its logits with a counter and
-// the last to arrive selects the top-k of the 16 rows.
-// GROUPS: chunks whose loads a wave keeps in flight at once. Three (two for
-// fp32 router weights) take one round trip per wave at d_model <= 3072 but
-// hold about 200 registers, so one workgroup fits a CU; one group lets two
-// workgroups share a CU, which pays when there are many token tiles.
-template <int NWP, int NU, bool WIDE>
+// b % 8) and share its L2: each publishes its logits with a counter and the
+// last to arrive selects the top-k of all the tile's tokens, one per 16-lane
+// row.
+template <bool XF32, int MT, int G, int NU>
 __global__ __launch_bounds__(64 * kWaves) void k_logits(RouterArgs a) {
-  constexpr int kGroup = !WIDE ? 1 : (NWP == 1) ? 3 : 2;
-  __shared__ float part[kWaves][kTokTile][17];
-  __shared__ float cv[kWaves][2][8];
-  __shared__ int ci[kWaves][2][8];
+  constexpr int kRows = 16 * MT;
+  constexpr int kXsBytes = XF32 ? 0 : kWaves * G * MT * 16 * kChunkRowBytes;
+  constexpr int kPartBytes = kWaves * kRows * 17 * 4;
+  constexpr int kBuf = kXsBytes > kPartBytes ? kXsBytes : kPartBytes;
+  __shared__ __attribute__((aligned(16))) char smem[kBuf];
+  __shared__ float ssq[kWaves][kRows];
   __shared__ int is_last;
+  float(*part)[kRows][17] = reinterpret_cast<float(*)[kRows][17]>(smem);
+
   const int tid = threadIdx.x, lane = tid & 63;
   const int kh = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int n_et = a.Epad / 16;
-  const int n_tt = (a.T + kTokTile - 1) / kTokTile;
+  const int n_tt = (a.T + kRows - 1) / kRows;
   const int xq = blockIdx.x % kQueues, jq = blockIdx.x / kQueues;
   const int tt = xq + kQueues * (jq / n_et);
   const int et = jq % n_et;
   if (tt >= n_tt) return;
-  const int t0 = tt * kTokTile;
+  const int t0 = tt * kRows;
   const int D = a.D;
-  // bias of this thread's output column, fetched before the long loads
-  float bias_v = 0.0f;
+  const int nks = D / 32;
+  float bias_v = 0.0f;  // bias of this thread's output column, fetched before the long loads
   {
     const int e = et * 16 + (tid & 15);
-    if (tid < kTokTile * 16 && a.bias != nullptr && e < a.E) bias_v = a.bias[e];
+    if (a.bias != nullptr && e < a.E) bias_v = a.bias[e];
   }
   const int m = lane & 15, g = lane >> 4;
-  const int t = min(t0 + m, a.T - 1);  // rows past T re-read the last token; never stored
-  const size_t plane = (size_t)a.T * D;
   const size_t wplane = (size_t)a.Epad * D;
-  const uint16_t* zr = a.z + (size_t)t * D + g * 8;
-  const uint16_t* wrow = a.wr + (size_t)(et * 16 + m) * D + g * 8;
+  const uint16_t* wfrag = a.wr + (size_t)et * nks * 512 + lane * 8;
   const int nc = D / kKChunk;
   const int n_my = (nc - kh + kWaves - 1) / kWaves;  // chunks kh, kh + 8, ...
 
-  f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
-  for (int c0 = 0; c0 < n_my; c0 += kGroup) {
-    u32x4 zb[kGroup][4][3], wb[kGroup][4][NWP];
+  f32x4 acc[3][MT];
+  float ss[MT];
 #pragma unroll
-    for (int q = 0; q < kGroup; ++q) {
-      const int col = (kh + kWaves * min(c0 + q, n_my - 1)) * kKChunk;
+  for (int mt = 0; mt < MT; ++mt) {
+    ss[mt] = 0.0f;
 #pragma unroll
-      for (int kk = 0; kk < 4; ++kk) {
+    for (int p = 0; p < 3; ++p) acc[p][mt] = f32x4{0.f, 0.f, 0.f, 0.f};
+  }
+
+  for (int c0 = 0; c0 < n_my; c0 += G) {
+    u32x4 wb[G][4][3];
+    u32x4 xf[XF32 ? G : 1][XF32 ? MT : 1][4][2];
 #pragma unroll
-        for (int p = 0; p < 3; ++p) zb[q][kk][p] = *reinterpret_cast<const u32x4*>(zr + p * plane + col + kk * 32);
+    for (int q = 0; q < G; ++q) {
+      const int chunk = kh + kWaves * min(c0 + q, n_my - 1);
+      const int col = chunk * kKChunk;
+      if constexpr (XF32) {
 #pragma unroll
-        for (int p = 0; p < NWP; ++p) wb[q][kk][p] = *reinterpret_cast<const u32x4*>(wrow + p * wplane + col + kk * 32);
+        for (int mt = 0; mt < MT; ++mt) {
+          const float* xr = static_cast<const float*>(a.x) + (size_t)min(t0 + mt * 16 + m, a.T - 1) * D + col + g * 8;
+#pragma unroll
+          for (int kk = 0; kk < 4; ++kk) {
+            xf[q][mt][kk][0] = *reinterpret_cast<const u32x4*>(xr + kk * 32);
+            xf[q][mt][kk][1] = *reinterpret_cast<const u32x4*>(xr + kk * 32 + 4);
+          }
+        }
+      } else {
+        const uint32_t base =
+            __builtin_amdgcn_readfirstlane(gemm::lds_addr(smem) + (kh * G + q) * MT * 16 * kChunkRowBytes);
+        const uint16_t* xb = static_cast<const uint16_t*>(a.x);
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const int r = mt * 16 + 4 * i + (lane >> 4);
+            const int s = (lane & 15) ^ (r & 15);
+            gemm::lds_dma16(base + (mt * 16 + 4 * i) * kChunkRowBytes,
+                            xb + (size_t)min(t0 + r, a.T - 1) * D + col + s * 8);
+          }
       }
-    }
-    // keep every load of the group ahead of the first multiply: one memory
-    // round trip per group instead of one per operand
-    __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-    for (int q = 0; q < kGroup; ++q) {
-      const uint32_t keep = (c0 + q < n_my) ? 0xffffffffu : 0u;
 #pragma unroll
       for (int kk = 0; kk < 4; ++kk)
 #pragma unroll
-        for (int p = 0; p < NWP; ++p) {
-          u32x4 w = wb[q][kk][p];
+        for (int p = 0; p < 3; ++p)
+          wb[q][kk][p] = *reinterpret_cast<const u32x4*>(wfrag + p * wplane + (size_t)(chunk * 4 + kk) * 512);
+    }
+    // all of the group's loads are in flight before the first multiply: one
+    // memory round trip per group
+    gemm::wait_vmcnt<0>();
+    asm volatile("" ::: "memory");
 #pragma unroll
-          for (int i = 0; i < 4; ++i) w[i] &= keep;
+    for (int q = 0; q < G; ++q) {
+      const bool valid = c0 + q < n_my;
+      const uint32_t keep = valid ? 0xffffffffu : 0u;
 #pragma unroll
-          for (int zp = 0; zp < 3; ++zp) acc = mfma_bf16(as_bf16x8(zb[q][kk][zp]), as_bf16x8(w), acc);
+      for (int kk = 0; kk < 4; ++kk) {
+        bf16x8 w[3];
+#pragma unroll
+        for (int p = 0; p < 3; ++p) {
+          u32x4 v = wb[q][kk][p];
+#pragma unroll
+          for (int i = 0; i < 4; ++i) v[i] &= keep;
+          w[p] = as_bf16x8(v);
         }
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt) {
+          if constexpr (XF32) {
+            float f[8], hi[8], mid[8], lo[8];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+              f[i] = __uint_as_float(xf[q][mt][kk][0][i]);
+              f[4 + i] = __uint_as_float(xf[q][mt][kk][1][i]);
+            }
+            float s = 0.0f;
+#pragma unroll
+            for (int i = 0; i < 8; ++i) {
+              s = fmaf(f[i], f[i], s);
+              split3(f[i], hi[i], mid[i], lo[i]);
+            }
+            ss[mt] += valid ? s : 0.0f;
+            u32x4 xh, xm, xl;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+              xh[i] = pack_hi(hi[2 * i], hi[2 * i + 1]);
+              xm[i] = pack_hi(mid[2 * i], mid[2 * i + 1]);
+              xl[i] = pack_hi(lo[2 * i], lo[2 * i + 1]);
+            }
+            // the products of weight >= 2^-24 relative: (hi, mid, lo) x
+            // (W0, W1, W2) with plane indices summing to at most 2
+            acc[0][mt] = mfma_bf16(as_bf16x8(xh), w[0], acc[0][mt]);
+            acc[1][mt] = mfma_bf16(as_bf16x8(xh), w[1], acc[1][mt]);
+            acc[1][mt] = mfma_bf16(as_bf16x8(xm), w[0], acc[1][mt]);
+            acc[2][mt] = mfma_bf16(as_bf16x8(xh), w[2], acc[2][mt]);
+            acc[2][mt] = mfma_bf16(as_bf16x8(xm), w[1], acc[2][mt]);
+            acc[2][mt] = mfma_bf16(as_bf16x8(xl), w[0], acc[2][mt]);
+          } else {
+            const int r = mt * 16 + m;
+            const u32x4 xv = *reinterpret_cast<const u32x4*>(smem + (kh * G + q) * MT * 16 * kChunkRowBytes +
+                                                              r * kChunkRowBytes + (((kk * 4 + g) ^ m) * 16));
+            ss[mt] += valid ? sumsq8(xv) : 0.0f;
+#pragma unroll
+            for (int p = 0; p < 3; ++p) acc[p][mt] = mfma_bf16(as_bf16x8(xv), w[p], acc[p][mt]);
+          }
+        }
+      }
     }
   }
+  // lanes m, m + 16, m + 32, m + 48 hold parts of row m's sum of squares
 #pragma unroll
-  for (int i = 0; i < 4; ++i) part[kh][g * 4 + i][m] = acc[i];
+  for (int mt = 0; mt < MT; ++mt) {
+    float s = ss[mt];
+    s += __shfl_xor(s, 16);
+    s += __shfl_xor(s, 32);
+    if (g == 0) ssq[kh][mt * 16 + m] = s;
+  }
+  __syncthreads();  // the x slots are free: their space takes the partial sums
+#pragma unroll
+  for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) part[kh][mt * 16 + g * 4 + i][m] = (acc[0][mt][i] + acc[1][mt][i]) + acc[2][mt][i];
   __syncthreads();
-  // [16 tokens x 16 experts] (+ bias); the eight partial sums in a fixed order
-  if (tid < kTokTile * 16) {
-    const int mm = tid >> 4, n = tid & 15;
-    float sum = part[0][mm][n];
+  // [16 MT tokens x 16 experts]: the eight partial sums in a fixed order, the
+  // same for r in every expert tile
+  for (int o = tid; o < kRows * 16; o += 64 * kWaves) {
+    const int row = o >> 4, n = o & 15;
+    float sum = part[0][row][n], tot = ssq[0][row];
 #pragma unroll
-    for (int w = 1; w < kWaves; ++w) sum += part[w][mm][n];
-    sum += bias_v;
-    if (t0 + mm < a.T) a.logits[(size_t)(t0 + mm) * a.Epad + et * 16 + n] = sum;
+    for (int w = 1; w < kWaves; ++w) {
+      sum += part[w][row][n];
+      tot += ssq[w][row];
+    }
+    const float r = 1.0f / sqrtf(tot / (float)D + a.eps);
+    if (t0 + row < a.T) {
+      a.logits[(size_t)(t0 + row) * a.Epad + et * 16 + n] = r * sum + bias_v;  // n == tid % 16
+      if (et == 0 && n == 0) a.rnorm[t0 + row] = r;
+    }
   }
   // publish: every thread's stores have reached L2 before the counter moves
   __builtin_amdgcn_s_waitcnt(0);
@@ -332,66 +343,162 @@ __global__ __launch_bounds__(64 * kWaves) void k_logits(RouterArgs a) {
   // Last expert tile of this token tile: the full logit rows come from this
   // XCD's L2 (every writer ran on this XCD and waited for its stores); no
   // workgroup on this CU read these rows earlier in the launch, so its L1
-  // holds no stale copy. Wave h takes tokens t0 + 2h (lanes 0..31) and
-  // t0 + 2h + 1 (lanes 32..63).
-  const int half = lane >> 5;
-  const int tk = t0 + 2 * kh + half;
-  const bool active = tk < a.T;
-  const size_t trow = (size_t)min(tk, a.T - 1);
-  topk_half<NU>(a.logits + trow * a.Epad, active, a.E, a.K, lane, cv[kh][half], ci[kh][half],
-                a.topk_idx + trow * a.K, a.topk_w + trow * a.K);
+  // holds no stale copy. Wave h takes tokens 4 h .. 4 h + 3 of each 32-token
+  // group of the tile, one per 16-lane row.
+  for (int tl0 = 4 * kh; tl0 < kRows; tl0 += 4 * kWaves) {
+    const int tl = tl0 + (lane >> 4);
+    const bool active = t0 + tl < a.T;
+    const size_t trow = (size_t)min(t0 + tl, a.T - 1);
+    topk_row<NU>(a.logits + trow * a.Epad, active, a.E, a.K, m, a.topk_idx + trow * a.K, a.topk_w + trow * a.K);
+  }
 }
 
-// Create-time: router weight [E, D] (fp32 or bf16) -> bf16 planes [P][Epad][D],
-// rows e >= E zero. fp32 weights are split exactly into three planes.
-__global__ void k_prep_router_w(const void* __restrict__ w, int w_f32, int E, int Epad, int D,
-                                uint16_t* __restrict__ planes) {
-  const size_t n = (size_t)Epad * D;
-  for (size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += (size_t)gridDim.x * blockDim.x) {
-    const int e = (int)(i / D);
-    if (w_f32) {
-      const float v = (e < E) ? static_cast<const float*>(w)[i] : 0.0f;
-      float b0, b1, b2;
-      split3(v, b0, b1, b2);
-      planes[i] = (uint16_t)(__float_as_uint(b0) >> 16);
-      planes[n + i] = (uint16_t)(__float_as_uint(b1) >> 16);
-      planes[2 * n + i] = (uint16_t)(__float_as_uint(b2) >> 16);
-    } else {
-      planes[i] = (e < E) ? static_cast<const uint16_t*>(w)[i] : (uint16_t)0;
+// Expert input h = x r (1 + gamma_e): one workgroup of 256 threads per token;
+// thread i owns the 8-column pieces i, i + 256, ... (up to NP of them:
+// d_model <= 2048 NP). All loads of a thread are issued together; one block
+// reduction gives r.
+template <bool XF32, int NP>
+__global__ __launch_bounds__(256) void k_norm(RouterArgs a) {
+  __shared__ float wsum[4];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int t = blockIdx.x;
+  const int D = a.D;
+  const int nseg = D / 8;
+  const size_t row = (size_t)t * D;
+  float f[NP][8];
+  float4 ge[NP][2];
+#pragma unroll
+  for (int i = 0; i < NP; ++i) {
+    const int sg = tid + 256 * i;
+    if (sg < nseg) {
+      if constexpr (XF32) {
+        const float4 v0 = *reinterpret_cast<const float4*>(static_cast<const float*>(a.x) + row + sg * 8);
+        const float4 v1 = *reinterpret_cast<const float4*>(static_cast<const float*>(a.x) + row + sg * 8 + 4);
+        f[i][0] = v0.x; f[i][1] = v0.y; f[i][2] = v0.z; f[i][3] = v0.w;
+        f[i][4] = v1.x; f[i][5] = v1.y; f[i][6] = v1.z; f[i][7] = v1.w;
+      } else {
+        const u32x4 v = *reinterpret_cast<const u32x4*>(static_cast<const uint16_t*>(a.x) + row + sg * 8);
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+          f[i][2 * k] = bf16_lo(v[k]);
+          f[i][2 * k + 1] = bf16_hi(v[k]);
+        }
+      }
+      ge[i][0] = *reinterpret_cast<const float4*>(a.gamma_e + sg * 8);
+      ge[i][1] = *reinterpret_cast<const float4*>(a.gamma_e + sg * 8 + 4);
     }
   }
+  float ss = 0.0f;
+#pragma unroll
+  for (int i = 0; i < NP; ++i)
+    if (tid + 256 * i < nseg)
+#pragma unroll
+      for (int k = 0; k < 8; ++k) ss = fmaf(f[i][k], f[i][k], ss);
+  for (int msk = 32; msk >= 1; msk >>= 1) ss += __shfl_xor(ss, msk);
+  if (lane == 0) wsum[wave] = ss;
+  __syncthreads();
+  const float tot = (wsum[0] + wsum[1]) + (wsum[2] + wsum[3]);
+  const float r = 1.0f / sqrtf(tot / (float)D + a.eps);
+#pragma unroll
+  for (int i = 0; i < NP; ++i) {
+    const int sg = tid + 256 * i;
+    if (sg >= nseg) continue;
+    const float g2[8] = {ge[i][0].x, ge[i][0].y, ge[i][0].z, ge[i][0].w, ge[i][1].x, ge[i][1].y, ge[i][1].z, ge[i][1].w};
+    u32x4 ho;
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      const float h0 = f[i][2 * k] * r * (1.0f + g2[2 * k]);
+      const float h1 = f[i][2 * k + 1] * r * (1.0f + g2[2 * k + 1]);
+      ho[k] = a.h_f16 ? pack_f16x2(h0, h1) : pack_bf16x2(h0, h1);
+    }
+    *reinterpret_cast<u32x4*>(a.h + row + sg * 8) = ho;
+  }
+}
+
+// Create time: W' = W_r diag(1 + gamma_r) in fp32 (router weight fp32 or
+// bf16), split exactly into three bf16 planes, in fragment order: plane p,
+// expert tile et, 32-column step s hold one 1 KB block whose lane l = n + 16 g
+// has the 8 values of expert 16 et + n at columns 32 s + 8 g .. + 7. Experts
+// >= E are zero.
+__global__ void k_prep_router_w(const void* __restrict__ w, int w_f32, const float* __restrict__ gamma, int E,
+                                int Epad, int D, uint16_t* __restrict__ planes) {
+  const int nks = D / 32;
+  const size_t n_items = (size_t)(Epad / 16) * nks * 64;
+  const size_t plane = (size_t)Epad * D;
+  for (size_t it = (size_t)blockIdx.x * blockDim.x + threadIdx.x; it < n_items; it += (size_t)gridDim.x * blockDim.x) {
+    const int l = (int)(it % 64);
+    const size_t blk = it / 64;
+    const int s = (int)(blk % nks);
+    const int et = (int)(blk / nks);
+    const int e = et * 16 + (l & 15);
+    const int d0 = s * 32 + (l >> 4) * 8;
+    float v[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      float wv = 0.0f;
+      if (e < E) {
+        const size_t src = (size_t)e * D + d0 + i;
+        wv = w_f32 ? static_cast<const float*>(w)[src] : bf16_bits_to_f32(static_cast<const uint16_t*>(w)[src]);
+      }
+      v[i] = wv * (1.0f + gamma[d0 + i]);
+    }
+    u32x4 o[3];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      float h0, m0, l0, h1, m1, l1;
+      split3(v[2 * i], h0, m0, l0);
+      split3(v[2 * i + 1], h1, m1, l1);
+      o[0][i] = pack_hi(h0, h1);
+      o[1][i] = pack_hi(m0, m1);
+      o[2][i] = pack_hi(l0, l1);
+    }
+#pragma unroll
+    for (int p = 0; p < 3; ++p) *reinterpret_cast<u32x4*>(planes + p * plane + blk * 512 + l * 8) = o[p];
+  }
+}
+
+template <bool XF32, int MT, int G>
+void (*pick_logits(int nu))(RouterArgs) {
+  return nu <= 2 ? k_logits<XF32, MT, G, 2> : nu <= 4 ? k_logits<XF32, MT, G, 4> : nu <= 8 ? k_logits<XF32, MT, G, 8>
+                                                                                             : k_logits<XF32, MT, G, 16>;
 }
 
 }  // namespace
 
-hipError_t launch_router(const RouterArgs& a, hipStream_t stream, const KernelEvents* ev) {
+hipError_t launch_norm(const RouterArgs& a, hipStream_t stream, const KernelEvents* ev) {
   void (*kn)(RouterArgs);
   if (a.D <= 2048 * 2)
     kn = a.x_f32 ? k_norm<true, 2> : k_norm<false, 2>;
   else
     kn = a.x_f32 ? k_norm<true, 8> : k_norm<false, 8>;
-  hipError_t e = launch_kernel(kn, dim3(a.T), dim3(256), stream, ev ? &ev[0] : nullptr, a);
-  if (e != hipSuccess) return e;
-  const int n_tt = (a.T + kTokTile - 1) / kTokTile;
-  const int n_et = a.Epad / 16;
-  const dim3 grid(kQueues * ((n_tt + kQueues - 1) / kQueues) * n_et);
-  // more workgroups than CUs: the narrow variant keeps two per CU
-  const bool wide = (size_t)n_tt * n_et <= 256;
-  const int nu = a.Epad / 32;  // 1 .. 8
-  void (*k)(RouterArgs);
-#define DG_LOGITS(NWP, W) \
-  (nu <= 1 ? k_logits<NWP, 1, W> : nu <= 2 ? k_logits<NWP, 2, W> : nu <= 4 ? k_logits<NWP, 4, W> : k_logits<NWP, 8, W>)
-  if (a.n_wplanes == 3)
-    k = wide ? DG_LOGITS(3, true) : DG_LOGITS(3, false);
-  else
-    k = wide ? DG_LOGITS(1, true) : DG_LOGITS(1, false);
-#undef DG_LOGITS
-  return launch_kernel(k, grid, dim3(64 * kWaves), stream, ev ? &ev[1] : nullptr, a);
+  return launch_kernel(kn, dim3(a.T), dim3(256), stream, ev, a);
 }
 
-hipError_t launch_prep_router_w(const void* w, int w_f32, int E, int Epad, int D, uint16_t* planes,
-                                hipStream_t stream) {
-  k_prep_router_w<<<dim3(512), dim3(256), 0, stream>>>(w, w_f32, E, Epad, D, planes);
+hipError_t launch_logits(const RouterArgs& a, hipStream_t stream, const KernelEvents* ev) {
+  const int n_et = a.Epad / 16;
+  // more m-tiles per workgroup once 16-token tiles would give more than two
+  // workgroups per CU: W' is then re-read by fewer workgroups
+  const size_t n16 = (size_t)((a.T + 15) / 16) * n_et;
+#ifndef DG_LOGITS_MT
+  const int mt = n16 <= 512 ? 1 : n16 <= 2048 ? 2 : 4;
+#else
+  const int mt = DG_LOGITS_MT;
+#endif
+  const int rows = 16 * (a.x_f32 ? min(mt, 2) : mt);
+  const int n_tt = (a.T + rows - 1) / rows;
+  const dim3 grid(kQueues * ((n_tt + kQueues - 1) / kQueues) * n_et);
+  const int nu = a.Epad / 16;  // 2 .. 16
+  void (*k)(RouterArgs);
+  if (a.x_f32)  // fp32 x lives in registers: at most two m-tiles
+    k = mt == 1 ? pick_logits<true, 1, 2>(nu) : pick_logits<true, 2, 1>(nu);
+  else
+    k = mt == 1 ? pick_logits<false, 1, 3>(nu) : mt == 2 ? pick_logits<false, 2, 2>(nu) : pick_logits<false, 4, 1>(nu);
+  return launch_kernel(k, grid, dim3(64 * kWaves), stream, ev, a);
+}
+
+hipError_t launch_prep_router_w(const void* w, int w_f32, const float* gamma, int E, int Epad, int D,
+                                uint16_t* planes, hipStream_t stream) {
+  k_prep_router_w<<<dim3(512), dim3(256), 0, stream>>>(w, w_f32, gamma, E, Epad, D, planes);
   return hipGetLastError();
 }
 

@@ -182,6 +182,9 @@ class MoELayer:
         _check(st, "dg_moe_create")
         self.handle = h
         self.max_tokens = max_tokens
+        # bf16 activations with packed bf16 experts: the expert norm rides on the gate_up weight and r, and the
+        # forward runs no norm kernel (its two profiling events are then recorded back to back)
+        self.expert_norm_folded = bool(pack and not i4 and act_dtype == torch.bfloat16)
 
     def forward(self, x, out=None, addend=None, add_input=False):
         import torch

@@ -65,9 +65,14 @@ typedef enum dg_status {
 
 /* dg_moe_config.flags */
 #define DG_MOE_PACK_WEIGHTS 0x1u /* copy the expert weights into handle-owned
-                                    memory at create (else borrow the caller's);
-                                    bf16 experts are rearranged into the matrix-core
-                                    fragment order, which the GEMMs stream faster */
+                                    memory at create (else borrow the caller's),
+                                    rearranged into the matrix-core fragment order,
+                                    which the GEMMs stream faster. With bf16 experts
+                                    and bf16 activations the gate_up copy also
+                                    carries the expert norm's scale: each value is
+                                    multiplied by (1 + ffn_gamma[input]) and rounded
+                                    to bf16, and the forward scales the gate and up
+                                    sums by r instead of forming h */
 
 /* dg_moe_forward flags */
 #define DG_FWD_ADD_INPUT 0x1u /* out = x + MoE(x) (+ addend) */
@@ -116,11 +121,12 @@ typedef struct dg_moe_s* dg_moe_handle;
  * workspace for config->max_tokens (so dg_moe_forward never allocates), and
  * prepares the router weight. In borrow mode (default) the expert weight
  * pointers are kept and must stay valid and unmodified for the handle's
- * lifetime; with DG_MOE_PACK_WEIGHTS they are copied (bf16 experts in
- * 16-row panels of 1 KB fragment blocks; int4 experts as given), after which
- * the caller's expert buffers are no longer read. router_gamma,
- * router_bias and ffn_gamma are always copied. Work is enqueued on `stream`
- * and the call synchronises that stream before returning.
+ * lifetime; with DG_MOE_PACK_WEIGHTS they are copied (in 16-row panels of
+ * 1 KB fragment blocks), after which the caller's expert buffers are no
+ * longer read. router_gamma is folded into the handle's copy of the router
+ * weight (W_r diag(1 + router_gamma), in fp32 precision); router_bias and
+ * ffn_gamma are always copied. Work is enqueued on `stream` and the call
+ * synchronises that stream before returning.
  * Errors: DG_ERR_INVALID_ARG (null cfg/weights/out, wrong struct_size),
  * DG_ERR_SHAPE, DG_ERR_DTYPE, DG_ERR_ALIGN, DG_ERR_OOM, DG_ERR_HIP,
  * DG_ERR_UNSUPPORTED (current device is not gfx950). *out is set to NULL on
@@ -144,14 +150,17 @@ dg_status dg_moe_forward(dg_moe_handle h, const void* x, void* out, int32_t T, c
 dg_status dg_moe_forward_debug(dg_moe_handle h, const void* x, void* out, int32_t T,
                                const dg_moe_debug* dbg, void* stream);
 
-/* Measurement entry point: dg_moe_forward whose six kernel launches also
- * stamp twelve caller-created hipEvent_t (passed as void*): events[2 i] at the
+/* Measurement entry point: dg_moe_forward whose kernel launches also stamp
+ * twelve caller-created hipEvent_t (passed as void*): events[2 i] at the
  * start and events[2 i + 1] at the end of kernel i, in launch order: the
- * norm, the router logits / top-k, the permutation, the gate_up GEMM, the down
- * GEMM and the combine. The events are recorded by the kernel dispatches
- * themselves (hipExtLaunchKernel), so hipEventElapsedTime(events[2 i],
- * events[2 i + 1]) is that kernel's own duration. T must be > 0; every event
- * must be non-NULL (else DG_ERR_INVALID_ARG, nothing launched). */
+ * expert-input norm, the router (r, logits, top-k), the permutation, the
+ * gate_up GEMM, the down GEMM and the combine. The events are recorded by the
+ * kernel dispatches themselves (hipExtLaunchKernel), so
+ * hipEventElapsedTime(events[2 i], events[2 i + 1]) is that kernel's own
+ * duration. Where the expert norm is folded into the packed gate_up weight
+ * (DG_MOE_PACK_WEIGHTS, bf16 experts and activations) no norm kernel runs and
+ * events 0 and 1 are recorded back to back. T must be > 0; every event must
+ * be non-NULL (else DG_ERR_INVALID_ARG, nothing launched). */
 dg_status dg_moe_forward_profiled(dg_moe_handle h, const void* x, void* out, int32_t T, const void* addend,
                                   uint32_t flags, void* const* events, void* stream);
 

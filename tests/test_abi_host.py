@@ -49,9 +49,9 @@ def test_version_and_status_strings():
 def test_workspace_bytes():
     good = dgmoe.make_config(max_tokens=256)
     ws = dgmoe.dg_moe_workspace_bytes(good)
-    # at least h, act and the bf16 per-slot outputs
-    T, K, D, F = 256, 8, 2816, 704
-    assert ws >= T * D * 2 + K * T * F * 2 + K * T * D * 2
+    # at least act and the bf16 per-slot outputs, plus the router weight in three bf16 planes
+    T, K, D, F, E = 256, 8, 2816, 704, 128
+    assert ws >= K * T * F * 2 + K * T * D * 2 + 3 * E * D * 2
     assert dgmoe.dg_moe_workspace_bytes(dgmoe.make_config(D=100)) == 0
 
 

@@ -228,12 +228,24 @@ def test_fold_invariance_bit_exact(canvas256):
 
 
 def test_pack_equals_borrow(canvas256):
+    # Packing changes the weight layout only, except that with bf16 activations the packed gate_up also
+    # carries the expert norm's (1 + gamma), rounded to bf16 with the weight (h is then never formed). The
+    # routing does not depend on the experts' storage; with fp32 activations nothing is folded and the
+    # outputs are bit-identical; with bf16 ones the two roundings differ by a few bf16 ulps.
     wl, x, w, wn = canvas256
     _say("pack vs borrow")
-    a = _layer(w, wl.T, torch.bfloat16).forward(x)
-    b = _layer(w, wl.T, torch.bfloat16, pack=True).forward(x)
+    a = _layer(w, wl.T, torch.bfloat16).forward_debug(x)
+    b = _layer(w, wl.T, torch.bfloat16, pack=True).forward_debug(x)
+    x32 = x.float()
+    a32 = _layer(w, wl.T, torch.float32).forward(x32)
+    b32 = _layer(w, wl.T, torch.float32, pack=True).forward(x32)
     torch.cuda.synchronize()
-    assert torch.equal(a.view(torch.int16), b.view(torch.int16))
+    for k in ("topk_idx", "topk_w", "sorted_slot", "row_of_slot"):
+        assert torch.equal(a[k], b[k]), k
+    assert torch.equal(a32.view(torch.int32), b32.view(torch.int32))
+    err = rel_max_err(to_f32(b["out"]), to_f32(a["out"]))
+    print(f"folded vs materialised expert input: max|d|/max|ref| = {err:.3e}")
+    assert err <= 1e-2
 
 
 def test_residual_and_addend(canvas256):
