@@ -377,6 +377,9 @@ static dg_status run_forward(dg_moe_handle hd, const void* x, void* out, int32_t
   pa.T = T;
   pa.K = c.top_k;
   pa.E = c.n_experts;
+  const bool tall = !i4 && dg::use_tall_tiles(T, c.top_k, c.n_experts);
+  pa.tile_rows = tall ? dg::kTallRows : dg::kTileRows;
+  pa.deal_experts = tall ? 1 : 0;
   for (int g = 0; g < 2; ++g) {
     pa.nb[g] = L.nb[g];
     pa.qmax[g] = dg::max_queue_len(T, c.top_k, c.n_experts, L.nb[g]);
@@ -407,12 +410,14 @@ static dg_status run_forward(dg_moe_handle hd, const void* x, void* out, int32_t
   ga.y = hd->at<uint16_t>(L.y);
   ga.D = c.d_model;
   ga.F = c.d_ff;
-  e = i4 ? dg::launch_gate_up_i4(ga, stream, ev(3)) : dg::launch_gate_up_bf16(ga, stream, ev(3));
+  e = i4 ? dg::launch_gate_up_i4(ga, stream, ev(3))
+         : tall ? dg::launch_gate_up_tall(ga, stream, ev(3)) : dg::launch_gate_up_bf16(ga, stream, ev(3));
   if (e != hipSuccess) return hip_fail(e, "gate_up launch");
   ga.tiles = pa.tasks[1];
   ga.qlen = pa.qlen + dg::kQueues;
   ga.qmax = pa.qmax[1];
-  e = i4 ? dg::launch_down_i4(ga, stream, ev(4)) : dg::launch_down_bf16(ga, stream, ev(4));
+  e = i4 ? dg::launch_down_i4(ga, stream, ev(4))
+         : tall ? dg::launch_down_tall(ga, stream, ev(4)) : dg::launch_down_bf16(ga, stream, ev(4));
   if (e != hipSuccess) return hip_fail(e, "down launch");
 
   dg::CombineArgs ca{};

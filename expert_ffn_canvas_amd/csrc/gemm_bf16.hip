@@ -64,9 +64,9 @@ __device__ __forceinline__ void load_w(const uint16_t* w0, const uint16_t* w1, i
   }
 }
 
-template <int NMT, int NS>
-__device__ __forceinline__ void mma_step(const char* stage, int lane, const Panels& p, f32x4 (&acc0)[kBMT],
-                                         f32x4 (&acc1)[kBMT]) {
+template <int NMT, int NS, int BMT>
+__device__ __forceinline__ void mma_step(const char* stage, int lane, const Panels& p, f32x4 (&acc0)[BMT],
+                                         f32x4 (&acc1)[BMT]) {
   const int g = lane >> 4, m = lane & 15;
 #pragma unroll
   for (int s = 0; s < NS; ++s) {
@@ -88,31 +88,34 @@ __device__ __forceinline__ void mma_step(const char* stage, int lane, const Pane
 // One step with NS sub-steps, issued after the previous one: DMA of the
 // activation rows into stage (it + 1) & 1, then the weight panels into `nxt`,
 // then the MFMAs of step `it` (NSP sub-steps) from `cur`.
-template <bool PK, int NMT, int NS, int NSP>
-__device__ __forceinline__ void step(char* As, const uint16_t* const (&rowp)[kDmaInstr], const uint16_t* w0,
+template <bool PK, int NMT, int NS, int NSP, int ROWS>
+__device__ __forceinline__ void step(char* As, const uint16_t* const (&rowp)[ROWS / 16], const uint16_t* w0,
                                      const uint16_t* w1, int k1, int it, int wave, int lane, const Panels& cur,
-                                     Panels& nxt, f32x4 (&acc0)[kBMT], f32x4 (&acc1)[kBMT]) {
-  dma_a<NMT, NS * 4>(As + ((it + 1) & 1) * kStageBytes, rowp, k1, wave, lane);
+                                     Panels& nxt, f32x4 (&acc0)[ROWS / 16], f32x4 (&acc1)[ROWS / 16]) {
+  constexpr int kSB = ROWS * kRowBytes;
+  dma_a<NMT, NS * 4>(As + ((it + 1) & 1) * kSB, rowp, k1, wave, lane);
   __builtin_amdgcn_sched_barrier(0);
   load_w<PK, NS>(w0, w1, k1, nxt);
   __builtin_amdgcn_sched_barrier(0);
-  mma_step<NMT, NSP>(As + (it & 1) * kStageBytes, lane, cur, acc0, acc1);
+  mma_step<NMT, NSP>(As + (it & 1) * kSB, lane, cur, acc0, acc1);
   wait_vmcnt<2 * NS>();  // this wave's DMA has landed; its weight loads may still fly
   lds_barrier();
 }
 
 // The last full step `last` (panels in `cur`) and the short tail, if any.
-template <bool PK, int NMT>
-__device__ __forceinline__ void finish(char* As, const uint16_t* const (&rowp)[kDmaInstr], const uint16_t* w0,
+template <bool PK, int NMT, int ROWS>
+__device__ __forceinline__ void finish(char* As, const uint16_t* const (&rowp)[ROWS / 16], const uint16_t* w0,
                                        const uint16_t* w1, int nfull, int ntail, int wave, int lane,
-                                       const Panels& cur, Panels& nxt, f32x4 (&acc0)[kBMT], f32x4 (&acc1)[kBMT]) {
+                                       const Panels& cur, Panels& nxt, f32x4 (&acc0)[ROWS / 16],
+                                       f32x4 (&acc1)[ROWS / 16]) {
+  constexpr int kSB = ROWS * kRowBytes;
   const int last = nfull - 1;
   const int k1 = nfull * kKS;
-  char* tail_stage = As + (nfull & 1) * kStageBytes;
+  char* tail_stage = As + (nfull & 1) * kSB;
   if (ntail == 0) {
-    mma_step<NMT, kNS>(As + (last & 1) * kStageBytes, lane, cur, acc0, acc1);
+    mma_step<NMT, kNS>(As + (last & 1) * kSB, lane, cur, acc0, acc1);
   } else {  // one 64-wide step remains (K % 128 == 64)
-    step<PK, NMT, 2, kNS>(As, rowp, w0, w1, k1, last, wave, lane, cur, nxt, acc0, acc1);
+    step<PK, NMT, 2, kNS, ROWS>(As, rowp, w0, w1, k1, last, wave, lane, cur, nxt, acc0, acc1);
     wait_vmcnt<0>();
     mma_step<NMT, 2>(tail_stage, lane, nxt, acc0, acc1);
   }
@@ -121,10 +124,10 @@ __device__ __forceinline__ void finish(char* As, const uint16_t* const (&rowp)[k
 // The K loop of one tile with NMT 16-row MFMA tiles. K is a multiple of 64.
 // Two panel buffers alternate roles (the loop is unrolled by two) so that no
 // register copies are needed between steps.
-template <bool PK, int NMT>
-__device__ __forceinline__ void k_loop(char* As, const uint16_t* const (&rowp)[kDmaInstr], const uint16_t* w0,
-                                       const uint16_t* w1, int K, int tid, f32x4 (&acc0)[kBMT],
-                                       f32x4 (&acc1)[kBMT]) {
+template <bool PK, int NMT, int ROWS>
+__device__ __forceinline__ void k_loop(char* As, const uint16_t* const (&rowp)[ROWS / 16], const uint16_t* w0,
+                                       const uint16_t* w1, int K, int tid, f32x4 (&acc0)[ROWS / 16],
+                                       f32x4 (&acc1)[ROWS / 16]) {
   const int lane = tid & 63, wave = tid >> 6;
   const int nfull = K / kKS;
   const int ntail = (K - nfull * kKS) / 32;  // 0, or 2 for a last 64-wide step (K is a multiple of 64)
@@ -145,23 +148,22 @@ __device__ __forceinline__ void k_loop(char* As, const uint16_t* const (&rowp)[k
   lds_barrier();
   int it = 0;
   for (; it + 2 < nfull; it += 2) {
-    step<PK, NMT, kNS, kNS>(As, rowp, w0, w1, (it + 1) * kKS, it, wave, lane, p0, p1, acc0, acc1);
-    step<PK, NMT, kNS, kNS>(As, rowp, w0, w1, (it + 2) * kKS, it + 1, wave, lane, p1, p0, acc0, acc1);
+    step<PK, NMT, kNS, kNS, ROWS>(As, rowp, w0, w1, (it + 1) * kKS, it, wave, lane, p0, p1, acc0, acc1);
+    step<PK, NMT, kNS, kNS, ROWS>(As, rowp, w0, w1, (it + 2) * kKS, it + 1, wave, lane, p1, p0, acc0, acc1);
   }
   if (it + 2 == nfull) {
-    step<PK, NMT, kNS, kNS>(As, rowp, w0, w1, (it + 1) * kKS, it, wave, lane, p0, p1, acc0, acc1);
-    finish<PK, NMT>(As, rowp, w0, w1, nfull, ntail, wave, lane, p1, p0, acc0, acc1);
+    step<PK, NMT, kNS, kNS, ROWS>(As, rowp, w0, w1, (it + 1) * kKS, it, wave, lane, p0, p1, acc0, acc1);
+    finish<PK, NMT, ROWS>(As, rowp, w0, w1, nfull, ntail, wave, lane, p1, p0, acc0, acc1);
   } else {
-    finish<PK, NMT>(As, rowp, w0, w1, nfull, ntail, wave, lane, p0, p1, acc0, acc1);
+    finish<PK, NMT, ROWS>(As, rowp, w0, w1, nfull, ntail, wave, lane, p0, p1, acc0, acc1);
   }
 }
 
-// Three workgroups per CU (waves_per_eu 3): the register budget that keeps
-// two K steps of weight panels per wave in flight without spilling.
-template <bool GATE_UP, bool PK>
-__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3, 3))) void k_gemm_bf16(GemmArgs a) {
-  __shared__ __attribute__((aligned(16))) char As[2 * kStageBytes];
-  __shared__ float rrow[kTileRows];  // gate_up: r of each row's token, or 1
+// The kernel body for tiles of up to ROWS rows (64, or 128 for experts that
+// receive many rows); `As` holds two K steps of ROWS activation rows.
+template <bool GATE_UP, bool PK, int ROWS>
+__device__ __forceinline__ void gemm_body(const GemmArgs& a, char* As, float* rrow) {
+  constexpr int kBM = ROWS / 16;  // 16-row MFMA tiles, and activation transfers per wave per step
   const int F = a.F, D = a.D;
   const int K = GATE_UP ? D : F;
   const int qx = blockIdx.x & (kQueues - 1);
@@ -173,16 +175,16 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3, 3))
   const int g = lane >> 4;
   const int nmt = (tl.mc + 15) >> 4;
   if (GATE_UP) {
-    if (tid < kTileRows)
+    if (tid < ROWS)
       rrow[tid] = (a.rnorm != nullptr && tid < tl.mc) ? a.rnorm[a.sorted_slot[tl.row0 + tid] / a.K] : 1.0f;
     __syncthreads();
   }
 
   // source row of each DMA instruction of this lane (rows past the tile re-read
   // its last row; their results are never stored)
-  const uint16_t* rowp[kDmaInstr];
+  const uint16_t* rowp[kBM];
 #pragma unroll
-  for (int i = 0; i < kDmaInstr; ++i) {
+  for (int i = 0; i < kBM; ++i) {
     const int r = min(kDmaRows * (wave + kWaves * i) + lane / kSegs, tl.mc - 1);
     rowp[i] = GATE_UP ? a.h + (size_t)(a.sorted_slot[tl.row0 + r] / a.K) * D : a.act + (size_t)(tl.row0 + r) * F;
   }
@@ -213,21 +215,30 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3, 3))
     }
   }
 
-  f32x4 acc0[kBMT], acc1[kBMT];
+  f32x4 acc0[kBM], acc1[kBM];
 #pragma unroll
-  for (int i = 0; i < kBMT; ++i) {
+  for (int i = 0; i < kBM; ++i) {
     acc0[i] = f32x4{0.f, 0.f, 0.f, 0.f};
     acc1[i] = f32x4{0.f, 0.f, 0.f, 0.f};
   }
-  switch (nmt) {
-    case 1: k_loop<PK, 1>(As, rowp, w0, w1, K, tid, acc0, acc1); break;
-    case 2: k_loop<PK, 2>(As, rowp, w0, w1, K, tid, acc0, acc1); break;
-    case 3: k_loop<PK, 3>(As, rowp, w0, w1, K, tid, acc0, acc1); break;
-    default: k_loop<PK, 4>(As, rowp, w0, w1, K, tid, acc0, acc1); break;
+  if constexpr (ROWS == 64) {
+    switch (nmt) {
+      case 1: k_loop<PK, 1, ROWS>(As, rowp, w0, w1, K, tid, acc0, acc1); break;
+      case 2: k_loop<PK, 2, ROWS>(As, rowp, w0, w1, K, tid, acc0, acc1); break;
+      case 3: k_loop<PK, 3, ROWS>(As, rowp, w0, w1, K, tid, acc0, acc1); break;
+      default: k_loop<PK, 4, ROWS>(As, rowp, w0, w1, K, tid, acc0, acc1); break;
+    }
+  } else {  // an even number of 16-row MFMA tiles (one spare at most)
+    switch ((nmt + 1) >> 1) {
+      case 1: k_loop<PK, 2, ROWS>(As, rowp, w0, w1, K, tid, acc0, acc1); break;
+      case 2: k_loop<PK, 4, ROWS>(As, rowp, w0, w1, K, tid, acc0, acc1); break;
+      case 3: k_loop<PK, 6, ROWS>(As, rowp, w0, w1, K, tid, acc0, acc1); break;
+      default: k_loop<PK, 8, ROWS>(As, rowp, w0, w1, K, tid, acc0, acc1); break;
+    }
   }
 
 #pragma unroll
-  for (int mt = 0; mt < kBMT; ++mt) {
+  for (int mt = 0; mt < kBM; ++mt) {
     if (mt < nmt) {
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
@@ -246,6 +257,24 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3, 3))
       }
     }
   }
+}
+
+// Three workgroups per CU (waves_per_eu 3): the register budget that keeps
+// two K steps of weight panels per wave in flight without spilling.
+template <bool GATE_UP, bool PK>
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3, 3))) void k_gemm_bf16(GemmArgs a) {
+  __shared__ __attribute__((aligned(16))) char As[2 * kTileRows * kRowBytes];
+  __shared__ float rrow[kTileRows];  // gate_up: r of each row's token, or 1
+  gemm_body<GATE_UP, PK, kTileRows>(a, As, rrow);
+}
+
+// 128-row tiles: twice the accumulators and 64 KB of activation stages, two
+// workgroups per CU.
+template <bool GATE_UP, bool PK>
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))) void k_gemm_tall(GemmArgs a) {
+  __shared__ __attribute__((aligned(16))) char As[2 * kTallRows * kRowBytes];
+  __shared__ float rrow[kTallRows];
+  gemm_body<GATE_UP, PK, kTallRows>(a, As, rrow);
 }
 
 // One wave per block of 64 lanes x 16 bytes: block b = (e, p, s). With
@@ -287,6 +316,18 @@ hipError_t launch_gate_up_bf16(const GemmArgs& a, hipStream_t stream, const Kern
 hipError_t launch_down_bf16(const GemmArgs& a, hipStream_t stream, const KernelEvents* ev) {
   const dim3 grid(kQueues * a.qmax);
   return launch_kernel(a.w_packed ? k_gemm_bf16<false, true> : k_gemm_bf16<false, false>, grid, dim3(kThreads),
+                       stream, ev, a);
+}
+
+hipError_t launch_gate_up_tall(const GemmArgs& a, hipStream_t stream, const KernelEvents* ev) {
+  const dim3 grid(kQueues * a.qmax);
+  return launch_kernel(a.w_packed ? k_gemm_tall<true, true> : k_gemm_tall<true, false>, grid, dim3(kThreads), stream,
+                       ev, a);
+}
+
+hipError_t launch_down_tall(const GemmArgs& a, hipStream_t stream, const KernelEvents* ev) {
+  const dim3 grid(kQueues * a.qmax);
+  return launch_kernel(a.w_packed ? k_gemm_tall<false, true> : k_gemm_tall<false, false>, grid, dim3(kThreads),
                        stream, ev, a);
 }
 

@@ -61,8 +61,8 @@ __device__ __forceinline__ void lds_dma16(uint32_t lds_base, const void* gaddr) 
 // slot l / kSegs, 16-byte position l % kSegs and carries logical segment
 // position ^ (row % kSegs), an XOR swizzle that makes the MFMA reads
 // bank-conflict free. Segments past a short last step re-read a valid one.
-template <int NMT, int NSEG>
-__device__ __forceinline__ void dma_a(char* stage, const uint16_t* const (&rowp)[kDmaInstr], int k0, int wave,
+template <int NMT, int NSEG, int NI>
+__device__ __forceinline__ void dma_a(char* stage, const uint16_t* const (&rowp)[NI], int k0, int wave,
                                       int lane) {
   const uint32_t base = __builtin_amdgcn_readfirstlane(lds_addr(stage) + wave * kDmaRows * kRowBytes);
 #pragma unroll

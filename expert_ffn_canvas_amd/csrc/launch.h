@@ -25,19 +25,25 @@ inline hipError_t launch_kernel(void (*kernel)(Arg), dim3 grid, dim3 block, hipS
 
 struct Tile;
 
-// Largest number of rows one tile holds (four 16-row MFMA tiles).
+// Largest number of rows one tile holds (four 16-row MFMA tiles), and the
+// largest of the tall tiles used once experts receive many rows each.
 constexpr int kTileRows = 64;
+constexpr int kTallRows = 128;
+// Tall tiles when the rows per expert average at least 64 (bf16 experts).
+inline bool use_tall_tiles(int T, int K, int E) { return (long)T * K >= 64L * E; }
 // GEMM tasks are spread over this many queues, one per XCD: queue x holds the
 // tasks that workgroups with blockIdx % kQueues == x process.
 constexpr int kQueues = 8;
 
 // Upper bound on the length of one task queue of a GEMM with NB column blocks
 // for T tokens: the tasks are dealt round robin in units of non-increasing
-// size, so no queue exceeds the mean by more than the largest unit (an
-// expert's tile count, at most ceil(T / 64)).
+// size, so no queue exceeds the mean by more than the largest unit: an
+// expert's tile count for one block (at most ceil(T / 64)), or with tall
+// tiles, dealt by expert, all its blocks (at most NB ceil(T / kTallRows)).
 inline int max_queue_len(int T, int K, int E, int NB) {
   const long max_tiles = ((long)K * T + kTileRows - 1) / kTileRows + E;
-  return (int)(((long)NB * max_tiles + kQueues - 1) / kQueues + (T + kTileRows - 1) / kTileRows);
+  const long largest_unit = (T + kTileRows - 1) / kTileRows + (long)NB * ((T + kTallRows - 1) / kTallRows);
+  return (int)(((long)NB * max_tiles + kQueues - 1) / kQueues + largest_unit);
 }
 
 // Column blocks of the two GEMMs: gate_up tasks cover 64 features (their gate
@@ -72,6 +78,8 @@ hipError_t launch_prep_router_w(const void* w, int w_f32, const float* gamma_r, 
 struct PermuteArgs {
   const int32_t* topk_idx;
   int T, K, E;
+  int tile_rows;          // largest rows per tile: kTileRows, or kTallRows for the tall GEMMs
+  int deal_experts;       // deal whole experts (all their column blocks) to one queue each, not units
   int nb[2];              // column blocks of gate_up and down
   int qmax[2];            // capacity of each queue of gate_up and down
   int32_t* counts;        // [E]
@@ -111,6 +119,9 @@ hipError_t launch_pack_panels(const uint16_t* src, uint16_t* dst, int E, int R, 
                               hipStream_t stream);
 hipError_t launch_gate_up_bf16(const GemmArgs& a, hipStream_t stream, const KernelEvents* ev);
 hipError_t launch_down_bf16(const GemmArgs& a, hipStream_t stream, const KernelEvents* ev);
+// The same products for tiles of up to kTallRows rows (bf16 weights, packed or not).
+hipError_t launch_gate_up_tall(const GemmArgs& a, hipStream_t stream, const KernelEvents* ev);
+hipError_t launch_down_tall(const GemmArgs& a, hipStream_t stream, const KernelEvents* ev);
 // Create-time relayout of int4-g128 expert weights (codes [E][R][K/2], scales
 // [E][R][ceil(K/128)]) into fragment order: 1 KB of codes and 16 scales per
 // (expert, 16-row panel, 128-input group), the short last group padded with

@@ -3,14 +3,17 @@
 //  * offsets: exclusive prefix sum of counts (the rows of expert e are
 //    offsets[e] .. offsets[e+1]-1 in expert-sorted order);
 //  * the task queues of the two grouped GEMMs. Each expert's rows are cut
-//    into ceil(count / 64) tiles of near-equal size; a task is one tile times
+//    into ceil(count / R) tiles of near-equal size (R = 64, or 192 for the
+//    tall-tile GEMMs); a task is one tile times
 //    one column block of the expert's weight. Units (expert, column block),
 //    each holding all tiles of that expert for that block, are ranked by
 //    expert (count descending, ties to the lower id), then block, and dealt
 //    round robin to the 8 per-XCD queues. So the tiles that read the same
 //    weight block run together on one XCD and share its L2, and since the
 //    unit sizes never grow along the deal, every queue holds the mean load
-//    to within one unit;
+//    to within one unit. With tall tiles the deal is by expert instead (all
+//    column blocks of rank r go to queue r % 8): an expert's tiles then share
+//    its activation rows, hundreds of them, in one L2;
 //  * the stable scatter: the rows of expert e hold its slots in increasing
 //    token order; sorted_slot[row] = t k + j (token t, slot j) and
 //    row_of_slot[t k + j] = row.
@@ -112,7 +115,7 @@ __global__ __launch_bounds__(kThreads) void k_permute(PermuteArgs a) {
       a.offsets[tid] = excl;
       a.counts[tid] = c;
       if (tid == E - 1) a.offsets[E] = excl + c;
-      ntile[tid] = (c + kTileRows - 1) / kTileRows;
+      ntile[tid] = (c + a.tile_rows - 1) / a.tile_rows;
     }
   }
   // --- rank of expert e by (count desc, id asc): four lanes per expert; lane
@@ -150,7 +153,8 @@ __global__ __launch_bounds__(kThreads) void k_permute(PermuteArgs a) {
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int r = 4 * lane + i;
-      v[i] = (r < E) ? ntile[order[r]] * (n_mod((r + 1) * NB, x) - n_mod(r * NB, x)) : 0;
+      const int units = a.deal_experts ? ((r % kQueues == x) ? NB : 0) : n_mod((r + 1) * NB, x) - n_mod(r * NB, x);
+      v[i] = (r < E) ? ntile[order[r]] * units : 0;
       run += v[i];
     }
     int incl2 = run;
@@ -211,13 +215,14 @@ __global__ __launch_bounds__(kThreads) void k_permute(PermuteArgs a) {
       const int e = order[r], nt = ntile[e];
       const int local = p - pre[r];
       const int m = local / nt, i = local - m * nt;
-      const int nb0 = (x - (r * NB) % kQueues + kQueues) % kQueues;
+      const int nb0 = a.deal_experts ? 0 : (x - (r * NB) % kQueues + kQueues) % kQueues;
+      const int nb_step = a.deal_experts ? 1 : kQueues;
       const int ce = cnt[e];
       Tile tl;
       tl.e = e;
       tl.row0 = base[e] + (ce * i) / nt;
       tl.mc = (ce * (i + 1)) / nt - (ce * i) / nt;
-      tl.nb = nb0 + kQueues * m;
+      tl.nb = nb0 + nb_step * m;
       a.tasks[g][pl] = tl;
     }
     __syncthreads();  // the table is rebuilt for the next GEMM / reused by the scatter

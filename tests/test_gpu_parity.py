@@ -43,9 +43,13 @@ def canvas256():
     (6, 2, 128, 64, 37, "bf16", "bf16"),
     (16, 4, 256, 128, 70, "f32", "f32"),
     (40, 8, 384, 192, 129, "bf16", "f32"),
-    # many rows per expert: 192-row tiles, a 64-wide last K step (down K = 192) and a single-step K (F = 64)
+    # many rows per expert (at least 64 on average: the tall-tile GEMMs), down K = 192 and K = 64
     (8, 4, 384, 192, 300, "bf16", "bf16"),
     (6, 2, 256, 64, 400, "bf16", "f32"),
+    # about 350 rows per expert: two tall tiles each, twelve 16-row MFMA tiles
+    (4, 2, 256, 128, 700, "bf16", "bf16"),
+    # just past the tall-tile threshold with a skewed load: tiles of every height
+    (16, 8, 256, 128, 130, "bf16", "bf16"),
 ])
 @pytest.mark.parametrize("pack", [False, True], ids=["borrow", "pack"])
 def test_small_shapes(E, K, D, F, T, act, rw, pack):
