@@ -1,4 +1,7 @@
-// Token -> expert permutation on gfx950, in one workgroup of 1024 threads:
+// Token -> expert permutation on gfx950, in three workgroups of 1024 threads
+// that share the histogram and scan and split the rest (on three CUs at once):
+// workgroup 0 writes counts, offsets and the gate_up task queues, workgroup 1
+// the down task queues, workgroup 2 the stable scatter. The outputs:
 //  * counts[e]: tokens routed to expert e (their sum is k T);
 //  * offsets: exclusive prefix sum of counts (the rows of expert e are
 //    offsets[e] .. offsets[e+1]-1 in expert-sorted order);
@@ -19,11 +22,11 @@
 //    row_of_slot[t k + j] = row.
 // Everything stays on the device; the host never reads the counts back.
 //
-// One workgroup issues every store of this kernel, and a store instruction
-// whose 64 lanes hit 64 different cache lines costs 64 line transactions, so
-// the layout of the writes is what bounds it: the task lists are written by
-// position (each lane finds which unit covers its position), and the sorted
-// slots are ranked into LDS and written out in order when they fit.
+// Each part runs in one workgroup, and a store instruction whose 64 lanes hit
+// 64 different cache lines costs 64 line transactions, so the layout of the
+// writes is what bounds it: the task lists are written by position (each lane
+// finds which unit covers its position), and the sorted slots are ranked into
+// LDS and written out in order when they fit.
 //
 // Source of the per-expert token counts: Quant-Tuner PR "Add DiffusionGemma
 // (Gemma-4 MoE block-diffusion) support", "Answers to the motivating
@@ -56,180 +59,12 @@ __device__ __forceinline__ void load_ids(const int32_t* idx, int t, int K, int (
   }
 }
 
-__global__ __launch_bounds__(kThreads) void k_permute(PermuteArgs a) {
-  __shared__ int cnt[kMaxE];
-  __shared__ int base[kMaxE];
-  __shared__ int cursor[kMaxE];
-  __shared__ int order[kMaxE];
-  __shared__ int ntile[kMaxE];
-  __shared__ int wsum[kMaxE / 64];
-  __shared__ int pq[2][kQueues][kMaxE + 1];   // per GEMM and queue: load of the ranks before r
-  __shared__ uint64_t masks[kWavesP][kMaxE];  // per wave and expert: lanes whose token has it
-  __shared__ int wpre[kWavesP][kMaxE];        // first row of (wave, expert) in the chunk
-  __shared__ int stage[kStage];
-
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+// The stable scatter, kThreads tokens at a time: lane masks per (wave,
+// expert) give each slot its rank among the chunk's earlier tokens.
+__device__ __forceinline__ void scatter(const PermuteArgs& a, int (&ids)[8], int* cursor,
+                                        uint64_t (*masks)[kMaxE], int (*wpre)[kMaxE], int* stage, bool staged,
+                                        int tid, int lane, int wave) {
   const int E = a.E, K = a.K, T = a.T;
-  const bool staged = (size_t)K * T <= (size_t)kStage;
-
-  // the first chunk of tokens is loaded once and kept for the scatter
-  int ids[8] = {0, 0, 0, 0, 0, 0, 0, 0};
-  if (tid < T) load_ids(a.topk_idx, tid, K, ids);
-
-  // --- histogram
-  if (tid < kMaxE) cnt[tid] = 0;
-  __syncthreads();
-  if (tid < T) {
-#pragma unroll
-    for (int j = 0; j < 8; ++j)
-      if (j < K) atomicAdd(&cnt[ids[j]], 1);
-  }
-  for (int t = tid + kThreads; t < T; t += kThreads) {
-    int ee[8];
-    load_ids(a.topk_idx, t, K, ee);
-#pragma unroll
-    for (int j = 0; j < 8; ++j)
-      if (j < K) atomicAdd(&cnt[ee[j]], 1);
-  }
-  __syncthreads();
-
-  // --- exclusive scan of the counts (four waves of 64 experts)
-  int c = 0, incl = 0;
-  if (tid < kMaxE) {
-    c = (tid < E) ? cnt[tid] : 0;
-    incl = c;
-    for (int d = 1; d < 64; d <<= 1) {
-      const int o = __shfl_up(incl, d);
-      if (lane >= d) incl += o;
-    }
-    if (lane == 63) wsum[wave] = incl;
-  }
-  __syncthreads();
-  if (tid < kMaxE) {
-    int before = 0;
-    for (int w = 0; w < wave; ++w) before += wsum[w];
-    const int excl = before + incl - c;
-    base[tid] = excl;
-    cursor[tid] = excl;
-    if (tid < E) {
-      a.offsets[tid] = excl;
-      a.counts[tid] = c;
-      if (tid == E - 1) a.offsets[E] = excl + c;
-      ntile[tid] = (c + a.tile_rows - 1) / a.tile_rows;
-    }
-  }
-  // --- rank of expert e by (count desc, id asc): four lanes per expert; lane
-  // q reads the counts 16 i + 4 q .. + 3 (consecutive lanes, consecutive
-  // banks) and compares against them
-  {
-    const int e = tid >> 2, q = tid & 3;
-    const int ce = (e < E) ? cnt[e] : 0;
-    int r = 0;
-#pragma unroll
-    for (int i = 0; i < kMaxE / 16; ++i) {
-      if (16 * i >= E) break;
-      const int4 c4 = *reinterpret_cast<const int4*>(&cnt[16 * i + 4 * q]);
-      const int cc[4] = {c4.x, c4.y, c4.z, c4.w};
-#pragma unroll
-      for (int k = 0; k < 4; ++k) {
-        const int e2 = 16 * i + 4 * q + k;
-        r += (e2 < E) && ((cc[k] > ce) || (cc[k] == ce && e2 < e));
-      }
-    }
-    r += __shfl_xor(r, 1);
-    r += __shfl_xor(r, 2);
-    if (q == 0 && e < E) order[r] = e;
-  }
-  __syncthreads();
-
-  // --- per GEMM g and queue x, the load that the units of experts ranked
-  // before r put into x: wave w = 8 g + x scans 4 ranks per lane. Expert rank
-  // r owns units r NB .. r NB + NB - 1; unit u goes to queue u % 8 and holds
-  // ntile tasks.
-  {
-    const int g = wave >> 3, x = wave & 7;
-    const int NB = a.nb[g];
-    int v[4], run = 0;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int r = 4 * lane + i;
-      const int units = a.deal_experts ? ((r % kQueues == x) ? NB : 0) : n_mod((r + 1) * NB, x) - n_mod(r * NB, x);
-      v[i] = (r < E) ? ntile[order[r]] * units : 0;
-      run += v[i];
-    }
-    int incl2 = run;
-    for (int d = 1; d < 64; d <<= 1) {
-      const int o = __shfl_up(incl2, d);
-      if (lane >= d) incl2 += o;
-    }
-    int before = incl2 - run;
-    if (lane == 0) pq[g][x][0] = 0;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      before += v[i];
-      pq[g][x][4 * lane + i + 1] = before;  // load of ranks 0 .. 4 lane + i
-    }
-  }
-  __syncthreads();
-  if (tid < 2 * kQueues) {
-    const int g = tid / kQueues, x = tid % kQueues;
-    a.qlen[tid] = min(pq[g][x][E], a.qmax[g]);
-  }
-
-  // --- the tasks, one lane per queue position: position p of queue x is
-  // tasks[8 p + x], so consecutive lanes write consecutive entries. The lane
-  // needs the expert rank r whose units cover p: a table of the rank at every
-  // position, built in the (not yet used) staging memory by one lane per
-  // (queue, rank), when the queues fit in it; else a binary search on the
-  // queue's prefix. Then it finds the unit and the tile inside it.
-#pragma unroll
-  for (int g = 0; g < 2; ++g) {
-    const int NB = a.nb[g];
-    int longest = 0;
-#pragma unroll
-    for (int x = 0; x < kQueues; ++x) longest = max(longest, min(pq[g][x][E], a.qmax[g]));
-    const bool table = kQueues * longest <= kStage;
-    if (table) {
-      for (int i = tid; i < kQueues * E; i += kThreads) {
-        const int x = i / E, r = i - x * E;
-        const int p1 = min(pq[g][x][r + 1], longest);
-        for (int p = pq[g][x][r]; p < p1; ++p) stage[kQueues * p + x] = r;
-      }
-      __syncthreads();
-    }
-    for (int pl = tid; pl < kQueues * longest; pl += kThreads) {
-      const int x = pl % kQueues, p = pl / kQueues;
-      const int* pre = pq[g][x];
-      if (p >= min(pre[E], a.qmax[g])) continue;
-      int r;
-      if (table) {
-        r = stage[pl];
-      } else {
-        int lo = 0, hi = E;  // pre[lo] <= p < pre[hi]
-        while (hi - lo > 1) {
-          const int mid = (lo + hi) >> 1;
-          if (pre[mid] <= p) lo = mid; else hi = mid;
-        }
-        r = lo;
-      }
-      const int e = order[r], nt = ntile[e];
-      const int local = p - pre[r];
-      const int m = local / nt, i = local - m * nt;
-      const int nb0 = a.deal_experts ? 0 : (x - (r * NB) % kQueues + kQueues) % kQueues;
-      const int nb_step = a.deal_experts ? 1 : kQueues;
-      const int ce = cnt[e];
-      Tile tl;
-      tl.e = e;
-      tl.row0 = base[e] + (ce * i) / nt;
-      tl.mc = (ce * (i + 1)) / nt - (ce * i) / nt;
-      tl.nb = nb0 + nb_step * m;
-      a.tasks[g][pl] = tl;
-    }
-    __syncthreads();  // the table is rebuilt for the next GEMM / reused by the scatter
-  }
-
-  // --- stable scatter, kThreads tokens at a time: lane masks per (wave,
-  // expert) give each slot its rank among the chunk's earlier tokens
   const uint64_t below = (1ull << lane) - 1ull;
   for (int c0 = 0; c0 < T; c0 += kThreads) {
     const int t = c0 + tid;
@@ -286,10 +121,185 @@ __global__ __launch_bounds__(kThreads) void k_permute(PermuteArgs a) {
   }
 }
 
+__global__ __launch_bounds__(kThreads) void k_permute(PermuteArgs a) {
+  __shared__ int cnt[kMaxE];
+  __shared__ int base[kMaxE];
+  __shared__ int cursor[kMaxE];
+  __shared__ int order[kMaxE];
+  __shared__ int ntile[kMaxE];
+  __shared__ int wsum[kMaxE / 64];
+  __shared__ int pq[kQueues][kMaxE + 1];      // per queue of this GEMM: load of the ranks before r
+  __shared__ uint64_t masks[kWavesP][kMaxE];  // per wave and expert: lanes whose token has it
+  __shared__ int wpre[kWavesP][kMaxE];        // first row of (wave, expert) in the chunk
+  __shared__ int stage[kStage];
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int E = a.E, K = a.K, T = a.T;
+  const int role = blockIdx.x;  // 0, 1: the task queues of GEMM `role`; 2: the scatter
+  const bool staged = (size_t)K * T <= (size_t)kStage;
+
+  // the first chunk of tokens is loaded once and kept for the scatter
+  int ids[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+  if (tid < T) load_ids(a.topk_idx, tid, K, ids);
+
+  // --- histogram
+  if (tid < kMaxE) cnt[tid] = 0;
+  __syncthreads();
+  if (tid < T) {
+#pragma unroll
+    for (int j = 0; j < 8; ++j)
+      if (j < K) atomicAdd(&cnt[ids[j]], 1);
+  }
+  for (int t = tid + kThreads; t < T; t += kThreads) {
+    int ee[8];
+    load_ids(a.topk_idx, t, K, ee);
+#pragma unroll
+    for (int j = 0; j < 8; ++j)
+      if (j < K) atomicAdd(&cnt[ee[j]], 1);
+  }
+  __syncthreads();
+
+  // --- exclusive scan of the counts (four waves of 64 experts)
+  int c = 0, incl = 0;
+  if (tid < kMaxE) {
+    c = (tid < E) ? cnt[tid] : 0;
+    incl = c;
+    for (int d = 1; d < 64; d <<= 1) {
+      const int o = __shfl_up(incl, d);
+      if (lane >= d) incl += o;
+    }
+    if (lane == 63) wsum[wave] = incl;
+  }
+  __syncthreads();
+  if (tid < kMaxE) {
+    int before = 0;
+    for (int w = 0; w < wave; ++w) before += wsum[w];
+    const int excl = before + incl - c;
+    base[tid] = excl;
+    cursor[tid] = excl;
+    if (tid < E) {
+      if (role == 0) {
+        a.offsets[tid] = excl;
+        a.counts[tid] = c;
+        if (tid == E - 1) a.offsets[E] = excl + c;
+      }
+      ntile[tid] = (c + a.tile_rows - 1) / a.tile_rows;
+    }
+  }
+  if (role == 2) {
+    scatter(a, ids, cursor, masks, wpre, stage, staged, tid, lane, wave);
+    return;
+  }
+  // --- rank of expert e by (count desc, id asc): four lanes per expert; lane
+  // q reads the counts 16 i + 4 q .. + 3 (consecutive lanes, consecutive
+  // banks) and compares against them
+  {
+    const int e = tid >> 2, q = tid & 3;
+    const int ce = (e < E) ? cnt[e] : 0;
+    int r = 0;
+#pragma unroll
+    for (int i = 0; i < kMaxE / 16; ++i) {
+      if (16 * i >= E) break;
+      const int4 c4 = *reinterpret_cast<const int4*>(&cnt[16 * i + 4 * q]);
+      const int cc[4] = {c4.x, c4.y, c4.z, c4.w};
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        const int e2 = 16 * i + 4 * q + k;
+        r += (e2 < E) && ((cc[k] > ce) || (cc[k] == ce && e2 < e));
+      }
+    }
+    r += __shfl_xor(r, 1);
+    r += __shfl_xor(r, 2);
+    if (q == 0 && e < E) order[r] = e;
+  }
+  __syncthreads();
+
+  // --- per queue x of this GEMM g, the load that the units of experts
+  // ranked before r put into x: wave x scans 4 ranks per lane. Expert rank r
+  // owns units r NB .. r NB + NB - 1; unit u goes to queue u % 8 (or, dealing
+  // by expert, all of them to queue r % 8) and holds ntile tasks.
+  const int g = role;
+  const int NB = a.nb[g];
+  if (wave < kQueues) {
+    const int x = wave;
+    int v[4], run = 0;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int r = 4 * lane + i;
+      const int units = a.deal_experts ? ((r % kQueues == x) ? NB : 0) : n_mod((r + 1) * NB, x) - n_mod(r * NB, x);
+      v[i] = (r < E) ? ntile[order[r]] * units : 0;
+      run += v[i];
+    }
+    int incl2 = run;
+    for (int d = 1; d < 64; d <<= 1) {
+      const int o = __shfl_up(incl2, d);
+      if (lane >= d) incl2 += o;
+    }
+    int before = incl2 - run;
+    if (lane == 0) pq[x][0] = 0;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      before += v[i];
+      pq[x][4 * lane + i + 1] = before;  // load of ranks 0 .. 4 lane + i
+    }
+  }
+  __syncthreads();
+  if (tid < kQueues) a.qlen[g * kQueues + tid] = min(pq[tid][E], a.qmax[g]);
+
+  // --- the tasks, one lane per queue position: position p of queue x is
+  // tasks[8 p + x], so consecutive lanes write consecutive entries. The lane
+  // needs the expert rank r whose units cover p: a table of the rank at every
+  // position, built in the (not yet used) staging memory by one lane per
+  // (queue, rank), when the queues fit in it; else a binary search on the
+  // queue's prefix. Then it finds the unit and the tile inside it.
+  {
+    int longest = 0;
+#pragma unroll
+    for (int x = 0; x < kQueues; ++x) longest = max(longest, min(pq[x][E], a.qmax[g]));
+    const bool table = kQueues * longest <= kStage;
+    if (table) {
+      for (int i = tid; i < kQueues * E; i += kThreads) {
+        const int x = i / E, r = i - x * E;
+        const int p1 = min(pq[x][r + 1], longest);
+        for (int p = pq[x][r]; p < p1; ++p) stage[kQueues * p + x] = r;
+      }
+      __syncthreads();
+    }
+    for (int pl = tid; pl < kQueues * longest; pl += kThreads) {
+      const int x = pl % kQueues, p = pl / kQueues;
+      const int* pre = pq[x];
+      if (p >= min(pre[E], a.qmax[g])) continue;
+      int r;
+      if (table) {
+        r = stage[pl];
+      } else {
+        int lo = 0, hi = E;  // pre[lo] <= p < pre[hi]
+        while (hi - lo > 1) {
+          const int mid = (lo + hi) >> 1;
+          if (pre[mid] <= p) lo = mid; else hi = mid;
+        }
+        r = lo;
+      }
+      const int e = order[r], nt = ntile[e];
+      const int local = p - pre[r];
+      const int m = local / nt, i = local - m * nt;
+      const int nb0 = a.deal_experts ? 0 : (x - (r * NB) % kQueues + kQueues) % kQueues;
+      const int nb_step = a.deal_experts ? 1 : kQueues;
+      const int ce = cnt[e];
+      Tile tl;
+      tl.e = e;
+      tl.row0 = base[e] + (ce * i) / nt;
+      tl.mc = (ce * (i + 1)) / nt - (ce * i) / nt;
+      tl.nb = nb0 + nb_step * m;
+      a.tasks[g][pl] = tl;
+    }
+  }
+}
+
 }  // namespace
 
 hipError_t launch_permute(const PermuteArgs& a, hipStream_t stream, const KernelEvents* ev) {
-  return launch_kernel(k_permute, dim3(1), dim3(kThreads), stream, ev, a);
+  return launch_kernel(k_permute, dim3(3), dim3(kThreads), stream, ev, a);
 }
 
 }  // namespace dg
