@@ -42,25 +42,22 @@ namespace {
 
 using namespace gemm;
 
+// The weight fragments of one K step (NS sub-steps of 32) of a wave's two
+// panels, and the stride of the stream they come from: elements between
+// consecutive 32-column blocks of a lane (32 in a row-major row; in the packed
+// layout, all of the expert's panels: their count times 512).
 struct Panels {
   u32x4 b0[kNS], b1[kNS];
+  int wstep;
 };
-
-// Element offset of column k (a multiple of 32) inside a lane's weight
-// stream: row-major rows advance one element per column; the packed panel
-// layout advances one 1 KB block (512 elements) per 32 columns.
-template <bool PK>
-__device__ __forceinline__ int koff(int k) {
-  return PK ? 16 * k : k;
-}
 
 // Weight panels of one K step: NS sub-steps of 32.
 template <bool PK, int NS>
 __device__ __forceinline__ void load_w(const uint16_t* w0, const uint16_t* w1, int k0, Panels& p) {
 #pragma unroll
   for (int s = 0; s < NS; ++s) {
-    p.b0[s] = *reinterpret_cast<const u32x4*>(w0 + koff<PK>(k0 + 32 * s));
-    p.b1[s] = *reinterpret_cast<const u32x4*>(w1 + koff<PK>(k0 + 32 * s));
+    p.b0[s] = *reinterpret_cast<const u32x4*>(w0 + (size_t)((k0 + 32 * s) >> 5) * p.wstep);
+    p.b1[s] = *reinterpret_cast<const u32x4*>(w1 + (size_t)((k0 + 32 * s) >> 5) * p.wstep);
   }
 }
 
@@ -127,11 +124,13 @@ __device__ __forceinline__ void finish(char* As, const uint16_t* const (&rowp)[R
 template <bool PK, int NMT, int ROWS>
 __device__ __forceinline__ void k_loop(char* As, const uint16_t* const (&rowp)[ROWS / 16], const uint16_t* w0,
                                        const uint16_t* w1, int K, int tid, f32x4 (&acc0)[ROWS / 16],
-                                       f32x4 (&acc1)[ROWS / 16]) {
+                                       f32x4 (&acc1)[ROWS / 16], int wstep) {
   const int lane = tid & 63, wave = tid >> 6;
   const int nfull = K / kKS;
   const int ntail = (K - nfull * kKS) / 32;  // 0, or 2 for a last 64-wide step (K is a multiple of 64)
   Panels p0, p1;
+  p0.wstep = wstep;
+  p1.wstep = wstep;
   if (nfull == 0) {
     // K = 64: one short step only
     dma_a<NMT, 8>(As, rowp, 0, wave, lane);
@@ -194,10 +193,10 @@ __device__ __forceinline__ void gemm_body(const GemmArgs& a, char* As, float* rr
   if (GATE_UP) {
     col = nb * 16 * kWaves + wave * 16 + (lane & 15);
     const uint16_t* W = static_cast<const uint16_t*>(a.w_gate_up);
-    if (PK) {  // gate panel nb * kWaves + wave, up panel F / 16 later
+    if (PK) {  // gate panel nb * kWaves + wave, up panel F / 16 later, in the same K-step row
       const int p = nb * kWaves + wave;
-      w0 = W + ((size_t)tl.e * (2 * F / 16) + p) * (size_t)(D / 32) * 512 + lane * 8;
-      w1 = w0 + (size_t)(F / 16) * (D / 32) * 512;
+      w0 = W + ((size_t)tl.e * (D / 32) * (2 * F / 16) + p) * 512 + lane * 8;
+      w1 = w0 + (size_t)(F / 16) * 512;
     } else {
       w0 = W + ((size_t)tl.e * 2 * F + col) * D + g * 8;
       w1 = w0 + (size_t)F * D;
@@ -207,14 +206,15 @@ __device__ __forceinline__ void gemm_body(const GemmArgs& a, char* As, float* rr
     const uint16_t* W = static_cast<const uint16_t*>(a.w_down);
     if (PK) {  // panels 2 (nb * kWaves + wave) and the next
       const int p = 2 * (nb * kWaves + wave);
-      w0 = W + ((size_t)tl.e * (D / 16) + p) * (size_t)(F / 32) * 512 + lane * 8;
-      w1 = w0 + (size_t)(F / 32) * 512;
+      w0 = W + ((size_t)tl.e * (F / 32) * (D / 16) + p) * 512 + lane * 8;
+      w1 = w0 + 512;
     } else {
       w0 = W + ((size_t)tl.e * D + col) * F + g * 8;
       w1 = w0 + (size_t)16 * F;
     }
   }
 
+  const int wstep = PK ? (GATE_UP ? 2 * F / 16 : D / 16) * 512 : 32;
   f32x4 acc0[kBM], acc1[kBM];
 #pragma unroll
   for (int i = 0; i < kBM; ++i) {
@@ -223,17 +223,17 @@ __device__ __forceinline__ void gemm_body(const GemmArgs& a, char* As, float* rr
   }
   if constexpr (ROWS == 64) {
     switch (nmt) {
-      case 1: k_loop<PK, 1, ROWS>(As, rowp, w0, w1, K, tid, acc0, acc1); break;
-      case 2: k_loop<PK, 2, ROWS>(As, rowp, w0, w1, K, tid, acc0, acc1); break;
-      case 3: k_loop<PK, 3, ROWS>(As, rowp, w0, w1, K, tid, acc0, acc1); break;
-      default: k_loop<PK, 4, ROWS>(As, rowp, w0, w1, K, tid, acc0, acc1); break;
+      case 1: k_loop<PK, 1, ROWS>(As, rowp, w0, w1, K, tid, acc0, acc1, wstep); break;
+      case 2: k_loop<PK, 2, ROWS>(As, rowp, w0, w1, K, tid, acc0, acc1, wstep); break;
+      case 3: k_loop<PK, 3, ROWS>(As, rowp, w0, w1, K, tid, acc0, acc1, wstep); break;
+      default: k_loop<PK, 4, ROWS>(As, rowp, w0, w1, K, tid, acc0, acc1, wstep); break;
     }
   } else {  // an even number of 16-row MFMA tiles (one spare at most)
     switch ((nmt + 1) >> 1) {
-      case 1: k_loop<PK, 2, ROWS>(As, rowp, w0, w1, K, tid, acc0, acc1); break;
-      case 2: k_loop<PK, 4, ROWS>(As, rowp, w0, w1, K, tid, acc0, acc1); break;
-      case 3: k_loop<PK, 6, ROWS>(As, rowp, w0, w1, K, tid, acc0, acc1); break;
-      default: k_loop<PK, 8, ROWS>(As, rowp, w0, w1, K, tid, acc0, acc1); break;
+      case 1: k_loop<PK, 2, ROWS>(As, rowp, w0, w1, K, tid, acc0, acc1, wstep); break;
+      case 2: k_loop<PK, 4, ROWS>(As, rowp, w0, w1, K, tid, acc0, acc1, wstep); break;
+      case 3: k_loop<PK, 6, ROWS>(As, rowp, w0, w1, K, tid, acc0, acc1, wstep); break;
+      default: k_loop<PK, 8, ROWS>(As, rowp, w0, w1, K, tid, acc0, acc1, wstep); break;
     }
   }
 
@@ -277,8 +277,9 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
   gemm_body<GATE_UP, PK, kTallRows>(a, As, rrow);
 }
 
-// One wave per block of 64 lanes x 16 bytes: block b = (e, p, s). With
-// `gamma`, value k is scaled by (1 + gamma[k]) and rounded to bf16.
+// One wave per block of 64 lanes x 16 bytes: source block (e, p, s) of 16 rows
+// x 32 columns goes to position (e, s, p). With `gamma`, value k is scaled by
+// (1 + gamma[k]) and rounded to bf16.
 __global__ __launch_bounds__(256) void k_pack_panels(const uint16_t* __restrict__ src, uint16_t* __restrict__ dst,
                                                      int E, int R, int K, const float* __restrict__ gamma) {
   const int nks = K / 32, np = R / 16;
@@ -295,7 +296,8 @@ __global__ __launch_bounds__(256) void k_pack_panels(const uint16_t* __restrict_
       for (int i = 0; i < 4; ++i)
         v[i] = pack_bf16x2(bf16_lo(v[i]) * (1.0f + gamma[k + 2 * i]), bf16_hi(v[i]) * (1.0f + gamma[k + 2 * i + 1]));
     }
-    *reinterpret_cast<u32x4*>(dst + b * 512 + lane * 8) = v;
+    const size_t e = ep / np, pp = ep % np;
+    *reinterpret_cast<u32x4*>(dst + ((e * nks + s) * np + pp) * 512 + lane * 8) = v;
   }
 }
 

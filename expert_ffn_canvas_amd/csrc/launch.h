@@ -110,11 +110,13 @@ struct GemmArgs {
   int w_packed;            // weights in the fragment layout of launch_pack_panels / launch_pack_i4
 };
 // Create-time relayout of bf16 expert weights [E][R][K] (R % 16 == 0,
-// K % 32 == 0) into MFMA fragment order: 1 KB block (e, p, s) holds, at lane
+// K % 32 == 0) into MFMA fragment order: 1 KB block (e, s, p) holds, at lane
 // l = n + 16 g, the 8 values W[e][16 p + n][32 s + 8 g .. + 7]; blocks are
-// ordered e-major, then p, then s. A wave reading one B-operand fragment of a
-// 16-row panel then reads 1 KB contiguously. With `gamma` ([K] fp32) each value
-// is first multiplied by (1 + gamma[k]) and rounded to bf16 (nearest even).
+// ordered e-major, then the 32-column step s, then the 16-row panel p. A wave
+// reading one B-operand fragment of a panel then reads 1 KB contiguously, and
+// the workgroups streaming an expert's panels at the same K step read one
+// contiguous region. With `gamma` ([K] fp32) each value is first multiplied
+// by (1 + gamma[k]) and rounded to bf16 (nearest even).
 hipError_t launch_pack_panels(const uint16_t* src, uint16_t* dst, int E, int R, int K, const float* gamma,
                               hipStream_t stream);
 hipError_t launch_gate_up_bf16(const GemmArgs& a, hipStream_t stream, const KernelEvents* ev);

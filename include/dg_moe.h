@@ -121,9 +121,9 @@ typedef struct dg_moe_s* dg_moe_handle;
  * workspace for config->max_tokens (so dg_moe_forward never allocates), and
  * prepares the router weight. In borrow mode (default) the expert weight
  * pointers are kept and must stay valid and unmodified for the handle's
- * lifetime; with DG_MOE_PACK_WEIGHTS they are copied (in 16-row panels of
- * 1 KB fragment blocks), after which the caller's expert buffers are no
- * longer read. router_gamma is folded into the handle's copy of the router
+ * lifetime; with DG_MOE_PACK_WEIGHTS they are copied (in 1 KB fragment
+ * blocks of 16 rows x 32 inputs, or 16 rows x 128 int4 inputs), after which
+ * the caller's expert buffers are no longer read. router_gamma is folded into the handle's copy of the router
  * weight (W_r diag(1 + router_gamma), in fp32 precision); router_bias and
  * ffn_gamma are always copied. Work is enqueued on `stream` and the call
  * synchronises that stream before returning.
