@@ -11,6 +11,7 @@ the canvas, two canvases, 30 MoE layers):
   canvas256  T=256,  all bf16, router bias -1.1*ln(e+1) (Zipf s=1.1 skew)
   encode2304 T=2304, all bf16, no router bias
   int4       T=256,  bf16 activations, int4-g128 experts (zero point 8)
+  q8         T=256,  bf16 activations, Q8_0 experts (blocks of 32, fp16 scale)
   stack30    T=512,  30 layers with their own bf16 weights, Zipf skew,
              a N(0, 0.5) offset [T, D] added after each layer
 
@@ -45,7 +46,7 @@ class Workload:
     T: int
     act: str            # "f32" | "bf16"
     router_w: str       # "f32" | "bf16"
-    experts: str        # "bf16" | "i4g128"
+    experts: str        # "bf16" | "i4g128" | "q8_0"
     bias: str | None    # None | "zipf"
     seed: int
     layers: int = 1
@@ -62,6 +63,7 @@ WORKLOADS = {
     "canvas256": Workload("canvas256", 256, "bf16", "bf16", "bf16", "zipf", 1),
     "encode2304": Workload("encode2304", 2304, "bf16", "bf16", "bf16", None, 2),
     "int4": Workload("int4", 256, "bf16", "bf16", "i4g128", None, 3),
+    "q8": Workload("q8", 256, "bf16", "bf16", "q8_0", None, 5),
     "stack30": Workload("stack30", 512, "bf16", "bf16", "bf16", "zipf", 4, layers=30, delta_std=0.5),
 }
 
@@ -103,6 +105,24 @@ def quantize_i4g128(w: torch.Tensor):
     return packed, s16.contiguous()
 
 
+def quantize_q8_0(w: torch.Tensor) -> torch.Tensor:
+    """Q8_0 blocks of 32 consecutive inputs along the last dim (K % 32 == 0), the
+    public ggml reference rule: d = amax / 127 (stored as fp16), q = the int8
+    nearest to w / d with halves away from zero (0 where the block is all zero).
+    Returns uint8 [..., K/32, 34]: per block the fp16 d (little endian), then the
+    32 codes as two's-complement bytes.
+    """
+    K = w.shape[-1]
+    assert K % 32 == 0
+    wb = w.reshape(*w.shape[:-1], K // 32, 32).to(torch.float32)
+    d = wb.abs().amax(dim=-1) / 127.0
+    inv = torch.where(d > 0, 1.0 / d, torch.zeros_like(d))
+    v = wb * inv.unsqueeze(-1)
+    q = (torch.sign(v) * torch.floor(v.abs() + 0.5)).clamp(-127, 127).to(torch.int8)
+    d16 = d.to(torch.float16).contiguous().view(torch.uint8).reshape(*d.shape, 2)
+    return torch.cat([d16, q.view(torch.uint8)], dim=-1).contiguous()
+
+
 def make_layer_weights(wl: Workload, gen: torch.Generator, device) -> dict:
     """Weights of one layer, drawn in the fixed order (router W, gammas, gate_up, down)."""
     E, D, F = wl.E, wl.D, wl.F
@@ -126,6 +146,10 @@ def make_layer_weights(wl: Workload, gen: torch.Generator, device) -> dict:
         dn = _randn((E, D, F), 0.02, gen, device)
         w["q_down"], w["s_down"] = quantize_i4g128(dn)
         del dn
+    elif wl.experts == "q8_0":
+        w["q8_gate_up"] = quantize_q8_0(gu)
+        del gu
+        w["q8_down"] = quantize_q8_0(_randn((E, D, F), 0.02, gen, device))
     else:
         w["w_gate_up"] = gu.to(torch.bfloat16)
         del gu

@@ -2,7 +2,7 @@
 
 All arrays are numpy arrays on the host. bf16 tensors are passed as their raw
 uint16 bit patterns, fp16 scales as uint16 bit patterns, int4 weights as the
-packed uint8 bytes.
+packed uint8 bytes, Q8_0 weights as their 34-byte blocks (uint8).
 """
 import ctypes
 import os
@@ -13,7 +13,7 @@ from .build import LIB, SRC, build
 
 _lib = None
 
-DT_F32, DT_BF16, DT_F16, DT_I4G128 = 0, 1, 2, 3
+DT_F32, DT_BF16, DT_F16, DT_I4G128, DT_Q8_0 = 0, 1, 2, 3, 4
 
 _p = ctypes.c_void_p
 _i = ctypes.c_int
@@ -37,6 +37,8 @@ def load():
     lib.oracle_float_to_bf16.argtypes = [ctypes.c_float]
     lib.oracle_dequant_i4.restype = None
     lib.oracle_dequant_i4.argtypes = [_p, _p, ctypes.c_int64, _i, _p]
+    lib.oracle_dequant_q8_0.restype = None
+    lib.oracle_dequant_q8_0.argtypes = [_p, ctypes.c_int64, _i, _p]
     lib.oracle_route.restype = _i
     lib.oracle_route.argtypes = [_i, _i, _i, _i, _d, _i, _p, _i, _p, _p, _p, _p, _p, _p, _p, _p, _p, _i]
     lib.oracle_permute.restype = _i
@@ -93,6 +95,28 @@ def dequant_i4(q, s, K):
     return out
 
 
+def dequant_q8_0(blocks, K):
+    """blocks: uint8 [rows, K/32 * 34] (or [rows, K/32, 34]) -> fp32 [rows, K]."""
+    rows = blocks.shape[0]
+    b = np.ascontiguousarray(blocks, dtype=np.uint8).reshape(rows, -1)
+    assert b.shape[1] == K // 32 * 34
+    out = np.empty((rows, K), dtype=np.float32)
+    load().oracle_dequant_q8_0(_ptr(b), rows, K, _ptr(out))
+    return out
+
+
+def _expert_arrays(w):
+    """(dtype code, gate_up, down, gate_up scales, down scales, F) of a weight dict."""
+    if "q_gate_up" in w:
+        gu = w["q_gate_up"]
+        return DT_I4G128, gu, w["q_down"], w["s_gate_up"], w["s_down"], gu.shape[1] // 2
+    if "q8_gate_up" in w:
+        gu = w["q8_gate_up"]
+        return DT_Q8_0, np.ascontiguousarray(gu), np.ascontiguousarray(w["q8_down"]), None, None, gu.shape[1] // 2
+    gu = w["w_gate_up"]
+    return DT_BF16, gu, w["w_down"], None, None, gu.shape[1] // 2
+
+
 def route(x, router_w, router_gamma, router_bias, k, eps, forced=None, n_threads=0):
     """Router only. Returns dict(idx [T,k] int32, w [T,k] f64, logits [T,E] f64, gap [T], r [T])."""
     T, D = x.shape
@@ -131,19 +155,13 @@ def moe_forward(w, x, k, eps, forced=None, tokens=None, add_input=False, addend=
     `w` is a dict of numpy arrays: router_w (f32 or uint16 bf16 bits) [E,D], router_gamma f32 [D],
     router_bias f32 [E] or None, ffn_gamma f32 [D], and either w_gate_up / w_down as uint16 bf16 bits
     ([E,2F,D] / [E,D,F]) or, for int4, q_gate_up uint8 [E,2F,D/2], s_gate_up uint16 [E,2F,D/128],
-    q_down uint8 [E,D,F/2], s_down uint16 [E,D,ceil(F/128)].
+    q_down uint8 [E,D,F/2], s_down uint16 [E,D,ceil(F/128)], or, for Q8_0, q8_gate_up uint8
+    [E,2F,D/32,34] and q8_down uint8 [E,D,F/32,34].
     Returns dict(out [n,D] f32, idx [n,k], w [n,k] f64, gap [n]).
     """
     T, D = x.shape
     E = w["router_w"].shape[0]
-    if "q_gate_up" in w:
-        ew = DT_I4G128
-        gu, dn, sgu, sdn = w["q_gate_up"], w["q_down"], w["s_gate_up"], w["s_down"]
-        F = gu.shape[1] // 2
-    else:
-        ew = DT_BF16
-        gu, dn, sgu, sdn = w["w_gate_up"], w["w_down"], None, None
-        F = gu.shape[1] // 2
+    ew, gu, dn, sgu, sdn, F = _expert_arrays(w)
     tok = None if tokens is None else np.ascontiguousarray(tokens, dtype=np.int32)
     n = T if tok is None else len(tok)
     out = np.empty((n, D), dtype=np.float32)
@@ -168,11 +186,7 @@ def expert_ffn(w, e, h):
     h = np.ascontiguousarray(h, dtype=np.float32)
     n, D = h.shape
     E = w["router_w"].shape[0]
-    if "q_gate_up" in w:
-        ew, gu, dn, sgu, sdn = DT_I4G128, w["q_gate_up"], w["q_down"], w["s_gate_up"], w["s_down"]
-    else:
-        ew, gu, dn, sgu, sdn = DT_BF16, w["w_gate_up"], w["w_down"], None, None
-    F = gu.shape[1] // 2
+    ew, gu, dn, sgu, sdn, F = _expert_arrays(w)
     y = np.empty((n, D), dtype=np.float32)
     rc = load().oracle_expert_ffn(D, F, E, e, ew, _ptr(gu), _ptr(dn), _ptr(sgu), _ptr(sdn), _ptr(h), n, _ptr(y))
     if rc != 0:

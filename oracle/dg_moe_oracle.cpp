@@ -20,6 +20,11 @@
 //    "Answers to the motivating questions", AWQ answer.
 //  * int4 weights: bits 4, group_size 128, symmetric, integer data type:
 //    auto-round PR, test log, quantization_config.
+//  * Q8_0 weights: the Q8 GGUF builds the pages measure (HF card
+//    "DiffusionGemma-26B-A4B-it - ROCmFP4 / ROCmFPX GGUF", Variants); the
+//    pages do not spell the format out, so it is read as the public ggml
+//    block of 32 consecutive inputs: an fp16 scale d followed by 32 int8
+//    codes q, standing for q * d.
 //
 // Readings where the pages are silent (each one is listed with its reason in
 // the design notes): router norm = the same (1+gamma) RMSNorm form as the
@@ -49,7 +54,7 @@
 
 namespace {
 
-enum { OR_F32 = 0, OR_BF16 = 1, OR_F16 = 2, OR_I4G128 = 3 };
+enum { OR_F32 = 0, OR_BF16 = 1, OR_F16 = 2, OR_I4G128 = 3, OR_Q8_0 = 4 };
 
 // bf16 -> fp32: a bf16 value is the upper 16 bits of an fp32 value.
 inline float bf16_bits_to_float(uint16_t b) {
@@ -106,7 +111,8 @@ inline float load_elem(const void* p, int dtype, size_t i) {
 // Weight element (row, k) of one expert matrix with K inputs per row.
 // bf16: dense [rows, K]. int4: bytes [rows, ceil(K/2)], element k in the low
 // nibble of byte k/2 when k is even and in the high nibble when k is odd;
-// scales fp16 [rows, ceil(K/128)].
+// scales fp16 [rows, ceil(K/128)]. Q8_0: K/32 blocks of 34 bytes per row,
+// block b = (fp16 scale d, little endian; int8 codes of inputs 32 b .. 32 b + 31).
 struct WeightView {
   int dtype;
   const void* data;
@@ -115,6 +121,12 @@ struct WeightView {
   float at(size_t row, int k) const {
     if (dtype == OR_BF16) {
       return bf16_bits_to_float(static_cast<const uint16_t*>(data)[row * K + k]);
+    }
+    if (dtype == OR_Q8_0) {
+      const uint8_t* blk = static_cast<const uint8_t*>(data) + (row * static_cast<size_t>(K / 32) + k / 32) * 34;
+      const uint16_t d = static_cast<uint16_t>(blk[0] | (blk[1] << 8));
+      const int q = static_cast<int8_t>(blk[2 + k % 32]);
+      return static_cast<float>(q) * half_bits_to_float(d);  // exact in fp32
     }
     const size_t row_bytes = (static_cast<size_t>(K) + 1) / 2;
     const uint8_t byte = static_cast<const uint8_t*>(data)[row * row_bytes + k / 2];
@@ -251,6 +263,13 @@ void oracle_dequant_i4(const uint8_t* q, const uint16_t* s, int64_t rows, int K,
     for (int k = 0; k < K; ++k) out[r * K + k] = v.at(static_cast<size_t>(r), k);
 }
 
+// Q8_0 blocks [rows, K/32, 34 bytes] -> fp32 [rows, K].
+void oracle_dequant_q8_0(const uint8_t* blocks, int64_t rows, int K, float* out) {
+  WeightView v{OR_Q8_0, blocks, nullptr, K};
+  for (int64_t r = 0; r < rows; ++r)
+    for (int k = 0; k < K; ++k) out[r * K + k] = v.at(static_cast<size_t>(r), k);
+}
+
 // Router only, for all T tokens. idx [T,K] int32, w [T,K] fp64, logits [T,E]
 // fp64 (nullable), gap [T] fp64 = 8th-largest minus 9th-largest logit
 // (nullable), r [T] fp64 (nullable). forced [T,K] (nullable) replaces the
@@ -306,7 +325,7 @@ int oracle_permute(int T, int K, int E, const int32_t* idx, int32_t* counts, int
 //   then, if add_input, out += fp32(x); if addend, out += fp32(addend).
 // out32 [n_tok, D] fp32 (before any output rounding). idx/w/gap per computed
 // token (nullable). dtypes: x/addend 0=f32 1=bf16; router_w 0=f32 1=bf16;
-// expert weights 1=bf16 3=int4-g128. Returns 0 or -1 on a bad argument.
+// expert weights 1=bf16 3=int4-g128 4=Q8_0. Returns 0 or -1 on a bad argument.
 int oracle_moe_forward(int T, int D, int F, int E, int K, double eps, int x_dtype, const void* x,
                        int rw_dtype, const void* router_w, const float* router_gamma,
                        const float* router_bias, const float* ffn_gamma, int ew_dtype,
@@ -315,8 +334,9 @@ int oracle_moe_forward(int T, int D, int F, int E, int K, double eps, int x_dtyp
                        int n_tok, int add_input, const void* addend, float* out32, int32_t* idx_out,
                        double* w_out, double* gap_out, int n_threads) {
   if (T < 0 || D <= 0 || F <= 0 || E <= 0 || K <= 0 || K > E) return -1;
-  if (ew_dtype != OR_BF16 && ew_dtype != OR_I4G128) return -1;
+  if (ew_dtype != OR_BF16 && ew_dtype != OR_I4G128 && ew_dtype != OR_Q8_0) return -1;
   if (ew_dtype == OR_I4G128 && (!s_gate_up || !s_down)) return -1;
+  if (ew_dtype == OR_Q8_0 && (D % 32 || F % 32)) return -1;
   Layer L{T, D, F, E, K, eps, x_dtype, x, rw_dtype, router_w, router_gamma, router_bias, ffn_gamma,
           ew_dtype, w_gate_up, w_down, s_gate_up, s_down};
   const int n = tokens ? n_tok : T;

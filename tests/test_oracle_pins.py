@@ -389,6 +389,52 @@ def test_int4_layer_matches_dense_reference_of_dequantised_weights():
     assert rel_err(o["out"], ref.numpy()) <= 2e-5
 
 
+def test_q8_0_block_layout_and_roundtrip():
+    # A hand-made block: fp16 scale 0.5 stored little endian (0x3800 -> bytes 00 38), then 32 int8
+    # codes in two's complement; each weight is code * 0.5 exactly.
+    codes = [-128, -127, -1, 0, 1, 2, 63, 127] + list(range(-12, 12))
+    blk = np.array([0x00, 0x38] + [c & 0xFF for c in codes], dtype=np.uint8)
+    assert blk.size == 34
+    deq = oracle.dequant_q8_0(blk.reshape(1, 34), 32)
+    assert np.array_equal(deq[0], np.array(codes, dtype=np.float32) * 0.5)
+    # Two blocks per row, two rows: the scale of block b covers inputs 32 b .. 32 b + 31 of its row.
+    two = np.zeros((2, 2, 34), dtype=np.uint8)
+    two[:, :, 0:2] = [[[0x00, 0x3C], [0x00, 0x40]], [[0x00, 0xBC], [0x00, 0x00]]]  # 1, 2, -1, 0
+    two[:, :, 2:] = 3
+    d2 = oracle.dequant_q8_0(two.reshape(2, 68), 64)
+    assert np.array_equal(d2, np.array([[3.0] * 32 + [6.0] * 32, [-3.0] * 32 + [0.0] * 32], dtype=np.float32))
+    # Round trip of the quantiser of the inputs: within half a step of the original weight, where the
+    # fp16 rounding of the scale (relative 2^-11) can move the largest code (127) by 127 * 2^-11 steps.
+    gen = torch.Generator().manual_seed(11)
+    w = torch.randn((5, 2816), generator=gen) * 0.02
+    w[1, 64:96] = 0.0  # an all-zero block: scale 0, codes 0
+    b = synth.quantize_q8_0(w)
+    assert b.shape == (5, 88, 34) and b.dtype == torch.uint8
+    deq = oracle.dequant_q8_0(b.numpy().reshape(5, -1), 2816)
+    step = np.repeat((w.reshape(5, 88, 32).abs().amax(-1) / 127.0).numpy(), 32, axis=1)
+    assert np.all(np.abs(deq - w.numpy()) <= step * (0.5 + 127 * 2 ** -11) + 1e-12)
+    assert np.all(deq[1, 64:96] == 0.0) and np.all(b[1, 2, :].numpy() == 0)
+    # the largest magnitude of every non-zero block maps to code +-127 (full range used)
+    q = b[..., 2:].numpy().view(np.int8).astype(np.int32)
+    nz = step[:, ::32] > 0
+    assert np.all(np.abs(q).max(axis=-1)[nz] == 127)
+
+
+def test_q8_0_layer_matches_dense_reference_of_dequantised_weights():
+    wl, x, w = small(T=12, E=6, K=2, D=256, F=192, seed=31, experts="q8_0")
+    xn, wn = np_inputs(x, w)
+    o = oracle.moe_forward(wn, xn, 2, EPS)
+    wf = f64_weights({k: v for k, v in wn.items() if k in ("router_w", "router_gamma", "ffn_gamma")})
+    wf["router_bias"] = None
+    E, D, Fd = 6, 256, 192
+    gu = oracle.dequant_q8_0(wn["q8_gate_up"].reshape(E * 2 * Fd, -1), D)
+    dn = oracle.dequant_q8_0(wn["q8_down"].reshape(E * D, -1), Fd)
+    wf["w_gate_up"] = torch.from_numpy(gu.reshape(E, 2 * Fd, D)).double()
+    wf["w_down"] = torch.from_numpy(dn.reshape(E, D, Fd)).double()
+    ref, _, _ = dense_moe_fp64(bits_to_f64(xn), wf, 2, EPS)
+    assert rel_err(o["out"], ref.numpy()) <= 2e-5
+
+
 # ----------------------------------------------------------------------------- shapes printed on the pages
 
 def test_shapes_from_the_pages():
