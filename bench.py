@@ -10,7 +10,7 @@ create into the GEMMs' fragment order (--borrow reads them in place, row-major).
 Prints one JSON line: tokens/s, the roofline of the dominant kernel (gate_up, HBM-bound) measured with
 HIP events on the launch stream, and the CPU oracle timed on the host on a bounded sample.
 
-  python bench.py [--steps K] [--warmup W] [--workload canvas256|encode2304|int4|canvas32|stack30]
+  python bench.py [--steps K] [--warmup W] [--workload canvas256|encode2304|int4|q8|canvas32|stack30]
 """
 import argparse
 import ctypes
@@ -69,6 +69,9 @@ def expert_bytes(wl):
     if wl.experts == "i4g128":
         gu = 2 * F * (D // 2) + 2 * F * (D // 128) * 2
         dn = D * (F // 2) + D * ((F + 127) // 128) * 2
+    elif wl.experts == "q8_0":  # 34 bytes per block of 32 inputs
+        gu = 2 * F * (D // 32) * 34
+        dn = D * (F // 32) * 34
     else:
         gu = 2 * F * D * 2
         dn = D * F * 2
@@ -164,6 +167,9 @@ def main():
     from expert_ffn_canvas_amd import dgmoe, synth
 
     wl = synth.WORKLOADS[args.workload]
+    if args.borrow and wl.experts == "q8_0":
+        print(json.dumps({"error": "Q8_0 experts are read from the packed copy only; drop --borrow"}))
+        sys.exit(2)
     dev = "cuda:0"
     torch.cuda.set_device(0)
     stream = torch.cuda.current_stream()
@@ -258,7 +264,7 @@ def main():
     layer_bytes, flops, gate_up_bytes = algorithmic(wl, T, touched)
     step_s = ms_per_step / 1e3
     layer_gbps = layer_bytes * n_layers / step_s / 1e9  # stack: touched of layer 0 as the estimate
-    peak_tflops = F16_PEAK_TFLOPS if wl.experts == "i4g128" else BF16_PEAK_TFLOPS
+    peak_tflops = F16_PEAK_TFLOPS if wl.experts in ("i4g128", "q8_0") else BF16_PEAK_TFLOPS
     roofline = None
     if kern_us:
         gu_s = kern_us["gate_up"] / 1e6
@@ -280,7 +286,7 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "int4-g128 weights, f16 MFMA" if wl.experts == "i4g128" else "bf16",
+        "dtype": {"i4g128": "int4-g128 weights, f16 MFMA", "q8_0": "q8_0 weights, f16 MFMA"}.get(wl.experts, "bf16"),
         "data": "synthetic",
         "config": {"workload": wl.name, "T": T, "n_experts": wl.E, "top_k": wl.K, "d_model": wl.D,
                    "d_ff": wl.F, "experts": wl.experts, "act": wl.act, "router_bias": wl.bias or "none",

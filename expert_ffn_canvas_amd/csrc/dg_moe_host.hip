@@ -119,9 +119,11 @@ dg_status check_config(const dg_moe_config* c) {
     return fail(DG_ERR_DTYPE, "act_dtype %d: only DG_F32 or DG_BF16", c->act_dtype);
   if (c->router_w_dtype != DG_F32 && c->router_w_dtype != DG_BF16)
     return fail(DG_ERR_DTYPE, "router_w_dtype %d: only DG_F32 or DG_BF16", c->router_w_dtype);
-  if (c->expert_w_dtype != DG_BF16 && c->expert_w_dtype != DG_I4G128)
-    return fail(DG_ERR_DTYPE, "expert_w_dtype %d: only DG_BF16 or DG_I4G128", c->expert_w_dtype);
+  if (c->expert_w_dtype != DG_BF16 && c->expert_w_dtype != DG_I4G128 && c->expert_w_dtype != DG_Q8_0)
+    return fail(DG_ERR_DTYPE, "expert_w_dtype %d: only DG_BF16, DG_I4G128 or DG_Q8_0", c->expert_w_dtype);
   if (c->flags & ~DG_MOE_PACK_WEIGHTS) return fail(DG_ERR_INVALID_ARG, "unknown config flags 0x%x", c->flags);
+  if (c->expert_w_dtype == DG_Q8_0 && !(c->flags & DG_MOE_PACK_WEIGHTS))
+    return fail(DG_ERR_DTYPE, "DG_Q8_0 experts are read from the packed copy only: set DG_MOE_PACK_WEIGHTS");
   return DG_OK;
 }
 
@@ -133,7 +135,7 @@ struct dg_moe_s {
   int device;
   char* ws;           // workspace + prepared router parameters
   void* packed;       // expert weights copied at create (pack mode), else null
-  int w_packed = 0;   // bf16 weights in the panel-fragment layout
+  int w_packed = 0;   // expert weights in the fragment layout of their packing kernel
   const void* w_gate_up;
   const void* w_down;
   const uint16_t* s_gate_up;
@@ -156,6 +158,12 @@ ExpertBytes expert_bytes(const dg_moe_config& c) {
   if (c.expert_w_dtype == DG_BF16) {
     b.gu = E * 2 * F * D * 2;
     b.dn = E * D * F * 2;
+  } else if (c.expert_w_dtype == DG_Q8_0) {  // packed only: 128 codes and 4 scales per (row, 128-input step)
+    const size_t nks_d = (D + 127) / 128, nks_f = (F + 127) / 128;
+    b.gu = E * 2 * F * nks_d * 128;
+    b.dn = E * D * nks_f * 128;
+    b.sgu = E * 2 * F * nks_d * 4 * 2;
+    b.sdn = E * D * nks_f * 4 * 2;
   } else {
     b.gu = E * 2 * F * (D / 2);
     b.dn = E * D * (F / 2);
@@ -202,6 +210,7 @@ dg_status dg_moe_create(const dg_moe_config* cfg, const dg_moe_weights* w, void*
   if (st != DG_OK) return st;
   if (!w || !out) return fail(DG_ERR_INVALID_ARG, "weights or out is NULL");
   const bool i4 = cfg->expert_w_dtype == DG_I4G128;
+  const bool q8 = cfg->expert_w_dtype == DG_Q8_0;
   if (!w->router_w || !w->router_gamma || !w->ffn_gamma || !w->w_gate_up || !w->w_down)
     return fail(DG_ERR_INVALID_ARG, "a required weight pointer is NULL");
   if (i4 && (!w->s_gate_up || !w->s_down)) return fail(DG_ERR_INVALID_ARG, "int4 weights need both scale tensors");
@@ -250,12 +259,23 @@ dg_status dg_moe_create(const dg_moe_config* cfg, const dg_moe_weights* w, void*
     char* p = static_cast<char*>(hd->packed);
     hd->w_gate_up = p;
     hd->w_down = p + round_up(eb.gu, 256);
-    hd->s_gate_up = i4 ? reinterpret_cast<const uint16_t*>(p + round_up(eb.gu, 256) + round_up(eb.dn, 256)) : nullptr;
-    hd->s_down = i4 ? reinterpret_cast<const uint16_t*>(p + round_up(eb.gu, 256) + round_up(eb.dn, 256) +
-                                                        round_up(eb.sgu, 256))
-                    : nullptr;
+    const bool scaled = i4 || q8;
+    hd->s_gate_up =
+        scaled ? reinterpret_cast<const uint16_t*>(p + round_up(eb.gu, 256) + round_up(eb.dn, 256)) : nullptr;
+    hd->s_down = scaled ? reinterpret_cast<const uint16_t*>(p + round_up(eb.gu, 256) + round_up(eb.dn, 256) +
+                                                            round_up(eb.sgu, 256))
+                        : nullptr;
     hipError_t c1, c2, c3 = hipSuccess, c4 = hipSuccess;
-    if (i4) {  // int4: codes and scales in fragment order
+    if (q8) {  // Q8_0: codes and scales in fragment order, per 128-input step
+      c1 = dg::launch_pack_q8(static_cast<const uint8_t*>(w->w_gate_up),
+                              static_cast<uint8_t*>(const_cast<void*>(hd->w_gate_up)),
+                              const_cast<uint16_t*>(hd->s_gate_up), cfg->n_experts, 2 * cfg->d_ff, cfg->d_model,
+                              stream);
+      c2 = dg::launch_pack_q8(static_cast<const uint8_t*>(w->w_down),
+                              static_cast<uint8_t*>(const_cast<void*>(hd->w_down)), const_cast<uint16_t*>(hd->s_down),
+                              cfg->n_experts, cfg->d_model, cfg->d_ff, stream);
+      hd->w_packed = 1;
+    } else if (i4) {  // int4: codes and scales in fragment order
       c1 = dg::launch_pack_i4(static_cast<const uint8_t*>(w->w_gate_up), w->s_gate_up,
                               static_cast<uint8_t*>(const_cast<void*>(hd->w_gate_up)),
                               const_cast<uint16_t*>(hd->s_gate_up), cfg->n_experts, 2 * cfg->d_ff, cfg->d_model,
@@ -333,6 +353,7 @@ static dg_status run_forward(dg_moe_handle hd, const void* x, void* out, int32_t
   hipStream_t stream = static_cast<hipStream_t>(stream_v);
   const Layout& L = hd->L;
   const bool i4 = c.expert_w_dtype == DG_I4G128;
+  const bool q8 = c.expert_w_dtype == DG_Q8_0;
   // per-kernel start/stop events: norm, logits, permute, gate_up, down, combine
   dg::KernelEvents kev[6];
   if (events)
@@ -354,7 +375,7 @@ static dg_status run_forward(dg_moe_handle hd, const void* x, void* out, int32_t
   ra.bias = hd->has_bias ? hd->at<float>(L.bias) : nullptr;
   ra.gamma_e = hd->at<float>(L.gamma_e);
   ra.eps = c.rms_eps;
-  ra.h_f16 = i4 ? 1 : 0;
+  ra.h_f16 = (i4 || q8) ? 1 : 0;
   ra.h = L.fold ? nullptr : hd->at<uint16_t>(L.h);
   ra.rnorm = hd->at<float>(L.rnorm);
   ra.logits = hd->at<float>(L.logits);
@@ -377,7 +398,7 @@ static dg_status run_forward(dg_moe_handle hd, const void* x, void* out, int32_t
   pa.T = T;
   pa.K = c.top_k;
   pa.E = c.n_experts;
-  const bool tall = !i4 && dg::use_tall_tiles(T, c.top_k, c.n_experts);
+  const bool tall = !i4 && !q8 && dg::use_tall_tiles(T, c.top_k, c.n_experts);
   pa.tile_rows = tall ? dg::kTallRows : dg::kTileRows;
   pa.deal_experts = tall ? 1 : 0;
   for (int g = 0; g < 2; ++g) {
@@ -410,14 +431,18 @@ static dg_status run_forward(dg_moe_handle hd, const void* x, void* out, int32_t
   ga.y = hd->at<uint16_t>(L.y);
   ga.D = c.d_model;
   ga.F = c.d_ff;
-  e = i4 ? dg::launch_gate_up_i4(ga, stream, ev(3))
-         : tall ? dg::launch_gate_up_tall(ga, stream, ev(3)) : dg::launch_gate_up_bf16(ga, stream, ev(3));
+  e = q8     ? dg::launch_gate_up_q8(ga, stream, ev(3))
+      : i4   ? dg::launch_gate_up_i4(ga, stream, ev(3))
+      : tall ? dg::launch_gate_up_tall(ga, stream, ev(3))
+             : dg::launch_gate_up_bf16(ga, stream, ev(3));
   if (e != hipSuccess) return hip_fail(e, "gate_up launch");
   ga.tiles = pa.tasks[1];
   ga.qlen = pa.qlen + dg::kQueues;
   ga.qmax = pa.qmax[1];
-  e = i4 ? dg::launch_down_i4(ga, stream, ev(4))
-         : tall ? dg::launch_down_tall(ga, stream, ev(4)) : dg::launch_down_bf16(ga, stream, ev(4));
+  e = q8     ? dg::launch_down_q8(ga, stream, ev(4))
+      : i4   ? dg::launch_down_i4(ga, stream, ev(4))
+      : tall ? dg::launch_down_tall(ga, stream, ev(4))
+             : dg::launch_down_bf16(ga, stream, ev(4));
   if (e != hipSuccess) return hip_fail(e, "down launch");
 
   dg::CombineArgs ca{};

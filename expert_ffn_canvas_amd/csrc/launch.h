@@ -59,7 +59,7 @@ struct RouterArgs {
   const float* bias;    // [E] or null
   const float* gamma_e;
   float eps;
-  int h_f16;            // expert input stored as fp16 (int4 experts) instead of bf16
+  int h_f16;            // expert input stored as fp16 (int4 or Q8_0 experts) instead of bf16
   uint16_t* h;          // [T, D] expert input (norm kernel only)
   float* rnorm;         // [T] r = 1/sqrt(mean x^2 + eps) of each token
   float* logits;        // [T, Epad]
@@ -97,17 +97,17 @@ struct GemmArgs {
   int qmax;                // their capacity
   const int32_t* sorted_slot;  // [K T] slot t K + j of each expert-sorted row
   int K;
-  const uint16_t* h;       // [T, D] expert input (bf16, or fp16 for int4 experts); the raw x when rnorm is set
+  const uint16_t* h;       // [T, D] expert input (bf16, or fp16 for int4 / Q8_0 experts); the raw x when rnorm is set
   const float* rnorm;      // [T] r of each token when h is the raw x and (1 + gamma_e) is folded into
                            // w_gate_up: the gate and up sums are scaled by it; else null
-  const void* w_gate_up;   // bf16 [E, 2F, D] or int4 bytes [E, 2F, D/2]
-  const void* w_down;      // bf16 [E, D, F] or int4 bytes [E, D, F/2]
+  const void* w_gate_up;   // bf16 [E, 2F, D], int4 bytes [E, 2F, D/2], or packed Q8_0 codes
+  const void* w_down;      // bf16 [E, D, F], int4 bytes [E, D, F/2], or packed Q8_0 codes
   const uint16_t* s_gate_up;
   const uint16_t* s_down;
   uint16_t* act;           // [K T, F] gelu_tanh(gate) * up, expert-sorted rows
   uint16_t* y;             // [K T, D] bf16 down(act), expert-sorted rows
   int D, F;
-  int w_packed;            // weights in the fragment layout of launch_pack_panels / launch_pack_i4
+  int w_packed;            // weights in the fragment layout of launch_pack_panels / _i4 / _q8
 };
 // Create-time relayout of bf16 expert weights [E][R][K] (R % 16 == 0,
 // K % 32 == 0) into MFMA fragment order: 1 KB block (e, s, p) holds, at lane
@@ -132,6 +132,16 @@ hipError_t launch_pack_i4(const uint8_t* codes, const uint16_t* scales, uint8_t*
                           int R, int K, hipStream_t stream);
 hipError_t launch_gate_up_i4(const GemmArgs& a, hipStream_t stream, const KernelEvents* ev);
 hipError_t launch_down_i4(const GemmArgs& a, hipStream_t stream, const KernelEvents* ev);
+// Create-time relayout of Q8_0 expert weights (rows of K / 32 blocks of 34
+// bytes: fp16 scale, 32 int8 codes) into fragment order: per (expert, 128-input
+// step, 16-row panel), 2 KB of codes (lane n + 16 g: 32 bytes of row n, 8 per
+// 32-input block, inputs 8 g .. 8 g + 7 in the order 0 2 1 3 4 6 5 7) and 64
+// scales [row][block]; a short last step is padded with zero codes and scales.
+hipError_t launch_pack_q8(const uint8_t* blocks, uint8_t* pcodes, uint16_t* pscales, int E, int R, int K,
+                          hipStream_t stream);
+// The products with packed Q8_0 weights (fp16 expert input and activation).
+hipError_t launch_gate_up_q8(const GemmArgs& a, hipStream_t stream, const KernelEvents* ev);
+hipError_t launch_down_q8(const GemmArgs& a, hipStream_t stream, const KernelEvents* ev);
 
 struct CombineArgs {
   const uint16_t* y;           // [K T, D] bf16 expert outputs, expert-sorted rows

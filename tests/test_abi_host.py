@@ -53,6 +53,9 @@ def test_workspace_bytes():
     T, K, D, F, E = 256, 8, 2816, 704, 128
     assert ws >= K * T * F * 2 + K * T * D * 2 + 3 * E * D * 2
     assert dgmoe.dg_moe_workspace_bytes(dgmoe.make_config(D=100)) == 0
+    q8 = dgmoe.make_config(max_tokens=256, experts=dgmoe.DG_Q8_0, flags=dgmoe.DG_MOE_PACK_WEIGHTS)
+    assert dgmoe.dg_moe_workspace_bytes(q8) >= K * T * F * 2 + K * T * D * 2 + 3 * E * D * 2
+    assert dgmoe.dg_moe_workspace_bytes(dgmoe.make_config(experts=dgmoe.DG_Q8_0)) == 0
 
 
 def _weights(align=16):
@@ -74,6 +77,9 @@ def _weights(align=16):
     ("act_dtype", dgmoe.DG_F16, dgmoe.DG_ERR_DTYPE),
     ("router_w_dtype", dgmoe.DG_I4G128, dgmoe.DG_ERR_DTYPE),
     ("expert_w_dtype", dgmoe.DG_F32, dgmoe.DG_ERR_DTYPE),
+    ("expert_w_dtype", 5, dgmoe.DG_ERR_DTYPE),
+    # Q8_0 blocks are read from the packed copy only: without DG_MOE_PACK_WEIGHTS it is refused
+    ("expert_w_dtype", dgmoe.DG_Q8_0, dgmoe.DG_ERR_DTYPE),
     ("flags", 0x80, dgmoe.DG_ERR_INVALID_ARG),
     ("struct_size", 12, dgmoe.DG_ERR_INVALID_ARG),
 ])
