@@ -88,7 +88,9 @@ def algorithmic(wl, T, touched):
     flops = T * K * 2 * 3 * D * F + T * 2 * E * D
     # gate_up launch: weights of touched experts + expert input rows [T, D] + gated activations [K T, F]
     gate_up_bytes = touched * gu + T * D * 2 + K * T * F * 2
-    return layer_bytes, flops, gate_up_bytes
+    # down launch: weights of touched experts + gated activations + per-slot outputs [K T, D]
+    down_bytes = touched * dn + K * T * F * 2 + K * T * D * 2
+    return layer_bytes, flops, gate_up_bytes, down_bytes
 
 
 def kernel_sources_digest():
@@ -100,9 +102,9 @@ def kernel_sources_digest():
     return h.hexdigest()[:16]
 
 
-def read_traffic(workload):
-    """HBM bytes per gate_up launch from the committed rocprofv3 counter summary, if it was taken on the
-    current kernel source for this workload; else None."""
+def read_traffic(workload, kernel):
+    """HBM bytes per launch of `kernel` from the committed rocprofv3 counter summary, if it was taken on the
+    current kernel source for this workload and kernel; else None."""
     if not os.path.exists(COUNTERS_FILE):
         return None
     kv = {}
@@ -110,7 +112,8 @@ def read_traffic(workload):
         if "=" in line and not line.startswith("#"):
             k, v = line.split("=", 1)
             kv[k.strip()] = v.strip()
-    if kv.get("source_digest") != kernel_sources_digest() or kv.get("workload") != workload:
+    if (kv.get("source_digest") != kernel_sources_digest() or kv.get("workload") != workload
+            or kv.get("kernel", "gate_up") != kernel):
         return None
     try:
         return float(kv["traffic_bytes_per_launch"])
@@ -257,23 +260,28 @@ def main():
         kern_us = {name: round(tot[k] / n_prof * 1e3, 2) for k, name in enumerate(KERNEL_NAMES)}
         if layers[0].expert_norm_folded:  # no norm kernel ran: its events bracket nothing
             kern_us["norm"] = 0.0
+        if layers[0].gemms_fused:  # one launch ran both GEMMs: its time is under gate_up+down
+            kern_us["gate_up+down"] = kern_us.pop("gate_up")
+            kern_us.pop("down")
         ev.destroy(evs)
     ev.destroy([e0, e1])
 
     n_layers = wl.layers
-    layer_bytes, flops, gate_up_bytes = algorithmic(wl, T, touched)
+    layer_bytes, flops, gate_up_bytes, down_bytes = algorithmic(wl, T, touched)
     step_s = ms_per_step / 1e3
     layer_gbps = layer_bytes * n_layers / step_s / 1e9  # stack: touched of layer 0 as the estimate
     peak_tflops = F16_PEAK_TFLOPS if wl.experts in ("i4g128", "q8_0") else BF16_PEAK_TFLOPS
     roofline = None
     if kern_us:
-        gu_s = kern_us["gate_up"] / 1e6
-        ach = gate_up_bytes / gu_s / 1e9
-        traffic = read_traffic(wl.name)
-        roofline = {"bound": "hbm", "kernel": "gate_up", "achieved": round(ach, 1), "peak": HBM_PEAK_GBPS,
+        # the dominant launch: gate_up, or the fused launch of both GEMMs
+        kname = "gate_up+down" if "gate_up+down" in kern_us else "gate_up"
+        kbytes = gate_up_bytes + down_bytes if kname == "gate_up+down" else gate_up_bytes
+        ach = kbytes / (kern_us[kname] / 1e6) / 1e9
+        traffic = read_traffic(wl.name, kname)
+        roofline = {"bound": "hbm", "kernel": kname, "achieved": round(ach, 1), "peak": HBM_PEAK_GBPS,
                     "unit": "GB/s", "frac": round(ach / HBM_PEAK_GBPS, 4),
-                    "traffic": traffic, "alg_bytes_per_launch": gate_up_bytes,
-                    "avg_launch_us": kern_us["gate_up"]}
+                    "traffic": traffic, "alg_bytes_per_launch": kbytes,
+                    "avg_launch_us": kern_us[kname]}
 
     result = {
         "metric": METRIC,

@@ -51,7 +51,7 @@ size_t act_elem_bytes(int dt) { return dt == DG_F32 ? 4 : 2; }
 // Sub-buffer layout of the workspace (byte offsets from the base).
 struct Layout {
   size_t h, rnorm, logits, tile_count, topk_idx, topk_w, counts, offsets, tasks[2], qlen, sorted_slot, row_of_slot, act,
-      y;
+      y, tile_done;
   size_t wr, bias, gamma_e;
   size_t total;
   int Epad, nb[2], qmax[2];  // per GEMM (gate_up, down): column blocks, queue capacity
@@ -60,6 +60,10 @@ struct Layout {
   // r, and the expert input h is never materialised
   bool fold;
 };
+
+// bf16 experts run both GEMMs in one launch (gate_up tasks, then each tile's
+// down tasks once its gate_up blocks are done), int4 and Q8_0 experts in two.
+bool fuses_gemms(const dg_moe_config& c) { return c.expert_w_dtype == DG_BF16; }
 
 bool folds_expert_norm(const dg_moe_config& c) {
   return (c.flags & DG_MOE_PACK_WEIGHTS) && c.expert_w_dtype == DG_BF16 && c.act_dtype == DG_BF16;
@@ -94,6 +98,7 @@ Layout plan(const dg_moe_config& c) {
   L.row_of_slot = take(K * T * 4);
   L.act = take(K * T * F * 2);
   L.y = take(K * T * D * 2);
+  L.tile_done = take(fuses_gemms(c) ? K * T * 4 : 0);
   L.wr = take(3 * (size_t)L.Epad * D * 2);
   L.bias = take(E * 4);
   L.gamma_e = take(D * 4);
@@ -399,8 +404,10 @@ static dg_status run_forward(dg_moe_handle hd, const void* x, void* out, int32_t
   pa.K = c.top_k;
   pa.E = c.n_experts;
   const bool tall = !i4 && !q8 && dg::use_tall_tiles(T, c.top_k, c.n_experts);
+  const bool fused = fuses_gemms(c);
   pa.tile_rows = tall ? dg::kTallRows : dg::kTileRows;
-  pa.deal_experts = tall ? 1 : 0;
+  pa.deal = fused ? dg::kDealBalanced : tall ? dg::kDealExperts : dg::kDealUnits;
+  pa.tile_done = fused ? hd->at<int32_t>(L.tile_done) : nullptr;
   for (int g = 0; g < 2; ++g) {
     pa.nb[g] = L.nb[g];
     pa.qmax[g] = dg::max_queue_len(T, c.top_k, c.n_experts, L.nb[g]);
@@ -431,19 +438,37 @@ static dg_status run_forward(dg_moe_handle hd, const void* x, void* out, int32_t
   ga.y = hd->at<uint16_t>(L.y);
   ga.D = c.d_model;
   ga.F = c.d_ff;
-  e = q8     ? dg::launch_gate_up_q8(ga, stream, ev(3))
-      : i4   ? dg::launch_gate_up_i4(ga, stream, ev(3))
-      : tall ? dg::launch_gate_up_tall(ga, stream, ev(3))
-             : dg::launch_gate_up_bf16(ga, stream, ev(3));
-  if (e != hipSuccess) return hip_fail(e, "gate_up launch");
-  ga.tiles = pa.tasks[1];
-  ga.qlen = pa.qlen + dg::kQueues;
-  ga.qmax = pa.qmax[1];
-  e = q8     ? dg::launch_down_q8(ga, stream, ev(4))
-      : i4   ? dg::launch_down_i4(ga, stream, ev(4))
-      : tall ? dg::launch_down_tall(ga, stream, ev(4))
-             : dg::launch_down_bf16(ga, stream, ev(4));
-  if (e != hipSuccess) return hip_fail(e, "down launch");
+  if (fused) {
+    dg::FusedGemmArgs fa{};
+    fa.gu = ga;
+    fa.dn = ga;
+    fa.dn.tiles = pa.tasks[1];
+    fa.dn.qlen = pa.qlen + dg::kQueues;
+    fa.dn.qmax = pa.qmax[1];
+    fa.tile_done = pa.tile_done;
+    fa.nb_gate_up = L.nb[0];
+    e = dg::launch_gemm_fused(fa, tall, stream, ev(3));
+    if (e != hipSuccess) return hip_fail(e, "GEMM launch");
+    if (events) {  // one launch for both GEMMs: the down events mark the point after it
+      e = hipEventRecord(kev[4].start, stream);
+      if (e == hipSuccess) e = hipEventRecord(kev[4].stop, stream);
+      if (e != hipSuccess) return hip_fail(e, "event record");
+    }
+  } else {
+    e = q8     ? dg::launch_gate_up_q8(ga, stream, ev(3))
+        : i4   ? dg::launch_gate_up_i4(ga, stream, ev(3))
+        : tall ? dg::launch_gate_up_tall(ga, stream, ev(3))
+               : dg::launch_gate_up_bf16(ga, stream, ev(3));
+    if (e != hipSuccess) return hip_fail(e, "gate_up launch");
+    ga.tiles = pa.tasks[1];
+    ga.qlen = pa.qlen + dg::kQueues;
+    ga.qmax = pa.qmax[1];
+    e = q8     ? dg::launch_down_q8(ga, stream, ev(4))
+        : i4   ? dg::launch_down_i4(ga, stream, ev(4))
+        : tall ? dg::launch_down_tall(ga, stream, ev(4))
+               : dg::launch_down_bf16(ga, stream, ev(4));
+    if (e != hipSuccess) return hip_fail(e, "down launch");
+  }
 
   dg::CombineArgs ca{};
   ca.y = ga.y;

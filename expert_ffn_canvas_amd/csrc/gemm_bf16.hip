@@ -158,17 +158,14 @@ __device__ __forceinline__ void k_loop(char* As, const uint16_t* const (&rowp)[R
   }
 }
 
-// The kernel body for tiles of up to ROWS rows (64, or 128 for experts that
-// receive many rows); `As` holds two K steps of ROWS activation rows.
+// The product of one task (tile `tl` of up to ROWS rows, 64 or 128 for
+// experts that receive many rows); `As` holds two K steps of ROWS activation
+// rows.
 template <bool GATE_UP, bool PK, int ROWS>
-__device__ __forceinline__ void gemm_body(const GemmArgs& a, char* As, float* rrow) {
+__device__ __forceinline__ void gemm_body(const GemmArgs& a, const Tile& tl, char* As, float* rrow) {
   constexpr int kBM = ROWS / 16;  // 16-row MFMA tiles, and activation transfers per wave per step
   const int F = a.F, D = a.D;
   const int K = GATE_UP ? D : F;
-  const int qx = blockIdx.x & (kQueues - 1);
-  const int j = blockIdx.x / kQueues;
-  if (j >= a.qlen[qx]) return;
-  const Tile tl = a.tiles[(size_t)j * kQueues + qx];
   const int nb = tl.nb;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int g = lane >> 4;
@@ -265,7 +262,9 @@ template <bool GATE_UP, bool PK>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3, 3))) void k_gemm_bf16(GemmArgs a) {
   __shared__ __attribute__((aligned(16))) char As[2 * kTileRows * kRowBytes];
   __shared__ float rrow[kTileRows];  // gate_up: r of each row's token, or 1
-  gemm_body<GATE_UP, PK, kTileRows>(a, As, rrow);
+  const int qx = blockIdx.x & (kQueues - 1), j = blockIdx.x / kQueues;
+  if (j >= a.qlen[qx]) return;
+  gemm_body<GATE_UP, PK, kTileRows>(a, a.tiles[(size_t)j * kQueues + qx], As, rrow);
 }
 
 // 128-row tiles: twice the accumulators and 64 KB of activation stages, two
@@ -274,7 +273,73 @@ template <bool GATE_UP, bool PK>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))) void k_gemm_tall(GemmArgs a) {
   __shared__ __attribute__((aligned(16))) char As[2 * kTallRows * kRowBytes];
   __shared__ float rrow[kTallRows];
-  gemm_body<GATE_UP, PK, kTallRows>(a, As, rrow);
+  const int qx = blockIdx.x & (kQueues - 1), j = blockIdx.x / kQueues;
+  if (j >= a.qlen[qx]) return;
+  gemm_body<GATE_UP, PK, kTallRows>(a, a.tiles[(size_t)j * kQueues + qx], As, rrow);
+}
+
+// Both GEMMs in one launch. Queue x (the workgroups b with b % 8 == x, all on
+// XCD x) runs its gate_up tasks, then its down tasks; the balanced deal put
+// every task of an expert's tiles into one queue. A gate_up task, once its
+// gated activations have reached this XCD's L2, counts itself on its tile;
+// a down task starts once its tile's count holds all gate_up blocks. The
+// workgroups of one XCD are dispatched in index order, so every gate_up task
+// a down task waits for is running or done and never waits itself. The wait
+// is bounded (about a tenth of a second): past it the task writes NaN for
+// its outputs instead of its product, so a broken assumption shows in the
+// result and the launch still ends.
+constexpr int kWaitPolls = 1 << 17;
+
+template <bool PK, int ROWS>
+__device__ __forceinline__ void fused_body(const FusedGemmArgs& f, char* As, float* rrow) {
+  __shared__ int ready;
+  const int qx = blockIdx.x & (kQueues - 1), j = blockIdx.x / kQueues;
+  const int ngu = f.gu.qlen[qx];
+  const int tid = threadIdx.x;
+  if (j < ngu) {
+    const Tile tl = f.gu.tiles[(size_t)j * kQueues + qx];
+    gemm_body<true, PK, ROWS>(f.gu, tl, As, rrow);
+    __builtin_amdgcn_s_waitcnt(0);  // this thread's stores have reached L2
+    __syncthreads();
+    if (tid == 0) atomicAdd(&f.tile_done[tl.row0], 1);
+    return;
+  }
+  const int jd = j - ngu;
+  if (jd >= f.dn.qlen[qx]) return;
+  const Tile tl = f.dn.tiles[(size_t)jd * kQueues + qx];
+  if (tid == 0) {
+    const int need = f.nb_gate_up;
+    int n = 0;
+    while (atomicAdd(&f.tile_done[tl.row0], 0) < need && n < kWaitPolls) {
+      __builtin_amdgcn_s_sleep(8);
+      ++n;
+    }
+    ready = n < kWaitPolls;
+  }
+  __syncthreads();
+  if (ready) {
+    gemm_body<false, PK, ROWS>(f.dn, tl, As, rrow);
+    return;
+  }
+  const int cols = 32 * kWaves;
+  for (int i = tid; i < tl.mc * cols; i += kThreads)
+    f.dn.y[(size_t)(tl.row0 + i / cols) * f.dn.D + tl.nb * cols + i % cols] = 0x7fc0;  // bf16 NaN
+}
+
+template <bool PK>
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3, 3))) void k_gemm_fused(
+    FusedGemmArgs f) {
+  __shared__ __attribute__((aligned(16))) char As[2 * kTileRows * kRowBytes];
+  __shared__ float rrow[kTileRows];
+  fused_body<PK, kTileRows>(f, As, rrow);
+}
+
+template <bool PK>
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))) void k_gemm_fused_tall(
+    FusedGemmArgs f) {
+  __shared__ __attribute__((aligned(16))) char As[2 * kTallRows * kRowBytes];
+  __shared__ float rrow[kTallRows];
+  fused_body<PK, kTallRows>(f, As, rrow);
 }
 
 // One wave per block of 64 lanes x 16 bytes: source block (e, p, s) of 16 rows
@@ -325,6 +390,14 @@ hipError_t launch_gate_up_tall(const GemmArgs& a, hipStream_t stream, const Kern
   const dim3 grid(kQueues * a.qmax);
   return launch_kernel(a.w_packed ? k_gemm_tall<true, true> : k_gemm_tall<true, false>, grid, dim3(kThreads), stream,
                        ev, a);
+}
+
+hipError_t launch_gemm_fused(const FusedGemmArgs& f, bool tall, hipStream_t stream, const KernelEvents* ev) {
+  const dim3 grid(kQueues * (f.gu.qmax + f.dn.qmax));
+  const bool pk = f.gu.w_packed != 0;
+  auto k = tall ? (pk ? k_gemm_fused_tall<true> : k_gemm_fused_tall<false>)
+                : (pk ? k_gemm_fused<true> : k_gemm_fused<false>);
+  return launch_kernel(k, grid, dim3(kThreads), stream, ev, f);
 }
 
 hipError_t launch_down_tall(const GemmArgs& a, hipStream_t stream, const KernelEvents* ev) {

@@ -36,13 +36,14 @@ inline bool use_tall_tiles(int T, int K, int E) { return (long)T * K >= 64L * E;
 constexpr int kQueues = 8;
 
 // Upper bound on the length of one task queue of a GEMM with NB column blocks
-// for T tokens: the tasks are dealt round robin in units of non-increasing
-// size, so no queue exceeds the mean by more than the largest unit: an
-// expert's tile count for one block (at most ceil(T / 64)), or with tall
-// tiles, dealt by expert, all its blocks (at most NB ceil(T / kTallRows)).
+// for T tokens. Every deal keeps each queue within one unit of the mean: round
+// robin over units of non-increasing size, and the balanced deal (each expert
+// to the least loaded queue, then level filling) alike. The largest unit is
+// all NB blocks of one expert's tiles, at most NB ceil(T / 64) tasks (tall
+// tiles are fewer), and the tile count never exceeds K T / 64 + E.
 inline int max_queue_len(int T, int K, int E, int NB) {
   const long max_tiles = ((long)K * T + kTileRows - 1) / kTileRows + E;
-  const long largest_unit = (T + kTileRows - 1) / kTileRows + (long)NB * ((T + kTallRows - 1) / kTallRows);
+  const long largest_unit = (long)NB * ((T + kTileRows - 1) / kTileRows);
   return (int)(((long)NB * max_tiles + kQueues - 1) / kQueues + largest_unit);
 }
 
@@ -75,11 +76,21 @@ hipError_t launch_logits(const RouterArgs& a, hipStream_t stream, const KernelEv
 hipError_t launch_prep_router_w(const void* w, int w_f32, const float* gamma_r, int E, int Epad, int D,
                                 uint16_t* planes, hipStream_t stream);
 
+// How the permutation deals the GEMM tasks to the per-XCD queues:
+//  kDealUnits: units (expert, column block) round robin, each GEMM on its own;
+//  kDealExperts: whole experts (all their tiles and blocks), rank r to queue r % 8;
+//  kDealBalanced: whole experts to balance the tile counts of the queues, the
+//    same expert to the same queue in both GEMMs (the fused GEMM needs each
+//    tile's gate_up and down tasks on one XCD).
+constexpr int kDealUnits = 0, kDealExperts = 1, kDealBalanced = 2;
+
 struct PermuteArgs {
   const int32_t* topk_idx;
   int T, K, E;
   int tile_rows;          // largest rows per tile: kTileRows, or kTallRows for the tall GEMMs
-  int deal_experts;       // deal whole experts (all their column blocks) to one queue each, not units
+  int deal;               // kDealUnits, kDealExperts or kDealBalanced
+  int32_t* tile_done;     // kDealBalanced: [K T], zeroed at the first row of every tile (the fused
+                          // GEMM's per-tile counters); else null
   int nb[2];              // column blocks of gate_up and down
   int qmax[2];            // capacity of each queue of gate_up and down
   int32_t* counts;        // [E]
@@ -124,6 +135,15 @@ hipError_t launch_down_bf16(const GemmArgs& a, hipStream_t stream, const KernelE
 // The same products for tiles of up to kTallRows rows (bf16 weights, packed or not).
 hipError_t launch_gate_up_tall(const GemmArgs& a, hipStream_t stream, const KernelEvents* ev);
 hipError_t launch_down_tall(const GemmArgs& a, hipStream_t stream, const KernelEvents* ev);
+// Both bf16 GEMMs in one launch (tasks dealt with kDealBalanced): the gate_up
+// tasks of each queue, then its down tasks, each down task waiting for the
+// gate_up blocks of its tile through tile_done (zeroed by the permutation).
+struct FusedGemmArgs {
+  GemmArgs gu, dn;
+  int32_t* tile_done;  // [K T] per tile, at its first row: gate_up tasks finished
+  int nb_gate_up;      // gate_up column blocks per tile
+};
+hipError_t launch_gemm_fused(const FusedGemmArgs& f, bool tall, hipStream_t stream, const KernelEvents* ev);
 // Create-time relayout of int4-g128 expert weights (codes [E][R][K/2], scales
 // [E][R][ceil(K/128)]) into fragment order: 1 KB of codes and 16 scales per
 // (expert, 16-row panel, 128-input group), the short last group padded with

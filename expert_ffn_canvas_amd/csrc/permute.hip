@@ -16,7 +16,10 @@
 //    unit sizes never grow along the deal, every queue holds the mean load
 //    to within one unit. With tall tiles the deal is by expert instead (all
 //    column blocks of rank r go to queue r % 8): an expert's tiles then share
-//    its activation rows, hundreds of them, in one L2;
+//    its activation rows, hundreds of them, in one L2. For the fused GEMM
+//    whole experts are dealt so that the queues' tile counts balance, the
+//    same expert to the same queue in both task lists, and the per-tile
+//    counters of that GEMM are zeroed;
 //  * the stable scatter: the rows of expert e hold its slots in increasing
 //    token order; sorted_slot[row] = t k + j (token t, slot j) and
 //    row_of_slot[t k + j] = row.
@@ -56,6 +59,66 @@ __device__ __forceinline__ void load_ids(const int32_t* idx, int t, int K, int (
   } else {
 #pragma unroll
     for (int j = 0; j < 8; ++j) e[j] = (j < K) ? idx[(size_t)t * K + j] : 0;
+  }
+}
+
+// Balanced deal of whole experts, all threads at once: qof[r] = queue of
+// expert rank r. Ranks come in non-increasing tile count; v1 is the smallest
+// nonzero count. The ranks with more than v1 tiles are dealt in snake order
+// (queues 0..7, then 7..0, ...); then the ranks of v1 tiles fill the least
+// loaded queues level by level: with queue q at level Lq = (tiles so far) / v1,
+// the i-th of them takes the i-th smallest pair (Lq + k, q), k = 0, 1, ...,
+// found by a binary search on the level. Deterministic, so both task lists
+// agree. Called by every thread of the block.
+__device__ void deal_balanced(const int* ntile, const int* order, int E, int tid, int* qof, int* shq) {
+  int* load = shq;       // [kQueues] tiles per queue after the snake part
+  int* v1s = shq + kQueues;
+  const int r = tid;
+  const int v = (r < E) ? ntile[order[r]] : 0;
+  if (tid < kQueues) load[tid] = 0;
+  const int nz = __syncthreads_count(r < E && v > 0);
+  if (nz == 0) return;
+  if (r == nz - 1) *v1s = v;
+  __syncthreads();
+  const int v1 = *v1s;
+  const bool heavy = r < nz && v > v1;
+  const int nh = __syncthreads_count(heavy);
+  if (heavy) {
+    const int q = ((r / kQueues) & 1) ? kQueues - 1 - r % kQueues : r % kQueues;
+    qof[r] = q;
+    atomicAdd(&load[q], v);
+  }
+  __syncthreads();
+  if (r >= nh && r < nz) {
+    int lv[kQueues];
+    int lmin = 0x7fffffff;
+#pragma unroll
+    for (int q = 0; q < kQueues; ++q) {
+      lv[q] = load[q] / v1;
+      lmin = min(lmin, lv[q]);
+    }
+    const int i = r - nh;
+    // the largest level lam with C(lam) <= i, C(lam) = sum_q max(0, lam - Lq)
+    int lo = lmin, hi = lmin + i;
+    while (lo < hi) {
+      const int mid = (lo + hi + 1) >> 1;
+      int c = 0;
+#pragma unroll
+      for (int q = 0; q < kQueues; ++q) c += max(0, mid - lv[q]);
+      if (c <= i) lo = mid; else hi = mid - 1;
+    }
+    int c = 0;
+#pragma unroll
+    for (int q = 0; q < kQueues; ++q) c += max(0, lo - lv[q]);
+    int j = i - c, pick = 0;
+#pragma unroll
+    for (int q = 0; q < kQueues; ++q) {  // the j-th queue (by index) at or below level lo
+      if (lv[q] <= lo) {
+        if (j == 0) pick = q;
+        --j;
+      }
+    }
+    qof[r] = pick;
   }
 }
 
@@ -126,6 +189,8 @@ __global__ __launch_bounds__(kThreads) void k_permute(PermuteArgs a) {
   __shared__ int base[kMaxE];
   __shared__ int cursor[kMaxE];
   __shared__ int order[kMaxE];
+  __shared__ int qof[kMaxE];  // kDealBalanced: queue of each expert rank
+  __shared__ int dshare[kQueues + 1];
   __shared__ int ntile[kMaxE];
   __shared__ int wsum[kMaxE / 64];
   __shared__ int pq[kQueues][kMaxE + 1];      // per queue of this GEMM: load of the ranks before r
@@ -212,12 +277,17 @@ __global__ __launch_bounds__(kThreads) void k_permute(PermuteArgs a) {
     r += __shfl_xor(r, 2);
     if (q == 0 && e < E) order[r] = e;
   }
+  if (a.deal == kDealBalanced) {
+    if (tid < kMaxE) qof[tid] = 0;
+    __syncthreads();
+    deal_balanced(ntile, order, E, tid, qof, dshare);
+  }
   __syncthreads();
 
   // --- per queue x of this GEMM g, the load that the units of experts
   // ranked before r put into x: wave x scans 4 ranks per lane. Expert rank r
   // owns units r NB .. r NB + NB - 1; unit u goes to queue u % 8 (or, dealing
-  // by expert, all of them to queue r % 8) and holds ntile tasks.
+  // by expert, all of them to queue r % 8 or qof[r]) and holds ntile tasks.
   const int g = role;
   const int NB = a.nb[g];
   if (wave < kQueues) {
@@ -226,7 +296,9 @@ __global__ __launch_bounds__(kThreads) void k_permute(PermuteArgs a) {
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int r = 4 * lane + i;
-      const int units = a.deal_experts ? ((r % kQueues == x) ? NB : 0) : n_mod((r + 1) * NB, x) - n_mod(r * NB, x);
+      const int units = a.deal == kDealUnits     ? n_mod((r + 1) * NB, x) - n_mod(r * NB, x)
+                        : a.deal == kDealExperts ? ((r % kQueues == x) ? NB : 0)
+                                                 : ((r < E && qof[r] == x) ? NB : 0);
       v[i] = (r < E) ? ntile[order[r]] * units : 0;
       run += v[i];
     }
@@ -283,8 +355,9 @@ __global__ __launch_bounds__(kThreads) void k_permute(PermuteArgs a) {
       const int e = order[r], nt = ntile[e];
       const int local = p - pre[r];
       const int m = local / nt, i = local - m * nt;
-      const int nb0 = a.deal_experts ? 0 : (x - (r * NB) % kQueues + kQueues) % kQueues;
-      const int nb_step = a.deal_experts ? 1 : kQueues;
+      const bool by_unit = a.deal == kDealUnits;
+      const int nb0 = by_unit ? (x - (r * NB) % kQueues + kQueues) % kQueues : 0;
+      const int nb_step = by_unit ? kQueues : 1;
       const int ce = cnt[e];
       Tile tl;
       tl.e = e;
@@ -292,6 +365,7 @@ __global__ __launch_bounds__(kThreads) void k_permute(PermuteArgs a) {
       tl.mc = (ce * (i + 1)) / nt - (ce * i) / nt;
       tl.nb = nb0 + nb_step * m;
       a.tasks[g][pl] = tl;
+      if (g == 0 && a.tile_done != nullptr && tl.nb == 0) a.tile_done[tl.row0] = 0;
     }
   }
 }

@@ -367,7 +367,10 @@ def test_profiled_forward_times_each_kernel(canvas256):
         assert hip.hipEventElapsedTime(ctypes.byref(t), evs[2 * k], evs[2 * k + 1]) == 0
         ms.append(t.value)
     print("kernel ms", [round(v, 4) for v in ms])
-    assert all(v > 0 for v in ms)
+    # the norm (folded here) and the down GEMM (fused with gate_up for bf16 experts) bracket no launch of
+    # their own: their pairs are recorded back to back
+    assert all(v >= 0 for v in ms)
+    assert all(ms[k] > 0 for k in (1, 2, 3, 5))
     # a NULL event is rejected before anything is launched
     bad = list(evs)
     bad[7] = None
