@@ -264,7 +264,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3, 3))
   __shared__ float rrow[kTileRows];  // gate_up: r of each row's token, or 1
   const int qx = blockIdx.x & (kQueues - 1), j = blockIdx.x / kQueues;
   if (j >= a.qlen[qx]) return;
-  gemm_body<GATE_UP, PK, kTileRows>(a, a.tiles[(size_t)j * kQueues + qx], As, rrow);
+  gemm_body<GATE_UP, PK, kTileRows>(a, a.tiles[(size_t)qx * a.qmax + j], As, rrow);
 }
 
 // 128-row tiles: twice the accumulators and 64 KB of activation stages, two
@@ -275,7 +275,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
   __shared__ float rrow[kTallRows];
   const int qx = blockIdx.x & (kQueues - 1), j = blockIdx.x / kQueues;
   if (j >= a.qlen[qx]) return;
-  gemm_body<GATE_UP, PK, kTallRows>(a, a.tiles[(size_t)j * kQueues + qx], As, rrow);
+  gemm_body<GATE_UP, PK, kTallRows>(a, a.tiles[(size_t)qx * a.qmax + j], As, rrow);
 }
 
 // Both GEMMs in one launch. Queue x (the workgroups b with b % 8 == x, all on
@@ -297,7 +297,7 @@ __device__ __forceinline__ void fused_body(const FusedGemmArgs& f, char* As, flo
   const int ngu = f.gu.qlen[qx];
   const int tid = threadIdx.x;
   if (j < ngu) {
-    const Tile tl = f.gu.tiles[(size_t)j * kQueues + qx];
+    const Tile tl = f.gu.tiles[(size_t)qx * f.gu.qmax + j];
     gemm_body<true, PK, ROWS>(f.gu, tl, As, rrow);
     __builtin_amdgcn_s_waitcnt(0);  // this thread's stores have reached L2
     __syncthreads();
@@ -306,7 +306,7 @@ __device__ __forceinline__ void fused_body(const FusedGemmArgs& f, char* As, flo
   }
   const int jd = j - ngu;
   if (jd >= f.dn.qlen[qx]) return;
-  const Tile tl = f.dn.tiles[(size_t)jd * kQueues + qx];
+  const Tile tl = f.dn.tiles[(size_t)qx * f.dn.qmax + jd];
   if (tid == 0) {
     const int need = f.nb_gate_up;
     int n = 0;

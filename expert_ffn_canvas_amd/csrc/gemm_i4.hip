@@ -88,7 +88,7 @@ __global__ __launch_bounds__(kThreads) void k_gate_up_i4(GemmArgs a) {
   const int qx = blockIdx.x & (kQueues - 1);
   const int jq = blockIdx.x / kQueues;
   if (jq >= a.qlen[qx]) return;
-  const Tile tl = a.tiles[(size_t)jq * kQueues + qx];
+  const Tile tl = a.tiles[(size_t)qx * a.qmax + jq];
   const int fb = tl.nb;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int nmt = (tl.mc + 15) >> 4;
@@ -191,7 +191,7 @@ __global__ __launch_bounds__(kThreads) void k_down_i4(GemmArgs a) {
   const int qx = blockIdx.x & (kQueues - 1);
   const int jq = blockIdx.x / kQueues;
   if (jq >= a.qlen[qx]) return;
-  const Tile tl = a.tiles[(size_t)jq * kQueues + qx];
+  const Tile tl = a.tiles[(size_t)qx * a.qmax + jq];
   const int nb = tl.nb;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int nmt = (tl.mc + 15) >> 4;
@@ -487,7 +487,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
   const int qx = blockIdx.x & (kQueues - 1);
   const int j = blockIdx.x / kQueues;
   if (j >= a.qlen[qx]) return;
-  const Tile tl = a.tiles[(size_t)j * kQueues + qx];
+  const Tile tl = a.tiles[(size_t)qx * a.qmax + j];
   const int nb = tl.nb;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int g = lane >> 4;

@@ -201,7 +201,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
   const int qx = blockIdx.x & (kQueues - 1);
   const int j = blockIdx.x / kQueues;
   if (j >= a.qlen[qx]) return;
-  const Tile tl = a.tiles[(size_t)j * kQueues + qx];
+  const Tile tl = a.tiles[(size_t)qx * a.qmax + j];
   const int nb = tl.nb;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int g = lane >> 4;

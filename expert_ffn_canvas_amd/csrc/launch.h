@@ -95,7 +95,7 @@ struct PermuteArgs {
   int qmax[2];            // capacity of each queue of gate_up and down
   int32_t* counts;        // [E]
   int32_t* offsets;       // [E + 1]
-  Tile* tasks[2];         // [qmax][kQueues] each: task p of queue x at tasks[p * kQueues + x]
+  Tile* tasks[2];         // [kQueues][qmax] each: task p of queue x at tasks[x * qmax + p]
   int32_t* qlen;          // [2][kQueues]
   int32_t* sorted_slot;   // [K T] slot t K + j of each expert-sorted row
   int32_t* row_of_slot;   // [K T]

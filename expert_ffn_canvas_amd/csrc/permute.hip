@@ -1,12 +1,13 @@
-// Token -> expert permutation on gfx950, in three workgroups of 1024 threads
-// that share the histogram and scan and split the rest (on three CUs at once):
-// workgroup 0 writes counts, offsets and the gate_up task queues, workgroup 1
-// the down task queues, workgroup 2 the stable scatter. The outputs:
+// Token -> expert permutation on gfx950, in 17 workgroups of 1024 threads on
+// 17 CUs at once. Each builds the histogram and the scan; then workgroup
+// g 8 + x (g = 0 for gate_up, 1 for down) ranks the experts, deals them and
+// writes task queue x of GEMM g (workgroup 0 also counts and offsets), and
+// workgroup 16 does the stable scatter. The outputs:
 //  * counts[e]: tokens routed to expert e (their sum is k T);
 //  * offsets: exclusive prefix sum of counts (the rows of expert e are
 //    offsets[e] .. offsets[e+1]-1 in expert-sorted order);
 //  * the task queues of the two grouped GEMMs. Each expert's rows are cut
-//    into ceil(count / R) tiles of near-equal size (R = 64, or 192 for the
+//    into ceil(count / R) tiles of near-equal size (R = 64, or 128 for the
 //    tall-tile GEMMs); a task is one tile times
 //    one column block of the expert's weight. Units (expert, column block),
 //    each holding all tiles of that expert for that block, are ranked by
@@ -27,9 +28,9 @@
 //
 // Each part runs in one workgroup, and a store instruction whose 64 lanes hit
 // 64 different cache lines costs 64 line transactions, so the layout of the
-// writes is what bounds it: the task lists are written by position (each lane
-// finds which unit covers its position), and the sorted slots are ranked into
-// LDS and written out in order when they fit.
+// writes is what bounds it: a queue's tasks are contiguous and written by
+// position (each lane finds which unit covers its position), and the sorted
+// slots are ranked into LDS and written out in order when they fit.
 //
 // Source of the per-expert token counts: Quant-Tuner PR "Add DiffusionGemma
 // (Gemma-4 MoE block-diffusion) support", "Answers to the motivating
@@ -45,6 +46,21 @@ constexpr int kThreads = 1024;
 constexpr int kWavesP = kThreads / 64;
 constexpr int kMaxE = 256;
 constexpr int kStage = 20480;  // sorted slots staged in LDS (k T up to this many)
+
+// floor(a / b) for a >= 0, 1 <= b < 2^24. Below 2^22 a float reciprocal
+// estimate is off by at most one and is corrected to the exact quotient;
+// larger numerators (a tile boundary of an expert with very many rows) take
+// the 64-bit division.
+__device__ __forceinline__ int div_small(long long a, int b) {
+  if (a < (1 << 22)) {
+    const int ai = (int)a;
+    int q = (int)((float)ai * __builtin_amdgcn_rcpf((float)b));
+    q -= (q * b > ai);
+    q += ((q + 1) * b <= ai);
+    return q;
+  }
+  return (int)(a / b);
+}
 
 // Number of v in [0, m) with v % kQueues == x (m >= 0, 0 <= x < kQueues).
 __device__ __forceinline__ int n_mod(int m, int x) { return m > x ? (m - x + kQueues - 1) / kQueues : 0; }
@@ -89,12 +105,14 @@ __device__ void deal_balanced(const int* ntile, const int* order, int E, int tid
     atomicAdd(&load[q], v);
   }
   __syncthreads();
+  if (tid < kQueues) load[tid] /= v1;
+  __syncthreads();
   if (r >= nh && r < nz) {
     int lv[kQueues];
     int lmin = 0x7fffffff;
 #pragma unroll
     for (int q = 0; q < kQueues; ++q) {
-      lv[q] = load[q] / v1;
+      lv[q] = load[q];
       lmin = min(lmin, lv[q]);
     }
     const int i = r - nh;
@@ -193,14 +211,14 @@ __global__ __launch_bounds__(kThreads) void k_permute(PermuteArgs a) {
   __shared__ int dshare[kQueues + 1];
   __shared__ int ntile[kMaxE];
   __shared__ int wsum[kMaxE / 64];
-  __shared__ int pq[kQueues][kMaxE + 1];      // per queue of this GEMM: load of the ranks before r
+  __shared__ int pq[1][kMaxE + 1];            // this queue: load of the ranks before r
   __shared__ uint64_t masks[kWavesP][kMaxE];  // per wave and expert: lanes whose token has it
   __shared__ int wpre[kWavesP][kMaxE];        // first row of (wave, expert) in the chunk
   __shared__ int stage[kStage];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int E = a.E, K = a.K, T = a.T;
-  const int role = blockIdx.x;  // 0, 1: the task queues of GEMM `role`; 2: the scatter
+  const int role = blockIdx.x;  // 0 .. 15: queue role % 8 of GEMM role / 8; 16: the scatter
   const bool staged = (size_t)K * T <= (size_t)kStage;
 
   // the first chunk of tokens is loaded once and kept for the scatter
@@ -243,7 +261,7 @@ __global__ __launch_bounds__(kThreads) void k_permute(PermuteArgs a) {
     base[tid] = excl;
     cursor[tid] = excl;
     if (tid < E) {
-      if (role == 0) {
+      if (role == 0) {  // counts and offsets: the first task-list workgroup
         a.offsets[tid] = excl;
         a.counts[tid] = c;
         if (tid == E - 1) a.offsets[E] = excl + c;
@@ -251,7 +269,7 @@ __global__ __launch_bounds__(kThreads) void k_permute(PermuteArgs a) {
       ntile[tid] = (c + a.tile_rows - 1) / a.tile_rows;
     }
   }
-  if (role == 2) {
+  if (role == 2 * kQueues) {
     scatter(a, ids, cursor, masks, wpre, stage, staged, tid, lane, wave);
     return;
   }
@@ -284,14 +302,14 @@ __global__ __launch_bounds__(kThreads) void k_permute(PermuteArgs a) {
   }
   __syncthreads();
 
-  // --- per queue x of this GEMM g, the load that the units of experts
-  // ranked before r put into x: wave x scans 4 ranks per lane. Expert rank r
-  // owns units r NB .. r NB + NB - 1; unit u goes to queue u % 8 (or, dealing
-  // by expert, all of them to queue r % 8 or qof[r]) and holds ntile tasks.
-  const int g = role;
+  // --- queue x of GEMM g: the load that the units of the experts ranked
+  // before r put into it (one wave, 4 ranks per lane). Expert rank r owns
+  // units r NB .. r NB + NB - 1; unit u goes to queue u % 8 (or, dealing by
+  // expert, all of them to queue r % 8 or qof[r]) and holds ntile tasks.
+  const int g = role / kQueues, x = role % kQueues;
   const int NB = a.nb[g];
-  if (wave < kQueues) {
-    const int x = wave;
+  int* pre = pq[0];
+  if (wave == 0) {
     int v[4], run = 0;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
@@ -308,72 +326,66 @@ __global__ __launch_bounds__(kThreads) void k_permute(PermuteArgs a) {
       if (lane >= d) incl2 += o;
     }
     int before = incl2 - run;
-    if (lane == 0) pq[x][0] = 0;
+    if (lane == 0) pre[0] = 0;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       before += v[i];
-      pq[x][4 * lane + i + 1] = before;  // load of ranks 0 .. 4 lane + i
+      pre[4 * lane + i + 1] = before;  // load of ranks 0 .. 4 lane + i
     }
   }
   __syncthreads();
-  if (tid < kQueues) a.qlen[g * kQueues + tid] = min(pq[tid][E], a.qmax[g]);
+  const int len = min(pre[E], a.qmax[g]);
+  if (tid == 0) a.qlen[g * kQueues + x] = len;
 
-  // --- the tasks, one lane per queue position: position p of queue x is
-  // tasks[8 p + x], so consecutive lanes write consecutive entries. The lane
+  // --- the tasks of the queue, one lane per position p, stored at
+  // tasks[x qmax + p] (consecutive lanes, consecutive entries). The lane
   // needs the expert rank r whose units cover p: a table of the rank at every
-  // position, built in the (not yet used) staging memory by one lane per
-  // (queue, rank), when the queues fit in it; else a binary search on the
-  // queue's prefix. Then it finds the unit and the tile inside it.
-  {
-    int longest = 0;
-#pragma unroll
-    for (int x = 0; x < kQueues; ++x) longest = max(longest, min(pq[x][E], a.qmax[g]));
-    const bool table = kQueues * longest <= kStage;
+  // position (one lane per rank fills its positions) for the unit deal, where
+  // each rank holds a few; else a binary search on the queue's prefix. Then
+  // it finds the unit and the tile inside it.
+  Tile* out = a.tasks[g] + (size_t)x * a.qmax[g];
+  const bool table = a.deal == kDealUnits && len <= kStage;
+  if (table) {
+    for (int r = tid; r < E; r += kThreads) {
+      const int p1 = min(pre[r + 1], len);
+      for (int p = pre[r]; p < p1; ++p) stage[p] = r;
+    }
+    __syncthreads();
+  }
+  const bool by_unit = a.deal == kDealUnits;
+  for (int p = tid; p < len; p += kThreads) {
+    int r;
     if (table) {
-      for (int i = tid; i < kQueues * E; i += kThreads) {
-        const int x = i / E, r = i - x * E;
-        const int p1 = min(pq[x][r + 1], longest);
-        for (int p = pq[x][r]; p < p1; ++p) stage[kQueues * p + x] = r;
+      r = stage[p];
+    } else {
+      int lo = 0, hi = E;  // pre[lo] <= p < pre[hi]
+      while (hi - lo > 1) {
+        const int mid = (lo + hi) >> 1;
+        if (pre[mid] <= p) lo = mid; else hi = mid;
       }
-      __syncthreads();
+      r = lo;
     }
-    for (int pl = tid; pl < kQueues * longest; pl += kThreads) {
-      const int x = pl % kQueues, p = pl / kQueues;
-      const int* pre = pq[x];
-      if (p >= min(pre[E], a.qmax[g])) continue;
-      int r;
-      if (table) {
-        r = stage[pl];
-      } else {
-        int lo = 0, hi = E;  // pre[lo] <= p < pre[hi]
-        while (hi - lo > 1) {
-          const int mid = (lo + hi) >> 1;
-          if (pre[mid] <= p) lo = mid; else hi = mid;
-        }
-        r = lo;
-      }
-      const int e = order[r], nt = ntile[e];
-      const int local = p - pre[r];
-      const int m = local / nt, i = local - m * nt;
-      const bool by_unit = a.deal == kDealUnits;
-      const int nb0 = by_unit ? (x - (r * NB) % kQueues + kQueues) % kQueues : 0;
-      const int nb_step = by_unit ? kQueues : 1;
-      const int ce = cnt[e];
-      Tile tl;
-      tl.e = e;
-      tl.row0 = base[e] + (ce * i) / nt;
-      tl.mc = (ce * (i + 1)) / nt - (ce * i) / nt;
-      tl.nb = nb0 + nb_step * m;
-      a.tasks[g][pl] = tl;
-      if (g == 0 && a.tile_done != nullptr && tl.nb == 0) a.tile_done[tl.row0] = 0;
-    }
+    const int e = order[r], nt = ntile[e];
+    const int local = p - pre[r];
+    const int m = div_small(local, nt), i = local - m * nt;
+    const int nb0 = by_unit ? (x - (r * NB) % kQueues + kQueues) % kQueues : 0;
+    const int nb_step = by_unit ? kQueues : 1;
+    const int ce = cnt[e];
+    Tile tl;
+    tl.e = e;
+    const int r0 = div_small((long long)ce * i, nt), r1 = div_small((long long)ce * (i + 1), nt);
+    tl.row0 = base[e] + r0;
+    tl.mc = r1 - r0;
+    tl.nb = nb0 + nb_step * m;
+    out[p] = tl;
+    if (g == 0 && a.tile_done != nullptr && tl.nb == 0) a.tile_done[tl.row0] = 0;
   }
 }
 
 }  // namespace
 
 hipError_t launch_permute(const PermuteArgs& a, hipStream_t stream, const KernelEvents* ev) {
-  return launch_kernel(k_permute, dim3(3), dim3(kThreads), stream, ev, a);
+  return launch_kernel(k_permute, dim3(2 * kQueues + 1), dim3(kThreads), stream, ev, a);
 }
 
 }  // namespace dg
