@@ -61,9 +61,11 @@ struct Layout {
   bool fold;
 };
 
-// bf16 experts run both GEMMs in one launch (gate_up tasks, then each tile's
-// down tasks once its gate_up blocks are done), int4 and Q8_0 experts in two.
-bool fuses_gemms(const dg_moe_config& c) { return c.expert_w_dtype == DG_BF16; }
+// Both GEMMs run in one launch (gate_up tasks, then each tile's down tasks once
+// its gate_up blocks are done), except for int4 experts read in place.
+bool fuses_gemms(const dg_moe_config& c) {
+  return c.expert_w_dtype != DG_I4G128 || (c.flags & DG_MOE_PACK_WEIGHTS);
+}
 
 bool folds_expert_norm(const dg_moe_config& c) {
   return (c.flags & DG_MOE_PACK_WEIGHTS) && c.expert_w_dtype == DG_BF16 && c.act_dtype == DG_BF16;
@@ -447,7 +449,9 @@ static dg_status run_forward(dg_moe_handle hd, const void* x, void* out, int32_t
     fa.dn.qmax = pa.qmax[1];
     fa.tile_done = pa.tile_done;
     fa.nb_gate_up = L.nb[0];
-    e = dg::launch_gemm_fused(fa, tall, stream, ev(3));
+    e = q8 ? dg::launch_gemm_fused_q8(fa, stream, ev(3))
+        : i4 ? dg::launch_gemm_fused_i4(fa, stream, ev(3))
+             : dg::launch_gemm_fused(fa, tall, stream, ev(3));
     if (e != hipSuccess) return hip_fail(e, "GEMM launch");
     if (events) {  // one launch for both GEMMs: the down events mark the point after it
       e = hipEventRecord(kev[4].start, stream);
@@ -455,18 +459,13 @@ static dg_status run_forward(dg_moe_handle hd, const void* x, void* out, int32_t
       if (e != hipSuccess) return hip_fail(e, "event record");
     }
   } else {
-    e = q8     ? dg::launch_gate_up_q8(ga, stream, ev(3))
-        : i4   ? dg::launch_gate_up_i4(ga, stream, ev(3))
-        : tall ? dg::launch_gate_up_tall(ga, stream, ev(3))
-               : dg::launch_gate_up_bf16(ga, stream, ev(3));
+    // int4 experts read in place (row-major codes): two launches
+    e = dg::launch_gate_up_i4(ga, stream, ev(3));
     if (e != hipSuccess) return hip_fail(e, "gate_up launch");
     ga.tiles = pa.tasks[1];
     ga.qlen = pa.qlen + dg::kQueues;
     ga.qmax = pa.qmax[1];
-    e = q8     ? dg::launch_down_q8(ga, stream, ev(4))
-        : i4   ? dg::launch_down_i4(ga, stream, ev(4))
-        : tall ? dg::launch_down_tall(ga, stream, ev(4))
-               : dg::launch_down_bf16(ga, stream, ev(4));
+    e = dg::launch_down_i4(ga, stream, ev(4));
     if (e != hipSuccess) return hip_fail(e, "down launch");
   }
 

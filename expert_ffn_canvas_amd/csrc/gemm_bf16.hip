@@ -21,17 +21,18 @@
 // Mapping: one workgroup = 4 waves = one (tile, column block). Each wave owns
 // two 16-row weight panels (gate+up, or two down panels) for every row of the
 // tile, so every weight byte is read by exactly one wave and goes straight
-// from global memory into MFMA operand registers; the next K step of
-// the panels is in flight while the current one is multiplied (256-wide K steps). The tile's
-// activation rows are staged once per K step into LDS (double-buffered) and
-// shared by the four waves. The main loop is specialised on the number of
-// 16-row MFMA tiles the tile needs (1..4) and is branch-free inside (rows past
-// the tile re-read its last row), so the next step's loads stay in flight
-// across the current step's MFMAs.
+// from global memory into MFMA operand registers; the next K step of the
+// panels (128 inputs) is in flight while the current one is multiplied. The
+// tile's activation rows are staged once per K step into LDS (double-buffered)
+// and shared by the four waves. The main loop is specialised on the number of
+// 16-row MFMA tiles the tile needs (1..4, or up to 8 for 128-row tiles) and is
+// branch-free inside (rows past the tile re-read its last row), so the next
+// step's loads stay in flight across the current step's MFMAs.
 //
-// Work distribution: workgroup b takes task b / 8 of queue b % 8 (its XCD); the
-// permutation kernel balanced the queues and put the tiles that share a
-// weight block into one queue, next to each other.
+// Work distribution: both GEMMs run in one launch. Workgroup b takes task
+// b / 8 of queue b % 8 (its XCD): the queue's gate_up tasks, then its down
+// tasks, each down task once its tile's gate_up blocks are done. The
+// permutation dealt whole experts to balance the queues.
 #include "dg_common.h"
 #include "gemm_common.h"
 #include "launch.h"
@@ -256,90 +257,29 @@ __device__ __forceinline__ void gemm_body(const GemmArgs& a, const Tile& tl, cha
   }
 }
 
-// Three workgroups per CU (waves_per_eu 3): the register budget that keeps
-// two K steps of weight panels per wave in flight without spilling.
-template <bool GATE_UP, bool PK>
-__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3, 3))) void k_gemm_bf16(GemmArgs a) {
-  __shared__ __attribute__((aligned(16))) char As[2 * kTileRows * kRowBytes];
-  __shared__ float rrow[kTileRows];  // gate_up: r of each row's token, or 1
-  const int qx = blockIdx.x & (kQueues - 1), j = blockIdx.x / kQueues;
-  if (j >= a.qlen[qx]) return;
-  gemm_body<GATE_UP, PK, kTileRows>(a, a.tiles[(size_t)qx * a.qmax + j], As, rrow);
-}
-
-// 128-row tiles: twice the accumulators and 64 KB of activation stages, two
-// workgroups per CU.
-template <bool GATE_UP, bool PK>
-__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))) void k_gemm_tall(GemmArgs a) {
-  __shared__ __attribute__((aligned(16))) char As[2 * kTallRows * kRowBytes];
-  __shared__ float rrow[kTallRows];
-  const int qx = blockIdx.x & (kQueues - 1), j = blockIdx.x / kQueues;
-  if (j >= a.qlen[qx]) return;
-  gemm_body<GATE_UP, PK, kTallRows>(a, a.tiles[(size_t)qx * a.qmax + j], As, rrow);
-}
-
-// Both GEMMs in one launch. Queue x (the workgroups b with b % 8 == x, all on
-// XCD x) runs its gate_up tasks, then its down tasks; the balanced deal put
-// every task of an expert's tiles into one queue. A gate_up task, once its
-// gated activations have reached this XCD's L2, counts itself on its tile;
-// a down task starts once its tile's count holds all gate_up blocks. The
-// workgroups of one XCD are dispatched in index order, so every gate_up task
-// a down task waits for is running or done and never waits itself. The wait
-// is bounded (about a tenth of a second): past it the task writes NaN for
-// its outputs instead of its product, so a broken assumption shows in the
-// result and the launch still ends.
-constexpr int kWaitPolls = 1 << 17;
-
-template <bool PK, int ROWS>
-__device__ __forceinline__ void fused_body(const FusedGemmArgs& f, char* As, float* rrow) {
-  __shared__ int ready;
-  const int qx = blockIdx.x & (kQueues - 1), j = blockIdx.x / kQueues;
-  const int ngu = f.gu.qlen[qx];
-  const int tid = threadIdx.x;
-  if (j < ngu) {
-    const Tile tl = f.gu.tiles[(size_t)qx * f.gu.qmax + j];
-    gemm_body<true, PK, ROWS>(f.gu, tl, As, rrow);
-    __builtin_amdgcn_s_waitcnt(0);  // this thread's stores have reached L2
-    __syncthreads();
-    if (tid == 0) atomicAdd(&f.tile_done[tl.row0], 1);
-    return;
-  }
-  const int jd = j - ngu;
-  if (jd >= f.dn.qlen[qx]) return;
-  const Tile tl = f.dn.tiles[(size_t)qx * f.dn.qmax + jd];
-  if (tid == 0) {
-    const int need = f.nb_gate_up;
-    int n = 0;
-    while (atomicAdd(&f.tile_done[tl.row0], 0) < need && n < kWaitPolls) {
-      __builtin_amdgcn_s_sleep(8);
-      ++n;
-    }
-    ready = n < kWaitPolls;
-  }
-  __syncthreads();
-  if (ready) {
-    gemm_body<false, PK, ROWS>(f.dn, tl, As, rrow);
-    return;
-  }
-  const int cols = 32 * kWaves;
-  for (int i = tid; i < tl.mc * cols; i += kThreads)
-    f.dn.y[(size_t)(tl.row0 + i / cols) * f.dn.D + tl.nb * cols + i % cols] = 0x7fc0;  // bf16 NaN
-}
-
+// Both GEMMs in one launch (the task logic of fused_tasks). Three workgroups
+// per CU (waves_per_eu 3): the register budget that keeps two K steps of
+// weight panels per wave in flight without spilling.
 template <bool PK>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3, 3))) void k_gemm_fused(
     FusedGemmArgs f) {
   __shared__ __attribute__((aligned(16))) char As[2 * kTileRows * kRowBytes];
-  __shared__ float rrow[kTileRows];
-  fused_body<PK, kTileRows>(f, As, rrow);
+  __shared__ float rrow[kTileRows];  // gate_up: r of each row's token, or 1
+  fused_tasks(
+      f, [&](const Tile& tl) { gemm_body<true, PK, kTileRows>(f.gu, tl, As, rrow); },
+      [&](const Tile& tl) { gemm_body<false, PK, kTileRows>(f.dn, tl, As, rrow); });
 }
 
+// 128-row tiles: twice the accumulators and 64 KB of activation stages, two
+// workgroups per CU.
 template <bool PK>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))) void k_gemm_fused_tall(
     FusedGemmArgs f) {
   __shared__ __attribute__((aligned(16))) char As[2 * kTallRows * kRowBytes];
   __shared__ float rrow[kTallRows];
-  fused_body<PK, kTallRows>(f, As, rrow);
+  fused_tasks(
+      f, [&](const Tile& tl) { gemm_body<true, PK, kTallRows>(f.gu, tl, As, rrow); },
+      [&](const Tile& tl) { gemm_body<false, PK, kTallRows>(f.dn, tl, As, rrow); });
 }
 
 // One wave per block of 64 lanes x 16 bytes: source block (e, p, s) of 16 rows
@@ -374,36 +314,12 @@ hipError_t launch_pack_panels(const uint16_t* src, uint16_t* dst, int E, int R, 
   return hipGetLastError();
 }
 
-hipError_t launch_gate_up_bf16(const GemmArgs& a, hipStream_t stream, const KernelEvents* ev) {
-  const dim3 grid(kQueues * a.qmax);
-  return launch_kernel(a.w_packed ? k_gemm_bf16<true, true> : k_gemm_bf16<true, false>, grid, dim3(kThreads), stream,
-                       ev, a);
-}
-
-hipError_t launch_down_bf16(const GemmArgs& a, hipStream_t stream, const KernelEvents* ev) {
-  const dim3 grid(kQueues * a.qmax);
-  return launch_kernel(a.w_packed ? k_gemm_bf16<false, true> : k_gemm_bf16<false, false>, grid, dim3(kThreads),
-                       stream, ev, a);
-}
-
-hipError_t launch_gate_up_tall(const GemmArgs& a, hipStream_t stream, const KernelEvents* ev) {
-  const dim3 grid(kQueues * a.qmax);
-  return launch_kernel(a.w_packed ? k_gemm_tall<true, true> : k_gemm_tall<true, false>, grid, dim3(kThreads), stream,
-                       ev, a);
-}
-
 hipError_t launch_gemm_fused(const FusedGemmArgs& f, bool tall, hipStream_t stream, const KernelEvents* ev) {
   const dim3 grid(kQueues * (f.gu.qmax + f.dn.qmax));
   const bool pk = f.gu.w_packed != 0;
   auto k = tall ? (pk ? k_gemm_fused_tall<true> : k_gemm_fused_tall<false>)
                 : (pk ? k_gemm_fused<true> : k_gemm_fused<false>);
   return launch_kernel(k, grid, dim3(kThreads), stream, ev, f);
-}
-
-hipError_t launch_down_tall(const GemmArgs& a, hipStream_t stream, const KernelEvents* ev) {
-  const dim3 grid(kQueues * a.qmax);
-  return launch_kernel(a.w_packed ? k_gemm_tall<false, true> : k_gemm_tall<false, false>, grid, dim3(kThreads),
-                       stream, ev, a);
 }
 
 }  // namespace dg

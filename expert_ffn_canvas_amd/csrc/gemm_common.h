@@ -1,6 +1,7 @@
 // Building blocks shared by the grouped GEMM kernels on gfx950: tile
 // constants, explicit vmcnt waits, the global -> LDS DMA of activation rows
-// with its XOR swizzle, and the LDS-only workgroup barrier.
+// with its XOR swizzle, the LDS-only workgroup barrier, and the task logic of
+// the fused gate_up + down launch.
 #pragma once
 
 #include "dg_common.h"
@@ -82,6 +83,55 @@ __device__ __forceinline__ void lds_barrier() {
   asm volatile("" ::: "memory");
   __builtin_amdgcn_s_barrier();
   asm volatile("" ::: "memory");
+}
+
+// The task logic of a fused launch of both GEMMs (tasks dealt whole expert
+// by whole expert, so a tile's gate_up and down tasks share a queue, hence an
+// XCD). Queue x, the workgroups b with b % 8 == x, runs its gate_up tasks,
+// then its down tasks. A gate_up task, once its gated activations have
+// reached this XCD's L2, counts itself on its tile; a down task starts once
+// its tile's count holds all gate_up blocks. The workgroups of one XCD are
+// dispatched in index order, so every gate_up task that a down task waits for
+// is running or done and never waits itself. The wait is bounded (about a
+// tenth of a second): past it the task writes NaN for its outputs instead of
+// its product, so a broken assumption shows in the result and the launch
+// still ends. gate_up(tile) and down(tile) run one task's product.
+constexpr int kWaitPolls = 1 << 17;
+
+template <typename GateUp, typename Down>
+__device__ __forceinline__ void fused_tasks(const FusedGemmArgs& f, GateUp gate_up, Down down) {
+  __shared__ int ready;
+  const int qx = blockIdx.x & (kQueues - 1), j = blockIdx.x / kQueues;
+  const int ngu = f.gu.qlen[qx];
+  const int tid = threadIdx.x;
+  if (j < ngu) {
+    const Tile tl = f.gu.tiles[(size_t)qx * f.gu.qmax + j];
+    gate_up(tl);
+    __builtin_amdgcn_s_waitcnt(0);  // this thread's stores have reached L2
+    __syncthreads();
+    if (tid == 0) atomicAdd(&f.tile_done[tl.row0], 1);
+    return;
+  }
+  const int jd = j - ngu;
+  if (jd >= f.dn.qlen[qx]) return;
+  const Tile tl = f.dn.tiles[(size_t)qx * f.dn.qmax + jd];
+  if (tid == 0) {
+    const int need = f.nb_gate_up;
+    int n = 0;
+    while (atomicAdd(&f.tile_done[tl.row0], 0) < need && n < kWaitPolls) {
+      __builtin_amdgcn_s_sleep(8);
+      ++n;
+    }
+    ready = n < kWaitPolls;
+  }
+  __syncthreads();
+  if (ready) {
+    down(tl);
+    return;
+  }
+  const int cols = 32 * kWaves;
+  for (int i = tid; i < tl.mc * cols; i += kThreads)
+    f.dn.y[(size_t)(tl.row0 + i / cols) * f.dn.D + tl.nb * cols + i % cols] = 0x7fc0;  // bf16 NaN
 }
 
 }  // namespace gemm

@@ -479,15 +479,10 @@ __device__ __forceinline__ void loop_i4(char* As, const uint16_t* const (&rowp)[
 // int4 weights widened exactly to fp16 in registers. gate_up writes the gated
 // activation as fp16, down its fp32 sums as bf16.
 template <bool GATE_UP>
-__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))) void k_gemm_i4p(GemmArgs a) {
-  __shared__ __attribute__((aligned(16))) char As[kDepthI4 * kStageBytes];
+__device__ __forceinline__ void i4p_body(const GemmArgs& a, const Tile& tl, char* As) {
   const int F = a.F, D = a.D;
   const int K = GATE_UP ? D : F;
   const int G = (K + kKS - 1) / kKS;
-  const int qx = blockIdx.x & (kQueues - 1);
-  const int j = blockIdx.x / kQueues;
-  if (j >= a.qlen[qx]) return;
-  const Tile tl = a.tiles[(size_t)qx * a.qmax + j];
   const int nb = tl.nb;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int g = lane >> 4;
@@ -553,6 +548,14 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
   }
 }
 
+// Both packed GEMMs in one launch (the task logic of fused_tasks).
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))) void k_gemm_i4p_fused(
+    FusedGemmArgs f) {
+  __shared__ __attribute__((aligned(16))) char As[kDepthI4 * kStageBytes];
+  fused_tasks(
+      f, [&](const Tile& tl) { i4p_body<true>(f.gu, tl, As); }, [&](const Tile& tl) { i4p_body<false>(f.dn, tl, As); });
+}
+
 }  // namespace
 
 hipError_t launch_pack_i4(const uint8_t* codes, const uint16_t* scales, uint8_t* pcodes, uint16_t* pscales, int E,
@@ -562,13 +565,15 @@ hipError_t launch_pack_i4(const uint8_t* codes, const uint16_t* scales, uint8_t*
 }
 
 hipError_t launch_gate_up_i4(const GemmArgs& a, hipStream_t stream, const KernelEvents* ev) {
-  if (a.w_packed) return launch_kernel(k_gemm_i4p<true>, dim3(kQueues * a.qmax), dim3(kThreads), stream, ev, a);
   return launch_kernel(k_gate_up_i4, dim3(kQueues * a.qmax), dim3(kThreads), stream, ev, a);
 }
 
 hipError_t launch_down_i4(const GemmArgs& a, hipStream_t stream, const KernelEvents* ev) {
-  if (a.w_packed) return launch_kernel(k_gemm_i4p<false>, dim3(kQueues * a.qmax), dim3(kThreads), stream, ev, a);
   return launch_kernel(k_down_i4, dim3(kQueues * a.qmax), dim3(kThreads), stream, ev, a);
+}
+
+hipError_t launch_gemm_fused_i4(const FusedGemmArgs& f, hipStream_t stream, const KernelEvents* ev) {
+  return launch_kernel(k_gemm_i4p_fused, dim3(kQueues * (f.gu.qmax + f.dn.qmax)), dim3(kThreads), stream, ev, f);
 }
 
 }  // namespace dg

@@ -26,7 +26,7 @@
 //
 // Mapping, activation path and work distribution as in the bf16 kernels (64-row
 // tiles, 4 waves, two 16-row panels per wave, activation rows staged in LDS by
-// DMA, tasks from the per-XCD queues).
+// DMA, both GEMMs in one launch from the per-XCD queues).
 #include "dg_common.h"
 #include "gemm_common.h"
 #include "launch.h"
@@ -190,18 +190,13 @@ __device__ __forceinline__ void qloop(char* As, const uint16_t* const (&rowp)[kD
   }
 }
 
-// gate_up writes the gated activation as fp16 (the down GEMM's fp16 operand),
-// down its fp32 sums as bf16.
+// The product of one task: gate_up writes the gated activation as fp16 (the
+// down GEMM's fp16 operand), down its fp32 sums as bf16.
 template <bool GATE_UP>
-__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))) void k_gemm_q8(GemmArgs a) {
-  __shared__ __attribute__((aligned(16))) char As[2 * kStageBytes];
+__device__ __forceinline__ void q8_body(const GemmArgs& a, const Tile& tl, char* As) {
   const int F = a.F, D = a.D;
   const int K = GATE_UP ? D : F;
   const int nks = (K + kKS - 1) / kKS;
-  const int qx = blockIdx.x & (kQueues - 1);
-  const int j = blockIdx.x / kQueues;
-  if (j >= a.qlen[qx]) return;
-  const Tile tl = a.tiles[(size_t)qx * a.qmax + j];
   const int nb = tl.nb;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int g = lane >> 4;
@@ -272,6 +267,15 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
   }
 }
 
+// Both GEMMs in one launch (the task logic of fused_tasks), two workgroups
+// per CU.
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))) void k_gemm_q8_fused(
+    FusedGemmArgs f) {
+  __shared__ __attribute__((aligned(16))) char As[2 * kStageBytes];
+  fused_tasks(
+      f, [&](const Tile& tl) { q8_body<true>(f.gu, tl, As); }, [&](const Tile& tl) { q8_body<false>(f.dn, tl, As); });
+}
+
 // One wave per packed block (e, s, p); lane l = n + 16 g reads its row's
 // blocks 4 s .. 4 s + 3, 8 codes each.
 __global__ __launch_bounds__(256) void k_pack_q8(const uint8_t* __restrict__ src, uint8_t* __restrict__ pcodes,
@@ -318,12 +322,8 @@ hipError_t launch_pack_q8(const uint8_t* blocks, uint8_t* pcodes, uint16_t* psca
   return hipGetLastError();
 }
 
-hipError_t launch_gate_up_q8(const GemmArgs& a, hipStream_t stream, const KernelEvents* ev) {
-  return launch_kernel(k_gemm_q8<true>, dim3(kQueues * a.qmax), dim3(kThreads), stream, ev, a);
-}
-
-hipError_t launch_down_q8(const GemmArgs& a, hipStream_t stream, const KernelEvents* ev) {
-  return launch_kernel(k_gemm_q8<false>, dim3(kQueues * a.qmax), dim3(kThreads), stream, ev, a);
+hipError_t launch_gemm_fused_q8(const FusedGemmArgs& f, hipStream_t stream, const KernelEvents* ev) {
+  return launch_kernel(k_gemm_q8_fused, dim3(kQueues * (f.gu.qmax + f.dn.qmax)), dim3(kThreads), stream, ev, f);
 }
 
 }  // namespace dg

@@ -130,11 +130,6 @@ struct GemmArgs {
 // by (1 + gamma[k]) and rounded to bf16 (nearest even).
 hipError_t launch_pack_panels(const uint16_t* src, uint16_t* dst, int E, int R, int K, const float* gamma,
                               hipStream_t stream);
-hipError_t launch_gate_up_bf16(const GemmArgs& a, hipStream_t stream, const KernelEvents* ev);
-hipError_t launch_down_bf16(const GemmArgs& a, hipStream_t stream, const KernelEvents* ev);
-// The same products for tiles of up to kTallRows rows (bf16 weights, packed or not).
-hipError_t launch_gate_up_tall(const GemmArgs& a, hipStream_t stream, const KernelEvents* ev);
-hipError_t launch_down_tall(const GemmArgs& a, hipStream_t stream, const KernelEvents* ev);
 // Both bf16 GEMMs in one launch (tasks dealt with kDealBalanced): the gate_up
 // tasks of each queue, then its down tasks, each down task waiting for the
 // gate_up blocks of its tile through tile_done (zeroed by the permutation).
@@ -150,8 +145,11 @@ hipError_t launch_gemm_fused(const FusedGemmArgs& f, bool tall, hipStream_t stre
 // code 8 (zero).
 hipError_t launch_pack_i4(const uint8_t* codes, const uint16_t* scales, uint8_t* pcodes, uint16_t* pscales, int E,
                           int R, int K, hipStream_t stream);
+// The two int4 products on the caller's row-major layout (borrow mode).
 hipError_t launch_gate_up_i4(const GemmArgs& a, hipStream_t stream, const KernelEvents* ev);
 hipError_t launch_down_i4(const GemmArgs& a, hipStream_t stream, const KernelEvents* ev);
+// Both products with packed int4 weights in one launch, as launch_gemm_fused.
+hipError_t launch_gemm_fused_i4(const FusedGemmArgs& f, hipStream_t stream, const KernelEvents* ev);
 // Create-time relayout of Q8_0 expert weights (rows of K / 32 blocks of 34
 // bytes: fp16 scale, 32 int8 codes) into fragment order: per (expert, 128-input
 // step, 16-row panel), 2 KB of codes (lane n + 16 g: 32 bytes of row n, 8 per
@@ -159,9 +157,9 @@ hipError_t launch_down_i4(const GemmArgs& a, hipStream_t stream, const KernelEve
 // scales [row][block]; a short last step is padded with zero codes and scales.
 hipError_t launch_pack_q8(const uint8_t* blocks, uint8_t* pcodes, uint16_t* pscales, int E, int R, int K,
                           hipStream_t stream);
-// The products with packed Q8_0 weights (fp16 expert input and activation).
-hipError_t launch_gate_up_q8(const GemmArgs& a, hipStream_t stream, const KernelEvents* ev);
-hipError_t launch_down_q8(const GemmArgs& a, hipStream_t stream, const KernelEvents* ev);
+// Both products with packed Q8_0 weights (fp16 expert input and activation)
+// in one launch, as launch_gemm_fused.
+hipError_t launch_gemm_fused_q8(const FusedGemmArgs& f, hipStream_t stream, const KernelEvents* ev);
 
 struct CombineArgs {
   const uint16_t* y;           // [K T, D] bf16 expert outputs, expert-sorted rows

@@ -188,9 +188,9 @@ class MoELayer:
         # bf16 activations with packed bf16 experts: the expert norm rides on the gate_up weight and r, and the
         # forward runs no norm kernel (its two profiling events are then recorded back to back)
         self.expert_norm_folded = bool(pack and not i4 and not q8 and act_dtype == torch.bfloat16)
-        # bf16 experts: both GEMMs run in one launch (its profiling events are the gate_up pair; the down pair is
-        # recorded back to back after it)
-        self.gemms_fused = not i4 and not q8
+        # both GEMMs run in one launch, except for int4 experts read in place (the fused launch's profiling
+        # events are the gate_up pair; the down pair is recorded back to back after it)
+        self.gemms_fused = bool(pack or not i4)
 
     def forward(self, x, out=None, addend=None, add_input=False):
         import torch

@@ -166,10 +166,10 @@ dg_status dg_moe_forward_debug(dg_moe_handle h, const void* x, void* out, int32_
  * hipEventElapsedTime(events[2 i], events[2 i + 1]) is that kernel's own
  * duration. Where the expert norm is folded into the packed gate_up weight
  * (DG_MOE_PACK_WEIGHTS, bf16 experts and activations) no norm kernel runs and
- * events 0 and 1 are recorded back to back. With bf16 experts one launch runs
- * both GEMMs: events 6 and 7 time it, and events 8 and 9 are recorded back to
- * back after it. T must be > 0; every event must be non-NULL (else
- * DG_ERR_INVALID_ARG, nothing launched). */
+ * events 0 and 1 are recorded back to back. One launch runs both GEMMs
+ * (except for int4 experts in borrow mode): events 6 and 7 time it, and events
+ * 8 and 9 are recorded back to back after it. T must be > 0; every event must
+ * be non-NULL (else DG_ERR_INVALID_ARG, nothing launched). */
 dg_status dg_moe_forward_profiled(dg_moe_handle h, const void* x, void* out, int32_t T, const void* addend,
                                   uint32_t flags, void* const* events, void* stream);
 
