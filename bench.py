@@ -27,7 +27,7 @@ METRIC = "MoE-layer tokens/s per canvas step (T=256, bf16) + % of HBM/MFMA roofl
 HBM_PEAK_GBPS = 8000.0         # MI355X HBM3E
 BF16_PEAK_TFLOPS = 2500.0      # MI355X dense bf16 MFMA
 F16_PEAK_TFLOPS = 2500.0
-COUNTERS_FILE = os.path.join(ROOT, "profiles", "gate_up_counters.txt")
+COUNTERS_FILE = os.path.join(ROOT, "profiles", "gemm_fused_counters.txt")
 KERNEL_NAMES = ("norm", "logits_topk", "permute", "gate_up", "down", "combine")
 
 
