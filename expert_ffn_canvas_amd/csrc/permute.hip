@@ -18,9 +18,9 @@
 //    to within one unit. With tall tiles the deal is by expert instead (all
 //    column blocks of rank r go to queue r % 8): an expert's tiles then share
 //    its activation rows, hundreds of them, in one L2. For the fused GEMM
-//    whole experts are dealt so that the queues' tile counts balance, the
-//    same expert to the same queue in both task lists, and the per-tile
-//    counters of that GEMM are zeroed;
+//    whole experts are dealt in id order so that the queues' tile counts
+//    balance, the same expert to the same queue in both task lists, and the
+//    per-tile counters of that GEMM are zeroed;
 //  * the stable scatter: the rows of expert e hold its slots in increasing
 //    token order; sorted_slot[row] = t k + j (token t, slot j) and
 //    row_of_slot[t k + j] = row.
@@ -78,44 +78,63 @@ __device__ __forceinline__ void load_ids(const int32_t* idx, int t, int K, int (
   }
 }
 
-// Balanced deal of whole experts, all threads at once: qof[r] = queue of
-// expert rank r. Ranks come in non-increasing tile count; v1 is the smallest
-// nonzero count. The ranks with more than v1 tiles are dealt in snake order
-// (queues 0..7, then 7..0, ...); then the ranks of v1 tiles fill the least
-// loaded queues level by level: with queue q at level Lq = (tiles so far) / v1,
-// the i-th of them takes the i-th smallest pair (Lq + k, q), k = 0, 1, ...,
-// found by a binary search on the level. Deterministic, so both task lists
-// agree. Called by every thread of the block.
-__device__ void deal_balanced(const int* ntile, const int* order, int E, int tid, int* qof, int* shq) {
-  int* load = shq;       // [kQueues] tiles per queue after the snake part
-  int* v1s = shq + kQueues;
-  const int r = tid;
-  const int v = (r < E) ? ntile[order[r]] : 0;
+// Balanced deal of whole experts, in expert id order: qof[e] = queue of
+// expert e. v1 is the smallest nonzero tile count. The experts with more
+// tiles are dealt in snake order (queues 0..7, then 7..0, ...); then the
+// experts of v1 tiles fill the least loaded queues level by level: with queue
+// q at level Lq = (tiles so far) / v1, the i-th of them takes the i-th
+// smallest pair (Lq + k, q), k = 0, 1, ..., found by a binary search on the
+// level, so consecutive ones go to different queues. Deterministic, so both
+// task lists agree. Called by every thread of the block; expert e is thread e.
+__device__ void deal_balanced(const int* ntile, int E, int tid, int lane, int wave, int* qof, int* sh) {
+  int* load = sh;       // [kQueues] tiles of the larger experts per queue
+  int* wmin = sh + 8;   // [4] per wave: smallest nonzero count
+  int* hcnt = sh + 12;  // [4] per wave: larger experts
+  int* tcnt = sh + 16;  // [4] per wave: experts of v1 tiles
+  const int e = tid;
+  const bool mine = wave < kMaxE / 64;
+  const int v = (e < E) ? ntile[e] : 0;
   if (tid < kQueues) load[tid] = 0;
-  const int nz = __syncthreads_count(r < E && v > 0);
-  if (nz == 0) return;
-  if (r == nz - 1) *v1s = v;
+  if (mine) {
+    int m = v > 0 ? v : 0x7fffffff;
+    for (int d = 32; d >= 1; d >>= 1) m = min(m, __shfl_xor(m, d));
+    if (lane == 0) wmin[wave] = m;
+  }
   __syncthreads();
-  const int v1 = *v1s;
-  const bool heavy = r < nz && v > v1;
-  const int nh = __syncthreads_count(heavy);
+  const int v1 = min(min(wmin[0], wmin[1]), min(wmin[2], wmin[3]));
+  if (v1 == 0x7fffffff) return;  // no expert has rows
+  const bool heavy = mine && v > v1, tail = mine && v == v1;
+  const uint64_t below = (1ull << lane) - 1ull;
+  uint64_t hb = 0, tb = 0;
+  if (mine) {
+    hb = __ballot(heavy);
+    tb = __ballot(tail);
+    if (lane == 0) {
+      hcnt[wave] = __popcll(hb);
+      tcnt[wave] = __popcll(tb);
+    }
+  }
+  __syncthreads();
+  int hbase = 0, tbase = 0;
+  for (int w = 0; w < kMaxE / 64; ++w) {
+    hbase += (w < wave) ? hcnt[w] : 0;
+    tbase += (w < wave) ? tcnt[w] : 0;
+  }
   if (heavy) {
-    const int q = ((r / kQueues) & 1) ? kQueues - 1 - r % kQueues : r % kQueues;
-    qof[r] = q;
+    const int h = hbase + __popcll(hb & below);
+    const int q = ((h / kQueues) & 1) ? kQueues - 1 - h % kQueues : h % kQueues;
+    qof[e] = q;
     atomicAdd(&load[q], v);
   }
   __syncthreads();
-  if (tid < kQueues) load[tid] /= v1;
-  __syncthreads();
-  if (r >= nh && r < nz) {
-    int lv[kQueues];
-    int lmin = 0x7fffffff;
+  if (tail) {
+    const int i = tbase + __popcll(tb & below);
+    int lv[kQueues], lmin = 0x7fffffff;
 #pragma unroll
     for (int q = 0; q < kQueues; ++q) {
-      lv[q] = load[q];
+      lv[q] = div_small(load[q], v1);
       lmin = min(lmin, lv[q]);
     }
-    const int i = r - nh;
     // the largest level lam with C(lam) <= i, C(lam) = sum_q max(0, lam - Lq)
     int lo = lmin, hi = lmin + i;
     while (lo < hi) {
@@ -136,7 +155,7 @@ __device__ void deal_balanced(const int* ntile, const int* order, int E, int tid
         --j;
       }
     }
-    qof[r] = pick;
+    qof[e] = pick;
   }
 }
 
@@ -207,8 +226,8 @@ __global__ __launch_bounds__(kThreads) void k_permute(PermuteArgs a) {
   __shared__ int base[kMaxE];
   __shared__ int cursor[kMaxE];
   __shared__ int order[kMaxE];
-  __shared__ int qof[kMaxE];  // kDealBalanced: queue of each expert rank
-  __shared__ int dshare[kQueues + 1];
+  __shared__ int qof[kMaxE];  // kDealBalanced: queue of each expert (rank = id)
+  __shared__ int dshare[32];  // kDealBalanced: queue loads and per-wave counts
   __shared__ int ntile[kMaxE];
   __shared__ int wsum[kMaxE / 64];
   __shared__ int pq[1][kMaxE + 1];            // this queue: load of the ranks before r
@@ -275,8 +294,11 @@ __global__ __launch_bounds__(kThreads) void k_permute(PermuteArgs a) {
   }
   // --- rank of expert e by (count desc, id asc): four lanes per expert; lane
   // q reads the counts 16 i + 4 q .. + 3 (consecutive lanes, consecutive
-  // banks) and compares against them
-  {
+  // banks) and compares against them. The balanced deal needs no size order:
+  // it deals in expert id order (rank = id).
+  if (a.deal == kDealBalanced) {
+    if (tid < kMaxE) order[tid] = tid;
+  } else {
     const int e = tid >> 2, q = tid & 3;
     const int ce = (e < E) ? cnt[e] : 0;
     int r = 0;
@@ -298,7 +320,7 @@ __global__ __launch_bounds__(kThreads) void k_permute(PermuteArgs a) {
   if (a.deal == kDealBalanced) {
     if (tid < kMaxE) qof[tid] = 0;
     __syncthreads();
-    deal_balanced(ntile, order, E, tid, qof, dshare);
+    deal_balanced(ntile, E, tid, lane, wave, qof, dshare);
   }
   __syncthreads();
 
