@@ -12,6 +12,7 @@ the canvas, two canvases, 30 MoE layers):
   encode2304 T=2304, all bf16, no router bias
   int4       T=256,  bf16 activations, int4-g128 experts (zero point 8)
   q8         T=256,  bf16 activations, Q8_0 experts (blocks of 32, fp16 scale)
+  mxfp4      T=256,  bf16 activations, MXFP4 experts (blocks of 32 E2M1 codes, E8M0 scale)
   stack30    T=512,  30 layers with their own bf16 weights, Zipf skew,
              a N(0, 0.5) offset [T, D] added after each layer
 
@@ -46,7 +47,7 @@ class Workload:
     T: int
     act: str            # "f32" | "bf16"
     router_w: str       # "f32" | "bf16"
-    experts: str        # "bf16" | "i4g128" | "q8_0"
+    experts: str        # "bf16" | "i4g128" | "q8_0" | "mxfp4"
     bias: str | None    # None | "zipf"
     seed: int
     layers: int = 1
@@ -64,6 +65,7 @@ WORKLOADS = {
     "encode2304": Workload("encode2304", 2304, "bf16", "bf16", "bf16", None, 2),
     "int4": Workload("int4", 256, "bf16", "bf16", "i4g128", None, 3),
     "q8": Workload("q8", 256, "bf16", "bf16", "q8_0", None, 5),
+    "mxfp4": Workload("mxfp4", 256, "bf16", "bf16", "mxfp4", None, 6),
     "stack30": Workload("stack30", 512, "bf16", "bf16", "bf16", "zipf", 4, layers=30, delta_std=0.5),
 }
 
@@ -123,6 +125,36 @@ def quantize_q8_0(w: torch.Tensor) -> torch.Tensor:
     return torch.cat([d16, q.view(torch.uint8)], dim=-1).contiguous()
 
 
+E2M1_GRID = (0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0)  # magnitudes of E2M1 codes 0..7 (OCP Microscaling)
+
+
+def quantize_mxfp4(w: torch.Tensor) -> torch.Tensor:
+    """MXFP4 blocks of 32 consecutive inputs along the last dim (K % 32 == 0), the
+    OCP Microscaling conversion: shared exponent X = floor(log2(amax)) - 2 (the
+    largest E2M1 power is 2^2), clamped to [-127, 127] (-127 for an all-zero
+    block); each input the E2M1 code nearest to w / 2^X, ties to the even code,
+    magnitudes above 6 saturating. Returns uint8 [..., K/32, 17]: per block the
+    E8M0 byte X + 127, then 16 bytes holding input j in the low nibble of byte j
+    (j < 16) or the high nibble of byte j - 16.
+    """
+    K = w.shape[-1]
+    assert K % 32 == 0
+    wb = w.reshape(*w.shape[:-1], K // 32, 32).to(torch.float32)
+    amax = wb.abs().amax(dim=-1)
+    _, ex = torch.frexp(amax)  # amax = m 2^ex with m in [0.5, 1): floor(log2(amax)) = ex - 1
+    X = torch.where(amax > 0, ex.to(torch.float32) - 1 - 2, torch.full_like(amax, -127.0)).clamp(-127, 127)
+    v = wb / torch.exp2(X).unsqueeze(-1)
+    grid = torch.tensor(E2M1_GRID, dtype=torch.float32, device=w.device)
+    dist = (v.abs().clamp(max=6.0).unsqueeze(-1) - grid).abs()
+    best = dist.min(dim=-1, keepdim=True).values
+    even = (torch.arange(8, device=w.device) % 2 == 0).to(torch.float32)
+    idx = ((dist == best).to(torch.float32) * (1.0 + even)).argmax(dim=-1)  # ties -> the even code
+    code = (idx | torch.where((v < 0) & (idx > 0), 8, 0)).to(torch.uint8)
+    packed = code[..., :16] | (code[..., 16:] << 4)
+    e8 = (X + 127).to(torch.uint8).unsqueeze(-1)
+    return torch.cat([e8, packed], dim=-1).contiguous()
+
+
 def make_layer_weights(wl: Workload, gen: torch.Generator, device) -> dict:
     """Weights of one layer, drawn in the fixed order (router W, gammas, gate_up, down)."""
     E, D, F = wl.E, wl.D, wl.F
@@ -150,6 +182,10 @@ def make_layer_weights(wl: Workload, gen: torch.Generator, device) -> dict:
         w["q8_gate_up"] = quantize_q8_0(gu)
         del gu
         w["q8_down"] = quantize_q8_0(_randn((E, D, F), 0.02, gen, device))
+    elif wl.experts == "mxfp4":
+        w["mx4_gate_up"] = quantize_mxfp4(gu)
+        del gu
+        w["mx4_down"] = quantize_mxfp4(_randn((E, D, F), 0.02, gen, device))
     else:
         w["w_gate_up"] = gu.to(torch.bfloat16)
         del gu

@@ -25,6 +25,15 @@
 //    pages do not spell the format out, so it is read as the public ggml
 //    block of 32 consecutive inputs: an fp16 scale d followed by 32 int8
 //    codes q, standing for q * d.
+//  * MXFP4 weights: the FP4 builds the same card compares (its finding that
+//    4-bit loses on gfx1151 turns on FP4 having no hardware path there). The
+//    pages do not define the format; it is read as the OCP Microscaling MXFP4
+//    format: blocks of 32 consecutive inputs sharing an E8M0 scale 2^(e-127)
+//    (e = 255: NaN), each input an E2M1 code (sign bit, two exponent bits with
+//    bias 1, one mantissa bit), stored per block as the scale byte and then 16
+//    code bytes, input j of the block in the low nibble of byte j for j < 16
+//    and in the high nibble of byte j - 16 for j >= 16 (the GGUF block
+//    arrangement).
 //
 // Readings where the pages are silent (each one is listed with its reason in
 // the design notes): router norm = the same (1+gamma) RMSNorm form as the
@@ -54,7 +63,18 @@
 
 namespace {
 
-enum { OR_F32 = 0, OR_BF16 = 1, OR_F16 = 2, OR_I4G128 = 3, OR_Q8_0 = 4 };
+enum { OR_F32 = 0, OR_BF16 = 1, OR_F16 = 2, OR_I4G128 = 3, OR_Q8_0 = 4, OR_MXFP4 = 5 };
+
+// E2M1 code (4 bits) -> value: exponent field 0 is subnormal (0 or 0.5),
+// otherwise 2^(exponent - 1) (1 + mantissa / 2); bit 3 is the sign.
+inline float e2m1_value(int code) {
+  const int ex = (code >> 1) & 3, m = code & 1;
+  const float mag = ex == 0 ? 0.5f * static_cast<float>(m) : std::ldexp(1.0f + 0.5f * static_cast<float>(m), ex - 1);
+  return (code & 8) ? -mag : mag;
+}
+
+// E8M0 scale byte -> 2^(e - 127); 255 encodes NaN.
+inline float e8m0_value(int e) { return e == 255 ? NAN : std::ldexp(1.0f, e - 127); }
 
 // bf16 -> fp32: a bf16 value is the upper 16 bits of an fp32 value.
 inline float bf16_bits_to_float(uint16_t b) {
@@ -113,6 +133,7 @@ inline float load_elem(const void* p, int dtype, size_t i) {
 // nibble of byte k/2 when k is even and in the high nibble when k is odd;
 // scales fp16 [rows, ceil(K/128)]. Q8_0: K/32 blocks of 34 bytes per row,
 // block b = (fp16 scale d, little endian; int8 codes of inputs 32 b .. 32 b + 31).
+// MXFP4: K/32 blocks of 17 bytes per row (E8M0 scale byte, 16 code bytes).
 struct WeightView {
   int dtype;
   const void* data;
@@ -127,6 +148,13 @@ struct WeightView {
       const uint16_t d = static_cast<uint16_t>(blk[0] | (blk[1] << 8));
       const int q = static_cast<int8_t>(blk[2 + k % 32]);
       return static_cast<float>(q) * half_bits_to_float(d);  // exact in fp32
+    }
+    if (dtype == OR_MXFP4) {
+      const uint8_t* blk = static_cast<const uint8_t*>(data) + (row * static_cast<size_t>(K / 32) + k / 32) * 17;
+      const int j = k % 32;
+      const uint8_t byte = blk[1 + (j & 15)];
+      const int code = j < 16 ? (byte & 0x0f) : (byte >> 4);
+      return e2m1_value(code) * e8m0_value(blk[0]);  // exact in fp32 (two significant bits times a power of two)
     }
     const size_t row_bytes = (static_cast<size_t>(K) + 1) / 2;
     const uint8_t byte = static_cast<const uint8_t*>(data)[row * row_bytes + k / 2];
@@ -263,6 +291,13 @@ void oracle_dequant_i4(const uint8_t* q, const uint16_t* s, int64_t rows, int K,
     for (int k = 0; k < K; ++k) out[r * K + k] = v.at(static_cast<size_t>(r), k);
 }
 
+// MXFP4 blocks [rows, K/32, 17 bytes] -> fp32 [rows, K].
+void oracle_dequant_mxfp4(const uint8_t* blocks, int64_t rows, int K, float* out) {
+  WeightView v{OR_MXFP4, blocks, nullptr, K};
+  for (int64_t r = 0; r < rows; ++r)
+    for (int k = 0; k < K; ++k) out[r * K + k] = v.at(static_cast<size_t>(r), k);
+}
+
 // Q8_0 blocks [rows, K/32, 34 bytes] -> fp32 [rows, K].
 void oracle_dequant_q8_0(const uint8_t* blocks, int64_t rows, int K, float* out) {
   WeightView v{OR_Q8_0, blocks, nullptr, K};
@@ -325,7 +360,7 @@ int oracle_permute(int T, int K, int E, const int32_t* idx, int32_t* counts, int
 //   then, if add_input, out += fp32(x); if addend, out += fp32(addend).
 // out32 [n_tok, D] fp32 (before any output rounding). idx/w/gap per computed
 // token (nullable). dtypes: x/addend 0=f32 1=bf16; router_w 0=f32 1=bf16;
-// expert weights 1=bf16 3=int4-g128 4=Q8_0. Returns 0 or -1 on a bad argument.
+// expert weights 1=bf16 3=int4-g128 4=Q8_0 5=MXFP4. Returns 0 or -1 on a bad argument.
 int oracle_moe_forward(int T, int D, int F, int E, int K, double eps, int x_dtype, const void* x,
                        int rw_dtype, const void* router_w, const float* router_gamma,
                        const float* router_bias, const float* ffn_gamma, int ew_dtype,
@@ -334,9 +369,9 @@ int oracle_moe_forward(int T, int D, int F, int E, int K, double eps, int x_dtyp
                        int n_tok, int add_input, const void* addend, float* out32, int32_t* idx_out,
                        double* w_out, double* gap_out, int n_threads) {
   if (T < 0 || D <= 0 || F <= 0 || E <= 0 || K <= 0 || K > E) return -1;
-  if (ew_dtype != OR_BF16 && ew_dtype != OR_I4G128 && ew_dtype != OR_Q8_0) return -1;
+  if (ew_dtype != OR_BF16 && ew_dtype != OR_I4G128 && ew_dtype != OR_Q8_0 && ew_dtype != OR_MXFP4) return -1;
   if (ew_dtype == OR_I4G128 && (!s_gate_up || !s_down)) return -1;
-  if (ew_dtype == OR_Q8_0 && (D % 32 || F % 32)) return -1;
+  if ((ew_dtype == OR_Q8_0 || ew_dtype == OR_MXFP4) && (D % 32 || F % 32)) return -1;
   Layer L{T, D, F, E, K, eps, x_dtype, x, rw_dtype, router_w, router_gamma, router_bias, ffn_gamma,
           ew_dtype, w_gate_up, w_down, s_gate_up, s_down};
   const int n = tokens ? n_tok : T;

@@ -435,6 +435,79 @@ def test_q8_0_layer_matches_dense_reference_of_dequantised_weights():
     assert rel_err(o["out"], ref.numpy()) <= 2e-5
 
 
+# E2M1 values of codes 0..15 as the OCP Microscaling specification tabulates them (sign bit 3; exponent
+# bits 2..1 with bias 1, code 0b001 the subnormal 0.5; mantissa bit 0).
+E2M1_SPEC = [0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0, -0.0, -0.5, -1.0, -1.5, -2.0, -3.0, -4.0, -6.0]
+
+
+def test_mxfp4_codes_scales_and_layout():
+    # One block with scale byte 127 (2^0): inputs 0..15 carry codes 0..15 in the low nibbles, inputs
+    # 16..31 carry codes 15..0 in the high nibbles of the same 16 bytes.
+    lo = np.arange(16, dtype=np.uint8)
+    hi = lo[::-1]
+    blk = np.concatenate([[127], lo | (hi << 4)]).astype(np.uint8)
+    deq = oracle.dequant_mxfp4(blk.reshape(1, 17), 32)[0]
+    spec = np.array(E2M1_SPEC, dtype=np.float32)
+    assert np.array_equal(deq[:16], spec) and np.array_equal(deq[16:], spec[::-1])
+    assert np.array_equal(np.signbit(deq[:16]), np.signbit(spec))
+    # E8M0: byte e scales by 2^(e - 127), down to 2^-127 (an fp32 subnormal); 255 is NaN.
+    for e, scale in [(128, 2.0), (126, 0.5), (120, 2.0 ** -7), (0, 2.0 ** -127), (200, 2.0 ** 73)]:
+        b = blk.copy()
+        b[0] = e
+        d = oracle.dequant_mxfp4(b.reshape(1, 17), 32)[0]
+        assert np.array_equal(d, (spec.astype(np.float64) * scale).astype(np.float32)[np.r_[0:16, 15:-1:-1]]), e
+    b = blk.copy()
+    b[0] = 255
+    assert np.all(np.isnan(oracle.dequant_mxfp4(b.reshape(1, 17), 32)))
+    # Two blocks per row: block b covers inputs 32 b .. 32 b + 31 of its row.
+    two = np.zeros((1, 2, 17), dtype=np.uint8)
+    two[0, 0, 0], two[0, 1, 0] = 127, 129  # 1 and 4
+    two[0, :, 1:] = 0x72  # inputs j < 16: code 2 (1.0); j >= 16: code 7 (6.0)
+    d2 = oracle.dequant_mxfp4(two.reshape(1, 34), 64)[0]
+    assert np.array_equal(d2, np.array([1.0] * 16 + [6.0] * 16 + [4.0] * 16 + [24.0] * 16, dtype=np.float32))
+
+
+def test_mxfp4_quantiser_roundtrip():
+    gen = torch.Generator().manual_seed(12)
+    w = torch.randn((5, 2816), generator=gen) * 0.02
+    w[2, 32:64] = 0.0  # an all-zero block
+    w[3, 0:32] = torch.tensor([6.0, -2.5, 1.25, 0.25] + [0.0] * 28)  # ties at scale 1 (amax 6 -> X = 0)
+    b = synth.quantize_mxfp4(w)
+    assert b.shape == (5, 88, 17) and b.dtype == torch.uint8
+    deq = oracle.dequant_mxfp4(b.numpy().reshape(5, -1), 2816)
+    wn = w.numpy()
+    amax = np.abs(wn.reshape(5, 88, 32)).max(-1)
+    X = np.where(amax > 0, np.floor(np.log2(np.where(amax > 0, amax, 1.0))) - 2, -127)
+    scale = np.repeat(2.0 ** X, 32, axis=1)
+    # the block's largest magnitude lands in [4, 8) scale units; rounding is within half a grid gap
+    # (a quarter of the value, or a quarter of the scale near zero), saturation above 6 within 2 units
+    err = np.abs(deq - wn)
+    assert np.all(err <= np.maximum(0.25 * scale, 0.25 * np.abs(wn)) + 1e-12)
+    assert np.all(deq[2, 32:64] == 0.0) and b[2, 1, 0].item() == 0
+    # ties go to the even code: 2.5 -> 2, 1.25 -> 1, 0.25 -> 0; 6 stays 6
+    assert b[3, 0, 0].item() == 127
+    assert np.array_equal(deq[3, :4], np.array([6.0, -2.0, 1.0, 0.0], dtype=np.float32))
+    # the scale uses the largest power of two that keeps every block's maximum within E2M1 range
+    top = np.abs(deq.reshape(5, 88, 32)).max(-1)
+    nz = amax > 0
+    assert np.all(top[nz] >= 4 * (2.0 ** X[nz]) - 1e-30)
+
+
+def test_mxfp4_layer_matches_dense_reference_of_dequantised_weights():
+    wl, x, w = small(T=12, E=6, K=2, D=256, F=192, seed=33, experts="mxfp4")
+    xn, wn = np_inputs(x, w)
+    o = oracle.moe_forward(wn, xn, 2, EPS)
+    wf = f64_weights({k: v for k, v in wn.items() if k in ("router_w", "router_gamma", "ffn_gamma")})
+    wf["router_bias"] = None
+    E, D, Fd = 6, 256, 192
+    gu = oracle.dequant_mxfp4(wn["mx4_gate_up"].reshape(E * 2 * Fd, -1), D)
+    dn = oracle.dequant_mxfp4(wn["mx4_down"].reshape(E * D, -1), Fd)
+    wf["w_gate_up"] = torch.from_numpy(gu.reshape(E, 2 * Fd, D)).double()
+    wf["w_down"] = torch.from_numpy(dn.reshape(E, D, Fd)).double()
+    ref, _, _ = dense_moe_fp64(bits_to_f64(xn), wf, 2, EPS)
+    assert rel_err(o["out"], ref.numpy()) <= 2e-5
+
+
 # ----------------------------------------------------------------------------- shapes printed on the pages
 
 def test_shapes_from_the_pages():
