@@ -126,11 +126,12 @@ dg_status check_config(const dg_moe_config* c) {
     return fail(DG_ERR_DTYPE, "act_dtype %d: only DG_F32 or DG_BF16", c->act_dtype);
   if (c->router_w_dtype != DG_F32 && c->router_w_dtype != DG_BF16)
     return fail(DG_ERR_DTYPE, "router_w_dtype %d: only DG_F32 or DG_BF16", c->router_w_dtype);
-  if (c->expert_w_dtype != DG_BF16 && c->expert_w_dtype != DG_I4G128 && c->expert_w_dtype != DG_Q8_0)
-    return fail(DG_ERR_DTYPE, "expert_w_dtype %d: only DG_BF16, DG_I4G128 or DG_Q8_0", c->expert_w_dtype);
+  if (c->expert_w_dtype != DG_BF16 && c->expert_w_dtype != DG_I4G128 && c->expert_w_dtype != DG_Q8_0 &&
+      c->expert_w_dtype != DG_MXFP4)
+    return fail(DG_ERR_DTYPE, "expert_w_dtype %d: only DG_BF16, DG_I4G128, DG_Q8_0 or DG_MXFP4", c->expert_w_dtype);
   if (c->flags & ~DG_MOE_PACK_WEIGHTS) return fail(DG_ERR_INVALID_ARG, "unknown config flags 0x%x", c->flags);
-  if (c->expert_w_dtype == DG_Q8_0 && !(c->flags & DG_MOE_PACK_WEIGHTS))
-    return fail(DG_ERR_DTYPE, "DG_Q8_0 experts are read from the packed copy only: set DG_MOE_PACK_WEIGHTS");
+  if ((c->expert_w_dtype == DG_Q8_0 || c->expert_w_dtype == DG_MXFP4) && !(c->flags & DG_MOE_PACK_WEIGHTS))
+    return fail(DG_ERR_DTYPE, "DG_Q8_0 and DG_MXFP4 experts are read from the packed copy only: set DG_MOE_PACK_WEIGHTS");
   return DG_OK;
 }
 
@@ -171,6 +172,12 @@ ExpertBytes expert_bytes(const dg_moe_config& c) {
     b.dn = E * D * nks_f * 128;
     b.sgu = E * 2 * F * nks_d * 4 * 2;
     b.sdn = E * D * nks_f * 4 * 2;
+  } else if (c.expert_w_dtype == DG_MXFP4) {  // packed only: 64 code bytes and 4 scale bytes per (row, step)
+    const size_t nks_d = (D + 127) / 128, nks_f = (F + 127) / 128;
+    b.gu = E * 2 * F * nks_d * 64;
+    b.dn = E * D * nks_f * 64;
+    b.sgu = E * 2 * F * nks_d * 4;
+    b.sdn = E * D * nks_f * 4;
   } else {
     b.gu = E * 2 * F * (D / 2);
     b.dn = E * D * (F / 2);
@@ -218,6 +225,7 @@ dg_status dg_moe_create(const dg_moe_config* cfg, const dg_moe_weights* w, void*
   if (!w || !out) return fail(DG_ERR_INVALID_ARG, "weights or out is NULL");
   const bool i4 = cfg->expert_w_dtype == DG_I4G128;
   const bool q8 = cfg->expert_w_dtype == DG_Q8_0;
+  const bool mx4 = cfg->expert_w_dtype == DG_MXFP4;
   if (!w->router_w || !w->router_gamma || !w->ffn_gamma || !w->w_gate_up || !w->w_down)
     return fail(DG_ERR_INVALID_ARG, "a required weight pointer is NULL");
   if (i4 && (!w->s_gate_up || !w->s_down)) return fail(DG_ERR_INVALID_ARG, "int4 weights need both scale tensors");
@@ -266,14 +274,24 @@ dg_status dg_moe_create(const dg_moe_config* cfg, const dg_moe_weights* w, void*
     char* p = static_cast<char*>(hd->packed);
     hd->w_gate_up = p;
     hd->w_down = p + round_up(eb.gu, 256);
-    const bool scaled = i4 || q8;
+    const bool scaled = i4 || q8 || mx4;
     hd->s_gate_up =
         scaled ? reinterpret_cast<const uint16_t*>(p + round_up(eb.gu, 256) + round_up(eb.dn, 256)) : nullptr;
     hd->s_down = scaled ? reinterpret_cast<const uint16_t*>(p + round_up(eb.gu, 256) + round_up(eb.dn, 256) +
                                                             round_up(eb.sgu, 256))
                         : nullptr;
     hipError_t c1, c2, c3 = hipSuccess, c4 = hipSuccess;
-    if (q8) {  // Q8_0: codes and scales in fragment order, per 128-input step
+    if (mx4) {  // MXFP4: codes and scale bytes in fragment order, per 128-input step
+      c1 = dg::launch_pack_mx4(static_cast<const uint8_t*>(w->w_gate_up),
+                               static_cast<uint8_t*>(const_cast<void*>(hd->w_gate_up)),
+                               reinterpret_cast<uint8_t*>(const_cast<uint16_t*>(hd->s_gate_up)), cfg->n_experts,
+                               2 * cfg->d_ff, cfg->d_model, stream);
+      c2 = dg::launch_pack_mx4(static_cast<const uint8_t*>(w->w_down),
+                               static_cast<uint8_t*>(const_cast<void*>(hd->w_down)),
+                               reinterpret_cast<uint8_t*>(const_cast<uint16_t*>(hd->s_down)), cfg->n_experts,
+                               cfg->d_model, cfg->d_ff, stream);
+      hd->w_packed = 1;
+    } else if (q8) {  // Q8_0: codes and scales in fragment order, per 128-input step
       c1 = dg::launch_pack_q8(static_cast<const uint8_t*>(w->w_gate_up),
                               static_cast<uint8_t*>(const_cast<void*>(hd->w_gate_up)),
                               const_cast<uint16_t*>(hd->s_gate_up), cfg->n_experts, 2 * cfg->d_ff, cfg->d_model,
@@ -361,6 +379,7 @@ static dg_status run_forward(dg_moe_handle hd, const void* x, void* out, int32_t
   const Layout& L = hd->L;
   const bool i4 = c.expert_w_dtype == DG_I4G128;
   const bool q8 = c.expert_w_dtype == DG_Q8_0;
+  const bool mx4 = c.expert_w_dtype == DG_MXFP4;
   // per-kernel start/stop events: norm, logits, permute, gate_up, down, combine
   dg::KernelEvents kev[6];
   if (events)
@@ -382,7 +401,7 @@ static dg_status run_forward(dg_moe_handle hd, const void* x, void* out, int32_t
   ra.bias = hd->has_bias ? hd->at<float>(L.bias) : nullptr;
   ra.gamma_e = hd->at<float>(L.gamma_e);
   ra.eps = c.rms_eps;
-  ra.h_f16 = (i4 || q8) ? 1 : 0;
+  ra.h_f16 = (i4 || q8 || mx4) ? 1 : 0;
   ra.h = L.fold ? nullptr : hd->at<uint16_t>(L.h);
   ra.rnorm = hd->at<float>(L.rnorm);
   ra.logits = hd->at<float>(L.logits);
@@ -405,7 +424,7 @@ static dg_status run_forward(dg_moe_handle hd, const void* x, void* out, int32_t
   pa.T = T;
   pa.K = c.top_k;
   pa.E = c.n_experts;
-  const bool tall = !i4 && !q8 && dg::use_tall_tiles(T, c.top_k, c.n_experts);
+  const bool tall = c.expert_w_dtype == DG_BF16 && dg::use_tall_tiles(T, c.top_k, c.n_experts);
   const bool fused = fuses_gemms(c);
   pa.tile_rows = tall ? dg::kTallRows : dg::kTileRows;
   pa.deal = fused ? dg::kDealBalanced : tall ? dg::kDealExperts : dg::kDealUnits;
@@ -449,7 +468,8 @@ static dg_status run_forward(dg_moe_handle hd, const void* x, void* out, int32_t
     fa.dn.qmax = pa.qmax[1];
     fa.tile_done = pa.tile_done;
     fa.nb_gate_up = L.nb[0];
-    e = q8 ? dg::launch_gemm_fused_q8(fa, stream, ev(3))
+    e = mx4  ? dg::launch_gemm_fused_mx4(fa, stream, ev(3))
+        : q8 ? dg::launch_gemm_fused_q8(fa, stream, ev(3))
         : i4 ? dg::launch_gemm_fused_i4(fa, stream, ev(3))
              : dg::launch_gemm_fused(fa, tall, stream, ev(3));
     if (e != hipSuccess) return hip_fail(e, "GEMM launch");

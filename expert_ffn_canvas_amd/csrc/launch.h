@@ -60,7 +60,7 @@ struct RouterArgs {
   const float* bias;    // [E] or null
   const float* gamma_e;
   float eps;
-  int h_f16;            // expert input stored as fp16 (int4 or Q8_0 experts) instead of bf16
+  int h_f16;            // expert input stored as fp16 (int4, Q8_0 or MXFP4 experts) instead of bf16
   uint16_t* h;          // [T, D] expert input (norm kernel only)
   float* rnorm;         // [T] r = 1/sqrt(mean x^2 + eps) of each token
   float* logits;        // [T, Epad]
@@ -108,11 +108,12 @@ struct GemmArgs {
   int qmax;                // their capacity
   const int32_t* sorted_slot;  // [K T] slot t K + j of each expert-sorted row
   int K;
-  const uint16_t* h;       // [T, D] expert input (bf16, or fp16 for int4 / Q8_0 experts); the raw x when rnorm is set
+  const uint16_t* h;       // [T, D] expert input (bf16, or fp16 for quantised experts); the raw x when rnorm is set
   const float* rnorm;      // [T] r of each token when h is the raw x and (1 + gamma_e) is folded into
                            // w_gate_up: the gate and up sums are scaled by it; else null
-  const void* w_gate_up;   // bf16 [E, 2F, D], int4 bytes [E, 2F, D/2], or packed Q8_0 codes
-  const void* w_down;      // bf16 [E, D, F], int4 bytes [E, D, F/2], or packed Q8_0 codes
+  const void* w_gate_up;   // bf16 [E, 2F, D], int4 bytes [E, 2F, D/2], or packed Q8_0 / MXFP4 codes
+  const void* w_down;      // bf16 [E, D, F], int4 bytes [E, D, F/2], or packed Q8_0 / MXFP4 codes
+  // scales: fp16 (int4, Q8_0), or E8M0 bytes (MXFP4) read through these pointers
   const uint16_t* s_gate_up;
   const uint16_t* s_down;
   uint16_t* act;           // [K T, F] gelu_tanh(gate) * up, expert-sorted rows
@@ -160,6 +161,18 @@ hipError_t launch_pack_q8(const uint8_t* blocks, uint8_t* pcodes, uint16_t* psca
 // Both products with packed Q8_0 weights (fp16 expert input and activation)
 // in one launch, as launch_gemm_fused.
 hipError_t launch_gemm_fused_q8(const FusedGemmArgs& f, hipStream_t stream, const KernelEvents* ev);
+// Create-time relayout of MXFP4 expert weights (rows of K / 32 blocks of 17
+// bytes: E8M0 scale byte, 16 bytes of E2M1 codes, input j in the low nibble of
+// byte j or the high nibble of byte j - 16) into fragment order: per (expert,
+// 128-input step, 16-row panel), 1 KB of codes (lane n + 16 g: 16 bytes of row
+// n, one dword per 32-input block holding inputs 8 g .. 8 g + 7, even input in
+// the low nibble) and 64 scale bytes [row][block]; a short last step is
+// padded with zero codes and scale bytes.
+hipError_t launch_pack_mx4(const uint8_t* blocks, uint8_t* pcodes, uint8_t* pscales, int E, int R, int K,
+                           hipStream_t stream);
+// Both products with packed MXFP4 weights (fp16 expert input and activation)
+// in one launch, as launch_gemm_fused.
+hipError_t launch_gemm_fused_mx4(const FusedGemmArgs& f, hipStream_t stream, const KernelEvents* ev);
 
 struct CombineArgs {
   const uint16_t* y;           // [K T, D] bf16 expert outputs, expert-sorted rows

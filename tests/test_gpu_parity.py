@@ -160,6 +160,34 @@ def test_q8_0_small(E, K, D, F, T):
     print(f"err {r['err']:.3e} near-ties {r['near_ties']}")
 
 
+def test_mxfp4():
+    wl = synth.WORKLOADS["mxfp4"]
+    _say(f"{wl.name} T={wl.T} pack=True")
+    inp = synth.make_inputs(wl, device="cuda")
+    w = inp["layers"][0]
+    layer = _layer(w, wl.T, torch.bfloat16, pack=True)
+    rng = np.random.default_rng(3)
+    tok = np.unique(np.concatenate([[0, wl.T - 1], rng.choice(wl.T, 100, replace=False)]))
+    r = layer_parity(layer, inp["x"], oracle_weights(w), wl.K, tokens=tok)
+    print(f"err {r['err']:.3e} near-ties {r['near_ties']}")
+
+
+@pytest.mark.parametrize("E,K,D,F,T", [
+    (12, 3, 256, 192, 50),   # down K = 192: a last 128-input step holding two blocks
+    (8, 4, 256, 192, 200),   # tiles of up to 64 rows
+    (6, 2, 128, 64, 37),     # gate_up K = 128 (one step), down K = 64 (a lone short step)
+    (4, 2, 384, 320, 300),   # gate_up three steps, down two full steps and a short one
+])
+def test_mxfp4_small(E, K, D, F, T):
+    _say(f"mxfp4 small E={E} K={K} D={D} F={F} T={T}")
+    wl = synth.small_workload(T=T, E=E, K=K, D=D, F=F, experts="mxfp4", bias="zipf", seed=40 + T)
+    inp = synth.make_inputs(wl, device="cuda")
+    w = inp["layers"][0]
+    layer = _layer(w, T, torch.bfloat16, K=K, pack=True)
+    r = layer_parity(layer, inp["x"], oracle_weights(w), K)
+    print(f"err {r['err']:.3e} near-ties {r['near_ties']}")
+
+
 # ----------------------------------------------------------------------------- edge cases
 
 @pytest.mark.parametrize("T", [1, 15, 17, 255, 257])
