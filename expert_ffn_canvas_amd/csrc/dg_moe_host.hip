@@ -401,7 +401,7 @@ static dg_status run_forward(dg_moe_handle hd, const void* x, void* out, int32_t
   ra.bias = hd->has_bias ? hd->at<float>(L.bias) : nullptr;
   ra.gamma_e = hd->at<float>(L.gamma_e);
   ra.eps = c.rms_eps;
-  ra.h_f16 = (i4 || q8 || mx4) ? 1 : 0;
+  ra.h_f16 = (i4 || q8) ? 1 : 0;  // MXFP4 widens to bf16 (its block scales need bf16's exponent range)
   ra.h = L.fold ? nullptr : hd->at<uint16_t>(L.h);
   ra.rnorm = hd->at<float>(L.rnorm);
   ra.logits = hd->at<float>(L.logits);

@@ -1,5 +1,6 @@
-// Grouped expert GEMMs with MXFP4 expert weights on gfx950 fp16 matrix cores,
-// the FP4 codes widened by the hardware conversion inside the weight load.
+// Grouped expert GEMMs with MXFP4 expert weights on gfx950 bf16 matrix cores,
+// the FP4 codes and their block scales widened by the hardware conversion
+// inside the weight load.
 //
 // Weight format: the FP4 builds that the HF card "DiffusionGemma-26B-A4B-it -
 // ROCmFP4 / ROCmFPX GGUF" compares (introduction; "The 4-bit is NOT the
@@ -18,16 +19,19 @@
 // bytes are [n][j]. Blocks past the row (the 64-input tail of a 704 row) are
 // padded with zero codes and scale bytes.
 //
-// Exact widening: v_cvt_scalef32_pk_f16_fp4 turns one code byte into its two
-// E2M1 values as fp16 (scale operand 1: every E2M1 value is an fp16 value).
-// These go into the fp16 MFMA against fp16 activations (products exact in
-// fp32); each 32-input block's partial sum is multiplied by its scale
-// 2^(e - 127), built as an fp32 bit pattern, and added. So every weight enters
-// as exactly its E2M1 value times its block scale, as in the oracle.
+// Exact widening: v_cvt_scalef32_pk_bf16_fp4 turns one code byte into its two
+// E2M1 values times the block scale 2^(e - 127) (built as an fp32 bit pattern)
+// as bf16. An E2M1 value has at most two significant bits and bf16 has fp32's
+// exponent range, so the product is exact (subnormal down to 2^-133; a scale
+// of 2^127 overflows to infinity for the codes 6 and -6, as in fp32). These
+// weights go into the bf16 MFMA against bf16 activations (products exact in
+// fp32), exactly like the bf16 kernels: every weight enters as exactly its
+// E2M1 value times its block scale, as in the oracle.
 //
 // Mapping, activation path and work distribution as in the bf16 and Q8_0
 // kernels (64-row tiles, 4 waves, two 16-row panels per wave, activation rows
-// staged in LDS by DMA, both GEMMs in one launch from the per-XCD queues).
+// staged in LDS by DMA, both GEMMs in one launch from the per-XCD queues), with
+// a quarter of the bf16 kernels' weight bytes per step.
 #include "dg_common.h"
 #include "gemm_common.h"
 #include "launch.h"
@@ -58,13 +62,14 @@ __device__ __forceinline__ void load_m(const uint8_t* c0, const uint8_t* c1, con
   p.s1 = *reinterpret_cast<const uint32_t*>(s1 + (size_t)step * sstep);
 }
 
-// 8 codes of one dword (natural order, even input in the low nibble) -> 8 fp16.
-__device__ __forceinline__ f16x8 mx4_to_f16(uint32_t v) {
-  const f16x2 p0 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(v, 1.0f, 0);
-  const f16x2 p1 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(v, 1.0f, 1);
-  const f16x2 p2 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(v, 1.0f, 2);
-  const f16x2 p3 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(v, 1.0f, 3);
-  f16x8 r;
+// 8 codes of one dword (natural order, even input in the low nibble) times the
+// block scale -> 8 bf16, exact.
+__device__ __forceinline__ bf16x8 mx4_to_bf16(uint32_t v, float scale) {
+  const bf16x2 p0 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(v, scale, 0);
+  const bf16x2 p1 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(v, scale, 1);
+  const bf16x2 p2 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(v, scale, 2);
+  const bf16x2 p3 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(v, scale, 3);
+  bf16x8 r;
   r[0] = p0[0]; r[1] = p0[1]; r[2] = p1[0]; r[3] = p1[1];
   r[4] = p2[0]; r[5] = p2[1]; r[6] = p3[0]; r[7] = p3[1];
   return r;
@@ -78,32 +83,24 @@ __device__ __forceinline__ float mx_scale(uint32_t s, int j) {
   return __uint_as_float(bits);
 }
 
-// NS blocks of one step: each block's MFMA into a zeroed accumulator, then
-// scaled by the block's scale into acc.
+// NS blocks of one step, each one MFMA K step of 32 inputs.
 template <int NMT, int NS>
 __device__ __forceinline__ void mma_mx4(const char* stage, int lane, const MPanels& p, f32x4 (&acc0)[kBMT],
                                         f32x4 (&acc1)[kBMT]) {
   const int g = lane >> 4, m = lane & 15;
-  const f32x4 zero = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
   for (int j = 0; j < NS; ++j) {
-    const f16x8 b0 = mx4_to_f16(p.c0[j]);
-    const f16x8 b1 = mx4_to_f16(p.c1[j]);
-    const float d0 = mx_scale(p.s0, j), d1 = mx_scale(p.s1, j);
+    const bf16x8 b0 = mx4_to_bf16(p.c0[j], mx_scale(p.s0, j));
+    const bf16x8 b1 = mx4_to_bf16(p.c1[j], mx_scale(p.s1, j));
 #pragma unroll
     for (int mt = 0; mt < NMT; ++mt) {
       const int r = mt * 16 + m;
       const int pos = (j * 4 + g) ^ (r % kSegs);
-      const f16x8 av = as_f16x8(*reinterpret_cast<const u32x4*>(stage + r * kRowBytes + pos * 16));
-      const f32x4 t0 = mfma_f16(av, b0, zero);
-      const f32x4 t1 = mfma_f16(av, b1, zero);
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        acc0[mt][i] = fmaf(d0, t0[i], acc0[mt][i]);
-        acc1[mt][i] = fmaf(d1, t1[i], acc1[mt][i]);
-      }
+      const bf16x8 av = as_bf16x8(*reinterpret_cast<const u32x4*>(stage + r * kRowBytes + pos * 16));
+      acc0[mt] = mfma_bf16(av, b0, acc0[mt]);
+      acc1[mt] = mfma_bf16(av, b1, acc1[mt]);
     }
-    __builtin_amdgcn_sched_barrier(0);  // one block's operands and partial sums live at a time
+    if (j & 1) __builtin_amdgcn_sched_barrier(0);  // at most two blocks' operands live at a time
   }
 }
 
@@ -181,8 +178,8 @@ __device__ __forceinline__ void mloop(char* As, const uint16_t* const (&rowp)[kD
   }
 }
 
-// The product of one task: gate_up writes the gated activation as fp16 (the
-// down GEMM's fp16 operand), down its fp32 sums as bf16.
+// The product of one task: gate_up writes the gated activation as bf16 (the
+// down GEMM's bf16 operand), down its fp32 sums as bf16.
 template <bool GATE_UP>
 __device__ __forceinline__ void mx4_body(const GemmArgs& a, const Tile& tl, char* As) {
   const int F = a.F, D = a.D;
@@ -245,8 +242,7 @@ __device__ __forceinline__ void mx4_body(const GemmArgs& a, const Tile& tl, char
         const int r = mt * 16 + g * 4 + i;
         if (r < tl.mc) {
           if (GATE_UP) {
-            const _Float16 v = (_Float16)(gelu_tanh(acc0[mt][i]) * acc1[mt][i]);
-            a.act[(size_t)(tl.row0 + r) * F + col] = __builtin_bit_cast(uint16_t, v);
+            a.act[(size_t)(tl.row0 + r) * F + col] = f32_to_bf16_bits(gelu_tanh(acc0[mt][i]) * acc1[mt][i]);
           } else {
             uint16_t* yr = a.y + (size_t)(tl.row0 + r) * D + col;
             yr[0] = f32_to_bf16_bits(acc0[mt][i]);
@@ -258,9 +254,9 @@ __device__ __forceinline__ void mx4_body(const GemmArgs& a, const Tile& tl, char
   }
 }
 
-// Both GEMMs in one launch (the task logic of fused_tasks), two workgroups
-// per CU.
-__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))) void k_gemm_mx4_fused(
+// Both GEMMs in one launch (the task logic of fused_tasks), three workgroups
+// per CU as the bf16 kernels.
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3, 3))) void k_gemm_mx4_fused(
     FusedGemmArgs f) {
   __shared__ __attribute__((aligned(16))) char As[2 * kStageBytes];
   fused_tasks(

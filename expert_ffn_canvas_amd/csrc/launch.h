@@ -60,7 +60,7 @@ struct RouterArgs {
   const float* bias;    // [E] or null
   const float* gamma_e;
   float eps;
-  int h_f16;            // expert input stored as fp16 (int4, Q8_0 or MXFP4 experts) instead of bf16
+  int h_f16;            // expert input stored as fp16 (int4 or Q8_0 experts) instead of bf16
   uint16_t* h;          // [T, D] expert input (norm kernel only)
   float* rnorm;         // [T] r = 1/sqrt(mean x^2 + eps) of each token
   float* logits;        // [T, Epad]
