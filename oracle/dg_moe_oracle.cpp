@@ -134,6 +134,22 @@ inline float load_elem(const void* p, int dtype, size_t i) {
 // scales fp16 [rows, ceil(K/128)]. Q8_0: K/32 blocks of 34 bytes per row,
 // block b = (fp16 scale d, little endian; int8 codes of inputs 32 b .. 32 b + 31).
 // MXFP4: K/32 blocks of 17 bytes per row (E8M0 scale byte, 16 code bytes).
+// Element (row, k) of a matrix stored in 32-input blocks (Q8_0 or MXFP4).
+// Kept out of line so that the bf16 and int4 reads stay small.
+__attribute__((noinline)) float block_weight(int dtype, const void* data, int K, size_t row, int k) {
+  if (dtype == OR_Q8_0) {
+    const uint8_t* blk = static_cast<const uint8_t*>(data) + (row * static_cast<size_t>(K / 32) + k / 32) * 34;
+    const uint16_t d = static_cast<uint16_t>(blk[0] | (blk[1] << 8));
+    const int q = static_cast<int8_t>(blk[2 + k % 32]);
+    return static_cast<float>(q) * half_bits_to_float(d);  // exact in fp32
+  }
+  const uint8_t* blk = static_cast<const uint8_t*>(data) + (row * static_cast<size_t>(K / 32) + k / 32) * 17;
+  const int j = k % 32;
+  const uint8_t byte = blk[1 + (j & 15)];
+  const int code = j < 16 ? (byte & 0x0f) : (byte >> 4);
+  return e2m1_value(code) * e8m0_value(blk[0]);  // exact in fp32 (two significant bits times a power of two)
+}
+
 struct WeightView {
   int dtype;
   const void* data;
@@ -143,19 +159,7 @@ struct WeightView {
     if (dtype == OR_BF16) {
       return bf16_bits_to_float(static_cast<const uint16_t*>(data)[row * K + k]);
     }
-    if (dtype == OR_Q8_0) {
-      const uint8_t* blk = static_cast<const uint8_t*>(data) + (row * static_cast<size_t>(K / 32) + k / 32) * 34;
-      const uint16_t d = static_cast<uint16_t>(blk[0] | (blk[1] << 8));
-      const int q = static_cast<int8_t>(blk[2 + k % 32]);
-      return static_cast<float>(q) * half_bits_to_float(d);  // exact in fp32
-    }
-    if (dtype == OR_MXFP4) {
-      const uint8_t* blk = static_cast<const uint8_t*>(data) + (row * static_cast<size_t>(K / 32) + k / 32) * 17;
-      const int j = k % 32;
-      const uint8_t byte = blk[1 + (j & 15)];
-      const int code = j < 16 ? (byte & 0x0f) : (byte >> 4);
-      return e2m1_value(code) * e8m0_value(blk[0]);  // exact in fp32 (two significant bits times a power of two)
-    }
+    if (dtype == OR_Q8_0 || dtype == OR_MXFP4) return block_weight(dtype, data, K, row, k);
     const size_t row_bytes = (static_cast<size_t>(K) + 1) / 2;
     const uint8_t byte = static_cast<const uint8_t*>(data)[row * row_bytes + k / 2];
     const int q = (k & 1) ? (byte >> 4) : (byte & 0x0f);
