@@ -13,6 +13,7 @@ the canvas, two canvases, 30 MoE layers):
   int4       T=256,  bf16 activations, int4-g128 experts (zero point 8)
   q8         T=256,  bf16 activations, Q8_0 experts (blocks of 32, fp16 scale)
   mxfp4      T=256,  bf16 activations, MXFP4 experts (blocks of 32 E2M1 codes, E8M0 scale)
+  mxfp8      T=256,  bf16 activations, MXFP8 experts (blocks of 32 E4M3 codes, E8M0 scale)
   stack30    T=512,  30 layers with their own bf16 weights, Zipf skew,
              a N(0, 0.5) offset [T, D] added after each layer
 
@@ -47,7 +48,7 @@ class Workload:
     T: int
     act: str            # "f32" | "bf16"
     router_w: str       # "f32" | "bf16"
-    experts: str        # "bf16" | "i4g128" | "q8_0" | "mxfp4"
+    experts: str        # "bf16" | "i4g128" | "q8_0" | "mxfp4" | "mxfp8"
     bias: str | None    # None | "zipf"
     seed: int
     layers: int = 1
@@ -66,6 +67,7 @@ WORKLOADS = {
     "int4": Workload("int4", 256, "bf16", "bf16", "i4g128", None, 3),
     "q8": Workload("q8", 256, "bf16", "bf16", "q8_0", None, 5),
     "mxfp4": Workload("mxfp4", 256, "bf16", "bf16", "mxfp4", None, 6),
+    "mxfp8": Workload("mxfp8", 256, "bf16", "bf16", "mxfp8", None, 7),
     "stack30": Workload("stack30", 512, "bf16", "bf16", "bf16", "zipf", 4, layers=30, delta_std=0.5),
 }
 
@@ -155,6 +157,46 @@ def quantize_mxfp4(w: torch.Tensor) -> torch.Tensor:
     return torch.cat([e8, packed], dim=-1).contiguous()
 
 
+E4M3_MAX = 448.0  # largest E4M3 magnitude (OCP 8-bit floating point, E4M3 with no infinities)
+
+
+def quantize_mxfp8(w: torch.Tensor) -> torch.Tensor:
+    """MXFP8 (E4M3) blocks of 32 consecutive inputs along the last dim (K % 32 == 0),
+    the OCP Microscaling conversion: shared exponent X = floor(log2(amax)) - 8 (the
+    largest E4M3 power is 2^8), clamped to [-127, 127] (-127 for an all-zero block);
+    each input the E4M3 value nearest to w / 2^X (three mantissa bits below the
+    input's own power of two, a fixed 2^-9 step under 2^-6), ties to the even
+    code, magnitudes above 448 saturating. Returns uint8 [..., K/32, 33]: per block
+    the E8M0 byte X + 127, then the 32 codes in input order.
+    """
+    K = w.shape[-1]
+    assert K % 32 == 0
+    out = torch.empty((*w.shape[:-1], K // 32, 33), dtype=torch.uint8, device=w.device)
+    flat_w = w.reshape(-1, K)
+    flat_o = out.view(-1, K // 32, 33)
+    step = max(1, (1 << 24) // K)  # rows per chunk: a few hundred MB of temporaries at most
+    for r0 in range(0, flat_w.shape[0], step):
+        wb = flat_w[r0:r0 + step].reshape(-1, K // 32, 32).to(torch.float32)
+        amax = wb.abs().amax(dim=-1)
+        _, ex = torch.frexp(amax)  # floor(log2(amax)) = ex - 1
+        X = torch.where(amax > 0, ex.to(torch.float32) - 1 - 8, torch.full_like(amax, -127.0)).clamp(-127, 127)
+        a = (wb / torch.exp2(X).unsqueeze(-1)).abs()
+        _, ea = torch.frexp(a)  # a in [2^(ea-1), 2^ea)
+        quantum = torch.exp2((ea.to(torch.float32) - 1 - 3).clamp(min=-9.0))
+        q = (torch.round(a / quantum) * quantum).clamp(max=E4M3_MAX)  # torch.round: half to even
+        # q is now an E4M3 magnitude; its code: under 2^-6 the subnormal m 2^-9
+        # (m = 8 is 2^-6, code 0x08, the first normal), else exponent and mantissa
+        _, eq = torch.frexp(q)
+        e_f = (eq - 1 + 7).to(torch.float32)
+        normal = q >= 2.0 ** -6
+        mant = torch.where(normal, q / torch.exp2(eq.to(torch.float32) - 1) * 8 - 8, q * 512)
+        code = torch.where(normal, e_f * 8 + mant, mant).to(torch.int32)
+        code = code | torch.where((wb < 0) & (code > 0), 0x80, 0)
+        flat_o[r0:r0 + step, :, 0] = (X + 127).to(torch.uint8)
+        flat_o[r0:r0 + step, :, 1:] = code.to(torch.uint8)
+    return out
+
+
 def make_layer_weights(wl: Workload, gen: torch.Generator, device) -> dict:
     """Weights of one layer, drawn in the fixed order (router W, gammas, gate_up, down)."""
     E, D, F = wl.E, wl.D, wl.F
@@ -186,6 +228,10 @@ def make_layer_weights(wl: Workload, gen: torch.Generator, device) -> dict:
         w["mx4_gate_up"] = quantize_mxfp4(gu)
         del gu
         w["mx4_down"] = quantize_mxfp4(_randn((E, D, F), 0.02, gen, device))
+    elif wl.experts == "mxfp8":
+        w["mx8_gate_up"] = quantize_mxfp8(gu)
+        del gu
+        w["mx8_down"] = quantize_mxfp8(_randn((E, D, F), 0.02, gen, device))
     else:
         w["w_gate_up"] = gu.to(torch.bfloat16)
         del gu

@@ -2,7 +2,7 @@
 
 All arrays are numpy arrays on the host. bf16 tensors are passed as their raw
 uint16 bit patterns, fp16 scales as uint16 bit patterns, int4 weights as the
-packed uint8 bytes, Q8_0 and MXFP4 weights as their 34- and 17-byte blocks (uint8).
+packed uint8 bytes, Q8_0, MXFP4 and MXFP8 weights as their 34-, 17- and 33-byte blocks (uint8).
 """
 import ctypes
 import os
@@ -13,7 +13,7 @@ from .build import LIB, SRC, build
 
 _lib = None
 
-DT_F32, DT_BF16, DT_F16, DT_I4G128, DT_Q8_0, DT_MXFP4 = 0, 1, 2, 3, 4, 5
+DT_F32, DT_BF16, DT_F16, DT_I4G128, DT_Q8_0, DT_MXFP4, DT_MXFP8 = 0, 1, 2, 3, 4, 5, 6
 
 _p = ctypes.c_void_p
 _i = ctypes.c_int
@@ -41,6 +41,8 @@ def load():
     lib.oracle_dequant_q8_0.argtypes = [_p, ctypes.c_int64, _i, _p]
     lib.oracle_dequant_mxfp4.restype = None
     lib.oracle_dequant_mxfp4.argtypes = [_p, ctypes.c_int64, _i, _p]
+    lib.oracle_dequant_mxfp8.restype = None
+    lib.oracle_dequant_mxfp8.argtypes = [_p, ctypes.c_int64, _i, _p]
     lib.oracle_route.restype = _i
     lib.oracle_route.argtypes = [_i, _i, _i, _i, _d, _i, _p, _i, _p, _p, _p, _p, _p, _p, _p, _p, _p, _i]
     lib.oracle_permute.restype = _i
@@ -117,6 +119,16 @@ def dequant_mxfp4(blocks, K):
     return out
 
 
+def dequant_mxfp8(blocks, K):
+    """blocks: uint8 [rows, K/32 * 33] (or [rows, K/32, 33]) -> fp32 [rows, K]."""
+    rows = blocks.shape[0]
+    b = np.ascontiguousarray(blocks, dtype=np.uint8).reshape(rows, -1)
+    assert b.shape[1] == K // 32 * 33
+    out = np.empty((rows, K), dtype=np.float32)
+    load().oracle_dequant_mxfp8(_ptr(b), rows, K, _ptr(out))
+    return out
+
+
 def _expert_arrays(w):
     """(dtype code, gate_up, down, gate_up scales, down scales, F) of a weight dict."""
     if "q_gate_up" in w:
@@ -128,6 +140,9 @@ def _expert_arrays(w):
     if "mx4_gate_up" in w:
         gu = w["mx4_gate_up"]
         return DT_MXFP4, np.ascontiguousarray(gu), np.ascontiguousarray(w["mx4_down"]), None, None, gu.shape[1] // 2
+    if "mx8_gate_up" in w:
+        gu = w["mx8_gate_up"]
+        return DT_MXFP8, np.ascontiguousarray(gu), np.ascontiguousarray(w["mx8_down"]), None, None, gu.shape[1] // 2
     gu = w["w_gate_up"]
     return DT_BF16, gu, w["w_down"], None, None, gu.shape[1] // 2
 
@@ -172,7 +187,8 @@ def moe_forward(w, x, k, eps, forced=None, tokens=None, add_input=False, addend=
     ([E,2F,D] / [E,D,F]) or, for int4, q_gate_up uint8 [E,2F,D/2], s_gate_up uint16 [E,2F,D/128],
     q_down uint8 [E,D,F/2], s_down uint16 [E,D,ceil(F/128)], or, for Q8_0, q8_gate_up uint8
     [E,2F,D/32,34] and q8_down uint8 [E,D,F/32,34], or, for MXFP4, mx4_gate_up uint8 [E,2F,D/32,17] and
-    mx4_down uint8 [E,D,F/32,17].
+    mx4_down uint8 [E,D,F/32,17], or, for MXFP8, mx8_gate_up uint8 [E,2F,D/32,33] and mx8_down uint8
+    [E,D,F/32,33].
     Returns dict(out [n,D] f32, idx [n,k], w [n,k] f64, gap [n]).
     """
     T, D = x.shape

@@ -34,6 +34,14 @@
 //    code bytes, input j of the block in the low nibble of byte j for j < 16
 //    and in the high nibble of byte j - 16 for j >= 16 (the GGUF block
 //    arrangement).
+//  * MXFP8 weights: the FP8 builds of the same card (its credits name FP4 and
+//    FP8 tensor types) are not defined on the pages either; they are read as
+//    the OCP Microscaling MXFP8 format with E4M3 elements: blocks of 32
+//    consecutive inputs sharing an E8M0 scale, each input an E4M3 code (sign
+//    bit, four exponent bits with bias 7, three mantissa bits; exponent field
+//    0 is subnormal, the all-ones pattern with mantissa 7 is NaN, there are no
+//    infinities), stored per block as the scale byte and then 32 code bytes,
+//    input j of the block in byte j.
 //
 // Readings where the pages are silent (each one is listed with its reason in
 // the design notes): router norm = the same (1+gamma) RMSNorm form as the
@@ -63,7 +71,7 @@
 
 namespace {
 
-enum { OR_F32 = 0, OR_BF16 = 1, OR_F16 = 2, OR_I4G128 = 3, OR_Q8_0 = 4, OR_MXFP4 = 5 };
+enum { OR_F32 = 0, OR_BF16 = 1, OR_F16 = 2, OR_I4G128 = 3, OR_Q8_0 = 4, OR_MXFP4 = 5, OR_MXFP8 = 6 };
 
 // E2M1 code (4 bits) -> value: exponent field 0 is subnormal (0 or 0.5),
 // otherwise 2^(exponent - 1) (1 + mantissa / 2); bit 3 is the sign.
@@ -71,6 +79,16 @@ inline float e2m1_value(int code) {
   const int ex = (code >> 1) & 3, m = code & 1;
   const float mag = ex == 0 ? 0.5f * static_cast<float>(m) : std::ldexp(1.0f + 0.5f * static_cast<float>(m), ex - 1);
   return (code & 8) ? -mag : mag;
+}
+
+// E4M3 code (8 bits) -> value: exponent field 0 is subnormal, m 2^-9;
+// otherwise 2^(exponent - 7) (1 + mantissa / 8); exponent 15 with mantissa 7
+// is NaN; bit 7 is the sign.
+inline float e4m3_value(int code) {
+  const int ex = (code >> 3) & 15, m = code & 7;
+  if (ex == 15 && m == 7) return NAN;
+  const float mag = ex == 0 ? std::ldexp(static_cast<float>(m), -9) : std::ldexp(1.0f + 0.125f * static_cast<float>(m), ex - 7);
+  return (code & 0x80) ? -mag : mag;
 }
 
 // E8M0 scale byte -> 2^(e - 127); 255 encodes NaN.
@@ -134,7 +152,8 @@ inline float load_elem(const void* p, int dtype, size_t i) {
 // scales fp16 [rows, ceil(K/128)]. Q8_0: K/32 blocks of 34 bytes per row,
 // block b = (fp16 scale d, little endian; int8 codes of inputs 32 b .. 32 b + 31).
 // MXFP4: K/32 blocks of 17 bytes per row (E8M0 scale byte, 16 code bytes).
-// Element (row, k) of a matrix stored in 32-input blocks (Q8_0 or MXFP4).
+// MXFP8: K/32 blocks of 33 bytes per row (E8M0 scale byte, 32 code bytes).
+// Element (row, k) of a matrix stored in 32-input blocks (Q8_0, MXFP4, MXFP8).
 // Kept out of line so that the bf16 and int4 reads stay small.
 __attribute__((noinline)) float block_weight(int dtype, const void* data, int K, size_t row, int k) {
   if (dtype == OR_Q8_0) {
@@ -142,6 +161,10 @@ __attribute__((noinline)) float block_weight(int dtype, const void* data, int K,
     const uint16_t d = static_cast<uint16_t>(blk[0] | (blk[1] << 8));
     const int q = static_cast<int8_t>(blk[2 + k % 32]);
     return static_cast<float>(q) * half_bits_to_float(d);  // exact in fp32
+  }
+  if (dtype == OR_MXFP8) {
+    const uint8_t* blk = static_cast<const uint8_t*>(data) + (row * static_cast<size_t>(K / 32) + k / 32) * 33;
+    return e4m3_value(blk[1 + k % 32]) * e8m0_value(blk[0]);  // exact in fp32 (four significant bits times 2^n; inf past fp32 range)
   }
   const uint8_t* blk = static_cast<const uint8_t*>(data) + (row * static_cast<size_t>(K / 32) + k / 32) * 17;
   const int j = k % 32;
@@ -159,7 +182,7 @@ struct WeightView {
     if (dtype == OR_BF16) {
       return bf16_bits_to_float(static_cast<const uint16_t*>(data)[row * K + k]);
     }
-    if (dtype == OR_Q8_0 || dtype == OR_MXFP4) return block_weight(dtype, data, K, row, k);
+    if (dtype == OR_Q8_0 || dtype == OR_MXFP4 || dtype == OR_MXFP8) return block_weight(dtype, data, K, row, k);
     const size_t row_bytes = (static_cast<size_t>(K) + 1) / 2;
     const uint8_t byte = static_cast<const uint8_t*>(data)[row * row_bytes + k / 2];
     const int q = (k & 1) ? (byte >> 4) : (byte & 0x0f);
@@ -302,6 +325,13 @@ void oracle_dequant_mxfp4(const uint8_t* blocks, int64_t rows, int K, float* out
     for (int k = 0; k < K; ++k) out[r * K + k] = v.at(static_cast<size_t>(r), k);
 }
 
+// MXFP8 blocks [rows, K/32, 33 bytes] -> fp32 [rows, K].
+void oracle_dequant_mxfp8(const uint8_t* blocks, int64_t rows, int K, float* out) {
+  WeightView v{OR_MXFP8, blocks, nullptr, K};
+  for (int64_t r = 0; r < rows; ++r)
+    for (int k = 0; k < K; ++k) out[r * K + k] = v.at(static_cast<size_t>(r), k);
+}
+
 // Q8_0 blocks [rows, K/32, 34 bytes] -> fp32 [rows, K].
 void oracle_dequant_q8_0(const uint8_t* blocks, int64_t rows, int K, float* out) {
   WeightView v{OR_Q8_0, blocks, nullptr, K};
@@ -364,7 +394,7 @@ int oracle_permute(int T, int K, int E, const int32_t* idx, int32_t* counts, int
 //   then, if add_input, out += fp32(x); if addend, out += fp32(addend).
 // out32 [n_tok, D] fp32 (before any output rounding). idx/w/gap per computed
 // token (nullable). dtypes: x/addend 0=f32 1=bf16; router_w 0=f32 1=bf16;
-// expert weights 1=bf16 3=int4-g128 4=Q8_0 5=MXFP4. Returns 0 or -1 on a bad argument.
+// expert weights 1=bf16 3=int4-g128 4=Q8_0 5=MXFP4 6=MXFP8. Returns 0 or -1 on a bad argument.
 int oracle_moe_forward(int T, int D, int F, int E, int K, double eps, int x_dtype, const void* x,
                        int rw_dtype, const void* router_w, const float* router_gamma,
                        const float* router_bias, const float* ffn_gamma, int ew_dtype,
@@ -373,9 +403,11 @@ int oracle_moe_forward(int T, int D, int F, int E, int K, double eps, int x_dtyp
                        int n_tok, int add_input, const void* addend, float* out32, int32_t* idx_out,
                        double* w_out, double* gap_out, int n_threads) {
   if (T < 0 || D <= 0 || F <= 0 || E <= 0 || K <= 0 || K > E) return -1;
-  if (ew_dtype != OR_BF16 && ew_dtype != OR_I4G128 && ew_dtype != OR_Q8_0 && ew_dtype != OR_MXFP4) return -1;
+  if (ew_dtype != OR_BF16 && ew_dtype != OR_I4G128 && ew_dtype != OR_Q8_0 && ew_dtype != OR_MXFP4 &&
+      ew_dtype != OR_MXFP8)
+    return -1;
   if (ew_dtype == OR_I4G128 && (!s_gate_up || !s_down)) return -1;
-  if ((ew_dtype == OR_Q8_0 || ew_dtype == OR_MXFP4) && (D % 32 || F % 32)) return -1;
+  if ((ew_dtype == OR_Q8_0 || ew_dtype == OR_MXFP4 || ew_dtype == OR_MXFP8) && (D % 32 || F % 32)) return -1;
   Layer L{T, D, F, E, K, eps, x_dtype, x, rw_dtype, router_w, router_gamma, router_bias, ffn_gamma,
           ew_dtype, w_gate_up, w_down, s_gate_up, s_down};
   const int n = tokens ? n_tok : T;

@@ -508,6 +508,92 @@ def test_mxfp4_layer_matches_dense_reference_of_dequantised_weights():
     assert rel_err(o["out"], ref.numpy()) <= 2e-5
 
 
+# E4M3 values fixed by the 8-bit floating-point format's definition (OCP): bias 7, three mantissa bits,
+# exponent field 0 subnormal with step 2^-9, the smallest normal 2^-6, the largest 448, and the all-ones
+# pattern NaN (no infinities).
+E4M3_SPEC = {0x00: 0.0, 0x01: 2.0 ** -9, 0x07: 7 * 2.0 ** -9, 0x08: 2.0 ** -6, 0x38: 1.0, 0x3C: 1.5,
+             0x40: 2.0, 0x7E: 448.0, 0x80: -0.0, 0xB8: -1.0, 0xFE: -448.0}
+
+
+def test_mxfp8_codes_scales_and_layout():
+    codes = np.arange(256, dtype=np.uint8)
+    rows = np.zeros((8, 33), dtype=np.uint8)
+    rows[:, 0] = 127
+    rows[:, 1:] = codes.reshape(8, 32)
+    deq = oracle.dequant_mxfp8(rows, 32).reshape(-1)
+    for c, v in E4M3_SPEC.items():
+        assert deq[c] == v and np.signbit(deq[c]) == np.signbit(v), hex(c)
+    assert np.isnan(deq[0x7F]) and np.isnan(deq[0xFF])
+    # every code against torch's own E4M3 decoder (a library routine of the same format)
+    lib = torch.from_numpy(codes).view(torch.float8_e4m3fn).to(torch.float32).numpy()
+    ok = ~np.isnan(lib)
+    assert np.array_equal(np.isnan(deq), np.isnan(lib))
+    assert np.array_equal(deq[ok], lib[ok]) and np.array_equal(np.signbit(deq[ok]), np.signbit(lib[ok]))
+    # E8M0: byte e scales by 2^(e - 127); even 2^-127 times the smallest code stays exact in fp32
+    for e, scale in [(128, 2.0), (126, 0.5), (120, 2.0 ** -7), (0, 2.0 ** -127), (200, 2.0 ** 73)]:
+        r = rows.copy()
+        r[:, 0] = e
+        d = oracle.dequant_mxfp8(r, 32).reshape(-1)
+        assert np.array_equal(d[ok], (lib[ok].astype(np.float64) * scale).astype(np.float32)), e
+    r = rows.copy()
+    r[:, 0] = 255
+    assert np.all(np.isnan(oracle.dequant_mxfp8(r, 32)))
+    # two blocks per row: block b covers inputs 32 b .. 32 b + 31, byte j of a block is input j
+    two = np.zeros((1, 2, 33), dtype=np.uint8)
+    two[0, 0, 0], two[0, 1, 0] = 127, 130  # 1 and 8
+    two[0, :, 1:] = 0x38  # 1.0
+    two[0, 1, 32] = 0xC0  # block 1, input 31: -2.0
+    d2 = oracle.dequant_mxfp8(two.reshape(1, 66), 64)[0]
+    assert np.array_equal(d2, np.array([1.0] * 32 + [8.0] * 31 + [-16.0], dtype=np.float32))
+
+
+def test_mxfp8_quantiser_roundtrip():
+    gen = torch.Generator().manual_seed(13)
+    w = torch.randn((5, 2816), generator=gen) * 0.02
+    w[2, 32:64] = 0.0  # an all-zero block
+    # at scale 2^0 (amax 460 -> X = 8 - 8): 460 saturates to 448; -1.0625 and 1.1875 are ties between
+    # neighbours 1/8 apart (-> the even mantissa: -1.0, 1.25); 2^-10 and 3 2^-10 are ties on the
+    # subnormal grid (-> 0 and 2^-8); 300 rounds to 288 (step 32 above 256)
+    w[3, 0:32] = torch.tensor([460.0, -1.0625, 1.1875, 2.0 ** -10, 3 * 2.0 ** -10, 300.0] + [0.0] * 26)
+    b = synth.quantize_mxfp8(w)
+    assert b.shape == (5, 88, 33) and b.dtype == torch.uint8
+    deq = oracle.dequant_mxfp8(b.numpy().reshape(5, -1), 2816)
+    assert b[3, 0, 0].item() == 127
+    assert np.array_equal(deq[3, :6], np.array([448.0, -1.0, 1.25, 0.0, 2.0 ** -8, 288.0], dtype=np.float32))
+    assert np.all(deq[2, 32:64] == 0.0) and b[2, 1, 0].item() == 0
+    wn = w.numpy()
+    amax = np.abs(wn.reshape(5, 88, 32)).max(-1)
+    X = np.where(amax > 0, np.floor(np.log2(np.where(amax > 0, amax, 1.0))) - 8, -127)
+    assert np.array_equal(b[..., 0].numpy().astype(np.int64), (X + 127).astype(np.int64))
+    # the codes are torch's round-to-nearest-even E4M3 conversion of w / 2^X clamped to +-448 (the
+    # sign of a zero aside)
+    v = torch.from_numpy(wn.reshape(5, 88, 32) / np.exp2(X)[..., None]).clamp(-448.0, 448.0)
+    lib = v.to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+    mine = b[..., 1:].numpy()
+    assert np.array_equal(np.where(lib == 0x80, 0, lib), np.where(mine == 0x80, 0, mine))
+    # error: at most half a step, 2^-4 of the magnitude (2^-10 of the scale near zero), unless saturated
+    scale = np.repeat(2.0 ** X, 32, axis=1)
+    sat = np.abs(wn) > 448 * scale
+    err = np.abs(deq - wn)
+    assert np.all(err[~sat] <= np.maximum(2.0 ** -4 * np.abs(wn), 2.0 ** -10 * scale)[~sat] + 1e-30)
+    assert np.all(np.abs(deq[sat]) == (448 * scale)[sat])
+
+
+def test_mxfp8_layer_matches_dense_reference_of_dequantised_weights():
+    wl, x, w = small(T=12, E=6, K=2, D=256, F=192, seed=34, experts="mxfp8")
+    xn, wn = np_inputs(x, w)
+    o = oracle.moe_forward(wn, xn, 2, EPS)
+    wf = f64_weights({k: v for k, v in wn.items() if k in ("router_w", "router_gamma", "ffn_gamma")})
+    wf["router_bias"] = None
+    E, D, Fd = 6, 256, 192
+    gu = oracle.dequant_mxfp8(wn["mx8_gate_up"].reshape(E * 2 * Fd, -1), D)
+    dn = oracle.dequant_mxfp8(wn["mx8_down"].reshape(E * D, -1), Fd)
+    wf["w_gate_up"] = torch.from_numpy(gu.reshape(E, 2 * Fd, D)).double()
+    wf["w_down"] = torch.from_numpy(dn.reshape(E, D, Fd)).double()
+    ref, _, _ = dense_moe_fp64(bits_to_f64(xn), wf, 2, EPS)
+    assert rel_err(o["out"], ref.numpy()) <= 2e-5
+
+
 # ----------------------------------------------------------------------------- shapes printed on the pages
 
 def test_shapes_from_the_pages():
