@@ -10,7 +10,7 @@ create into the GEMMs' fragment order (--borrow reads them in place, row-major).
 Prints one JSON line: tokens/s, the roofline of the dominant kernel (gate_up, HBM-bound) measured with
 HIP events on the launch stream, and the CPU oracle timed on the host on a bounded sample.
 
-  python bench.py [--steps K] [--warmup W] [--workload canvas256|encode2304|int4|q8|mxfp4|canvas32|stack30]
+  python bench.py [--steps K] [--warmup W] [--workload canvas256|encode2304|int4|q8|mxfp4|mxfp8|canvas32|stack30]
 """
 import argparse
 import ctypes
@@ -72,9 +72,10 @@ def expert_bytes(wl):
     elif wl.experts == "q8_0":  # 34 bytes per block of 32 inputs
         gu = 2 * F * (D // 32) * 34
         dn = D * (F // 32) * 34
-    elif wl.experts == "mxfp4":  # 17 bytes per block of 32 inputs
-        gu = 2 * F * (D // 32) * 17
-        dn = D * (F // 32) * 17
+    elif wl.experts in ("mxfp4", "mxfp8"):  # 17 or 33 bytes per block of 32 inputs
+        blk = 17 if wl.experts == "mxfp4" else 33
+        gu = 2 * F * (D // 32) * blk
+        dn = D * (F // 32) * blk
     else:
         gu = 2 * F * D * 2
         dn = D * F * 2
@@ -173,8 +174,8 @@ def main():
     from expert_ffn_canvas_amd import dgmoe, synth
 
     wl = synth.WORKLOADS[args.workload]
-    if args.borrow and wl.experts in ("q8_0", "mxfp4"):
-        print(json.dumps({"error": "Q8_0 and MXFP4 experts are read from the packed copy only; drop --borrow"}))
+    if args.borrow and wl.experts in ("q8_0", "mxfp4", "mxfp8"):
+        print(json.dumps({"error": "Q8_0, MXFP4 and MXFP8 experts are read from the packed copy only; drop --borrow"}))
         sys.exit(2)
     dev = "cuda:0"
     torch.cuda.set_device(0)
@@ -273,7 +274,7 @@ def main():
     layer_bytes, flops, gate_up_bytes, down_bytes = algorithmic(wl, T, touched)
     step_s = ms_per_step / 1e3
     layer_gbps = layer_bytes * n_layers / step_s / 1e9  # stack: touched of layer 0 as the estimate
-    peak_tflops = F16_PEAK_TFLOPS if wl.experts in ("i4g128", "q8_0", "mxfp4") else BF16_PEAK_TFLOPS
+    peak_tflops = F16_PEAK_TFLOPS if wl.experts in ("i4g128", "q8_0") else BF16_PEAK_TFLOPS
     roofline = None
     if kern_us:
         # the dominant launch: gate_up, or the fused launch of both GEMMs
@@ -298,7 +299,7 @@ def main():
         "scaling": "weak",
         "vs_baseline": None,
         "dtype": {"i4g128": "int4-g128 weights, f16 MFMA", "q8_0": "q8_0 weights, f16 MFMA",
-                  "mxfp4": "mxfp4 weights, f16 MFMA"}.get(wl.experts, "bf16"),
+                  "mxfp4": "mxfp4 weights, bf16 MFMA", "mxfp8": "mxfp8 weights, bf16 MFMA"}.get(wl.experts, "bf16"),
         "data": "synthetic",
         "config": {"workload": wl.name, "T": T, "n_experts": wl.E, "top_k": wl.K, "d_model": wl.D,
                    "d_ff": wl.F, "experts": wl.experts, "act": wl.act, "router_bias": wl.bias or "none",

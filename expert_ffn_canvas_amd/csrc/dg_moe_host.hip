@@ -127,11 +127,14 @@ dg_status check_config(const dg_moe_config* c) {
   if (c->router_w_dtype != DG_F32 && c->router_w_dtype != DG_BF16)
     return fail(DG_ERR_DTYPE, "router_w_dtype %d: only DG_F32 or DG_BF16", c->router_w_dtype);
   if (c->expert_w_dtype != DG_BF16 && c->expert_w_dtype != DG_I4G128 && c->expert_w_dtype != DG_Q8_0 &&
-      c->expert_w_dtype != DG_MXFP4)
-    return fail(DG_ERR_DTYPE, "expert_w_dtype %d: only DG_BF16, DG_I4G128, DG_Q8_0 or DG_MXFP4", c->expert_w_dtype);
+      c->expert_w_dtype != DG_MXFP4 && c->expert_w_dtype != DG_MXFP8)
+    return fail(DG_ERR_DTYPE, "expert_w_dtype %d: only DG_BF16, DG_I4G128, DG_Q8_0, DG_MXFP4 or DG_MXFP8",
+                c->expert_w_dtype);
   if (c->flags & ~DG_MOE_PACK_WEIGHTS) return fail(DG_ERR_INVALID_ARG, "unknown config flags 0x%x", c->flags);
-  if ((c->expert_w_dtype == DG_Q8_0 || c->expert_w_dtype == DG_MXFP4) && !(c->flags & DG_MOE_PACK_WEIGHTS))
-    return fail(DG_ERR_DTYPE, "DG_Q8_0 and DG_MXFP4 experts are read from the packed copy only: set DG_MOE_PACK_WEIGHTS");
+  if ((c->expert_w_dtype == DG_Q8_0 || c->expert_w_dtype == DG_MXFP4 || c->expert_w_dtype == DG_MXFP8) &&
+      !(c->flags & DG_MOE_PACK_WEIGHTS))
+    return fail(DG_ERR_DTYPE,
+                "DG_Q8_0, DG_MXFP4 and DG_MXFP8 experts are read from the packed copy only: set DG_MOE_PACK_WEIGHTS");
   return DG_OK;
 }
 
@@ -172,10 +175,12 @@ ExpertBytes expert_bytes(const dg_moe_config& c) {
     b.dn = E * D * nks_f * 128;
     b.sgu = E * 2 * F * nks_d * 4 * 2;
     b.sdn = E * D * nks_f * 4 * 2;
-  } else if (c.expert_w_dtype == DG_MXFP4) {  // packed only: 64 code bytes and 4 scale bytes per (row, step)
+  } else if (c.expert_w_dtype == DG_MXFP4 || c.expert_w_dtype == DG_MXFP8) {
+    // packed only: 64 (MXFP4) or 128 (MXFP8) code bytes and 4 scale bytes per (row, 128-input step)
     const size_t nks_d = (D + 127) / 128, nks_f = (F + 127) / 128;
-    b.gu = E * 2 * F * nks_d * 64;
-    b.dn = E * D * nks_f * 64;
+    const size_t cb = c.expert_w_dtype == DG_MXFP4 ? 64 : 128;
+    b.gu = E * 2 * F * nks_d * cb;
+    b.dn = E * D * nks_f * cb;
     b.sgu = E * 2 * F * nks_d * 4;
     b.sdn = E * D * nks_f * 4;
   } else {
@@ -226,6 +231,7 @@ dg_status dg_moe_create(const dg_moe_config* cfg, const dg_moe_weights* w, void*
   const bool i4 = cfg->expert_w_dtype == DG_I4G128;
   const bool q8 = cfg->expert_w_dtype == DG_Q8_0;
   const bool mx4 = cfg->expert_w_dtype == DG_MXFP4;
+  const bool mx8 = cfg->expert_w_dtype == DG_MXFP8;
   if (!w->router_w || !w->router_gamma || !w->ffn_gamma || !w->w_gate_up || !w->w_down)
     return fail(DG_ERR_INVALID_ARG, "a required weight pointer is NULL");
   if (i4 && (!w->s_gate_up || !w->s_down)) return fail(DG_ERR_INVALID_ARG, "int4 weights need both scale tensors");
@@ -274,22 +280,21 @@ dg_status dg_moe_create(const dg_moe_config* cfg, const dg_moe_weights* w, void*
     char* p = static_cast<char*>(hd->packed);
     hd->w_gate_up = p;
     hd->w_down = p + round_up(eb.gu, 256);
-    const bool scaled = i4 || q8 || mx4;
+    const bool scaled = i4 || q8 || mx4 || mx8;
     hd->s_gate_up =
         scaled ? reinterpret_cast<const uint16_t*>(p + round_up(eb.gu, 256) + round_up(eb.dn, 256)) : nullptr;
     hd->s_down = scaled ? reinterpret_cast<const uint16_t*>(p + round_up(eb.gu, 256) + round_up(eb.dn, 256) +
                                                             round_up(eb.sgu, 256))
                         : nullptr;
     hipError_t c1, c2, c3 = hipSuccess, c4 = hipSuccess;
-    if (mx4) {  // MXFP4: codes and scale bytes in fragment order, per 128-input step
-      c1 = dg::launch_pack_mx4(static_cast<const uint8_t*>(w->w_gate_up),
-                               static_cast<uint8_t*>(const_cast<void*>(hd->w_gate_up)),
-                               reinterpret_cast<uint8_t*>(const_cast<uint16_t*>(hd->s_gate_up)), cfg->n_experts,
-                               2 * cfg->d_ff, cfg->d_model, stream);
-      c2 = dg::launch_pack_mx4(static_cast<const uint8_t*>(w->w_down),
-                               static_cast<uint8_t*>(const_cast<void*>(hd->w_down)),
-                               reinterpret_cast<uint8_t*>(const_cast<uint16_t*>(hd->s_down)), cfg->n_experts,
-                               cfg->d_model, cfg->d_ff, stream);
+    if (mx4 || mx8) {  // MXFP4 / MXFP8: codes and scale bytes in fragment order, per 128-input step
+      auto pack = mx4 ? dg::launch_pack_mx4 : dg::launch_pack_mx8;
+      c1 = pack(static_cast<const uint8_t*>(w->w_gate_up), static_cast<uint8_t*>(const_cast<void*>(hd->w_gate_up)),
+                reinterpret_cast<uint8_t*>(const_cast<uint16_t*>(hd->s_gate_up)), cfg->n_experts, 2 * cfg->d_ff,
+                cfg->d_model, stream);
+      c2 = pack(static_cast<const uint8_t*>(w->w_down), static_cast<uint8_t*>(const_cast<void*>(hd->w_down)),
+                reinterpret_cast<uint8_t*>(const_cast<uint16_t*>(hd->s_down)), cfg->n_experts, cfg->d_model,
+                cfg->d_ff, stream);
       hd->w_packed = 1;
     } else if (q8) {  // Q8_0: codes and scales in fragment order, per 128-input step
       c1 = dg::launch_pack_q8(static_cast<const uint8_t*>(w->w_gate_up),
@@ -380,6 +385,7 @@ static dg_status run_forward(dg_moe_handle hd, const void* x, void* out, int32_t
   const bool i4 = c.expert_w_dtype == DG_I4G128;
   const bool q8 = c.expert_w_dtype == DG_Q8_0;
   const bool mx4 = c.expert_w_dtype == DG_MXFP4;
+  const bool mx8 = c.expert_w_dtype == DG_MXFP8;
   // per-kernel start/stop events: norm, logits, permute, gate_up, down, combine
   dg::KernelEvents kev[6];
   if (events)
@@ -401,7 +407,7 @@ static dg_status run_forward(dg_moe_handle hd, const void* x, void* out, int32_t
   ra.bias = hd->has_bias ? hd->at<float>(L.bias) : nullptr;
   ra.gamma_e = hd->at<float>(L.gamma_e);
   ra.eps = c.rms_eps;
-  ra.h_f16 = (i4 || q8) ? 1 : 0;  // MXFP4 widens to bf16 (its block scales need bf16's exponent range)
+  ra.h_f16 = (i4 || q8) ? 1 : 0;  // MXFP4 / MXFP8 widen to bf16 (their block scales need bf16's exponent range)
   ra.h = L.fold ? nullptr : hd->at<uint16_t>(L.h);
   ra.rnorm = hd->at<float>(L.rnorm);
   ra.logits = hd->at<float>(L.logits);
@@ -469,6 +475,7 @@ static dg_status run_forward(dg_moe_handle hd, const void* x, void* out, int32_t
     fa.tile_done = pa.tile_done;
     fa.nb_gate_up = L.nb[0];
     e = mx4  ? dg::launch_gemm_fused_mx4(fa, stream, ev(3))
+        : mx8 ? dg::launch_gemm_fused_mx8(fa, stream, ev(3))
         : q8 ? dg::launch_gemm_fused_q8(fa, stream, ev(3))
         : i4 ? dg::launch_gemm_fused_i4(fa, stream, ev(3))
              : dg::launch_gemm_fused(fa, tall, stream, ev(3));

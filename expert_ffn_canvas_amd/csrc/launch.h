@@ -111,9 +111,9 @@ struct GemmArgs {
   const uint16_t* h;       // [T, D] expert input (bf16, or fp16 for quantised experts); the raw x when rnorm is set
   const float* rnorm;      // [T] r of each token when h is the raw x and (1 + gamma_e) is folded into
                            // w_gate_up: the gate and up sums are scaled by it; else null
-  const void* w_gate_up;   // bf16 [E, 2F, D], int4 bytes [E, 2F, D/2], or packed Q8_0 / MXFP4 codes
-  const void* w_down;      // bf16 [E, D, F], int4 bytes [E, D, F/2], or packed Q8_0 / MXFP4 codes
-  // scales: fp16 (int4, Q8_0), or E8M0 bytes (MXFP4) read through these pointers
+  const void* w_gate_up;   // bf16 [E, 2F, D], int4 bytes [E, 2F, D/2], or packed Q8_0 / MX codes
+  const void* w_down;      // bf16 [E, D, F], int4 bytes [E, D, F/2], or packed Q8_0 / MX codes
+  // scales: fp16 (int4, Q8_0), or E8M0 bytes (MXFP4, MXFP8) read through these pointers
   const uint16_t* s_gate_up;
   const uint16_t* s_down;
   uint16_t* act;           // [K T, F] gelu_tanh(gate) * up, expert-sorted rows
@@ -170,9 +170,20 @@ hipError_t launch_gemm_fused_q8(const FusedGemmArgs& f, hipStream_t stream, cons
 // padded with zero codes and scale bytes.
 hipError_t launch_pack_mx4(const uint8_t* blocks, uint8_t* pcodes, uint8_t* pscales, int E, int R, int K,
                            hipStream_t stream);
-// Both products with packed MXFP4 weights (fp16 expert input and activation)
+// Both products with packed MXFP4 weights (bf16 expert input and activation)
 // in one launch, as launch_gemm_fused.
 hipError_t launch_gemm_fused_mx4(const FusedGemmArgs& f, hipStream_t stream, const KernelEvents* ev);
+// Create-time relayout of MXFP8 expert weights (rows of K / 32 blocks of 33
+// bytes: E8M0 scale byte, 32 E4M3 codes in input order) into fragment order:
+// per (expert, 128-input step, 16-row panel), 2 KB of codes (lane n + 16 g:
+// 32 bytes of row n, two dwords per 32-input block holding inputs
+// 8 g .. 8 g + 7 in order) and 64 scale bytes [row][block]; a short last step
+// is padded with zero codes and scale bytes.
+hipError_t launch_pack_mx8(const uint8_t* blocks, uint8_t* pcodes, uint8_t* pscales, int E, int R, int K,
+                           hipStream_t stream);
+// Both products with packed MXFP8 weights (bf16 expert input and activation)
+// in one launch, as launch_gemm_fused.
+hipError_t launch_gemm_fused_mx8(const FusedGemmArgs& f, hipStream_t stream, const KernelEvents* ev);
 
 struct CombineArgs {
   const uint16_t* y;           // [K T, D] bf16 expert outputs, expert-sorted rows

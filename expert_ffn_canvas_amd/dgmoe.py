@@ -15,7 +15,7 @@ import os
 HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(HERE, "libdgmoe.so")
 
-DG_F32, DG_BF16, DG_F16, DG_I4G128, DG_Q8_0, DG_MXFP4 = 0, 1, 2, 3, 4, 5
+DG_F32, DG_BF16, DG_F16, DG_I4G128, DG_Q8_0, DG_MXFP4, DG_MXFP8 = 0, 1, 2, 3, 4, 5, 6
 DG_OK = 0
 DG_ERR_INVALID_ARG, DG_ERR_SHAPE, DG_ERR_DTYPE, DG_ERR_ALIGN = -1, -2, -3, -4
 DG_ERR_OOM, DG_ERR_HIP, DG_ERR_UNSUPPORTED = -5, -6, -7
@@ -166,8 +166,9 @@ class MoELayer:
         i4 = "q_gate_up" in weights
         q8 = "q8_gate_up" in weights  # Q8_0 blocks [E, rows, K/32, 34]; read from the packed copy only
         mx4 = "mx4_gate_up" in weights  # MXFP4 blocks [E, rows, K/32, 17]; read from the packed copy only
+        mx8 = "mx8_gate_up" in weights  # MXFP8 blocks [E, rows, K/32, 33]; read from the packed copy only
         E, D = rw.shape
-        key = "q_" if i4 else "q8_" if q8 else "mx4_" if mx4 else "w_"
+        key = "q_" if i4 else "q8_" if q8 else "mx4_" if mx4 else "mx8_" if mx8 else "w_"
         gu, dn = weights[key + "gate_up"], weights[key + "down"]
         F = gu.shape[1] // 2
         self.E, self.D, self.F = E, D, F
@@ -175,7 +176,7 @@ class MoELayer:
         self.act_dtype = act_dtype
         cfg = make_config(E=E, K=self.K, D=D, F=F, max_tokens=max_tokens, eps=eps, act=_dtype_code(
             torch.empty((), dtype=act_dtype)), router_w=_dtype_code(rw),
-            experts=DG_I4G128 if i4 else DG_Q8_0 if q8 else DG_MXFP4 if mx4 else DG_BF16,
+            experts=DG_I4G128 if i4 else DG_Q8_0 if q8 else DG_MXFP4 if mx4 else DG_MXFP8 if mx8 else DG_BF16,
             flags=DG_MOE_PACK_WEIGHTS if pack else 0)
         wts = dg_moe_weights(
             _ptr(rw), _ptr(weights["router_gamma"]), _ptr(weights.get("router_bias")), _ptr(weights["ffn_gamma"]),
@@ -188,7 +189,7 @@ class MoELayer:
         self.max_tokens = max_tokens
         # bf16 activations with packed bf16 experts: the expert norm rides on the gate_up weight and r, and the
         # forward runs no norm kernel (its two profiling events are then recorded back to back)
-        self.expert_norm_folded = bool(pack and not i4 and not q8 and not mx4 and act_dtype == torch.bfloat16)
+        self.expert_norm_folded = bool(pack and not (i4 or q8 or mx4 or mx8) and act_dtype == torch.bfloat16)
         # both GEMMs run in one launch, except for int4 experts read in place (the fused launch's profiling
         # events are the gate_up pair; the down pair is recorded back to back after it)
         self.gemms_fused = bool(pack or not i4)

@@ -60,8 +60,24 @@ extern "C" {
  * 255 is NaN) then 16 bytes of E2M1 codes (sign, two exponent bits with bias 1,
  * one mantissa bit: 0, 0.5, 1, 1.5, 2, 3, 4, 6), input j in the low nibble of
  * byte j for j < 16 and in the high nibble of byte j - 16 otherwise; each code
- * stands for its value times the block scale. */
-typedef enum dg_dtype { DG_F32 = 0, DG_BF16 = 1, DG_F16 = 2, DG_I4G128 = 3, DG_Q8_0 = 4, DG_MXFP4 = 5 } dg_dtype;
+ * stands for its value times the block scale.
+ * DG_MXFP8: OCP Microscaling MXFP8 with E4M3 elements, read for the FP8 builds
+ * of the same card (Credits: FP4 and FP8 tensor types): each run of 32
+ * consecutive inputs of a row is 33 bytes, an E8M0 scale byte e (as above)
+ * then 32 E4M3 codes in input order (sign, four exponent bits with bias 7,
+ * three mantissa bits; exponent field 0 is subnormal, m 2^-9; 0x7f and 0xff
+ * are NaN; 448 the largest); each code stands for its value times the block
+ * scale. Scale bytes below 3 can put the smallest codes under bf16's smallest
+ * subnormal (2^-133); the GPU then rounds those weights to it. */
+typedef enum dg_dtype {
+  DG_F32 = 0,
+  DG_BF16 = 1,
+  DG_F16 = 2,
+  DG_I4G128 = 3,
+  DG_Q8_0 = 4,
+  DG_MXFP4 = 5,
+  DG_MXFP8 = 6
+} dg_dtype;
 
 typedef enum dg_status {
   DG_OK = 0,
@@ -98,9 +114,9 @@ typedef struct dg_moe_config {
   float rms_eps;          /* eps of both RMSNorms (> 0)                                */
   int32_t act_dtype;      /* x / out / addend: DG_F32 or DG_BF16                       */
   int32_t router_w_dtype; /* router weight: DG_F32 or DG_BF16                          */
-  int32_t expert_w_dtype; /* expert weights: DG_BF16, DG_I4G128, DG_Q8_0 or DG_MXFP4
-                             (Q8_0 and MXFP4 need DG_MOE_PACK_WEIGHTS, else
-                             DG_ERR_DTYPE)                                            */
+  int32_t expert_w_dtype; /* expert weights: DG_BF16, DG_I4G128, DG_Q8_0, DG_MXFP4 or
+                             DG_MXFP8 (the last three need DG_MOE_PACK_WEIGHTS,
+                             else DG_ERR_DTYPE)                                       */
   uint32_t flags;         /* DG_MOE_PACK_WEIGHTS                                       */
 } dg_moe_config;
 
@@ -112,9 +128,10 @@ typedef struct dg_moe_weights {
   const float* ffn_gamma;     /* [D] fp32; the expert-input norm multiplies by (1 + gamma)  */
   const void* w_gate_up;      /* bf16 [E, 2F, D]: rows 0..F-1 gate, F..2F-1 up;
                                  int4: uint8 [E, 2F, D/2]; Q8_0: uint8 [E, 2F, D/32, 34];
-                                 MXFP4: uint8 [E, 2F, D/32, 17]                            */
+                                 MXFP4: uint8 [E, 2F, D/32, 17]; MXFP8: [E, 2F, D/32, 33]  */
   const void* w_down;         /* bf16 [E, D, F]; int4: uint8 [E, D, F/2];
-                                 Q8_0: uint8 [E, D, F/32, 34]; MXFP4: uint8 [E, D, F/32, 17] */
+                                 Q8_0: uint8 [E, D, F/32, 34]; MXFP4: uint8 [E, D, F/32, 17];
+                                 MXFP8: uint8 [E, D, F/32, 33]                             */
   const uint16_t* s_gate_up;  /* int4 only: fp16 [E, 2F, D/128]                            */
   const uint16_t* s_down;     /* int4 only: fp16 [E, D, ceil(F/128)]                       */
 } dg_moe_weights;
@@ -138,8 +155,8 @@ typedef struct dg_moe_s* dg_moe_handle;
  * pointers are kept and must stay valid and unmodified for the handle's
  * lifetime; with DG_MOE_PACK_WEIGHTS they are copied (in 1 KB fragment
  * blocks of 16 rows x 32 inputs, or 16 rows x 128 int4 inputs, or 2 KB of
- * 16 rows x 128 Q8_0 codes plus their 64 scales, or 1 KB of 16 rows x 128
- * MXFP4 codes plus their 64 scale bytes), after which
+ * 16 rows x 128 Q8_0 codes plus their 64 scales, or 1 KB (MXFP4) or 2 KB
+ * (MXFP8) of 16 rows x 128 codes plus their 64 scale bytes), after which
  * the caller's expert buffers are no longer read. router_gamma is folded into the handle's copy of the router
  * weight (W_r diag(1 + router_gamma), in fp32 precision); router_bias and
  * ffn_gamma are always copied. Work is enqueued on `stream` and the call

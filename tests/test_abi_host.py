@@ -77,10 +77,11 @@ def _weights(align=16):
     ("act_dtype", dgmoe.DG_F16, dgmoe.DG_ERR_DTYPE),
     ("router_w_dtype", dgmoe.DG_I4G128, dgmoe.DG_ERR_DTYPE),
     ("expert_w_dtype", dgmoe.DG_F32, dgmoe.DG_ERR_DTYPE),
-    ("expert_w_dtype", 6, dgmoe.DG_ERR_DTYPE),
-    # Q8_0 blocks are read from the packed copy only: without DG_MOE_PACK_WEIGHTS it is refused
+    ("expert_w_dtype", 7, dgmoe.DG_ERR_DTYPE),
+    # Q8_0 and MX blocks are read from the packed copy only: without DG_MOE_PACK_WEIGHTS they are refused
     ("expert_w_dtype", dgmoe.DG_Q8_0, dgmoe.DG_ERR_DTYPE),
     ("expert_w_dtype", dgmoe.DG_MXFP4, dgmoe.DG_ERR_DTYPE),
+    ("expert_w_dtype", dgmoe.DG_MXFP8, dgmoe.DG_ERR_DTYPE),
     ("flags", 0x80, dgmoe.DG_ERR_INVALID_ARG),
     ("struct_size", 12, dgmoe.DG_ERR_INVALID_ARG),
 ])

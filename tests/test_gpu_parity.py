@@ -188,6 +188,40 @@ def test_mxfp4_small(E, K, D, F, T):
     print(f"err {r['err']:.3e} near-ties {r['near_ties']}")
 
 
+def test_mxfp8():
+    wl = synth.WORKLOADS["mxfp8"]
+    _say(f"{wl.name} T={wl.T} pack=True")
+    inp = synth.make_inputs(wl, device="cuda")
+    w = inp["layers"][0]
+    layer = _layer(w, wl.T, torch.bfloat16, pack=True)
+    rng = np.random.default_rng(4)
+    tok = np.unique(np.concatenate([[0, wl.T - 1], rng.choice(wl.T, 100, replace=False)]))
+    r = layer_parity(layer, inp["x"], oracle_weights(w), wl.K, tokens=tok)
+    print(f"err {r['err']:.3e} near-ties {r['near_ties']}")
+
+
+@pytest.mark.parametrize("E,K,D,F,T,jitter", [
+    (12, 3, 256, 192, 50, 0),   # down K = 192: a last 128-input step holding two blocks
+    (8, 4, 256, 192, 200, 6),   # tiles of up to 64 rows; every block's scale byte moved by -6..6
+    (6, 2, 128, 64, 37, 0),     # gate_up K = 128 (one step), down K = 64 (a lone short step)
+    (4, 2, 384, 320, 300, 3),   # gate_up three steps, down two full steps and a short one
+])
+def test_mxfp8_small(E, K, D, F, T, jitter):
+    _say(f"mxfp8 small E={E} K={K} D={D} F={F} T={T} jitter={jitter}")
+    wl = synth.small_workload(T=T, E=E, K=K, D=D, F=F, experts="mxfp8", bias="zipf", seed=60 + T)
+    inp = synth.make_inputs(wl, device="cuda")
+    w = inp["layers"][0]
+    if jitter:  # per-block scales far apart, so a block read with another block's scale shows
+        gen = torch.Generator(device="cpu").manual_seed(T)
+        for key in ("mx8_gate_up", "mx8_down"):
+            sc = w[key][..., 0].to(torch.int32)
+            off = torch.randint(-jitter, jitter + 1, sc.shape, generator=gen).to(sc.device)
+            w[key][..., 0] = (sc + off).clamp(1, 254).to(torch.uint8)
+    layer = _layer(w, T, torch.bfloat16, K=K, pack=True)
+    r = layer_parity(layer, inp["x"], oracle_weights(w), K)
+    print(f"err {r['err']:.3e} near-ties {r['near_ties']}")
+
+
 # ----------------------------------------------------------------------------- edge cases
 
 @pytest.mark.parametrize("T", [1, 15, 17, 255, 257])
