@@ -17,6 +17,13 @@ the canvas, two canvases, 30 MoE layers):
   stack30    T=512,  30 layers with their own bf16 weights, Zipf skew,
              a N(0, 0.5) offset [T, D] added after each layer
 
+Canvas output stage (tied LM head + entropy), a workload of its own:
+
+  head256    T=256 canvas positions, vocab 262144, d_model 2816, bf16 hidden
+             states and embedding table; each position leans towards a random
+             token by a logit margin drawn uniformly from [0, 24], so the
+             per-position entropies span near zero to near ln(vocab)
+
 Draw order from one torch generator seeded with the workload's seed:
 x, then per layer: router weight, router gamma, expert-norm gamma, gate_up,
 down (then, for the stack, the offset of that layer). Normal draws are fp32
@@ -257,6 +264,42 @@ def make_inputs(wl: Workload, device="cpu", layers: int | None = None, T: int | 
             d = _randn((T, wl.D), wl.delta_std, gen, device)
             out["deltas"].append(d.to(torch.bfloat16) if wl.act == "bf16" else d)
     return out
+
+
+@dataclass
+class HeadWorkload:
+    name: str
+    T: int
+    V: int
+    D: int
+    seed: int
+    max_margin: float = 24.0
+
+
+HEAD_WORKLOADS = {
+    "head256": HeadWorkload("head256", 256, 262144, D_MODEL, 8),
+}
+
+
+def make_head_inputs(hw: HeadWorkload, device="cpu"):
+    """Embedding table emb [V, D] ~ N(0, 0.02) and canvas hidden states h [T, D], both bf16.
+
+    Draw order from one generator seeded with hw.seed: emb, then z ~ N(0, 1) [T, D], then a target
+    token y_t and a margin L_t ~ U(0, max_margin) per position (position 0 gets margin 0 and the last
+    position max_margin). h_t = z_t + L_t emb[y_t] / |emb[y_t]|^2, so the target's logit is raised
+    by about L_t over the rest. Returns dict(emb, h, target, margin).
+    """
+    gen = torch.Generator(device=device).manual_seed(hw.seed)
+    emb = _randn((hw.V, hw.D), 0.02, gen, device).to(torch.bfloat16)
+    z = torch.randn((hw.T, hw.D), generator=gen, device=device, dtype=torch.float32)
+    y = torch.randint(0, hw.V, (hw.T,), generator=gen, device=device)
+    L = torch.rand((hw.T,), generator=gen, device=device, dtype=torch.float32) * hw.max_margin
+    if hw.T > 0:
+        L[0] = 0.0
+        L[-1] = hw.max_margin
+    ey = emb[y].to(torch.float32)
+    h = (z + L.unsqueeze(1) * ey / (ey * ey).sum(dim=1, keepdim=True)).to(torch.bfloat16)
+    return {"emb": emb, "h": h, "target": y, "margin": L}
 
 
 def small_workload(name="tiny", T=16, E=6, K=2, D=128, F=64, act="bf16", router_w="bf16",

@@ -9,7 +9,7 @@ import os
 
 import numpy as np
 
-from .build import LIB, SRC, build
+from .build import LIB, SOURCES, build
 
 _lib = None
 
@@ -24,7 +24,7 @@ def load():
     global _lib
     if _lib is not None:
         return _lib
-    if not os.path.exists(LIB) or os.path.getmtime(LIB) < os.path.getmtime(SRC):
+    if not os.path.exists(LIB) or os.path.getmtime(LIB) < max(os.path.getmtime(s) for s in SOURCES):
         build()
     lib = ctypes.CDLL(LIB)
     lib.oracle_gelu_tanh_f32.restype = ctypes.c_float
@@ -52,6 +52,8 @@ def load():
                                        _p, _p, _p, _p, _i, _i, _p, _p, _p, _p, _p, _i]
     lib.oracle_expert_ffn.restype = _i
     lib.oracle_expert_ffn.argtypes = [_i, _i, _i, _i, _i, _p, _p, _p, _p, _p, _i, _p]
+    lib.oracle_canvas_head.restype = _i
+    lib.oracle_canvas_head.argtypes = [_i, _i, _i, _p, _p, _d, _p, _i, _p, _p, _p, _p, _i]
     lib.oracle_round_bf16.restype = None
     lib.oracle_round_bf16.argtypes = [_p, _p, ctypes.c_int64]
     _lib = lib
@@ -224,3 +226,27 @@ def expert_ffn(w, e, h):
     if rc != 0:
         raise ValueError("bad expert id")
     return y
+
+
+def canvas_head(h, emb, beta=1.0, tokens=None, want_logits=False, n_threads=0):
+    """Canvas output stage on the host: h uint16 bf16 bits [T, D], emb uint16 bf16 bits [V, D].
+
+    Returns dict(entropy [n] f64, argmax [n] int32, gap [n] f64, logits [n, V] f64 or None) for the
+    positions `tokens` (all T if None).
+    """
+    h = np.ascontiguousarray(h, dtype=np.uint16)
+    emb = np.ascontiguousarray(emb, dtype=np.uint16)
+    T, D = h.shape
+    V = emb.shape[0]
+    assert emb.shape[1] == D
+    tok = None if tokens is None else np.ascontiguousarray(tokens, dtype=np.int32)
+    n = T if tok is None else len(tok)
+    ent = np.empty(n, dtype=np.float64)
+    am = np.empty(n, dtype=np.int32)
+    gap = np.empty(n, dtype=np.float64)
+    lg = np.empty((n, V), dtype=np.float64) if want_logits else None
+    rc = load().oracle_canvas_head(T, V, D, _ptr(h), _ptr(emb), float(beta), _ptr(tok), n, _ptr(lg), _ptr(ent),
+                                   _ptr(am), _ptr(gap), n_threads)
+    if rc != 0:
+        raise ValueError("oracle_canvas_head: bad argument")
+    return {"entropy": ent, "argmax": am, "gap": gap, "logits": lg}

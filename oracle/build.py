@@ -9,12 +9,13 @@ import subprocess
 
 HERE = os.path.dirname(os.path.abspath(__file__))
 SRC = os.path.join(HERE, "dg_moe_oracle.cpp")
+SOURCES = [SRC, os.path.join(HERE, "canvas_head_oracle.cpp")]
 LIB = os.path.join(HERE, "liboracle.so")
 
 
 def build(verbose: bool = False) -> str:
     cmd = ["g++", "-O2", "-std=c++17", "-fopenmp", "-ffp-contract=off", "-fPIC", "-shared",
-           SRC, "-o", LIB + ".tmp"]
+           *SOURCES, "-o", LIB + ".tmp"]
     if verbose:
         print(" ".join(cmd))
     subprocess.run(cmd, check=True)

@@ -594,6 +594,83 @@ def test_mxfp8_layer_matches_dense_reference_of_dequantised_weights():
     assert rel_err(o["out"], ref.numpy()) <= 2e-5
 
 
+# ----------------------------------------------------------------------------- canvas output stage
+
+
+def _head_small(T=7, V=600, D=96, seed=5, max_margin=24.0):
+    hw = synth.HeadWorkload("t", T, V, D, seed, max_margin)
+    inp = synth.make_head_inputs(hw)
+    return synth.to_numpy_bits(inp["h"]), synth.to_numpy_bits(inp["emb"])
+
+
+def test_canvas_head_logits_match_a_library_matmul():
+    h, emb = _head_small()
+    r = oracle.canvas_head(h, emb, want_logits=True)
+    ref = (bits_to_f64(h) @ bits_to_f64(emb).T).numpy()  # a library fp64 matmul of the exact bf16 values
+    assert np.max(np.abs(r["logits"] - ref)) <= 1e-12 * np.max(np.abs(ref))
+    # argmax (lowest id on ties) and the top-1 / top-2 gap against numpy
+    assert np.array_equal(r["argmax"], np.argmax(ref, axis=1))
+    srt = np.sort(ref, axis=1)
+    assert np.allclose(r["gap"], srt[:, -1] - srt[:, -2], rtol=0, atol=1e-12)
+
+
+@pytest.mark.parametrize("beta", [1.0, 1 / 0.8, 1 / 0.4])
+def test_canvas_head_entropy_matches_library_routines(beta):
+    from scipy.special import softmax
+    from scipy.stats import entropy
+    h, emb = _head_small(seed=6)
+    r = oracle.canvas_head(h, emb, beta=beta, want_logits=True)
+    ref = entropy(softmax(beta * r["logits"], axis=1), axis=1)  # nats
+    assert np.max(np.abs(r["entropy"] - ref)) <= 1e-10
+    assert np.all(r["entropy"] >= 0) and np.all(r["entropy"] <= np.log(600) + 1e-12)
+
+
+def test_canvas_head_closed_forms():
+    D, V = 64, 50
+    gen = torch.Generator().manual_seed(9)
+    emb = torch.randn((V, D), generator=gen).to(torch.bfloat16)
+    # h = 0: every logit is 0, the softmax is uniform, H = ln V, the argmax is id 0, the gap 0
+    h0 = torch.zeros((1, D), dtype=torch.bfloat16)
+    r = oracle.canvas_head(synth.to_numpy_bits(h0), synth.to_numpy_bits(emb))
+    assert abs(r["entropy"][0] - math.log(V)) <= 1e-12 and r["argmax"][0] == 0 and r["gap"][0] == 0.0
+    # two tokens only, logits 0 and a: H = ln(1 + e^-a) + a e^-a / (1 + e^-a)
+    e2 = torch.zeros((2, D), dtype=torch.bfloat16)
+    e2[1, 0] = 1.0
+    for a in [0.5, 2.0, 7.25]:
+        h = torch.zeros((1, D), dtype=torch.bfloat16)
+        h[0, 0] = a
+        r = oracle.canvas_head(synth.to_numpy_bits(h), synth.to_numpy_bits(e2))
+        want = math.log1p(math.exp(-a)) + a * math.exp(-a) / (1 + math.exp(-a))
+        assert abs(r["entropy"][0] - want) <= 1e-12 and r["argmax"][0] == 1 and r["gap"][0] == a
+    # two equal maxima far above the rest: H -> ln 2, the argmax the lower id
+    e3 = torch.zeros((V, D), dtype=torch.bfloat16)
+    e3[17, 1] = 1.0
+    e3[9, 1] = 1.0
+    h = torch.zeros((1, D), dtype=torch.bfloat16)
+    h[0, 1] = 60.0
+    r = oracle.canvas_head(synth.to_numpy_bits(h), synth.to_numpy_bits(e3))
+    assert abs(r["entropy"][0] - math.log(2)) <= 1e-12 and r["argmax"][0] == 9 and r["gap"][0] == 0.0
+    # one logit 80 above the rest: H ~ 0, and beta scales the margin
+    e3[9, 1] = 0.0
+    r = oracle.canvas_head(synth.to_numpy_bits(h), synth.to_numpy_bits(e3), beta=0.1)
+    # logits: 60 on id 17, 0 elsewhere; at beta 0.1 the margin is 6 over V - 1 equal others
+    p1 = 1 / (1 + (V - 1) * math.exp(-6.0))
+    q = (1 - p1) / (V - 1)
+    want = -(p1 * math.log(p1) + (V - 1) * q * math.log(q))
+    assert abs(r["entropy"][0] - want) <= 1e-12 and r["argmax"][0] == 17
+
+
+def test_canvas_head_input_recipe():
+    # the margin puts the target on top once it clears the rest, and the entropies spread out
+    hw = synth.HeadWorkload("t", 24, 4096, 256, 11)
+    inp = synth.make_head_inputs(hw)
+    r = oracle.canvas_head(synth.to_numpy_bits(inp["h"]), synth.to_numpy_bits(inp["emb"]))
+    big = inp["margin"].numpy() > 16
+    assert np.all(r["argmax"][big] == inp["target"].numpy()[big])
+    assert r["entropy"][0] > 0.8 * math.log(4096) and r["entropy"][-1] < 1e-3
+    assert np.min(r["entropy"]) < 0.1 and np.max(r["entropy"]) > 7.0
+
+
 # ----------------------------------------------------------------------------- shapes printed on the pages
 
 def test_shapes_from_the_pages():
