@@ -12,7 +12,7 @@ ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libdgmoe.so")
 SOURCES = ["dg_moe_host.hip", "router.hip", "permute.hip", "gemm_bf16.hip", "gemm_i4.hip", "gemm_q8.hip",
-           "gemm_mx.hip", "combine.hip"]
+           "gemm_mx.hip", "combine.hip", "head.hip"]
 
 HIPCC_FLAGS = [
     "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-shared",

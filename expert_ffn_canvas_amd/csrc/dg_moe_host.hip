@@ -9,6 +9,9 @@
 //   -> down grouped GEMM (x routing weight)
 //   -> combine back to token order.
 //
+// It also holds the host side of include/dg_head.h, the canvas output stage
+// (tied LM head and softmax entropy): validation, its workspace, its launches.
+//
 // Nothing in a forward allocates, synchronises or reads device data back.
 #include <hip/hip_runtime.h>
 
@@ -20,6 +23,7 @@
 #include <string>
 
 #include "dg_common.h"
+#include "dg_head.h"
 #include "dg_moe.h"
 #include "launch.h"
 
@@ -558,6 +562,166 @@ dg_status dg_moe_destroy(dg_moe_handle hd) {
   delete hd;
   if (e1 != hipSuccess) return hip_fail(e1, "hipFree(workspace)");
   if (e2 != hipSuccess) return hip_fail(e2, "hipFree(packed weights)");
+  return ok();
+}
+
+}  // extern "C"
+
+// ---------------------------------------------------------------------------
+// Canvas output stage
+
+struct dg_head_s {
+  dg_head_config cfg;
+  const uint16_t* emb;
+  char* ws;
+  size_t nvb;  // vocabulary tiles of 256
+};
+
+namespace {
+
+constexpr int kHeadVocabTile = 256;
+
+dg_status check_head_config(const dg_head_config* c) {
+  if (!c) return fail(DG_ERR_INVALID_ARG, "config is NULL");
+  if (c->struct_size != sizeof(dg_head_config))
+    return fail(DG_ERR_INVALID_ARG, "struct_size %u != %zu", c->struct_size, sizeof(dg_head_config));
+  if (c->vocab < 1 || c->vocab > (1 << 24)) return fail(DG_ERR_SHAPE, "vocab %d not in [1, 2^24]", c->vocab);
+  if (c->d_model < 64 || c->d_model > 16384 || c->d_model % 64)
+    return fail(DG_ERR_SHAPE, "d_model %d must be a multiple of 64 in [64, 16384]", c->d_model);
+  if (c->max_tokens < 1 || c->max_tokens > (1 << 20))
+    return fail(DG_ERR_SHAPE, "max_tokens %d not in [1, 2^20]", c->max_tokens);
+  if (c->h_dtype != DG_BF16) return fail(DG_ERR_DTYPE, "h_dtype %d: only DG_BF16", c->h_dtype);
+  if (c->emb_dtype != DG_BF16) return fail(DG_ERR_DTYPE, "emb_dtype %d: only DG_BF16", c->emb_dtype);
+  if (c->flags != 0) return fail(DG_ERR_INVALID_ARG, "unknown config flags 0x%x", c->flags);
+  return DG_OK;
+}
+
+size_t head_nvb(const dg_head_config& c) { return ((size_t)c.vocab + kHeadVocabTile - 1) / kHeadVocabTile; }
+
+// Five arrays of nvb x max_tokens 4-byte partials, each 256-byte aligned.
+size_t head_part_bytes(const dg_head_config& c) { return round_up(head_nvb(c) * c.max_tokens * 4, 256); }
+
+bool spans_overlap(const void* a, size_t na, const void* b, size_t nb) {
+  if (!a || !b) return false;
+  const uintptr_t x = reinterpret_cast<uintptr_t>(a), y = reinterpret_cast<uintptr_t>(b);
+  return x < y + nb && y < x + na;
+}
+
+dg_status head_launch(dg_head_handle hd, const void* h, int32_t T, float beta, float* logits, float* entropy,
+                      int32_t* argmax, float* mean_entropy, void* const* events, void* stream_v) {
+  if (!hd) return fail(DG_ERR_INVALID_ARG, "handle is NULL");
+  if (!h || !entropy || !argmax) return fail(DG_ERR_INVALID_ARG, "h, entropy or argmax is NULL");
+  if (!(beta > 0.0f) || !std::isfinite(beta)) return fail(DG_ERR_INVALID_ARG, "beta must be finite and > 0");
+  const dg_head_config& c = hd->cfg;
+  if (T < 0 || T > c.max_tokens) return fail(DG_ERR_SHAPE, "T = %d not in [0, max_tokens = %d]", T, c.max_tokens);
+  if (!aligned16(h)) return fail(DG_ERR_ALIGN, "h is not 16-byte aligned");
+  const void* outs[] = {logits, entropy, argmax, mean_entropy};
+  for (const void* p : outs)
+    if (p && (reinterpret_cast<uintptr_t>(p) & 3u)) return fail(DG_ERR_ALIGN, "output %p is not 4-byte aligned", p);
+  const size_t nh = (size_t)T * c.d_model * 2;
+  const size_t sizes[] = {(size_t)T * c.vocab * 4, (size_t)T * 4, (size_t)T * 4, 4};
+  for (int i = 0; i < 4; ++i) {
+    if (spans_overlap(outs[i], sizes[i], h, nh)) return fail(DG_ERR_INVALID_ARG, "an output overlaps h");
+    for (int j = i + 1; j < 4; ++j)
+      if (spans_overlap(outs[i], sizes[i], outs[j], sizes[j])) return fail(DG_ERR_INVALID_ARG, "outputs overlap");
+  }
+  if (events) {
+    if (T == 0) return fail(DG_ERR_INVALID_ARG, "a profiled forward needs T > 0");
+    for (int i = 0; i < 6; ++i)
+      if (!events[i]) return fail(DG_ERR_INVALID_ARG, "event %d is NULL", i);
+  }
+  if (T == 0) return ok();
+  hipStream_t stream = static_cast<hipStream_t>(stream_v);
+  dg::HeadArgs a{};
+  a.h = static_cast<const uint16_t*>(h);
+  a.emb = hd->emb;
+  a.T = T;
+  a.V = c.vocab;
+  a.D = c.d_model;
+  a.beta = beta;
+  a.logits = logits;
+  a.entropy = entropy;
+  a.argmax = argmax;
+  a.mean_entropy = mean_entropy;
+  const size_t pb = head_part_bytes(c);
+  // partials laid out [nvb][T] for this T (a prefix of each array)
+  a.part_m = reinterpret_cast<float*>(hd->ws);
+  a.part_s = reinterpret_cast<float*>(hd->ws + pb);
+  a.part_u = reinterpret_cast<float*>(hd->ws + 2 * pb);
+  a.part_best = reinterpret_cast<float*>(hd->ws + 3 * pb);
+  a.part_id = reinterpret_cast<int32_t*>(hd->ws + 4 * pb);
+  dg::KernelEvents kev[3];
+  if (events)
+    for (int i = 0; i < 3; ++i) {
+      kev[i].start = static_cast<hipEvent_t>(events[2 * i]);
+      kev[i].stop = static_cast<hipEvent_t>(events[2 * i + 1]);
+    }
+  hipError_t e = dg::launch_head(a, stream, events ? kev : nullptr);
+  if (e != hipSuccess) return hip_fail(e, "output stage launch");
+  if (events && !mean_entropy) {
+    e = hipEventRecord(kev[2].start, stream);
+    if (e == hipSuccess) e = hipEventRecord(kev[2].stop, stream);
+    if (e != hipSuccess) return hip_fail(e, "event record");
+  }
+  return ok();
+}
+
+}  // namespace
+
+extern "C" {
+
+uint64_t dg_head_workspace_bytes(const dg_head_config* cfg) {
+  if (check_head_config(cfg) != DG_OK) return 0;
+  return 5 * (uint64_t)head_part_bytes(*cfg);
+}
+
+dg_status dg_head_create(const dg_head_config* cfg, const void* emb, dg_head_handle* out) {
+  if (out) *out = nullptr;
+  dg_status st = check_head_config(cfg);
+  if (st != DG_OK) return st;
+  if (!emb || !out) return fail(DG_ERR_INVALID_ARG, "emb or out is NULL");
+  if (!aligned16(emb)) return fail(DG_ERR_ALIGN, "emb is not 16-byte aligned");
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
+  hipDeviceProp_t prop;
+  e = hipGetDeviceProperties(&prop, dev);
+  if (e != hipSuccess) return hip_fail(e, "hipGetDeviceProperties");
+  if (std::strncmp(prop.gcnArchName, "gfx950", 6) != 0)
+    return fail(DG_ERR_UNSUPPORTED, "device %d is %s; this library is built for gfx950", dev, prop.gcnArchName);
+  dg_head_s* hd = new (std::nothrow) dg_head_s();
+  if (!hd) return fail(DG_ERR_OOM, "host allocation failed");
+  hd->cfg = *cfg;
+  hd->emb = static_cast<const uint16_t*>(emb);
+  hd->nvb = head_nvb(*cfg);
+  const size_t bytes = 5 * head_part_bytes(*cfg);
+  e = hipMalloc(reinterpret_cast<void**>(&hd->ws), bytes);
+  if (e != hipSuccess) {
+    delete hd;
+    (void)hipGetLastError();
+    return fail(DG_ERR_OOM, "workspace of %zu bytes: %s", bytes, hipGetErrorString(e));
+  }
+  *out = hd;
+  return ok();
+}
+
+dg_status dg_head_forward(dg_head_handle hd, const void* h, int32_t T, float beta, float* logits, float* entropy,
+                          int32_t* argmax, float* mean_entropy, void* stream) {
+  return head_launch(hd, h, T, beta, logits, entropy, argmax, mean_entropy, nullptr, stream);
+}
+
+dg_status dg_head_forward_profiled(dg_head_handle hd, const void* h, int32_t T, float beta, float* logits,
+                                   float* entropy, int32_t* argmax, float* mean_entropy, void* const* events,
+                                   void* stream) {
+  if (!events) return fail(DG_ERR_INVALID_ARG, "events is NULL");
+  return head_launch(hd, h, T, beta, logits, entropy, argmax, mean_entropy, events, stream);
+}
+
+dg_status dg_head_destroy(dg_head_handle hd) {
+  if (!hd) return ok();
+  hipError_t e = hd->ws ? hipFree(hd->ws) : hipSuccess;
+  delete hd;
+  if (e != hipSuccess) return hip_fail(e, "hipFree");
   return ok();
 }
 

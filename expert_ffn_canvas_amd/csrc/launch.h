@@ -197,4 +197,27 @@ struct CombineArgs {
 };
 hipError_t launch_combine(const CombineArgs& a, hipStream_t stream, const KernelEvents* ev);
 
+// Canvas output stage (tied LM head + softmax entropy), all device pointers.
+struct HeadArgs {
+  const uint16_t* h;    // [T, D] bf16
+  const uint16_t* emb;  // [V, D] bf16
+  int T, V, D;
+  float beta;           // inverse temperature of the softmax
+  float* logits;        // [T, V] fp32 or null
+  float* entropy;       // [T]
+  int32_t* argmax;      // [T]
+  float* mean_entropy;  // [1] or null
+  // per (vocabulary tile of 256, position) softmax partials, [ceil(V/256)][T]
+  float* part_m;
+  float* part_s;
+  float* part_u;
+  float* part_best;
+  int32_t* part_id;
+};
+
+// The stage: logits + per-tile partials, the merge per position, the mean
+// (skipped when mean_entropy is null). ev, if not null, points at three
+// KernelEvents, one per launch.
+hipError_t launch_head(const HeadArgs& a, hipStream_t stream, const KernelEvents* ev);
+
 }  // namespace dg

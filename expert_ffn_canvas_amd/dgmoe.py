@@ -1,8 +1,8 @@
-"""ctypes binding of libdgmoe.so (include/dg_moe.h): argument marshalling only.
+"""ctypes binding of libdgmoe.so (include/dg_moe.h, include/dg_head.h): argument marshalling only.
 
-The C entry points are exposed under their own names. `MoELayer` is a small
-convenience wrapper that keeps torch tensors (device memory) alive next to a
-handle; every step of the layer runs in the HIP library.
+The C entry points are exposed under their own names. `MoELayer` and
+`CanvasHead` are small convenience wrappers that keep torch tensors (device
+memory) alive next to a handle; every step runs in the HIP library.
 
 Importing this module loads the library and fails loudly if it has not been
 built: there is no CPU fallback.
@@ -24,7 +24,9 @@ DG_FWD_ADD_INPUT = 0x1
 ABI_VERSION = 1
 
 EXPORTED = ("dg_moe_create", "dg_moe_forward", "dg_moe_forward_debug", "dg_moe_forward_profiled", "dg_moe_destroy",
-            "dg_moe_status_string", "dg_moe_last_error", "dg_moe_abi_version", "dg_moe_workspace_bytes")
+            "dg_moe_status_string", "dg_moe_last_error", "dg_moe_abi_version", "dg_moe_workspace_bytes",
+            "dg_head_create", "dg_head_forward", "dg_head_forward_profiled", "dg_head_destroy",
+            "dg_head_workspace_bytes")
 
 
 class dg_moe_config(ctypes.Structure):
@@ -43,6 +45,12 @@ class dg_moe_weights(ctypes.Structure):
 class dg_moe_debug(ctypes.Structure):
     _fields_ = [("topk_idx", ctypes.c_void_p), ("topk_w", ctypes.c_void_p), ("counts", ctypes.c_void_p),
                 ("offsets", ctypes.c_void_p), ("sorted_slot", ctypes.c_void_p), ("row_of_slot", ctypes.c_void_p)]
+
+
+class dg_head_config(ctypes.Structure):
+    _fields_ = [("struct_size", ctypes.c_uint32), ("vocab", ctypes.c_int32), ("d_model", ctypes.c_int32),
+                ("max_tokens", ctypes.c_int32), ("h_dtype", ctypes.c_int32), ("emb_dtype", ctypes.c_int32),
+                ("flags", ctypes.c_uint32)]
 
 
 def _load():
@@ -73,6 +81,17 @@ def _load():
     lib.dg_moe_abi_version.restype = i32
     lib.dg_moe_workspace_bytes.argtypes = [ctypes.POINTER(dg_moe_config)]
     lib.dg_moe_workspace_bytes.restype = ctypes.c_uint64
+    f32 = ctypes.c_float
+    lib.dg_head_create.argtypes = [ctypes.POINTER(dg_head_config), vp, ctypes.POINTER(vp)]
+    lib.dg_head_create.restype = i32
+    lib.dg_head_forward.argtypes = [vp, vp, i32, f32, vp, vp, vp, vp, vp]
+    lib.dg_head_forward.restype = i32
+    lib.dg_head_forward_profiled.argtypes = [vp, vp, i32, f32, vp, vp, vp, vp, ctypes.POINTER(vp), vp]
+    lib.dg_head_forward_profiled.restype = i32
+    lib.dg_head_destroy.argtypes = [vp]
+    lib.dg_head_destroy.restype = i32
+    lib.dg_head_workspace_bytes.argtypes = [ctypes.POINTER(dg_head_config)]
+    lib.dg_head_workspace_bytes.restype = ctypes.c_uint64
     if lib.dg_moe_abi_version() != ABI_VERSION:
         raise ImportError("libdgmoe.so ABI version mismatch")
     return lib
@@ -137,6 +156,40 @@ def dg_moe_abi_version() -> int:
 
 def dg_moe_workspace_bytes(cfg: dg_moe_config) -> int:
     return _lib.dg_moe_workspace_bytes(ctypes.byref(cfg))
+
+
+def dg_head_create(cfg: dg_head_config, emb: int):
+    """Returns (status, handle)."""
+    h = ctypes.c_void_p()
+    st = _lib.dg_head_create(ctypes.byref(cfg), ctypes.c_void_p(emb), ctypes.byref(h))
+    return st, h
+
+
+def dg_head_forward(handle, h: int, T: int, beta: float, logits: int | None, entropy: int, argmax: int,
+                    mean_entropy: int | None, stream: int) -> int:
+    return _lib.dg_head_forward(handle, h, T, beta, logits, entropy, argmax, mean_entropy, ctypes.c_void_p(stream))
+
+
+def dg_head_forward_profiled(handle, h: int, T: int, beta: float, logits: int | None, entropy: int, argmax: int,
+                             mean_entropy: int | None, events, stream: int) -> int:
+    """events: six hipEvent_t handles (ints): start/stop of each of the three kernels."""
+    if len(events) != 6:
+        raise ValueError("dg_head_forward_profiled takes 6 events")
+    arr = (ctypes.c_void_p * 6)(*events)
+    return _lib.dg_head_forward_profiled(handle, h, T, beta, logits, entropy, argmax, mean_entropy, arr,
+                                         ctypes.c_void_p(stream))
+
+
+def dg_head_destroy(handle) -> int:
+    return _lib.dg_head_destroy(handle)
+
+
+def dg_head_workspace_bytes(cfg: dg_head_config) -> int:
+    return _lib.dg_head_workspace_bytes(ctypes.byref(cfg))
+
+
+def make_head_config(V=262144, D=2816, max_tokens=256, h_dtype=DG_BF16, emb_dtype=DG_BF16, flags=0) -> dg_head_config:
+    return dg_head_config(ctypes.sizeof(dg_head_config), V, D, max_tokens, h_dtype, emb_dtype, flags)
 
 
 def make_config(E=128, K=8, D=2816, F=704, max_tokens=256, eps=1e-6, act=DG_BF16, router_w=DG_BF16,
@@ -229,6 +282,49 @@ class MoELayer:
     def close(self):
         if getattr(self, "handle", None):
             _check(dg_moe_destroy(self.handle), "dg_moe_destroy")
+            self.handle = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+
+class CanvasHead:
+    """The canvas output stage over a borrowed bf16 embedding table emb [V, D] (a torch device tensor)."""
+
+    def __init__(self, emb, max_tokens: int, stream=None):
+        import torch
+        if emb.dtype != torch.bfloat16:
+            raise TypeError("the embedding table must be bf16")
+        self.emb = emb  # borrowed: kept alive with the handle
+        self.V, self.D = emb.shape
+        st, h = dg_head_create(make_head_config(self.V, self.D, max_tokens), _ptr(emb))
+        _check(st, "dg_head_create")
+        self.handle = h
+        self.max_tokens = max_tokens
+        self.stream = stream if stream is not None else torch.cuda.current_stream()
+
+    def forward(self, h, beta: float = 1.0, want_logits: bool = True, out=None):
+        """Returns dict(logits [T, V] f32 or None, entropy [T] f32, argmax [T] int32, mean_entropy [1] f32)."""
+        import torch
+        T = h.shape[0]
+        dev = h.device
+        r = out if out is not None else {
+            "logits": torch.empty((T, self.V), dtype=torch.float32, device=dev) if want_logits else None,
+            "entropy": torch.empty((T,), dtype=torch.float32, device=dev),
+            "argmax": torch.empty((T,), dtype=torch.int32, device=dev),
+            "mean_entropy": torch.empty((1,), dtype=torch.float32, device=dev),
+        }
+        st = dg_head_forward(self.handle, _ptr(h), T, beta, _ptr(r["logits"]), _ptr(r["entropy"]), _ptr(r["argmax"]),
+                             _ptr(r["mean_entropy"]), self.stream.cuda_stream)
+        _check(st, "dg_head_forward")
+        return r
+
+    def close(self):
+        if getattr(self, "handle", None):
+            _check(dg_head_destroy(self.handle), "dg_head_destroy")
             self.handle = None
 
     def __del__(self):

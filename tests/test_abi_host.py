@@ -9,18 +9,22 @@ import pytest
 from expert_ffn_canvas_amd import dgmoe
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
-HEADER = os.path.join(ROOT, "include", "dg_moe.h")
+HEADERS = [os.path.join(ROOT, "include", n) for n in sorted(os.listdir(os.path.join(ROOT, "include")))
+           if n.endswith(".h")]
 
 
 def declared_functions():
-    src = open(HEADER).read()
-    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
-    return sorted(set(re.findall(r"\b(dg_moe_\w+)\s*\(", src)))
+    names = set()
+    for hdr in HEADERS:
+        src = re.sub(r"/\*.*?\*/", "", open(hdr).read(), flags=re.S)
+        names |= set(re.findall(r"\b(dg_\w+)\s*\(", src))
+    return sorted(names)
 
 
 def test_header_declares_the_entry_points():
     names = declared_functions()
-    for n in ("dg_moe_create", "dg_moe_forward", "dg_moe_destroy"):
+    for n in ("dg_moe_create", "dg_moe_forward", "dg_moe_destroy", "dg_head_create", "dg_head_forward",
+              "dg_head_destroy"):
         assert n in names
     assert set(names) == set(dgmoe.EXPORTED)
 
@@ -114,3 +118,47 @@ def test_forward_and_destroy_with_null_handle():
     dbg = dgmoe.dg_moe_debug()
     assert dgmoe.dg_moe_forward_debug(None, 16, 32, 4, dbg, 0) == dgmoe.DG_ERR_INVALID_ARG
     assert dgmoe.dg_moe_destroy(None) == dgmoe.DG_OK
+
+
+# ----------------------------------------------------------------------------- canvas output stage
+
+def test_head_struct_layout_and_workspace():
+    assert ctypes.sizeof(dgmoe.dg_head_config) == 28
+    cfg = dgmoe.make_head_config(V=262144, D=2816, max_tokens=256)
+    # five arrays of (V / 256) x max_tokens four-byte partials
+    assert dgmoe.dg_head_workspace_bytes(cfg) == 5 * 1024 * 256 * 4
+    assert dgmoe.dg_head_workspace_bytes(dgmoe.make_head_config(D=100)) == 0
+
+
+@pytest.mark.parametrize("field,value,status", [
+    ("vocab", 0, dgmoe.DG_ERR_SHAPE),
+    ("vocab", (1 << 24) + 1, dgmoe.DG_ERR_SHAPE),
+    ("d_model", 2800, dgmoe.DG_ERR_SHAPE),
+    ("d_model", 0, dgmoe.DG_ERR_SHAPE),
+    ("max_tokens", 0, dgmoe.DG_ERR_SHAPE),
+    ("h_dtype", dgmoe.DG_F32, dgmoe.DG_ERR_DTYPE),
+    ("emb_dtype", dgmoe.DG_MXFP8, dgmoe.DG_ERR_DTYPE),
+    ("flags", 1, dgmoe.DG_ERR_INVALID_ARG),
+    ("struct_size", 12, dgmoe.DG_ERR_INVALID_ARG),
+])
+def test_head_create_rejects_bad_config(field, value, status):
+    cfg = dgmoe.make_head_config()
+    setattr(cfg, field, value)
+    st, h = dgmoe.dg_head_create(cfg, 1 << 20)
+    assert st == status and not h.value
+    assert dgmoe.dg_moe_last_error() != ""
+
+
+def test_head_create_rejects_null_and_misaligned_table():
+    cfg = dgmoe.make_head_config()
+    st, h = dgmoe.dg_head_create(cfg, 0)
+    assert st == dgmoe.DG_ERR_INVALID_ARG and not h.value
+    st, h = dgmoe.dg_head_create(cfg, (1 << 20) + 8)
+    assert st == dgmoe.DG_ERR_ALIGN and not h.value
+
+
+def test_head_forward_and_destroy_with_null_handle():
+    assert dgmoe.dg_head_forward(None, 16, 4, 1.0, None, 32, 48, None, 0) == dgmoe.DG_ERR_INVALID_ARG
+    assert dgmoe.dg_head_forward_profiled(None, 16, 4, 1.0, None, 32, 48, None, [1] * 6, 0) == \
+        dgmoe.DG_ERR_INVALID_ARG
+    assert dgmoe.dg_head_destroy(None) == dgmoe.DG_OK
