@@ -70,6 +70,18 @@ __device__ __forceinline__ f32x4 mfma_f16(const f16x8& a, const f16x8& b, const 
 }
 
 __device__ __forceinline__ bf16x8 as_bf16x8(const u32x4& v) { return __builtin_bit_cast(bf16x8, v); }
+
+// Lane exchange inside a 16-lane row by DPP (no LDS traffic): the value of the
+// partner lane that pattern CTRL names.
+template <int CTRL>
+__device__ __forceinline__ uint32_t dpp(uint32_t v) {
+  return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, CTRL, 0xf, 0xf, false);
+}
+// Patterns inside a 16-lane row: swap neighbours, swap pairs, mirror each
+// half row, mirror the row. Combining with the partner after each of the four
+// in turn leaves every lane with the combination of all sixteen (every step
+// joins two disjoint groups, the same two in both partners).
+constexpr int kDppXor1 = 0xb1, kDppXor2 = 0x4e, kDppHalfMirror = 0x141, kDppMirror = 0x140;
 __device__ __forceinline__ f16x8 as_f16x8(const u32x4& v) { return __builtin_bit_cast(f16x8, v); }
 
 }  // namespace dg

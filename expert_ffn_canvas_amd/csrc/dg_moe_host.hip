@@ -572,7 +572,8 @@ dg_status dg_moe_destroy(dg_moe_handle hd) {
 
 struct dg_head_s {
   dg_head_config cfg;
-  const uint16_t* emb;
+  int n_cu;             // compute units of the device (persistent workgroups)
+  const uint16_t* emb;  // the borrowed table
   char* ws;
   size_t nvb;  // vocabulary tiles of 256
 };
@@ -635,6 +636,7 @@ dg_status head_launch(dg_head_handle hd, const void* h, int32_t T, float beta, f
   dg::HeadArgs a{};
   a.h = static_cast<const uint16_t*>(h);
   a.emb = hd->emb;
+  a.n_wg = hd->n_cu;
   a.T = T;
   a.V = c.vocab;
   a.D = c.d_model;
@@ -692,6 +694,7 @@ dg_status dg_head_create(const dg_head_config* cfg, const void* emb, dg_head_han
   dg_head_s* hd = new (std::nothrow) dg_head_s();
   if (!hd) return fail(DG_ERR_OOM, "host allocation failed");
   hd->cfg = *cfg;
+  hd->n_cu = prop.multiProcessorCount > 0 ? prop.multiProcessorCount : 256;
   hd->emb = static_cast<const uint16_t*>(emb);
   hd->nvb = head_nvb(*cfg);
   const size_t bytes = 5 * head_part_bytes(*cfg);

@@ -14,19 +14,24 @@
 // knobs); vocabulary 262144 (auto-round PR "Add quantization support for
 // DiffusionGemma", test log).
 //
-// k_head: one workgroup of 8 waves per tile of 256 positions x 256 vocabulary
-// rows. Both operands are row-major in HBM ([T, D] and [V, D]); 64-input
-// stages of both tiles (32 KB each) are copied by LDS DMA into a two-stage
-// ring, each 128-byte row's 16-byte segments XOR-swizzled so the MFMA operand
-// reads are free of bank conflicts. Wave w owns positions 128 (w & 1) .. + 127
-// and vocabulary rows 64 (w >> 1) .. + 63 of the tile: 8 x 4 accumulator
-// tiles of v_mfma_f32_16x16x32_bf16. The epilogue writes the logits (fp32,
-// non-temporal) and reduces each position's 256 values to a softmax partial
-// (m = max of beta l, s = sum e^(beta l - m), u = sum e^(beta l - m)(beta l - m),
-// and the argmax), merged across lanes and waves in a fixed order.
-// k_head_merge: one wave per position merges the partials of all vocabulary
-// tiles in a fixed order: entropy = ln s - u / s. k_head_mean: one wave sums
-// the entropies in a fixed order. Every result is bit-reproducible.
+// k_head: one workgroup of 8 waves per CU, looping over tiles of 256
+// positions x 256 vocabulary rows (persistent). 64-input stages of both tiles
+// (32 KB each) are copied by LDS DMA, the positions (read from L2) into a
+// two-stage ring and the vocabulary rows (streamed from HBM, the longer wait)
+// into a three-stage ring: 160 KB of LDS, two vocabulary stages in flight
+// while one is multiplied. Each staged 128-byte row has its 16-byte segments
+// XOR-swizzled so the MFMA operand reads are free of bank conflicts. Both
+// operands are read row-major ([T, D] and [V, D]) in place. Wave w multiplies
+// positions 128 (w & 1) .. + 127 and vocabulary rows 64 (w >> 1) .. + 63 of
+// the tile: 8 x 4 accumulator tiles of v_mfma_f32_16x16x32_bf16. The epilogue
+// of a tile writes the logits (fp32, non-temporal) and reduces each
+// position's 256 values to a softmax partial (m = max of beta l,
+// s = sum e^(beta l - m), u = sum e^(beta l - m)(beta l - m), and the argmax),
+// first over each 16-lane row by DPP, then over the four vocabulary quarters
+// in a fixed order, while the next tile's first stages are already loading.
+// k_head_merge: one workgroup per position merges the partials of all
+// vocabulary tiles in a fixed order: entropy = ln s - u / s. k_head_mean: one
+// wave sums the entropies in a fixed order. Every result is bit-reproducible.
 #include "dg_common.h"
 #include "gemm_common.h"
 #include "launch.h"
@@ -43,11 +48,10 @@ constexpr int kHSegs = kHK / 8;                  // 16-byte segments per row
 constexpr int kHWaves = 8;
 constexpr int kHThreads = 64 * kHWaves;
 constexpr int kHTileBytes = kHTok * kHRowBytes;  // 32 KB (A and B alike)
-constexpr int kHStageBytes = 2 * kHTileBytes;    // A then B
-constexpr int kHStages = 2;
+constexpr int kHARing = 2;                       // position stages
+constexpr int kHBRing = 3;                       // vocabulary stages
 constexpr int kHRowsPerDma = 1024 / kHRowBytes;  // rows one wave-wide transfer fills (8)
 constexpr int kHDmaPerTile = kHTok / (kHRowsPerDma * kHWaves);  // transfers per wave and tile (4)
-constexpr int kHDma = 2 * kHDmaPerTile;          // transfers per wave and stage
 
 static_assert(kHTok == kHVoc, "A and B tiles share the transfer pattern");
 
@@ -57,23 +61,37 @@ static_assert(kHTok == kHVoc, "A and B tiles share the transfer pattern");
 // 128-byte line.
 __device__ __forceinline__ int hswz(int r, int s) { return s ^ ((r >> 1) & (kHSegs - 1)); }
 
-// One stage: rows of the position tile (from h) and of the vocabulary tile
-// (from emb), inputs k0 .. k0 + 63. Rows past T or V re-read the last row.
-__device__ __forceinline__ void head_dma(uint32_t stage, const uint16_t* h, const uint16_t* emb, int t0, int v0,
-                                         int T, int V, int D, int k0, int wave, int lane) {
+// Stage k0 .. k0 + 63 of the position tile (rows of h; rows past T re-read
+// the last one): instruction i of wave w fills the 8-row block w + 8 i.
+__device__ __forceinline__ void head_dma_a(uint32_t stage, const uint16_t* h, int t0, int T, int D, int k0, int wave,
+                                           int lane) {
 #pragma unroll
   for (int i = 0; i < kHDmaPerTile; ++i) {
-    const int blk = wave + kHWaves * i;  // 8-row block of the tile
+    const int blk = wave + kHWaves * i;
     const int r = blk * kHRowsPerDma + lane / kHSegs;
     const int sg = hswz(r, lane % kHSegs);
-    const uint32_t off = __builtin_amdgcn_readfirstlane(stage + blk * 1024);
-    gemm::lds_dma16(off, h + (size_t)min(t0 + r, T - 1) * D + k0 + sg * 8);
-    gemm::lds_dma16(off + kHTileBytes, emb + (size_t)min(v0 + r, V - 1) * D + k0 + sg * 8);
+    gemm::lds_dma16(__builtin_amdgcn_readfirstlane(stage + blk * 1024),
+                    h + (size_t)min(t0 + r, T - 1) * D + k0 + sg * 8);
+  }
+}
+
+// Stage k of the vocabulary tile vb (rows of the row-major table; rows past V
+// re-read the last one).
+__device__ __forceinline__ void head_dma_b(uint32_t stage, const uint16_t* emb, int vb, int V, int D, int k,
+                                           int wave, int lane) {
+#pragma unroll
+  for (int i = 0; i < kHDmaPerTile; ++i) {
+    const int blk = wave + kHWaves * i;
+    const int r = blk * kHRowsPerDma + lane / kHSegs;
+    const int sg = hswz(r, lane % kHSegs);
+    gemm::lds_dma16(__builtin_amdgcn_readfirstlane(stage + blk * 1024),
+                    emb + (size_t)min(vb * kHVoc + r, V - 1) * D + k * kHK + sg * 8);
   }
 }
 
 // Softmax partial of a set of values x = beta l: m = max x, s = sum e^(x - m),
 // u = sum e^(x - m)(x - m); the argmax of l (value and id, lowest id on ties).
+// An empty set has s = 0.
 struct SmPart {
   float m, s, u, best;
   int id;
@@ -111,17 +129,78 @@ __device__ __forceinline__ SmPart sm_shfl_xor(const SmPart& p, int mask) {
   return o;
 }
 
+template <int CTRL>
+__device__ __forceinline__ float dpp_f(float v) {
+  return __uint_as_float(dpp<CTRL>(__float_as_uint(v)));
+}
+
+// Max, sum and argmax over the 16 lanes of a row (every lane gets the result;
+// a sum is formed in the same grouping in every lane, so it is the same bits).
+__device__ __forceinline__ float row_max(float v) {
+  v = fmaxf(v, dpp_f<kDppXor1>(v));
+  v = fmaxf(v, dpp_f<kDppXor2>(v));
+  v = fmaxf(v, dpp_f<kDppHalfMirror>(v));
+  return fmaxf(v, dpp_f<kDppMirror>(v));
+}
+
+__device__ __forceinline__ float row_sum(float v) {
+  v += dpp_f<kDppXor1>(v);
+  v += dpp_f<kDppXor2>(v);
+  v += dpp_f<kDppHalfMirror>(v);
+  return v + dpp_f<kDppMirror>(v);
+}
+
+template <int CTRL>
+__device__ __forceinline__ void argmax_with(float& best, int& id) {
+  const float ob = dpp_f<CTRL>(best);
+  const int oi = (int)dpp<CTRL>((uint32_t)id);
+  const bool take = ob > best || (ob == best && oi < id);
+  best = take ? ob : best;
+  id = take ? oi : id;
+}
+
+__device__ __forceinline__ void row_argmax(float& best, int& id) {
+  argmax_with<kDppXor1>(best, id);
+  argmax_with<kDppXor2>(best, id);
+  argmax_with<kDppHalfMirror>(best, id);
+  argmax_with<kDppMirror>(best, id);
+}
+
+// Persistent: workgroup b takes tiles b, b + G, b + 2 G, ... (G workgroups,
+// one per CU) and runs their stages as one stream, so the first stages of the
+// next tile are on their way while this tile's epilogue runs. Stage g of the
+// stream is stage g % nk of the workgroup's tile g / nk; it goes to position
+// slot g % 2 and vocabulary slot g % 3.
 __global__ __launch_bounds__(kHThreads) void k_head(HeadArgs a) {
-  __shared__ __attribute__((aligned(16))) char smem[kHStages * kHStageBytes];
+  __shared__ __attribute__((aligned(16))) char smem[(kHARing + kHBRing) * kHTileBytes];
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int th = wave & 1, vq = wave >> 1;
   const int ntb = (a.T + kHTok - 1) / kHTok;
-  const int vb = blockIdx.x / ntb, tb = blockIdx.x - vb * ntb;
-  const int t0 = tb * kHTok, v0 = vb * kHVoc;
+  const int ntiles = ((a.V + kHVoc - 1) / kHVoc) * ntb;
+  const int G = gridDim.x;
+  if ((int)blockIdx.x >= ntiles) return;
   const int D = a.D, nk = D / kHK;
-  const uint32_t base = gemm::lds_addr(smem);
+  const int nstage = ((ntiles - (int)blockIdx.x + G - 1) / G) * nk;
+  const uint32_t abase = gemm::lds_addr(smem), bbase = abase + kHARing * kHTileBytes;
   const int m = lane & 15, g = lane >> 4;
+
+  // tile of stream stage q: vocabulary tile and first position
+  auto tile_of = [&](int q, int& vb, int& t0) {
+    const int tl = (int)blockIdx.x + (q / nk) * G;
+    vb = tl / ntb;
+    t0 = (tl - vb * ntb) * kHTok;
+  };
+  auto issue_a = [&](int q) {
+    int vb, t0;
+    tile_of(q, vb, t0);
+    head_dma_a(abase + (q & 1) * kHTileBytes, a.h, t0, a.T, D, (q % nk) * kHK, wave, lane);
+  };
+  auto issue_b = [&](int q) {
+    int vb, t0;
+    tile_of(q, vb, t0);
+    head_dma_b(bbase + (q % kHBRing) * kHTileBytes, a.emb, vb, a.V, D, q % nk, wave, lane);
+  };
 
   f32x4 acc[8][4];
 #pragma unroll
@@ -129,14 +208,23 @@ __global__ __launch_bounds__(kHThreads) void k_head(HeadArgs a) {
 #pragma unroll
     for (int p = 0; p < 4; ++p) acc[i][p] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  head_dma(base, a.h, a.emb, t0, v0, a.T, a.V, D, 0, wave, lane);
-  for (int k = 0; k < nk; ++k) {
-    gemm::wait_vmcnt<0>();  // this wave's transfers of stage k have landed
-    gemm::lds_barrier();    // everyone's have, and everyone is done with stage k - 1
-    if (k + 1 < nk)
-      head_dma(base + ((k + 1) & 1) * kHStageBytes, a.h, a.emb, t0, v0, a.T, a.V, D, (k + 1) * kHK, wave, lane);
-    const char* As = smem + (k & 1) * kHStageBytes;
-    const char* Bs = As + kHTileBytes;
+  // issue order: A0 B0 B1, then per stage q: A(q + 1) B(q + 2); vmcnt retires
+  // loads in order, so stage q is in once at most B(q + 1) is outstanding. The
+  // stage after a tile's epilogue (which stores) waits for everything.
+  issue_a(0);
+  issue_b(0);
+  if (nstage > 1) issue_b(1);
+  bool after_epilogue = false;
+  for (int q = 0; q < nstage; ++q) {
+    if (q + 1 < nstage && !after_epilogue)
+      gemm::wait_vmcnt<kHDmaPerTile>();
+    else
+      gemm::wait_vmcnt<0>();
+    gemm::lds_barrier();  // stage q is in for every wave; everyone is done with stage q - 1
+    if (q + 1 < nstage) issue_a(q + 1);
+    if (q + 2 < nstage) issue_b(q + 2);
+    const char* As = smem + (q & 1) * kHTileBytes;
+    const char* Bs = smem + (kHARing + q % kHBRing) * kHTileBytes;
 #pragma unroll
     for (int kk = 0; kk < kHK / 32; ++kk) {
       const int s = kk * 4 + g;
@@ -154,92 +242,128 @@ __global__ __launch_bounds__(kHThreads) void k_head(HeadArgs a) {
         for (int p = 0; p < 4; ++p) acc[mt][p] = mfma_bf16(av, b[p], acc[mt][p]);
       }
     }
-  }
+    after_epilogue = false;
+    if (q % nk != nk - 1) continue;
 
-  // logits: lane (m, g) holds vocabulary row v0 + 64 vq + 16 p + m of
-  // positions 128 th + 16 mt + 4 g + i
-  if (a.logits != nullptr) {
+    // ---- epilogue of the tile: lane (m, g) holds vocabulary row
+    // v0 + 64 vq + 16 p + m of positions t0 + 128 th + 16 mt + 4 g + i
+    after_epilogue = true;
+    int vb, t0;
+    tile_of(q, vb, t0);
+    const int v0 = vb * kHVoc;
+    if (a.logits != nullptr) {
+#pragma unroll
+      for (int mt = 0; mt < 8; ++mt)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int t = t0 + th * 128 + mt * 16 + g * 4 + i;
+          if (t < a.T) {
+            float* row = a.logits + (size_t)t * a.V;
+#pragma unroll
+            for (int p = 0; p < 4; ++p) {
+              const int v = v0 + vq * 64 + p * 16 + m;
+              if (v < a.V) __builtin_nontemporal_store(acc[mt][p][i], row + v);
+            }
+          }
+        }
+    }
+    // per position and wave: the max, then the sums against it, then the
+    // argmax, each over this lane's 4 values (p ascending) and the row's 16
+    // lanes; the wave partials go to the position slot of stage q (every wave
+    // is done reading it once all have passed the barrier below)
+    gemm::lds_barrier();
+    SmPart* wpart = reinterpret_cast<SmPart*>(smem + (q & 1) * kHTileBytes);  // [vq][256 positions]
 #pragma unroll
     for (int mt = 0; mt < 8; ++mt)
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        const int t = t0 + th * 128 + mt * 16 + g * 4 + i;
-        if (t < a.T) {
-          float* row = a.logits + (size_t)t * a.V;
+        float x[4];
+        bool ok[4];
 #pragma unroll
-          for (int p = 0; p < 4; ++p) {
-            const int v = v0 + vq * 64 + p * 16 + m;
-            if (v < a.V) __builtin_nontemporal_store(acc[mt][p][i], row + v);
+        for (int p = 0; p < 4; ++p) {
+          ok[p] = v0 + vq * 64 + p * 16 + m < a.V;
+          x[p] = ok[p] ? a.beta * acc[mt][p][i] : -INFINITY;
+        }
+        const float mx = row_max(fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3])));
+        float sv = 0.0f, uv = 0.0f, best = -INFINITY;
+        int id = 0x7fffffff;
+#pragma unroll
+        for (int p = 0; p < 4; ++p) {
+          if (ok[p]) {
+            const float d = x[p] - mx;
+            const float e = __expf(d);
+            sv += e;
+            uv = fmaf(e, d, uv);
+            const float l = acc[mt][p][i];
+            if (l > best) {  // strict: the lower id (lower p) stays on a tie
+              best = l;
+              id = v0 + vq * 64 + p * 16 + m;
+            }
           }
         }
+        sv = row_sum(sv);
+        uv = row_sum(uv);
+        row_argmax(best, id);
+        if (m == 0) wpart[vq * kHTok + th * 128 + mt * 16 + g * 4 + i] = SmPart{mx, sv, uv, best, id};
       }
-  }
-
-  // softmax partials: per position, this lane's 4 values (p ascending, so the
-  // lowest id wins a tie), then the 16 lanes of the row group, then the 4
-  // vocabulary quarters through LDS in vq order
-  __syncthreads();  // the stages are free: their space takes the wave partials
-  SmPart* wpart = reinterpret_cast<SmPart*>(smem);  // [vq][256 positions]
+    gemm::lds_barrier();
+    for (int r = tid; r < kHTok; r += kHThreads) {
+      const int t = t0 + r;
+      if (t >= a.T) continue;
+      SmPart sp = wpart[r];
 #pragma unroll
-  for (int mt = 0; mt < 8; ++mt)
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      SmPart q = sm_empty();
-#pragma unroll
-      for (int p = 0; p < 4; ++p) {
-        const int v = v0 + vq * 64 + p * 16 + m;
-        if (v < a.V) {
-          const float l = acc[mt][p][i];
-          const float x = a.beta * l;
-          SmPart one{x, 1.0f, 0.0f, l, v};
-          q = sm_merge(q, one);
-        }
-      }
-#pragma unroll
-      for (int msk = 1; msk < 16; msk <<= 1) {
-        const SmPart o = sm_shfl_xor(q, msk);
-        // fixed order: the lower lane's set first
-        q = (m & msk) ? sm_merge(o, q) : sm_merge(q, o);
-      }
-      if (m == 0) wpart[vq * kHTok + th * 128 + mt * 16 + g * 4 + i] = q;
+      for (int w = 1; w < 4; ++w) sp = sm_merge(sp, wpart[w * kHTok + r]);
+      const size_t o = (size_t)vb * a.T + t;
+      a.part_m[o] = sp.m;
+      a.part_s[o] = sp.s;
+      a.part_u[o] = sp.u;
+      a.part_best[o] = sp.best;
+      a.part_id[o] = sp.id;
     }
-  __syncthreads();
-  for (int r = tid; r < kHTok; r += kHThreads) {
-    const int t = t0 + r;
-    if (t >= a.T) continue;
-    SmPart q = wpart[r];
 #pragma unroll
-    for (int w = 1; w < 4; ++w) q = sm_merge(q, wpart[w * kHTok + r]);
-    const size_t o = (size_t)vb * a.T + t;
-    a.part_m[o] = q.m;
-    a.part_s[o] = q.s;
-    a.part_u[o] = q.u;
-    a.part_best[o] = q.best;
-    a.part_id[o] = q.id;
+    for (int i = 0; i < 8; ++i)
+#pragma unroll
+      for (int p = 0; p < 4; ++p) acc[i][p] = f32x4{0.f, 0.f, 0.f, 0.f};
   }
 }
 
-// One wave per position: lane j merges the partials of vocabulary tiles
-// j, j + 64, ... in order, then the 64 lanes merge in a fixed butterfly.
+// One workgroup of 256 threads per position: thread j merges the partials of
+// vocabulary tiles j, j + 256, ... in order (four loads in flight at a time),
+// then each wave's lanes merge in a fixed butterfly, then the four waves in
+// order.
 __global__ __launch_bounds__(256) void k_head_merge(HeadArgs a) {
-  const int lane = threadIdx.x & 63;
-  const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
-  if (t >= a.T) return;
+  __shared__ SmPart wp[4];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int t = blockIdx.x;
   const int nvb = (a.V + kHVoc - 1) / kHVoc;
   SmPart q = sm_empty();
-  for (int vb = lane; vb < nvb; vb += 64) {
-    const size_t o = (size_t)vb * a.T + t;
-    const SmPart b{a.part_m[o], a.part_s[o], a.part_u[o], a.part_best[o], a.part_id[o]};
-    q = sm_merge(q, b);
+  for (int c = tid; c < nvb; c += 4 * 256) {
+    SmPart b[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int vb = c + 256 * u;
+      b[u] = sm_empty();
+      if (vb < nvb) {
+        const size_t o = (size_t)vb * a.T + t;
+        b[u] = SmPart{a.part_m[o], a.part_s[o], a.part_u[o], a.part_best[o], a.part_id[o]};
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < 4; ++u) q = sm_merge(q, b[u]);
   }
 #pragma unroll
   for (int msk = 1; msk < 64; msk <<= 1) {
     const SmPart o = sm_shfl_xor(q, msk);
-    q = (lane & msk) ? sm_merge(o, q) : sm_merge(q, o);
+    q = (lane & msk) ? sm_merge(o, q) : sm_merge(q, o);  // the lower lane's set first, in both lanes
   }
-  if (lane == 0) {
-    a.entropy[t] = logf(q.s) - q.u / q.s;
-    a.argmax[t] = q.id;
+  if (lane == 0) wp[wave] = q;
+  __syncthreads();
+  if (tid == 0) {
+    SmPart r = wp[0];
+#pragma unroll
+    for (int w = 1; w < 4; ++w) r = sm_merge(r, wp[w]);
+    a.entropy[t] = logf(r.s) - r.u / r.s;
+    a.argmax[t] = r.id;
   }
 }
 
@@ -258,9 +382,10 @@ __global__ __launch_bounds__(64) void k_head_mean(HeadArgs a) {
 
 hipError_t launch_head(const HeadArgs& a, hipStream_t stream, const KernelEvents* ev) {
   const int ntb = (a.T + kHTok - 1) / kHTok, nvb = (a.V + kHVoc - 1) / kHVoc;
-  hipError_t e = launch_kernel(k_head, dim3(nvb * ntb), dim3(kHThreads), stream, ev, a);
+  const int grid = min(nvb * ntb, a.n_wg);
+  hipError_t e = launch_kernel(k_head, dim3(grid), dim3(kHThreads), stream, ev, a);
   if (e != hipSuccess) return e;
-  e = launch_kernel(k_head_merge, dim3((a.T + 3) / 4), dim3(256), stream, ev ? ev + 1 : nullptr, a);
+  e = launch_kernel(k_head_merge, dim3(a.T), dim3(256), stream, ev ? ev + 1 : nullptr, a);
   if (e != hipSuccess || a.mean_entropy == nullptr) return e;
   return launch_kernel(k_head_mean, dim3(1), dim3(64), stream, ev ? ev + 2 : nullptr, a);
 }

@@ -200,7 +200,8 @@ hipError_t launch_combine(const CombineArgs& a, hipStream_t stream, const Kernel
 // Canvas output stage (tied LM head + softmax entropy), all device pointers.
 struct HeadArgs {
   const uint16_t* h;    // [T, D] bf16
-  const uint16_t* emb;  // [V, D] bf16
+  const uint16_t* emb;  // [V, D] bf16 row-major
+  int n_wg;             // persistent workgroups of the logits kernel (one per CU)
   int T, V, D;
   float beta;           // inverse temperature of the softmax
   float* logits;        // [T, V] fp32 or null

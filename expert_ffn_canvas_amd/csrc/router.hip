@@ -55,15 +55,6 @@ __device__ __forceinline__ float key_float(uint32_t k) {
   return __uint_as_float((k & 0x80000000u) ? (k & 0x7fffffffu) : ~k);
 }
 
-template <int CTRL>
-__device__ __forceinline__ uint32_t dpp(uint32_t v) {
-  return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, CTRL, 0xf, 0xf, false);
-}
-// DPP patterns inside a 16-lane row: swap neighbours, swap pairs, mirror
-// each half row, mirror the row. After all four every lane has combined all
-// sixteen.
-constexpr int kDppXor1 = 0xb1, kDppXor2 = 0x4e, kDppHalfMirror = 0x141, kDppMirror = 0x140;
-
 // Keep the larger (key, -id) of this lane's and the partner lane's.
 template <int CTRL>
 __device__ __forceinline__ void argmax_step(uint32_t& key, uint32_t& id) {

@@ -300,11 +300,11 @@ class CanvasHead:
             raise TypeError("the embedding table must be bf16")
         self.emb = emb  # borrowed: kept alive with the handle
         self.V, self.D = emb.shape
+        self.stream = stream if stream is not None else torch.cuda.current_stream()
         st, h = dg_head_create(make_head_config(self.V, self.D, max_tokens), _ptr(emb))
         _check(st, "dg_head_create")
         self.handle = h
         self.max_tokens = max_tokens
-        self.stream = stream if stream is not None else torch.cuda.current_stream()
 
     def forward(self, h, beta: float = 1.0, want_logits: bool = True, out=None):
         """Returns dict(logits [T, V] f32 or None, entropy [T] f32, argmax [T] int32, mean_entropy [1] f32)."""

@@ -50,11 +50,11 @@ typedef struct dg_head_config {
 typedef struct dg_head_s* dg_head_handle;
 
 /* Create an output-stage handle for the embedding table emb [V, D] (device,
- * bf16, 16-byte aligned). The table is borrowed: it must stay valid and
- * unmodified for the handle's lifetime (it is the model's input embedding as
- * well, read in place). Allocates the workspace for config->max_tokens (the
- * per-tile softmax partials, 20 bytes per position and 256 vocabulary rows),
- * so dg_head_forward never allocates. Errors: DG_ERR_INVALID_ARG (null
+ * bf16, 16-byte aligned). The table is borrowed and read in place: it must
+ * stay valid and unmodified for the handle's lifetime (it is the model's input
+ * embedding as well). Allocates the workspace for config->max_tokens (the per-tile
+ * softmax partials, 20 bytes per position and 256 vocabulary rows), so
+ * dg_head_forward never allocates. Errors: DG_ERR_INVALID_ARG (null
  * cfg/emb/out, wrong struct_size, unknown flag), DG_ERR_SHAPE, DG_ERR_DTYPE,
  * DG_ERR_ALIGN, DG_ERR_OOM, DG_ERR_HIP, DG_ERR_UNSUPPORTED (current device is
  * not gfx950). *out is NULL on any error. */
@@ -85,8 +85,8 @@ dg_status dg_head_forward_profiled(dg_head_handle hd, const void* h, int32_t T, 
                                    void* stream);
 
 /* Release the handle and its workspace (not the borrowed table). NULL is a
- * no-op. Not stream ordered: the caller makes sure no forward on it is still
- * running. */
+ * no-op. Not stream ordered: the caller makes sure no
+ * forward on it is still running. */
 dg_status dg_head_destroy(dg_head_handle hd);
 
 /* Bytes of device workspace a handle with this configuration allocates; 0 if

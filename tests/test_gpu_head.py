@@ -87,6 +87,9 @@ def check_head(h, emb, beta, tokens=None, want_logits=True):
     (1, 257, 64, 2.5),        # one position, a lone vocabulary row in the last tile
     (256, 4096, 2816, 1.25),  # the model's d_model: 44 stages per tile
     (64, 512, 2816, 1.0),
+    (5, 300, 64, 1.0),        # one stage per tile
+    (3, 700, 128, 1.0),       # two stages per tile: the pipeline's prologue and tail only
+    (16, 70000, 64, 1.0),     # 274 tiles: some workgroups run two tiles back to back
 ])
 def test_head_small(T, V, D, beta):
     _say(f"head small T={T} V={V} D={D} beta={beta}")
