@@ -7,10 +7,16 @@ over a 256-token canvas, bf16, with the Zipf-skewed router bias; the weights rot
 resident copies so that no cache holds them from one step to the next. The expert weights are packed at
 create into the GEMMs' fragment order (--borrow reads them in place, row-major).
 
-Prints one JSON line: tokens/s, the roofline of the dominant kernel (gate_up, HBM-bound) measured with
-HIP events on the launch stream, and the CPU oracle timed on the host on a bounded sample.
+Prints one JSON line: tokens/s, the roofline of the dominant kernel (the fused gate_up + down launch,
+HBM-bound) measured with HIP events on the launch stream, and the CPU oracle timed on the host on a
+bounded sample.
 
-  python bench.py [--steps K] [--warmup W] [--workload canvas256|encode2304|int4|q8|mxfp4|mxfp8|canvas32|stack30]
+--workload head256 measures the canvas output stage instead (dg_head_forward: the tied LM head over a
+256-position canvas, vocabulary 262144, fp32 logits written, plus the per-position softmax entropy), one
+step = one call; the same JSON fields, with the logits kernel as the dominant one.
+
+  python bench.py [--steps K] [--warmup W]
+                  [--workload canvas256|encode2304|int4|q8|mxfp4|mxfp8|canvas32|stack30|head256]
 """
 import argparse
 import ctypes
@@ -29,6 +35,9 @@ BF16_PEAK_TFLOPS = 2500.0      # MI355X dense bf16 MFMA
 F16_PEAK_TFLOPS = 2500.0
 COUNTERS_FILE = os.path.join(ROOT, "profiles", "gemm_fused_counters.txt")
 KERNEL_NAMES = ("norm", "logits_topk", "permute", "gate_up", "down", "combine")
+HEAD_METRIC = ("canvas output stage tokens/s (tied LM head, T=256 x vocab 262144, fp32 logits, softmax entropy) "
+               "+ % of HBM roofline")
+HEAD_KERNEL_NAMES = ("logits_partials", "merge", "mean")
 
 
 class HipEvents:
@@ -149,6 +158,126 @@ def cpu_baseline(wl, x, w, threads):
                       f"{reps} times; {dt:.2f} s wall"}
 
 
+def head_cpu_baseline(hw, h, emb, threads):
+    """The output-stage oracle, as it stands, on a bounded sample of positions of the batch."""
+    import oracle
+    from expert_ffn_canvas_amd import synth
+
+    hb, eb = synth.to_numpy_bits(h.cpu()), synth.to_numpy_bits(emb.cpu())
+    tok = [0, hw.T - 1]
+    oracle.load()
+    reps, t0 = 0, time.perf_counter()
+    while True:
+        oracle.canvas_head(hb, eb, beta=1.0, tokens=tok, n_threads=threads)
+        reps += 1
+        dt = time.perf_counter() - t0
+        if dt >= 10.0 or reps >= 64:
+            break
+    return {"value": round(reps * len(tok) / dt, 3), "unit": "tokens/s", "cores": threads, "kind": "oracle",
+            "sample": f"positions 0 and {hw.T - 1} of the {hw.name} batch, each against all {hw.V} vocabulary rows "
+                      f"(logits, entropy, argmax), {reps} times; {dt:.2f} s wall"}
+
+
+def run_head(args, torch, dgmoe, synth):
+    hw = synth.HEAD_WORKLOADS[args.workload]
+    dev = "cuda:0"
+    torch.cuda.set_device(0)
+    sp = torch.cuda.current_stream().cuda_stream
+    t_setup = time.perf_counter()
+    inp = synth.make_head_inputs(hw, device=dev)
+    h, emb = inp["h"], inp["emb"]
+    head = dgmoe.CanvasHead(emb, max_tokens=hw.T)
+    T, V, D = hw.T, hw.V, hw.D
+    logits = torch.empty((T, V), dtype=torch.float32, device=dev)
+    ent = torch.empty((T,), dtype=torch.float32, device=dev)
+    am = torch.empty((T,), dtype=torch.int32, device=dev)
+    mean = torch.empty((1,), dtype=torch.float32, device=dev)
+    ptrs = (logits.data_ptr(), ent.data_ptr(), am.data_ptr(), mean.data_ptr())
+    print(f"[bench] {hw.name}: T={T} V={V} D={D} setup {time.perf_counter() - t_setup:.1f}s", file=sys.stderr,
+          flush=True)
+
+    def step():
+        st = dgmoe.dg_head_forward(head.handle, h.data_ptr(), T, 1.0, *ptrs, sp)
+        assert st == 0, dgmoe.dg_moe_last_error()
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    ev = HipEvents()
+    e0, e1 = ev.create(2)
+    w0 = time.perf_counter()
+    ev.record(e0, sp)
+    for _ in range(args.steps):
+        step()
+    ev.record(e1, sp)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - w0
+    gpu_ms = ev.elapsed_ms(e0, e1)
+    ms_per_step = gpu_ms / args.steps
+    print(f"[bench] timed {args.steps} steps: {ms_per_step * 1e3:.1f} us/step (wall {wall:.3f}s)", file=sys.stderr,
+          flush=True)
+
+    kern_us = None
+    n_prof = 0 if args.no_profile else min(args.steps, 50)
+    if n_prof:
+        nk = len(HEAD_KERNEL_NAMES)
+        evs = ev.create(2 * nk * n_prof)
+        for i in range(n_prof):
+            st = dgmoe.dg_head_forward_profiled(head.handle, h.data_ptr(), T, 1.0, *ptrs,
+                                                evs[2 * nk * i:2 * nk * (i + 1)], sp)
+            assert st == 0, dgmoe.dg_moe_last_error()
+        torch.cuda.synchronize()
+        tot = [0.0] * nk
+        for i in range(n_prof):
+            for k in range(nk):
+                tot[k] += ev.elapsed_ms(evs[2 * nk * i + 2 * k], evs[2 * nk * i + 2 * k + 1])
+        kern_us = {name: round(tot[k] / n_prof * 1e3, 2) for k, name in enumerate(HEAD_KERNEL_NAMES)}
+        ev.destroy(evs)
+    ev.destroy([e0, e1])
+
+    # algorithmic work: the table and the hidden states read once, the logits written once
+    stage_bytes = V * D * 2 + T * D * 2 + T * V * 4 + T * 4 * 2 + 4
+    flops = 2 * T * V * D
+    step_s = ms_per_step / 1e3
+    roofline = None
+    if kern_us:
+        kbytes = V * D * 2 + T * D * 2 + T * V * 4
+        ach = kbytes / (kern_us["logits_partials"] / 1e6) / 1e9
+        roofline = {"bound": "hbm", "kernel": "logits_partials", "achieved": round(ach, 1), "peak": HBM_PEAK_GBPS,
+                    "unit": "GB/s", "frac": round(ach / HBM_PEAK_GBPS, 4), "traffic": None,
+                    "alg_bytes_per_launch": kbytes, "avg_launch_us": kern_us["logits_partials"],
+                    "mfma_frac": round(flops / (kern_us["logits_partials"] / 1e6) / 1e12 / BF16_PEAK_TFLOPS, 4)}
+    result = {
+        "metric": HEAD_METRIC,
+        "value": round(T * args.steps / (gpu_ms / 1e3), 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": hw.name, "T": T, "vocab": V, "d_model": D, "beta": 1.0,
+                   "logits": "fp32, written", "table": "bf16 row-major, read in place"},
+        "roofline": roofline,
+        "stage": {"alg_bytes": stage_bytes, "alg_flops": flops,
+                  "achieved_GBps": round(stage_bytes / step_s / 1e9, 1),
+                  "hbm_frac": round(stage_bytes / step_s / 1e9 / HBM_PEAK_GBPS, 4),
+                  "mfma_frac": round(flops / step_s / 1e12 / BF16_PEAK_TFLOPS, 4),
+                  "mean_entropy": round(float(mean.item()), 5)},
+        "kernels_us": kern_us,
+        "cpu_baseline": None,
+    }
+    if not args.no_cpu_baseline:
+        threads = int(os.environ.get("OMP_NUM_THREADS", "0")) or os.cpu_count()
+        result["cpu_baseline"] = head_cpu_baseline(hw, h, emb, threads)
+    head.close()
+    print(json.dumps(result), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -173,6 +302,9 @@ def main():
 
     from expert_ffn_canvas_amd import dgmoe, synth
 
+    if args.workload in synth.HEAD_WORKLOADS:
+        run_head(args, torch, dgmoe, synth)
+        return
     wl = synth.WORKLOADS[args.workload]
     if args.borrow and wl.experts in ("q8_0", "mxfp4", "mxfp8"):
         print(json.dumps({"error": "Q8_0, MXFP4 and MXFP8 experts are read from the packed copy only; drop --borrow"}))
