@@ -646,7 +646,7 @@ dg_status head_launch(dg_head_handle hd, const void* h, int32_t T, float beta, f
   a.argmax = argmax;
   a.mean_entropy = mean_entropy;
   const size_t pb = head_part_bytes(c);
-  // partials laid out [nvb][T] for this T (a prefix of each array)
+  // partials laid out [T][nvb] (a prefix of each array)
   a.part_m = reinterpret_cast<float*>(hd->ws);
   a.part_s = reinterpret_cast<float*>(hd->ws + pb);
   a.part_u = reinterpret_cast<float*>(hd->ws + 2 * pb);

@@ -313,7 +313,7 @@ __global__ __launch_bounds__(kHThreads) void k_head(HeadArgs a) {
       SmPart sp = wpart[r];
 #pragma unroll
       for (int w = 1; w < 4; ++w) sp = sm_merge(sp, wpart[w * kHTok + r]);
-      const size_t o = (size_t)vb * a.T + t;
+      const size_t o = (size_t)t * ((a.V + kHVoc - 1) / kHVoc) + vb;  // position-major
       a.part_m[o] = sp.m;
       a.part_s[o] = sp.s;
       a.part_u[o] = sp.u;
@@ -344,7 +344,7 @@ __global__ __launch_bounds__(256) void k_head_merge(HeadArgs a) {
       const int vb = c + 256 * u;
       b[u] = sm_empty();
       if (vb < nvb) {
-        const size_t o = (size_t)vb * a.T + t;
+        const size_t o = (size_t)t * nvb + vb;  // consecutive threads read consecutive tiles
         b[u] = SmPart{a.part_m[o], a.part_s[o], a.part_u[o], a.part_best[o], a.part_id[o]};
       }
     }

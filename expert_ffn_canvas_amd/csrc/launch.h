@@ -208,7 +208,7 @@ struct HeadArgs {
   float* entropy;       // [T]
   int32_t* argmax;      // [T]
   float* mean_entropy;  // [1] or null
-  // per (vocabulary tile of 256, position) softmax partials, [ceil(V/256)][T]
+  // per (position, vocabulary tile of 256) softmax partials, [T][ceil(V/256)]
   float* part_m;
   float* part_s;
   float* part_u;
