@@ -295,7 +295,7 @@ def main():
     args = ap.parse_args()
 
     if args.gpus != 1:
-        print(json.dumps({"error": "this build runs on one GPU only; --gpus must be 1", "n_gpus": args.gpus}))
+        print(json.dumps({"error": "the layer runs on one GPU here; --gpus must be 1", "n_gpus": args.gpus}))
         sys.exit(2)
 
     import torch
