@@ -468,10 +468,12 @@ hipError_t launch_norm(const RouterArgs& a, hipStream_t stream, const KernelEven
 hipError_t launch_logits(const RouterArgs& a, hipStream_t stream, const KernelEvents* ev) {
   const int n_et = a.Epad / 16;
   // more m-tiles per workgroup once 16-token tiles would give more than two
-  // workgroups per CU: W' is then re-read by fewer workgroups
+  // workgroups per CU: W' is then re-read by fewer workgroups, and the grid
+  // fits the chip in one round (T = 2304: 288 workgroups of 64 tokens, 35 us,
+  // against 576 of 32 tokens, 38 us)
   const size_t n16 = (size_t)((a.T + 15) / 16) * n_et;
 #ifndef DG_LOGITS_MT
-  const int mt = n16 <= 512 ? 1 : n16 <= 2048 ? 2 : 4;
+  const int mt = n16 <= 512 ? 1 : n16 <= 1024 ? 2 : 4;
 #else
   const int mt = DG_LOGITS_MT;
 #endif
