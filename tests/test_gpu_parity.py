@@ -149,6 +149,7 @@ def test_q8_0():
     (8, 4, 256, 192, 200),   # tiles of up to 64 rows
     (6, 2, 128, 64, 37),     # gate_up K = 128 (one step), down K = 64 (a lone short step)
     (4, 2, 384, 320, 300),   # gate_up three steps, down two full steps and a short one
+    (16, 8, 256, 192, 1),    # one token: eight one-row tiles, every other expert empty
 ])
 def test_q8_0_small(E, K, D, F, T):
     _say(f"q8_0 small E={E} K={K} D={D} F={F} T={T}")
@@ -177,6 +178,7 @@ def test_mxfp4():
     (8, 4, 256, 192, 200),   # tiles of up to 64 rows
     (6, 2, 128, 64, 37),     # gate_up K = 128 (one step), down K = 64 (a lone short step)
     (4, 2, 384, 320, 300),   # gate_up three steps, down two full steps and a short one
+    (16, 8, 256, 192, 1),    # one token: eight one-row tiles, every other expert empty
 ])
 def test_mxfp4_small(E, K, D, F, T):
     _say(f"mxfp4 small E={E} K={K} D={D} F={F} T={T}")
@@ -205,6 +207,7 @@ def test_mxfp8():
     (8, 4, 256, 192, 200, 6),   # tiles of up to 64 rows; every block's scale byte moved by -6..6
     (6, 2, 128, 64, 37, 0),     # gate_up K = 128 (one step), down K = 64 (a lone short step)
     (4, 2, 384, 320, 300, 3),   # gate_up three steps, down two full steps and a short one
+    (16, 8, 256, 192, 1, 0),    # one token: eight one-row tiles, every other expert empty
 ])
 def test_mxfp8_small(E, K, D, F, T, jitter):
     _say(f"mxfp8 small E={E} K={K} D={D} F={F} T={T} jitter={jitter}")
