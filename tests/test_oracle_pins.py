@@ -603,6 +603,21 @@ def _head_small(T=7, V=600, D=96, seed=5, max_margin=24.0):
     return synth.to_numpy_bits(inp["h"]), synth.to_numpy_bits(inp["emb"])
 
 
+def test_output_stage_workload_from_the_pages():
+    with open(os.path.join(GOLDEN, "output_stage.json")) as f:
+        g = json.load(f)
+    with open(os.path.join(GOLDEN, "expert_shapes.json")) as f:
+        e = json.load(f)
+    hw = synth.HEAD_WORKLOADS["head256"]
+    # the tied head reads the token embedding [vocab, d_model] at 16 bits and writes fp32 logits for the
+    # whole canvas
+    assert g["tie_word_embeddings"] and g["embed_tokens_bits"] == 16 and g["logits_dtype"] == "f32"
+    assert (hw.T, hw.V, hw.D) == (g["canvas_length"], g["vocab"], e["expert_linears"]["gate_proj"]["in_features"])
+    assert g["canvas_length"] == e["canvas_length"]
+    inp = synth.make_head_inputs(synth.HeadWorkload("t", 4, 512, 64, 1))
+    assert inp["emb"].dtype == torch.bfloat16 and inp["h"].dtype == torch.bfloat16
+
+
 def test_canvas_head_logits_match_a_library_matmul():
     h, emb = _head_small()
     r = oracle.canvas_head(h, emb, want_logits=True)
