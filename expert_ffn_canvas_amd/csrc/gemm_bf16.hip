@@ -226,11 +226,15 @@ __device__ __forceinline__ void gemm_body(const GemmArgs& a, const Tile& tl, cha
       case 3: k_loop<PK, 3, ROWS>(As, rowp, w0, w1, K, tid, acc0, acc1, wstep); break;
       default: k_loop<PK, 4, ROWS>(As, rowp, w0, w1, K, tid, acc0, acc1, wstep); break;
     }
-  } else {  // an even number of 16-row MFMA tiles (one spare at most)
-    switch ((nmt + 1) >> 1) {
-      case 1: k_loop<PK, 2, ROWS>(As, rowp, w0, w1, K, tid, acc0, acc1, wstep); break;
-      case 2: k_loop<PK, 4, ROWS>(As, rowp, w0, w1, K, tid, acc0, acc1, wstep); break;
-      case 3: k_loop<PK, 6, ROWS>(As, rowp, w0, w1, K, tid, acc0, acc1, wstep); break;
+  } else {
+    switch (nmt) {
+      case 1: k_loop<PK, 1, ROWS>(As, rowp, w0, w1, K, tid, acc0, acc1, wstep); break;
+      case 2: k_loop<PK, 2, ROWS>(As, rowp, w0, w1, K, tid, acc0, acc1, wstep); break;
+      case 3: k_loop<PK, 3, ROWS>(As, rowp, w0, w1, K, tid, acc0, acc1, wstep); break;
+      case 4: k_loop<PK, 4, ROWS>(As, rowp, w0, w1, K, tid, acc0, acc1, wstep); break;
+      case 5: k_loop<PK, 5, ROWS>(As, rowp, w0, w1, K, tid, acc0, acc1, wstep); break;
+      case 6: k_loop<PK, 6, ROWS>(As, rowp, w0, w1, K, tid, acc0, acc1, wstep); break;
+      case 7: k_loop<PK, 7, ROWS>(As, rowp, w0, w1, K, tid, acc0, acc1, wstep); break;
       default: k_loop<PK, 8, ROWS>(As, rowp, w0, w1, K, tid, acc0, acc1, wstep); break;
     }
   }

@@ -46,8 +46,10 @@ def canvas256():
     # many rows per expert (at least 64 on average: the tall-tile GEMMs), down K = 192 and K = 64
     (8, 4, 384, 192, 300, "bf16", "bf16"),
     (6, 2, 256, 64, 400, "bf16", "f32"),
-    # about 350 rows per expert: two tall tiles each, twelve 16-row MFMA tiles
+    # about 350 rows per expert on average: about three tall tiles each
     (4, 2, 256, 128, 700, "bf16", "bf16"),
+    # every token to both experts: 600 rows each, five tall tiles of 120 rows
+    (2, 2, 256, 128, 600, "bf16", "bf16"),
     # just past the tall-tile threshold with a skewed load: tiles of every height
     (16, 8, 256, 128, 130, "bf16", "bf16"),
 ])
