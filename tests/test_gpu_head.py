@@ -90,6 +90,7 @@ def check_head(h, emb, beta, tokens=None, want_logits=True):
     (5, 300, 64, 1.0),        # one stage per tile
     (3, 700, 128, 1.0),       # two stages per tile: the pipeline's prologue and tail only
     (16, 70000, 64, 1.0),     # 274 tiles: some workgroups run two tiles back to back
+    (16, 700, 16384, 1.0),    # the largest d_model: 256 stages per tile
 ])
 def test_head_small(T, V, D, beta):
     _say(f"head small T={T} V={V} D={D} beta={beta}")

@@ -64,6 +64,23 @@ def test_small_shapes(E, K, D, F, T, act, rw, pack):
     print(f"err {r['err']:.3e} near-ties {r['near_ties']}")
 
 
+@pytest.mark.parametrize("E,K,D,F,T", [
+    (256, 8, 256, 128, 300),    # the most experts a layer may have
+    (16, 8, 256, 128, 3000),    # k T = 24000 slots: past what the permutation stages in LDS; tall tiles
+    (8, 2, 1024, 4096, 40),     # the largest d_ff: 64 gate_up column blocks, down over K = 4096
+    (4, 1, 16384, 64, 20),      # the largest d_model: 128 router chunks, gate_up over K = 16384
+])
+def test_shape_limits(E, K, D, F, T):
+    _say(f"limits E={E} K={K} D={D} F={F} T={T}")
+    wl = synth.small_workload(T=T, E=E, K=K, D=D, F=F, bias="zipf", seed=80 + E)
+    inp = synth.make_inputs(wl, device="cuda")
+    w = inp["layers"][0]
+    layer = _layer(w, T, torch.bfloat16, K=K, pack=True)
+    r = layer_parity(layer, inp["x"], oracle_weights(w), K)
+    print(f"err {r['err']:.3e} near-ties {r['near_ties']}")
+    layer.close()
+
+
 def test_single_expert_closed_form():
     _say("E=1 k=1 D=256 F=128 T=33")
     wl = synth.small_workload(T=33, E=1, K=1, D=256, F=128, seed=5)
