@@ -150,8 +150,11 @@ __device__ __forceinline__ float sumsq8(const u32x4& v) {
 // All expert tiles of a token tile run on one XCD (workgroup b runs on XCD
 // b % 8) and share its L2: each publishes its logits with a counter and the
 // last to arrive selects the top-k of all the tile's tokens, one per 16-lane
-// row.
-template <bool XF32, int MT, int G, int NU>
+// row. With SPLIT = 2 (few token tiles) each expert tile is shared by two
+// workgroups, one per half of its 16 experts: each loads only its half of
+// every W' fragment (the other lanes' operands are zero), so the W' bytes a
+// CU takes in are halved and twice as many CUs share them.
+template <bool XF32, int MT, int G, int NU, int SPLIT>
 __global__ __launch_bounds__(64 * kWaves) void k_logits(RouterArgs a) {
   constexpr int kRows = 16 * MT;
   constexpr int kXsBytes = XF32 ? 0 : kWaves * G * MT * 16 * kChunkRowBytes;
@@ -164,11 +167,11 @@ __global__ __launch_bounds__(64 * kWaves) void k_logits(RouterArgs a) {
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int kh = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int n_et = a.Epad / 16;
+  const int n_eh = a.Epad / 16 * SPLIT;  // workgroups per token tile
   const int n_tt = (a.T + kRows - 1) / kRows;
   const int xq = blockIdx.x % kQueues, jq = blockIdx.x / kQueues;
-  const int tt = xq + kQueues * (jq / n_et);
-  const int et = jq % n_et;
+  const int tt = xq + kQueues * (jq / n_eh);
+  const int et = (jq % n_eh) / SPLIT, half = (jq % n_eh) % SPLIT;
   if (tt >= n_tt) return;
   const int t0 = tt * kRows;
   const int D = a.D;
@@ -179,6 +182,7 @@ __global__ __launch_bounds__(64 * kWaves) void k_logits(RouterArgs a) {
     if (a.bias != nullptr && e < a.E) bias_v = a.bias[e];
   }
   const int m = lane & 15, g = lane >> 4;
+  const bool wmine = SPLIT == 1 || (m >> 3) == half;  // this lane's expert is in the workgroup's half
   const size_t wplane = (size_t)a.Epad * D;
   const uint16_t* wfrag = a.wr + (size_t)et * nks * 512 + lane * 8;
   const int nc = D / kKChunk;
@@ -228,7 +232,8 @@ __global__ __launch_bounds__(64 * kWaves) void k_logits(RouterArgs a) {
       for (int kk = 0; kk < 4; ++kk)
 #pragma unroll
         for (int p = 0; p < 3; ++p)
-          wb[q][kk][p] = *reinterpret_cast<const u32x4*>(wfrag + p * wplane + (size_t)(chunk * 4 + kk) * 512);
+          wb[q][kk][p] = wmine ? *reinterpret_cast<const u32x4*>(wfrag + p * wplane + (size_t)(chunk * 4 + kk) * 512)
+                               : u32x4{0u, 0u, 0u, 0u};
     }
     // all of the group's loads are in flight before the first multiply: one
     // memory round trip per group
@@ -316,7 +321,7 @@ __global__ __launch_bounds__(64 * kWaves) void k_logits(RouterArgs a) {
       tot += ssq[w][row];
     }
     const float r = 1.0f / sqrtf(tot / (float)D + a.eps);
-    if (t0 + row < a.T) {
+    if (t0 + row < a.T && (SPLIT == 1 || (n >> 3) == half)) {
       a.logits[(size_t)(t0 + row) * a.Epad + et * 16 + n] = r * sum + bias_v;  // n == tid % 16
       if (et == 0 && n == 0) a.rnorm[t0 + row] = r;
     }
@@ -326,7 +331,7 @@ __global__ __launch_bounds__(64 * kWaves) void k_logits(RouterArgs a) {
   __syncthreads();
   if (tid == 0) {
     const int old = atomicAdd(&a.tile_count[tt], 1);
-    is_last = (old == n_et - 1);
+    is_last = (old == n_eh - 1);
     if (is_last) a.tile_count[tt] = 0;  // ready for the next forward
   }
   __syncthreads();
@@ -448,10 +453,12 @@ __global__ void k_prep_router_w(const void* __restrict__ w, int w_f32, const flo
   }
 }
 
-template <bool XF32, int MT, int G>
+template <bool XF32, int MT, int G, int SPLIT = 1>
 void (*pick_logits(int nu))(RouterArgs) {
-  return nu <= 2 ? k_logits<XF32, MT, G, 2> : nu <= 4 ? k_logits<XF32, MT, G, 4> : nu <= 8 ? k_logits<XF32, MT, G, 8>
-                                                                                             : k_logits<XF32, MT, G, 16>;
+  return nu <= 2   ? k_logits<XF32, MT, G, 2, SPLIT>
+         : nu <= 4 ? k_logits<XF32, MT, G, 4, SPLIT>
+         : nu <= 8 ? k_logits<XF32, MT, G, 8, SPLIT>
+                   : k_logits<XF32, MT, G, 16, SPLIT>;
 }
 
 }  // namespace
@@ -479,13 +486,21 @@ hipError_t launch_logits(const RouterArgs& a, hipStream_t stream, const KernelEv
 #endif
   const int rows = 16 * (a.x_f32 ? min(mt, 2) : mt);
   const int n_tt = (a.T + rows - 1) / rows;
-  const dim3 grid(kQueues * ((n_tt + kQueues - 1) / kQueues) * n_et);
+  // at most 64 workgroups of 16-token tiles: two workgroups per expert tile
+  // (T = 32: 128 workgroups of 8 experts, 17.4 against 18.3 us; at T = 256,
+  // 256 against 128 workgroups gained nothing)
+  const int tiles = kQueues * ((n_tt + kQueues - 1) / kQueues) * n_et;
+  const int split = (mt == 1 && tiles <= 64) ? 2 : 1;
+  const dim3 grid(tiles * split);
   const int nu = a.Epad / 16;  // 2 .. 16
   void (*k)(RouterArgs);
   if (a.x_f32)  // fp32 x lives in registers: at most two m-tiles
-    k = mt == 1 ? pick_logits<true, 1, 2>(nu) : pick_logits<true, 2, 1>(nu);
+    k = mt == 1 ? (split == 2 ? pick_logits<true, 1, 2, 2>(nu) : pick_logits<true, 1, 2>(nu))
+                : pick_logits<true, 2, 1>(nu);
   else
-    k = mt == 1 ? pick_logits<false, 1, 3>(nu) : mt == 2 ? pick_logits<false, 2, 2>(nu) : pick_logits<false, 4, 1>(nu);
+    k = mt == 1   ? (split == 2 ? pick_logits<false, 1, 3, 2>(nu) : pick_logits<false, 1, 3>(nu))
+        : mt == 2 ? pick_logits<false, 2, 2>(nu)
+                  : pick_logits<false, 4, 1>(nu);
   return launch_kernel(k, grid, dim3(64 * kWaves), stream, ev, a);
 }
 
