@@ -105,7 +105,7 @@ Layout plan(const dg_moe_config& c) {
   L.act = take(K * T * F * 2);
   L.y = take(K * T * D * 2);
   L.tile_done = take(fuses_gemms(c) ? K * T * 4 : 0);
-  L.wr = take(3 * (size_t)L.Epad * D * 2);
+  L.wr = take((size_t)L.Epad * D * 4);
   L.bias = take(E * 4);
   L.gamma_e = take(D * 4);
   L.total = off;
@@ -344,7 +344,7 @@ dg_status dg_moe_create(const dg_moe_config* cfg, const dg_moe_weights* w, void*
   c[1] = hd->has_bias ? hipMemcpyAsync(hd->ws + hd->L.bias, w->router_bias, E * 4, hipMemcpyDeviceToDevice, stream)
                       : hipSuccess;
   c[2] = dg::launch_prep_router_w(w->router_w, cfg->router_w_dtype == DG_F32, w->router_gamma, (int)E, hd->L.Epad,
-                                  (int)D, hd->at<uint16_t>(hd->L.wr), stream);
+                                  (int)D, hd->at<float>(hd->L.wr), stream);
   for (hipError_t ci : c) {
     if (ci != hipSuccess) {
       dg_moe_destroy(hd);
@@ -407,7 +407,7 @@ static dg_status run_forward(dg_moe_handle hd, const void* x, void* out, int32_t
   ra.E = c.n_experts;
   ra.Epad = L.Epad;
   ra.K = c.top_k;
-  ra.wr = hd->at<uint16_t>(L.wr);
+  ra.wr = hd->at<float>(L.wr);
   ra.bias = hd->has_bias ? hd->at<float>(L.bias) : nullptr;
   ra.gamma_e = hd->at<float>(L.gamma_e);
   ra.eps = c.rms_eps;

@@ -56,7 +56,7 @@ struct RouterArgs {
   const void* x;        // [T, D] fp32 or bf16
   int x_f32;
   int T, D, E, Epad, K;
-  const uint16_t* wr;   // W' = W_r diag(1 + gamma_r): three exact bf16 planes [3][Epad][D], fragment order
+  const float* wr;      // W' = W_r diag(1 + gamma_r), fp32 [Epad][D] in fragment order (see launch_prep_router_w)
   const float* bias;    // [E] or null
   const float* gamma_e;
   float eps;
@@ -72,9 +72,12 @@ struct RouterArgs {
 hipError_t launch_norm(const RouterArgs& a, hipStream_t stream, const KernelEvents* ev);
 // r, logits, top-k and the routing weights.
 hipError_t launch_logits(const RouterArgs& a, hipStream_t stream, const KernelEvents* ev);
-// Create time: W' planes from the router weight (fp32 or bf16 [E, D]) and gamma_r [D].
+// Create time: W' in fp32 from the router weight (fp32 or bf16 [E, D]) and gamma_r [D].
+// Layout: 2 KB block (expert tile et, 32-column step s) holds, for lane
+// l = n + 16 g, W'[16 et + n][32 s + 8 g + j] at float 256 (j / 4) + 4 l + j % 4,
+// so each half of a lane's 8 values is one 1 KB wave-wide read.
 hipError_t launch_prep_router_w(const void* w, int w_f32, const float* gamma_r, int E, int Epad, int D,
-                                uint16_t* planes, hipStream_t stream);
+                                float* wf, hipStream_t stream);
 
 // How the permutation deals the GEMM tasks to the per-XCD queues:
 //  kDealUnits: units (expert, column block) round robin, each GEMM on its own;

@@ -3,7 +3,7 @@
 //  logits + top-k (one kernel): per token r = 1/sqrt(mean_d x^2 + eps) and
 //          logits = r (W' x) + b with W' = W_r diag(1 + gamma_r), the router
 //          norm's scale folded into the router weight at create time. W' is
-//          kept in fp32 precision as three exact bf16 planes
+//          kept in fp32 and split in registers into three exact bf16 planes
 //          (W' = W0 + W1 + W2, each plane the next 8 significant bits), so
 //          the products on the bf16 matrix cores are exact and accumulate in
 //          fp32: the logits have fp32 dot-product accuracy. Then per token the
@@ -183,8 +183,7 @@ __global__ __launch_bounds__(64 * kWaves) void k_logits(RouterArgs a) {
   }
   const int m = lane & 15, g = lane >> 4;
   const bool wmine = SPLIT == 1 || (m >> 3) == half;  // this lane's expert is in the workgroup's half
-  const size_t wplane = (size_t)a.Epad * D;
-  const uint16_t* wfrag = a.wr + (size_t)et * nks * 512 + lane * 8;
+  const float* wfrag = a.wr + (size_t)et * nks * 512 + lane * 4;
   const int nc = D / kKChunk;
   const int n_my = (nc - kh + kWaves - 1) / kWaves;  // chunks kh, kh + 8, ...
 
@@ -198,7 +197,7 @@ __global__ __launch_bounds__(64 * kWaves) void k_logits(RouterArgs a) {
   }
 
   for (int c0 = 0; c0 < n_my; c0 += G) {
-    u32x4 wb[G][4][3];
+    u32x4 wb[G][4][2];
     u32x4 xf[XF32 ? G : 1][XF32 ? MT : 1][4][2];
 #pragma unroll
     for (int q = 0; q < G; ++q) {
@@ -231,8 +230,8 @@ __global__ __launch_bounds__(64 * kWaves) void k_logits(RouterArgs a) {
 #pragma unroll
       for (int kk = 0; kk < 4; ++kk)
 #pragma unroll
-        for (int p = 0; p < 3; ++p)
-          wb[q][kk][p] = wmine ? *reinterpret_cast<const u32x4*>(wfrag + p * wplane + (size_t)(chunk * 4 + kk) * 512)
+        for (int h = 0; h < 2; ++h)
+          wb[q][kk][h] = wmine ? *reinterpret_cast<const u32x4*>(wfrag + (size_t)(chunk * 4 + kk) * 512 + h * 256)
                                : u32x4{0u, 0u, 0u, 0u};
     }
     // all of the group's loads are in flight before the first multiply: one
@@ -245,13 +244,23 @@ __global__ __launch_bounds__(64 * kWaves) void k_logits(RouterArgs a) {
       const uint32_t keep = valid ? 0xffffffffu : 0u;
 #pragma unroll
       for (int kk = 0; kk < 4; ++kk) {
+        // the lane's 8 fp32 weights -> three exact bf16 planes (W' = W0 + W1 + W2)
         bf16x8 w[3];
+        {
+          u32x4 o[3];
 #pragma unroll
-        for (int p = 0; p < 3; ++p) {
-          u32x4 v = wb[q][kk][p];
+          for (int i = 0; i < 4; ++i) {
+            const float v0 = __uint_as_float(wb[q][kk][i >> 1][2 * (i & 1)] & keep);
+            const float v1 = __uint_as_float(wb[q][kk][i >> 1][2 * (i & 1) + 1] & keep);
+            float h0, m0, l0, h1, m1, l1;
+            split3(v0, h0, m0, l0);
+            split3(v1, h1, m1, l1);
+            o[0][i] = pack_hi(h0, h1);
+            o[1][i] = pack_hi(m0, m1);
+            o[2][i] = pack_hi(l0, l1);
+          }
 #pragma unroll
-          for (int i = 0; i < 4; ++i) v[i] &= keep;
-          w[p] = as_bf16x8(v);
+          for (int p = 0; p < 3; ++p) w[p] = as_bf16x8(o[p]);
         }
 #pragma unroll
         for (int mt = 0; mt < MT; ++mt) {
@@ -417,10 +426,9 @@ __global__ __launch_bounds__(256) void k_norm(RouterArgs a) {
 // has the 8 values of expert 16 et + n at columns 32 s + 8 g .. + 7. Experts
 // >= E are zero.
 __global__ void k_prep_router_w(const void* __restrict__ w, int w_f32, const float* __restrict__ gamma, int E,
-                                int Epad, int D, uint16_t* __restrict__ planes) {
+                                int Epad, int D, float* __restrict__ wf) {
   const int nks = D / 32;
   const size_t n_items = (size_t)(Epad / 16) * nks * 64;
-  const size_t plane = (size_t)Epad * D;
   for (size_t it = (size_t)blockIdx.x * blockDim.x + threadIdx.x; it < n_items; it += (size_t)gridDim.x * blockDim.x) {
     const int l = (int)(it % 64);
     const size_t blk = it / 64;
@@ -438,18 +446,10 @@ __global__ void k_prep_router_w(const void* __restrict__ w, int w_f32, const flo
       }
       v[i] = wv * (1.0f + gamma[d0 + i]);
     }
-    u32x4 o[3];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      float h0, m0, l0, h1, m1, l1;
-      split3(v[2 * i], h0, m0, l0);
-      split3(v[2 * i + 1], h1, m1, l1);
-      o[0][i] = pack_hi(h0, h1);
-      o[1][i] = pack_hi(m0, m1);
-      o[2][i] = pack_hi(l0, l1);
-    }
-#pragma unroll
-    for (int p = 0; p < 3; ++p) *reinterpret_cast<u32x4*>(planes + p * plane + blk * 512 + l * 8) = o[p];
+    for (int h = 0; h < 2; ++h)
+      *reinterpret_cast<float4*>(wf + blk * 512 + h * 256 + l * 4) =
+          make_float4(v[4 * h], v[4 * h + 1], v[4 * h + 2], v[4 * h + 3]);
   }
 }
 
@@ -505,8 +505,8 @@ hipError_t launch_logits(const RouterArgs& a, hipStream_t stream, const KernelEv
 }
 
 hipError_t launch_prep_router_w(const void* w, int w_f32, const float* gamma, int E, int Epad, int D,
-                                uint16_t* planes, hipStream_t stream) {
-  k_prep_router_w<<<dim3(512), dim3(256), 0, stream>>>(w, w_f32, gamma, E, Epad, D, planes);
+                                float* wf, hipStream_t stream) {
+  k_prep_router_w<<<dim3(512), dim3(256), 0, stream>>>(w, w_f32, gamma, E, Epad, D, wf);
   return hipGetLastError();
 }
 

@@ -53,12 +53,12 @@ def test_version_and_status_strings():
 def test_workspace_bytes():
     good = dgmoe.make_config(max_tokens=256)
     ws = dgmoe.dg_moe_workspace_bytes(good)
-    # at least act and the bf16 per-slot outputs, plus the router weight in three bf16 planes
+    # at least act and the bf16 per-slot outputs, plus the router weight in fp32
     T, K, D, F, E = 256, 8, 2816, 704, 128
-    assert ws >= K * T * F * 2 + K * T * D * 2 + 3 * E * D * 2
+    assert ws >= K * T * F * 2 + K * T * D * 2 + E * D * 4
     assert dgmoe.dg_moe_workspace_bytes(dgmoe.make_config(D=100)) == 0
     q8 = dgmoe.make_config(max_tokens=256, experts=dgmoe.DG_Q8_0, flags=dgmoe.DG_MOE_PACK_WEIGHTS)
-    assert dgmoe.dg_moe_workspace_bytes(q8) >= K * T * F * 2 + K * T * D * 2 + 3 * E * D * 2
+    assert dgmoe.dg_moe_workspace_bytes(q8) >= K * T * F * 2 + K * T * D * 2 + E * D * 4
     assert dgmoe.dg_moe_workspace_bytes(dgmoe.make_config(experts=dgmoe.DG_Q8_0)) == 0
 
 
