@@ -33,7 +33,7 @@ METRIC = "MoE-layer tokens/s per canvas step (T=256, bf16) + % of HBM/MFMA roofl
 HBM_PEAK_GBPS = 8000.0         # MI355X HBM3E
 BF16_PEAK_TFLOPS = 2500.0      # MI355X dense bf16 MFMA
 F16_PEAK_TFLOPS = 2500.0
-COUNTERS_FILE = os.path.join(ROOT, "profiles", "gemm_fused_counters.txt")
+PROFILES = os.path.join(ROOT, "profiles")
 KERNEL_NAMES = ("norm", "logits_topk", "permute", "gate_up", "down", "combine")
 HEAD_METRIC = ("canvas output stage tokens/s (tied LM head, T=256 x vocab 262144, fp32 logits, softmax entropy) "
                "+ % of HBM roofline")
@@ -92,70 +92,116 @@ def expert_bytes(wl):
 
 
 def algorithmic(wl, T, touched):
-    """Bytes and FLOPs the method must move / compute for one forward (intermediates excluded)."""
+    """Bytes and FLOPs the method must move / compute for one forward; intermediates (h, the gated
+    activations, the per-slot outputs) are excluded. Returns (layer bytes, layer FLOPs, bytes of the fused
+    GEMM launch: the touched experts' weights and the input rows x, bytes of the gate_up GEMM alone)."""
     D, F, E, K = wl.D, wl.F, wl.E, wl.K
     act_b = 4 if wl.act == "f32" else 2
     rw_b = 4 if wl.router_w == "f32" else 2
     gu, dn = expert_bytes(wl)
     layer_bytes = touched * (gu + dn) + E * D * rw_b + 2 * D * 4 + E * 4 + 2 * T * D * act_b
     flops = T * K * 2 * 3 * D * F + T * 2 * E * D
-    # gate_up launch: weights of touched experts + expert input rows [T, D] + gated activations [K T, F]
-    gate_up_bytes = touched * gu + T * D * 2 + K * T * F * 2
-    # down launch: weights of touched experts + gated activations + per-slot outputs [K T, D]
-    down_bytes = touched * dn + K * T * F * 2 + K * T * D * 2
-    return layer_bytes, flops, gate_up_bytes, down_bytes
+    gemm_bytes = touched * (gu + dn) + T * D * act_b
+    gate_up_bytes = touched * gu + T * D * act_b
+    return layer_bytes, flops, gemm_bytes, gate_up_bytes
 
 
 def kernel_sources_digest():
+    """Digest of every source of the layer's library (the GEMMs, and the router, permutation and host code
+    that set what they read): counters taken on other sources do not describe this build."""
     h = hashlib.sha256()
     csrc = os.path.join(ROOT, "expert_ffn_canvas_amd", "csrc")
-    for name in ("gemm_bf16.hip", "gemm_common.h", "dg_common.h", "launch.h"):
+    for name in sorted(os.listdir(csrc)):
+        if name == "head.hip" or not name.endswith((".hip", ".h")):
+            continue
         with open(os.path.join(csrc, name), "rb") as f:
+            h.update(name.encode())
             h.update(f.read())
     return h.hexdigest()[:16]
 
 
-def read_traffic(workload, kernel):
-    """HBM bytes per launch of `kernel` from the committed rocprofv3 counter summary, if it was taken on the
-    current kernel source for this workload and kernel; else None."""
-    if not os.path.exists(COUNTERS_FILE):
+def read_counters(workload, kernel):
+    """The committed rocprofv3 record of `kernel` for this workload (profiles/<workload>_gemm_counters.txt):
+    HBM bytes per launch (FETCH_SIZE and WRITE_SIZE scaled by a plain copy's reading) and the kernel's
+    average duration in the kernel trace, if the record was taken on the current sources; else None."""
+    path = os.path.join(PROFILES, f"{workload}_gemm_counters.txt")
+    if not os.path.exists(path):
         return None
     kv = {}
-    for line in open(COUNTERS_FILE):
+    for line in open(path):
         if "=" in line and not line.startswith("#"):
             k, v = line.split("=", 1)
             kv[k.strip()] = v.strip()
     if (kv.get("source_digest") != kernel_sources_digest() or kv.get("workload") != workload
-            or kv.get("kernel", "gate_up") != kernel):
+            or kv.get("kernel") != kernel):
         return None
+    out = {}
+    for key in ("traffic_bytes_per_launch", "rocprof_avg_us"):
+        try:
+            out[key] = float(kv[key])
+        except (KeyError, ValueError):
+            out[key] = None
+    return out
+
+
+def host_cpu():
+    """Model name of the host CPU (from /proc/cpuinfo) and the threads the OS offers."""
+    model = "unknown"
     try:
-        return float(kv["traffic_bytes_per_launch"])
-    except (KeyError, ValueError):
-        return None
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                model = line.split(":", 1)[1].strip()
+                break
+    except OSError:
+        pass
+    return model, os.cpu_count()
+
+
+def percentiles(us):
+    """Median, p10, p90, min, max of per-step times (us) and the spread p90 / p10."""
+    import statistics
+    v = sorted(us)
+    q = lambda f: v[min(len(v) - 1, max(0, int(round(f * (len(v) - 1)))))]
+    return {"median": round(statistics.median(v), 2), "p10": round(q(0.1), 2), "p90": round(q(0.9), 2),
+            "min": round(v[0], 2), "max": round(v[-1], 2), "spread_p90_p10": round(q(0.9) / q(0.1), 4),
+            "n": len(v)}
+
+
+def _time_oracle(fn, budget_s, max_reps=64):
+    reps, t0 = 0, time.perf_counter()
+    while True:
+        fn()
+        reps += 1
+        dt = time.perf_counter() - t0
+        if dt >= budget_s or reps >= max_reps:
+            return reps, dt
 
 
 def cpu_baseline(wl, x, w, threads):
-    """The oracle, as it stands, on the whole batch of this workload (one step), on the host cores."""
+    """The oracle, as it stands, on a bounded sample of this workload's batch on the host: all threads the
+    host offers over 256 tokens (about ten seconds of work), and one thread over 16 tokens."""
     import oracle
     from expert_ffn_canvas_amd import synth
 
     wn = synth.weights_to_numpy(w)
     xn = synth.to_numpy_bits(x)
     T = x.shape[0]
-    n_tok = T if T <= 256 else 256
+    n_tok = min(T, 256)
     tok = list(range(n_tok))
     oracle.load()
-    # repeated until about ten seconds of host work have been timed (at least once)
-    reps, t0 = 0, time.perf_counter()
-    while True:
-        oracle.moe_forward(wn, xn, wl.K, synth.RMS_EPS, tokens=tok, n_threads=threads)
-        reps += 1
-        dt = time.perf_counter() - t0
-        if dt >= 10.0 or reps >= 64:
-            break
+    reps, dt = _time_oracle(lambda: oracle.moe_forward(wn, xn, wl.K, synth.RMS_EPS, tokens=tok, n_threads=threads),
+                            10.0)
+    tok1 = list(range(min(T, 16)))
+    reps1, dt1 = _time_oracle(lambda: oracle.moe_forward(wn, xn, wl.K, synth.RMS_EPS, tokens=tok1, n_threads=1),
+                              3.0)
+    model, n_os = host_cpu()
     return {"value": round(reps * n_tok / dt, 3), "unit": "tokens/s", "cores": threads, "kind": "oracle",
+            "cpu_model": model, "threads": threads, "os_threads": n_os,
+            "one_thread_value": round(reps1 * len(tok1) / dt1, 3),
             "sample": f"{n_tok} tokens of the {wl.name} batch (T={T}), all {wl.K} slots each, one layer, "
-                      f"{reps} times; {dt:.2f} s wall"}
+                      f"{reps} times on {threads} threads ({dt:.2f} s wall); one-thread leg: {len(tok1)} "
+                      f"tokens, {reps1} times ({dt1:.2f} s wall). cores = the threads used (OpenMP), "
+                      f"not physical cores"}
 
 
 def head_cpu_baseline(hw, h, emb, threads):
@@ -173,9 +219,12 @@ def head_cpu_baseline(hw, h, emb, threads):
         dt = time.perf_counter() - t0
         if dt >= 10.0 or reps >= 64:
             break
+    model, n_os = host_cpu()
     return {"value": round(reps * len(tok) / dt, 3), "unit": "tokens/s", "cores": threads, "kind": "oracle",
+            "cpu_model": model, "threads": threads, "os_threads": n_os,
             "sample": f"positions 0 and {hw.T - 1} of the {hw.name} batch, each against all {hw.V} vocabulary rows "
-                      f"(logits, entropy, argmax), {reps} times; {dt:.2f} s wall"}
+                      f"(logits, entropy, argmax), {reps} times on {threads} threads; {dt:.2f} s wall. cores = the "
+                      f"threads used (OpenMP), not physical cores"}
 
 
 def run_head(args, torch, dgmoe, synth):
@@ -216,6 +265,17 @@ def run_head(args, torch, dgmoe, synth):
     ms_per_step = gpu_ms / args.steps
     print(f"[bench] timed {args.steps} steps: {ms_per_step * 1e3:.1f} us/step (wall {wall:.3f}s)", file=sys.stderr,
           flush=True)
+
+    step_stats = None
+    if not args.no_profile:
+        evs = ev.create(2 * args.steps)
+        for i in range(args.steps):
+            ev.record(evs[2 * i], sp)
+            step()
+            ev.record(evs[2 * i + 1], sp)
+        torch.cuda.synchronize()
+        step_stats = percentiles([ev.elapsed_ms(evs[2 * i], evs[2 * i + 1]) * 1e3 for i in range(args.steps)])
+        ev.destroy(evs)
 
     kern_us = None
     n_prof = 0 if args.no_profile else min(args.steps, 50)
@@ -268,6 +328,7 @@ def run_head(args, torch, dgmoe, synth):
                   "hbm_frac": round(stage_bytes / step_s / 1e9 / HBM_PEAK_GBPS, 4),
                   "mfma_frac": round(flops / step_s / 1e12 / BF16_PEAK_TFLOPS, 4),
                   "mean_entropy": round(float(mean.item()), 5)},
+        "step_us": step_stats,
         "kernels_us": kern_us,
         "cpu_baseline": None,
     }
@@ -348,14 +409,19 @@ def main():
             st = dgmoe.dg_moe_forward(layer.handle, x.data_ptr(), out.data_ptr(), T, None, 0, sp)
             assert st == 0, dgmoe.dg_moe_last_error()
 
-    # routing statistics of the benchmark batch (first layer)
-    dbg = layers[0].forward_debug(x)
+    # routing statistics of the benchmark batch: every layer's touched experts (the bytes it must read)
+    touched_l, max_load = [], 0
+    src = x
+    for l, layer in enumerate(layers if wl.layers > 1 else layers[:1]):
+        c = layer.forward_debug(src)["counts"].cpu()
+        touched_l.append(int((c > 0).sum()))
+        max_load = max(max_load, int(c.max()))
+        if wl.layers > 1:  # the next layer's input, as the timed steps form it
+            src = layer.forward(src, addend=deltas[l], add_input=True)
     torch.cuda.synchronize()
-    counts = dbg["counts"].cpu()
-    touched = int((counts > 0).sum())
-    max_load = int(counts.max())
-    print(f"[bench] {wl.name}: T={T} touched={touched} max_load={max_load} rotate={rotate} "
-          f"setup {time.perf_counter() - t_setup:.1f}s", file=sys.stderr, flush=True)
+    touched = touched_l[0]
+    print(f"[bench] {wl.name}: T={T} touched={touched_l if wl.layers > 1 else touched} max_load={max_load} "
+          f"rotate={rotate} setup {time.perf_counter() - t_setup:.1f}s", file=sys.stderr, flush=True)
 
     for i in range(args.warmup):
         step(i)
@@ -377,8 +443,21 @@ def main():
     print(f"[bench] timed {args.steps} steps: {ms_per_step * 1e3:.1f} us/step (wall {wall:.3f}s)",
           file=sys.stderr, flush=True)
 
-    # per-kernel durations: a second pass with events between the kernels (single-layer workloads)
-    kern_us = None
+    # per-step distribution: a second pass of the same steps, an event pair around each
+    step_stats = None
+    if not args.no_profile:
+        evs = ev.create(2 * args.steps)
+        for i in range(args.steps):
+            ev.record(evs[2 * i], sp)
+            step(i)
+            ev.record(evs[2 * i + 1], sp)
+        torch.cuda.synchronize()
+        step_stats = percentiles([ev.elapsed_ms(evs[2 * i], evs[2 * i + 1]) * 1e3 for i in range(args.steps)])
+        ev.destroy(evs)
+
+    # per-kernel durations: a third pass with events stamped by each kernel's dispatch (single-layer
+    # workloads)
+    kern_us, kern_stats = None, None
     n_prof = 0 if (args.no_profile or wl.layers > 1) else min(args.steps, 100)
     if n_prof:
         nk = len(KERNEL_NAMES)
@@ -389,35 +468,44 @@ def main():
                                                evs[2 * nk * i:2 * nk * (i + 1)], sp)
             assert st == 0, dgmoe.dg_moe_last_error()
         torch.cuda.synchronize()
-        tot = [0.0] * nk
-        for i in range(n_prof):
-            for k in range(nk):
-                tot[k] += ev.elapsed_ms(evs[2 * nk * i + 2 * k], evs[2 * nk * i + 2 * k + 1])
-        kern_us = {name: round(tot[k] / n_prof * 1e3, 2) for k, name in enumerate(KERNEL_NAMES)}
-        if layers[0].expert_norm_folded:  # no norm kernel ran: its events bracket nothing
-            kern_us["norm"] = 0.0
+        per = [[ev.elapsed_ms(evs[2 * nk * i + 2 * k], evs[2 * nk * i + 2 * k + 1]) * 1e3 for i in range(n_prof)]
+               for k in range(nk)]
+        kern_us = {name: round(sum(per[k]) / n_prof, 2) for k, name in enumerate(KERNEL_NAMES)}
+        kern_stats = {name: percentiles(per[k]) for k, name in enumerate(KERNEL_NAMES)}
+        kern_us["norm"] = 0.0  # no norm kernel runs (the router writes h): its events bracket nothing
+        kern_stats.pop("norm")
         if layers[0].gemms_fused:  # one launch ran both GEMMs: its time is under gate_up+down
             kern_us["gate_up+down"] = kern_us.pop("gate_up")
             kern_us.pop("down")
+            kern_stats["gate_up+down"] = kern_stats.pop("gate_up")
+            kern_stats.pop("down")
         ev.destroy(evs)
     ev.destroy([e0, e1])
 
     n_layers = wl.layers
-    layer_bytes, flops, gate_up_bytes, down_bytes = algorithmic(wl, T, touched)
+    layer_bytes = 0
+    for t_l in touched_l:
+        lb, flops, gemm_bytes, gate_up_bytes = algorithmic(wl, T, t_l)
+        layer_bytes += lb
+    layer_bytes_1, flops, gemm_bytes, gate_up_bytes = algorithmic(wl, T, touched)
     step_s = ms_per_step / 1e3
-    layer_gbps = layer_bytes * n_layers / step_s / 1e9  # stack: touched of layer 0 as the estimate
+    layer_gbps = layer_bytes / step_s / 1e9
     peak_tflops = F16_PEAK_TFLOPS if wl.experts in ("i4g128", "q8_0") else BF16_PEAK_TFLOPS
     roofline = None
     if kern_us:
-        # the dominant launch: gate_up, or the fused launch of both GEMMs
+        # the dominant launch: the fused launch of both GEMMs (or gate_up where they run apart); its
+        # algorithmic bytes are the touched experts' weights and the input rows
         kname = "gate_up+down" if "gate_up+down" in kern_us else "gate_up"
-        kbytes = gate_up_bytes + down_bytes if kname == "gate_up+down" else gate_up_bytes
+        kbytes = gemm_bytes if kname == "gate_up+down" else gate_up_bytes
         ach = kbytes / (kern_us[kname] / 1e6) / 1e9
-        traffic = read_traffic(wl.name, kname)
+        rec = read_counters(wl.name, kname) or {}
         roofline = {"bound": "hbm", "kernel": kname, "achieved": round(ach, 1), "peak": HBM_PEAK_GBPS,
                     "unit": "GB/s", "frac": round(ach / HBM_PEAK_GBPS, 4),
-                    "traffic": traffic, "alg_bytes_per_launch": kbytes,
+                    "traffic": rec.get("traffic_bytes_per_launch"), "alg_bytes_per_launch": kbytes,
                     "avg_launch_us": kern_us[kname]}
+        if rec.get("rocprof_avg_us"):
+            roofline["rocprof_avg_launch_us"] = rec["rocprof_avg_us"]
+            roofline["frac_rocprof"] = round(kbytes / (rec["rocprof_avg_us"] / 1e6) / 1e9 / HBM_PEAK_GBPS, 4)
 
     result = {
         "metric": METRIC,
@@ -438,11 +526,13 @@ def main():
                    "layers": n_layers, "weight_copies_rotated": rotate,
                    "expert_weights": "borrowed row-major" if args.borrow else "packed at create"},
         "roofline": roofline,
-        "layer": {"alg_bytes": layer_bytes * n_layers, "alg_flops": flops * n_layers,
+        "layer": {"alg_bytes": layer_bytes, "alg_flops": flops * n_layers,
                   "achieved_GBps": round(layer_gbps, 1), "hbm_frac": round(layer_gbps / HBM_PEAK_GBPS, 4),
                   "mfma_frac": round(flops * n_layers / step_s / 1e12 / peak_tflops, 4),
-                  "touched_experts": touched, "max_expert_load": max_load},
+                  "touched_experts": touched_l if n_layers > 1 else touched, "max_expert_load": max_load},
+        "step_us": step_stats,
         "kernels_us": kern_us,
+        "kernels_us_stats": kern_stats,
         "cpu_baseline": None,
     }
     if not args.no_cpu_baseline:

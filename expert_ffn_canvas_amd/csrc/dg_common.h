@@ -4,6 +4,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include "dg_moe.h"
+
 namespace dg {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
@@ -83,5 +85,14 @@ __device__ __forceinline__ uint32_t dpp(uint32_t v) {
 // joins two disjoint groups, the same two in both partners).
 constexpr int kDppXor1 = 0xb1, kDppXor2 = 0x4e, kDppHalfMirror = 0x141, kDppMirror = 0x140;
 __device__ __forceinline__ f16x8 as_f16x8(const u32x4& v) { return __builtin_bit_cast(f16x8, v); }
+
+// Index of the XCD (accelerator complex die) this wave runs on, from the
+// hardware register that holds it (HW_REG_XCC_ID, bits 3:0); 0..7 on MI355X.
+__device__ __forceinline__ int xcc_id() { return (int)(__builtin_amdgcn_s_getreg((3 << 11) | (0 << 6) | 20) & 7u); }
+
+// Sets bits of a sticky device status word (a vector atomic in global memory).
+__device__ __forceinline__ void raise_flag(uint32_t* flags, uint32_t bits) {
+  if (flags != nullptr) atomicOr(flags, bits);
+}
 
 }  // namespace dg

@@ -2,8 +2,8 @@
 // workspace allocated once at create time, router-weight preparation, and the
 // asynchronous launch sequence of one forward:
 //
-//   router (the expert input where it is materialised, then r + logits +
-//   top-k + weights)
+//   router (r + logits + top-k + weights, and the expert input where it is
+//   materialised)
 //   -> permutation (counts, offsets, tile list, stable scatter)
 //   -> gate_up grouped GEMM (+ GELU-tanh gating)
 //   -> down grouped GEMM (x routing weight)
@@ -55,7 +55,7 @@ size_t act_elem_bytes(int dt) { return dt == DG_F32 ? 4 : 2; }
 // Sub-buffer layout of the workspace (byte offsets from the base).
 struct Layout {
   size_t h, rnorm, logits, tile_count, topk_idx, topk_w, counts, offsets, tasks[2], qlen, sorted_slot, row_of_slot, act,
-      y, tile_done;
+      y, tile_done, dev_flags;
   size_t wr, bias, gamma_e;
   size_t total;
   int Epad, nb[2], qmax[2];  // per GEMM (gate_up, down): column blocks, queue capacity
@@ -83,7 +83,8 @@ Layout plan(const dg_moe_config& c) {
   L.fold = folds_expert_norm(c);
   L.nb[0] = dg::gate_up_blocks((int)F);
   L.nb[1] = dg::down_blocks((int)D);
-  for (int g = 0; g < 2; ++g) L.qmax[g] = dg::max_queue_len((int)T, (int)K, (int)E, L.nb[g]);
+  // the shortest tiles give the longest queues
+  for (int g = 0; g < 2; ++g) L.qmax[g] = dg::max_queue_len((int)T, (int)K, (int)E, L.nb[g], dg::kTileRows);
   size_t off = 0;
   auto take = [&](size_t bytes) {
     const size_t at = off;
@@ -93,18 +94,19 @@ Layout plan(const dg_moe_config& c) {
   L.h = take(L.fold ? 0 : T * D * 2);
   L.rnorm = take(T * 4);
   L.logits = take(T * (size_t)L.Epad * 4);
-  L.tile_count = take((T + 15) / 16 * 4);
+  L.tile_count = take((T + 15) / 16 * 8);
   L.topk_idx = take(T * K * 4);
   L.topk_w = take(T * K * 4);
   L.counts = take(E * 4);
   L.offsets = take((E + 1) * 4);
   for (int g = 0; g < 2; ++g) L.tasks[g] = take((size_t)L.qmax[g] * dg::kQueues * sizeof(dg::Tile));
-  L.qlen = take(2 * dg::kQueues * 4);
+  L.qlen = take((2 * dg::kQueues + 2) * 4);  // the queue lengths, then the two capacities
   L.sorted_slot = take(K * T * 4);
   L.row_of_slot = take(K * T * 4);
   L.act = take(K * T * F * 2);
   L.y = take(K * T * D * 2);
-  L.tile_done = take(fuses_gemms(c) ? K * T * 4 : 0);
+  L.tile_done = take(fuses_gemms(c) ? K * T * 8 : 0);
+  L.dev_flags = take(4);
   L.wr = take((size_t)L.Epad * D * 4);
   L.bias = take(E * 4);
   L.gamma_e = take(D * 4);
@@ -351,10 +353,11 @@ dg_status dg_moe_create(const dg_moe_config* cfg, const dg_moe_weights* w, void*
       return hip_fail(ci, "preparing router parameters");
     }
   }
-  e = hipMemsetAsync(hd->ws + hd->L.tile_count, 0, ((size_t)cfg->max_tokens + 15) / 16 * 4, stream);
+  e = hipMemsetAsync(hd->ws + hd->L.tile_count, 0, ((size_t)cfg->max_tokens + 15) / 16 * 8, stream);
+  if (e == hipSuccess) e = hipMemsetAsync(hd->ws + hd->L.dev_flags, 0, 4, stream);
   if (e != hipSuccess) {
     dg_moe_destroy(hd);
-    return hip_fail(e, "create: clearing the arrival counters");
+    return hip_fail(e, "create: clearing the arrival counters and the status word");
   }
   e = hipStreamSynchronize(stream);
   if (e != hipSuccess) {
@@ -415,17 +418,16 @@ static dg_status run_forward(dg_moe_handle hd, const void* x, void* out, int32_t
   ra.h = L.fold ? nullptr : hd->at<uint16_t>(L.h);
   ra.rnorm = hd->at<float>(L.rnorm);
   ra.logits = hd->at<float>(L.logits);
-  ra.tile_count = hd->at<int32_t>(L.tile_count);
+  ra.tile_count = hd->at<uint64_t>(L.tile_count);
   ra.topk_idx = hd->at<int32_t>(L.topk_idx);
   ra.topk_w = hd->at<float>(L.topk_w);
+  ra.dev_flags = hd->at<uint32_t>(L.dev_flags);
   hipError_t e = hipSuccess;
-  if (!L.fold) {
-    e = dg::launch_norm(ra, stream, ev(0));
-  } else if (events) {  // no norm kernel: its two events mark the same point
+  if (events) {  // the router writes the expert input: the norm's two events mark the same point
     e = hipEventRecord(kev[0].start, stream);
     if (e == hipSuccess) e = hipEventRecord(kev[0].stop, stream);
   }
-  if (e != hipSuccess) return hip_fail(e, "norm launch");
+  if (e != hipSuccess) return hip_fail(e, "event record");
   e = dg::launch_logits(ra, stream, ev(1));
   if (e != hipSuccess) return hip_fail(e, "router launch");
 
@@ -438,10 +440,10 @@ static dg_status run_forward(dg_moe_handle hd, const void* x, void* out, int32_t
   const bool fused = fuses_gemms(c);
   pa.tile_rows = tall ? dg::kTallRows : dg::kTileRows;
   pa.deal = fused ? dg::kDealBalanced : tall ? dg::kDealExperts : dg::kDealUnits;
-  pa.tile_done = fused ? hd->at<int32_t>(L.tile_done) : nullptr;
+  pa.tile_done = fused ? hd->at<uint64_t>(L.tile_done) : nullptr;
   for (int g = 0; g < 2; ++g) {
     pa.nb[g] = L.nb[g];
-    pa.qmax[g] = dg::max_queue_len(T, c.top_k, c.n_experts, L.nb[g]);
+    pa.qmax[g] = dg::max_queue_len(T, c.top_k, c.n_experts, L.nb[g], pa.tile_rows);
     pa.tasks[g] = hd->at<dg::Tile>(L.tasks[g]);
   }
   pa.counts = hd->at<int32_t>(L.counts);
@@ -449,6 +451,7 @@ static dg_status run_forward(dg_moe_handle hd, const void* x, void* out, int32_t
   pa.qlen = hd->at<int32_t>(L.qlen);
   pa.sorted_slot = hd->at<int32_t>(L.sorted_slot);
   pa.row_of_slot = hd->at<int32_t>(L.row_of_slot);
+  pa.dev_flags = ra.dev_flags;
   e = dg::launch_permute(pa, stream, ev(2));
   if (e != hipSuccess) return hip_fail(e, "permute launch");
 
@@ -478,6 +481,7 @@ static dg_status run_forward(dg_moe_handle hd, const void* x, void* out, int32_t
     fa.dn.qmax = pa.qmax[1];
     fa.tile_done = pa.tile_done;
     fa.nb_gate_up = L.nb[0];
+    fa.dev_flags = ra.dev_flags;
     e = mx4  ? dg::launch_gemm_fused_mx4(fa, stream, ev(3))
         : mx8 ? dg::launch_gemm_fused_mx8(fa, stream, ev(3))
         : q8 ? dg::launch_gemm_fused_q8(fa, stream, ev(3))
@@ -525,7 +529,9 @@ static dg_status run_forward(dg_moe_handle hd, const void* x, void* out, int32_t
                {dbg->counts, L.counts, (size_t)c.n_experts * 4},
                {dbg->offsets, L.offsets, (size_t)(c.n_experts + 1) * 4},
                {dbg->sorted_slot, L.sorted_slot, tk * 4},
-               {dbg->row_of_slot, L.row_of_slot, tk * 4}};
+               {dbg->row_of_slot, L.row_of_slot, tk * 4},
+               {dbg->queue_len, L.qlen, (2 * dg::kQueues + 2) * 4},
+               {dbg->dev_flags, L.dev_flags, 4}};
     for (const Cp& cp : cps) {
       if (!cp.dst) continue;
       e = hipMemcpyAsync(cp.dst, hd->ws + cp.off, cp.bytes, hipMemcpyDeviceToDevice, stream);
@@ -608,12 +614,11 @@ bool spans_overlap(const void* a, size_t na, const void* b, size_t nb) {
   return x < y + nb && y < x + na;
 }
 
-dg_status head_launch(dg_head_handle hd, const void* h, int32_t T, float beta, float* logits, float* entropy,
-                      int32_t* argmax, float* mean_entropy, void* const* events, void* stream_v) {
-  if (!hd) return fail(DG_ERR_INVALID_ARG, "handle is NULL");
+// Checks the arguments of one call of the stage (config c, T positions); DG_OK or the error.
+dg_status head_check_call(const dg_head_config& c, const void* h, int32_t T, float beta, float* logits,
+                          float* entropy, int32_t* argmax, float* mean_entropy, void* const* events) {
   if (!h || !entropy || !argmax) return fail(DG_ERR_INVALID_ARG, "h, entropy or argmax is NULL");
   if (!(beta > 0.0f) || !std::isfinite(beta)) return fail(DG_ERR_INVALID_ARG, "beta must be finite and > 0");
-  const dg_head_config& c = hd->cfg;
   if (T < 0 || T > c.max_tokens) return fail(DG_ERR_SHAPE, "T = %d not in [0, max_tokens = %d]", T, c.max_tokens);
   if (!aligned16(h)) return fail(DG_ERR_ALIGN, "h is not 16-byte aligned");
   const void* outs[] = {logits, entropy, argmax, mean_entropy};
@@ -631,12 +636,19 @@ dg_status head_launch(dg_head_handle hd, const void* h, int32_t T, float beta, f
     for (int i = 0; i < 6; ++i)
       if (!events[i]) return fail(DG_ERR_INVALID_ARG, "event %d is NULL", i);
   }
-  if (T == 0) return ok();
+  return DG_OK;
+}
+
+// Enqueues the stage (arguments already checked, T > 0) with the per-tile
+// partials in five arrays of `pb` bytes from `ws` (each laid out [T][nvb]).
+dg_status head_enqueue(const dg_head_config& c, const void* emb, int n_cu, char* ws, size_t pb, const void* h,
+                       int32_t T, float beta, float* logits, float* entropy, int32_t* argmax, float* mean_entropy,
+                       void* const* events, void* stream_v) {
   hipStream_t stream = static_cast<hipStream_t>(stream_v);
   dg::HeadArgs a{};
   a.h = static_cast<const uint16_t*>(h);
-  a.emb = hd->emb;
-  a.n_wg = hd->n_cu;
+  a.emb = static_cast<const uint16_t*>(emb);
+  a.n_wg = n_cu;
   a.T = T;
   a.V = c.vocab;
   a.D = c.d_model;
@@ -645,13 +657,11 @@ dg_status head_launch(dg_head_handle hd, const void* h, int32_t T, float beta, f
   a.entropy = entropy;
   a.argmax = argmax;
   a.mean_entropy = mean_entropy;
-  const size_t pb = head_part_bytes(c);
-  // partials laid out [T][nvb] (a prefix of each array)
-  a.part_m = reinterpret_cast<float*>(hd->ws);
-  a.part_s = reinterpret_cast<float*>(hd->ws + pb);
-  a.part_u = reinterpret_cast<float*>(hd->ws + 2 * pb);
-  a.part_best = reinterpret_cast<float*>(hd->ws + 3 * pb);
-  a.part_id = reinterpret_cast<int32_t*>(hd->ws + 4 * pb);
+  a.part_m = reinterpret_cast<float*>(ws);
+  a.part_s = reinterpret_cast<float*>(ws + pb);
+  a.part_u = reinterpret_cast<float*>(ws + 2 * pb);
+  a.part_best = reinterpret_cast<float*>(ws + 3 * pb);
+  a.part_id = reinterpret_cast<int32_t*>(ws + 4 * pb);
   dg::KernelEvents kev[3];
   if (events)
     for (int i = 0; i < 3; ++i) {
@@ -666,6 +676,17 @@ dg_status head_launch(dg_head_handle hd, const void* h, int32_t T, float beta, f
     if (e != hipSuccess) return hip_fail(e, "event record");
   }
   return ok();
+}
+
+dg_status head_launch(dg_head_handle hd, const void* h, int32_t T, float beta, float* logits, float* entropy,
+                      int32_t* argmax, float* mean_entropy, void* const* events, void* stream) {
+  if (!hd) return fail(DG_ERR_INVALID_ARG, "handle is NULL");
+  const dg_status st = head_check_call(hd->cfg, h, T, beta, logits, entropy, argmax, mean_entropy, events);
+  if (st != DG_OK) return st;
+  if (T == 0) return ok();
+  // partials laid out [T][nvb] (a prefix of each array sized for max_tokens)
+  return head_enqueue(hd->cfg, hd->emb, hd->n_cu, hd->ws, head_part_bytes(hd->cfg), h, T, beta, logits, entropy,
+                      argmax, mean_entropy, events, stream);
 }
 
 }  // namespace

@@ -95,7 +95,12 @@ __device__ __forceinline__ void lds_barrier() {
 // is running or done and never waits itself. The wait is bounded (about a
 // tenth of a second): past it the task writes NaN for its outputs instead of
 // its product, so a broken assumption shows in the result and the launch
-// still ends. gate_up(tile) and down(tile) run one task's product.
+// still ends; it also raises DG_DEV_WAIT_TIMEOUT. The dispatcher may start a
+// launch's round robin on any XCD (workgroup b then runs on XCD (b + c) % 8
+// for a c fixed within the launch), which keeps every queue on one XCD. Each
+// gate_up task also counts itself under the XCD it ran on, and a down task
+// whose tile's gate_up tasks did not all run on its own XCD raises
+// DG_DEV_XCD_GEMM. gate_up(tile) and down(tile) run one task's product.
 constexpr int kWaitPolls = 1 << 17;
 
 template <typename GateUp, typename Down>
@@ -109,26 +114,31 @@ __device__ __forceinline__ void fused_tasks(const FusedGemmArgs& f, GateUp gate_
     gate_up(tl);
     __builtin_amdgcn_s_waitcnt(0);  // this thread's stores have reached L2
     __syncthreads();
-    if (tid == 0) atomicAdd(&f.tile_done[tl.row0], 1);
+    if (tid == 0)
+      atomicAdd(reinterpret_cast<unsigned long long*>(&f.tile_done[tl.row0]), 1ull | (1ull << (8 + 7 * xcc_id())));
     return;
   }
   const int jd = j - ngu;
   if (jd >= f.dn.qlen[qx]) return;
   const Tile tl = f.dn.tiles[(size_t)qx * f.dn.qmax + jd];
+  const unsigned long long need = (unsigned long long)f.nb_gate_up;  // <= 64
+  unsigned long long* cnt = reinterpret_cast<unsigned long long*>(&f.tile_done[tl.row0]);
   if (tid == 0) {
-    const int need = f.nb_gate_up;
+    unsigned long long v = 0;
     int n = 0;
-    while (atomicAdd(&f.tile_done[tl.row0], 0) < need && n < kWaitPolls) {
+    while (((v = atomicAdd(cnt, 0ull)) & 0xffull) < need && n < kWaitPolls) {
       __builtin_amdgcn_s_sleep(8);
       ++n;
     }
     ready = n < kWaitPolls;
+    if (ready && ((v >> (8 + 7 * xcc_id())) & 127ull) != need) raise_flag(f.dev_flags, DG_DEV_XCD_GEMM);
   }
   __syncthreads();
   if (ready) {
     down(tl);
     return;
   }
+  if (tid == 0) raise_flag(f.dev_flags, DG_DEV_WAIT_TIMEOUT);
   const int cols = 32 * kWaves;
   for (int i = tid; i < tl.mc * cols; i += kThreads)
     f.dn.y[(size_t)(tl.row0 + i / cols) * f.dn.D + tl.nb * cols + i % cols] = 0x7fc0;  // bf16 NaN

@@ -36,15 +36,24 @@ inline bool use_tall_tiles(int T, int K, int E) { return (long)T * K >= 64L * E;
 constexpr int kQueues = 8;
 
 // Upper bound on the length of one task queue of a GEMM with NB column blocks
-// for T tokens. Every deal keeps each queue within one unit of the mean: round
-// robin over units of non-increasing size, and the balanced deal (each expert
-// to the least loaded queue, then level filling) alike. The largest unit is
-// all NB blocks of one expert's tiles, at most NB ceil(T / 64) tasks (tall
-// tiles are fewer), and the tile count never exceeds K T / 64 + E.
-inline int max_queue_len(int T, int K, int E, int NB) {
-  const long max_tiles = ((long)K * T + kTileRows - 1) / kTileRows + E;
-  const long largest_unit = (long)NB * ((T + kTileRows - 1) / kTileRows);
-  return (int)(((long)NB * max_tiles + kQueues - 1) / kQueues + largest_unit);
+// for T tokens cut into tiles of at most R rows. The tile count is at most
+// K T / R + E (each expert's ceil(M_e / R) exceeds M_e / R by less than one),
+// and one expert holds at most ceil(T / R) tiles (a token routes to it once).
+// Every deal keeps each queue within twice that of the mean, in tiles:
+//  * round robin over units of non-increasing size (the unit deal, the deal
+//    by expert): within one unit of the mean;
+//  * the balanced deal: the experts with more than the smallest tile count v1
+//    are dealt in snake order of that count, non-increasing, which keeps any
+//    two queues within the largest count of each other; the experts of v1
+//    tiles then fill the least loaded levels, after which a queue that took
+//    some ends below the common level plus 2 v1, and one that took none is
+//    where the snake left it.
+// The permutation still clamps a queue at this length and raises
+// DG_DEV_QUEUE_OVERFLOW if it ever had to.
+inline int max_queue_len(int T, int K, int E, int NB, int R) {
+  const long max_tiles = ((long)K * T + R - 1) / R + E;
+  const long largest_unit = (long)NB * ((T + R - 1) / R);
+  return (int)(((long)NB * max_tiles + kQueues - 1) / kQueues + 2 * largest_unit);
 }
 
 // Column blocks of the two GEMMs: gate_up tasks cover 64 features (their gate
@@ -61,16 +70,17 @@ struct RouterArgs {
   const float* gamma_e;
   float eps;
   int h_f16;            // expert input stored as fp16 (int4 or Q8_0 experts) instead of bf16
-  uint16_t* h;          // [T, D] expert input (norm kernel only)
+  uint16_t* h;          // [T, D] expert input, or null where the GEMM reads x (the norm folded)
   float* rnorm;         // [T] r = 1/sqrt(mean x^2 + eps) of each token
   float* logits;        // [T, Epad]
-  int32_t* tile_count;  // [ceil(T / 16)] arrival counters of the logits kernel, zero between forwards
+  uint64_t* tile_count; // [ceil(T / 16)] arrival counters of the logits kernel, zero between forwards: the
+                        // arrivals in bits 0..7, and per XCD x the arrivals from it in bits 8 + 6 x ..
   int32_t* topk_idx;    // [T, K]
   float* topk_w;        // [T, K]
+  uint32_t* dev_flags;  // sticky device status word (DG_DEV_* bits of dg_moe.h)
 };
-// h = x r (1 + gamma_e).
-hipError_t launch_norm(const RouterArgs& a, hipStream_t stream, const KernelEvents* ev);
-// r, logits, top-k and the routing weights.
+// r, logits, top-k and the routing weights, and h = x r (1 + gamma_e) where h
+// is not null.
 hipError_t launch_logits(const RouterArgs& a, hipStream_t stream, const KernelEvents* ev);
 // Create time: W' in fp32 from the router weight (fp32 or bf16 [E, D]) and gamma_r [D].
 // Layout: 2 KB block (expert tile et, 32-column step s) holds, for lane
@@ -92,16 +102,17 @@ struct PermuteArgs {
   int T, K, E;
   int tile_rows;          // largest rows per tile: kTileRows, or kTallRows for the tall GEMMs
   int deal;               // kDealUnits, kDealExperts or kDealBalanced
-  int32_t* tile_done;     // kDealBalanced: [K T], zeroed at the first row of every tile (the fused
+  uint64_t* tile_done;    // kDealBalanced: [K T], zeroed at the first row of every tile (the fused
                           // GEMM's per-tile counters); else null
   int nb[2];              // column blocks of gate_up and down
   int qmax[2];            // capacity of each queue of gate_up and down
   int32_t* counts;        // [E]
   int32_t* offsets;       // [E + 1]
   Tile* tasks[2];         // [kQueues][qmax] each: task p of queue x at tasks[x * qmax + p]
-  int32_t* qlen;          // [2][kQueues]
+  int32_t* qlen;          // [2][kQueues] queue lengths, then qmax[0], qmax[1]
   int32_t* sorted_slot;   // [K T] slot t K + j of each expert-sorted row
   int32_t* row_of_slot;   // [K T]
+  uint32_t* dev_flags;    // sticky device status word (DG_DEV_* bits of dg_moe.h)
 };
 hipError_t launch_permute(const PermuteArgs& a, hipStream_t stream, const KernelEvents* ev);
 
@@ -139,8 +150,10 @@ hipError_t launch_pack_panels(const uint16_t* src, uint16_t* dst, int E, int R, 
 // gate_up blocks of its tile through tile_done (zeroed by the permutation).
 struct FusedGemmArgs {
   GemmArgs gu, dn;
-  int32_t* tile_done;  // [K T] per tile, at its first row: gate_up tasks finished
+  uint64_t* tile_done; // [K T] per tile, at its first row: gate_up tasks finished in bits 0..7, and per
+                       // XCD x those that ran there in bits 8 + 7 x ..
   int nb_gate_up;      // gate_up column blocks per tile
+  uint32_t* dev_flags; // sticky device status word (DG_DEV_* bits of dg_moe.h)
 };
 hipError_t launch_gemm_fused(const FusedGemmArgs& f, bool tall, hipStream_t stream, const KernelEvents* ev);
 // Create-time relayout of int4-g128 expert weights (codes [E][R][K/2], scales

@@ -18,9 +18,10 @@
 //    to within one unit. With tall tiles the deal is by expert instead (all
 //    column blocks of rank r go to queue r % 8): an expert's tiles then share
 //    its activation rows, hundreds of them, in one L2. For the fused GEMM
-//    whole experts are dealt in id order so that the queues' tile counts
-//    balance, the same expert to the same queue in both task lists, and the
-//    per-tile counters of that GEMM are zeroed;
+//    whole experts are dealt so that the queues' tile counts balance (the
+//    larger experts in snake order, the rest level by level in id order), the same
+//    expert to the same queue in both task lists, each queue laid out in
+//    expert id order, and the per-tile counters of that GEMM are zeroed;
 //  * the stable scatter: the rows of expert e hold its slots in increasing
 //    token order; sorted_slot[row] = t k + j (token t, slot j) and
 //    row_of_slot[t k + j] = row.
@@ -78,31 +79,57 @@ __device__ __forceinline__ void load_ids(const int32_t* idx, int t, int K, int (
   }
 }
 
-// Balanced deal of whole experts, in expert id order: qof[e] = queue of
-// expert e. v1 is the smallest nonzero tile count. The experts with more
-// tiles are dealt in snake order (queues 0..7, then 7..0, ...); then the
-// experts of v1 tiles fill the least loaded queues level by level: with queue
-// q at level Lq = (tiles so far) / v1, the i-th of them takes the i-th
+// Balanced deal of whole experts: qof[e] = queue of expert e. v1 is the
+// smallest nonzero tile count. The experts with more tiles ("larger") are
+// dealt in snake order (queues 0..7, then 7..0, ...) by id; the experts of v1
+// tiles then fill the least loaded queues level by level, in id order: with
+// queue q at level Lq = (tiles so far) / v1, the i-th of them takes the i-th
 // smallest pair (Lq + k, q), k = 0, 1, ..., found by a binary search on the
-// level, so consecutive ones go to different queues. Deterministic, so both
-// task lists agree. Called by every thread of the block; expert e is thread e.
-__device__ void deal_balanced(const int* ntile, int E, int tid, int lane, int wave, int* qof, int* sh) {
+// level, so consecutive ones go to different queues.
+// Dealt by id, the larger experts can pile up on one queue (under a skew that
+// tracks the ids they come nearly in order of size, but not in general). So
+// if the most loaded queue then exceeds an even share of all tiles by more
+// than the largest expert, the larger experts are dealt again in snake order
+// of their rank by count (descending, ties to the lower id; the larger
+// experts hold exactly the ranks before all others; rank fills crank): dealt
+// in non-increasing size, the snake keeps any two queues within the largest
+// tile count of each other. Either way the larger experts leave no queue
+// above the even share plus the largest count, and the level filling then
+// leaves none above the even share plus twice the largest count (a queue that
+// takes some ends below the common level plus 2 v1): the queues' capacity.
+// Deterministic, so both task lists agree. Called by every thread of the
+// block; expert e is thread e.
+template <typename Rank>
+__device__ void deal_balanced(const int* ntile, int* crank, int E, int tid, int lane, int wave, int* qof, int* sh,
+                              Rank rank) {
   int* load = sh;       // [kQueues] tiles of the larger experts per queue
   int* wmin = sh + 8;   // [4] per wave: smallest nonzero count
   int* hcnt = sh + 12;  // [4] per wave: larger experts
   int* tcnt = sh + 16;  // [4] per wave: experts of v1 tiles
+  int* wsum = sh + 20;  // [4] per wave: tiles
+  int* wmax = sh + 24;  // [4] per wave: largest count
   const int e = tid;
   const bool mine = wave < kMaxE / 64;
   const int v = (e < E) ? ntile[e] : 0;
   if (tid < kQueues) load[tid] = 0;
   if (mine) {
-    int m = v > 0 ? v : 0x7fffffff;
-    for (int d = 32; d >= 1; d >>= 1) m = min(m, __shfl_xor(m, d));
-    if (lane == 0) wmin[wave] = m;
+    int m = v > 0 ? v : 0x7fffffff, sm = v, mx = v;
+    for (int d = 32; d >= 1; d >>= 1) {
+      m = min(m, __shfl_xor(m, d));
+      sm += __shfl_xor(sm, d);
+      mx = max(mx, __shfl_xor(mx, d));
+    }
+    if (lane == 0) {
+      wmin[wave] = m;
+      wsum[wave] = sm;
+      wmax[wave] = mx;
+    }
   }
   __syncthreads();
   const int v1 = min(min(wmin[0], wmin[1]), min(wmin[2], wmin[3]));
   if (v1 == 0x7fffffff) return;  // no expert has rows
+  const int total = (wsum[0] + wsum[1]) + (wsum[2] + wsum[3]);
+  const int a_max = max(max(wmax[0], wmax[1]), max(wmax[2], wmax[3]));
   const bool heavy = mine && v > v1, tail = mine && v == v1;
   const uint64_t below = (1ull << lane) - 1ull;
   uint64_t hb = 0, tb = 0;
@@ -120,13 +147,22 @@ __device__ void deal_balanced(const int* ntile, int E, int tid, int lane, int wa
     hbase += (w < wave) ? hcnt[w] : 0;
     tbase += (w < wave) ? tcnt[w] : 0;
   }
-  if (heavy) {
-    const int h = hbase + __popcll(hb & below);
-    const int q = ((h / kQueues) & 1) ? kQueues - 1 - h % kQueues : h % kQueues;
-    qof[e] = q;
-    atomicAdd(&load[q], v);
-  }
+  auto snake = [](int h) { return ((h / kQueues) & 1) ? kQueues - 1 - h % kQueues : h % kQueues; };
+  if (heavy) atomicAdd(&load[snake(hbase + __popcll(hb & below))], v);
   __syncthreads();
+  int hmax = 0;
+#pragma unroll
+  for (int q = 0; q < kQueues; ++q) hmax = max(hmax, load[q]);
+  if (hmax > (total + kQueues - 1) / kQueues + a_max) {
+    // the larger experts again, in order of size (the same decision in every thread)
+    rank(crank);
+    __syncthreads();
+    if (tid < kQueues) load[tid] = 0;
+    __syncthreads();
+    if (heavy) atomicAdd(&load[snake(crank[e])], v);
+    __syncthreads();
+  }
+  if (heavy) qof[e] = snake(crank[e] >= 0 ? crank[e] : hbase + __popcll(hb & below));
   if (tail) {
     const int i = tbase + __popcll(tb & below);
     int lv[kQueues], lmin = 0x7fffffff;
@@ -157,6 +193,30 @@ __device__ void deal_balanced(const int* ntile, int E, int tid, int lane, int wa
     }
     qof[e] = pick;
   }
+}
+
+// Rank of each expert by (count desc, id asc), four lanes per expert: lane q
+// reads the counts 16 i + 4 q .. + 3 (consecutive lanes, consecutive banks)
+// and compares against them. Calls rank_out(e, r) for e < E.
+template <typename Out>
+__device__ __forceinline__ void rank_experts(const int* cnt, int E, int tid, Out rank_out) {
+  const int e = tid >> 2, q = tid & 3;
+  const int ce = (e < E) ? cnt[e] : 0;
+  int r = 0;
+#pragma unroll
+  for (int i = 0; i < kMaxE / 16; ++i) {
+    if (16 * i >= E) break;
+    const int4 c4 = *reinterpret_cast<const int4*>(&cnt[16 * i + 4 * q]);
+    const int cc[4] = {c4.x, c4.y, c4.z, c4.w};
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      const int e2 = 16 * i + 4 * q + k;
+      r += (e2 < E) && ((cc[k] > ce) || (cc[k] == ce && e2 < e));
+    }
+  }
+  r += __shfl_xor(r, 1);
+  r += __shfl_xor(r, 2);
+  if (q == 0 && e < E) rank_out(e, r);
 }
 
 // The stable scatter, kThreads tokens at a time: lane masks per (wave,
@@ -226,6 +286,7 @@ __global__ __launch_bounds__(kThreads) void k_permute(PermuteArgs a) {
   __shared__ int base[kMaxE];
   __shared__ int cursor[kMaxE];
   __shared__ int order[kMaxE];
+  __shared__ int crank[kMaxE];  // kDealBalanced: rank of each expert by (count desc, id asc)
   __shared__ int qof[kMaxE];  // kDealBalanced: queue of each expert (rank = id)
   __shared__ int dshare[32];  // kDealBalanced: queue loads and per-wave counts
   __shared__ int ntile[kMaxE];
@@ -288,39 +349,29 @@ __global__ __launch_bounds__(kThreads) void k_permute(PermuteArgs a) {
       ntile[tid] = (c + a.tile_rows - 1) / a.tile_rows;
     }
   }
+  if (role == 0 && tid < 2) a.qlen[2 * kQueues + tid] = a.qmax[tid];  // the queue capacities, for inspection
   if (role == 2 * kQueues) {
     scatter(a, ids, cursor, masks, wpre, stage, staged, tid, lane, wave);
     return;
   }
-  // --- rank of expert e by (count desc, id asc): four lanes per expert; lane
-  // q reads the counts 16 i + 4 q .. + 3 (consecutive lanes, consecutive
-  // banks) and compares against them. The balanced deal needs no size order:
-  // it deals in expert id order (rank = id).
+  // --- the deal. The unit deal and the deal by expert lay their queues out in
+  // the experts' order by count; the balanced deal lays them out in id order
+  // and deals its larger experts by id, which is fast and almost always within
+  // the queues' capacity. If it is not (the largest queue, in tasks of either
+  // GEMM, over that GEMM's capacity), the larger experts are dealt again in
+  // order of size, which provably fits (the capacity's bound). Both task-list
+  // workgroups of a queue take the same decision.
   if (a.deal == kDealBalanced) {
-    if (tid < kMaxE) order[tid] = tid;
-  } else {
-    const int e = tid >> 2, q = tid & 3;
-    const int ce = (e < E) ? cnt[e] : 0;
-    int r = 0;
-#pragma unroll
-    for (int i = 0; i < kMaxE / 16; ++i) {
-      if (16 * i >= E) break;
-      const int4 c4 = *reinterpret_cast<const int4*>(&cnt[16 * i + 4 * q]);
-      const int cc[4] = {c4.x, c4.y, c4.z, c4.w};
-#pragma unroll
-      for (int k = 0; k < 4; ++k) {
-        const int e2 = 16 * i + 4 * q + k;
-        r += (e2 < E) && ((cc[k] > ce) || (cc[k] == ce && e2 < e));
-      }
+    if (tid < kMaxE) {
+      order[tid] = tid;
+      qof[tid] = 0;
+      crank[tid] = -1;  // no rank by size unless the deal by id is set aside
     }
-    r += __shfl_xor(r, 1);
-    r += __shfl_xor(r, 2);
-    if (q == 0 && e < E) order[r] = e;
-  }
-  if (a.deal == kDealBalanced) {
-    if (tid < kMaxE) qof[tid] = 0;
     __syncthreads();
-    deal_balanced(ntile, E, tid, lane, wave, qof, dshare);
+    deal_balanced(ntile, crank, E, tid, lane, wave, qof, dshare,
+                  [&](int* cr) { rank_experts(cnt, E, tid, [&](int e, int r) { cr[e] = r; }); });
+  } else {
+    rank_experts(cnt, E, tid, [&](int e, int r) { order[r] = e; });
   }
   __syncthreads();
 
@@ -357,7 +408,10 @@ __global__ __launch_bounds__(kThreads) void k_permute(PermuteArgs a) {
   }
   __syncthreads();
   const int len = min(pre[E], a.qmax[g]);
-  if (tid == 0) a.qlen[g * kQueues + x] = len;
+  if (tid == 0) {
+    a.qlen[g * kQueues + x] = len;
+    if (pre[E] > a.qmax[g]) raise_flag(a.dev_flags, DG_DEV_QUEUE_OVERFLOW);
+  }
 
   // --- the tasks of the queue, one lane per position p, stored at
   // tasks[x qmax + p] (consecutive lanes, consecutive entries). The lane

@@ -9,11 +9,12 @@
 //          fp32: the logits have fp32 dot-product accuracy. Then per token the
 //          k largest logits (ties: lower expert id), in that order, with their
 //          softmax renormalised over the k.
-//  norm:   only where the expert input has to be materialised (fp32
-//          activations, int4 experts, borrowed weights): r again and
-//          h = x r (1 + gamma_e), bf16 (fp16 for int4 experts). Otherwise the
-//          gate_up GEMM reads x itself, with (1 + gamma_e) folded into its
-//          packed weight and r applied to its sums.
+//          Where the expert input has to be materialised (fp32 activations,
+//          quantised or borrowed experts), the same kernel also writes
+//          h = x r (1 + gamma_e), bf16 (fp16 for int4 and Q8_0 experts): each
+//          workgroup of a token tile writes its share of the columns once r is
+//          known. Otherwise the gate_up GEMM reads x itself, with (1 + gamma_e)
+//          folded into its packed weight and r applied to its sums.
 //
 // Sources: Quant-Tuner PR "Add DiffusionGemma (Gemma-4 MoE block-diffusion)
 // support", "Answers to the motivating questions" (the router reads the raw
@@ -134,6 +135,47 @@ __device__ __forceinline__ float sumsq8(const u32x4& v) {
   return s;
 }
 
+// The expert input h = x r (1 + gamma_e) of rows t0 .. t0 + ROWS - 1 (r from
+// rs), columns of 8-wide segments [s0, s1): one 16-byte store per segment.
+template <bool XF32, int ROWS>
+__device__ __forceinline__ void write_h(const RouterArgs& a, const float* rs, int t0, int s0, int s1, int tid,
+                                        int nthreads) {
+  const int ns = s1 - s0;
+  const int D = a.D;
+  for (int i = tid; i < ROWS * ns; i += nthreads) {
+    const int row = i / ns, sg = s0 + i % ns;
+    const int t = t0 + row;
+    if (t >= a.T) continue;
+    const size_t at = (size_t)t * D + sg * 8;
+    float f[8];
+    if constexpr (XF32) {
+      const float4 v0 = *reinterpret_cast<const float4*>(static_cast<const float*>(a.x) + at);
+      const float4 v1 = *reinterpret_cast<const float4*>(static_cast<const float*>(a.x) + at + 4);
+      f[0] = v0.x; f[1] = v0.y; f[2] = v0.z; f[3] = v0.w;
+      f[4] = v1.x; f[5] = v1.y; f[6] = v1.z; f[7] = v1.w;
+    } else {
+      const u32x4 v = *reinterpret_cast<const u32x4*>(static_cast<const uint16_t*>(a.x) + at);
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        f[2 * k] = bf16_lo(v[k]);
+        f[2 * k + 1] = bf16_hi(v[k]);
+      }
+    }
+    const float4 g0 = *reinterpret_cast<const float4*>(a.gamma_e + sg * 8);
+    const float4 g1 = *reinterpret_cast<const float4*>(a.gamma_e + sg * 8 + 4);
+    const float g[8] = {g0.x, g0.y, g0.z, g0.w, g1.x, g1.y, g1.z, g1.w};
+    const float r = rs[row];
+    u32x4 ho;
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      const float h0 = f[2 * k] * r * (1.0f + g[2 * k]);
+      const float h1 = f[2 * k + 1] * r * (1.0f + g[2 * k + 1]);
+      ho[k] = a.h_f16 ? pack_f16x2(h0, h1) : pack_bf16x2(h0, h1);
+    }
+    *reinterpret_cast<u32x4*>(a.h + at) = ho;
+  }
+}
+
 // Workgroup (token tile tt, expert tile et): 16 MT tokens x 16 experts, 8
 // waves; wave h owns the 128-column chunks h, h + 8, ... of d_model and keeps
 // G of them in flight. Per chunk, bf16 x rows are copied into the wave's own
@@ -148,7 +190,7 @@ __device__ __forceinline__ float sumsq8(const u32x4& v) {
 // the sums of squares) are added through LDS in a fixed order; every expert
 // tile of a token tile computes the same r bit for bit.
 // All expert tiles of a token tile run on one XCD (workgroup b runs on XCD
-// b % 8) and share its L2: each publishes its logits with a counter and the
+// (b + c) % 8, c fixed within a launch) and share its L2: each publishes its logits with a counter and the
 // last to arrive selects the top-k of all the tile's tokens, one per 16-lane
 // row. With SPLIT = 2 (few token tiles) each expert tile is shared by two
 // workgroups, one per half of its 16 experts: each loads only its half of
@@ -162,6 +204,7 @@ __global__ __launch_bounds__(64 * kWaves) void k_logits(RouterArgs a) {
   constexpr int kBuf = kXsBytes > kPartBytes ? kXsBytes : kPartBytes;
   __shared__ __attribute__((aligned(16))) char smem[kBuf];
   __shared__ float ssq[kWaves][kRows];
+  __shared__ float rs[kRows];  // r of each row
   __shared__ int is_last;
   float(*part)[kRows][17] = reinterpret_cast<float(*)[kRows][17]>(smem);
 
@@ -330,6 +373,7 @@ __global__ __launch_bounds__(64 * kWaves) void k_logits(RouterArgs a) {
       tot += ssq[w][row];
     }
     const float r = 1.0f / sqrtf(tot / (float)D + a.eps);
+    if (n == 0) rs[row] = r;
     if (t0 + row < a.T && (SPLIT == 1 || (n >> 3) == half)) {
       a.logits[(size_t)(t0 + row) * a.Epad + et * 16 + n] = r * sum + bias_v;  // n == tid % 16
       if (et == 0 && n == 0) a.rnorm[t0 + row] = r;
@@ -338,13 +382,28 @@ __global__ __launch_bounds__(64 * kWaves) void k_logits(RouterArgs a) {
   // publish: every thread's stores have reached L2 before the counter moves
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
+  // each arrival also counts under its XCD: the last arriver checks that all
+  // of the token tile's workgroups ran on its own (it reads their logits from
+  // its L2) and raises DG_DEV_XCD_ROUTER if not
   if (tid == 0) {
-    const int old = atomicAdd(&a.tile_count[tt], 1);
-    is_last = (old == n_eh - 1);
-    if (is_last) a.tile_count[tt] = 0;  // ready for the next forward
+    const int xcc = xcc_id();
+    const unsigned long long mine = 1ull | (1ull << (8 + 6 * xcc));
+    const unsigned long long now =
+        atomicAdd(reinterpret_cast<unsigned long long*>(&a.tile_count[tt]), mine) + mine;
+    is_last = (int)(now & 0xffull) == n_eh;  // n_eh <= 32
+    if (is_last) {
+      if ((int)((now >> (8 + 6 * xcc)) & 63ull) != n_eh) raise_flag(a.dev_flags, DG_DEV_XCD_ROUTER);
+      a.tile_count[tt] = 0;  // ready for the next forward
+    }
   }
   __syncthreads();
-  if (!is_last) return;
+  // this workgroup's share of the expert input's columns (8-wide segments)
+  const int w = jq % n_eh, nseg = D / 8;
+  const int s0 = w * nseg / n_eh, s1 = (w + 1) * nseg / n_eh;
+  if (!is_last) {
+    if (a.h != nullptr) write_h<XF32, kRows>(a, rs, t0, s0, s1, tid, 64 * kWaves);
+    return;
+  }
   // Last expert tile of this token tile: the full logit rows come from this
   // XCD's L2 (every writer ran on this XCD and waited for its stores); no
   // workgroup on this CU read these rows earlier in the launch, so its L1
@@ -356,68 +415,7 @@ __global__ __launch_bounds__(64 * kWaves) void k_logits(RouterArgs a) {
     const size_t trow = (size_t)min(t0 + tl, a.T - 1);
     topk_row<NU>(a.logits + trow * a.Epad, active, a.E, a.K, m, a.topk_idx + trow * a.K, a.topk_w + trow * a.K);
   }
-}
-
-// Expert input h = x r (1 + gamma_e): one workgroup of 256 threads per token;
-// thread i owns the 8-column pieces i, i + 256, ... (up to NP of them:
-// d_model <= 2048 NP). All loads of a thread are issued together; one block
-// reduction gives r.
-template <bool XF32, int NP>
-__global__ __launch_bounds__(256) void k_norm(RouterArgs a) {
-  __shared__ float wsum[4];
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int t = blockIdx.x;
-  const int D = a.D;
-  const int nseg = D / 8;
-  const size_t row = (size_t)t * D;
-  float f[NP][8];
-  float4 ge[NP][2];
-#pragma unroll
-  for (int i = 0; i < NP; ++i) {
-    const int sg = tid + 256 * i;
-    if (sg < nseg) {
-      if constexpr (XF32) {
-        const float4 v0 = *reinterpret_cast<const float4*>(static_cast<const float*>(a.x) + row + sg * 8);
-        const float4 v1 = *reinterpret_cast<const float4*>(static_cast<const float*>(a.x) + row + sg * 8 + 4);
-        f[i][0] = v0.x; f[i][1] = v0.y; f[i][2] = v0.z; f[i][3] = v0.w;
-        f[i][4] = v1.x; f[i][5] = v1.y; f[i][6] = v1.z; f[i][7] = v1.w;
-      } else {
-        const u32x4 v = *reinterpret_cast<const u32x4*>(static_cast<const uint16_t*>(a.x) + row + sg * 8);
-#pragma unroll
-        for (int k = 0; k < 4; ++k) {
-          f[i][2 * k] = bf16_lo(v[k]);
-          f[i][2 * k + 1] = bf16_hi(v[k]);
-        }
-      }
-      ge[i][0] = *reinterpret_cast<const float4*>(a.gamma_e + sg * 8);
-      ge[i][1] = *reinterpret_cast<const float4*>(a.gamma_e + sg * 8 + 4);
-    }
-  }
-  float ss = 0.0f;
-#pragma unroll
-  for (int i = 0; i < NP; ++i)
-    if (tid + 256 * i < nseg)
-#pragma unroll
-      for (int k = 0; k < 8; ++k) ss = fmaf(f[i][k], f[i][k], ss);
-  for (int msk = 32; msk >= 1; msk >>= 1) ss += __shfl_xor(ss, msk);
-  if (lane == 0) wsum[wave] = ss;
-  __syncthreads();
-  const float tot = (wsum[0] + wsum[1]) + (wsum[2] + wsum[3]);
-  const float r = 1.0f / sqrtf(tot / (float)D + a.eps);
-#pragma unroll
-  for (int i = 0; i < NP; ++i) {
-    const int sg = tid + 256 * i;
-    if (sg >= nseg) continue;
-    const float g2[8] = {ge[i][0].x, ge[i][0].y, ge[i][0].z, ge[i][0].w, ge[i][1].x, ge[i][1].y, ge[i][1].z, ge[i][1].w};
-    u32x4 ho;
-#pragma unroll
-    for (int k = 0; k < 4; ++k) {
-      const float h0 = f[i][2 * k] * r * (1.0f + g2[2 * k]);
-      const float h1 = f[i][2 * k + 1] * r * (1.0f + g2[2 * k + 1]);
-      ho[k] = a.h_f16 ? pack_f16x2(h0, h1) : pack_bf16x2(h0, h1);
-    }
-    *reinterpret_cast<u32x4*>(a.h + row + sg * 8) = ho;
-  }
+  if (a.h != nullptr) write_h<XF32, kRows>(a, rs, t0, s0, s1, tid, 64 * kWaves);
 }
 
 // Create time: W' = W_r diag(1 + gamma_r) in fp32 (router weight fp32 or
@@ -462,15 +460,6 @@ void (*pick_logits(int nu))(RouterArgs) {
 }
 
 }  // namespace
-
-hipError_t launch_norm(const RouterArgs& a, hipStream_t stream, const KernelEvents* ev) {
-  void (*kn)(RouterArgs);
-  if (a.D <= 2048 * 2)
-    kn = a.x_f32 ? k_norm<true, 2> : k_norm<false, 2>;
-  else
-    kn = a.x_f32 ? k_norm<true, 8> : k_norm<false, 8>;
-  return launch_kernel(kn, dim3(a.T), dim3(256), stream, ev, a);
-}
 
 hipError_t launch_logits(const RouterArgs& a, hipStream_t stream, const KernelEvents* ev) {
   const int n_et = a.Epad / 16;

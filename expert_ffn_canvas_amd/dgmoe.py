@@ -21,7 +21,8 @@ DG_ERR_INVALID_ARG, DG_ERR_SHAPE, DG_ERR_DTYPE, DG_ERR_ALIGN = -1, -2, -3, -4
 DG_ERR_OOM, DG_ERR_HIP, DG_ERR_UNSUPPORTED = -5, -6, -7
 DG_MOE_PACK_WEIGHTS = 0x1
 DG_FWD_ADD_INPUT = 0x1
-ABI_VERSION = 1
+ABI_VERSION = 2
+DG_DEV_QUEUE_OVERFLOW, DG_DEV_XCD_ROUTER, DG_DEV_XCD_GEMM, DG_DEV_WAIT_TIMEOUT = 0x1, 0x2, 0x4, 0x8
 
 EXPORTED = ("dg_moe_create", "dg_moe_forward", "dg_moe_forward_debug", "dg_moe_forward_profiled", "dg_moe_destroy",
             "dg_moe_status_string", "dg_moe_last_error", "dg_moe_abi_version", "dg_moe_workspace_bytes",
@@ -44,7 +45,8 @@ class dg_moe_weights(ctypes.Structure):
 
 class dg_moe_debug(ctypes.Structure):
     _fields_ = [("topk_idx", ctypes.c_void_p), ("topk_w", ctypes.c_void_p), ("counts", ctypes.c_void_p),
-                ("offsets", ctypes.c_void_p), ("sorted_slot", ctypes.c_void_p), ("row_of_slot", ctypes.c_void_p)]
+                ("offsets", ctypes.c_void_p), ("sorted_slot", ctypes.c_void_p), ("row_of_slot", ctypes.c_void_p),
+                ("queue_len", ctypes.c_void_p), ("dev_flags", ctypes.c_void_p)]
 
 
 class dg_head_config(ctypes.Structure):
@@ -258,7 +260,9 @@ class MoELayer:
         return out
 
     def forward_debug(self, x, out=None):
-        """Forward plus routing/permutation outputs (device tensors)."""
+        """Forward plus routing/permutation outputs (device tensors): the routing, counts, offsets, the sorted
+        slots, queue_len (8 gate_up and 8 down queue lengths, then the two capacities) and the handle's
+        sticky device status word dev_flags (DG_DEV_* bits)."""
         import torch
         T = x.shape[0]
         dev = x.device
@@ -271,9 +275,11 @@ class MoELayer:
             offsets=torch.empty((self.E + 1,), dtype=torch.int32, device=dev),
             sorted_slot=torch.empty((T * self.K,), dtype=torch.int32, device=dev),
             row_of_slot=torch.empty((T * self.K,), dtype=torch.int32, device=dev),
+            queue_len=torch.empty((18,), dtype=torch.int32, device=dev),
+            dev_flags=torch.empty((1,), dtype=torch.int32, device=dev),
         )
         dbg = dg_moe_debug(*(_ptr(r[k]) for k in ("topk_idx", "topk_w", "counts", "offsets", "sorted_slot",
-                                                   "row_of_slot")))
+                                                   "row_of_slot", "queue_len", "dev_flags")))
         st = dg_moe_forward_debug(self.handle, _ptr(x), _ptr(out), T, dbg, self.stream.cuda_stream)
         _check(st, "dg_moe_forward_debug")
         r["out"] = out

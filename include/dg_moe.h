@@ -44,7 +44,7 @@
 extern "C" {
 #endif
 
-#define DG_MOE_ABI_VERSION 1
+#define DG_MOE_ABI_VERSION 2
 
 /* Element types. DG_I4G128: 4-bit codes q in [0,15] standing for (q - 8) * s,
  * two codes per byte (even input index in the low nibble), with one fp16
@@ -136,6 +136,24 @@ typedef struct dg_moe_weights {
   const uint16_t* s_down;     /* int4 only: fp16 [E, D, ceil(F/128)]                       */
 } dg_moe_weights;
 
+/* Bits of the handle's device status word: each is set by a kernel that finds
+ * a condition the layer's design rules out, and stays set for the handle's
+ * lifetime. dg_moe_forward_debug copies the word out. None of them is set by
+ * a correct run; a set bit means that the output of some forward may be wrong.
+ *  DG_DEV_QUEUE_OVERFLOW: a GEMM task queue needed more entries than its
+ *    capacity; the permutation dropped the excess tasks.
+ *  DG_DEV_XCD_ROUTER, DG_DEV_XCD_GEMM: the router workgroups of one token
+ *    tile, or the fused-GEMM tasks of one tile, did not all run on one XCD.
+ *    They pass data through that XCD's L2 and rely on workgroups b and b + 8
+ *    of a launch sharing an XCD (the dispatcher deals workgroups to the 8
+ *    XCDs round robin, from an XCD that may differ between launches).
+ *  DG_DEV_WAIT_TIMEOUT: a down task of the fused GEMM launch gave up waiting
+ *    for its tile's gate_up tasks and wrote NaN for its outputs. */
+#define DG_DEV_QUEUE_OVERFLOW 0x1u
+#define DG_DEV_XCD_ROUTER 0x2u
+#define DG_DEV_XCD_GEMM 0x4u
+#define DG_DEV_WAIT_TIMEOUT 0x8u
+
 /* Optional routing outputs of dg_moe_forward_debug; any member may be NULL. */
 typedef struct dg_moe_debug {
   int32_t* topk_idx;     /* [T, k] selected experts, by logit descending then id     */
@@ -145,6 +163,10 @@ typedef struct dg_moe_debug {
   int32_t* sorted_slot;  /* [k T] slot t k + j of each expert-sorted row (increasing
                             token order inside an expert)                            */
   int32_t* row_of_slot;  /* [k T] expert-sorted row of slot (t, j)                   */
+  int32_t* queue_len;    /* [2, 8] tasks in each per-XCD queue of the gate_up GEMM,
+                            then of the down GEMM, and their common capacity:
+                            queue_len[16] (gate_up), queue_len[17] (down): 18 ints   */
+  uint32_t* dev_flags;   /* [1] the handle's device status word (DG_DEV_* bits)      */
 } dg_moe_debug;
 
 typedef struct dg_moe_s* dg_moe_handle;
@@ -191,9 +213,10 @@ dg_status dg_moe_forward_debug(dg_moe_handle h, const void* x, void* out, int32_
  * gate_up GEMM, the down GEMM and the combine. The events are recorded by the
  * kernel dispatches themselves (hipExtLaunchKernel), so
  * hipEventElapsedTime(events[2 i], events[2 i + 1]) is that kernel's own
- * duration. Where the expert norm is folded into the packed gate_up weight
- * (DG_MOE_PACK_WEIGHTS, bf16 experts and activations) no norm kernel runs and
- * events 0 and 1 are recorded back to back. One launch runs both GEMMs
+ * duration. No kernel of its own runs the expert-input norm (the router
+ * writes h where it is materialised, and where the norm is folded into the
+ * packed gate_up weight h is never formed): events 0 and 1 are recorded back
+ * to back. One launch runs both GEMMs
  * (except for int4 experts in borrow mode): events 6 and 7 time it, and events
  * 8 and 9 are recorded back to back after it. T must be > 0; every event must
  * be non-NULL (else DG_ERR_INVALID_ARG, nothing launched). */

@@ -78,6 +78,27 @@ def check_permutation(dbg, K, E, T):
     assert int(pm["counts"].sum()) == K * T
 
 
+def check_device_state(dbg, K, E, T, D, F):
+    """The handle's sticky device status word is clear, and the per-XCD task queues hold their tasks within the
+    capacity and within the balance the deal guarantees: no queue more than 2 tiles of the largest expert above
+    an even share of all tiles (per column block of each GEMM)."""
+    flags = int(dbg["dev_flags"].cpu().numpy()[0])
+    assert flags == 0, f"device status word 0x{flags:x}"
+    ql = dbg["queue_len"].cpu().numpy()
+    counts = dbg["counts"].cpu().numpy()
+    lens, caps = ql[:16].reshape(2, 8), ql[16:18]
+    for g, nb in enumerate((F // 64, D // 128)):
+        assert np.all(lens[g] <= caps[g]), f"GEMM {g}: queue lengths {lens[g]} over capacity {caps[g]}"
+        assert lens[g].sum() % nb == 0
+        tiles = lens[g].sum() // nb
+        # the tile height the permutation used is the one whose tile count matches
+        rows = [R for R in (64, 128) if int(np.sum((counts + R - 1) // R)) == tiles]
+        assert rows, f"GEMM {g}: {tiles} tiles match no tile height"
+        a_max = int((counts.max() + rows[0] - 1) // rows[0])
+        bound = nb * (-(-tiles // 8) + 2 * a_max)
+        assert lens[g].max() <= bound, f"GEMM {g}: queue {lens[g].max()} > balance bound {bound} ({lens[g]})"
+
+
 def rel_max_err(gpu, ref):
     gpu = np.asarray(gpu, dtype=np.float64)
     ref = np.asarray(ref, dtype=np.float64)
@@ -102,6 +123,7 @@ def layer_parity(layer, x, wn, K, eps=synth.RMS_EPS, tokens=None, n_threads=0):
     gw = dbg["topk_w"].cpu().numpy()
     near = check_routing(gidx, gw, orc, K, T)
     check_permutation(dbg, K, layer.E, T)
+    check_device_state(dbg, K, layer.E, T, layer.D, layer.F)
     tok = np.arange(T) if tokens is None else np.asarray(tokens)
     ref = oracle.moe_forward(wn, xn, K, eps, forced=gidx, tokens=tok, n_threads=n_threads)
     gout = to_f32(dbg["out"])[tok]

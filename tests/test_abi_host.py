@@ -36,14 +36,14 @@ def test_library_exports_every_declared_symbol():
 
 
 def test_struct_layouts_match_the_header():
-    # dg_moe_config: 11 four-byte fields; dg_moe_weights: 8 pointers; dg_moe_debug: 6 pointers
+    # dg_moe_config: 11 four-byte fields; dg_moe_weights: 8 pointers; dg_moe_debug: 8 pointers
     assert ctypes.sizeof(dgmoe.dg_moe_config) == 44
     assert ctypes.sizeof(dgmoe.dg_moe_weights) == 64
-    assert ctypes.sizeof(dgmoe.dg_moe_debug) == 48
+    assert ctypes.sizeof(dgmoe.dg_moe_debug) == 64
 
 
 def test_version_and_status_strings():
-    assert dgmoe.dg_moe_abi_version() == 1
+    assert dgmoe.dg_moe_abi_version() == 2
     assert dgmoe.dg_moe_status_string(dgmoe.DG_OK) == "ok"
     for st in range(-7, 0):
         assert dgmoe.dg_moe_status_string(st) not in ("", "unknown status")
