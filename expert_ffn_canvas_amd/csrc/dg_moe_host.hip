@@ -17,6 +17,7 @@
 
 #include <cmath>
 #include <cstdarg>
+#include <mutex>
 #include <cstdio>
 #include <cstring>
 #include <new>
@@ -689,9 +690,81 @@ dg_status head_launch(dg_head_handle hd, const void* h, int32_t T, float beta, f
                       argmax, mean_entropy, events, stream);
 }
 
+// ---------------------------------------------------------------------------
+// The stage without a handle, for callers that cannot allocate: its partials
+// live in this library-owned device array (one copy per device, held until the
+// process ends). Host code never passes the array's name to a kernel or a copy:
+// the name is a host-side stand-in; the device address of each device's copy
+// comes from hipGetSymbolAddress, taken once per device with it current.
+constexpr size_t kHeadScratchBytes = DG_HEAD_NOALLOC_SCRATCH_BYTES;
+
+}  // namespace
+
+static __device__ __align__(256) char scratch[DG_HEAD_NOALLOC_SCRATCH_BYTES];
+
+namespace {
+
+constexpr int kMaxDevices = 64;
+struct DeviceScratch {
+  void* ptr = nullptr;  // this device's copy of `scratch`
+  int n_cu = 0;
+  bool ready = false;
+};
+std::mutex g_scratch_mu;
+DeviceScratch g_scratch[kMaxDevices];
+
+// The device address of the current device's scratch copy and its compute
+// units, set up on the device's first call.
+dg_status device_scratch(int* dev_out, DeviceScratch* out) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
+  if (dev < 0 || dev >= kMaxDevices) return fail(DG_ERR_UNSUPPORTED, "device index %d beyond %d", dev, kMaxDevices);
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  DeviceScratch& d = g_scratch[dev];
+  if (!d.ready) {
+    hipDeviceProp_t prop;
+    e = hipGetDeviceProperties(&prop, dev);
+    if (e != hipSuccess) return hip_fail(e, "hipGetDeviceProperties");
+    if (std::strncmp(prop.gcnArchName, "gfx950", 6) != 0)
+      return fail(DG_ERR_UNSUPPORTED, "device %d is %s; this library is built for gfx950", dev, prop.gcnArchName);
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || p == nullptr) return hip_fail(e, "hipGetSymbolAddress(scratch)");
+    d.ptr = p;
+    d.n_cu = prop.multiProcessorCount > 0 ? prop.multiProcessorCount : 256;
+    d.ready = true;
+  }
+  *dev_out = dev;
+  *out = d;
+  return DG_OK;
+}
+
 }  // namespace
 
 extern "C" {
+
+dg_status dg_head_forward_noalloc(const dg_head_config* cfg, const void* emb, const void* h, int32_t T, float beta,
+                                  float* logits, float* entropy, int32_t* argmax, float* mean_entropy, void* stream) {
+  dg_status st = check_head_config(cfg);
+  if (st != DG_OK) return st;
+  if (!emb) return fail(DG_ERR_INVALID_ARG, "emb is NULL");
+  if (!aligned16(emb)) return fail(DG_ERR_ALIGN, "emb is not 16-byte aligned");
+  st = head_check_call(*cfg, h, T, beta, logits, entropy, argmax, mean_entropy, nullptr);
+  if (st != DG_OK) return st;
+  const size_t pb = round_up(head_nvb(*cfg) * (size_t)T * 4, 256);
+  if (5 * pb > kHeadScratchBytes)
+    return fail(DG_ERR_SHAPE, "T = %d positions over %d vocabulary rows need %zu bytes of partials; the static "
+                "scratch holds %zu (T * ceil(V / 256) * 20 bytes, each of the five arrays rounded to 256)",
+                T, cfg->vocab, 5 * pb, kHeadScratchBytes);
+  if (T == 0) return ok();
+  int dev = 0;
+  DeviceScratch d;
+  st = device_scratch(&dev, &d);
+  if (st != DG_OK) return st;
+  return head_enqueue(*cfg, emb, d.n_cu, static_cast<char*>(d.ptr), pb, h, T, beta, logits, entropy, argmax,
+                      mean_entropy, nullptr, stream);
+}
 
 uint64_t dg_head_workspace_bytes(const dg_head_config* cfg) {
   if (check_head_config(cfg) != DG_OK) return 0;

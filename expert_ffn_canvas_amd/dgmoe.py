@@ -27,7 +27,8 @@ DG_DEV_QUEUE_OVERFLOW, DG_DEV_XCD_ROUTER, DG_DEV_XCD_GEMM, DG_DEV_WAIT_TIMEOUT =
 EXPORTED = ("dg_moe_create", "dg_moe_forward", "dg_moe_forward_debug", "dg_moe_forward_profiled", "dg_moe_destroy",
             "dg_moe_status_string", "dg_moe_last_error", "dg_moe_abi_version", "dg_moe_workspace_bytes",
             "dg_head_create", "dg_head_forward", "dg_head_forward_profiled", "dg_head_destroy",
-            "dg_head_workspace_bytes")
+            "dg_head_workspace_bytes", "dg_head_forward_noalloc")
+DG_HEAD_NOALLOC_SCRATCH_BYTES = 8 << 20
 
 
 class dg_moe_config(ctypes.Structure):
@@ -94,6 +95,8 @@ def _load():
     lib.dg_head_destroy.restype = i32
     lib.dg_head_workspace_bytes.argtypes = [ctypes.POINTER(dg_head_config)]
     lib.dg_head_workspace_bytes.restype = ctypes.c_uint64
+    lib.dg_head_forward_noalloc.argtypes = [ctypes.POINTER(dg_head_config), vp, vp, i32, f32, vp, vp, vp, vp, vp]
+    lib.dg_head_forward_noalloc.restype = i32
     if lib.dg_moe_abi_version() != ABI_VERSION:
         raise ImportError("libdgmoe.so ABI version mismatch")
     return lib
@@ -188,6 +191,12 @@ def dg_head_destroy(handle) -> int:
 
 def dg_head_workspace_bytes(cfg: dg_head_config) -> int:
     return _lib.dg_head_workspace_bytes(ctypes.byref(cfg))
+
+
+def dg_head_forward_noalloc(cfg: dg_head_config, emb: int, h: int, T: int, beta: float, logits: int | None,
+                            entropy: int, argmax: int, mean_entropy: int | None, stream: int) -> int:
+    return _lib.dg_head_forward_noalloc(ctypes.byref(cfg), emb, h, T, beta, logits, entropy, argmax, mean_entropy,
+                                        ctypes.c_void_p(stream))
 
 
 def make_head_config(V=262144, D=2816, max_tokens=256, h_dtype=DG_BF16, emb_dtype=DG_BF16, flags=0) -> dg_head_config:

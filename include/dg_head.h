@@ -93,6 +93,29 @@ dg_status dg_head_destroy(dg_head_handle hd);
  * the configuration is invalid. */
 uint64_t dg_head_workspace_bytes(const dg_head_config* cfg);
 
+/* Size of the library-owned device scratch of dg_head_forward_noalloc. */
+#define DG_HEAD_NOALLOC_SCRATCH_BYTES (8u << 20)
+
+/* For callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc): the stage of
+ * dg_head_forward without a handle, for the table emb [V, D] (bf16, 16-byte
+ * aligned, read in place) and the sizes in cfg (validated as for
+ * dg_head_create; T <= cfg->max_tokens). It allocates nothing: the per-tile
+ * softmax partials go to a library-owned device array of
+ * DG_HEAD_NOALLOC_SCRATCH_BYTES (8 MiB), one copy per device, set up on the
+ * device's first call and held until the process ends. Five arrays of
+ * T * ceil(V / 256) 4-byte partials, each rounded up to 256 bytes, must fit
+ * in it (T <= 409 positions at V = 262144), else DG_ERR_SHAPE and nothing is
+ * launched. Every call on a device shares that device's array: calls that
+ * overlap in time on one device (two streams, two threads) race and give
+ * wrong results; issue them on one stream. Each call writes every partial it
+ * reads, so nothing needs clearing between calls. The outputs, their meaning,
+ * the other argument rules and errors are those of dg_head_forward, and the
+ * results are bit-identical to it. Errors: as dg_head_create and
+ * dg_head_forward. */
+dg_status dg_head_forward_noalloc(const dg_head_config* cfg, const void* emb, const void* h, int32_t T, float beta,
+                                  float* logits, float* entropy, int32_t* argmax, float* mean_entropy, void* stream);
+
 #ifdef __cplusplus
 }
 #endif
