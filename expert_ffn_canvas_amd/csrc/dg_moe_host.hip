@@ -437,14 +437,17 @@ static dg_status run_forward(dg_moe_handle hd, const void* x, void* out, int32_t
   pa.T = T;
   pa.K = c.top_k;
   pa.E = c.n_experts;
-  const bool tall = c.expert_w_dtype == DG_BF16 && dg::use_tall_tiles(T, c.top_k, c.n_experts);
+  const int tile_rows =
+      c.expert_w_dtype == DG_BF16 ? dg::bf16_tile_rows(T, c.top_k, c.n_experts) : dg::kTileRows;
+  const bool tall = tile_rows != dg::kTileRows;
   const bool fused = fuses_gemms(c);
-  pa.tile_rows = tall ? dg::kTallRows : dg::kTileRows;
+  pa.tile_rows = tile_rows;
   pa.deal = fused ? dg::kDealBalanced : tall ? dg::kDealExperts : dg::kDealUnits;
   pa.tile_done = fused ? hd->at<uint64_t>(L.tile_done) : nullptr;
+  pa.nb[0] = dg::gate_up_blocks(c.d_ff, tile_rows);
+  pa.nb[1] = dg::down_blocks(c.d_model, tile_rows);
   for (int g = 0; g < 2; ++g) {
-    pa.nb[g] = L.nb[g];
-    pa.qmax[g] = dg::max_queue_len(T, c.top_k, c.n_experts, L.nb[g], pa.tile_rows);
+    pa.qmax[g] = dg::max_queue_len(T, c.top_k, c.n_experts, pa.nb[g], pa.tile_rows);
     pa.tasks[g] = hd->at<dg::Tile>(L.tasks[g]);
   }
   pa.counts = hd->at<int32_t>(L.counts);
@@ -481,13 +484,13 @@ static dg_status run_forward(dg_moe_handle hd, const void* x, void* out, int32_t
     fa.dn.qlen = pa.qlen + dg::kQueues;
     fa.dn.qmax = pa.qmax[1];
     fa.tile_done = pa.tile_done;
-    fa.nb_gate_up = L.nb[0];
+    fa.nb_gate_up = pa.nb[0];
     fa.dev_flags = ra.dev_flags;
     e = mx4  ? dg::launch_gemm_fused_mx4(fa, stream, ev(3))
         : mx8 ? dg::launch_gemm_fused_mx8(fa, stream, ev(3))
         : q8 ? dg::launch_gemm_fused_q8(fa, stream, ev(3))
         : i4 ? dg::launch_gemm_fused_i4(fa, stream, ev(3))
-             : dg::launch_gemm_fused(fa, tall, stream, ev(3));
+             : dg::launch_gemm_fused(fa, tile_rows, stream, ev(3));
     if (e != hipSuccess) return hip_fail(e, "GEMM launch");
     if (events) {  // one launch for both GEMMs: the down events mark the point after it
       e = hipEventRecord(kev[4].start, stream);

@@ -65,6 +65,8 @@ __device__ __forceinline__ void load_w(const uint16_t* w0, const uint16_t* w1, i
 template <int NMT, int NS, int BMT>
 __device__ __forceinline__ void mma_step(const char* stage, int lane, const Panels& p, f32x4 (&acc0)[BMT],
                                          f32x4 (&acc1)[BMT]) {
+  // activation fragments live at a time: two sub-steps, one above 8 tiles
+  constexpr int kLive = NMT > 8 ? 1 : 2;
   const int g = lane >> 4, m = lane & 15;
 #pragma unroll
   for (int s = 0; s < NS; ++s) {
@@ -78,20 +80,19 @@ __device__ __forceinline__ void mma_step(const char* stage, int lane, const Pane
       acc0[mt] = mfma_bf16(av, bb0, acc0[mt]);
       acc1[mt] = mfma_bf16(av, bb1, acc1[mt]);
     }
-    // keep at most two sub-steps of activation fragments live at a time
-    if (s & 1) __builtin_amdgcn_sched_barrier(0);
+    if (s % kLive == kLive - 1) __builtin_amdgcn_sched_barrier(0);
   }
 }
 
 // One step with NS sub-steps, issued after the previous one: DMA of the
 // activation rows into stage (it + 1) & 1, then the weight panels into `nxt`,
 // then the MFMAs of step `it` (NSP sub-steps) from `cur`.
-template <bool PK, int NMT, int NS, int NSP, int ROWS>
-__device__ __forceinline__ void step(char* As, const uint16_t* const (&rowp)[ROWS / 16], const uint16_t* w0,
+template <bool PK, int NMT, int NS, int NSP, int ROWS, int WV>
+__device__ __forceinline__ void step(char* As, const uint16_t* const (&rowp)[dma_per_wave(ROWS, WV)], const uint16_t* w0,
                                      const uint16_t* w1, int k1, int it, int wave, int lane, const Panels& cur,
                                      Panels& nxt, f32x4 (&acc0)[ROWS / 16], f32x4 (&acc1)[ROWS / 16]) {
   constexpr int kSB = ROWS * kRowBytes;
-  dma_a<NMT, NS * 4>(As + ((it + 1) & 1) * kSB, rowp, k1, wave, lane);
+  dma_a<NMT, NS * 4, dma_per_wave(ROWS, WV), WV>(As + ((it + 1) & 1) * kSB, rowp, k1, wave, lane);
   __builtin_amdgcn_sched_barrier(0);
   load_w<PK, NS>(w0, w1, k1, nxt);
   __builtin_amdgcn_sched_barrier(0);
@@ -101,8 +102,8 @@ __device__ __forceinline__ void step(char* As, const uint16_t* const (&rowp)[ROW
 }
 
 // The last full step `last` (panels in `cur`) and the short tail, if any.
-template <bool PK, int NMT, int ROWS>
-__device__ __forceinline__ void finish(char* As, const uint16_t* const (&rowp)[ROWS / 16], const uint16_t* w0,
+template <bool PK, int NMT, int ROWS, int WV>
+__device__ __forceinline__ void finish(char* As, const uint16_t* const (&rowp)[dma_per_wave(ROWS, WV)], const uint16_t* w0,
                                        const uint16_t* w1, int nfull, int ntail, int wave, int lane,
                                        const Panels& cur, Panels& nxt, f32x4 (&acc0)[ROWS / 16],
                                        f32x4 (&acc1)[ROWS / 16]) {
@@ -113,7 +114,7 @@ __device__ __forceinline__ void finish(char* As, const uint16_t* const (&rowp)[R
   if (ntail == 0) {
     mma_step<NMT, kNS>(As + (last & 1) * kSB, lane, cur, acc0, acc1);
   } else {  // one 64-wide step remains (K % 128 == 64)
-    step<PK, NMT, 2, kNS, ROWS>(As, rowp, w0, w1, k1, last, wave, lane, cur, nxt, acc0, acc1);
+    step<PK, NMT, 2, kNS, ROWS, WV>(As, rowp, w0, w1, k1, last, wave, lane, cur, nxt, acc0, acc1);
     wait_vmcnt<0>();
     mma_step<NMT, 2>(tail_stage, lane, nxt, acc0, acc1);
   }
@@ -122,8 +123,8 @@ __device__ __forceinline__ void finish(char* As, const uint16_t* const (&rowp)[R
 // The K loop of one tile with NMT 16-row MFMA tiles. K is a multiple of 64.
 // Two panel buffers alternate roles (the loop is unrolled by two) so that no
 // register copies are needed between steps.
-template <bool PK, int NMT, int ROWS>
-__device__ __forceinline__ void k_loop(char* As, const uint16_t* const (&rowp)[ROWS / 16], const uint16_t* w0,
+template <bool PK, int NMT, int ROWS, int WV>
+__device__ __forceinline__ void k_loop(char* As, const uint16_t* const (&rowp)[dma_per_wave(ROWS, WV)], const uint16_t* w0,
                                        const uint16_t* w1, int K, int tid, f32x4 (&acc0)[ROWS / 16],
                                        f32x4 (&acc1)[ROWS / 16], int wstep) {
   const int lane = tid & 63, wave = tid >> 6;
@@ -134,35 +135,38 @@ __device__ __forceinline__ void k_loop(char* As, const uint16_t* const (&rowp)[R
   p1.wstep = wstep;
   if (nfull == 0) {
     // K = 64: one short step only
-    dma_a<NMT, 8>(As, rowp, 0, wave, lane);
+    dma_a<NMT, 8, dma_per_wave(ROWS, WV), WV>(As, rowp, 0, wave, lane);
     load_w<PK, 2>(w0, w1, 0, p0);
     wait_vmcnt<0>();
     lds_barrier();
     mma_step<NMT, 2>(As, lane, p0, acc0, acc1);
     return;
   }
-  dma_a<NMT, kSegs>(As, rowp, 0, wave, lane);
+  dma_a<NMT, kSegs, dma_per_wave(ROWS, WV), WV>(As, rowp, 0, wave, lane);
   __builtin_amdgcn_sched_barrier(0);
   load_w<PK, kNS>(w0, w1, 0, p0);
   wait_vmcnt<2 * kNS>();
   lds_barrier();
   int it = 0;
   for (; it + 2 < nfull; it += 2) {
-    step<PK, NMT, kNS, kNS, ROWS>(As, rowp, w0, w1, (it + 1) * kKS, it, wave, lane, p0, p1, acc0, acc1);
-    step<PK, NMT, kNS, kNS, ROWS>(As, rowp, w0, w1, (it + 2) * kKS, it + 1, wave, lane, p1, p0, acc0, acc1);
+    step<PK, NMT, kNS, kNS, ROWS, WV>(As, rowp, w0, w1, (it + 1) * kKS, it, wave, lane, p0, p1, acc0, acc1);
+    step<PK, NMT, kNS, kNS, ROWS, WV>(As, rowp, w0, w1, (it + 2) * kKS, it + 1, wave, lane, p1, p0, acc0, acc1);
   }
   if (it + 2 == nfull) {
-    step<PK, NMT, kNS, kNS, ROWS>(As, rowp, w0, w1, (it + 1) * kKS, it, wave, lane, p0, p1, acc0, acc1);
-    finish<PK, NMT, ROWS>(As, rowp, w0, w1, nfull, ntail, wave, lane, p1, p0, acc0, acc1);
+    step<PK, NMT, kNS, kNS, ROWS, WV>(As, rowp, w0, w1, (it + 1) * kKS, it, wave, lane, p0, p1, acc0, acc1);
+    finish<PK, NMT, ROWS, WV>(As, rowp, w0, w1, nfull, ntail, wave, lane, p1, p0, acc0, acc1);
   } else {
-    finish<PK, NMT, ROWS>(As, rowp, w0, w1, nfull, ntail, wave, lane, p0, p1, acc0, acc1);
+    finish<PK, NMT, ROWS, WV>(As, rowp, w0, w1, nfull, ntail, wave, lane, p0, p1, acc0, acc1);
   }
 }
 
-// The product of one task (tile `tl` of up to ROWS rows, 64 or 128 for
-// experts that receive many rows); `As` holds two K steps of ROWS activation
-// rows.
-template <bool GATE_UP, bool PK, int ROWS>
+// The product of one task (tile `tl` of up to ROWS rows, 64, 128 or 160 for
+// experts that receive many rows) by WV waves (4, or 8 with 160 rows: 128
+// gate_up features or 256 down outputs per task); `As` holds two K steps of
+// ROWS activation rows. A wave whose panels lie past the last column block's
+// end (F or D not a multiple of the block) streams the block's last panels
+// again (cache hits) and stores nothing.
+template <bool GATE_UP, bool PK, int ROWS, int WV = kWaves>
 __device__ __forceinline__ void gemm_body(const GemmArgs& a, const Tile& tl, char* As, float* rrow) {
   constexpr int kBM = ROWS / 16;  // 16-row MFMA tiles, and activation transfers per wave per step
   const int F = a.F, D = a.D;
@@ -179,20 +183,26 @@ __device__ __forceinline__ void gemm_body(const GemmArgs& a, const Tile& tl, cha
 
   // source row of each DMA instruction of this lane (rows past the tile re-read
   // its last row; their results are never stored)
-  const uint16_t* rowp[kBM];
+  constexpr int kNI = dma_per_wave(ROWS, WV);
+  const uint16_t* rowp[kNI];
 #pragma unroll
-  for (int i = 0; i < kBM; ++i) {
-    const int r = min(kDmaRows * (wave + kWaves * i) + lane / kSegs, tl.mc - 1);
+  for (int i = 0; i < kNI; ++i) {
+    const int r = min(kDmaRows * (wave + WV * i) + lane / kSegs, tl.mc - 1);
     rowp[i] = GATE_UP ? a.h + (size_t)(a.sorted_slot[tl.row0 + r] / a.K) * D : a.act + (size_t)(tl.row0 + r) * F;
   }
   int col;  // gate_up: feature f; down: first output d
   const uint16_t* w0;
   const uint16_t* w1;
+  // this wave's panel (pair) inside the matrix, clamped to the last one
+  const int pw = nb * WV + wave;           // gate_up: gate panel; down: panel pair
+  const int npw = GATE_UP ? F / 16 : D / 32;
+  const bool live = pw < npw;
+  const int pc = live ? pw : npw - 1;
   if (GATE_UP) {
-    col = nb * 16 * kWaves + wave * 16 + (lane & 15);
+    col = pc * 16 + (lane & 15);
     const uint16_t* W = static_cast<const uint16_t*>(a.w_gate_up);
-    if (PK) {  // gate panel nb * kWaves + wave, up panel F / 16 later, in the same K-step row
-      const int p = nb * kWaves + wave;
+    if (PK) {  // gate panel pc, up panel F / 16 later, in the same K-step row
+      const int p = pc;
       w0 = W + ((size_t)tl.e * (D / 32) * (2 * F / 16) + p) * 512 + lane * 8;
       w1 = w0 + (size_t)(F / 16) * 512;
     } else {
@@ -200,10 +210,10 @@ __device__ __forceinline__ void gemm_body(const GemmArgs& a, const Tile& tl, cha
       w1 = w0 + (size_t)F * D;
     }
   } else {
-    col = nb * 32 * kWaves + wave * 32 + (lane & 15);
+    col = pc * 32 + (lane & 15);
     const uint16_t* W = static_cast<const uint16_t*>(a.w_down);
-    if (PK) {  // panels 2 (nb * kWaves + wave) and the next
-      const int p = 2 * (nb * kWaves + wave);
+    if (PK) {  // panels 2 pc and the next
+      const int p = 2 * pc;
       w0 = W + ((size_t)tl.e * (F / 32) * (D / 16) + p) * 512 + lane * 8;
       w1 = w0 + 512;
     } else {
@@ -221,21 +231,31 @@ __device__ __forceinline__ void gemm_body(const GemmArgs& a, const Tile& tl, cha
   }
   if constexpr (ROWS == 64) {
     switch (nmt) {
-      case 1: k_loop<PK, 1, ROWS>(As, rowp, w0, w1, K, tid, acc0, acc1, wstep); break;
-      case 2: k_loop<PK, 2, ROWS>(As, rowp, w0, w1, K, tid, acc0, acc1, wstep); break;
-      case 3: k_loop<PK, 3, ROWS>(As, rowp, w0, w1, K, tid, acc0, acc1, wstep); break;
-      default: k_loop<PK, 4, ROWS>(As, rowp, w0, w1, K, tid, acc0, acc1, wstep); break;
+      case 1: k_loop<PK, 1, ROWS, WV>(As, rowp, w0, w1, K, tid, acc0, acc1, wstep); break;
+      case 2: k_loop<PK, 2, ROWS, WV>(As, rowp, w0, w1, K, tid, acc0, acc1, wstep); break;
+      case 3: k_loop<PK, 3, ROWS, WV>(As, rowp, w0, w1, K, tid, acc0, acc1, wstep); break;
+      default: k_loop<PK, 4, ROWS, WV>(As, rowp, w0, w1, K, tid, acc0, acc1, wstep); break;
+    }
+  } else if constexpr (ROWS == 128) {
+    switch (nmt) {
+      case 1: k_loop<PK, 1, ROWS, WV>(As, rowp, w0, w1, K, tid, acc0, acc1, wstep); break;
+      case 2: k_loop<PK, 2, ROWS, WV>(As, rowp, w0, w1, K, tid, acc0, acc1, wstep); break;
+      case 3: k_loop<PK, 3, ROWS, WV>(As, rowp, w0, w1, K, tid, acc0, acc1, wstep); break;
+      case 4: k_loop<PK, 4, ROWS, WV>(As, rowp, w0, w1, K, tid, acc0, acc1, wstep); break;
+      case 5: k_loop<PK, 5, ROWS, WV>(As, rowp, w0, w1, K, tid, acc0, acc1, wstep); break;
+      case 6: k_loop<PK, 6, ROWS, WV>(As, rowp, w0, w1, K, tid, acc0, acc1, wstep); break;
+      case 7: k_loop<PK, 7, ROWS, WV>(As, rowp, w0, w1, K, tid, acc0, acc1, wstep); break;
+      default: k_loop<PK, 8, ROWS, WV>(As, rowp, w0, w1, K, tid, acc0, acc1, wstep); break;
     }
   } else {
-    switch (nmt) {
-      case 1: k_loop<PK, 1, ROWS>(As, rowp, w0, w1, K, tid, acc0, acc1, wstep); break;
-      case 2: k_loop<PK, 2, ROWS>(As, rowp, w0, w1, K, tid, acc0, acc1, wstep); break;
-      case 3: k_loop<PK, 3, ROWS>(As, rowp, w0, w1, K, tid, acc0, acc1, wstep); break;
-      case 4: k_loop<PK, 4, ROWS>(As, rowp, w0, w1, K, tid, acc0, acc1, wstep); break;
-      case 5: k_loop<PK, 5, ROWS>(As, rowp, w0, w1, K, tid, acc0, acc1, wstep); break;
-      case 6: k_loop<PK, 6, ROWS>(As, rowp, w0, w1, K, tid, acc0, acc1, wstep); break;
-      case 7: k_loop<PK, 7, ROWS>(As, rowp, w0, w1, K, tid, acc0, acc1, wstep); break;
-      default: k_loop<PK, 8, ROWS>(As, rowp, w0, w1, K, tid, acc0, acc1, wstep); break;
+    switch (nmt) {  // wide tiles: up to 80 rows run as 5 MFMA tiles
+      case 1: case 2: case 3: case 4: case 5:
+        k_loop<PK, 5, ROWS, WV>(As, rowp, w0, w1, K, tid, acc0, acc1, wstep); break;
+      case 6: k_loop<PK, 6, ROWS, WV>(As, rowp, w0, w1, K, tid, acc0, acc1, wstep); break;
+      case 7: k_loop<PK, 7, ROWS, WV>(As, rowp, w0, w1, K, tid, acc0, acc1, wstep); break;
+      case 8: k_loop<PK, 8, ROWS, WV>(As, rowp, w0, w1, K, tid, acc0, acc1, wstep); break;
+      case 9: k_loop<PK, 9, ROWS, WV>(As, rowp, w0, w1, K, tid, acc0, acc1, wstep); break;
+      default: k_loop<PK, 10, ROWS, WV>(As, rowp, w0, w1, K, tid, acc0, acc1, wstep); break;
     }
   }
 
@@ -245,7 +265,7 @@ __device__ __forceinline__ void gemm_body(const GemmArgs& a, const Tile& tl, cha
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int r = mt * 16 + g * 4 + i;
-        if (r < tl.mc) {
+        if (r < tl.mc && live) {
           if (GATE_UP) {
             const float rr = rrow[r];
             a.act[(size_t)(tl.row0 + r) * F + col] =
@@ -286,6 +306,20 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
       [&](const Tile& tl) { gemm_body<false, PK, kTallRows>(f.dn, tl, As, rrow); });
 }
 
+// Wide tiles of up to 160 rows (every row an expert receives at the 2304-token
+// encode, so each weight block is streamed once): 8 waves share the tile's
+// activation stages (80 KB, one workgroup per CU, two waves per SIMD) and
+// cover 128 gate_up features or 256 down outputs per task.
+template <bool PK>
+__global__ __launch_bounds__(64 * kWideWaves) __attribute__((amdgpu_waves_per_eu(2, 2))) void k_gemm_fused_wide(
+    FusedGemmArgs f) {
+  __shared__ __attribute__((aligned(16))) char As[2 * kWideRows * kRowBytes];
+  __shared__ float rrow[kWideRows];
+  fused_tasks<kWideWaves>(
+      f, [&](const Tile& tl) { gemm_body<true, PK, kWideRows, kWideWaves>(f.gu, tl, As, rrow); },
+      [&](const Tile& tl) { gemm_body<false, PK, kWideRows, kWideWaves>(f.dn, tl, As, rrow); });
+}
+
 // One wave per block of 64 lanes x 16 bytes: source block (e, p, s) of 16 rows
 // x 32 columns goes to position (e, s, p). With `gamma`, value k is scaled by
 // (1 + gamma[k]) and rounded to bf16.
@@ -318,11 +352,14 @@ hipError_t launch_pack_panels(const uint16_t* src, uint16_t* dst, int E, int R, 
   return hipGetLastError();
 }
 
-hipError_t launch_gemm_fused(const FusedGemmArgs& f, bool tall, hipStream_t stream, const KernelEvents* ev) {
+hipError_t launch_gemm_fused(const FusedGemmArgs& f, int tile_rows, hipStream_t stream, const KernelEvents* ev) {
   const dim3 grid(kQueues * (f.gu.qmax + f.dn.qmax));
   const bool pk = f.gu.w_packed != 0;
-  auto k = tall ? (pk ? k_gemm_fused_tall<true> : k_gemm_fused_tall<false>)
-                : (pk ? k_gemm_fused<true> : k_gemm_fused<false>);
+  if (tile_rows == kWideRows)
+    return launch_kernel(pk ? k_gemm_fused_wide<true> : k_gemm_fused_wide<false>, grid, dim3(64 * kWideWaves), stream,
+                         ev, f);
+  auto k = tile_rows == kTallRows ? (pk ? k_gemm_fused_tall<true> : k_gemm_fused_tall<false>)
+                                  : (pk ? k_gemm_fused<true> : k_gemm_fused<false>);
   return launch_kernel(k, grid, dim3(kThreads), stream, ev, f);
 }
 

@@ -57,21 +57,26 @@ __device__ __forceinline__ void lds_dma16(uint32_t lds_base, const void* gaddr) 
       : "memory");
 }
 
+// DMA transfers per wave that stage ROWS activation rows with WV waves.
+constexpr int dma_per_wave(int rows, int wv) { return (rows + wv * kDmaRows - 1) / (wv * kDmaRows); }
+
 // Activation rows of one K step straight into LDS: instruction i of wave w
-// fills the kDmaRows rows starting at kDmaRows (w + kWaves i); lane l lands in row
-// slot l / kSegs, 16-byte position l % kSegs and carries logical segment
-// position ^ (row % kSegs), an XOR swizzle that makes the MFMA reads
+// (of WV waves) fills the kDmaRows rows starting at kDmaRows (w + WV i); lane l
+// lands in row slot l / kSegs, 16-byte position l % kSegs and carries logical
+// segment position ^ (row % kSegs), an XOR swizzle that makes the MFMA reads
 // bank-conflict free. Segments past a short last step re-read a valid one.
-template <int NMT, int NSEG, int NI>
+// With 8 waves an odd count of 16-row tiles rounds up to whole transfers (the
+// stage holds the extra rows).
+template <int NMT, int NSEG, int NI, int WV = kWaves>
 __device__ __forceinline__ void dma_a(char* stage, const uint16_t* const (&rowp)[NI], int k0, int wave,
                                       int lane) {
   const uint32_t base = __builtin_amdgcn_readfirstlane(lds_addr(stage) + wave * kDmaRows * kRowBytes);
 #pragma unroll
-  for (int i = 0; i < 16 * NMT / (kWaves * kDmaRows); ++i) {
-    const int r = kDmaRows * (wave + kWaves * i) + lane / kSegs;
+  for (int i = 0; i < (16 * NMT + WV * kDmaRows - 1) / (WV * kDmaRows); ++i) {
+    const int r = kDmaRows * (wave + WV * i) + lane / kSegs;
     int sg = (lane % kSegs) ^ (r % kSegs);
     if (NSEG < kSegs) sg = sg % NSEG;
-    lds_dma16(base + i * kWaves * kDmaRows * kRowBytes, rowp[i] + k0 + sg * 8);
+    lds_dma16(base + i * WV * kDmaRows * kRowBytes, rowp[i] + k0 + sg * 8);
   }
 }
 
@@ -103,7 +108,7 @@ __device__ __forceinline__ void lds_barrier() {
 // DG_DEV_XCD_GEMM. gate_up(tile) and down(tile) run one task's product.
 constexpr int kWaitPolls = 1 << 17;
 
-template <typename GateUp, typename Down>
+template <int WV = kWaves, typename GateUp, typename Down>
 __device__ __forceinline__ void fused_tasks(const FusedGemmArgs& f, GateUp gate_up, Down down) {
   __shared__ int ready;
   const int qx = blockIdx.x & (kQueues - 1), j = blockIdx.x / kQueues;
@@ -139,9 +144,10 @@ __device__ __forceinline__ void fused_tasks(const FusedGemmArgs& f, GateUp gate_
     return;
   }
   if (tid == 0) raise_flag(f.dev_flags, DG_DEV_WAIT_TIMEOUT);
-  const int cols = 32 * kWaves;
-  for (int i = tid; i < tl.mc * cols; i += kThreads)
-    f.dn.y[(size_t)(tl.row0 + i / cols) * f.dn.D + tl.nb * cols + i % cols] = 0x7fc0;  // bf16 NaN
+  const int cols = 32 * WV;
+  for (int i = tid; i < tl.mc * cols; i += 64 * WV)
+    if (tl.nb * cols + i % cols < f.dn.D)
+      f.dn.y[(size_t)(tl.row0 + i / cols) * f.dn.D + tl.nb * cols + i % cols] = 0x7fc0;  // bf16 NaN
 }
 
 }  // namespace gemm

@@ -29,8 +29,17 @@ struct Tile;
 // largest of the tall tiles used once experts receive many rows each.
 constexpr int kTileRows = 64;
 constexpr int kTallRows = 128;
-// Tall tiles when the rows per expert average at least 64 (bf16 experts).
-inline bool use_tall_tiles(int T, int K, int E) { return (long)T * K >= 64L * E; }
+// Wide tiles of 8-wave workgroups (one per CU): every row of an expert up to
+// this many in one tile.
+constexpr int kWideRows = 160;
+constexpr int kWideWaves = 8;
+// Tile height of the bf16 GEMMs from the rows per expert on average: 64-row
+// tiles below 64, 128-row tiles up to kWideFrom, wide tiles from there.
+constexpr int kWideFrom = 96;
+inline int bf16_tile_rows(int T, int K, int E) {
+  const long rows = (long)T * K;
+  return rows >= (long)kWideFrom * E ? kWideRows : rows >= 64L * E ? kTallRows : kTileRows;
+}
 // GEMM tasks are spread over this many queues, one per XCD: queue x holds the
 // tasks that workgroups with blockIdx % kQueues == x process.
 constexpr int kQueues = 8;
@@ -57,9 +66,14 @@ inline int max_queue_len(int T, int K, int E, int NB, int R) {
 }
 
 // Column blocks of the two GEMMs: gate_up tasks cover 64 features (their gate
-// and up rows), down tasks 128 outputs.
-inline int gate_up_blocks(int F) { return F / 64; }
-inline int down_blocks(int D) { return D / 128; }
+// and up rows), down tasks 128 outputs; with wide tiles 128 and 256 (the last
+// block may be partial).
+inline int gate_up_blocks(int F, int tile_rows = kTileRows) {
+  return tile_rows == kWideRows ? (F + 127) / 128 : F / 64;
+}
+inline int down_blocks(int D, int tile_rows = kTileRows) {
+  return tile_rows == kWideRows ? (D + 255) / 256 : D / 128;
+}
 
 struct RouterArgs {
   const void* x;        // [T, D] fp32 or bf16
@@ -155,7 +169,7 @@ struct FusedGemmArgs {
   int nb_gate_up;      // gate_up column blocks per tile
   uint32_t* dev_flags; // sticky device status word (DG_DEV_* bits of dg_moe.h)
 };
-hipError_t launch_gemm_fused(const FusedGemmArgs& f, bool tall, hipStream_t stream, const KernelEvents* ev);
+hipError_t launch_gemm_fused(const FusedGemmArgs& f, int tile_rows, hipStream_t stream, const KernelEvents* ev);
 // Create-time relayout of int4-g128 expert weights (codes [E][R][K/2], scales
 // [E][R][ceil(K/128)]) into fragment order: 1 KB of codes and 16 scales per
 // (expert, 16-row panel, 128-input group), the short last group padded with

@@ -87,14 +87,17 @@ def check_device_state(dbg, K, E, T, D, F):
     ql = dbg["queue_len"].cpu().numpy()
     counts = dbg["counts"].cpu().numpy()
     lens, caps = ql[:16].reshape(2, 8), ql[16:18]
-    for g, nb in enumerate((F // 64, D // 128)):
+    # the tile height and column blocks the launch used: 64- or 128-row tiles with blocks of 64 gate_up
+    # features and 128 down outputs, or 160-row tiles with blocks of 128 and 256 (the last one partial)
+    shapes = [(64, (F // 64, D // 128)), (128, (F // 64, D // 128)), (160, (-(-F // 128), -(-D // 256)))]
+    match = [(R, nbs) for R, nbs in shapes
+             if all(lens[g].sum() == nbs[g] * int(np.sum((counts + R - 1) // R)) for g in range(2))]
+    assert match, f"queue lengths {lens} match no tile height"
+    R, nbs = match[0]
+    tiles = int(np.sum((counts + R - 1) // R))
+    a_max = int((counts.max() + R - 1) // R)
+    for g, nb in enumerate(nbs):
         assert np.all(lens[g] <= caps[g]), f"GEMM {g}: queue lengths {lens[g]} over capacity {caps[g]}"
-        assert lens[g].sum() % nb == 0
-        tiles = lens[g].sum() // nb
-        # the tile height the permutation used is the one whose tile count matches
-        rows = [R for R in (64, 128) if int(np.sum((counts + R - 1) // R)) == tiles]
-        assert rows, f"GEMM {g}: {tiles} tiles match no tile height"
-        a_max = int((counts.max() + rows[0] - 1) // rows[0])
         bound = nb * (-(-tiles // 8) + 2 * a_max)
         assert lens[g].max() <= bound, f"GEMM {g}: queue {lens[g].max()} > balance bound {bound} ({lens[g]})"
 
