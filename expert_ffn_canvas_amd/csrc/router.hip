@@ -28,9 +28,7 @@ namespace dg {
 
 namespace {
 
-constexpr int kKChunk = 128;  // d_model columns per chunk
-constexpr int kWaves = 8;     // waves per workgroup; wave h owns chunks h, h + 8, ...
-constexpr int kChunkRowBytes = kKChunk * 2;
+constexpr int kWaves = 8;  // waves per workgroup; wave h owns chunks h, h + 8, ... of d_model
 
 // z = hi + mid + lo exactly: hi keeps the top 8 significant bits of z
 // (truncated), mid the next 8 of the remainder, and the last remainder has at
@@ -196,10 +194,15 @@ __device__ __forceinline__ void write_h(const RouterArgs& a, const float* rs, in
 // workgroups, one per half of its 16 experts: each loads only its half of
 // every W' fragment (the other lanes' operands are zero), so the W' bytes a
 // CU takes in are halved and twice as many CUs share them.
-template <bool XF32, int MT, int G, int NU, int SPLIT>
+template <bool XF32, int MT, int G, int NU, int SPLIT, int CH>
 __global__ __launch_bounds__(64 * kWaves) void k_logits(RouterArgs a) {
   constexpr int kRows = 16 * MT;
-  constexpr int kXsBytes = XF32 ? 0 : kWaves * G * MT * 16 * kChunkRowBytes;
+  constexpr int kKK = CH / 32;         // 32-column MFMA steps per chunk
+  constexpr int kSeg = CH / 8;         // 16-byte segments per staged row
+  constexpr int kRB = CH * 2;          // bytes per staged row
+  constexpr int kRPD = 1024 / kRB;     // rows per wave-wide transfer
+  static_assert(!XF32 || CH == 128, "fp32 rows are read in 128-column chunks");
+  constexpr int kXsBytes = XF32 ? 0 : kWaves * G * MT * 16 * kRB;
   constexpr int kPartBytes = kWaves * kRows * 17 * 4;
   constexpr int kBuf = kXsBytes > kPartBytes ? kXsBytes : kPartBytes;
   __shared__ __attribute__((aligned(16))) char smem[kBuf];
@@ -227,7 +230,7 @@ __global__ __launch_bounds__(64 * kWaves) void k_logits(RouterArgs a) {
   const int m = lane & 15, g = lane >> 4;
   const bool wmine = SPLIT == 1 || (m >> 3) == half;  // this lane's expert is in the workgroup's half
   const float* wfrag = a.wr + (size_t)et * nks * 512 + lane * 4;
-  const int nc = D / kKChunk;
+  const int nc = D / CH;
   const int n_my = (nc - kh + kWaves - 1) / kWaves;  // chunks kh, kh + 8, ...
 
   f32x4 acc[3][MT];
@@ -240,41 +243,40 @@ __global__ __launch_bounds__(64 * kWaves) void k_logits(RouterArgs a) {
   }
 
   for (int c0 = 0; c0 < n_my; c0 += G) {
-    u32x4 wb[G][4][2];
+    u32x4 wb[G][kKK][2];
     u32x4 xf[XF32 ? G : 1][XF32 ? MT : 1][4][2];
 #pragma unroll
     for (int q = 0; q < G; ++q) {
       const int chunk = kh + kWaves * min(c0 + q, n_my - 1);
-      const int col = chunk * kKChunk;
+      const int col = chunk * CH;
       if constexpr (XF32) {
 #pragma unroll
         for (int mt = 0; mt < MT; ++mt) {
           const float* xr = static_cast<const float*>(a.x) + (size_t)min(t0 + mt * 16 + m, a.T - 1) * D + col + g * 8;
 #pragma unroll
-          for (int kk = 0; kk < 4; ++kk) {
+          for (int kk = 0; kk < kKK; ++kk) {
             xf[q][mt][kk][0] = *reinterpret_cast<const u32x4*>(xr + kk * 32);
             xf[q][mt][kk][1] = *reinterpret_cast<const u32x4*>(xr + kk * 32 + 4);
           }
         }
       } else {
         const uint32_t base =
-            __builtin_amdgcn_readfirstlane(gemm::lds_addr(smem) + (kh * G + q) * MT * 16 * kChunkRowBytes);
+            __builtin_amdgcn_readfirstlane(gemm::lds_addr(smem) + (kh * G + q) * MT * 16 * kRB);
         const uint16_t* xb = static_cast<const uint16_t*>(a.x);
 #pragma unroll
         for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            const int r = mt * 16 + 4 * i + (lane >> 4);
-            const int s = (lane & 15) ^ (r & 15);
-            gemm::lds_dma16(base + (mt * 16 + 4 * i) * kChunkRowBytes,
-                            xb + (size_t)min(t0 + r, a.T - 1) * D + col + s * 8);
+          for (int i = 0; i < 16 / kRPD; ++i) {
+            const int r = mt * 16 + kRPD * i + lane / kSeg;
+            const int s = (lane % kSeg) ^ (r % kSeg);
+            gemm::lds_dma16(base + (mt * 16 + kRPD * i) * kRB, xb + (size_t)min(t0 + r, a.T - 1) * D + col + s * 8);
           }
       }
 #pragma unroll
-      for (int kk = 0; kk < 4; ++kk)
+      for (int kk = 0; kk < kKK; ++kk)
 #pragma unroll
         for (int h = 0; h < 2; ++h)
-          wb[q][kk][h] = wmine ? *reinterpret_cast<const u32x4*>(wfrag + (size_t)(chunk * 4 + kk) * 512 + h * 256)
+          wb[q][kk][h] = wmine ? *reinterpret_cast<const u32x4*>(wfrag + (size_t)(chunk * kKK + kk) * 512 + h * 256)
                                : u32x4{0u, 0u, 0u, 0u};
     }
     // all of the group's loads are in flight before the first multiply: one
@@ -286,7 +288,7 @@ __global__ __launch_bounds__(64 * kWaves) void k_logits(RouterArgs a) {
       const bool valid = c0 + q < n_my;
       const uint32_t keep = valid ? 0xffffffffu : 0u;
 #pragma unroll
-      for (int kk = 0; kk < 4; ++kk) {
+      for (int kk = 0; kk < kKK; ++kk) {
         // the lane's 8 fp32 weights -> three exact bf16 planes (W' = W0 + W1 + W2)
         bf16x8 w[3];
         {
@@ -338,8 +340,8 @@ __global__ __launch_bounds__(64 * kWaves) void k_logits(RouterArgs a) {
             acc[2][mt] = mfma_bf16(as_bf16x8(xl), w[0], acc[2][mt]);
           } else {
             const int r = mt * 16 + m;
-            const u32x4 xv = *reinterpret_cast<const u32x4*>(smem + (kh * G + q) * MT * 16 * kChunkRowBytes +
-                                                              r * kChunkRowBytes + (((kk * 4 + g) ^ m) * 16));
+            const u32x4 xv = *reinterpret_cast<const u32x4*>(smem + (kh * G + q) * MT * 16 * kRB + r * kRB +
+                                                              (((kk * 4 + g) ^ (m % kSeg)) * 16));
             ss[mt] += valid ? sumsq8(xv) : 0.0f;
 #pragma unroll
             for (int p = 0; p < 3; ++p) acc[p][mt] = mfma_bf16(as_bf16x8(xv), w[p], acc[p][mt]);
@@ -451,12 +453,12 @@ __global__ void k_prep_router_w(const void* __restrict__ w, int w_f32, const flo
   }
 }
 
-template <bool XF32, int MT, int G, int SPLIT = 1>
+template <bool XF32, int MT, int G, int SPLIT = 1, int CH = 128>
 void (*pick_logits(int nu))(RouterArgs) {
-  return nu <= 2   ? k_logits<XF32, MT, G, 2, SPLIT>
-         : nu <= 4 ? k_logits<XF32, MT, G, 4, SPLIT>
-         : nu <= 8 ? k_logits<XF32, MT, G, 8, SPLIT>
-                   : k_logits<XF32, MT, G, 16, SPLIT>;
+  return nu <= 2   ? k_logits<XF32, MT, G, 2, SPLIT, CH>
+         : nu <= 4 ? k_logits<XF32, MT, G, 4, SPLIT, CH>
+         : nu <= 8 ? k_logits<XF32, MT, G, 8, SPLIT, CH>
+                   : k_logits<XF32, MT, G, 16, SPLIT, CH>;
 }
 
 }  // namespace
@@ -486,10 +488,10 @@ hipError_t launch_logits(const RouterArgs& a, hipStream_t stream, const KernelEv
   if (a.x_f32)  // fp32 x lives in registers: at most two m-tiles
     k = mt == 1 ? (split == 2 ? pick_logits<true, 1, 2, 2>(nu) : pick_logits<true, 1, 2>(nu))
                 : pick_logits<true, 2, 1>(nu);
-  else
+  else  // 32 and 64 tokens: 64-column chunks, so the x stages take 64 KB and two workgroups share a CU
     k = mt == 1   ? (split == 2 ? pick_logits<false, 1, 3, 2>(nu) : pick_logits<false, 1, 3>(nu))
-        : mt == 2 ? pick_logits<false, 2, 2>(nu)
-                  : pick_logits<false, 4, 1>(nu);
+        : mt == 2 ? pick_logits<false, 2, 2, 1, 64>(nu)
+                  : pick_logits<false, 4, 1, 1, 64>(nu);
   return launch_kernel(k, grid, dim3(64 * kWaves), stream, ev, a);
 }
 
