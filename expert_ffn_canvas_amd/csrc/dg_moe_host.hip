@@ -151,6 +151,7 @@ struct dg_moe_s {
   dg_moe_config cfg;
   Layout L;
   int device;
+  int n_cu;           // compute units of the device
   char* ws;           // workspace + prepared router parameters
   void* packed;       // expert weights copied at create (pack mode), else null
   int w_packed = 0;   // expert weights in the fragment layout of their packing kernel
@@ -261,6 +262,7 @@ dg_status dg_moe_create(const dg_moe_config* cfg, const dg_moe_weights* w, void*
   hd->cfg = *cfg;
   hd->L = plan(*cfg);
   hd->device = dev;
+  hd->n_cu = prop.multiProcessorCount > 0 ? prop.multiProcessorCount : 256;
   hipStream_t stream = static_cast<hipStream_t>(stream_v);
 
   e = hipMalloc(reinterpret_cast<void**>(&hd->ws), hd->L.total);
@@ -415,6 +417,7 @@ static dg_status run_forward(dg_moe_handle hd, const void* x, void* out, int32_t
   ra.bias = hd->has_bias ? hd->at<float>(L.bias) : nullptr;
   ra.gamma_e = hd->at<float>(L.gamma_e);
   ra.eps = c.rms_eps;
+  ra.n_cu = hd->n_cu;
   ra.h_f16 = (i4 || q8) ? 1 : 0;  // MXFP4 / MXFP8 widen to bf16 (their block scales need bf16's exponent range)
   ra.h = L.fold ? nullptr : hd->at<uint16_t>(L.h);
   ra.rnorm = hd->at<float>(L.rnorm);

@@ -92,6 +92,7 @@ struct RouterArgs {
   int32_t* topk_idx;    // [T, K]
   float* topk_w;        // [T, K]
   uint32_t* dev_flags;  // sticky device status word (DG_DEV_* bits of dg_moe.h)
+  int n_cu;             // compute units of the device (sets the token-tile height)
 };
 // r, logits, top-k and the routing weights, and h = x r (1 + gamma_e) where h
 // is not null.

@@ -68,35 +68,54 @@ __device__ __forceinline__ float add_step(float v) {
   return v + __uint_as_float(dpp<CTRL>(__float_as_uint(v)));
 }
 
-// Top-k of one token per 16-lane row: lane j holds the logits of experts
-// j + 16 u (u < NU, E <= 16 NU), read from `row`. Round q takes the largest
-// remaining (logit, lowest id) of the row and removes it, so the k rounds
-// produce the selection in slot order (logit descending, ties by id). Lane
-// q < k keeps round q's pick and writes slot q with its softmax over the k
-// (the shift by the largest logit cancels in the renormalisation). A NaN
-// logit ranks below every number; experts >= E are never picked.
+// The logits of one token for top-k, 16 lanes per token: lane j holds those
+// of experts NU j .. NU j + NU - 1, read as whole 16-byte pieces (8 bytes for
+// NU = 2). Epad is a multiple of 16, so each lane's range lies either wholly
+// inside the row or wholly past it; a lane past it re-reads the row's start
+// (those experts are >= E and never picked).
 template <int NU>
-__device__ __forceinline__ void topk_row(const float* row, bool active, int E, int K, int j, int32_t* idx_out,
-                                         float* w_out) {
-  // all NU loads issued at once (a clamped index instead of a guarded load,
-  // which would wait for each load in turn), masked afterwards
-  float lv[NU];
+__device__ __forceinline__ void load_row(const float* row, int j, int Epad, float (&lv)[NU]) {
+  j = (NU * j < Epad) ? j : 0;
+  if constexpr (NU == 2) {
+    const float2 v = *reinterpret_cast<const float2*>(row + 2 * j);
+    lv[0] = v.x;
+    lv[1] = v.y;
+  } else {
 #pragma unroll
-  for (int u = 0; u < NU; ++u) lv[u] = row[min(j + 16 * u, E - 1)];
+    for (int i = 0; i < NU / 4; ++i) {
+      const float4 v = *reinterpret_cast<const float4*>(row + NU * j + 4 * i);
+      lv[4 * i] = v.x;
+      lv[4 * i + 1] = v.y;
+      lv[4 * i + 2] = v.z;
+      lv[4 * i + 3] = v.w;
+    }
+  }
+}
+
+// Top-k of one token per 16-lane row, from the logits load_row gave lane j.
+// Round q takes the largest remaining (logit, lowest id) of the row and
+// removes it, so the k rounds produce the selection in slot order (logit
+// descending, ties by id). Lane q < k keeps round q's pick and writes slot q
+// with its softmax over the k (the shift by the largest logit cancels in the
+// renormalisation). A NaN logit ranks below every number; experts >= E are
+// never picked.
+template <int NU>
+__device__ __forceinline__ void topk_row(const float (&lv)[NU], bool active, int E, int K, int j, int32_t* idx_out,
+                                         float* w_out) {
   uint32_t key[NU];
 #pragma unroll
   for (int u = 0; u < NU; ++u) {
     const float l = (lv[u] == lv[u]) ? lv[u] : -INFINITY;
-    key[u] = (j + 16 * u < E) ? float_key(l) : 0u;  // every real expert's key is > 0
+    key[u] = (NU * j + u < E) ? float_key(l) : 0u;  // every real expert's key is > 0
   }
   uint32_t my_key = 0, my_id = 0, top = 0;
   for (int q = 0; q < K; ++q) {
-    uint32_t bk = key[0], bi = (uint32_t)j;
+    uint32_t bk = key[0], bi = (uint32_t)(NU * j);
 #pragma unroll
     for (int u = 1; u < NU; ++u) {
       const bool gt = key[u] > bk;  // strict: on equal keys the lower id stays
       bk = gt ? key[u] : bk;
-      bi = gt ? (uint32_t)(j + 16 * u) : bi;
+      bi = gt ? (uint32_t)(NU * j + u) : bi;
     }
     argmax_step<kDppXor1>(bk, bi);
     argmax_step<kDppXor2>(bk, bi);
@@ -107,9 +126,9 @@ __device__ __forceinline__ void topk_row(const float* row, bool active, int E, i
       my_key = bk;
       my_id = bi;
     }
-    const bool own = (int)(bi & 15u) == j;
+    const bool own = (int)(bi / NU) == j;
 #pragma unroll
-    for (int u = 0; u < NU; ++u) key[u] = (own && (int)(bi >> 4) == u) ? 0u : key[u];
+    for (int u = 0; u < NU; ++u) key[u] = (own && (int)(bi % NU) == u) ? 0u : key[u];
   }
   const float ex = (j < K) ? __expf(key_float(my_key) - key_float(top)) : 0.0f;
   float den = add_step<kDppXor1>(ex);
@@ -410,12 +429,21 @@ __global__ __launch_bounds__(64 * kWaves) void k_logits(RouterArgs a) {
   // XCD's L2 (every writer ran on this XCD and waited for its stores); no
   // workgroup on this CU read these rows earlier in the launch, so its L1
   // holds no stale copy. Wave h takes tokens 4 h .. 4 h + 3 of each 32-token
-  // group of the tile, one per 16-lane row.
-  for (int tl0 = 4 * kh; tl0 < kRows; tl0 += 4 * kWaves) {
-    const int tl = tl0 + (lane >> 4);
-    const bool active = t0 + tl < a.T;
+  // group of the tile, one per 16-lane row; all of a wave's rows are loaded
+  // before the first selection (one memory round trip).
+  constexpr int kPass = (kRows + 4 * kWaves - 1) / (4 * kWaves);
+  float lv[kPass][NU];
+#pragma unroll
+  for (int it = 0; it < kPass; ++it) {
+    const int tl = 4 * kh + 4 * kWaves * it + (lane >> 4);
+    if (4 * kh + 4 * kWaves * it < kRows) load_row<NU>(a.logits + (size_t)min(t0 + tl, a.T - 1) * a.Epad, m, a.Epad, lv[it]);
+  }
+#pragma unroll
+  for (int it = 0; it < kPass; ++it) {
+    const int tl = 4 * kh + 4 * kWaves * it + (lane >> 4);
+    if (4 * kh + 4 * kWaves * it >= kRows) break;
     const size_t trow = (size_t)min(t0 + tl, a.T - 1);
-    topk_row<NU>(a.logits + trow * a.Epad, active, a.E, a.K, m, a.topk_idx + trow * a.K, a.topk_w + trow * a.K);
+    topk_row<NU>(lv[it], t0 + tl < a.T, a.E, a.K, m, a.topk_idx + trow * a.K, a.topk_w + trow * a.K);
   }
   if (a.h != nullptr) write_h<XF32, kRows>(a, rs, t0, s0, s1, tid, 64 * kWaves);
 }
@@ -465,18 +493,31 @@ void (*pick_logits(int nu))(RouterArgs) {
 
 hipError_t launch_logits(const RouterArgs& a, hipStream_t stream, const KernelEvents* ev) {
   const int n_et = a.Epad / 16;
-  // more m-tiles per workgroup once 16-token tiles would give more than two
-  // workgroups per CU: W' is then re-read by fewer workgroups, and the grid
-  // fits the chip in one round (T = 2304: 288 workgroups of 64 tokens, 35 us,
-  // against 576 of 32 tokens, 38 us)
-  const size_t n16 = (size_t)((a.T + 15) / 16) * n_et;
+  // Token-tile height, 16 mt rows. A workgroup's time follows the bytes it
+  // reads: 16 mt rows of x and 16 rows of W' (fp32, twice a bf16 x row), so
+  // it grows as mt + 2 (bf16 x) or mt + 1 (fp32 x); a CU that holds two
+  // workgroups takes about twice as long. The launch then takes about
+  // ceil(workgroups / CUs) (mt + 2): the height that minimises this, the
+  // taller on ties (W' is then re-read by fewer workgroups). T = 2304: 232
+  // workgroups of 80 tokens, one round, against 288 of 64 tokens.
 #ifndef DG_LOGITS_MT
-  const int mt = n16 <= 512 ? 1 : n16 <= 1024 ? 2 : 4;
+  static const int kCandBf16[] = {1, 2, 4, 5}, kCandF32[] = {1, 2};
+  const int* cand = a.x_f32 ? kCandF32 : kCandBf16;
+  const int n_cand = a.x_f32 ? 2 : 4;
+  int mt = 1;
+  long long best = -1;
+  for (int i = 0; i < n_cand; ++i) {
+    const long long wgs = (long long)((a.T + 16 * cand[i] - 1) / (16 * cand[i])) * n_et;
+    const long long cost = (wgs + a.n_cu - 1) / a.n_cu * (cand[i] + (a.x_f32 ? 1 : 2));
+    if (best < 0 || cost <= best) {
+      best = cost;
+      mt = cand[i];
+    }
+  }
 #else
   const int mt = DG_LOGITS_MT;
 #endif
-  const int rows = 16 * (a.x_f32 ? min(mt, 2) : mt);
-  const int n_tt = (a.T + rows - 1) / rows;
+  const int n_tt = (a.T + 16 * mt - 1) / (16 * mt);
   // at most 64 workgroups of 16-token tiles: two workgroups per expert tile
   // (T = 32: 128 workgroups of 8 experts, 17.4 against 18.3 us; at T = 256,
   // 256 against 128 workgroups gained nothing)
@@ -488,10 +529,11 @@ hipError_t launch_logits(const RouterArgs& a, hipStream_t stream, const KernelEv
   if (a.x_f32)  // fp32 x lives in registers: at most two m-tiles
     k = mt == 1 ? (split == 2 ? pick_logits<true, 1, 2, 2>(nu) : pick_logits<true, 1, 2>(nu))
                 : pick_logits<true, 2, 1>(nu);
-  else  // 32 and 64 tokens: 64-column chunks, so the x stages take 64 KB and two workgroups share a CU
+  else  // from 32 tokens: 64-column chunks, so the x stages take 64 KB (80 KB at 80 tokens)
     k = mt == 1   ? (split == 2 ? pick_logits<false, 1, 3, 2>(nu) : pick_logits<false, 1, 3>(nu))
         : mt == 2 ? pick_logits<false, 2, 2, 1, 64>(nu)
-                  : pick_logits<false, 4, 1, 1, 64>(nu);
+        : mt == 4 ? pick_logits<false, 4, 1, 1, 64>(nu)
+                  : pick_logits<false, 5, 1, 1, 64>(nu);
   return launch_kernel(k, grid, dim3(64 * kWaves), stream, ev, a);
 }
 

@@ -138,13 +138,15 @@ def test_encode2304_sampled(encode2304, pack):
     layer.close()
 
 
-# The router's kernel variant depends on T, the number of experts and the activation type: 16, 32 or 64
-# tokens per workgroup (more once 16-token tiles would give more than 512 or 1024 workgroups), two
-# workgroups per expert tile when the 16-token tiles give at most 64, fp32 rows held in registers (at most 32
-# tokens). These cases reach each variant at the model's E = 128 and d_model, with a ragged last token tile.
+# The router's kernel variant depends on T, the number of experts, the CU count and the activation type:
+# 16, 32, 64 or 80 tokens per workgroup (the height that fills the CUs in the fewest rounds for the bytes
+# each workgroup reads), two workgroups per expert tile when the 16-token tiles give at most 64, fp32 rows
+# held in registers (at most 32 tokens). These cases reach each variant at the model's E = 128 and d_model
+# on a 256-CU device, with a ragged last token tile.
 @pytest.mark.parametrize("T,act,variant", [
-    (1500, "bf16", "bf16 x, 32-token workgroups, ragged last tile (1500 = 46 x 32 + 28)"),
-    (2200, "bf16", "bf16 x, 64-token workgroups, ragged last tile (2200 = 34 x 64 + 24)"),
+    (1000, "bf16", "bf16 x, 32-token workgroups, ragged last tile (1000 = 31 x 32 + 8)"),
+    (1500, "bf16", "bf16 x, 64-token workgroups, ragged last tile (1500 = 23 x 64 + 28)"),
+    (2200, "bf16", "bf16 x, 80-token workgroups, ragged last tile (2200 = 27 x 80 + 40)"),
     (256, "f32", "fp32 x, 16-token workgroups, one per expert tile"),
     (1500, "f32", "fp32 x, 32-token workgroups, ragged last tile"),
     (40, "f32", "fp32 x, 16-token workgroups, two per expert tile, ragged"),
