@@ -78,7 +78,52 @@ def check_permutation(dbg, K, E, T):
     assert int(pm["counts"].sum()) == K * T
 
 
-def check_device_state(dbg, K, E, T, D, F):
+def snake(h):
+    """Queue of the h-th expert dealt in snake order over the 8 queues (0..7, then 7..0, ...)."""
+    return 7 - h % 8 if (h // 8) % 2 else h % 8
+
+
+def balanced_deal(ntile, counts):
+    """The queue of every expert under the permutation's balanced deal of whole experts, from the tile counts
+    (ntile) and token counts of the experts, written out step by step as the deal is specified: the experts
+    with more than the smallest nonzero tile count v1 are dealt in snake order by id; if the most loaded queue
+    then exceeds an even share of all tiles by more than the largest tile count, they are dealt again in snake
+    order of their rank by token count (descending, ties to the lower id); the experts of v1 tiles then fill
+    the queues level by level (queue q at level load_q // v1), the i-th of them (in id order) taking the i-th
+    smallest (level, queue) pair at or above each queue's level. Returns a list (None for experts without
+    rows)."""
+    ntile = [int(v) for v in ntile]
+    E = len(ntile)
+    nz = [v for v in ntile if v > 0]
+    qof = [None] * E
+    if not nz:
+        return qof
+    v1, total, a_max = min(nz), sum(ntile), max(ntile)
+    heavy = [e for e in range(E) if ntile[e] > v1]
+    tail = [e for e in range(E) if ntile[e] == v1]
+    pos = {e: i for i, e in enumerate(heavy)}
+    load = [0] * 8
+    for e in heavy:
+        load[snake(pos[e])] += ntile[e]
+    if max(load) > (total + 7) // 8 + a_max:
+        order = sorted(range(E), key=lambda e: (-int(counts[e]), e))
+        pos = {e: r for r, e in enumerate(order) if e in pos}
+        load = [0] * 8
+        for e in heavy:
+            load[snake(pos[e])] += ntile[e]
+    for e in heavy:
+        qof[e] = snake(pos[e])
+    lv = [l // v1 for l in load]
+    for i, e in enumerate(tail):
+        lam = min(lv)
+        while sum(max(0, lam + 1 - l) for l in lv) <= i:
+            lam += 1
+        j = i - sum(max(0, lam - l) for l in lv)
+        qof[e] = [q for q in range(8) if lv[q] <= lam][j]
+    return qof
+
+
+def check_device_state(dbg, K, E, T, D, F, balanced=None):
     """The handle's sticky device status word is clear, and the per-XCD task queues hold their tasks within the
     capacity and within the balance the deal guarantees: no queue more than 2 tiles of the largest expert above
     an even share of all tiles (per column block of each GEMM)."""
@@ -100,6 +145,16 @@ def check_device_state(dbg, K, E, T, D, F):
         assert np.all(lens[g] <= caps[g]), f"GEMM {g}: queue lengths {lens[g]} over capacity {caps[g]}"
         bound = nb * (-(-tiles // 8) + 2 * a_max)
         assert lens[g].max() <= bound, f"GEMM {g}: queue {lens[g].max()} > balance bound {bound} ({lens[g]})"
+    if balanced:
+        # every queue holds exactly the tiles the balanced deal gives it
+        ntile = (counts + R - 1) // R
+        qof = balanced_deal(ntile, counts)
+        want = np.zeros(8, dtype=np.int64)
+        for e in range(E):
+            if qof[e] is not None:
+                want[qof[e]] += ntile[e]
+        for g, nb in enumerate(nbs):
+            assert np.array_equal(lens[g], nb * want), f"GEMM {g}: queue lengths {lens[g]}, deal gives {nb * want}"
 
 
 def rel_max_err(gpu, ref):
@@ -126,7 +181,7 @@ def layer_parity(layer, x, wn, K, eps=synth.RMS_EPS, tokens=None, n_threads=0):
     gw = dbg["topk_w"].cpu().numpy()
     near = check_routing(gidx, gw, orc, K, T)
     check_permutation(dbg, K, layer.E, T)
-    check_device_state(dbg, K, layer.E, T, layer.D, layer.F)
+    check_device_state(dbg, K, layer.E, T, layer.D, layer.F, balanced=layer.gemms_fused)
     tok = np.arange(T) if tokens is None else np.asarray(tokens)
     ref = oracle.moe_forward(wn, xn, K, eps, forced=gidx, tokens=tok, n_threads=n_threads)
     gout = to_f32(dbg["out"])[tok]
