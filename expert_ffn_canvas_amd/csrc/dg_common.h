@@ -27,6 +27,16 @@ struct Tile {
 
 constexpr int kWave = 64;
 
+// Load with the non-temporal hint, for the expert weights (and the embedding
+// table): each launch reads them once, so they stream past the caches
+// instead of displacing the activations, gated rows and routing tables that
+// the launch and the kernels after it re-read from L2 and the memory-side
+// cache (canvas 256: the layer 204 -> 195 us).
+template <typename T>
+__device__ __forceinline__ T ld_stream(const T* p) {
+  return __builtin_nontemporal_load(p);
+}
+
 // fp32 -> bf16 bits, round to nearest even (NaN stays NaN).
 __device__ __forceinline__ uint16_t f32_to_bf16_bits(float f) {
   uint32_t u = __float_as_uint(f);

@@ -57,8 +57,8 @@ template <bool PK, int NS>
 __device__ __forceinline__ void load_w(const uint16_t* w0, const uint16_t* w1, int k0, Panels& p) {
 #pragma unroll
   for (int s = 0; s < NS; ++s) {
-    p.b0[s] = *reinterpret_cast<const u32x4*>(w0 + (size_t)((k0 + 32 * s) >> 5) * p.wstep);
-    p.b1[s] = *reinterpret_cast<const u32x4*>(w1 + (size_t)((k0 + 32 * s) >> 5) * p.wstep);
+    p.b0[s] = ld_stream(reinterpret_cast<const u32x4*>(w0 + (size_t)((k0 + 32 * s) >> 5) * p.wstep));
+    p.b1[s] = ld_stream(reinterpret_cast<const u32x4*>(w1 + (size_t)((k0 + 32 * s) >> 5) * p.wstep));
   }
 }
 

@@ -43,18 +43,31 @@ __device__ __forceinline__ uint32_t lds_addr(const void* p) {
 // is awaited explicitly (vmcnt) before the workgroup barrier that publishes it.
 // No register is written, so nothing is left in flight in a register.
 // M0 is saved and restored around the transfer, so nothing the compiler keeps
-// in M0 is disturbed.
+// in M0 is disturbed. NT: with the non-temporal hint, for data read once
+// (an embedding table streamed past the caches).
+template <bool NT = false>
 __device__ __forceinline__ void lds_dma16(uint32_t lds_base, const void* gaddr) {
   uint32_t saved;
-  asm volatile(
-      "s_mov_b32 %0, m0\n\t"
-      "s_mov_b32 m0, %1\n\t"
-      "s_nop 0\n\t"
-      "global_load_lds_dwordx4 %2, off\n\t"
-      "s_mov_b32 m0, %0"
-      : "=&s"(saved)
-      : "s"(lds_base), "v"(gaddr)
-      : "memory");
+  if constexpr (NT)
+    asm volatile(
+        "s_mov_b32 %0, m0\n\t"
+        "s_mov_b32 m0, %1\n\t"
+        "s_nop 0\n\t"
+        "global_load_lds_dwordx4 %2, off nt\n\t"
+        "s_mov_b32 m0, %0"
+        : "=&s"(saved)
+        : "s"(lds_base), "v"(gaddr)
+        : "memory");
+  else
+    asm volatile(
+        "s_mov_b32 %0, m0\n\t"
+        "s_mov_b32 m0, %1\n\t"
+        "s_nop 0\n\t"
+        "global_load_lds_dwordx4 %2, off\n\t"
+        "s_mov_b32 m0, %0"
+        : "=&s"(saved)
+        : "s"(lds_base), "v"(gaddr)
+        : "memory");
 }
 
 // DMA transfers per wave that stage ROWS activation rows with WV waves.

@@ -117,9 +117,9 @@ __global__ __launch_bounds__(kThreads) void k_gate_up_i4(GemmArgs a) {
 
   u32x4 ra[kAPass];
   load_a(src, 0, seg, D, ra);
-  u32x4 qg = *reinterpret_cast<const u32x4*>(wg);
-  u32x4 qu = *reinterpret_cast<const u32x4*>(wu);
-  uint16_t scg = sg[0], scu = su[0];
+  u32x4 qg = ld_stream(reinterpret_cast<const u32x4*>(wg));
+  u32x4 qu = ld_stream(reinterpret_cast<const u32x4*>(wu));
+  uint16_t scg = ld_stream(sg), scu = ld_stream(su);
   store_a(As[0], src, tid, ra);
   __syncthreads();
 
@@ -131,10 +131,10 @@ __global__ __launch_bounds__(kThreads) void k_gate_up_i4(GemmArgs a) {
     if (more) {
       const int k1 = (it + 1) * kSlab;
       load_a(src, k1, seg, D, ra);
-      qgn = *reinterpret_cast<const u32x4*>(wg + (size_t)(it + 1) * (kSlab / 2));
-      qun = *reinterpret_cast<const u32x4*>(wu + (size_t)(it + 1) * (kSlab / 2));
-      scgn = sg[it + 1];
-      scun = su[it + 1];
+      qgn = ld_stream(reinterpret_cast<const u32x4*>(wg + (size_t)(it + 1) * (kSlab / 2)));
+      qun = ld_stream(reinterpret_cast<const u32x4*>(wu + (size_t)(it + 1) * (kSlab / 2)));
+      scgn = ld_stream(sg + it + 1);
+      scun = ld_stream(su + it + 1);
     }
     f16x8 bg[4], bu[4];
 #pragma unroll
@@ -224,9 +224,9 @@ __global__ __launch_bounds__(kThreads) void k_down_i4(GemmArgs a) {
   const u32x4 zero4 = u32x4{0x88888888u, 0x88888888u, 0x88888888u, 0x88888888u};
   u32x4 ra[kAPass];
   load_a(src, 0, seg, F, ra);
-  u32x4 q0 = (g * 32 < F) ? *reinterpret_cast<const u32x4*>(w0) : zero4;
-  u32x4 q1 = (g * 32 < F) ? *reinterpret_cast<const u32x4*>(w1) : zero4;
-  uint16_t sc0 = s0[0], sc1 = s1[0];
+  u32x4 q0 = (g * 32 < F) ? ld_stream(reinterpret_cast<const u32x4*>(w0)) : zero4;
+  u32x4 q1 = (g * 32 < F) ? ld_stream(reinterpret_cast<const u32x4*>(w1)) : zero4;
+  uint16_t sc0 = ld_stream(s0), sc1 = ld_stream(s1);
   store_a(As[0], src, tid, ra);
   __syncthreads();
 
@@ -239,11 +239,11 @@ __global__ __launch_bounds__(kThreads) void k_down_i4(GemmArgs a) {
       const int k1 = (it + 1) * kSlab;
       load_a(src, k1, seg, F, ra);
       if (k1 + g * 32 < F) {
-        q0n = *reinterpret_cast<const u32x4*>(w0 + (size_t)(it + 1) * (kSlab / 2));
-        q1n = *reinterpret_cast<const u32x4*>(w1 + (size_t)(it + 1) * (kSlab / 2));
+        q0n = ld_stream(reinterpret_cast<const u32x4*>(w0 + (size_t)(it + 1) * (kSlab / 2)));
+        q1n = ld_stream(reinterpret_cast<const u32x4*>(w1 + (size_t)(it + 1) * (kSlab / 2)));
       }
-      sc0n = s0[it + 1];
-      sc1n = s1[it + 1];
+      sc0n = ld_stream(s0 + it + 1);
+      sc1n = ld_stream(s1 + it + 1);
     }
     f16x8 b0[4], b1[4];
 #pragma unroll
@@ -362,10 +362,10 @@ struct WGroup {
 
 __device__ __forceinline__ void load_wg(const uint8_t* c0, const uint8_t* c1, const uint16_t* s0, const uint16_t* s1,
                                         int gi, WGroup& w) {
-  w.c0 = *reinterpret_cast<const u32x4*>(c0 + (size_t)gi * 1024);
-  w.c1 = *reinterpret_cast<const u32x4*>(c1 + (size_t)gi * 1024);
-  w.s0 = s0[gi * 16];
-  w.s1 = s1[gi * 16];
+  w.c0 = ld_stream(reinterpret_cast<const u32x4*>(c0 + (size_t)gi * 1024));
+  w.c1 = ld_stream(reinterpret_cast<const u32x4*>(c1 + (size_t)gi * 1024));
+  w.s0 = ld_stream(s0 + gi * 16);
+  w.s1 = ld_stream(s1 + gi * 16);
 }
 
 // One group's MFMAs: partial sums over the 128 inputs in t, then scaled into acc.

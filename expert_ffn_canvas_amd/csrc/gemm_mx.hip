@@ -20,8 +20,10 @@
 // (1 KB for MXFP4, 2 KB for MXFP8) and 64 scale bytes. Lane l = n + 16 g of a
 // code block holds its row 16 p + n's inputs 128 s + 32 j + 8 g .. + 7 (block
 // 4 s + j) for j = 0..3: one dword per block for MXFP4 (two codes per byte,
-// the even input in the low nibble), two for MXFP8 (one code per byte, in
-// input order); the scale bytes are [n][j]. Blocks past the row (the 64-input
+// the even input in the low nibble; 16 bytes at 16 l), two for MXFP8 (one
+// code per byte, in input order; 32 bytes in two halves at 16 l and
+// 1024 + 16 l, so each 16-byte load of a wave reads whole cache lines); the
+// scale bytes are [n][j]. Blocks past the row (the 64-input
 // tail of a 704 row) are padded with zero codes and scale bytes.
 //
 // Exact widening: v_cvt_scalef32_pk_bf16_fp4 (one code byte) and
@@ -78,11 +80,11 @@ __device__ __forceinline__ void load_m(const uint8_t* c0, const uint8_t* c1, con
                                        int step, size_t cstep, size_t sstep, MPanels<BITS>& p) {
 #pragma unroll
   for (int h = 0; h < BITS / 4; ++h) {
-    p.c0[h] = *reinterpret_cast<const u32x4*>(c0 + (size_t)step * cstep + 16 * h);
-    p.c1[h] = *reinterpret_cast<const u32x4*>(c1 + (size_t)step * cstep + 16 * h);
+    p.c0[h] = ld_stream(reinterpret_cast<const u32x4*>(c0 + (size_t)step * cstep + 1024 * h));
+    p.c1[h] = ld_stream(reinterpret_cast<const u32x4*>(c1 + (size_t)step * cstep + 1024 * h));
   }
-  p.s0 = *reinterpret_cast<const uint32_t*>(s0 + (size_t)step * sstep);
-  p.s1 = *reinterpret_cast<const uint32_t*>(s1 + (size_t)step * sstep);
+  p.s0 = ld_stream(reinterpret_cast<const uint32_t*>(s0 + (size_t)step * sstep));
+  p.s1 = ld_stream(reinterpret_cast<const uint32_t*>(s1 + (size_t)step * sstep));
 }
 
 // 8 E2M1 codes of one dword (natural order, even input in the low nibble)
@@ -260,8 +262,8 @@ __device__ __forceinline__ void mx_body(const GemmArgs& a, const Tile& tl, char*
   const uint8_t* S = reinterpret_cast<const uint8_t*>(GATE_UP ? a.s_gate_up : a.s_down);
   const size_t blk0 = (size_t)tl.e * nks * np;  // block (e, 0, 0)
   MStream w;
-  w.c0 = C + (blk0 + p0) * kCB + lane * (kCB / 64);
-  w.c1 = C + (blk0 + p1) * kCB + lane * (kCB / 64);
+  w.c0 = C + (blk0 + p0) * kCB + lane * 16;
+  w.c1 = C + (blk0 + p1) * kCB + lane * 16;
   w.s0 = S + (blk0 + p0) * kMScaleBytes + (lane & 15) * 4;
   w.s1 = S + (blk0 + p1) * kMScaleBytes + (lane & 15) * 4;
   w.cstep = (size_t)np * kCB;
@@ -359,10 +361,10 @@ __global__ __launch_bounds__(256) void k_pack_mx(const uint8_t* __restrict__ src
       for (int h = 0; h < BITS / 4; ++h) o[j * (BITS / 4) + h] = v[h];
       sc |= ex << (8 * j);
     }
-    uint8_t* dst = pcodes + (b * 64 + lane) * (4 * BITS);
+    uint8_t* dst = pcodes + b * (64 * 4 * BITS) + lane * 16;
 #pragma unroll
     for (int h = 0; h < BITS / 4; ++h)
-      *reinterpret_cast<u32x4*>(dst + 16 * h) = u32x4{o[4 * h], o[4 * h + 1], o[4 * h + 2], o[4 * h + 3]};
+      *reinterpret_cast<u32x4*>(dst + 1024 * h) = u32x4{o[4 * h], o[4 * h + 1], o[4 * h + 2], o[4 * h + 3]};
     if (g == 0) *reinterpret_cast<uint32_t*>(pscales + b * kMScaleBytes + n * 4) = sc;
   }
 }

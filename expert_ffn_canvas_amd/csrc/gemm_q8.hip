@@ -10,12 +10,15 @@
 // Packed at create (the blocks are 34 bytes, unfit for 16-byte loads): per
 // (expert e, 128-input step s, 16-row panel p), in that order, 2 KB of codes
 // in MFMA fragment order and 64 fp16 scales. Lane l = n + 16 g of a code block
-// holds 32 bytes for row 16 p + n: bytes 8 j .. 8 j + 7 are the codes of inputs
-// 128 s + 32 j + 8 g .. + 7 (block 4 s + j), stored in the order k0 k2 k1 k3
-// k4 k6 k5 k7 so that the widening below yields natural order; the scales are
-// [n][j]. Blocks past the row (the 64-input tail of a 704 row) are padded with
-// zero codes and scales. So a wave reads its weight fragments as 2 KB
-// contiguous, and the panels of one expert at one step lie together.
+// holds 32 bytes for row 16 p + n, in two halves at 16 l and 1024 + 16 l:
+// bytes 8 j .. 8 j + 7 of the pair are the codes of inputs 128 s + 32 j +
+// 8 g .. + 7 (block 4 s + j), stored in the order k0 k2 k1 k3 k4 k6 k5 k7 so
+// that the widening below yields natural order; the scales are [n][j].
+// Blocks past the row (the 64-input tail of a 704 row) are padded with zero
+// codes and scales. So a wave reads its weight fragments as two 1 KB
+// contiguous loads (whole cache lines each, so the streaming hint never
+// drops a line that the other load still needs), and the panels of one expert
+// at one step lie together.
 //
 // Exact widening: a code byte masked into the low byte of each fp16 half, its
 // sign bit flipped and 0x64 put above it gives fp16 1024 + q + 128 exactly; one
@@ -53,12 +56,14 @@ __device__ __forceinline__ void load_q(const uint8_t* c0, const uint8_t* c1, con
                                        int step, size_t cstep, size_t sstep, QPanels& p) {
   const uint8_t* a = c0 + (size_t)step * cstep;
   const uint8_t* b = c1 + (size_t)step * cstep;
-  p.c0[0] = *reinterpret_cast<const u32x4*>(a);
-  p.c0[1] = *reinterpret_cast<const u32x4*>(a + 16);
-  p.c1[0] = *reinterpret_cast<const u32x4*>(b);
-  p.c1[1] = *reinterpret_cast<const u32x4*>(b + 16);
-  p.s0 = *reinterpret_cast<const uint2*>(s0 + (size_t)step * sstep);
-  p.s1 = *reinterpret_cast<const uint2*>(s1 + (size_t)step * sstep);
+  p.c0[0] = ld_stream(reinterpret_cast<const u32x4*>(a));
+  p.c0[1] = ld_stream(reinterpret_cast<const u32x4*>(a + 1024));
+  p.c1[0] = ld_stream(reinterpret_cast<const u32x4*>(b));
+  p.c1[1] = ld_stream(reinterpret_cast<const u32x4*>(b + 1024));
+  const uint64_t v0 = ld_stream(reinterpret_cast<const uint64_t*>(s0 + (size_t)step * sstep));
+  const uint64_t v1 = ld_stream(reinterpret_cast<const uint64_t*>(s1 + (size_t)step * sstep));
+  p.s0 = make_uint2((uint32_t)v0, (uint32_t)(v0 >> 32));
+  p.s1 = make_uint2((uint32_t)v1, (uint32_t)(v1 >> 32));
 }
 
 // Bytes 0 and 2 of v as fp16 1024 + 128 + q: (v & 0x00FF00FF) ^ 0x64806480
@@ -226,8 +231,8 @@ __device__ __forceinline__ void q8_body(const GemmArgs& a, const Tile& tl, char*
   const uint16_t* S = GATE_UP ? a.s_gate_up : a.s_down;
   const size_t blk0 = (size_t)tl.e * nks * np;  // block (e, 0, 0)
   QStream w;
-  w.c0 = C + (blk0 + p0) * kQCodeBytes + lane * 32;
-  w.c1 = C + (blk0 + p1) * kQCodeBytes + lane * 32;
+  w.c0 = C + (blk0 + p0) * kQCodeBytes + lane * 16;
+  w.c1 = C + (blk0 + p1) * kQCodeBytes + lane * 16;
   w.s0 = S + (blk0 + p0) * kQScales + (lane & 15) * 4;
   w.s1 = S + (blk0 + p1) * kQScales + (lane & 15) * 4;
   w.cstep = (size_t)np * kQCodeBytes;
@@ -307,9 +312,9 @@ __global__ __launch_bounds__(256) void k_pack_q8(const uint8_t* __restrict__ src
       o[j >> 1][(j & 1) * 2 + 1] = q[4] | (q[6] << 8) | (q[5] << 16) | (q[7] << 24);
       sc[j >> 1] |= d << (16 * (j & 1));
     }
-    uint8_t* dst = pcodes + (b * 64 + lane) * 32;
+    uint8_t* dst = pcodes + b * kQCodeBytes + lane * 16;
     *reinterpret_cast<u32x4*>(dst) = o[0];
-    *reinterpret_cast<u32x4*>(dst + 16) = o[1];
+    *reinterpret_cast<u32x4*>(dst + 1024) = o[1];
     if (g == 0) *reinterpret_cast<uint2*>(pscales + b * kQScales + n * 4) = make_uint2(sc[0], sc[1]);
   }
 }

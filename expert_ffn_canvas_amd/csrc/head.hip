@@ -84,8 +84,8 @@ __device__ __forceinline__ void head_dma_b(uint32_t stage, const uint16_t* emb, 
     const int blk = wave + kHWaves * i;
     const int r = blk * kHRowsPerDma + lane / kHSegs;
     const int sg = hswz(r, lane % kHSegs);
-    gemm::lds_dma16(__builtin_amdgcn_readfirstlane(stage + blk * 1024),
-                    emb + (size_t)min(vb * kHVoc + r, V - 1) * D + k * kHK + sg * 8);
+    gemm::lds_dma16<true>(__builtin_amdgcn_readfirstlane(stage + blk * 1024),
+                          emb + (size_t)min(vb * kHVoc + r, V - 1) * D + k * kHK + sg * 8);
   }
 }
 

@@ -184,9 +184,10 @@ hipError_t launch_down_i4(const GemmArgs& a, hipStream_t stream, const KernelEve
 hipError_t launch_gemm_fused_i4(const FusedGemmArgs& f, hipStream_t stream, const KernelEvents* ev);
 // Create-time relayout of Q8_0 expert weights (rows of K / 32 blocks of 34
 // bytes: fp16 scale, 32 int8 codes) into fragment order: per (expert, 128-input
-// step, 16-row panel), 2 KB of codes (lane n + 16 g: 32 bytes of row n, 8 per
-// 32-input block, inputs 8 g .. 8 g + 7 in the order 0 2 1 3 4 6 5 7) and 64
-// scales [row][block]; a short last step is padded with zero codes and scales.
+// step, 16-row panel), 2 KB of codes (lane l = n + 16 g: 32 bytes of row n in
+// two halves at 16 l and 1024 + 16 l, 8 per 32-input block, inputs
+// 8 g .. 8 g + 7 in the order 0 2 1 3 4 6 5 7) and 64 scales [row][block]; a
+// short last step is padded with zero codes and scales.
 hipError_t launch_pack_q8(const uint8_t* blocks, uint8_t* pcodes, uint16_t* pscales, int E, int R, int K,
                           hipStream_t stream);
 // Both products with packed Q8_0 weights (fp16 expert input and activation)
@@ -206,10 +207,10 @@ hipError_t launch_pack_mx4(const uint8_t* blocks, uint8_t* pcodes, uint8_t* psca
 hipError_t launch_gemm_fused_mx4(const FusedGemmArgs& f, hipStream_t stream, const KernelEvents* ev);
 // Create-time relayout of MXFP8 expert weights (rows of K / 32 blocks of 33
 // bytes: E8M0 scale byte, 32 E4M3 codes in input order) into fragment order:
-// per (expert, 128-input step, 16-row panel), 2 KB of codes (lane n + 16 g:
-// 32 bytes of row n, two dwords per 32-input block holding inputs
-// 8 g .. 8 g + 7 in order) and 64 scale bytes [row][block]; a short last step
-// is padded with zero codes and scale bytes.
+// per (expert, 128-input step, 16-row panel), 2 KB of codes (lane l = n + 16 g:
+// 32 bytes of row n in two halves at 16 l and 1024 + 16 l, two dwords per
+// 32-input block holding inputs 8 g .. 8 g + 7 in order) and 64 scale bytes
+// [row][block]; a short last step is padded with zero codes and scale bytes.
 hipError_t launch_pack_mx8(const uint8_t* blocks, uint8_t* pcodes, uint8_t* pscales, int E, int R, int K,
                            hipStream_t stream);
 // Both products with packed MXFP8 weights (bf16 expert input and activation)

@@ -79,119 +79,156 @@ __device__ __forceinline__ void load_ids(const int32_t* idx, int t, int K, int (
   }
 }
 
-// Balanced deal of whole experts: qof[e] = queue of expert e. v1 is the
-// smallest nonzero tile count. The experts with more tiles ("larger") are
-// dealt in snake order (queues 0..7, then 7..0, ...) by id; the experts of v1
-// tiles then fill the least loaded queues level by level, in id order: with
-// queue q at level Lq = (tiles so far) / v1, the i-th of them takes the i-th
-// smallest pair (Lq + k, q), k = 0, 1, ..., found by a binary search on the
-// level, so consecutive ones go to different queues.
+// Inclusive scan over the 64 lanes of a wave, for values >= 0 under + or
+// max (0 is the identity of both): row shifts by 1, 2, 4 and 8 scan each
+// 16-lane row, then row 0's total is broadcast into row 1 and row 2's into
+// row 3, and rows 0-1's total into rows 2 and 3 (gfx9 DPP).
+template <bool kMax>
+__device__ __forceinline__ int wave_scan(int x) {
+  auto op = [](int a, int b) { return kMax ? max(a, b) : a + b; };
+  x = op(x, __builtin_amdgcn_update_dpp(0, x, 0x111, 0xf, 0xf, true));   // row_shr:1
+  x = op(x, __builtin_amdgcn_update_dpp(0, x, 0x112, 0xf, 0xf, true));   // row_shr:2
+  x = op(x, __builtin_amdgcn_update_dpp(0, x, 0x114, 0xf, 0xf, true));   // row_shr:4
+  x = op(x, __builtin_amdgcn_update_dpp(0, x, 0x118, 0xf, 0xf, true));   // row_shr:8
+  x = op(x, __builtin_amdgcn_update_dpp(0, x, 0x142, 0xa, 0xf, false));  // row_bcast:15
+  x = op(x, __builtin_amdgcn_update_dpp(0, x, 0x143, 0xc, 0xf, false));  // row_bcast:31
+  return x;
+}
+// The wave's total (+ or max) of values >= 0, in every lane.
+template <bool kMax>
+__device__ __forceinline__ int wave_total(int x) {
+  return __builtin_amdgcn_readlane(wave_scan<kMax>(x), 63);
+}
+
+__device__ __forceinline__ int snake(int h) {
+  return ((h / kQueues) & 1) ? kQueues - 1 - h % kQueues : h % kQueues;
+}
+
+// Balanced deal of whole experts, in one wave: lane l holds experts
+// 4 l .. 4 l + 3 (tile counts v, token counts c) and gets their queues in q.
+// v1 is the smallest nonzero tile count. The experts with more tiles
+// ("larger") are dealt in snake order (queues 0..7, then 7..0, ...) by id;
+// the experts of v1 tiles then fill the least loaded queues level by level,
+// in id order: with queue x at level L_x = (tiles so far) / v1, the i-th of
+// them takes the i-th smallest pair (L_x + k, x), k = 0, 1, ..., so
+// consecutive ones go to different queues.
 // Dealt by id, the larger experts can pile up on one queue (under a skew that
 // tracks the ids they come nearly in order of size, but not in general). So
 // if the most loaded queue then exceeds an even share of all tiles by more
 // than the largest expert, the larger experts are dealt again in snake order
-// of their rank by count (descending, ties to the lower id; the larger
-// experts hold exactly the ranks before all others; rank fills crank): dealt
-// in non-increasing size, the snake keeps any two queues within the largest
-// tile count of each other. Either way the larger experts leave no queue
-// above the even share plus the largest count, and the level filling then
-// leaves none above the even share plus twice the largest count (a queue that
-// takes some ends below the common level plus 2 v1): the queues' capacity.
-// Deterministic, so both task lists agree. Called by every thread of the
-// block; expert e is thread e.
-template <typename Rank>
-__device__ void deal_balanced(const int* ntile, int* crank, int E, int tid, int lane, int wave, int* qof, int* sh,
-                              Rank rank) {
-  int* load = sh;       // [kQueues] tiles of the larger experts per queue
-  int* wmin = sh + 8;   // [4] per wave: smallest nonzero count
-  int* hcnt = sh + 12;  // [4] per wave: larger experts
-  int* tcnt = sh + 16;  // [4] per wave: experts of v1 tiles
-  int* wsum = sh + 20;  // [4] per wave: tiles
-  int* wmax = sh + 24;  // [4] per wave: largest count
-  const int e = tid;
-  const bool mine = wave < kMaxE / 64;
-  const int v = (e < E) ? ntile[e] : 0;
-  if (tid < kQueues) load[tid] = 0;
-  if (mine) {
-    int m = v > 0 ? v : 0x7fffffff, sm = v, mx = v;
-    for (int d = 32; d >= 1; d >>= 1) {
-      m = min(m, __shfl_xor(m, d));
-      sm += __shfl_xor(sm, d);
-      mx = max(mx, __shfl_xor(mx, d));
-    }
-    if (lane == 0) {
-      wmin[wave] = m;
-      wsum[wave] = sm;
-      wmax[wave] = mx;
-    }
+// of their rank by token count (descending, ties to the lower id; the larger
+// experts hold exactly the ranks before all others): dealt in non-increasing
+// size, the snake keeps any two queues within the largest tile count of each
+// other. Either way the larger experts leave no queue above the even share
+// plus the largest count, and the level filling then leaves none above the
+// even share plus twice the largest count (a queue that takes some ends
+// below the common level plus 2 v1): the queues' capacity. Deterministic, so
+// both task lists agree. Experts without rows get queue 0 (and no tasks).
+__device__ void deal_balanced(const int (&v)[4], const int* cnt, int E, int lane, int (&q)[4]) {
+  int big = 0, sum = 0, mx = 0;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    big = max(big, v[i] > 0 ? 0x7fffffff - v[i] : 0);
+    sum += v[i];
+    mx = max(mx, v[i]);
   }
-  __syncthreads();
-  const int v1 = min(min(wmin[0], wmin[1]), min(wmin[2], wmin[3]));
-  if (v1 == 0x7fffffff) return;  // no expert has rows
-  const int total = (wsum[0] + wsum[1]) + (wsum[2] + wsum[3]);
-  const int a_max = max(max(wmax[0], wmax[1]), max(wmax[2], wmax[3]));
-  const bool heavy = mine && v > v1, tail = mine && v == v1;
-  const uint64_t below = (1ull << lane) - 1ull;
-  uint64_t hb = 0, tb = 0;
-  if (mine) {
-    hb = __ballot(heavy);
-    tb = __ballot(tail);
-    if (lane == 0) {
-      hcnt[wave] = __popcll(hb);
-      tcnt[wave] = __popcll(tb);
+  big = wave_total<true>(big);
+#pragma unroll
+  for (int i = 0; i < 4; ++i) q[i] = 0;
+  if (big == 0) return;  // no expert has rows
+  const int v1 = 0x7fffffff - big, total = wave_total<false>(sum), a_max = wave_total<true>(mx);
+  int nh = 0, nt = 0;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    nh += v[i] > v1;
+    nt += v[i] == v1;
+  }
+  // position of each larger expert in the deal: its index among them by id
+  int h[4];
+  {
+    int k = wave_scan<false>(nh) - nh;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      h[i] = (v[i] > v1) ? k : -1;
+      k += v[i] > v1;
     }
   }
-  __syncthreads();
-  int hbase = 0, tbase = 0;
-  for (int w = 0; w < kMaxE / 64; ++w) {
-    hbase += (w < wave) ? hcnt[w] : 0;
-    tbase += (w < wave) ? tcnt[w] : 0;
-  }
-  auto snake = [](int h) { return ((h / kQueues) & 1) ? kQueues - 1 - h % kQueues : h % kQueues; };
-  if (heavy) atomicAdd(&load[snake(hbase + __popcll(hb & below))], v);
-  __syncthreads();
+  int load[kQueues];
+  auto deal_loads = [&]() {
+#pragma unroll
+    for (int x = 0; x < kQueues; ++x) {
+      int part = 0;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) part += (h[i] >= 0 && snake(h[i]) == x) ? v[i] : 0;
+      load[x] = wave_total<false>(part);
+    }
+  };
+  deal_loads();
   int hmax = 0;
 #pragma unroll
-  for (int q = 0; q < kQueues; ++q) hmax = max(hmax, load[q]);
+  for (int x = 0; x < kQueues; ++x) hmax = max(hmax, load[x]);
   if (hmax > (total + kQueues - 1) / kQueues + a_max) {
-    // the larger experts again, in order of size (the same decision in every thread)
-    rank(crank);
-    __syncthreads();
-    if (tid < kQueues) load[tid] = 0;
-    __syncthreads();
-    if (heavy) atomicAdd(&load[snake(crank[e])], v);
-    __syncthreads();
+    // positions by rank of token count instead (count desc, id asc)
+    int ce[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      ce[i] = (4 * lane + i < E) ? cnt[4 * lane + i] : 0;
+      if (h[i] >= 0) h[i] = 0;
+    }
+    for (int e0 = 0; e0 < E; e0 += 4) {
+      const int4 c4 = *reinterpret_cast<const int4*>(&cnt[e0]);  // the same address in every lane
+      const int cc[4] = {c4.x, c4.y, c4.z, c4.w};
+#pragma unroll
+      for (int k = 0; k < 4; ++k)
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          h[i] += (h[i] >= 0 && e0 + k < E && (cc[k] > ce[i] || (cc[k] == ce[i] && e0 + k < 4 * lane + i)));
+    }
+    deal_loads();
   }
-  if (heavy) qof[e] = snake(crank[e] >= 0 ? crank[e] : hbase + __popcll(hb & below));
-  if (tail) {
-    const int i = tbase + __popcll(tb & below);
-    int lv[kQueues], lmin = 0x7fffffff;
+  // levels of the queues after the larger experts, and the level filling:
+  // the first tail expert of this lane (index i0 among them by id) takes the
+  // largest level lam with C(lam) = sum_x max(0, lam - L_x) <= i0 and the
+  // (i0 - C(lam))-th queue (by index) at or below it; each later one the next
+  // queue at that level, or the first at the next level.
+  int lv[kQueues], lmin = 0x7fffffff;
 #pragma unroll
-    for (int q = 0; q < kQueues; ++q) {
-      lv[q] = div_small(load[q], v1);
-      lmin = min(lmin, lv[q]);
-    }
-    // the largest level lam with C(lam) <= i, C(lam) = sum_q max(0, lam - Lq)
-    int lo = lmin, hi = lmin + i;
-    while (lo < hi) {
-      const int mid = (lo + hi + 1) >> 1;
-      int c = 0;
-#pragma unroll
-      for (int q = 0; q < kQueues; ++q) c += max(0, mid - lv[q]);
-      if (c <= i) lo = mid; else hi = mid - 1;
-    }
+  for (int x = 0; x < kQueues; ++x) {
+    lv[x] = div_small(load[x], v1);
+    lmin = min(lmin, lv[x]);
+  }
+  const int i0 = wave_scan<false>(nt) - nt;
+  int lo = lmin, hi = lmin + i0;
+  while (lo < hi) {
+    const int mid = (lo + hi + 1) >> 1;
     int c = 0;
 #pragma unroll
-    for (int q = 0; q < kQueues; ++q) c += max(0, lo - lv[q]);
-    int j = i - c, pick = 0;
+    for (int x = 0; x < kQueues; ++x) c += max(0, mid - lv[x]);
+    if (c <= i0) lo = mid; else hi = mid - 1;
+  }
+  int c = 0;
 #pragma unroll
-    for (int q = 0; q < kQueues; ++q) {  // the j-th queue (by index) at or below level lo
-      if (lv[q] <= lo) {
-        if (j == 0) pick = q;
-        --j;
+  for (int x = 0; x < kQueues; ++x) c += max(0, lo - lv[x]);
+  int j = i0 - c;  // index among the queues at or below level lo
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    if (v[i] > v1) {
+      q[i] = snake(h[i]);
+    } else if (v[i] == v1) {
+      int n = 0, pick = 0;
+#pragma unroll
+      for (int x = 0; x < kQueues; ++x) {
+        if (lv[x] <= lo) {
+          if (n == j) pick = x;
+          ++n;
+        }
+      }
+      q[i] = pick;
+      if (++j == n) {  // the level is used up: on to the next
+        ++lo;
+        j = 0;
       }
     }
-    qof[e] = pick;
   }
 }
 
@@ -282,15 +319,12 @@ __device__ __forceinline__ void scatter(const PermuteArgs& a, int (&ids)[8], int
 }
 
 __global__ __launch_bounds__(kThreads) void k_permute(PermuteArgs a) {
-  __shared__ int cnt[kMaxE];
-  __shared__ int base[kMaxE];
-  __shared__ int cursor[kMaxE];
-  __shared__ int order[kMaxE];
-  __shared__ int crank[kMaxE];  // kDealBalanced: rank of each expert by (count desc, id asc)
-  __shared__ int qof[kMaxE];  // kDealBalanced: queue of each expert (rank = id)
-  __shared__ int dshare[32];  // kDealBalanced: queue loads and per-wave counts
-  __shared__ int ntile[kMaxE];
-  __shared__ int wsum[kMaxE / 64];
+  // (16-byte aligned: wave 0 moves four experts per lane at a time)
+  __shared__ __attribute__((aligned(16))) int cnt[kMaxE];
+  __shared__ __attribute__((aligned(16))) int base[kMaxE];
+  __shared__ __attribute__((aligned(16))) int cursor[kMaxE];
+  __shared__ __attribute__((aligned(16))) int order[kMaxE];  // expert of each rank (the balanced deal: rank = id)
+  __shared__ __attribute__((aligned(16))) int ntile[kMaxE];
   __shared__ int pq[1][kMaxE + 1];            // this queue: load of the ranks before r
   __shared__ uint64_t masks[kWavesP][kMaxE];  // per wave and expert: lanes whose token has it
   __shared__ int wpre[kWavesP][kMaxE];        // first row of (wave, expert) in the chunk
@@ -322,87 +356,76 @@ __global__ __launch_bounds__(kThreads) void k_permute(PermuteArgs a) {
   }
   __syncthreads();
 
-  // --- exclusive scan of the counts (four waves of 64 experts)
-  int c = 0, incl = 0;
-  if (tid < kMaxE) {
-    c = (tid < E) ? cnt[tid] : 0;
-    incl = c;
-    for (int d = 1; d < 64; d <<= 1) {
-      const int o = __shfl_up(incl, d);
-      if (lane >= d) incl += o;
-    }
-    if (lane == 63) wsum[wave] = incl;
-  }
-  __syncthreads();
-  if (tid < kMaxE) {
-    int before = 0;
-    for (int w = 0; w < wave; ++w) before += wsum[w];
-    const int excl = before + incl - c;
-    base[tid] = excl;
-    cursor[tid] = excl;
-    if (tid < E) {
-      if (role == 0) {  // counts and offsets: the first task-list workgroup
-        a.offsets[tid] = excl;
-        a.counts[tid] = c;
-        if (tid == E - 1) a.offsets[E] = excl + c;
+  // --- exclusive scan of the counts, in wave 0 (lane l: experts 4 l .. 4 l + 3)
+  int v[4] = {0, 0, 0, 0};  // wave 0: tile counts of the lane's experts
+  if (wave == 0) {
+    const int4 c4 = *reinterpret_cast<const int4*>(&cnt[4 * lane]);
+    const int c[4] = {c4.x, c4.y, c4.z, c4.w};  // zero for experts >= E
+    const int sum = (c[0] + c[1]) + (c[2] + c[3]);
+    int run = wave_scan<false>(sum) - sum;
+    int b[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int e = 4 * lane + i;
+      b[i] = run;
+      v[i] = (c[i] + a.tile_rows - 1) / a.tile_rows;
+      if (role == 0 && e < E) {  // counts and offsets: the first task-list workgroup
+        a.offsets[e] = run;
+        a.counts[e] = c[i];
+        if (e == E - 1) a.offsets[E] = run + c[i];
       }
-      ntile[tid] = (c + a.tile_rows - 1) / a.tile_rows;
+      run += c[i];
     }
+    *reinterpret_cast<int4*>(&base[4 * lane]) = make_int4(b[0], b[1], b[2], b[3]);
+    *reinterpret_cast<int4*>(&cursor[4 * lane]) = make_int4(b[0], b[1], b[2], b[3]);
+    *reinterpret_cast<int4*>(&ntile[4 * lane]) = make_int4(v[0], v[1], v[2], v[3]);
   }
   if (role == 0 && tid < 2) a.qlen[2 * kQueues + tid] = a.qmax[tid];  // the queue capacities, for inspection
   if (role == 2 * kQueues) {
+    __syncthreads();
     scatter(a, ids, cursor, masks, wpre, stage, staged, tid, lane, wave);
     return;
   }
-  // --- the deal. The unit deal and the deal by expert lay their queues out in
-  // the experts' order by count; the balanced deal lays them out in id order
-  // and deals its larger experts by id, which is fast and almost always within
-  // the queues' capacity. If it is not (the largest queue, in tasks of either
-  // GEMM, over that GEMM's capacity), the larger experts are dealt again in
-  // order of size, which provably fits (the capacity's bound). Both task-list
-  // workgroups of a queue take the same decision.
-  if (a.deal == kDealBalanced) {
-    if (tid < kMaxE) {
-      order[tid] = tid;
-      qof[tid] = 0;
-      crank[tid] = -1;  // no rank by size unless the deal by id is set aside
-    }
-    __syncthreads();
-    deal_balanced(ntile, crank, E, tid, lane, wave, qof, dshare,
-                  [&](int* cr) { rank_experts(cnt, E, tid, [&](int e, int r) { cr[e] = r; }); });
-  } else {
-    rank_experts(cnt, E, tid, [&](int e, int r) { order[r] = e; });
-  }
-  __syncthreads();
-
-  // --- queue x of GEMM g: the load that the units of the experts ranked
-  // before r put into it (one wave, 4 ranks per lane). Expert rank r owns
-  // units r NB .. r NB + NB - 1; unit u goes to queue u % 8 (or, dealing by
-  // expert, all of them to queue r % 8 or qof[r]) and holds ntile tasks.
+  // --- the deal, and queue x of GEMM g: the load that the units of the
+  // experts ranked before r put into it (wave 0, 4 ranks per lane). Expert
+  // rank r owns units r NB .. r NB + NB - 1; unit u goes to queue u % 8 (or,
+  // dealing by expert, all of them to queue r % 8 or, balanced, to the
+  // expert's queue) and holds ntile tasks. The unit deal and the deal by
+  // expert lay their queues out in the experts' order by count; the balanced
+  // deal lays them out in id order.
   const int g = role / kQueues, x = role % kQueues;
   const int NB = a.nb[g];
   int* pre = pq[0];
-  if (wave == 0) {
-    int v[4], run = 0;
+  int w4[4];
+  if (a.deal == kDealBalanced) {
+    if (wave == 0) {
+      int q[4];
+      deal_balanced(v, cnt, E, lane, q);
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int r = 4 * lane + i;
-      const int units = a.deal == kDealUnits     ? n_mod((r + 1) * NB, x) - n_mod(r * NB, x)
-                        : a.deal == kDealExperts ? ((r % kQueues == x) ? NB : 0)
-                                                 : ((r < E && qof[r] == x) ? NB : 0);
-      v[i] = (r < E) ? ntile[order[r]] * units : 0;
-      run += v[i];
+      for (int i = 0; i < 4; ++i) w4[i] = (q[i] == x) ? v[i] * NB : 0;
+      *reinterpret_cast<int4*>(&order[4 * lane]) = make_int4(4 * lane, 4 * lane + 1, 4 * lane + 2, 4 * lane + 3);
     }
-    int incl2 = run;
-    for (int d = 1; d < 64; d <<= 1) {
-      const int o = __shfl_up(incl2, d);
-      if (lane >= d) incl2 += o;
+  } else {
+    __syncthreads();
+    rank_experts(cnt, E, tid, [&](int e, int r) { order[r] = e; });
+    __syncthreads();
+    if (wave == 0) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int r = 4 * lane + i;
+        const int units = a.deal == kDealUnits ? n_mod((r + 1) * NB, x) - n_mod(r * NB, x)
+                                               : ((r % kQueues == x) ? NB : 0);
+        w4[i] = (r < E) ? ntile[order[r]] * units : 0;
+      }
     }
-    int before = incl2 - run;
+  }
+  if (wave == 0) {
+    const int run = (w4[0] + w4[1]) + (w4[2] + w4[3]);
+    int before = wave_scan<false>(run) - run;
     if (lane == 0) pre[0] = 0;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      before += v[i];
+      before += w4[i];
       pre[4 * lane + i + 1] = before;  // load of ranks 0 .. 4 lane + i
     }
   }
