@@ -4,7 +4,7 @@
 // slots are accumulated (fused multiply-add, fp32) in their routing order
 // (logit descending), always in the same order, so the result is
 // bit-reproducible; the output is rounded once (round-to-nearest-even for
-// bf16).
+// bf16). The expert outputs are read once, with the non-temporal hint.
 #include "dg_common.h"
 #include "launch.h"
 
@@ -34,7 +34,10 @@ __global__ __launch_bounds__(kThreads) void k_combine(CombineArgs a) {
     uint2 yv[8];
 #pragma unroll
     for (int j = 0; j < 8; ++j)
-      if (j < K) yv[j] = *reinterpret_cast<const uint2*>(a.y + (size_t)rows[j] * D + c);
+      if (j < K) {
+        const uint64_t v = ld_stream(reinterpret_cast<const uint64_t*>(a.y + (size_t)rows[j] * D + c));
+        yv[j] = make_uint2((uint32_t)v, (uint32_t)(v >> 32));
+      }
     float4 s = make_float4(w[0] * bf16_lo(yv[0].x), w[0] * bf16_hi(yv[0].x), w[0] * bf16_lo(yv[0].y),
                            w[0] * bf16_hi(yv[0].y));
 #pragma unroll
