@@ -44,25 +44,41 @@ inline int bf16_tile_rows(int T, int K, int E) {
 // tasks that workgroups with blockIdx % kQueues == x process.
 constexpr int kQueues = 8;
 
+// The cost of an expert of t tiles and m rows for the balanced deal of wide
+// tiles: each task of a tile streams its weight block whatever its rows, and
+// its rows add about as much again per row as that block costs per
+// kTileCost rows (task timelines of the fused launch at 2304 tokens: a
+// 160-row tile's tasks cost as much as 120 of its rows), so
+// cost = kTileCost t + m.
+constexpr int kTileCost = 128;
+
 // Upper bound on the length of one task queue of a GEMM with NB column blocks
 // for T tokens cut into tiles of at most R rows. The tile count is at most
 // K T / R + E (each expert's ceil(M_e / R) exceeds M_e / R by less than one),
 // and one expert holds at most ceil(T / R) tiles (a token routes to it once).
-// Every deal keeps each queue within twice that of the mean, in tiles:
 //  * round robin over units of non-increasing size (the unit deal, the deal
 //    by expert): within one unit of the mean;
-//  * the balanced deal: the experts with more than the smallest tile count v1
-//    are dealt in snake order of that count, non-increasing, which keeps any
-//    two queues within the largest count of each other; the experts of v1
-//    tiles then fill the least loaded levels, after which a queue that took
-//    some ends below the common level plus 2 v1, and one that took none is
-//    where the snake left it.
+//  * the balanced deal by tiles: the experts with more than the smallest tile
+//    count v1 are dealt in snake order of that count, non-increasing, which
+//    keeps any two queues within the largest count of each other; the
+//    experts of v1 tiles then fill the least loaded levels, after which a
+//    queue that took some ends below the common level plus 2 v1, and one that
+//    took none is where the snake left it: within twice the largest count of
+//    the mean;
+//  * the balanced deal by cost (wide tiles): the experts in snake order of
+//    cost, non-increasing, keep any two queues within the largest cost
+//    c_max <= kTileCost ceil(T / R) + T of each other, so none above the mean
+//    cost (kTileCost tiles + K T) / 8 plus c_max; a queue's tiles are at most
+//    its cost / kTileCost: tiles / 8 + ceil(T / R) + (K T / 8 + T) / kTileCost.
 // The permutation still clamps a queue at this length and raises
 // DG_DEV_QUEUE_OVERFLOW if it ever had to.
 inline int max_queue_len(int T, int K, int E, int NB, int R) {
   const long max_tiles = ((long)K * T + R - 1) / R + E;
-  const long largest_unit = (long)NB * ((T + R - 1) / R);
-  return (int)(((long)NB * max_tiles + kQueues - 1) / kQueues + 2 * largest_unit);
+  const long per_expert = (T + R - 1) / R;
+  const long by_tiles = ((long)NB * max_tiles + kQueues - 1) / kQueues + 2 * NB * per_expert;
+  const long rows_term = ((long)K * T + 8L * T + 8L * kTileCost - 1) / (8L * kTileCost);
+  const long by_cost = (long)NB * ((max_tiles + kQueues - 1) / kQueues + per_expert + rows_term + 1);
+  return (int)(by_tiles > by_cost ? by_tiles : by_cost);
 }
 
 // Column blocks of the two GEMMs: gate_up tasks cover 64 features (their gate
@@ -107,9 +123,10 @@ hipError_t launch_prep_router_w(const void* w, int w_f32, const float* gamma_r, 
 // How the permutation deals the GEMM tasks to the per-XCD queues:
 //  kDealUnits: units (expert, column block) round robin, each GEMM on its own;
 //  kDealExperts: whole experts (all their tiles and blocks), rank r to queue r % 8;
-//  kDealBalanced: whole experts to balance the tile counts of the queues, the
-//    same expert to the same queue in both GEMMs (the fused GEMM needs each
-//    tile's gate_up and down tasks on one XCD).
+//  kDealBalanced: whole experts to balance the queues (their tile counts, or
+//    with wide tiles their cost kTileCost per tile plus the rows), the same
+//    expert to the same queue in both GEMMs (the fused GEMM needs each tile's
+//    gate_up and down tasks on one XCD).
 constexpr int kDealUnits = 0, kDealExperts = 1, kDealBalanced = 2;
 
 struct PermuteArgs {

@@ -19,8 +19,9 @@
 //    column blocks of rank r go to queue r % 8): an expert's tiles then share
 //    its activation rows, hundreds of them, in one L2. For the fused GEMM
 //    whole experts are dealt so that the queues' tile counts balance (the
-//    larger experts in snake order, the rest level by level in id order), the same
-//    expert to the same queue in both task lists, each queue laid out in
+//    larger experts in snake order, the rest level by level in id order), or
+//    with wide tiles their costs (all experts in snake order of cost), the
+//    same expert to the same queue in both task lists, each queue laid out in
 //    expert id order, and the per-tile counters of that GEMM are zeroed;
 //  * the stable scatter: the rows of expert e hold its slots in increasing
 //    token order; sorted_slot[row] = t k + j (token t, slot j) and
@@ -232,8 +233,8 @@ __device__ void deal_balanced(const int (&v)[4], const int* cnt, int E, int lane
   }
 }
 
-// Rank of each expert by (count desc, id asc), four lanes per expert: lane q
-// reads the counts 16 i + 4 q .. + 3 (consecutive lanes, consecutive banks)
+// Rank of each expert by (key desc, id asc), four lanes per expert: lane q
+// reads the keys 16 i + 4 q .. + 3 (consecutive lanes, consecutive banks)
 // and compares against them. Calls rank_out(e, r) for e < E.
 template <typename Out>
 __device__ __forceinline__ void rank_experts(const int* cnt, int E, int tid, Out rank_out) {
@@ -325,6 +326,8 @@ __global__ __launch_bounds__(kThreads) void k_permute(PermuteArgs a) {
   __shared__ __attribute__((aligned(16))) int cursor[kMaxE];
   __shared__ __attribute__((aligned(16))) int order[kMaxE];  // expert of each rank (the balanced deal: rank = id)
   __shared__ __attribute__((aligned(16))) int ntile[kMaxE];
+  __shared__ __attribute__((aligned(16))) int dcost[kMaxE];  // wide tiles: the deal's cost of each expert
+  __shared__ __attribute__((aligned(16))) int qof[kMaxE];    // wide tiles: the queue of each expert
   __shared__ int pq[1][kMaxE + 1];            // this queue: load of the ranks before r
   __shared__ uint64_t masks[kWavesP][kMaxE];  // per wave and expert: lanes whose token has it
   __shared__ int wpre[kWavesP][kMaxE];        // first row of (wave, expert) in the chunk
@@ -379,6 +382,12 @@ __global__ __launch_bounds__(kThreads) void k_permute(PermuteArgs a) {
     *reinterpret_cast<int4*>(&base[4 * lane]) = make_int4(b[0], b[1], b[2], b[3]);
     *reinterpret_cast<int4*>(&cursor[4 * lane]) = make_int4(b[0], b[1], b[2], b[3]);
     *reinterpret_cast<int4*>(&ntile[4 * lane]) = make_int4(v[0], v[1], v[2], v[3]);
+    if (a.deal == kDealBalanced && a.tile_rows == kWideRows) {
+      int k4[4];  // the cost of each expert for the deal of wide tiles (0 without rows)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) k4[i] = v[i] > 0 ? kTileCost * v[i] + c[i] : 0;
+      *reinterpret_cast<int4*>(&dcost[4 * lane]) = make_int4(k4[0], k4[1], k4[2], k4[3]);
+    }
   }
   if (role == 0 && tid < 2) a.qlen[2 * kQueues + tid] = a.qmax[tid];  // the queue capacities, for inspection
   if (role == 2 * kQueues) {
@@ -397,7 +406,8 @@ __global__ __launch_bounds__(kThreads) void k_permute(PermuteArgs a) {
   const int NB = a.nb[g];
   int* pre = pq[0];
   int w4[4];
-  if (a.deal == kDealBalanced) {
+  const bool wide = a.deal == kDealBalanced && a.tile_rows == kWideRows;
+  if (a.deal == kDealBalanced && !wide) {
     if (wave == 0) {
       int q[4];
       deal_balanced(v, cnt, E, lane, q);
@@ -406,16 +416,36 @@ __global__ __launch_bounds__(kThreads) void k_permute(PermuteArgs a) {
       *reinterpret_cast<int4*>(&order[4 * lane]) = make_int4(4 * lane, 4 * lane + 1, 4 * lane + 2, 4 * lane + 3);
     }
   } else {
+    // Experts ranked by count (the unit deal, the deal by expert: their queue
+    // order), or with wide tiles by cost, dealt in snake order of that rank
+    // (descending, ties to the lower id). A wide tile's tasks take about
+    // kTileCost rows' time plus their rows, so balancing the tile counts
+    // alone left the queues up to one tile and its rows apart (2304 tokens:
+    // 140 tiles over 8 queues, the last ended 35 us after the first; by cost
+    // the launch takes 343 against 353 us).
     __syncthreads();
-    rank_experts(cnt, E, tid, [&](int e, int r) { order[r] = e; });
+    rank_experts(wide ? dcost : cnt, E, tid, [&](int e, int r) {
+      if (wide)
+        qof[e] = snake(r);
+      else
+        order[r] = e;
+    });
     __syncthreads();
     if (wave == 0) {
+      if (wide) {
+        const int4 q4 = *reinterpret_cast<const int4*>(&qof[4 * lane]);
+        const int q[4] = {q4.x, q4.y, q4.z, q4.w};
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int r = 4 * lane + i;
-        const int units = a.deal == kDealUnits ? n_mod((r + 1) * NB, x) - n_mod(r * NB, x)
-                                               : ((r % kQueues == x) ? NB : 0);
-        w4[i] = (r < E) ? ntile[order[r]] * units : 0;
+        for (int i = 0; i < 4; ++i) w4[i] = (v[i] > 0 && q[i] == x) ? v[i] * NB : 0;
+        *reinterpret_cast<int4*>(&order[4 * lane]) = make_int4(4 * lane, 4 * lane + 1, 4 * lane + 2, 4 * lane + 3);
+      } else {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int r = 4 * lane + i;
+          const int units = a.deal == kDealUnits ? n_mod((r + 1) * NB, x) - n_mod(r * NB, x)
+                                                 : ((r % kQueues == x) ? NB : 0);
+          w4[i] = (r < E) ? ntile[order[r]] * units : 0;
+        }
       }
     }
   }

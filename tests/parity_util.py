@@ -83,6 +83,24 @@ def snake(h):
     return 7 - h % 8 if (h // 8) % 2 else h % 8
 
 
+TILE_COST = 128  # the cost of a tile, in rows, for the deal of wide tiles
+WIDE_ROWS = 160   # the height of wide tiles
+
+
+def cost_snake_deal(ntile, counts):
+    """The balanced deal of wide tiles: each expert with rows costs TILE_COST per tile plus its rows; the experts
+    in order of cost (descending, ties to the lower id) go to the queues in snake order (0..7, then 7..0, ...).
+    Returns a list (None for experts without rows)."""
+    E = len(ntile)
+    cost = [TILE_COST * int(ntile[e]) + int(counts[e]) if ntile[e] > 0 else 0 for e in range(E)]
+    order = sorted(range(E), key=lambda e: (-cost[e], e))
+    qof = [None] * E
+    for r, e in enumerate(order):
+        if ntile[e] > 0:
+            qof[e] = snake(r)
+    return qof
+
+
 def balanced_deal(ntile, counts):
     """The queue of every expert under the permutation's balanced deal of whole experts, from the tile counts
     (ntile) and token counts of the experts, written out step by step as the deal is specified: the experts
@@ -126,7 +144,8 @@ def balanced_deal(ntile, counts):
 def check_device_state(dbg, K, E, T, D, F, balanced=None):
     """The handle's sticky device status word is clear, and the per-XCD task queues hold their tasks within the
     capacity and within the balance the deal guarantees: no queue more than 2 tiles of the largest expert above
-    an even share of all tiles (per column block of each GEMM)."""
+    an even share of all tiles (per column block of each GEMM), or, for the deal of wide tiles by cost, exactly
+    the model's queues. balanced: the fused launch's balanced deal (its queues are compared with the model)."""
     flags = int(dbg["dev_flags"].cpu().numpy()[0])
     assert flags == 0, f"device status word 0x{flags:x}"
     ql = dbg["queue_len"].cpu().numpy()
@@ -143,12 +162,13 @@ def check_device_state(dbg, K, E, T, D, F, balanced=None):
     a_max = int((counts.max() + R - 1) // R)
     for g, nb in enumerate(nbs):
         assert np.all(lens[g] <= caps[g]), f"GEMM {g}: queue lengths {lens[g]} over capacity {caps[g]}"
-        bound = nb * (-(-tiles // 8) + 2 * a_max)
-        assert lens[g].max() <= bound, f"GEMM {g}: queue {lens[g].max()} > balance bound {bound} ({lens[g]})"
+        if not (balanced and R == WIDE_ROWS):
+            bound = nb * (-(-tiles // 8) + 2 * a_max)
+            assert lens[g].max() <= bound, f"GEMM {g}: queue {lens[g].max()} > balance bound {bound} ({lens[g]})"
     if balanced:
-        # every queue holds exactly the tiles the balanced deal gives it
+        # every queue holds exactly the tiles the balanced deal gives it (by cost for wide tiles)
         ntile = (counts + R - 1) // R
-        qof = balanced_deal(ntile, counts)
+        qof = cost_snake_deal(ntile, counts) if R == WIDE_ROWS else balanced_deal(ntile, counts)
         want = np.zeros(8, dtype=np.int64)
         for e in range(E):
             if qof[e] is not None:

@@ -1,11 +1,13 @@
-"""The balanced deal of whole experts to the 8 per-XCD task queues, on the CPU: its balance guarantee (no queue
-more than twice the largest expert's tile count above an even share of all tiles), which sizes the queues'
-capacity, over random, skewed and adversarial loads. The GPU tests check that the permutation kernel deals
-exactly as this model does (tests/parity_util.py, check_device_state)."""
+"""The balanced deals of whole experts to the 8 per-XCD task queues, on the CPU: their balance guarantees, which
+size the queues' capacity, over random, skewed and adversarial loads. By tiles: no queue more than twice the
+largest expert's tile count above an even share of all tiles. By cost (wide tiles; TILE_COST per tile plus the
+rows): no two queues more than the costliest expert apart, so no queue's tiles above the capacity's cost term.
+The GPU tests check that the permutation kernel deals exactly as these models do (tests/parity_util.py,
+check_device_state)."""
 import numpy as np
 import pytest
 
-from parity_util import balanced_deal, snake
+from parity_util import TILE_COST, balanced_deal, cost_snake_deal, snake
 
 
 def queue_tiles(ntile, qof):
@@ -72,3 +74,61 @@ def test_bound_adversarial(T):
                 counts[others[i % n_use]] += 1
             for R in (64, 128, 160):
                 check_bound(counts, R)
+
+
+def capacity_tiles(T, K, E, R):
+    """The library's queue capacity (launch.h max_queue_len) for one column block, in tiles."""
+    max_tiles = -(-(K * T) // R) + E
+    per_expert = -(-T // R)
+    by_tiles = -(-max_tiles // 8) + 2 * per_expert
+    by_cost = -(-max_tiles // 8) + per_expert + -(-(K * T + 8 * T) // (8 * TILE_COST)) + 1
+    return max(by_tiles, by_cost)
+
+
+def check_cost_bound(counts, T, K, R=160):
+    counts = np.asarray(counts, dtype=np.int64)
+    ntile = (counts + R - 1) // R
+    qof = cost_snake_deal(ntile, counts)
+    cost = np.where(ntile > 0, TILE_COST * ntile + counts, 0)
+    load = np.zeros(8, dtype=np.int64)
+    for e, x in enumerate(qof):
+        if x is not None:
+            load[x] += cost[e]
+    assert load.sum() == cost.sum()
+    assert load.max() - load.min() <= cost.max(), (load, cost.max())
+    q = queue_tiles(ntile, qof)
+    assert q.sum() == ntile.sum()
+    assert q.max() <= capacity_tiles(T, K, len(counts), R), (q.max(), capacity_tiles(T, K, len(counts), R))
+    return load
+
+
+def test_cost_deal_by_hand():
+    # costs 128 t + rows: 456, then 138 x 9; snake: ranks 0..7 to queues 0..7, ranks 8, 9 to queues 7, 6
+    assert cost_snake_deal([2] + [1] * 9, [200] + [10] * 9) == [0, 1, 2, 3, 4, 5, 6, 7, 7, 6]
+
+
+@pytest.mark.parametrize("seed", range(20))
+def test_cost_bound_random(seed):
+    rng = np.random.default_rng(100 + seed)
+    E, K = 128, 8
+    T = int(rng.choice([1536, 2304, 4096, 8192, 65536]))
+    p = rng.dirichlet(np.ones(E) * rng.uniform(0.3, 30))
+    counts = np.bincount(rng.choice(E, size=T * K, p=p), minlength=E)
+    check_cost_bound(counts, T, K)
+
+
+@pytest.mark.parametrize("T", [2304, 8192, 65536])
+def test_cost_bound_adversarial(T):
+    E, K = 128, 8
+    for big in ([0, 15, 16, 31, 32], [0, 1, 2, 3, 4, 5, 6, 7]):
+        counts = np.zeros(E, dtype=np.int64)
+        counts[big] = T
+        rest = [e for e in range(E) if e not in big]
+        for i in range((K - len(big)) * T):
+            counts[rest[i % len(rest)]] += 1
+        check_cost_bound(counts, T, K)
+    # one row each for all but one expert
+    counts = np.ones(E, dtype=np.int64)
+    counts[0] = K * T - (E - 1)
+    counts[0] = min(counts[0], T)
+    check_cost_bound(counts, T, K)
