@@ -489,6 +489,7 @@ static dg_status run_forward(dg_moe_handle hd, const void* x, void* out, int32_t
     fa.tile_done = pa.tile_done;
     fa.nb_gate_up = pa.nb[0];
     fa.dev_flags = ra.dev_flags;
+    fa.counts = pa.counts;
     e = mx4  ? dg::launch_gemm_fused_mx4(fa, stream, ev(3))
         : mx8 ? dg::launch_gemm_fused_mx8(fa, stream, ev(3))
         : q8 ? dg::launch_gemm_fused_q8(fa, stream, ev(3))

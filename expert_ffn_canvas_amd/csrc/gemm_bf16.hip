@@ -53,12 +53,17 @@ struct Panels {
 };
 
 // Weight panels of one K step: NS sub-steps of 32.
-template <bool PK, int NS>
+template <bool PK, int NS, bool NT = true>
 __device__ __forceinline__ void load_w(const uint16_t* w0, const uint16_t* w1, int k0, Panels& p) {
 #pragma unroll
   for (int s = 0; s < NS; ++s) {
-    p.b0[s] = ld_stream(reinterpret_cast<const u32x4*>(w0 + (size_t)((k0 + 32 * s) >> 5) * p.wstep));
-    p.b1[s] = ld_stream(reinterpret_cast<const u32x4*>(w1 + (size_t)((k0 + 32 * s) >> 5) * p.wstep));
+    if constexpr (NT) {
+      p.b0[s] = ld_stream(reinterpret_cast<const u32x4*>(w0 + (size_t)((k0 + 32 * s) >> 5) * p.wstep));
+      p.b1[s] = ld_stream(reinterpret_cast<const u32x4*>(w1 + (size_t)((k0 + 32 * s) >> 5) * p.wstep));
+    } else {
+      p.b0[s] = *reinterpret_cast<const u32x4*>(w0 + (size_t)((k0 + 32 * s) >> 5) * p.wstep);
+      p.b1[s] = *reinterpret_cast<const u32x4*>(w1 + (size_t)((k0 + 32 * s) >> 5) * p.wstep);
+    }
   }
 }
 
@@ -87,14 +92,14 @@ __device__ __forceinline__ void mma_step(const char* stage, int lane, const Pane
 // One step with NS sub-steps, issued after the previous one: DMA of the
 // activation rows into stage (it + 1) & 1, then the weight panels into `nxt`,
 // then the MFMAs of step `it` (NSP sub-steps) from `cur`.
-template <bool PK, int NMT, int NS, int NSP, int ROWS, int WV>
+template <bool PK, int NMT, int NS, int NSP, int ROWS, int WV, bool NT>
 __device__ __forceinline__ void step(char* As, const uint16_t* const (&rowp)[dma_per_wave(ROWS, WV)], const uint16_t* w0,
                                      const uint16_t* w1, int k1, int it, int wave, int lane, const Panels& cur,
                                      Panels& nxt, f32x4 (&acc0)[ROWS / 16], f32x4 (&acc1)[ROWS / 16]) {
   constexpr int kSB = ROWS * kRowBytes;
   dma_a<NMT, NS * 4, dma_per_wave(ROWS, WV), WV>(As + ((it + 1) & 1) * kSB, rowp, k1, wave, lane);
   __builtin_amdgcn_sched_barrier(0);
-  load_w<PK, NS>(w0, w1, k1, nxt);
+  load_w<PK, NS, NT>(w0, w1, k1, nxt);
   __builtin_amdgcn_sched_barrier(0);
   mma_step<NMT, NSP>(As + (it & 1) * kSB, lane, cur, acc0, acc1);
   wait_vmcnt<2 * NS>();  // this wave's DMA has landed; its weight loads may still fly
@@ -102,7 +107,7 @@ __device__ __forceinline__ void step(char* As, const uint16_t* const (&rowp)[dma
 }
 
 // The last full step `last` (panels in `cur`) and the short tail, if any.
-template <bool PK, int NMT, int ROWS, int WV>
+template <bool PK, int NMT, int ROWS, int WV, bool NT>
 __device__ __forceinline__ void finish(char* As, const uint16_t* const (&rowp)[dma_per_wave(ROWS, WV)], const uint16_t* w0,
                                        const uint16_t* w1, int nfull, int ntail, int wave, int lane,
                                        const Panels& cur, Panels& nxt, f32x4 (&acc0)[ROWS / 16],
@@ -114,7 +119,7 @@ __device__ __forceinline__ void finish(char* As, const uint16_t* const (&rowp)[d
   if (ntail == 0) {
     mma_step<NMT, kNS>(As + (last & 1) * kSB, lane, cur, acc0, acc1);
   } else {  // one 64-wide step remains (K % 128 == 64)
-    step<PK, NMT, 2, kNS, ROWS, WV>(As, rowp, w0, w1, k1, last, wave, lane, cur, nxt, acc0, acc1);
+    step<PK, NMT, 2, kNS, ROWS, WV, NT>(As, rowp, w0, w1, k1, last, wave, lane, cur, nxt, acc0, acc1);
     wait_vmcnt<0>();
     mma_step<NMT, 2>(tail_stage, lane, nxt, acc0, acc1);
   }
@@ -123,7 +128,7 @@ __device__ __forceinline__ void finish(char* As, const uint16_t* const (&rowp)[d
 // The K loop of one tile with NMT 16-row MFMA tiles. K is a multiple of 64.
 // Two panel buffers alternate roles (the loop is unrolled by two) so that no
 // register copies are needed between steps.
-template <bool PK, int NMT, int ROWS, int WV>
+template <bool PK, int NMT, int ROWS, int WV, bool NT>
 __device__ __forceinline__ void k_loop(char* As, const uint16_t* const (&rowp)[dma_per_wave(ROWS, WV)], const uint16_t* w0,
                                        const uint16_t* w1, int K, int tid, f32x4 (&acc0)[ROWS / 16],
                                        f32x4 (&acc1)[ROWS / 16], int wstep) {
@@ -136,7 +141,7 @@ __device__ __forceinline__ void k_loop(char* As, const uint16_t* const (&rowp)[d
   if (nfull == 0) {
     // K = 64: one short step only
     dma_a<NMT, 8, dma_per_wave(ROWS, WV), WV>(As, rowp, 0, wave, lane);
-    load_w<PK, 2>(w0, w1, 0, p0);
+    load_w<PK, 2, NT>(w0, w1, 0, p0);
     wait_vmcnt<0>();
     lds_barrier();
     mma_step<NMT, 2>(As, lane, p0, acc0, acc1);
@@ -144,19 +149,19 @@ __device__ __forceinline__ void k_loop(char* As, const uint16_t* const (&rowp)[d
   }
   dma_a<NMT, kSegs, dma_per_wave(ROWS, WV), WV>(As, rowp, 0, wave, lane);
   __builtin_amdgcn_sched_barrier(0);
-  load_w<PK, kNS>(w0, w1, 0, p0);
+  load_w<PK, kNS, NT>(w0, w1, 0, p0);
   wait_vmcnt<2 * kNS>();
   lds_barrier();
   int it = 0;
   for (; it + 2 < nfull; it += 2) {
-    step<PK, NMT, kNS, kNS, ROWS, WV>(As, rowp, w0, w1, (it + 1) * kKS, it, wave, lane, p0, p1, acc0, acc1);
-    step<PK, NMT, kNS, kNS, ROWS, WV>(As, rowp, w0, w1, (it + 2) * kKS, it + 1, wave, lane, p1, p0, acc0, acc1);
+    step<PK, NMT, kNS, kNS, ROWS, WV, NT>(As, rowp, w0, w1, (it + 1) * kKS, it, wave, lane, p0, p1, acc0, acc1);
+    step<PK, NMT, kNS, kNS, ROWS, WV, NT>(As, rowp, w0, w1, (it + 2) * kKS, it + 1, wave, lane, p1, p0, acc0, acc1);
   }
   if (it + 2 == nfull) {
-    step<PK, NMT, kNS, kNS, ROWS, WV>(As, rowp, w0, w1, (it + 1) * kKS, it, wave, lane, p0, p1, acc0, acc1);
-    finish<PK, NMT, ROWS, WV>(As, rowp, w0, w1, nfull, ntail, wave, lane, p1, p0, acc0, acc1);
+    step<PK, NMT, kNS, kNS, ROWS, WV, NT>(As, rowp, w0, w1, (it + 1) * kKS, it, wave, lane, p0, p1, acc0, acc1);
+    finish<PK, NMT, ROWS, WV, NT>(As, rowp, w0, w1, nfull, ntail, wave, lane, p1, p0, acc0, acc1);
   } else {
-    finish<PK, NMT, ROWS, WV>(As, rowp, w0, w1, nfull, ntail, wave, lane, p0, p1, acc0, acc1);
+    finish<PK, NMT, ROWS, WV, NT>(As, rowp, w0, w1, nfull, ntail, wave, lane, p0, p1, acc0, acc1);
   }
 }
 
@@ -166,7 +171,7 @@ __device__ __forceinline__ void k_loop(char* As, const uint16_t* const (&rowp)[d
 // ROWS activation rows. A wave whose panels lie past the last column block's
 // end (F or D not a multiple of the block) streams the block's last panels
 // again (cache hits) and stores nothing.
-template <bool GATE_UP, bool PK, int ROWS, int WV = kWaves>
+template <bool GATE_UP, bool PK, int ROWS, int WV = kWaves, bool NT = true>
 __device__ __forceinline__ void gemm_body(const GemmArgs& a, const Tile& tl, char* As, float* rrow) {
   constexpr int kBM = ROWS / 16;  // 16-row MFMA tiles, and activation transfers per wave per step
   const int F = a.F, D = a.D;
@@ -231,31 +236,31 @@ __device__ __forceinline__ void gemm_body(const GemmArgs& a, const Tile& tl, cha
   }
   if constexpr (ROWS == 64) {
     switch (nmt) {
-      case 1: k_loop<PK, 1, ROWS, WV>(As, rowp, w0, w1, K, tid, acc0, acc1, wstep); break;
-      case 2: k_loop<PK, 2, ROWS, WV>(As, rowp, w0, w1, K, tid, acc0, acc1, wstep); break;
-      case 3: k_loop<PK, 3, ROWS, WV>(As, rowp, w0, w1, K, tid, acc0, acc1, wstep); break;
-      default: k_loop<PK, 4, ROWS, WV>(As, rowp, w0, w1, K, tid, acc0, acc1, wstep); break;
+      case 1: k_loop<PK, 1, ROWS, WV, NT>(As, rowp, w0, w1, K, tid, acc0, acc1, wstep); break;
+      case 2: k_loop<PK, 2, ROWS, WV, NT>(As, rowp, w0, w1, K, tid, acc0, acc1, wstep); break;
+      case 3: k_loop<PK, 3, ROWS, WV, NT>(As, rowp, w0, w1, K, tid, acc0, acc1, wstep); break;
+      default: k_loop<PK, 4, ROWS, WV, NT>(As, rowp, w0, w1, K, tid, acc0, acc1, wstep); break;
     }
   } else if constexpr (ROWS == 128) {
     switch (nmt) {
-      case 1: k_loop<PK, 1, ROWS, WV>(As, rowp, w0, w1, K, tid, acc0, acc1, wstep); break;
-      case 2: k_loop<PK, 2, ROWS, WV>(As, rowp, w0, w1, K, tid, acc0, acc1, wstep); break;
-      case 3: k_loop<PK, 3, ROWS, WV>(As, rowp, w0, w1, K, tid, acc0, acc1, wstep); break;
-      case 4: k_loop<PK, 4, ROWS, WV>(As, rowp, w0, w1, K, tid, acc0, acc1, wstep); break;
-      case 5: k_loop<PK, 5, ROWS, WV>(As, rowp, w0, w1, K, tid, acc0, acc1, wstep); break;
-      case 6: k_loop<PK, 6, ROWS, WV>(As, rowp, w0, w1, K, tid, acc0, acc1, wstep); break;
-      case 7: k_loop<PK, 7, ROWS, WV>(As, rowp, w0, w1, K, tid, acc0, acc1, wstep); break;
-      default: k_loop<PK, 8, ROWS, WV>(As, rowp, w0, w1, K, tid, acc0, acc1, wstep); break;
+      case 1: k_loop<PK, 1, ROWS, WV, NT>(As, rowp, w0, w1, K, tid, acc0, acc1, wstep); break;
+      case 2: k_loop<PK, 2, ROWS, WV, NT>(As, rowp, w0, w1, K, tid, acc0, acc1, wstep); break;
+      case 3: k_loop<PK, 3, ROWS, WV, NT>(As, rowp, w0, w1, K, tid, acc0, acc1, wstep); break;
+      case 4: k_loop<PK, 4, ROWS, WV, NT>(As, rowp, w0, w1, K, tid, acc0, acc1, wstep); break;
+      case 5: k_loop<PK, 5, ROWS, WV, NT>(As, rowp, w0, w1, K, tid, acc0, acc1, wstep); break;
+      case 6: k_loop<PK, 6, ROWS, WV, NT>(As, rowp, w0, w1, K, tid, acc0, acc1, wstep); break;
+      case 7: k_loop<PK, 7, ROWS, WV, NT>(As, rowp, w0, w1, K, tid, acc0, acc1, wstep); break;
+      default: k_loop<PK, 8, ROWS, WV, NT>(As, rowp, w0, w1, K, tid, acc0, acc1, wstep); break;
     }
   } else {
     switch (nmt) {  // wide tiles: up to 80 rows run as 5 MFMA tiles
       case 1: case 2: case 3: case 4: case 5:
-        k_loop<PK, 5, ROWS, WV>(As, rowp, w0, w1, K, tid, acc0, acc1, wstep); break;
-      case 6: k_loop<PK, 6, ROWS, WV>(As, rowp, w0, w1, K, tid, acc0, acc1, wstep); break;
-      case 7: k_loop<PK, 7, ROWS, WV>(As, rowp, w0, w1, K, tid, acc0, acc1, wstep); break;
-      case 8: k_loop<PK, 8, ROWS, WV>(As, rowp, w0, w1, K, tid, acc0, acc1, wstep); break;
-      case 9: k_loop<PK, 9, ROWS, WV>(As, rowp, w0, w1, K, tid, acc0, acc1, wstep); break;
-      default: k_loop<PK, 10, ROWS, WV>(As, rowp, w0, w1, K, tid, acc0, acc1, wstep); break;
+        k_loop<PK, 5, ROWS, WV, NT>(As, rowp, w0, w1, K, tid, acc0, acc1, wstep); break;
+      case 6: k_loop<PK, 6, ROWS, WV, NT>(As, rowp, w0, w1, K, tid, acc0, acc1, wstep); break;
+      case 7: k_loop<PK, 7, ROWS, WV, NT>(As, rowp, w0, w1, K, tid, acc0, acc1, wstep); break;
+      case 8: k_loop<PK, 8, ROWS, WV, NT>(As, rowp, w0, w1, K, tid, acc0, acc1, wstep); break;
+      case 9: k_loop<PK, 9, ROWS, WV, NT>(As, rowp, w0, w1, K, tid, acc0, acc1, wstep); break;
+      default: k_loop<PK, 10, ROWS, WV, NT>(As, rowp, w0, w1, K, tid, acc0, acc1, wstep); break;
     }
   }
 
@@ -284,14 +289,31 @@ __device__ __forceinline__ void gemm_body(const GemmArgs& a, const Tile& tl, cha
 // Both GEMMs in one launch (the task logic of fused_tasks). Three workgroups
 // per CU (waves_per_eu 3): the register budget that keeps two K steps of
 // weight panels per wave in flight without spilling.
+// One task of a fused launch. Expert weights are read once per launch and
+// stream past the caches (ld_stream), except those of an expert cut into
+// several tiles: each of its tiles reads the same weight blocks, close together
+// in time (the tiles of one column block are neighbours in the queue), so they
+// are loaded normally and the later tiles find them in L2 (30 stacked layers
+// at 512 tokens, where the Zipf-loaded experts hold up to 8 tiles: 8.26 ->
+// 7.53 ms per stack; canvas256 170.1 -> 167.8 us and encode 347 -> 341 us for
+// the fused launch).
+template <bool GATE_UP, bool PK, int ROWS, int WV = kWaves>
+__device__ __forceinline__ void task_body(const FusedGemmArgs& f, const GemmArgs& a, const Tile& tl, char* As,
+                                          float* rrow) {
+  if ((f.counts[tl.e] + ROWS - 1) / ROWS > 1)
+    gemm_body<GATE_UP, PK, ROWS, WV, false>(a, tl, As, rrow);
+  else
+    gemm_body<GATE_UP, PK, ROWS, WV, true>(a, tl, As, rrow);
+}
+
 template <bool PK>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3, 3))) void k_gemm_fused(
     FusedGemmArgs f) {
   __shared__ __attribute__((aligned(16))) char As[2 * kTileRows * kRowBytes];
   __shared__ float rrow[kTileRows];  // gate_up: r of each row's token, or 1
   fused_tasks(
-      f, [&](const Tile& tl) { gemm_body<true, PK, kTileRows>(f.gu, tl, As, rrow); },
-      [&](const Tile& tl) { gemm_body<false, PK, kTileRows>(f.dn, tl, As, rrow); });
+      f, [&](const Tile& tl) { task_body<true, PK, kTileRows>(f, f.gu, tl, As, rrow); },
+      [&](const Tile& tl) { task_body<false, PK, kTileRows>(f, f.dn, tl, As, rrow); });
 }
 
 // 128-row tiles: twice the accumulators and 64 KB of activation stages, two
@@ -302,8 +324,8 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
   __shared__ __attribute__((aligned(16))) char As[2 * kTallRows * kRowBytes];
   __shared__ float rrow[kTallRows];
   fused_tasks(
-      f, [&](const Tile& tl) { gemm_body<true, PK, kTallRows>(f.gu, tl, As, rrow); },
-      [&](const Tile& tl) { gemm_body<false, PK, kTallRows>(f.dn, tl, As, rrow); });
+      f, [&](const Tile& tl) { task_body<true, PK, kTallRows>(f, f.gu, tl, As, rrow); },
+      [&](const Tile& tl) { task_body<false, PK, kTallRows>(f, f.dn, tl, As, rrow); });
 }
 
 // Wide tiles of up to 160 rows (every row an expert receives at the 2304-token
@@ -316,8 +338,8 @@ __global__ __launch_bounds__(64 * kWideWaves) __attribute__((amdgpu_waves_per_eu
   __shared__ __attribute__((aligned(16))) char As[2 * kWideRows * kRowBytes];
   __shared__ float rrow[kWideRows];
   fused_tasks<kWideWaves>(
-      f, [&](const Tile& tl) { gemm_body<true, PK, kWideRows, kWideWaves>(f.gu, tl, As, rrow); },
-      [&](const Tile& tl) { gemm_body<false, PK, kWideRows, kWideWaves>(f.dn, tl, As, rrow); });
+      f, [&](const Tile& tl) { task_body<true, PK, kWideRows, kWideWaves>(f, f.gu, tl, As, rrow); },
+      [&](const Tile& tl) { task_body<false, PK, kWideRows, kWideWaves>(f, f.dn, tl, As, rrow); });
 }
 
 // One wave per block of 64 lanes x 16 bytes: source block (e, p, s) of 16 rows

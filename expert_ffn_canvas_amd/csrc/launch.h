@@ -186,6 +186,7 @@ struct FusedGemmArgs {
                        // XCD x those that ran there in bits 8 + 7 x ..
   int nb_gate_up;      // gate_up column blocks per tile
   uint32_t* dev_flags; // sticky device status word (DG_DEV_* bits of dg_moe.h)
+  const int32_t* counts; // [E] rows of each expert (its tile count: whether its weights are shared by tiles)
 };
 hipError_t launch_gemm_fused(const FusedGemmArgs& f, int tile_rows, hipStream_t stream, const KernelEvents* ev);
 // Create-time relayout of int4-g128 expert weights (codes [E][R][K/2], scales
