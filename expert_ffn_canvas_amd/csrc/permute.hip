@@ -1,8 +1,9 @@
-// Token -> expert permutation on gfx950, in 17 workgroups of 1024 threads on
-// 17 CUs at once. Each builds the histogram and the scan; then workgroup
-// g 8 + x (g = 0 for gate_up, 1 for down) ranks the experts, deals them and
-// writes task queue x of GEMM g (workgroup 0 also counts and offsets), and
-// workgroup 16 does the stable scatter. The outputs:
+// Token -> expert permutation on gfx950, in 17 to 24 workgroups of 1024
+// threads on as many CUs at once. Each builds the histogram and the scan;
+// then workgroup g 8 + x (g = 0 for gate_up, 1 for down) ranks the experts,
+// deals them and writes task queue x of GEMM g (workgroup 0 also counts and
+// offsets), and workgroups 16 .. do the stable scatter, each for a range of
+// tokens (one per 1024 tokens, at most 8). The outputs:
 //  * counts[e]: tokens routed to expert e (their sum is k T);
 //  * offsets: exclusive prefix sum of counts (the rows of expert e are
 //    offsets[e] .. offsets[e+1]-1 in expert-sorted order);
@@ -257,20 +258,34 @@ __device__ __forceinline__ void rank_experts(const int* cnt, int E, int tid, Out
   if (q == 0 && e < E) rank_out(e, r);
 }
 
-// The stable scatter, kThreads tokens at a time: lane masks per (wave,
-// expert) give each slot its rank among the chunk's earlier tokens.
-__device__ __forceinline__ void scatter(const PermuteArgs& a, int (&ids)[8], int* cursor,
+// Workgroups that share the stable scatter: the chunks of kThreads tokens are
+// split into this many contiguous ranges (at most kMaxScatter), one per
+// workgroup, each starting from the rows the earlier tokens take.
+constexpr int kMaxScatter = 8;
+__host__ __device__ inline int scatter_groups(int T) {
+  const int chunks = (T + kThreads - 1) / kThreads;
+  return chunks < kMaxScatter ? (chunks > 0 ? chunks : 1) : kMaxScatter;
+}
+
+// The stable scatter of tokens [t0, t1), kThreads at a time: lane masks per
+// (wave, expert) give each slot its rank among the chunk's earlier tokens;
+// cursor[e] starts at the first row of expert e these tokens take (cstart).
+// With `staged`, the slots go to LDS compactly, expert e's run at soff[e],
+// each with its expert in the top bits (slot < K T <= 2^23, expert < 256),
+// and are written out in order at the end.
+__device__ __forceinline__ void scatter(const PermuteArgs& a, int (&ids)[8], int t0, int t1, int* cursor,
+                                        const int* cstart, const int* soff, int n_mine,
                                         uint64_t (*masks)[kMaxE], int (*wpre)[kMaxE], int* stage, bool staged,
                                         int tid, int lane, int wave) {
-  const int E = a.E, K = a.K, T = a.T;
+  const int E = a.E, K = a.K;
   const uint64_t below = (1ull << lane) - 1ull;
-  for (int c0 = 0; c0 < T; c0 += kThreads) {
+  for (int c0 = t0; c0 < t1; c0 += kThreads) {
     const int t = c0 + tid;
-    if (c0 > 0 && t < T) load_ids(a.topk_idx, t, K, ids);
+    if (c0 > 0 && t < t1) load_ids(a.topk_idx, t, K, ids);
     for (int i = lane; i < E; i += 64) masks[wave][i] = 0ull;
     __builtin_amdgcn_wave_barrier();
     __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
-    if (t < T) {
+    if (t < t1) {
 #pragma unroll
       for (int j = 0; j < 8; ++j)
         if (j < K) atomicOr(reinterpret_cast<unsigned long long*>(&masks[wave][ids[j]]), 1ull << lane);
@@ -286,7 +301,7 @@ __device__ __forceinline__ void scatter(const PermuteArgs& a, int (&ids)[8], int
       cursor[tid] = run;
     }
     __syncthreads();
-    if (t < T) {
+    if (t < t1) {
       int rows[8];
 #pragma unroll
       for (int j = 0; j < 8; ++j) {
@@ -295,7 +310,7 @@ __device__ __forceinline__ void scatter(const PermuteArgs& a, int (&ids)[8], int
           rows[j] = wpre[wave][ej] + __popcll(masks[wave][ej] & below);
           const int slot = t * K + j;
           if (staged)
-            stage[rows[j]] = slot;
+            stage[soff[ej] + rows[j] - cstart[ej]] = (ej << 23) | slot;
           else
             a.sorted_slot[rows[j]] = slot;
         } else {
@@ -314,8 +329,10 @@ __device__ __forceinline__ void scatter(const PermuteArgs& a, int (&ids)[8], int
     __syncthreads();
   }
   if (staged) {
-    const int n = K * T;
-    for (int i = tid; i < n; i += kThreads) a.sorted_slot[i] = stage[i];
+    for (int i = tid; i < n_mine; i += kThreads) {
+      const int v = stage[i], e = v >> 23;
+      a.sorted_slot[cstart[e] + (i - soff[e])] = v & ((1 << 23) - 1);
+    }
   }
 }
 
@@ -332,30 +349,55 @@ __global__ __launch_bounds__(kThreads) void k_permute(PermuteArgs a) {
   __shared__ uint64_t masks[kWavesP][kMaxE];  // per wave and expert: lanes whose token has it
   __shared__ int wpre[kWavesP][kMaxE];        // first row of (wave, expert) in the chunk
   __shared__ int stage[kStage];
+  __shared__ __attribute__((aligned(16))) int before[kMaxE];  // scatter: slots of expert e in earlier tokens
+  __shared__ __attribute__((aligned(16))) int mine[kMaxE];    // scatter: slots of expert e in this range
+  __shared__ int soff[kMaxE + 4];                             // scatter: start of expert e's run in the stage
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int E = a.E, K = a.K, T = a.T;
-  const int role = blockIdx.x;  // 0 .. 15: queue role % 8 of GEMM role / 8; 16: the scatter
-  const bool staged = (size_t)K * T <= (size_t)kStage;
+  const int role = blockIdx.x;  // 0 .. 15: queue role % 8 of GEMM role / 8; from 16: the scatter
+  // a scatter workgroup's token range [t0, t1): whole chunks of kThreads tokens
+  const bool scat = role >= 2 * kQueues;
+  int t0 = 0, t1 = 0;
+  if (scat) {
+    const int chunks = (T + kThreads - 1) / kThreads, S = scatter_groups(T), s = role - 2 * kQueues;
+    t0 = min(T, (int)((long)s * chunks / S) * kThreads);
+    t1 = min(T, (int)((long)(s + 1) * chunks / S) * kThreads);
+  }
+  const bool staged = (size_t)K * (t1 - t0) <= (size_t)kStage;
 
   // the first chunk of tokens is loaded once and kept for the scatter
   int ids[8] = {0, 0, 0, 0, 0, 0, 0, 0};
   if (tid < T) load_ids(a.topk_idx, tid, K, ids);
 
-  // --- histogram
-  if (tid < kMaxE) cnt[tid] = 0;
+  // --- histogram (a scatter workgroup also counts the slots before its range and in it)
+  if (tid < kMaxE) {
+    cnt[tid] = 0;
+    before[tid] = 0;
+    mine[tid] = 0;
+  }
   __syncthreads();
   if (tid < T) {
+    int* part = (scat && tid < t0) ? before : (scat && tid < t1) ? mine : nullptr;
 #pragma unroll
-    for (int j = 0; j < 8; ++j)
-      if (j < K) atomicAdd(&cnt[ids[j]], 1);
+    for (int j = 0; j < 8; ++j) {
+      if (j < K) {
+        atomicAdd(&cnt[ids[j]], 1);
+        if (part) atomicAdd(&part[ids[j]], 1);
+      }
+    }
   }
   for (int t = tid + kThreads; t < T; t += kThreads) {
     int ee[8];
     load_ids(a.topk_idx, t, K, ee);
+    int* part = (scat && t < t0) ? before : (scat && t < t1) ? mine : nullptr;
 #pragma unroll
-    for (int j = 0; j < 8; ++j)
-      if (j < K) atomicAdd(&cnt[ee[j]], 1);
+    for (int j = 0; j < 8; ++j) {
+      if (j < K) {
+        atomicAdd(&cnt[ee[j]], 1);
+        if (part) atomicAdd(&part[ee[j]], 1);
+      }
+    }
   }
   __syncthreads();
 
@@ -390,9 +432,28 @@ __global__ __launch_bounds__(kThreads) void k_permute(PermuteArgs a) {
     }
   }
   if (role == 0 && tid < 2) a.qlen[2 * kQueues + tid] = a.qmax[tid];  // the queue capacities, for inspection
-  if (role == 2 * kQueues) {
+  if (scat) {
+    // the range's first row of each expert (kept in base: cursor advances),
+    // and the runs of its slots in the stage
+    if (wave == 0) {
+      const int4 b4 = *reinterpret_cast<const int4*>(&base[4 * lane]);
+      const int4 p4 = *reinterpret_cast<const int4*>(&before[4 * lane]);
+      const int4 m4 = *reinterpret_cast<const int4*>(&mine[4 * lane]);
+      const int4 st = make_int4(b4.x + p4.x, b4.y + p4.y, b4.z + p4.z, b4.w + p4.w);
+      *reinterpret_cast<int4*>(&base[4 * lane]) = st;
+      *reinterpret_cast<int4*>(&cursor[4 * lane]) = st;
+      const int m[4] = {m4.x, m4.y, m4.z, m4.w};
+      const int sum = (m[0] + m[1]) + (m[2] + m[3]);
+      int run = wave_scan<false>(sum) - sum;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        soff[4 * lane + i] = run;
+        run += m[i];
+      }
+      if (lane == 63) soff[kMaxE] = run;  // experts >= E have no slots: soff[E] is the range's slot count
+    }
     __syncthreads();
-    scatter(a, ids, cursor, masks, wpre, stage, staged, tid, lane, wave);
+    scatter(a, ids, t0, t1, cursor, base, soff, soff[kMaxE], masks, wpre, stage, staged, tid, lane, wave);
     return;
   }
   // --- the deal, and queue x of GEMM g: the load that the units of the
@@ -514,7 +575,7 @@ __global__ __launch_bounds__(kThreads) void k_permute(PermuteArgs a) {
 }  // namespace
 
 hipError_t launch_permute(const PermuteArgs& a, hipStream_t stream, const KernelEvents* ev) {
-  return launch_kernel(k_permute, dim3(2 * kQueues + 1), dim3(kThreads), stream, ev, a);
+  return launch_kernel(k_permute, dim3(2 * kQueues + scatter_groups(a.T)), dim3(kThreads), stream, ev, a);
 }
 
 }  // namespace dg

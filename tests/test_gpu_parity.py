@@ -66,7 +66,9 @@ def test_small_shapes(E, K, D, F, T, act, rw, pack):
 
 @pytest.mark.parametrize("E,K,D,F,T", [
     (256, 8, 256, 128, 300),    # the most experts a layer may have
-    (16, 8, 256, 128, 3000),    # k T = 24000 slots: past what the permutation stages in LDS; tall tiles
+    (16, 8, 256, 128, 3000),    # three scatter workgroups of 1024 tokens; wide tiles
+    (16, 8, 256, 128, 24000),   # eight scatter workgroups of 3 chunks: 24576 slots of a range past what
+                                # one stages in LDS (written directly), the last range staged
     (8, 2, 1024, 4096, 40),     # the largest d_ff: 64 gate_up column blocks, down over K = 4096
     (4, 1, 16384, 64, 20),      # the largest d_model: 128 router chunks, gate_up over K = 16384
 ])
@@ -76,7 +78,10 @@ def test_shape_limits(E, K, D, F, T):
     inp = synth.make_inputs(wl, device="cuda")
     w = inp["layers"][0]
     layer = _layer(w, T, torch.bfloat16, K=K, pack=True)
-    r = layer_parity(layer, inp["x"], oracle_weights(w), K)
+    # routing and permutation are checked for every token; outputs on a sample past 10000 tokens
+    tok = None if T <= 10000 else np.unique(np.concatenate(
+        [np.arange(0, T, 997), np.arange(T - 40, T), np.random.default_rng(T).choice(T, 200, replace=False)]))
+    r = layer_parity(layer, inp["x"], oracle_weights(w), K, tokens=tok)
     print(f"err {r['err']:.3e} near-ties {r['near_ties']}")
     layer.close()
 
