@@ -21,6 +21,7 @@ step = one call; the same JSON fields, with the logits kernel as the dominant on
 import argparse
 import ctypes
 import hashlib
+import re
 import json
 import os
 import sys
@@ -106,17 +107,25 @@ def algorithmic(wl, T, touched):
     return layer_bytes, flops, gemm_bytes, gate_up_bytes
 
 
+def _code_only(text):
+    """Source text without its comments and blank lines (what the compiler sees of it)."""
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    lines = (re.sub(r"//.*", "", ln).rstrip() for ln in text.splitlines())
+    return "\n".join(ln for ln in lines if ln)
+
+
 def kernel_sources_digest():
-    """Digest of every source of the layer's library (the GEMMs, and the router, permutation and host code
-    that set what they read): counters taken on other sources do not describe this build."""
+    """Digest of the code of every source of the layer's library (the GEMMs, and the router, permutation and
+    host code that set what they read), comments left out: counters taken on other code do not describe this
+    build."""
     h = hashlib.sha256()
     csrc = os.path.join(ROOT, "expert_ffn_canvas_amd", "csrc")
     for name in sorted(os.listdir(csrc)):
         if name == "head.hip" or not name.endswith((".hip", ".h")):
             continue
-        with open(os.path.join(csrc, name), "rb") as f:
+        with open(os.path.join(csrc, name), encoding="utf-8") as f:
             h.update(name.encode())
-            h.update(f.read())
+            h.update(_code_only(f.read()).encode())
     return h.hexdigest()[:16]
 
 

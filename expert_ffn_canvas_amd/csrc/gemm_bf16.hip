@@ -286,9 +286,6 @@ __device__ __forceinline__ void gemm_body(const GemmArgs& a, const Tile& tl, cha
   }
 }
 
-// Both GEMMs in one launch (the task logic of fused_tasks). Three workgroups
-// per CU (waves_per_eu 3): the register budget that keeps two K steps of
-// weight panels per wave in flight without spilling.
 // One task of a fused launch. Expert weights are read once per launch and
 // stream past the caches (ld_stream), except those of an expert cut into
 // several tiles: each of its tiles reads the same weight blocks, close together
@@ -306,6 +303,9 @@ __device__ __forceinline__ void task_body(const FusedGemmArgs& f, const GemmArgs
     gemm_body<GATE_UP, PK, ROWS, WV, true>(a, tl, As, rrow);
 }
 
+// Both GEMMs in one launch (the task logic of fused_tasks). Three workgroups
+// per CU (waves_per_eu 3): the register budget that keeps two K steps of
+// weight panels per wave in flight without spilling.
 template <bool PK>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3, 3))) void k_gemm_fused(
     FusedGemmArgs f) {
