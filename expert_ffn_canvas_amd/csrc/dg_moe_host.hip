@@ -95,7 +95,7 @@ Layout plan(const dg_moe_config& c) {
   L.h = take(L.fold ? 0 : T * D * 2);
   L.rnorm = take(T * 4);
   L.logits = take(T * (size_t)L.Epad * 4);
-  L.tile_count = take((T + 15) / 16 * 8);
+  L.tile_count = take((T + 15) / 16 * 128);
   L.topk_idx = take(T * K * 4);
   L.topk_w = take(T * K * 4);
   L.counts = take(E * 4);
@@ -356,7 +356,7 @@ dg_status dg_moe_create(const dg_moe_config* cfg, const dg_moe_weights* w, void*
       return hip_fail(ci, "preparing router parameters");
     }
   }
-  e = hipMemsetAsync(hd->ws + hd->L.tile_count, 0, ((size_t)cfg->max_tokens + 15) / 16 * 8, stream);
+  e = hipMemsetAsync(hd->ws + hd->L.tile_count, 0, ((size_t)cfg->max_tokens + 15) / 16 * 128, stream);
   if (e == hipSuccess) e = hipMemsetAsync(hd->ws + hd->L.dev_flags, 0, 4, stream);
   if (e != hipSuccess) {
     dg_moe_destroy(hd);
@@ -374,7 +374,8 @@ dg_status dg_moe_create(const dg_moe_config* cfg, const dg_moe_weights* w, void*
 static dg_status run_forward(dg_moe_handle hd, const void* x, void* out, int32_t T, const void* addend,
                              uint32_t flags, const dg_moe_debug* dbg, void* const* events, void* stream_v) {
   if (!hd) return fail(DG_ERR_INVALID_ARG, "handle is NULL");
-  if (flags & ~DG_FWD_ADD_INPUT) return fail(DG_ERR_INVALID_ARG, "unknown forward flags 0x%x", flags);
+  if (flags & ~(DG_FWD_ADD_INPUT | DG_FWD_ROUTER_NO_WAIT))
+    return fail(DG_ERR_INVALID_ARG, "unknown forward flags 0x%x", flags);
   const dg_moe_config& c = hd->cfg;
   if (T < 0 || T > c.max_tokens) return fail(DG_ERR_SHAPE, "T = %d not in [0, max_tokens = %d]", T, c.max_tokens);
   if (T == 0) return ok();
@@ -418,6 +419,7 @@ static dg_status run_forward(dg_moe_handle hd, const void* x, void* out, int32_t
   ra.gamma_e = hd->at<float>(L.gamma_e);
   ra.eps = c.rms_eps;
   ra.n_cu = hd->n_cu;
+  ra.no_wait = (flags & DG_FWD_ROUTER_NO_WAIT) ? 1 : 0;
   ra.h_f16 = (i4 || q8) ? 1 : 0;  // MXFP4 / MXFP8 widen to bf16 (their block scales need bf16's exponent range)
   ra.h = L.fold ? nullptr : hd->at<uint16_t>(L.h);
   ra.rnorm = hd->at<float>(L.rnorm);

@@ -103,12 +103,18 @@ struct RouterArgs {
   uint16_t* h;          // [T, D] expert input, or null where the GEMM reads x (the norm folded)
   float* rnorm;         // [T] r = 1/sqrt(mean x^2 + eps) of each token
   float* logits;        // [T, Epad]
-  uint64_t* tile_count; // [ceil(T / 16)] arrival counters of the logits kernel, zero between forwards: the
-                        // arrivals in bits 0..7, and per XCD x the arrivals from it in bits 8 + 6 x ..
+  uint64_t* tile_count; // [16 ceil(T / 16)] counters of the logits kernel, zero between forwards, one 128-byte
+                        // line per token tile tt: word 16 tt holds the arrivals in bits 0..7 and per XCD x
+                        // the arrivals from it in bits 8 + 6 x ..; word 16 tt + 1 the shares given up (bit
+                        // per workgroup of the tile) and in bits 32..39 the workgroups done
   int32_t* topk_idx;    // [T, K]
   float* topk_w;        // [T, K]
   uint32_t* dev_flags;  // sticky device status word (DG_DEV_* bits of dg_moe.h)
   int n_cu;             // compute units of the device (sets the token-tile height)
+  int no_wait;          // no workgroup waits for its token tile's last arrival (the path of a wait that ran out)
+  int polls;            // set by launch_logits: < 0, the last arriver of a token tile selects the top-k of all
+                        // its tokens; >= 0, each workgroup waits up to this many polls for the last arrival,
+                        // then selects for its own share of the tokens
 };
 // r, logits, top-k and the routing weights, and h = x r (1 + gamma_e) where h
 // is not null.

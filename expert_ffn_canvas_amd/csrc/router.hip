@@ -141,6 +141,30 @@ __device__ __forceinline__ void topk_row(const float (&lv)[NU], bool active, int
   }
 }
 
+// Top-k of tokens lo .. hi - 1 of the token tile at t0, whose logit rows are
+// complete in this XCD's L2. Wave h takes tokens lo + 4 h .. lo + 4 h + 3 of
+// each 32-token group, one per 16-lane row; all of a wave's rows are loaded
+// before the first selection (one memory round trip). Rows are read at
+// clamped indices, so every load is in bounds.
+template <int NU, int kPass>
+__device__ __forceinline__ void topk_span(const RouterArgs& a, int t0, int lo, int hi, int kh, int lane) {
+  const int m = lane & 15;
+  float lv[kPass][NU];
+#pragma unroll
+  for (int it = 0; it < kPass; ++it) {
+    const int tl = lo + 4 * kh + 4 * kWaves * it + (lane >> 4);
+    if (lo + 4 * kh + 4 * kWaves * it < hi)
+      load_row<NU>(a.logits + (size_t)min(t0 + min(tl, hi - 1), a.T - 1) * a.Epad, m, a.Epad, lv[it]);
+  }
+#pragma unroll
+  for (int it = 0; it < kPass; ++it) {
+    const int tl = lo + 4 * kh + 4 * kWaves * it + (lane >> 4);
+    if (lo + 4 * kh + 4 * kWaves * it >= hi) break;
+    const size_t trow = (size_t)min(t0 + min(tl, hi - 1), a.T - 1);
+    topk_row<NU>(lv[it], tl < hi && t0 + tl < a.T, a.E, a.K, m, a.topk_idx + trow * a.K, a.topk_w + trow * a.K);
+  }
+}
+
 // bf16 x values of one MFMA operand (8 consecutive columns) -> sum of squares.
 __device__ __forceinline__ float sumsq8(const u32x4& v) {
   float s = 0.0f;
@@ -207,9 +231,16 @@ __device__ __forceinline__ void write_h(const RouterArgs& a, const float* rs, in
 // the sums of squares) are added through LDS in a fixed order; every expert
 // tile of a token tile computes the same r bit for bit.
 // All expert tiles of a token tile run on one XCD (workgroup b runs on XCD
-// (b + c) % 8, c fixed within a launch) and share its L2: each publishes its logits with a counter and the
-// last to arrive selects the top-k of all the tile's tokens, one per 16-lane
-// row. With SPLIT = 2 (few token tiles) each expert tile is shared by two
+// (b + c) % 8, c fixed within a launch) and share its L2: each publishes its
+// logits with a counter. Either the last to arrive selects the top-k of all
+// the tile's tokens, one per 16-lane row, or (a.polls >= 0: tall tiles whose
+// launch fits the CUs at once) every workgroup waits, a bounded number of
+// polls, for the last arrival and then selects for its own share of the
+// tokens: a workgroup that stops waiting marks its share given up, and the
+// last arriver, after its own share, takes every share so marked. A share
+// is given up before the last arrival or its owner sees that arrival, so
+// each share is selected at least once, and twice only with identical
+// results. With SPLIT = 2 (few token tiles) each expert tile is shared by two
 // workgroups, one per half of its 16 experts: each loads only its half of
 // every W' fragment (the other lanes' operands are zero), so the W' bytes a
 // CU takes in are halved and twice as many CUs share them.
@@ -227,7 +258,8 @@ __global__ __launch_bounds__(64 * kWaves) void k_logits(RouterArgs a) {
   __shared__ __attribute__((aligned(16))) char smem[kBuf];
   __shared__ float ssq[kWaves][kRows];
   __shared__ float rs[kRows];  // r of each row
-  __shared__ int is_last;
+  __shared__ int pick;  // 0: no selection; 1: the whole tile; 2: own share; 3: own share, then those given up
+  __shared__ uint32_t given_up;
   float(*part)[kRows][17] = reinterpret_cast<float(*)[kRows][17]>(smem);
 
   const int tid = threadIdx.x, lane = tid & 63;
@@ -405,47 +437,74 @@ __global__ __launch_bounds__(64 * kWaves) void k_logits(RouterArgs a) {
   __syncthreads();
   // each arrival also counts under its XCD: the last arriver checks that all
   // of the token tile's workgroups ran on its own (it reads their logits from
-  // its L2) and raises DG_DEV_XCD_ROUTER if not
+  // its L2) and raises DG_DEV_XCD_ROUTER if not. Counters of tile tt: word
+  // 16 tt (arrivals) and 16 tt + 1 (shares given up, workgroups done), one
+  // 128-byte line per tile, so the tiles' polls and arrivals do not queue on
+  // one line.
+  const int w = jq % n_eh;  // this workgroup's share: tokens, and columns of h
+  unsigned long long* arrive = reinterpret_cast<unsigned long long*>(&a.tile_count[16 * tt]);
+  unsigned long long* aux = reinterpret_cast<unsigned long long*>(&a.tile_count[16 * tt + 1]);
   if (tid == 0) {
     const int xcc = xcc_id();
     const unsigned long long mine = 1ull | (1ull << (8 + 6 * xcc));
-    const unsigned long long now =
-        atomicAdd(reinterpret_cast<unsigned long long*>(&a.tile_count[tt]), mine) + mine;
-    is_last = (int)(now & 0xffull) == n_eh;  // n_eh <= 32
-    if (is_last) {
-      if ((int)((now >> (8 + 6 * xcc)) & 63ull) != n_eh) raise_flag(a.dev_flags, DG_DEV_XCD_ROUTER);
-      a.tile_count[tt] = 0;  // ready for the next forward
+    const unsigned long long now = atomicAdd(arrive, mine) + mine;
+    const bool last = (int)(now & 0xffull) == n_eh;  // n_eh <= 32
+    if (last && (int)((now >> (8 + 6 * xcc)) & 63ull) != n_eh) raise_flag(a.dev_flags, DG_DEV_XCD_ROUTER);
+    int sel = 0;
+    if (a.polls < 0) {
+      sel = last ? 1 : 0;
+      if (last) *arrive = 0;  // ready for the next forward
+    } else if (last) {
+      sel = n_eh == 1 ? 1 : 3;
+    } else {
+      bool seen = false;
+      for (int n = 0; n <= a.polls && !seen; ++n) {
+        seen = (int)(__hip_atomic_load(arrive, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) & 0xffull) == n_eh;
+        if (!seen && n < a.polls) __builtin_amdgcn_s_sleep(1);
+      }
+      if (!seen) {
+        // give the share up, then look once more: if the last arrival came
+        // meanwhile, its arriver may have read the given-up shares already
+        atomicOr(aux, 1ull << w);
+        __builtin_amdgcn_s_waitcnt(0);
+        asm volatile("" ::: "memory");
+        seen = (int)(atomicAdd(arrive, 0ull) & 0xffull) == n_eh;
+      }
+      sel = seen ? 2 : 0;
     }
+    pick = sel;
   }
   __syncthreads();
-  // this workgroup's share of the expert input's columns (8-wide segments)
-  const int w = jq % n_eh, nseg = D / 8;
-  const int s0 = w * nseg / n_eh, s1 = (w + 1) * nseg / n_eh;
-  if (!is_last) {
-    if (a.h != nullptr) write_h<XF32, kRows>(a, rs, t0, s0, s1, tid, 64 * kWaves);
-    return;
-  }
-  // Last expert tile of this token tile: the full logit rows come from this
-  // XCD's L2 (every writer ran on this XCD and waited for its stores); no
-  // workgroup on this CU read these rows earlier in the launch, so its L1
-  // holds no stale copy. Wave h takes tokens 4 h .. 4 h + 3 of each 32-token
-  // group of the tile, one per 16-lane row; all of a wave's rows are loaded
-  // before the first selection (one memory round trip).
+  const int sel = __builtin_amdgcn_readfirstlane(pick);
+  // Selection: the full logit rows come from this XCD's L2 (every writer ran
+  // on this XCD and waited for its stores before counting itself); this CU
+  // read none of the tile's rows before they were complete, so its L1 holds
+  // no stale copy.
   constexpr int kPass = (kRows + 4 * kWaves - 1) / (4 * kWaves);
-  float lv[kPass][NU];
-#pragma unroll
-  for (int it = 0; it < kPass; ++it) {
-    const int tl = 4 * kh + 4 * kWaves * it + (lane >> 4);
-    if (4 * kh + 4 * kWaves * it < kRows) load_row<NU>(a.logits + (size_t)min(t0 + tl, a.T - 1) * a.Epad, m, a.Epad, lv[it]);
+  if (sel == 1) {
+    topk_span<NU, kPass>(a, t0, 0, kRows, kh, lane);
+  } else if (sel >= 2) {
+    topk_span<NU, kPass>(a, t0, w * kRows / n_eh, (w + 1) * kRows / n_eh, kh, lane);
+    if (sel == 3) {
+      if (tid == 0) given_up = (uint32_t)atomicAdd(aux, 0ull) & ~(1u << w);  // bits of shares < n_eh <= 16
+      __syncthreads();
+      for (uint32_t left = __builtin_amdgcn_readfirstlane(given_up); left != 0u; left &= left - 1u) {
+        const int sh = __builtin_ctz(left);
+        topk_span<NU, kPass>(a, t0, sh * kRows / n_eh, (sh + 1) * kRows / n_eh, kh, lane);
+      }
+    }
   }
-#pragma unroll
-  for (int it = 0; it < kPass; ++it) {
-    const int tl = 4 * kh + 4 * kWaves * it + (lane >> 4);
-    if (4 * kh + 4 * kWaves * it >= kRows) break;
-    const size_t trow = (size_t)min(t0 + tl, a.T - 1);
-    topk_row<NU>(lv[it], t0 + tl < a.T, a.E, a.K, m, a.topk_idx + trow * a.K, a.topk_w + trow * a.K);
+  if (a.polls >= 0 && tid == 0) {
+    // the tile's last workgroup to get here, when no other reads the
+    // counters any more, clears them for the next forward
+    const unsigned long long old = atomicAdd(aux, 1ull << 32);
+    if ((int)((old >> 32) & 0xffull) == n_eh - 1) {
+      *arrive = 0;
+      *aux = 0;
+    }
   }
-  if (a.h != nullptr) write_h<XF32, kRows>(a, rs, t0, s0, s1, tid, 64 * kWaves);
+  const int nseg = D / 8;
+  if (a.h != nullptr) write_h<XF32, kRows>(a, rs, t0, w * nseg / n_eh, (w + 1) * nseg / n_eh, tid, 64 * kWaves);
 }
 
 // Create time: W' = W_r diag(1 + gamma_r) in fp32 (router weight fp32 or
@@ -524,6 +583,11 @@ hipError_t launch_logits(const RouterArgs& a, hipStream_t stream, const KernelEv
   const int tiles = kQueues * ((n_tt + kQueues - 1) / kQueues) * n_et;
   const int split = (mt == 1 && tiles <= 64) ? 2 : 1;
   const dim3 grid(tiles * split);
+  // Tiles of 64 or 80 tokens share the top-k out when the whole launch fits
+  // the CUs at once (every workgroup of a tile then runs at the same time):
+  // up to 64 polls of about a microsecond each before a share is given up.
+  RouterArgs ac = a;
+  ac.polls = (mt >= 4 && (int)grid.x <= a.n_cu) ? (a.no_wait ? 0 : 64) : -1;
   const int nu = a.Epad / 16;  // 2 .. 16
   void (*k)(RouterArgs);
   if (a.x_f32)  // fp32 x lives in registers: at most two m-tiles
@@ -534,7 +598,7 @@ hipError_t launch_logits(const RouterArgs& a, hipStream_t stream, const KernelEv
         : mt == 2 ? pick_logits<false, 2, 2, 1, 64>(nu)
         : mt == 4 ? pick_logits<false, 4, 1, 1, 64>(nu)
                   : pick_logits<false, 5, 1, 1, 64>(nu);
-  return launch_kernel(k, grid, dim3(64 * kWaves), stream, ev, a);
+  return launch_kernel(k, grid, dim3(64 * kWaves), stream, ev, ac);
 }
 
 hipError_t launch_prep_router_w(const void* w, int w_f32, const float* gamma, int E, int Epad, int D,

@@ -21,6 +21,7 @@ DG_ERR_INVALID_ARG, DG_ERR_SHAPE, DG_ERR_DTYPE, DG_ERR_ALIGN = -1, -2, -3, -4
 DG_ERR_OOM, DG_ERR_HIP, DG_ERR_UNSUPPORTED = -5, -6, -7
 DG_MOE_PACK_WEIGHTS = 0x1
 DG_FWD_ADD_INPUT = 0x1
+DG_FWD_ROUTER_NO_WAIT = 0x2
 ABI_VERSION = 2
 DG_DEV_QUEUE_OVERFLOW, DG_DEV_XCD_ROUTER, DG_DEV_XCD_GEMM, DG_DEV_WAIT_TIMEOUT = 0x1, 0x2, 0x4, 0x8
 
@@ -258,13 +259,13 @@ class MoELayer:
         # events are the gate_up pair; the down pair is recorded back to back after it)
         self.gemms_fused = bool(pack or not i4)
 
-    def forward(self, x, out=None, addend=None, add_input=False):
+    def forward(self, x, out=None, addend=None, add_input=False, router_no_wait=False):
         import torch
         T = x.shape[0]
         if out is None:
             out = torch.empty((T, self.D), dtype=x.dtype, device=x.device)
-        st = dg_moe_forward(self.handle, _ptr(x), _ptr(out), T, _ptr(addend), DG_FWD_ADD_INPUT if add_input else 0,
-                            self.stream.cuda_stream)
+        flags = (DG_FWD_ADD_INPUT if add_input else 0) | (DG_FWD_ROUTER_NO_WAIT if router_no_wait else 0)
+        st = dg_moe_forward(self.handle, _ptr(x), _ptr(out), T, _ptr(addend), flags, self.stream.cuda_stream)
         _check(st, "dg_moe_forward")
         return out
 

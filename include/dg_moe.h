@@ -103,6 +103,12 @@ typedef enum dg_status {
 
 /* dg_moe_forward flags */
 #define DG_FWD_ADD_INPUT 0x1u /* out = x + MoE(x) (+ addend) */
+/* For tests: where the router's workgroups of one token tile would wait for
+ * the last of them and share out the top-k selection, each looks for that
+ * arrival only once and otherwise leaves its share to the last arriver (the
+ * path taken when such a wait runs out). The results are bit-identical;
+ * only the timing differs. */
+#define DG_FWD_ROUTER_NO_WAIT 0x2u
 
 typedef struct dg_moe_config {
   uint32_t struct_size;   /* = sizeof(dg_moe_config)                                  */

@@ -171,6 +171,41 @@ def test_router_variants(T, act, variant):
     layer.close()
 
 
+# Tiles of 64 or 80 tokens whose launch fits the CUs at once share the top-k selection out among their
+# workgroups (each waits, a bounded number of polls, for the tile's last logits, then selects for its share);
+# a workgroup that stops waiting leaves its share to the last arriver. DG_FWD_ROUTER_NO_WAIT makes every
+# workgroup stop at once. Both paths must give the same bits, run right after a forward of other input, so
+# that a share nobody selected would keep that forward's routing and show.
+@pytest.mark.parametrize("T,E,D,F,case", [
+    (2200, 128, 512, 128, "80-token tiles, 8 shares of 10 tokens"),
+    (1500, 128, 512, 128, "64-token tiles, 8 shares of 8 tokens, ragged last tile"),
+    (3000, 40, 512, 128, "64-token tiles, 3 shares of 21-22 tokens, ragged last tile"),
+])
+def test_router_shared_selection(T, E, D, F, case):
+    _say(f"router shared selection T={T} E={E}: {case}")
+    wl = synth.small_workload(T=T, E=E, K=8, D=D, F=F, act="bf16", router_w="bf16", bias="zipf", seed=300 + T)
+    inp = synth.make_inputs(wl, device="cuda")
+    w = inp["layers"][0]
+    x2 = inp["x"]
+    x1 = torch.roll(x2, shifts=7, dims=0).contiguous()
+    layer = _layer(w, T, torch.bfloat16, pack=True)
+    o1 = layer.forward(x1).clone()
+    o_nowait = layer.forward(x2, router_no_wait=True).clone()
+    o_wait = layer.forward(x2).clone()
+    o1b = layer.forward(x1).clone()
+    o_nowait2 = layer.forward(x2, router_no_wait=True).clone()
+    torch.cuda.synchronize()
+    assert not torch.equal(o1.view(torch.int16), o_wait.view(torch.int16))
+    assert torch.equal(o1.view(torch.int16), o1b.view(torch.int16))
+    assert torch.equal(o_nowait.view(torch.int16), o_wait.view(torch.int16))
+    assert torch.equal(o_nowait2.view(torch.int16), o_wait.view(torch.int16))
+    rng = np.random.default_rng(T)
+    tok = np.unique(np.concatenate([[0, T - 1], rng.choice(T, 40, replace=False)]))
+    r = layer_parity(layer, x2, oracle_weights(w), wl.K, tokens=tok)
+    print(f"err {r['err']:.3e} near-ties {r['near_ties']}")
+    layer.close()
+
+
 def test_adversarial_expert_loads():
     # Six experts take every token (bias +30) and 24 more most of the other two slots (bias +3), at expert
     # ids placed so that dealing the larger experts in id order would stack three of the six on one queue;
