@@ -85,7 +85,9 @@ Layout plan(const dg_moe_config& c) {
   L.nb[0] = dg::gate_up_blocks((int)F);
   L.nb[1] = dg::down_blocks((int)D);
   // the shortest tiles give the longest queues
-  for (int g = 0; g < 2; ++g) L.qmax[g] = dg::max_queue_len((int)T, (int)K, (int)E, L.nb[g], dg::kTileRows);
+  const int min_rows = (c.expert_w_dtype == DG_I4G128 && (c.flags & DG_MOE_PACK_WEIGHTS)) ? dg::kShortRows
+                                                                                          : dg::kTileRows;
+  for (int g = 0; g < 2; ++g) L.qmax[g] = dg::max_queue_len((int)T, (int)K, (int)E, L.nb[g], min_rows);
   size_t off = 0;
   auto take = [&](size_t bytes) {
     const size_t at = off;
@@ -442,10 +444,11 @@ static dg_status run_forward(dg_moe_handle hd, const void* x, void* out, int32_t
   pa.T = T;
   pa.K = c.top_k;
   pa.E = c.n_experts;
-  const int tile_rows =
-      c.expert_w_dtype == DG_BF16 ? dg::bf16_tile_rows(T, c.top_k, c.n_experts) : dg::kTileRows;
-  const bool tall = tile_rows != dg::kTileRows;
   const bool fused = fuses_gemms(c);
+  const int tile_rows = c.expert_w_dtype == DG_BF16 ? dg::bf16_tile_rows(T, c.top_k, c.n_experts)
+                        : (i4 && fused)             ? dg::i4_tile_rows(T, c.top_k, c.n_experts)
+                                                    : dg::kTileRows;
+  const bool tall = tile_rows > dg::kTileRows;
   pa.tile_rows = tile_rows;
   pa.deal = fused ? dg::kDealBalanced : tall ? dg::kDealExperts : dg::kDealUnits;
   pa.tile_done = fused ? hd->at<uint64_t>(L.tile_done) : nullptr;
@@ -495,7 +498,7 @@ static dg_status run_forward(dg_moe_handle hd, const void* x, void* out, int32_t
     e = mx4  ? dg::launch_gemm_fused_mx4(fa, stream, ev(3))
         : mx8 ? dg::launch_gemm_fused_mx8(fa, stream, ev(3))
         : q8 ? dg::launch_gemm_fused_q8(fa, stream, ev(3))
-        : i4 ? dg::launch_gemm_fused_i4(fa, stream, ev(3))
+        : i4 ? dg::launch_gemm_fused_i4(fa, tile_rows, stream, ev(3))
              : dg::launch_gemm_fused(fa, tile_rows, stream, ev(3));
     if (e != hipSuccess) return hip_fail(e, "GEMM launch");
     if (events) {  // one launch for both GEMMs: the down events mark the point after it

@@ -369,11 +369,11 @@ __device__ __forceinline__ void load_wg(const uint8_t* c0, const uint8_t* c1, co
 }
 
 // One group's MFMAs: partial sums over the 128 inputs in t, then scaled into acc.
-template <int NMT>
-__device__ __forceinline__ void mma_i4(const char* stage, int lane, const WGroup& w, f32x4 (&acc0)[kBMT],
-                                       f32x4 (&acc1)[kBMT]) {
+template <int NMT, int MB>
+__device__ __forceinline__ void mma_i4(const char* stage, int lane, const WGroup& w, f32x4 (&acc0)[MB],
+                                       f32x4 (&acc1)[MB]) {
   const int g = lane >> 4, m = lane & 15;
-  f32x4 t0[kBMT], t1[kBMT];
+  f32x4 t0[MB], t1[MB];
 #pragma unroll
   for (int mt = 0; mt < NMT; ++mt) {
     t0[mt] = f32x4{0.f, 0.f, 0.f, 0.f};
@@ -405,11 +405,20 @@ __device__ __forceinline__ void mma_i4(const char* stage, int lane, const WGroup
 
 constexpr int kDepthI4 = 3;  // LDS stages and weight buffers; step i + 2 is issued during step i
 
-template <int NMT>
-__device__ __forceinline__ void issue_i4(char* As, const uint16_t* const (&rowp)[kDmaInstr], const uint8_t* c0,
+// The packed kernels' tile heights: 64 rows, or 32 where experts hold few rows
+// (half the registers for the sums, so three workgroups share a CU).
+template <int ROWS>
+struct I4Tile {
+  static constexpr int kMB = ROWS / 16;                       // m-tiles
+  static constexpr int kStage = ROWS * kRowBytes;             // bytes of one LDS stage
+  static constexpr int kNI = dma_per_wave(ROWS, kWaves);      // activation transfers per wave
+};
+
+template <int ROWS, int NMT>
+__device__ __forceinline__ void issue_i4(char* As, const uint16_t* const (&rowp)[I4Tile<ROWS>::kNI], const uint8_t* c0,
                                          const uint8_t* c1, const uint16_t* s0, const uint16_t* s1, int j, int K,
                                          int wave, int lane, WGroup& w) {
-  char* st = As + (j % kDepthI4) * kStageBytes;
+  char* st = As + (j % kDepthI4) * I4Tile<ROWS>::kStage;
   const int k0 = j * kKS;
   if (k0 + kKS <= K)
     dma_a<NMT, kSegs>(st, rowp, k0, wave, lane);
@@ -423,54 +432,54 @@ __device__ __forceinline__ void issue_i4(char* As, const uint16_t* const (&rowp)
 // Step i: wait until step i's transfers have landed (those of step i + 1,
 // NMT DMA transfers and 4 weight loads, may still fly; WAIT = 0 for the last
 // step), publish, issue step i + 2, multiply step i.
-template <int NMT, bool ISSUE, int WAIT>
-__device__ __forceinline__ void step_i4(char* As, const uint16_t* const (&rowp)[kDmaInstr], const uint8_t* c0,
+template <int ROWS, int NMT, bool ISSUE, int WAIT>
+__device__ __forceinline__ void step_i4(char* As, const uint16_t* const (&rowp)[I4Tile<ROWS>::kNI], const uint8_t* c0,
                                         const uint8_t* c1, const uint16_t* s0, const uint16_t* s1, int i, int K,
-                                        int wave, int lane, const WGroup& wb, WGroup& wn2, f32x4 (&acc0)[kBMT],
-                                        f32x4 (&acc1)[kBMT]) {
+                                        int wave, int lane, const WGroup& wb, WGroup& wn2,
+                                        f32x4 (&acc0)[I4Tile<ROWS>::kMB], f32x4 (&acc1)[I4Tile<ROWS>::kMB]) {
   wait_vmcnt<WAIT>();
   lds_barrier();
-  if (ISSUE) issue_i4<NMT>(As, rowp, c0, c1, s0, s1, i + 2, K, wave, lane, wn2);
-  mma_i4<NMT>(As + (i % kDepthI4) * kStageBytes, lane, wb, acc0, acc1);
+  if (ISSUE) issue_i4<ROWS, NMT>(As, rowp, c0, c1, s0, s1, i + 2, K, wave, lane, wn2);
+  mma_i4<NMT>(As + (i % kDepthI4) * I4Tile<ROWS>::kStage, lane, wb, acc0, acc1);
 }
 
 // The group loop: unrolled by three (one weight buffer per position), the last
 // two to four groups written out so that every wait count is exact.
-template <int NMT>
-__device__ __forceinline__ void loop_i4(char* As, const uint16_t* const (&rowp)[kDmaInstr], const uint8_t* c0,
+template <int ROWS, int NMT>
+__device__ __forceinline__ void loop_i4(char* As, const uint16_t* const (&rowp)[I4Tile<ROWS>::kNI], const uint8_t* c0,
                                         const uint8_t* c1, const uint16_t* s0, const uint16_t* s1, int K, int tid,
-                                        f32x4 (&acc0)[kBMT], f32x4 (&acc1)[kBMT]) {
+                                        f32x4 (&acc0)[I4Tile<ROWS>::kMB], f32x4 (&acc1)[I4Tile<ROWS>::kMB]) {
   constexpr int kW = NMT + 4;
   const int lane = tid & 63, wave = tid >> 6;
   const int n = (K + kKS - 1) / kKS;
   WGroup w0, w1, w2;
-  issue_i4<NMT>(As, rowp, c0, c1, s0, s1, 0, K, wave, lane, w0);
+  issue_i4<ROWS, NMT>(As, rowp, c0, c1, s0, s1, 0, K, wave, lane, w0);
   if (n == 1) {
-    step_i4<NMT, false, 0>(As, rowp, c0, c1, s0, s1, 0, K, wave, lane, w0, w2, acc0, acc1);
+    step_i4<ROWS, NMT, false, 0>(As, rowp, c0, c1, s0, s1, 0, K, wave, lane, w0, w2, acc0, acc1);
     return;
   }
-  issue_i4<NMT>(As, rowp, c0, c1, s0, s1, 1, K, wave, lane, w1);
+  issue_i4<ROWS, NMT>(As, rowp, c0, c1, s0, s1, 1, K, wave, lane, w1);
   int i = 0;
   for (; i + 5 <= n; i += 3) {
-    step_i4<NMT, true, kW>(As, rowp, c0, c1, s0, s1, i, K, wave, lane, w0, w2, acc0, acc1);
-    step_i4<NMT, true, kW>(As, rowp, c0, c1, s0, s1, i + 1, K, wave, lane, w1, w0, acc0, acc1);
-    step_i4<NMT, true, kW>(As, rowp, c0, c1, s0, s1, i + 2, K, wave, lane, w2, w1, acc0, acc1);
+    step_i4<ROWS, NMT, true, kW>(As, rowp, c0, c1, s0, s1, i, K, wave, lane, w0, w2, acc0, acc1);
+    step_i4<ROWS, NMT, true, kW>(As, rowp, c0, c1, s0, s1, i + 1, K, wave, lane, w1, w0, acc0, acc1);
+    step_i4<ROWS, NMT, true, kW>(As, rowp, c0, c1, s0, s1, i + 2, K, wave, lane, w2, w1, acc0, acc1);
   }
   switch (n - i) {
     case 2:
-      step_i4<NMT, false, kW>(As, rowp, c0, c1, s0, s1, i, K, wave, lane, w0, w2, acc0, acc1);
-      step_i4<NMT, false, 0>(As, rowp, c0, c1, s0, s1, i + 1, K, wave, lane, w1, w0, acc0, acc1);
+      step_i4<ROWS, NMT, false, kW>(As, rowp, c0, c1, s0, s1, i, K, wave, lane, w0, w2, acc0, acc1);
+      step_i4<ROWS, NMT, false, 0>(As, rowp, c0, c1, s0, s1, i + 1, K, wave, lane, w1, w0, acc0, acc1);
       break;
     case 3:
-      step_i4<NMT, true, kW>(As, rowp, c0, c1, s0, s1, i, K, wave, lane, w0, w2, acc0, acc1);
-      step_i4<NMT, false, kW>(As, rowp, c0, c1, s0, s1, i + 1, K, wave, lane, w1, w0, acc0, acc1);
-      step_i4<NMT, false, 0>(As, rowp, c0, c1, s0, s1, i + 2, K, wave, lane, w2, w1, acc0, acc1);
+      step_i4<ROWS, NMT, true, kW>(As, rowp, c0, c1, s0, s1, i, K, wave, lane, w0, w2, acc0, acc1);
+      step_i4<ROWS, NMT, false, kW>(As, rowp, c0, c1, s0, s1, i + 1, K, wave, lane, w1, w0, acc0, acc1);
+      step_i4<ROWS, NMT, false, 0>(As, rowp, c0, c1, s0, s1, i + 2, K, wave, lane, w2, w1, acc0, acc1);
       break;
     default:  // 4
-      step_i4<NMT, true, kW>(As, rowp, c0, c1, s0, s1, i, K, wave, lane, w0, w2, acc0, acc1);
-      step_i4<NMT, true, kW>(As, rowp, c0, c1, s0, s1, i + 1, K, wave, lane, w1, w0, acc0, acc1);
-      step_i4<NMT, false, kW>(As, rowp, c0, c1, s0, s1, i + 2, K, wave, lane, w2, w1, acc0, acc1);
-      step_i4<NMT, false, 0>(As, rowp, c0, c1, s0, s1, i + 3, K, wave, lane, w0, w2, acc0, acc1);
+      step_i4<ROWS, NMT, true, kW>(As, rowp, c0, c1, s0, s1, i, K, wave, lane, w0, w2, acc0, acc1);
+      step_i4<ROWS, NMT, true, kW>(As, rowp, c0, c1, s0, s1, i + 1, K, wave, lane, w1, w0, acc0, acc1);
+      step_i4<ROWS, NMT, false, kW>(As, rowp, c0, c1, s0, s1, i + 2, K, wave, lane, w2, w1, acc0, acc1);
+      step_i4<ROWS, NMT, false, 0>(As, rowp, c0, c1, s0, s1, i + 3, K, wave, lane, w0, w2, acc0, acc1);
       break;
   }
 }
@@ -478,8 +487,9 @@ __device__ __forceinline__ void loop_i4(char* As, const uint16_t* const (&rowp)[
 // Packed-weight grouped GEMMs: the bf16 kernels' mapping and activation path,
 // int4 weights widened exactly to fp16 in registers. gate_up writes the gated
 // activation as fp16, down its fp32 sums as bf16.
-template <bool GATE_UP>
+template <bool GATE_UP, int ROWS>
 __device__ __forceinline__ void i4p_body(const GemmArgs& a, const Tile& tl, char* As) {
+  constexpr int MB = I4Tile<ROWS>::kMB, NI = I4Tile<ROWS>::kNI;
   const int F = a.F, D = a.D;
   const int K = GATE_UP ? D : F;
   const int G = (K + kKS - 1) / kKS;
@@ -488,9 +498,9 @@ __device__ __forceinline__ void i4p_body(const GemmArgs& a, const Tile& tl, char
   const int g = lane >> 4;
   const int nmt = (tl.mc + 15) >> 4;
 
-  const uint16_t* rowp[kDmaInstr];
+  const uint16_t* rowp[NI];
 #pragma unroll
-  for (int i = 0; i < kDmaInstr; ++i) {
+  for (int i = 0; i < NI; ++i) {
     const int r = min(kDmaRows * (wave + kWaves * i) + lane / kSegs, tl.mc - 1);
     rowp[i] = GATE_UP ? a.h + (size_t)(a.sorted_slot[tl.row0 + r] / a.K) * D : a.act + (size_t)(tl.row0 + r) * F;
   }
@@ -514,21 +524,28 @@ __device__ __forceinline__ void i4p_body(const GemmArgs& a, const Tile& tl, char
   const uint16_t* s0 = S + b0 * 16 + (lane & 15);
   const uint16_t* s1 = S + b1 * 16 + (lane & 15);
 
-  f32x4 acc0[kBMT], acc1[kBMT];
+  f32x4 acc0[MB], acc1[MB];
 #pragma unroll
-  for (int i = 0; i < kBMT; ++i) {
+  for (int i = 0; i < MB; ++i) {
     acc0[i] = f32x4{0.f, 0.f, 0.f, 0.f};
     acc1[i] = f32x4{0.f, 0.f, 0.f, 0.f};
   }
-  switch (nmt) {
-    case 1: loop_i4<1>(As, rowp, c0, c1, s0, s1, K, tid, acc0, acc1); break;
-    case 2: loop_i4<2>(As, rowp, c0, c1, s0, s1, K, tid, acc0, acc1); break;
-    case 3: loop_i4<3>(As, rowp, c0, c1, s0, s1, K, tid, acc0, acc1); break;
-    default: loop_i4<4>(As, rowp, c0, c1, s0, s1, K, tid, acc0, acc1); break;
+  if constexpr (MB == 2) {
+    if (nmt == 1)
+      loop_i4<ROWS, 1>(As, rowp, c0, c1, s0, s1, K, tid, acc0, acc1);
+    else
+      loop_i4<ROWS, 2>(As, rowp, c0, c1, s0, s1, K, tid, acc0, acc1);
+  } else {
+    switch (nmt) {
+      case 1: loop_i4<ROWS, 1>(As, rowp, c0, c1, s0, s1, K, tid, acc0, acc1); break;
+      case 2: loop_i4<ROWS, 2>(As, rowp, c0, c1, s0, s1, K, tid, acc0, acc1); break;
+      case 3: loop_i4<ROWS, 3>(As, rowp, c0, c1, s0, s1, K, tid, acc0, acc1); break;
+      default: loop_i4<ROWS, 4>(As, rowp, c0, c1, s0, s1, K, tid, acc0, acc1); break;
+    }
   }
 
 #pragma unroll
-  for (int mt = 0; mt < kBMT; ++mt) {
+  for (int mt = 0; mt < MB; ++mt) {
     if (mt < nmt) {
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
@@ -548,12 +565,22 @@ __device__ __forceinline__ void i4p_body(const GemmArgs& a, const Tile& tl, char
   }
 }
 
-// Both packed GEMMs in one launch (the task logic of fused_tasks).
+// Both packed GEMMs in one launch (the task logic of fused_tasks): 64-row
+// tiles at two workgroups per CU, or 32-row tiles at three.
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))) void k_gemm_i4p_fused(
     FusedGemmArgs f) {
-  __shared__ __attribute__((aligned(16))) char As[kDepthI4 * kStageBytes];
+  __shared__ __attribute__((aligned(16))) char As[kDepthI4 * I4Tile<kTileRows>::kStage];
   fused_tasks(
-      f, [&](const Tile& tl) { i4p_body<true>(f.gu, tl, As); }, [&](const Tile& tl) { i4p_body<false>(f.dn, tl, As); });
+      f, [&](const Tile& tl) { i4p_body<true, kTileRows>(f.gu, tl, As); },
+      [&](const Tile& tl) { i4p_body<false, kTileRows>(f.dn, tl, As); });
+}
+
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3, 3))) void k_gemm_i4p_fused_short(
+    FusedGemmArgs f) {
+  __shared__ __attribute__((aligned(16))) char As[kDepthI4 * I4Tile<kShortRows>::kStage];
+  fused_tasks(
+      f, [&](const Tile& tl) { i4p_body<true, kShortRows>(f.gu, tl, As); },
+      [&](const Tile& tl) { i4p_body<false, kShortRows>(f.dn, tl, As); });
 }
 
 }  // namespace
@@ -572,8 +599,9 @@ hipError_t launch_down_i4(const GemmArgs& a, hipStream_t stream, const KernelEve
   return launch_kernel(k_down_i4, dim3(kQueues * a.qmax), dim3(kThreads), stream, ev, a);
 }
 
-hipError_t launch_gemm_fused_i4(const FusedGemmArgs& f, hipStream_t stream, const KernelEvents* ev) {
-  return launch_kernel(k_gemm_i4p_fused, dim3(kQueues * (f.gu.qmax + f.dn.qmax)), dim3(kThreads), stream, ev, f);
+hipError_t launch_gemm_fused_i4(const FusedGemmArgs& f, int tile_rows, hipStream_t stream, const KernelEvents* ev) {
+  return launch_kernel(tile_rows == kShortRows ? k_gemm_i4p_fused_short : k_gemm_i4p_fused,
+                       dim3(kQueues * (f.gu.qmax + f.dn.qmax)), dim3(kThreads), stream, ev, f);
 }
 
 }  // namespace dg

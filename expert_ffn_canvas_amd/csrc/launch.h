@@ -40,6 +40,14 @@ inline int bf16_tile_rows(int T, int K, int E) {
   const long rows = (long)T * K;
   return rows >= (long)kWideFrom * E ? kWideRows : rows >= 64L * E ? kTallRows : kTileRows;
 }
+// Short tiles of the packed int4 GEMMs, used while the rows per expert average
+// at most kShortUpTo: nearly every expert then fits one tile, and the kernel's
+// smaller sums let three workgroups share a CU.
+constexpr int kShortRows = 32;
+constexpr int kShortUpTo = 20;
+inline int i4_tile_rows(int T, int K, int E) {
+  return (long)T * K <= (long)kShortUpTo * E ? kShortRows : kTileRows;
+}
 // GEMM tasks are spread over this many queues, one per XCD: queue x holds the
 // tasks that workgroups with blockIdx % kQueues == x process.
 constexpr int kQueues = 8;
@@ -138,7 +146,7 @@ constexpr int kDealUnits = 0, kDealExperts = 1, kDealBalanced = 2;
 struct PermuteArgs {
   const int32_t* topk_idx;
   int T, K, E;
-  int tile_rows;          // largest rows per tile: kTileRows, or kTallRows for the tall GEMMs
+  int tile_rows;          // largest rows per tile: kTileRows, kShortRows, kTallRows or kWideRows
   int deal;               // kDealUnits, kDealExperts or kDealBalanced
   uint64_t* tile_done;    // kDealBalanced: [K T], zeroed at the first row of every tile (the fused
                           // GEMM's per-tile counters); else null
@@ -204,8 +212,9 @@ hipError_t launch_pack_i4(const uint8_t* codes, const uint16_t* scales, uint8_t*
 // The two int4 products on the caller's row-major layout (borrow mode).
 hipError_t launch_gate_up_i4(const GemmArgs& a, hipStream_t stream, const KernelEvents* ev);
 hipError_t launch_down_i4(const GemmArgs& a, hipStream_t stream, const KernelEvents* ev);
-// Both products with packed int4 weights in one launch, as launch_gemm_fused.
-hipError_t launch_gemm_fused_i4(const FusedGemmArgs& f, hipStream_t stream, const KernelEvents* ev);
+// Both products with packed int4 weights in one launch, as launch_gemm_fused,
+// for tiles of tile_rows (kTileRows or kShortRows) rows.
+hipError_t launch_gemm_fused_i4(const FusedGemmArgs& f, int tile_rows, hipStream_t stream, const KernelEvents* ev);
 // Create-time relayout of Q8_0 expert weights (rows of K / 32 blocks of 34
 // bytes: fp16 scale, 32 int8 codes) into fragment order: per (expert, 128-input
 // step, 16-row panel), 2 KB of codes (lane l = n + 16 g: 32 bytes of row n in

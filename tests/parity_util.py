@@ -151,9 +151,10 @@ def check_device_state(dbg, K, E, T, D, F, balanced=None):
     ql = dbg["queue_len"].cpu().numpy()
     counts = dbg["counts"].cpu().numpy()
     lens, caps = ql[:16].reshape(2, 8), ql[16:18]
-    # the tile height and column blocks the launch used: 64- or 128-row tiles with blocks of 64 gate_up
+    # the tile height and column blocks the launch used: 32-, 64- or 128-row tiles with blocks of 64 gate_up
     # features and 128 down outputs, or 160-row tiles with blocks of 128 and 256 (the last one partial)
-    shapes = [(64, (F // 64, D // 128)), (128, (F // 64, D // 128)), (160, (-(-F // 128), -(-D // 256)))]
+    shapes = [(32, (F // 64, D // 128)), (64, (F // 64, D // 128)), (128, (F // 64, D // 128)),
+              (160, (-(-F // 128), -(-D // 256)))]
     match = [(R, nbs) for R, nbs in shapes
              if all(lens[g].sum() == nbs[g] * int(np.sum((counts + R - 1) // R)) for g in range(2))]
     assert match, f"queue lengths {lens} match no tile height"

@@ -289,13 +289,14 @@ def test_int4_g128(pack):
     print(f"err {r['err']:.3e} near-ties {r['near_ties']}")
 
 
-@pytest.mark.parametrize("E,K,T", [(12, 3, 50), (8, 4, 200)])
+@pytest.mark.parametrize("E,K,T,bias", [(12, 3, 50, None), (8, 4, 200, None), (16, 2, 150, "zipf")])
 @pytest.mark.parametrize("pack", [False, True], ids=["borrow", "pack"])
-def test_int4_small_tail_group(E, K, T, pack):
-    # d_ff = 192 = 128 + 64: the down projection's last scale group is 64 wide;
-    # T = 200 on 8 experts fills tiles of up to 64 rows
-    _say(f"int4 small E={E} K={K} D=256 F=192 T={T} pack={pack}")
-    wl = synth.small_workload(T=T, E=E, K=K, D=256, F=192, experts="i4g128", seed=8 + T)
+def test_int4_small_tail_group(E, K, T, bias, pack):
+    # d_ff = 192 = 128 + 64: the down projection's last scale group is 64 wide. Packed, up to 20 rows per
+    # expert on average run in 32-row tiles (T = 50 on 12 experts; T = 150 on 16 with a skew that puts some
+    # experts in two of them), more in 64-row tiles (T = 200 on 8 experts)
+    _say(f"int4 small E={E} K={K} D=256 F=192 T={T} bias={bias} pack={pack}")
+    wl = synth.small_workload(T=T, E=E, K=K, D=256, F=192, experts="i4g128", bias=bias, seed=8 + T)
     inp = synth.make_inputs(wl, device="cuda")
     w = inp["layers"][0]
     layer = _layer(w, T, torch.bfloat16, K=K, pack=pack)
