@@ -360,12 +360,22 @@ struct WGroup {
   uint16_t s0, s1;
 };
 
+// NT: past the caches (an expert in one tile reads its weights once); else
+// normal loads, so that the expert's other tiles find them in L2.
+template <bool NT>
 __device__ __forceinline__ void load_wg(const uint8_t* c0, const uint8_t* c1, const uint16_t* s0, const uint16_t* s1,
                                         int gi, WGroup& w) {
-  w.c0 = ld_stream(reinterpret_cast<const u32x4*>(c0 + (size_t)gi * 1024));
-  w.c1 = ld_stream(reinterpret_cast<const u32x4*>(c1 + (size_t)gi * 1024));
-  w.s0 = ld_stream(s0 + gi * 16);
-  w.s1 = ld_stream(s1 + gi * 16);
+  if constexpr (NT) {
+    w.c0 = ld_stream(reinterpret_cast<const u32x4*>(c0 + (size_t)gi * 1024));
+    w.c1 = ld_stream(reinterpret_cast<const u32x4*>(c1 + (size_t)gi * 1024));
+    w.s0 = ld_stream(s0 + gi * 16);
+    w.s1 = ld_stream(s1 + gi * 16);
+  } else {
+    w.c0 = *reinterpret_cast<const u32x4*>(c0 + (size_t)gi * 1024);
+    w.c1 = *reinterpret_cast<const u32x4*>(c1 + (size_t)gi * 1024);
+    w.s0 = s0[gi * 16];
+    w.s1 = s1[gi * 16];
+  }
 }
 
 // One group's MFMAs: partial sums over the 128 inputs in t, then scaled into acc.
@@ -414,7 +424,7 @@ struct I4Tile {
   static constexpr int kNI = dma_per_wave(ROWS, kWaves);      // activation transfers per wave
 };
 
-template <int ROWS, int NMT>
+template <int ROWS, int NMT, bool NT>
 __device__ __forceinline__ void issue_i4(char* As, const uint16_t* const (&rowp)[I4Tile<ROWS>::kNI], const uint8_t* c0,
                                          const uint8_t* c1, const uint16_t* s0, const uint16_t* s1, int j, int K,
                                          int wave, int lane, WGroup& w) {
@@ -425,27 +435,27 @@ __device__ __forceinline__ void issue_i4(char* As, const uint16_t* const (&rowp)
   else
     dma_a<NMT, kSegs / 2>(st, rowp, k0, wave, lane);
   __builtin_amdgcn_sched_barrier(0);
-  load_wg(c0, c1, s0, s1, j, w);
+  load_wg<NT>(c0, c1, s0, s1, j, w);
   __builtin_amdgcn_sched_barrier(0);
 }
 
 // Step i: wait until step i's transfers have landed (those of step i + 1,
 // NMT DMA transfers and 4 weight loads, may still fly; WAIT = 0 for the last
 // step), publish, issue step i + 2, multiply step i.
-template <int ROWS, int NMT, bool ISSUE, int WAIT>
+template <int ROWS, int NMT, bool NT, bool ISSUE, int WAIT>
 __device__ __forceinline__ void step_i4(char* As, const uint16_t* const (&rowp)[I4Tile<ROWS>::kNI], const uint8_t* c0,
                                         const uint8_t* c1, const uint16_t* s0, const uint16_t* s1, int i, int K,
                                         int wave, int lane, const WGroup& wb, WGroup& wn2,
                                         f32x4 (&acc0)[I4Tile<ROWS>::kMB], f32x4 (&acc1)[I4Tile<ROWS>::kMB]) {
   wait_vmcnt<WAIT>();
   lds_barrier();
-  if (ISSUE) issue_i4<ROWS, NMT>(As, rowp, c0, c1, s0, s1, i + 2, K, wave, lane, wn2);
+  if (ISSUE) issue_i4<ROWS, NMT, NT>(As, rowp, c0, c1, s0, s1, i + 2, K, wave, lane, wn2);
   mma_i4<NMT>(As + (i % kDepthI4) * I4Tile<ROWS>::kStage, lane, wb, acc0, acc1);
 }
 
 // The group loop: unrolled by three (one weight buffer per position), the last
 // two to four groups written out so that every wait count is exact.
-template <int ROWS, int NMT>
+template <int ROWS, int NMT, bool NT>
 __device__ __forceinline__ void loop_i4(char* As, const uint16_t* const (&rowp)[I4Tile<ROWS>::kNI], const uint8_t* c0,
                                         const uint8_t* c1, const uint16_t* s0, const uint16_t* s1, int K, int tid,
                                         f32x4 (&acc0)[I4Tile<ROWS>::kMB], f32x4 (&acc1)[I4Tile<ROWS>::kMB]) {
@@ -453,33 +463,33 @@ __device__ __forceinline__ void loop_i4(char* As, const uint16_t* const (&rowp)[
   const int lane = tid & 63, wave = tid >> 6;
   const int n = (K + kKS - 1) / kKS;
   WGroup w0, w1, w2;
-  issue_i4<ROWS, NMT>(As, rowp, c0, c1, s0, s1, 0, K, wave, lane, w0);
+  issue_i4<ROWS, NMT, NT>(As, rowp, c0, c1, s0, s1, 0, K, wave, lane, w0);
   if (n == 1) {
-    step_i4<ROWS, NMT, false, 0>(As, rowp, c0, c1, s0, s1, 0, K, wave, lane, w0, w2, acc0, acc1);
+    step_i4<ROWS, NMT, NT, false, 0>(As, rowp, c0, c1, s0, s1, 0, K, wave, lane, w0, w2, acc0, acc1);
     return;
   }
-  issue_i4<ROWS, NMT>(As, rowp, c0, c1, s0, s1, 1, K, wave, lane, w1);
+  issue_i4<ROWS, NMT, NT>(As, rowp, c0, c1, s0, s1, 1, K, wave, lane, w1);
   int i = 0;
   for (; i + 5 <= n; i += 3) {
-    step_i4<ROWS, NMT, true, kW>(As, rowp, c0, c1, s0, s1, i, K, wave, lane, w0, w2, acc0, acc1);
-    step_i4<ROWS, NMT, true, kW>(As, rowp, c0, c1, s0, s1, i + 1, K, wave, lane, w1, w0, acc0, acc1);
-    step_i4<ROWS, NMT, true, kW>(As, rowp, c0, c1, s0, s1, i + 2, K, wave, lane, w2, w1, acc0, acc1);
+    step_i4<ROWS, NMT, NT, true, kW>(As, rowp, c0, c1, s0, s1, i, K, wave, lane, w0, w2, acc0, acc1);
+    step_i4<ROWS, NMT, NT, true, kW>(As, rowp, c0, c1, s0, s1, i + 1, K, wave, lane, w1, w0, acc0, acc1);
+    step_i4<ROWS, NMT, NT, true, kW>(As, rowp, c0, c1, s0, s1, i + 2, K, wave, lane, w2, w1, acc0, acc1);
   }
   switch (n - i) {
     case 2:
-      step_i4<ROWS, NMT, false, kW>(As, rowp, c0, c1, s0, s1, i, K, wave, lane, w0, w2, acc0, acc1);
-      step_i4<ROWS, NMT, false, 0>(As, rowp, c0, c1, s0, s1, i + 1, K, wave, lane, w1, w0, acc0, acc1);
+      step_i4<ROWS, NMT, NT, false, kW>(As, rowp, c0, c1, s0, s1, i, K, wave, lane, w0, w2, acc0, acc1);
+      step_i4<ROWS, NMT, NT, false, 0>(As, rowp, c0, c1, s0, s1, i + 1, K, wave, lane, w1, w0, acc0, acc1);
       break;
     case 3:
-      step_i4<ROWS, NMT, true, kW>(As, rowp, c0, c1, s0, s1, i, K, wave, lane, w0, w2, acc0, acc1);
-      step_i4<ROWS, NMT, false, kW>(As, rowp, c0, c1, s0, s1, i + 1, K, wave, lane, w1, w0, acc0, acc1);
-      step_i4<ROWS, NMT, false, 0>(As, rowp, c0, c1, s0, s1, i + 2, K, wave, lane, w2, w1, acc0, acc1);
+      step_i4<ROWS, NMT, NT, true, kW>(As, rowp, c0, c1, s0, s1, i, K, wave, lane, w0, w2, acc0, acc1);
+      step_i4<ROWS, NMT, NT, false, kW>(As, rowp, c0, c1, s0, s1, i + 1, K, wave, lane, w1, w0, acc0, acc1);
+      step_i4<ROWS, NMT, NT, false, 0>(As, rowp, c0, c1, s0, s1, i + 2, K, wave, lane, w2, w1, acc0, acc1);
       break;
     default:  // 4
-      step_i4<ROWS, NMT, true, kW>(As, rowp, c0, c1, s0, s1, i, K, wave, lane, w0, w2, acc0, acc1);
-      step_i4<ROWS, NMT, true, kW>(As, rowp, c0, c1, s0, s1, i + 1, K, wave, lane, w1, w0, acc0, acc1);
-      step_i4<ROWS, NMT, false, kW>(As, rowp, c0, c1, s0, s1, i + 2, K, wave, lane, w2, w1, acc0, acc1);
-      step_i4<ROWS, NMT, false, 0>(As, rowp, c0, c1, s0, s1, i + 3, K, wave, lane, w0, w2, acc0, acc1);
+      step_i4<ROWS, NMT, NT, true, kW>(As, rowp, c0, c1, s0, s1, i, K, wave, lane, w0, w2, acc0, acc1);
+      step_i4<ROWS, NMT, NT, true, kW>(As, rowp, c0, c1, s0, s1, i + 1, K, wave, lane, w1, w0, acc0, acc1);
+      step_i4<ROWS, NMT, NT, false, kW>(As, rowp, c0, c1, s0, s1, i + 2, K, wave, lane, w2, w1, acc0, acc1);
+      step_i4<ROWS, NMT, NT, false, 0>(As, rowp, c0, c1, s0, s1, i + 3, K, wave, lane, w0, w2, acc0, acc1);
       break;
   }
 }
@@ -487,7 +497,7 @@ __device__ __forceinline__ void loop_i4(char* As, const uint16_t* const (&rowp)[
 // Packed-weight grouped GEMMs: the bf16 kernels' mapping and activation path,
 // int4 weights widened exactly to fp16 in registers. gate_up writes the gated
 // activation as fp16, down its fp32 sums as bf16.
-template <bool GATE_UP, int ROWS>
+template <bool GATE_UP, int ROWS, bool NT>
 __device__ __forceinline__ void i4p_body(const GemmArgs& a, const Tile& tl, char* As) {
   constexpr int MB = I4Tile<ROWS>::kMB, NI = I4Tile<ROWS>::kNI;
   const int F = a.F, D = a.D;
@@ -532,15 +542,15 @@ __device__ __forceinline__ void i4p_body(const GemmArgs& a, const Tile& tl, char
   }
   if constexpr (MB == 2) {
     if (nmt == 1)
-      loop_i4<ROWS, 1>(As, rowp, c0, c1, s0, s1, K, tid, acc0, acc1);
+      loop_i4<ROWS, 1, NT>(As, rowp, c0, c1, s0, s1, K, tid, acc0, acc1);
     else
-      loop_i4<ROWS, 2>(As, rowp, c0, c1, s0, s1, K, tid, acc0, acc1);
+      loop_i4<ROWS, 2, NT>(As, rowp, c0, c1, s0, s1, K, tid, acc0, acc1);
   } else {
     switch (nmt) {
-      case 1: loop_i4<ROWS, 1>(As, rowp, c0, c1, s0, s1, K, tid, acc0, acc1); break;
-      case 2: loop_i4<ROWS, 2>(As, rowp, c0, c1, s0, s1, K, tid, acc0, acc1); break;
-      case 3: loop_i4<ROWS, 3>(As, rowp, c0, c1, s0, s1, K, tid, acc0, acc1); break;
-      default: loop_i4<ROWS, 4>(As, rowp, c0, c1, s0, s1, K, tid, acc0, acc1); break;
+      case 1: loop_i4<ROWS, 1, NT>(As, rowp, c0, c1, s0, s1, K, tid, acc0, acc1); break;
+      case 2: loop_i4<ROWS, 2, NT>(As, rowp, c0, c1, s0, s1, K, tid, acc0, acc1); break;
+      case 3: loop_i4<ROWS, 3, NT>(As, rowp, c0, c1, s0, s1, K, tid, acc0, acc1); break;
+      default: loop_i4<ROWS, 4, NT>(As, rowp, c0, c1, s0, s1, K, tid, acc0, acc1); break;
     }
   }
 
@@ -565,22 +575,31 @@ __device__ __forceinline__ void i4p_body(const GemmArgs& a, const Tile& tl, char
   }
 }
 
+// One task: weights past the caches when the expert has one tile only.
+template <bool GATE_UP, int ROWS>
+__device__ __forceinline__ void i4p_task(const FusedGemmArgs& f, const GemmArgs& a, const Tile& tl, char* As) {
+  if ((f.counts[tl.e] + ROWS - 1) / ROWS > 1)
+    i4p_body<GATE_UP, ROWS, false>(a, tl, As);
+  else
+    i4p_body<GATE_UP, ROWS, true>(a, tl, As);
+}
+
 // Both packed GEMMs in one launch (the task logic of fused_tasks): 64-row
 // tiles at two workgroups per CU, or 32-row tiles at three.
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))) void k_gemm_i4p_fused(
     FusedGemmArgs f) {
   __shared__ __attribute__((aligned(16))) char As[kDepthI4 * I4Tile<kTileRows>::kStage];
   fused_tasks(
-      f, [&](const Tile& tl) { i4p_body<true, kTileRows>(f.gu, tl, As); },
-      [&](const Tile& tl) { i4p_body<false, kTileRows>(f.dn, tl, As); });
+      f, [&](const Tile& tl) { i4p_task<true, kTileRows>(f, f.gu, tl, As); },
+      [&](const Tile& tl) { i4p_task<false, kTileRows>(f, f.dn, tl, As); });
 }
 
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3, 3))) void k_gemm_i4p_fused_short(
     FusedGemmArgs f) {
   __shared__ __attribute__((aligned(16))) char As[kDepthI4 * I4Tile<kShortRows>::kStage];
   fused_tasks(
-      f, [&](const Tile& tl) { i4p_body<true, kShortRows>(f.gu, tl, As); },
-      [&](const Tile& tl) { i4p_body<false, kShortRows>(f.dn, tl, As); });
+      f, [&](const Tile& tl) { i4p_task<true, kShortRows>(f, f.gu, tl, As); },
+      [&](const Tile& tl) { i4p_task<false, kShortRows>(f, f.dn, tl, As); });
 }
 
 }  // namespace
