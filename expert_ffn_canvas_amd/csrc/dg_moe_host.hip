@@ -85,8 +85,11 @@ Layout plan(const dg_moe_config& c) {
   L.nb[0] = dg::gate_up_blocks((int)F);
   L.nb[1] = dg::down_blocks((int)D);
   // the shortest tiles give the longest queues
-  const int min_rows = (c.expert_w_dtype == DG_I4G128 && (c.flags & DG_MOE_PACK_WEIGHTS)) ? dg::kShortRows
-                                                                                          : dg::kTileRows;
+  // (bf16 experts and int4 read in place never take short tiles)
+  const int min_rows =
+      (c.expert_w_dtype == DG_BF16 || (c.expert_w_dtype == DG_I4G128 && !(c.flags & DG_MOE_PACK_WEIGHTS)))
+          ? dg::kTileRows
+          : dg::kShortRows;
   for (int g = 0; g < 2; ++g) L.qmax[g] = dg::max_queue_len((int)T, (int)K, (int)E, L.nb[g], min_rows);
   size_t off = 0;
   auto take = [&](size_t bytes) {
@@ -446,8 +449,8 @@ static dg_status run_forward(dg_moe_handle hd, const void* x, void* out, int32_t
   pa.E = c.n_experts;
   const bool fused = fuses_gemms(c);
   const int tile_rows = c.expert_w_dtype == DG_BF16 ? dg::bf16_tile_rows(T, c.top_k, c.n_experts)
-                        : (i4 && fused)             ? dg::i4_tile_rows(T, c.top_k, c.n_experts)
-                                                    : dg::kTileRows;
+                        : (i4 && !fused)            ? dg::kTileRows
+                                                    : dg::quant_tile_rows(T, c.top_k, c.n_experts);
   const bool tall = tile_rows > dg::kTileRows;
   pa.tile_rows = tile_rows;
   pa.deal = fused ? dg::kDealBalanced : tall ? dg::kDealExperts : dg::kDealUnits;
@@ -495,9 +498,9 @@ static dg_status run_forward(dg_moe_handle hd, const void* x, void* out, int32_t
     fa.nb_gate_up = pa.nb[0];
     fa.dev_flags = ra.dev_flags;
     fa.counts = pa.counts;
-    e = mx4  ? dg::launch_gemm_fused_mx4(fa, stream, ev(3))
-        : mx8 ? dg::launch_gemm_fused_mx8(fa, stream, ev(3))
-        : q8 ? dg::launch_gemm_fused_q8(fa, stream, ev(3))
+    e = mx4  ? dg::launch_gemm_fused_mx4(fa, tile_rows, stream, ev(3))
+        : mx8 ? dg::launch_gemm_fused_mx8(fa, tile_rows, stream, ev(3))
+        : q8 ? dg::launch_gemm_fused_q8(fa, tile_rows, stream, ev(3))
         : i4 ? dg::launch_gemm_fused_i4(fa, tile_rows, stream, ev(3))
              : dg::launch_gemm_fused(fa, tile_rows, stream, ev(3));
     if (e != hipSuccess) return hip_fail(e, "GEMM launch");

@@ -75,16 +75,24 @@ constexpr int kMLoads = 2 * (BITS / 4) + 2;
 
 // Step `step`'s codes and scales; consecutive steps are `cstep` and `sstep`
 // bytes apart.
-template <int BITS>
+// NT: past the caches (an expert in one tile reads its weights once); else
+// normal loads, so that the expert's other tiles find them in L2.
+template <int BITS, bool NT>
 __device__ __forceinline__ void load_m(const uint8_t* c0, const uint8_t* c1, const uint8_t* s0, const uint8_t* s1,
                                        int step, size_t cstep, size_t sstep, MPanels<BITS>& p) {
+  auto ld16 = [](const uint8_t* q) {
+    return NT ? ld_stream(reinterpret_cast<const u32x4*>(q)) : *reinterpret_cast<const u32x4*>(q);
+  };
+  auto ld4 = [](const uint8_t* q) {
+    return NT ? ld_stream(reinterpret_cast<const uint32_t*>(q)) : *reinterpret_cast<const uint32_t*>(q);
+  };
 #pragma unroll
   for (int h = 0; h < BITS / 4; ++h) {
-    p.c0[h] = ld_stream(reinterpret_cast<const u32x4*>(c0 + (size_t)step * cstep + 1024 * h));
-    p.c1[h] = ld_stream(reinterpret_cast<const u32x4*>(c1 + (size_t)step * cstep + 1024 * h));
+    p.c0[h] = ld16(c0 + (size_t)step * cstep + 1024 * h);
+    p.c1[h] = ld16(c1 + (size_t)step * cstep + 1024 * h);
   }
-  p.s0 = ld_stream(reinterpret_cast<const uint32_t*>(s0 + (size_t)step * sstep));
-  p.s1 = ld_stream(reinterpret_cast<const uint32_t*>(s1 + (size_t)step * sstep));
+  p.s0 = ld4(s0 + (size_t)step * sstep);
+  p.s1 = ld4(s1 + (size_t)step * sstep);
 }
 
 // 8 E2M1 codes of one dword (natural order, even input in the low nibble)
@@ -131,9 +139,9 @@ __device__ __forceinline__ float mx_scale(uint32_t s, int j) {
 }
 
 // NS blocks of one step, each one MFMA K step of 32 inputs.
-template <int BITS, int NMT, int NS>
-__device__ __forceinline__ void mma_mx(const char* stage, int lane, const MPanels<BITS>& p, f32x4 (&acc0)[kBMT],
-                                       f32x4 (&acc1)[kBMT]) {
+template <int BITS, int NMT, int NS, int MB>
+__device__ __forceinline__ void mma_mx(const char* stage, int lane, const MPanels<BITS>& p, f32x4 (&acc0)[MB],
+                                       f32x4 (&acc1)[MB]) {
   const int g = lane >> 4, m = lane & 15;
 #pragma unroll
   for (int j = 0; j < NS; ++j) {
@@ -164,44 +172,48 @@ struct MStream {
 // One step, as in the bf16 kernels: DMA of the next step's activation rows,
 // then its codes and scales, then the MFMAs of step `it` (NSP blocks) from
 // `cur`; the wait lets the weight loads fly.
-template <int BITS, int NMT, int NS, int NSP>
-__device__ __forceinline__ void mstep(char* As, const uint16_t* const (&rowp)[kDmaInstr], const MStream& w, int k1,
-                                      int it, int wave, int lane, const MPanels<BITS>& cur, MPanels<BITS>& nxt,
-                                      f32x4 (&acc0)[kBMT], f32x4 (&acc1)[kBMT]) {
-  dma_a<NMT, NS * 4>(As + ((it + 1) & 1) * kStageBytes, rowp, k1, wave, lane);
+template <int BITS, int ROWS, bool NT, int NMT, int NS, int NSP>
+__device__ __forceinline__ void mstep(char* As, const uint16_t* const (&rowp)[dma_per_wave(ROWS, kWaves)],
+                                      const MStream& w, int k1, int it, int wave, int lane, const MPanels<BITS>& cur,
+                                      MPanels<BITS>& nxt, f32x4 (&acc0)[ROWS / 16], f32x4 (&acc1)[ROWS / 16]) {
+  constexpr int kSB = ROWS * kRowBytes;
+  dma_a<NMT, NS * 4>(As + ((it + 1) & 1) * kSB, rowp, k1, wave, lane);
   __builtin_amdgcn_sched_barrier(0);
-  load_m<BITS>(w.c0, w.c1, w.s0, w.s1, it + 1, w.cstep, w.sstep, nxt);
+  load_m<BITS, NT>(w.c0, w.c1, w.s0, w.s1, it + 1, w.cstep, w.sstep, nxt);
   __builtin_amdgcn_sched_barrier(0);
-  mma_mx<BITS, NMT, NSP>(As + (it & 1) * kStageBytes, lane, cur, acc0, acc1);
+  mma_mx<BITS, NMT, NSP>(As + (it & 1) * kSB, lane, cur, acc0, acc1);
   wait_vmcnt<kMLoads<BITS>>();
   lds_barrier();
 }
 
-template <int BITS, int NMT>
-__device__ __forceinline__ void mfinish(char* As, const uint16_t* const (&rowp)[kDmaInstr], const MStream& w,
-                                        int nfull, int ntail, int wave, int lane, const MPanels<BITS>& cur,
-                                        MPanels<BITS>& nxt, f32x4 (&acc0)[kBMT], f32x4 (&acc1)[kBMT]) {
+template <int BITS, int ROWS, bool NT, int NMT>
+__device__ __forceinline__ void mfinish(char* As, const uint16_t* const (&rowp)[dma_per_wave(ROWS, kWaves)],
+                                        const MStream& w, int nfull, int ntail, int wave, int lane,
+                                        const MPanels<BITS>& cur, MPanels<BITS>& nxt, f32x4 (&acc0)[ROWS / 16],
+                                        f32x4 (&acc1)[ROWS / 16]) {
+  constexpr int kSB = ROWS * kRowBytes;
   const int last = nfull - 1;
   if (ntail == 0) {
-    mma_mx<BITS, NMT, 4>(As + (last & 1) * kStageBytes, lane, cur, acc0, acc1);
+    mma_mx<BITS, NMT, 4>(As + (last & 1) * kSB, lane, cur, acc0, acc1);
   } else {  // one 64-wide step remains (K % 128 == 64): its two blocks
-    mstep<BITS, NMT, 2, 4>(As, rowp, w, nfull * kKS, last, wave, lane, cur, nxt, acc0, acc1);
+    mstep<BITS, ROWS, NT, NMT, 2, 4>(As, rowp, w, nfull * kKS, last, wave, lane, cur, nxt, acc0, acc1);
     wait_vmcnt<0>();
-    mma_mx<BITS, NMT, 2>(As + (nfull & 1) * kStageBytes, lane, nxt, acc0, acc1);
+    mma_mx<BITS, NMT, 2>(As + (nfull & 1) * kSB, lane, nxt, acc0, acc1);
   }
 }
 
 // The K loop of one tile (K a multiple of 64), the bf16 kernels' ping-pong.
-template <int BITS, int NMT>
-__device__ __forceinline__ void mloop(char* As, const uint16_t* const (&rowp)[kDmaInstr], const MStream& w, int K,
-                                      int tid, f32x4 (&acc0)[kBMT], f32x4 (&acc1)[kBMT]) {
+template <int BITS, int ROWS, bool NT, int NMT>
+__device__ __forceinline__ void mloop(char* As, const uint16_t* const (&rowp)[dma_per_wave(ROWS, kWaves)],
+                                      const MStream& w, int K, int tid, f32x4 (&acc0)[ROWS / 16],
+                                      f32x4 (&acc1)[ROWS / 16]) {
   const int lane = tid & 63, wave = tid >> 6;
   const int nfull = K / kKS;
   const int ntail = (K - nfull * kKS) / 32;
   MPanels<BITS> p0, p1;
   if (nfull == 0) {  // K = 64
     dma_a<NMT, 8>(As, rowp, 0, wave, lane);
-    load_m<BITS>(w.c0, w.c1, w.s0, w.s1, 0, w.cstep, w.sstep, p0);
+    load_m<BITS, NT>(w.c0, w.c1, w.s0, w.s1, 0, w.cstep, w.sstep, p0);
     wait_vmcnt<0>();
     lds_barrier();
     mma_mx<BITS, NMT, 2>(As, lane, p0, acc0, acc1);
@@ -209,26 +221,27 @@ __device__ __forceinline__ void mloop(char* As, const uint16_t* const (&rowp)[kD
   }
   dma_a<NMT, kSegs>(As, rowp, 0, wave, lane);
   __builtin_amdgcn_sched_barrier(0);
-  load_m<BITS>(w.c0, w.c1, w.s0, w.s1, 0, w.cstep, w.sstep, p0);
+  load_m<BITS, NT>(w.c0, w.c1, w.s0, w.s1, 0, w.cstep, w.sstep, p0);
   wait_vmcnt<kMLoads<BITS>>();
   lds_barrier();
   int it = 0;
   for (; it + 2 < nfull; it += 2) {
-    mstep<BITS, NMT, 4, 4>(As, rowp, w, (it + 1) * kKS, it, wave, lane, p0, p1, acc0, acc1);
-    mstep<BITS, NMT, 4, 4>(As, rowp, w, (it + 2) * kKS, it + 1, wave, lane, p1, p0, acc0, acc1);
+    mstep<BITS, ROWS, NT, NMT, 4, 4>(As, rowp, w, (it + 1) * kKS, it, wave, lane, p0, p1, acc0, acc1);
+    mstep<BITS, ROWS, NT, NMT, 4, 4>(As, rowp, w, (it + 2) * kKS, it + 1, wave, lane, p1, p0, acc0, acc1);
   }
   if (it + 2 == nfull) {
-    mstep<BITS, NMT, 4, 4>(As, rowp, w, (it + 1) * kKS, it, wave, lane, p0, p1, acc0, acc1);
-    mfinish<BITS, NMT>(As, rowp, w, nfull, ntail, wave, lane, p1, p0, acc0, acc1);
+    mstep<BITS, ROWS, NT, NMT, 4, 4>(As, rowp, w, (it + 1) * kKS, it, wave, lane, p0, p1, acc0, acc1);
+    mfinish<BITS, ROWS, NT, NMT>(As, rowp, w, nfull, ntail, wave, lane, p1, p0, acc0, acc1);
   } else {
-    mfinish<BITS, NMT>(As, rowp, w, nfull, ntail, wave, lane, p0, p1, acc0, acc1);
+    mfinish<BITS, ROWS, NT, NMT>(As, rowp, w, nfull, ntail, wave, lane, p0, p1, acc0, acc1);
   }
 }
 
 // The product of one task: gate_up writes the gated activation as bf16 (the
 // down GEMM's bf16 operand), down its fp32 sums as bf16.
-template <int BITS, bool GATE_UP>
+template <int BITS, bool GATE_UP, int ROWS, bool NT>
 __device__ __forceinline__ void mx_body(const GemmArgs& a, const Tile& tl, char* As) {
+  constexpr int MB = ROWS / 16, NI = dma_per_wave(ROWS, kWaves);
   const int F = a.F, D = a.D;
   const int K = GATE_UP ? D : F;
   const int nks = (K + kKS - 1) / kKS;
@@ -239,9 +252,9 @@ __device__ __forceinline__ void mx_body(const GemmArgs& a, const Tile& tl, char*
 
   // source row of each DMA instruction of this lane (rows past the tile re-read
   // its last row; their results are never stored)
-  const uint16_t* rowp[kDmaInstr];
+  const uint16_t* rowp[NI];
 #pragma unroll
-  for (int i = 0; i < kDmaInstr; ++i) {
+  for (int i = 0; i < NI; ++i) {
     const int r = min(kDmaRows * (wave + kWaves * i) + lane / kSegs, tl.mc - 1);
     rowp[i] = GATE_UP ? a.h + (size_t)(a.sorted_slot[tl.row0 + r] / a.K) * D : a.act + (size_t)(tl.row0 + r) * F;
   }
@@ -269,21 +282,28 @@ __device__ __forceinline__ void mx_body(const GemmArgs& a, const Tile& tl, char*
   w.cstep = (size_t)np * kCB;
   w.sstep = (size_t)np * kMScaleBytes;
 
-  f32x4 acc0[kBMT], acc1[kBMT];
+  f32x4 acc0[MB], acc1[MB];
 #pragma unroll
-  for (int i = 0; i < kBMT; ++i) {
+  for (int i = 0; i < MB; ++i) {
     acc0[i] = f32x4{0.f, 0.f, 0.f, 0.f};
     acc1[i] = f32x4{0.f, 0.f, 0.f, 0.f};
   }
-  switch (nmt) {
-    case 1: mloop<BITS, 1>(As, rowp, w, K, tid, acc0, acc1); break;
-    case 2: mloop<BITS, 2>(As, rowp, w, K, tid, acc0, acc1); break;
-    case 3: mloop<BITS, 3>(As, rowp, w, K, tid, acc0, acc1); break;
-    default: mloop<BITS, 4>(As, rowp, w, K, tid, acc0, acc1); break;
+  if constexpr (MB == 2) {
+    if (nmt == 1)
+      mloop<BITS, ROWS, NT, 1>(As, rowp, w, K, tid, acc0, acc1);
+    else
+      mloop<BITS, ROWS, NT, 2>(As, rowp, w, K, tid, acc0, acc1);
+  } else {
+    switch (nmt) {
+      case 1: mloop<BITS, ROWS, NT, 1>(As, rowp, w, K, tid, acc0, acc1); break;
+      case 2: mloop<BITS, ROWS, NT, 2>(As, rowp, w, K, tid, acc0, acc1); break;
+      case 3: mloop<BITS, ROWS, NT, 3>(As, rowp, w, K, tid, acc0, acc1); break;
+      default: mloop<BITS, ROWS, NT, 4>(As, rowp, w, K, tid, acc0, acc1); break;
+    }
   }
 
 #pragma unroll
-  for (int mt = 0; mt < kBMT; ++mt) {
+  for (int mt = 0; mt < MB; ++mt) {
     if (mt < nmt) {
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
@@ -302,22 +322,47 @@ __device__ __forceinline__ void mx_body(const GemmArgs& a, const Tile& tl, char*
   }
 }
 
-// Both GEMMs in one launch (the task logic of fused_tasks), three workgroups
-// per CU as the bf16 kernels (162 registers for MXFP8, no spills).
+// One task: weights past the caches when the expert has one tile only.
+template <int BITS, bool GATE_UP, int ROWS>
+__device__ __forceinline__ void mx_task(const FusedGemmArgs& f, const GemmArgs& a, const Tile& tl, char* As) {
+  if ((f.counts[tl.e] + ROWS - 1) / ROWS > 1)
+    mx_body<BITS, GATE_UP, ROWS, false>(a, tl, As);
+  else
+    mx_body<BITS, GATE_UP, ROWS, true>(a, tl, As);
+}
+
+// Both GEMMs in one launch (the task logic of fused_tasks): 64-row tiles at
+// three workgroups per CU as the bf16 kernels (162 registers for MXFP8, no
+// spills), or 32-row tiles at four.
+template <int BITS, int ROWS>
+__device__ __forceinline__ void mx_fused(const FusedGemmArgs& f, char* As) {
+  fused_tasks(
+      f, [&](const Tile& tl) { mx_task<BITS, true, ROWS>(f, f.gu, tl, As); },
+      [&](const Tile& tl) { mx_task<BITS, false, ROWS>(f, f.dn, tl, As); });
+}
+
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3, 3))) void k_gemm_mx4_fused(
     FusedGemmArgs f) {
-  __shared__ __attribute__((aligned(16))) char As[2 * kStageBytes];
-  fused_tasks(
-      f, [&](const Tile& tl) { mx_body<4, true>(f.gu, tl, As); },
-      [&](const Tile& tl) { mx_body<4, false>(f.dn, tl, As); });
+  __shared__ __attribute__((aligned(16))) char As[2 * kTileRows * kRowBytes];
+  mx_fused<4, kTileRows>(f, As);
 }
 
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3, 3))) void k_gemm_mx8_fused(
     FusedGemmArgs f) {
-  __shared__ __attribute__((aligned(16))) char As[2 * kStageBytes];
-  fused_tasks(
-      f, [&](const Tile& tl) { mx_body<8, true>(f.gu, tl, As); },
-      [&](const Tile& tl) { mx_body<8, false>(f.dn, tl, As); });
+  __shared__ __attribute__((aligned(16))) char As[2 * kTileRows * kRowBytes];
+  mx_fused<8, kTileRows>(f, As);
+}
+
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4, 4))) void k_gemm_mx4_fused_short(
+    FusedGemmArgs f) {
+  __shared__ __attribute__((aligned(16))) char As[2 * kShortRows * kRowBytes];
+  mx_fused<4, kShortRows>(f, As);
+}
+
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4, 4))) void k_gemm_mx8_fused_short(
+    FusedGemmArgs f) {
+  __shared__ __attribute__((aligned(16))) char As[2 * kShortRows * kRowBytes];
+  mx_fused<8, kShortRows>(f, As);
 }
 
 // One wave per packed block (e, s, p); lane l = n + 16 g gathers its row's
@@ -383,12 +428,14 @@ hipError_t launch_pack_mx8(const uint8_t* blocks, uint8_t* pcodes, uint8_t* psca
   return hipGetLastError();
 }
 
-hipError_t launch_gemm_fused_mx4(const FusedGemmArgs& f, hipStream_t stream, const KernelEvents* ev) {
-  return launch_kernel(k_gemm_mx4_fused, dim3(kQueues * (f.gu.qmax + f.dn.qmax)), dim3(kThreads), stream, ev, f);
+hipError_t launch_gemm_fused_mx4(const FusedGemmArgs& f, int tile_rows, hipStream_t stream, const KernelEvents* ev) {
+  return launch_kernel(tile_rows == kShortRows ? k_gemm_mx4_fused_short : k_gemm_mx4_fused,
+                       dim3(kQueues * (f.gu.qmax + f.dn.qmax)), dim3(kThreads), stream, ev, f);
 }
 
-hipError_t launch_gemm_fused_mx8(const FusedGemmArgs& f, hipStream_t stream, const KernelEvents* ev) {
-  return launch_kernel(k_gemm_mx8_fused, dim3(kQueues * (f.gu.qmax + f.dn.qmax)), dim3(kThreads), stream, ev, f);
+hipError_t launch_gemm_fused_mx8(const FusedGemmArgs& f, int tile_rows, hipStream_t stream, const KernelEvents* ev) {
+  return launch_kernel(tile_rows == kShortRows ? k_gemm_mx8_fused_short : k_gemm_mx8_fused,
+                       dim3(kQueues * (f.gu.qmax + f.dn.qmax)), dim3(kThreads), stream, ev, f);
 }
 
 }  // namespace dg

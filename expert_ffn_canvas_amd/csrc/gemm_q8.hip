@@ -28,8 +28,9 @@
 // enters as exactly q * d, as in the oracle.
 //
 // Mapping, activation path and work distribution as in the bf16 kernels (64-row
-// tiles, 4 waves, two 16-row panels per wave, activation rows staged in LDS by
-// DMA, both GEMMs in one launch from the per-XCD queues).
+// tiles, or 32-row tiles where experts hold few rows; 4 waves, two 16-row
+// panels per wave, activation rows staged in LDS by DMA, both GEMMs in one
+// launch from the per-XCD queues).
 #include "dg_common.h"
 #include "gemm_common.h"
 #include "launch.h"
@@ -52,16 +53,25 @@ struct QPanels {
 
 // Step `step`'s codes and scales; consecutive steps are `cstep` bytes and
 // `sstep` scales apart.
+// NT: past the caches (an expert in one tile reads its weights once); else
+// normal loads, so that the expert's other tiles find them in L2.
+template <bool NT>
 __device__ __forceinline__ void load_q(const uint8_t* c0, const uint8_t* c1, const uint16_t* s0, const uint16_t* s1,
                                        int step, size_t cstep, size_t sstep, QPanels& p) {
   const uint8_t* a = c0 + (size_t)step * cstep;
   const uint8_t* b = c1 + (size_t)step * cstep;
-  p.c0[0] = ld_stream(reinterpret_cast<const u32x4*>(a));
-  p.c0[1] = ld_stream(reinterpret_cast<const u32x4*>(a + 1024));
-  p.c1[0] = ld_stream(reinterpret_cast<const u32x4*>(b));
-  p.c1[1] = ld_stream(reinterpret_cast<const u32x4*>(b + 1024));
-  const uint64_t v0 = ld_stream(reinterpret_cast<const uint64_t*>(s0 + (size_t)step * sstep));
-  const uint64_t v1 = ld_stream(reinterpret_cast<const uint64_t*>(s1 + (size_t)step * sstep));
+  auto ld16 = [](const uint8_t* q) {
+    return NT ? ld_stream(reinterpret_cast<const u32x4*>(q)) : *reinterpret_cast<const u32x4*>(q);
+  };
+  auto ld8 = [](const uint16_t* q) {
+    return NT ? ld_stream(reinterpret_cast<const uint64_t*>(q)) : *reinterpret_cast<const uint64_t*>(q);
+  };
+  p.c0[0] = ld16(a);
+  p.c0[1] = ld16(a + 1024);
+  p.c1[0] = ld16(b);
+  p.c1[1] = ld16(b + 1024);
+  const uint64_t v0 = ld8(s0 + (size_t)step * sstep);
+  const uint64_t v1 = ld8(s1 + (size_t)step * sstep);
   p.s0 = make_uint2((uint32_t)v0, (uint32_t)(v0 >> 32));
   p.s1 = make_uint2((uint32_t)v1, (uint32_t)(v1 >> 32));
 }
@@ -93,9 +103,9 @@ __device__ __forceinline__ float scale_of(const uint2& s, int j) {
 
 // NS blocks of one step: each block's MFMA into a zeroed accumulator, then
 // scaled by the block's d into acc.
-template <int NMT, int NS>
-__device__ __forceinline__ void mma_q8(const char* stage, int lane, const QPanels& p, f32x4 (&acc0)[kBMT],
-                                       f32x4 (&acc1)[kBMT]) {
+template <int NMT, int NS, int MB>
+__device__ __forceinline__ void mma_q8(const char* stage, int lane, const QPanels& p, f32x4 (&acc0)[MB],
+                                       f32x4 (&acc1)[MB]) {
   const int g = lane >> 4, m = lane & 15;
   const f32x4 zero = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
@@ -134,44 +144,47 @@ struct QStream {
 // One step, as in the bf16 kernels: DMA of the next step's activation rows,
 // then its codes and scales, then the MFMAs of step `it` (NSP blocks) from
 // `cur`; the wait lets the six weight loads fly.
-template <int NMT, int NS, int NSP>
-__device__ __forceinline__ void qstep(char* As, const uint16_t* const (&rowp)[kDmaInstr], const QStream& w, int k1,
-                                      int it, int wave, int lane, const QPanels& cur, QPanels& nxt,
-                                      f32x4 (&acc0)[kBMT], f32x4 (&acc1)[kBMT]) {
-  dma_a<NMT, NS * 4>(As + ((it + 1) & 1) * kStageBytes, rowp, k1, wave, lane);
+template <int ROWS, bool NT, int NMT, int NS, int NSP>
+__device__ __forceinline__ void qstep(char* As, const uint16_t* const (&rowp)[dma_per_wave(ROWS, kWaves)],
+                                      const QStream& w, int k1, int it, int wave, int lane, const QPanels& cur,
+                                      QPanels& nxt, f32x4 (&acc0)[ROWS / 16], f32x4 (&acc1)[ROWS / 16]) {
+  constexpr int kSB = ROWS * kRowBytes;
+  dma_a<NMT, NS * 4>(As + ((it + 1) & 1) * kSB, rowp, k1, wave, lane);
   __builtin_amdgcn_sched_barrier(0);
-  load_q(w.c0, w.c1, w.s0, w.s1, it + 1, w.cstep, w.sstep, nxt);
+  load_q<NT>(w.c0, w.c1, w.s0, w.s1, it + 1, w.cstep, w.sstep, nxt);
   __builtin_amdgcn_sched_barrier(0);
-  mma_q8<NMT, NSP>(As + (it & 1) * kStageBytes, lane, cur, acc0, acc1);
+  mma_q8<NMT, NSP>(As + (it & 1) * kSB, lane, cur, acc0, acc1);
   wait_vmcnt<6>();
   lds_barrier();
 }
 
-template <int NMT>
-__device__ __forceinline__ void qfinish(char* As, const uint16_t* const (&rowp)[kDmaInstr], const QStream& w,
-                                        int nfull, int ntail, int wave, int lane, const QPanels& cur, QPanels& nxt,
-                                        f32x4 (&acc0)[kBMT], f32x4 (&acc1)[kBMT]) {
+template <int ROWS, bool NT, int NMT>
+__device__ __forceinline__ void qfinish(char* As, const uint16_t* const (&rowp)[dma_per_wave(ROWS, kWaves)],
+                                        const QStream& w, int nfull, int ntail, int wave, int lane, const QPanels& cur,
+                                        QPanels& nxt, f32x4 (&acc0)[ROWS / 16], f32x4 (&acc1)[ROWS / 16]) {
+  constexpr int kSB = ROWS * kRowBytes;
   const int last = nfull - 1;
   if (ntail == 0) {
-    mma_q8<NMT, 4>(As + (last & 1) * kStageBytes, lane, cur, acc0, acc1);
+    mma_q8<NMT, 4>(As + (last & 1) * kSB, lane, cur, acc0, acc1);
   } else {  // one 64-wide step remains (K % 128 == 64): its two blocks
-    qstep<NMT, 2, 4>(As, rowp, w, nfull * kKS, last, wave, lane, cur, nxt, acc0, acc1);
+    qstep<ROWS, NT, NMT, 2, 4>(As, rowp, w, nfull * kKS, last, wave, lane, cur, nxt, acc0, acc1);
     wait_vmcnt<0>();
-    mma_q8<NMT, 2>(As + (nfull & 1) * kStageBytes, lane, nxt, acc0, acc1);
+    mma_q8<NMT, 2>(As + (nfull & 1) * kSB, lane, nxt, acc0, acc1);
   }
 }
 
 // The K loop of one tile (K a multiple of 64), the bf16 kernels' ping-pong.
-template <int NMT>
-__device__ __forceinline__ void qloop(char* As, const uint16_t* const (&rowp)[kDmaInstr], const QStream& w, int K,
-                                      int tid, f32x4 (&acc0)[kBMT], f32x4 (&acc1)[kBMT]) {
+template <int ROWS, bool NT, int NMT>
+__device__ __forceinline__ void qloop(char* As, const uint16_t* const (&rowp)[dma_per_wave(ROWS, kWaves)],
+                                      const QStream& w, int K, int tid, f32x4 (&acc0)[ROWS / 16],
+                                      f32x4 (&acc1)[ROWS / 16]) {
   const int lane = tid & 63, wave = tid >> 6;
   const int nfull = K / kKS;
   const int ntail = (K - nfull * kKS) / 32;
   QPanels p0, p1;
   if (nfull == 0) {  // K = 64
     dma_a<NMT, 8>(As, rowp, 0, wave, lane);
-    load_q(w.c0, w.c1, w.s0, w.s1, 0, w.cstep, w.sstep, p0);
+    load_q<NT>(w.c0, w.c1, w.s0, w.s1, 0, w.cstep, w.sstep, p0);
     wait_vmcnt<0>();
     lds_barrier();
     mma_q8<NMT, 2>(As, lane, p0, acc0, acc1);
@@ -179,26 +192,27 @@ __device__ __forceinline__ void qloop(char* As, const uint16_t* const (&rowp)[kD
   }
   dma_a<NMT, kSegs>(As, rowp, 0, wave, lane);
   __builtin_amdgcn_sched_barrier(0);
-  load_q(w.c0, w.c1, w.s0, w.s1, 0, w.cstep, w.sstep, p0);
+  load_q<NT>(w.c0, w.c1, w.s0, w.s1, 0, w.cstep, w.sstep, p0);
   wait_vmcnt<6>();
   lds_barrier();
   int it = 0;
   for (; it + 2 < nfull; it += 2) {
-    qstep<NMT, 4, 4>(As, rowp, w, (it + 1) * kKS, it, wave, lane, p0, p1, acc0, acc1);
-    qstep<NMT, 4, 4>(As, rowp, w, (it + 2) * kKS, it + 1, wave, lane, p1, p0, acc0, acc1);
+    qstep<ROWS, NT, NMT, 4, 4>(As, rowp, w, (it + 1) * kKS, it, wave, lane, p0, p1, acc0, acc1);
+    qstep<ROWS, NT, NMT, 4, 4>(As, rowp, w, (it + 2) * kKS, it + 1, wave, lane, p1, p0, acc0, acc1);
   }
   if (it + 2 == nfull) {
-    qstep<NMT, 4, 4>(As, rowp, w, (it + 1) * kKS, it, wave, lane, p0, p1, acc0, acc1);
-    qfinish<NMT>(As, rowp, w, nfull, ntail, wave, lane, p1, p0, acc0, acc1);
+    qstep<ROWS, NT, NMT, 4, 4>(As, rowp, w, (it + 1) * kKS, it, wave, lane, p0, p1, acc0, acc1);
+    qfinish<ROWS, NT, NMT>(As, rowp, w, nfull, ntail, wave, lane, p1, p0, acc0, acc1);
   } else {
-    qfinish<NMT>(As, rowp, w, nfull, ntail, wave, lane, p0, p1, acc0, acc1);
+    qfinish<ROWS, NT, NMT>(As, rowp, w, nfull, ntail, wave, lane, p0, p1, acc0, acc1);
   }
 }
 
 // The product of one task: gate_up writes the gated activation as fp16 (the
 // down GEMM's fp16 operand), down its fp32 sums as bf16.
-template <bool GATE_UP>
+template <bool GATE_UP, int ROWS, bool NT>
 __device__ __forceinline__ void q8_body(const GemmArgs& a, const Tile& tl, char* As) {
+  constexpr int MB = ROWS / 16, NI = dma_per_wave(ROWS, kWaves);
   const int F = a.F, D = a.D;
   const int K = GATE_UP ? D : F;
   const int nks = (K + kKS - 1) / kKS;
@@ -209,9 +223,9 @@ __device__ __forceinline__ void q8_body(const GemmArgs& a, const Tile& tl, char*
 
   // source row of each DMA instruction of this lane (rows past the tile re-read
   // its last row; their results are never stored)
-  const uint16_t* rowp[kDmaInstr];
+  const uint16_t* rowp[NI];
 #pragma unroll
-  for (int i = 0; i < kDmaInstr; ++i) {
+  for (int i = 0; i < NI; ++i) {
     const int r = min(kDmaRows * (wave + kWaves * i) + lane / kSegs, tl.mc - 1);
     rowp[i] = GATE_UP ? a.h + (size_t)(a.sorted_slot[tl.row0 + r] / a.K) * D : a.act + (size_t)(tl.row0 + r) * F;
   }
@@ -238,21 +252,28 @@ __device__ __forceinline__ void q8_body(const GemmArgs& a, const Tile& tl, char*
   w.cstep = (size_t)np * kQCodeBytes;
   w.sstep = (size_t)np * kQScales;
 
-  f32x4 acc0[kBMT], acc1[kBMT];
+  f32x4 acc0[MB], acc1[MB];
 #pragma unroll
-  for (int i = 0; i < kBMT; ++i) {
+  for (int i = 0; i < MB; ++i) {
     acc0[i] = f32x4{0.f, 0.f, 0.f, 0.f};
     acc1[i] = f32x4{0.f, 0.f, 0.f, 0.f};
   }
-  switch (nmt) {
-    case 1: qloop<1>(As, rowp, w, K, tid, acc0, acc1); break;
-    case 2: qloop<2>(As, rowp, w, K, tid, acc0, acc1); break;
-    case 3: qloop<3>(As, rowp, w, K, tid, acc0, acc1); break;
-    default: qloop<4>(As, rowp, w, K, tid, acc0, acc1); break;
+  if constexpr (MB == 2) {
+    if (nmt == 1)
+      qloop<ROWS, NT, 1>(As, rowp, w, K, tid, acc0, acc1);
+    else
+      qloop<ROWS, NT, 2>(As, rowp, w, K, tid, acc0, acc1);
+  } else {
+    switch (nmt) {
+      case 1: qloop<ROWS, NT, 1>(As, rowp, w, K, tid, acc0, acc1); break;
+      case 2: qloop<ROWS, NT, 2>(As, rowp, w, K, tid, acc0, acc1); break;
+      case 3: qloop<ROWS, NT, 3>(As, rowp, w, K, tid, acc0, acc1); break;
+      default: qloop<ROWS, NT, 4>(As, rowp, w, K, tid, acc0, acc1); break;
+    }
   }
 
 #pragma unroll
-  for (int mt = 0; mt < kBMT; ++mt) {
+  for (int mt = 0; mt < MB; ++mt) {
     if (mt < nmt) {
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
@@ -272,13 +293,31 @@ __device__ __forceinline__ void q8_body(const GemmArgs& a, const Tile& tl, char*
   }
 }
 
-// Both GEMMs in one launch (the task logic of fused_tasks), two workgroups
-// per CU.
+// One task: weights past the caches when the expert has one tile only.
+template <bool GATE_UP, int ROWS>
+__device__ __forceinline__ void q8_task(const FusedGemmArgs& f, const GemmArgs& a, const Tile& tl, char* As) {
+  if ((f.counts[tl.e] + ROWS - 1) / ROWS > 1)
+    q8_body<GATE_UP, ROWS, false>(a, tl, As);
+  else
+    q8_body<GATE_UP, ROWS, true>(a, tl, As);
+}
+
+// Both GEMMs in one launch (the task logic of fused_tasks): 64-row tiles at
+// two workgroups per CU, or 32-row tiles at three.
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))) void k_gemm_q8_fused(
     FusedGemmArgs f) {
-  __shared__ __attribute__((aligned(16))) char As[2 * kStageBytes];
+  __shared__ __attribute__((aligned(16))) char As[2 * kTileRows * kRowBytes];
   fused_tasks(
-      f, [&](const Tile& tl) { q8_body<true>(f.gu, tl, As); }, [&](const Tile& tl) { q8_body<false>(f.dn, tl, As); });
+      f, [&](const Tile& tl) { q8_task<true, kTileRows>(f, f.gu, tl, As); },
+      [&](const Tile& tl) { q8_task<false, kTileRows>(f, f.dn, tl, As); });
+}
+
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3, 3))) void k_gemm_q8_fused_short(
+    FusedGemmArgs f) {
+  __shared__ __attribute__((aligned(16))) char As[2 * kShortRows * kRowBytes];
+  fused_tasks(
+      f, [&](const Tile& tl) { q8_task<true, kShortRows>(f, f.gu, tl, As); },
+      [&](const Tile& tl) { q8_task<false, kShortRows>(f, f.dn, tl, As); });
 }
 
 // One wave per packed block (e, s, p); lane l = n + 16 g reads its row's
@@ -327,8 +366,9 @@ hipError_t launch_pack_q8(const uint8_t* blocks, uint8_t* pcodes, uint16_t* psca
   return hipGetLastError();
 }
 
-hipError_t launch_gemm_fused_q8(const FusedGemmArgs& f, hipStream_t stream, const KernelEvents* ev) {
-  return launch_kernel(k_gemm_q8_fused, dim3(kQueues * (f.gu.qmax + f.dn.qmax)), dim3(kThreads), stream, ev, f);
+hipError_t launch_gemm_fused_q8(const FusedGemmArgs& f, int tile_rows, hipStream_t stream, const KernelEvents* ev) {
+  return launch_kernel(tile_rows == kShortRows ? k_gemm_q8_fused_short : k_gemm_q8_fused,
+                       dim3(kQueues * (f.gu.qmax + f.dn.qmax)), dim3(kThreads), stream, ev, f);
 }
 
 }  // namespace dg

@@ -40,12 +40,13 @@ inline int bf16_tile_rows(int T, int K, int E) {
   const long rows = (long)T * K;
   return rows >= (long)kWideFrom * E ? kWideRows : rows >= 64L * E ? kTallRows : kTileRows;
 }
-// Short tiles of the packed int4 GEMMs, used while the rows per expert average
-// at most kShortUpTo: nearly every expert then fits one tile, and the kernel's
-// smaller sums let three workgroups share a CU.
+// Short tiles of the quantised GEMMs (packed int4, Q8_0, MXFP4, MXFP8), used
+// while the rows per expert average at most kShortUpTo: nearly every expert
+// then fits one tile, and the kernels' smaller sums let one more workgroup
+// share a CU (three for int4 and Q8_0, four for MXFP4 and MXFP8).
 constexpr int kShortRows = 32;
 constexpr int kShortUpTo = 20;
-inline int i4_tile_rows(int T, int K, int E) {
+inline int quant_tile_rows(int T, int K, int E) {
   return (long)T * K <= (long)kShortUpTo * E ? kShortRows : kTileRows;
 }
 // GEMM tasks are spread over this many queues, one per XCD: queue x holds the
@@ -225,7 +226,7 @@ hipError_t launch_pack_q8(const uint8_t* blocks, uint8_t* pcodes, uint16_t* psca
                           hipStream_t stream);
 // Both products with packed Q8_0 weights (fp16 expert input and activation)
 // in one launch, as launch_gemm_fused.
-hipError_t launch_gemm_fused_q8(const FusedGemmArgs& f, hipStream_t stream, const KernelEvents* ev);
+hipError_t launch_gemm_fused_q8(const FusedGemmArgs& f, int tile_rows, hipStream_t stream, const KernelEvents* ev);
 // Create-time relayout of MXFP4 expert weights (rows of K / 32 blocks of 17
 // bytes: E8M0 scale byte, 16 bytes of E2M1 codes, input j in the low nibble of
 // byte j or the high nibble of byte j - 16) into fragment order: per (expert,
@@ -237,7 +238,7 @@ hipError_t launch_pack_mx4(const uint8_t* blocks, uint8_t* pcodes, uint8_t* psca
                            hipStream_t stream);
 // Both products with packed MXFP4 weights (bf16 expert input and activation)
 // in one launch, as launch_gemm_fused.
-hipError_t launch_gemm_fused_mx4(const FusedGemmArgs& f, hipStream_t stream, const KernelEvents* ev);
+hipError_t launch_gemm_fused_mx4(const FusedGemmArgs& f, int tile_rows, hipStream_t stream, const KernelEvents* ev);
 // Create-time relayout of MXFP8 expert weights (rows of K / 32 blocks of 33
 // bytes: E8M0 scale byte, 32 E4M3 codes in input order) into fragment order:
 // per (expert, 128-input step, 16-row panel), 2 KB of codes (lane l = n + 16 g:
@@ -248,7 +249,7 @@ hipError_t launch_pack_mx8(const uint8_t* blocks, uint8_t* pcodes, uint8_t* psca
                            hipStream_t stream);
 // Both products with packed MXFP8 weights (bf16 expert input and activation)
 // in one launch, as launch_gemm_fused.
-hipError_t launch_gemm_fused_mx8(const FusedGemmArgs& f, hipStream_t stream, const KernelEvents* ev);
+hipError_t launch_gemm_fused_mx8(const FusedGemmArgs& f, int tile_rows, hipStream_t stream, const KernelEvents* ev);
 
 struct CombineArgs {
   const uint16_t* y;           // [K T, D] bf16 expert outputs, expert-sorted rows
