@@ -30,7 +30,7 @@ namespace dg {
 
 namespace {
 
-using namespace gemm;  // kThreads (256), kBMT (4), the DMA and wait helpers
+using namespace gemm;  // kThreads (256), kBMT (4: the borrowed kernels' 64-row tiles), the DMA and wait helpers
 
 constexpr int kSlab = 128;              // inputs per scale group = K per step
 constexpr int kPitch = kSlab + 8;       // LDS row pitch in fp16 elements

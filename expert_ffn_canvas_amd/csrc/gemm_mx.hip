@@ -40,10 +40,10 @@
 // scale, as in the oracle.
 //
 // Mapping, activation path and work distribution as in the bf16 and Q8_0
-// kernels (64-row tiles, 4 waves, two 16-row panels per wave, activation rows
-// staged in LDS by DMA, both GEMMs in one launch from the per-XCD queues), with
-// a quarter (MXFP4) or a half (MXFP8) of the bf16 kernels' weight bytes per
-// step.
+// kernels (64-row tiles, or 32-row tiles where experts hold few rows; 4 waves,
+// two 16-row panels per wave, activation rows staged in LDS by DMA, both GEMMs
+// in one launch from the per-XCD queues), with a quarter (MXFP4) or a half
+// (MXFP8) of the bf16 kernels' weight bytes per step.
 #include "dg_common.h"
 #include "gemm_common.h"
 #include "launch.h"
