@@ -258,13 +258,15 @@ __device__ __forceinline__ void rank_experts(const int* cnt, int E, int tid, Out
   if (q == 0 && e < E) rank_out(e, r);
 }
 
-// Workgroups that share the stable scatter: the chunks of kThreads tokens are
-// split into this many contiguous ranges (at most kMaxScatter), one per
-// workgroup, each starting from the rows the earlier tokens take.
+// Workgroups that share the stable scatter: the tokens are split into this
+// many contiguous ranges of at least kScatterMin tokens (at most kMaxScatter
+// ranges), one per workgroup, each starting from the rows the earlier tokens
+// take.
 constexpr int kMaxScatter = 8;
+constexpr int kScatterMin = 256;
 __host__ __device__ inline int scatter_groups(int T) {
-  const int chunks = (T + kThreads - 1) / kThreads;
-  return chunks < kMaxScatter ? (chunks > 0 ? chunks : 1) : kMaxScatter;
+  const int n = (T + kScatterMin - 1) / kScatterMin;
+  return n < kMaxScatter ? (n > 0 ? n : 1) : kMaxScatter;
 }
 
 // The stable scatter of tokens [t0, t1), kThreads at a time: lane masks per
@@ -356,13 +358,13 @@ __global__ __launch_bounds__(kThreads) void k_permute(PermuteArgs a) {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int E = a.E, K = a.K, T = a.T;
   const int role = blockIdx.x;  // 0 .. 15: queue role % 8 of GEMM role / 8; from 16: the scatter
-  // a scatter workgroup's token range [t0, t1): whole chunks of kThreads tokens
+  // a scatter workgroup's token range [t0, t1)
   const bool scat = role >= 2 * kQueues;
   int t0 = 0, t1 = 0;
   if (scat) {
-    const int chunks = (T + kThreads - 1) / kThreads, S = scatter_groups(T), s = role - 2 * kQueues;
-    t0 = min(T, (int)((long)s * chunks / S) * kThreads);
-    t1 = min(T, (int)((long)(s + 1) * chunks / S) * kThreads);
+    const int S = scatter_groups(T), s = role - 2 * kQueues;
+    t0 = (int)((long)s * T / S);
+    t1 = (int)((long)(s + 1) * T / S);
   }
   const bool staged = (size_t)K * (t1 - t0) <= (size_t)kStage;
 

@@ -66,9 +66,11 @@ def test_small_shapes(E, K, D, F, T, act, rw, pack):
 
 @pytest.mark.parametrize("E,K,D,F,T", [
     (256, 8, 256, 128, 300),    # the most experts a layer may have
-    (16, 8, 256, 128, 3000),    # three scatter workgroups of 1024 tokens; wide tiles
-    (16, 8, 256, 128, 24000),   # eight scatter workgroups of 3 chunks: 24576 slots of a range past what
-                                # one stages in LDS (written directly), the last range staged
+    (16, 8, 256, 128, 3000),    # eight scatter workgroups of 375 tokens (ranges off the 1024-token
+                                # chunks, staged in LDS); wide tiles
+    (16, 8, 256, 128, 24000),   # eight scatter workgroups of 3000 tokens (three chunks, the last one
+                                # partial): 24000 slots of a range, past what one stages in LDS, so
+                                # written directly
     (8, 2, 1024, 4096, 40),     # the largest d_ff: 64 gate_up column blocks, down over K = 4096
     (4, 1, 16384, 64, 20),      # the largest d_model: 128 router chunks, gate_up over K = 16384
 ])
