@@ -240,7 +240,8 @@ __device__ void deal_balanced(const int (&v)[4], const int* cnt, int E, int lane
 template <typename Out>
 __device__ __forceinline__ void rank_experts(const int* cnt, int E, int tid, Out rank_out) {
   const int e = tid >> 2, q = tid & 3;
-  const int ce = (e < E) ? cnt[e] : 0;
+  if (e >= E) return;  // threads past the last expert (an expert's 4 lanes leave together)
+  const int ce = cnt[e];
   int r = 0;
 #pragma unroll
   for (int i = 0; i < kMaxE / 16; ++i) {
@@ -255,7 +256,7 @@ __device__ __forceinline__ void rank_experts(const int* cnt, int E, int tid, Out
   }
   r += __shfl_xor(r, 1);
   r += __shfl_xor(r, 2);
-  if (q == 0 && e < E) rank_out(e, r);
+  if (q == 0) rank_out(e, r);
 }
 
 // Workgroups that share the stable scatter: the tokens are split into this
