@@ -593,8 +593,11 @@ hipError_t launch_logits(const RouterArgs& a, hipStream_t stream, const KernelEv
   if (a.x_f32)  // fp32 x lives in registers: at most two m-tiles
     k = mt == 1 ? (split == 2 ? pick_logits<true, 1, 2, 2>(nu) : pick_logits<true, 1, 2>(nu))
                 : pick_logits<true, 2, 1>(nu);
-  else  // from 32 tokens: 64-column chunks, so the x stages take 64 KB (80 KB at 80 tokens)
-    k = mt == 1   ? (split == 2 ? pick_logits<false, 1, 3, 2>(nu) : pick_logits<false, 1, 3>(nu))
+  else  // 16 tokens: one 128-column chunk in flight per wave (32 KB of x stages; with three, 96 KB, the
+        // canvas256 router took 12.2 against 10.7 us and the 512-token stack 3 us more per layer: the
+        // workgroups of the larger stages started up to 2.7 us apart). From 32 tokens: 64-column chunks,
+        // so the x stages take 64 KB (80 KB at 80 tokens)
+    k = mt == 1   ? (split == 2 ? pick_logits<false, 1, 1, 2>(nu) : pick_logits<false, 1, 1>(nu))
         : mt == 2 ? pick_logits<false, 2, 2, 1, 64>(nu)
         : mt == 4 ? pick_logits<false, 4, 1, 1, 64>(nu)
                   : pick_logits<false, 5, 1, 1, 64>(nu);
