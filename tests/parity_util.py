@@ -61,6 +61,32 @@ def check_routing(gpu_idx, gpu_w, orc, K, T):
     return near
 
 
+def check_routing_many(gpu_idx, gpu_w, orc, K, T):
+    """check_routing's acceptance rules for many tokens: vectorised over the tokens without a near tie, the
+    near-tie tokens one by one through check_routing. Returns the number of near-tie tokens."""
+    gi = np.asarray(gpu_idx).astype(np.int64)
+    gw = np.asarray(gpu_w, dtype=np.float64)
+    assert gi.shape == (T, K) and gw.shape == (T, K)
+    srt = np.sort(gi, axis=1)
+    assert np.all(np.diff(srt, axis=1) != 0), "a token with duplicate experts"
+    clear = orc["gap"] >= TIE
+    differ = clear & np.any(srt != np.sort(orc["idx"].astype(np.int64), axis=1), axis=1)
+    assert not differ.any(), f"tokens {np.nonzero(differ)[0][:8]}: expert sets differ from the oracle's"
+    wo = np.zeros(orc["logits"].shape, dtype=np.float64)
+    np.put_along_axis(wo, orc["idx"].astype(np.int64), orc["w"], axis=1)
+    dw = np.abs(gw - np.take_along_axis(wo, gi, axis=1))[clear]
+    assert dw.size == 0 or float(dw.max()) <= W_TOL, f"a routing weight off by {float(dw.max()):.3g}"
+    assert np.all(np.abs(gw.sum(axis=1) - 1.0) <= SUM_TOL)
+    assert np.all(np.diff(np.asarray(gpu_w), axis=1) <= 1e-7), "slots not ordered by weight"
+    near = np.nonzero(~clear)[0]
+    if len(near):
+        sub = {k: orc[k][near] for k in ("idx", "w", "logits", "gap")}
+        check_routing(np.asarray(gpu_idx)[near], np.asarray(gpu_w)[near], sub, K, len(near))
+    print(f"routing: {T} tokens, near-tie tokens {len(near)}, max |w_gpu - w_oracle| "
+          f"{float(dw.max()) if dw.size else 0.0:.3g}")
+    return len(near)
+
+
 def check_permutation(dbg, K, E, T):
     """The GPU permutation equals the oracle's permutation of the GPU routing, integer-exact."""
     idx = dbg["topk_idx"].cpu().numpy().astype(np.int32)

@@ -8,7 +8,8 @@ import torch
 
 from expert_ffn_canvas_amd import synth
 from tests.conftest import gpu_available
-from tests.parity_util import OUT_TOL, host, layer_parity, oracle_weights, rel_max_err, to_f32
+from tests.parity_util import (OUT_TOL, check_device_state, check_permutation, check_routing_many, host,
+                               layer_parity, oracle_weights, rel_max_err, to_f32)
 
 pytestmark = pytest.mark.gpu
 
@@ -85,6 +86,35 @@ def test_shape_limits(E, K, D, F, T):
         [np.arange(0, T, 997), np.arange(T - 40, T), np.random.default_rng(T).choice(T, 200, replace=False)]))
     r = layer_parity(layer, inp["x"], oracle_weights(w), K, tokens=tok)
     print(f"err {r['err']:.3e} near-ties {r['near_ties']}")
+    layer.close()
+
+
+def test_max_tokens():
+    # the largest token count a layer accepts (max_tokens = 2^20), with K T D = 2^32 expert-output elements
+    # and K T F = 2^32 gated activations, so every offset into y and act needs 64 bits; wide tiles (524288
+    # rows per expert, 3277 tiles each). Routing and permutation over all tokens, outputs on a sample.
+    T, E, K, D, F = 1 << 20, 16, 8, 512, 512
+    _say(f"max tokens E={E} K={K} D={D} F={F} T={T}")
+    wl = synth.small_workload(T=T, E=E, K=K, D=D, F=F, bias="zipf", seed=97)
+    inp = synth.make_inputs(wl, device="cuda")
+    w = inp["layers"][0]
+    layer = _layer(w, T, torch.bfloat16, K=K, pack=True)
+    dbg = layer.forward_debug(inp["x"])
+    torch.cuda.synchronize()
+    xn, wn = host(inp["x"]), oracle_weights(w)
+    orc = oracle.route(xn, wn["router_w"], wn["router_gamma"], wn.get("router_bias"), K, synth.RMS_EPS)
+    gidx = dbg["topk_idx"].cpu().numpy()
+    check_routing_many(gidx, dbg["topk_w"].cpu().numpy(), orc, K, T)
+    check_permutation(dbg, K, E, T)
+    check_device_state(dbg, K, E, T, D, F, balanced=layer.gemms_fused)
+    tok = np.unique(np.concatenate([[0, 1, T - 1], np.arange(0, T, 8191),
+                                    np.random.default_rng(97).choice(T, 200, replace=False)]))
+    ref = oracle.moe_forward(wn, xn, K, synth.RMS_EPS, forced=gidx, tokens=tok)
+    gout = dbg["out"][torch.from_numpy(tok).to(dbg["out"].device)].float().cpu().numpy()
+    err = rel_max_err(gout, ref["out"])
+    print(f"{len(tok)} tokens: err {err:.3e}")
+    assert np.all(np.isfinite(gout))
+    assert err <= OUT_TOL, f"max|d|/max|ref| = {err:.3e} > {OUT_TOL}"
     layer.close()
 
 
