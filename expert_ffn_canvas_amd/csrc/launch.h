@@ -68,8 +68,11 @@ constexpr int kTileCost = 128;
 //  * round robin over units of non-increasing size (the unit deal, the deal
 //    by expert): within one unit of the mean;
 //  * the balanced deal by tiles: the experts with more than the smallest tile
-//    count v1 are dealt in snake order of that count, non-increasing, which
-//    keeps any two queues within the largest count of each other; the
+//    count v1 are dealt in snake order by id, or, when that leaves a queue
+//    more than the largest count above an even share, in snake order of
+//    their count, non-increasing (which keeps any two queues within the
+//    largest count of each other): either way no queue ends more than the
+//    largest count above the even share; the
 //    experts of v1 tiles then fill the least loaded levels, after which a
 //    queue that took some ends below the common level plus 2 v1, and one that
 //    took none is where the snake left it: within twice the largest count of

@@ -508,10 +508,12 @@ __global__ __launch_bounds__(64 * kWaves) void k_logits(RouterArgs a) {
 }
 
 // Create time: W' = W_r diag(1 + gamma_r) in fp32 (router weight fp32 or
-// bf16), split exactly into three bf16 planes, in fragment order: plane p,
-// expert tile et, 32-column step s hold one 1 KB block whose lane l = n + 16 g
-// has the 8 values of expert 16 et + n at columns 32 s + 8 g .. + 7. Experts
-// >= E are zero.
+// bf16), in fragment order: expert tile et and 32-column step s hold one 2 KB
+// block; lane l = n + 16 g keeps the 8 values of expert 16 et + n at columns
+// 32 s + 8 g .. + 7, the first four at floats 4 l .. 4 l + 3 of the block's
+// first 1 KB and the last four at the same place in its second 1 KB, so each
+// half is one wave-wide 1 KB read. The logits kernel splits each value exactly
+// into three bf16 planes in registers as it loads it. Experts >= E are zero.
 __global__ void k_prep_router_w(const void* __restrict__ w, int w_f32, const float* __restrict__ gamma, int E,
                                 int Epad, int D, float* __restrict__ wf) {
   const int nks = D / 32;
