@@ -126,7 +126,11 @@ __device__ __forceinline__ int snake(int h) {
 // even share plus twice the largest count (a queue that takes some ends
 // below the common level plus 2 v1): the queues' capacity. Deterministic, so
 // both task lists agree. Experts without rows get queue 0 (and no tasks).
-__device__ void deal_balanced(const int (&v)[4], const int* cnt, int E, int lane, int (&q)[4]) {
+// sh: 16 ints of LDS for this wave alone. The wave runs the deal with no other
+// wave working, straight-line code it fetches once per launch, so the code is
+// kept short: the eight queue loads are summed by LDS atomics and the eight
+// levels divided in eight lanes, not reduced or divided one by one.
+__device__ void deal_balanced(const int (&v)[4], const int* cnt, int E, int lane, int (&q)[4], int* sh) {
   int big = 0, sum = 0, mx = 0;
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
@@ -156,14 +160,20 @@ __device__ void deal_balanced(const int (&v)[4], const int* cnt, int E, int lane
     }
   }
   int load[kQueues];
+  // the tiles each queue takes from the larger experts (integer sums: the
+  // same in any order), in every lane
   auto deal_loads = [&]() {
+    if (lane < kQueues) sh[lane] = 0;
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
 #pragma unroll
-    for (int x = 0; x < kQueues; ++x) {
-      int part = 0;
-#pragma unroll
-      for (int i = 0; i < 4; ++i) part += (h[i] >= 0 && snake(h[i]) == x) ? v[i] : 0;
-      load[x] = wave_total<false>(part);
-    }
+    for (int i = 0; i < 4; ++i)
+      if (h[i] >= 0) atomicAdd(&sh[snake(h[i])], v[i]);
+    __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    const int4 l0 = *reinterpret_cast<const int4*>(sh), l1 = *reinterpret_cast<const int4*>(sh + 4);
+    load[0] = l0.x; load[1] = l0.y; load[2] = l0.z; load[3] = l0.w;
+    load[4] = l1.x; load[5] = l1.y; load[6] = l1.z; load[7] = l1.w;
   };
   deal_loads();
   int hmax = 0;
@@ -193,12 +203,18 @@ __device__ void deal_balanced(const int (&v)[4], const int* cnt, int E, int lane
   // largest level lam with C(lam) = sum_x max(0, lam - L_x) <= i0 and the
   // (i0 - C(lam))-th queue (by index) at or below it; each later one the next
   // queue at that level, or the first at the next level.
+  // queue x's level, divided in lane x
+  if (lane < kQueues) sh[kQueues + lane] = div_small(sh[lane], v1);
+  __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
+  __builtin_amdgcn_wave_barrier();
   int lv[kQueues], lmin = 0x7fffffff;
-#pragma unroll
-  for (int x = 0; x < kQueues; ++x) {
-    lv[x] = div_small(load[x], v1);
-    lmin = min(lmin, lv[x]);
+  {
+    const int4 a0 = *reinterpret_cast<const int4*>(sh + kQueues), a1 = *reinterpret_cast<const int4*>(sh + kQueues + 4);
+    lv[0] = a0.x; lv[1] = a0.y; lv[2] = a0.z; lv[3] = a0.w;
+    lv[4] = a1.x; lv[5] = a1.y; lv[6] = a1.z; lv[7] = a1.w;
   }
+#pragma unroll
+  for (int x = 0; x < kQueues; ++x) lmin = min(lmin, lv[x]);
   const int i0 = wave_scan<false>(nt) - nt;
   int lo = lmin, hi = lmin + i0;
   while (lo < hi) {
@@ -355,6 +371,7 @@ __global__ __launch_bounds__(kThreads) void k_permute(PermuteArgs a) {
   __shared__ __attribute__((aligned(16))) int before[kMaxE];  // scatter: slots of expert e in earlier tokens
   __shared__ __attribute__((aligned(16))) int mine[kMaxE];    // scatter: slots of expert e in this range
   __shared__ int soff[kMaxE + 4];                             // scatter: start of expert e's run in the stage
+  __shared__ __attribute__((aligned(16))) int dscratch[16];   // the balanced deal's queue loads and levels
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int E = a.E, K = a.K, T = a.T;
@@ -474,7 +491,7 @@ __global__ __launch_bounds__(kThreads) void k_permute(PermuteArgs a) {
   if (a.deal == kDealBalanced && !wide) {
     if (wave == 0) {
       int q[4];
-      deal_balanced(v, cnt, E, lane, q);
+      deal_balanced(v, cnt, E, lane, q, dscratch);
 #pragma unroll
       for (int i = 0; i < 4; ++i) w4[i] = (q[i] == x) ? v[i] * NB : 0;
       *reinterpret_cast<int4*>(&order[4 * lane]) = make_int4(4 * lane, 4 * lane + 1, 4 * lane + 2, 4 * lane + 3);
