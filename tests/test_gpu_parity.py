@@ -364,6 +364,25 @@ def test_q8_0_small(E, K, D, F, T):
     print(f"err {r['err']:.3e} near-ties {r['near_ties']}")
 
 
+@pytest.mark.parametrize("experts", ["i4g128", "q8_0", "mxfp4", "mxfp8"])
+def test_quantised_many_tiles(experts):
+    # T = 32768 over 16 experts (Zipf): 64-row tiles, about 256 of them per expert, so every weight block is
+    # read through the caches by many tiles; d_ff 192 gives the down GEMM a 64-input last step. Routing and
+    # permutation on every token, outputs on a sample.
+    T, E, K, D, F = 32768, 16, 8, 256, 192
+    _say(f"{experts} many tiles E={E} K={K} D={D} F={F} T={T}")
+    wl = synth.small_workload(T=T, E=E, K=K, D=D, F=F, experts=experts, bias="zipf", seed=61)
+    inp = synth.make_inputs(wl, device="cuda")
+    w = inp["layers"][0]
+    layer = _layer(w, T, torch.bfloat16, K=K, pack=True)
+    tok = np.unique(np.concatenate([[0, T - 1], np.arange(0, T, 997), np.random.default_rng(61).choice(T, 150, replace=False)]))
+    r = layer_parity(layer, inp["x"], oracle_weights(w), K, tokens=tok)
+    counts = r["dbg"]["counts"].cpu().numpy()
+    assert counts.max() >= 64 * 64, "the largest expert should span many 64-row tiles"
+    print(f"err {r['err']:.3e} near-ties {r['near_ties']} largest expert {counts.max()} rows")
+    layer.close()
+
+
 def test_mxfp4():
     wl = synth.WORKLOADS["mxfp4"]
     _say(f"{wl.name} T={wl.T} pack=True")
