@@ -379,7 +379,7 @@ dg_status dg_moe_create(const dg_moe_config* cfg, const dg_moe_weights* w, void*
 static dg_status run_forward(dg_moe_handle hd, const void* x, void* out, int32_t T, const void* addend,
                              uint32_t flags, const dg_moe_debug* dbg, void* const* events, void* stream_v) {
   if (!hd) return fail(DG_ERR_INVALID_ARG, "handle is NULL");
-  if (flags & ~(DG_FWD_ADD_INPUT | DG_FWD_ROUTER_NO_WAIT))
+  if (flags & ~(DG_FWD_ADD_INPUT | DG_FWD_ROUTER_NO_WAIT | DG_FWD_GEMM_NO_WAIT))
     return fail(DG_ERR_INVALID_ARG, "unknown forward flags 0x%x", flags);
   const dg_moe_config& c = hd->cfg;
   if (T < 0 || T > c.max_tokens) return fail(DG_ERR_SHAPE, "T = %d not in [0, max_tokens = %d]", T, c.max_tokens);
@@ -497,6 +497,7 @@ static dg_status run_forward(dg_moe_handle hd, const void* x, void* out, int32_t
     fa.tile_done = pa.tile_done;
     fa.nb_gate_up = pa.nb[0];
     fa.dev_flags = ra.dev_flags;
+    fa.wait_polls = (flags & DG_FWD_GEMM_NO_WAIT) ? 0 : dg::kGemmWaitPolls;
     fa.counts = pa.counts;
     e = mx4  ? dg::launch_gemm_fused_mx4(fa, tile_rows, stream, ev(3))
         : mx8 ? dg::launch_gemm_fused_mx8(fa, tile_rows, stream, ev(3))

@@ -110,8 +110,9 @@ __device__ __forceinline__ void lds_barrier() {
 // reached this XCD's L2, counts itself on its tile; a down task starts once
 // its tile's count holds all gate_up blocks. The workgroups of one XCD are
 // dispatched in index order, so every gate_up task that a down task waits for
-// is running or done and never waits itself. The wait is bounded (about a
-// tenth of a second): past it the task writes NaN for its outputs instead of
+// is running or done and never waits itself. The wait is bounded
+// (f.wait_polls, about a tenth of a second; none with DG_FWD_GEMM_NO_WAIT,
+// which tests this path): past it the task writes NaN for its outputs instead of
 // its product, so a broken assumption shows in the result and the launch
 // still ends; it also raises DG_DEV_WAIT_TIMEOUT. The dispatcher may start a
 // launch's round robin on any XCD (workgroup b then runs on XCD (b + c) % 8
@@ -119,7 +120,6 @@ __device__ __forceinline__ void lds_barrier() {
 // gate_up task also counts itself under the XCD it ran on, and a down task
 // whose tile's gate_up tasks did not all run on its own XCD raises
 // DG_DEV_XCD_GEMM. gate_up(tile) and down(tile) run one task's product.
-constexpr int kWaitPolls = 1 << 17;
 
 template <int WV = kWaves, typename GateUp, typename Down>
 __device__ __forceinline__ void fused_tasks(const FusedGemmArgs& f, GateUp gate_up, Down down) {
@@ -144,11 +144,11 @@ __device__ __forceinline__ void fused_tasks(const FusedGemmArgs& f, GateUp gate_
   if (tid == 0) {
     unsigned long long v = 0;
     int n = 0;
-    while (((v = atomicAdd(cnt, 0ull)) & 0xffull) < need && n < kWaitPolls) {
+    while (n < f.wait_polls && ((v = atomicAdd(cnt, 0ull)) & 0xffull) < need) {
       __builtin_amdgcn_s_sleep(8);
       ++n;
     }
-    ready = n < kWaitPolls;
+    ready = n < f.wait_polls;
     if (ready && ((v >> (8 + 7 * xcc_id())) & 127ull) != need) raise_flag(f.dev_flags, DG_DEV_XCD_GEMM);
   }
   __syncthreads();

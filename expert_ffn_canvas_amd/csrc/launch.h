@@ -205,7 +205,11 @@ struct FusedGemmArgs {
   int nb_gate_up;      // gate_up column blocks per tile
   uint32_t* dev_flags; // sticky device status word (DG_DEV_* bits of dg_moe.h)
   const int32_t* counts; // [E] rows of each expert (its tile count: whether its weights are shared by tiles)
+  int wait_polls;      // polls of a down task for its tile's gate_up tasks before it gives up
+                       // (kGemmWaitPolls; 0 with DG_FWD_GEMM_NO_WAIT)
 };
+// A down task's bounded wait: about a tenth of a second of polls.
+constexpr int kGemmWaitPolls = 1 << 17;
 hipError_t launch_gemm_fused(const FusedGemmArgs& f, int tile_rows, hipStream_t stream, const KernelEvents* ev);
 // Create-time relayout of int4-g128 expert weights (codes [E][R][K/2], scales
 // [E][R][ceil(K/128)]) into fragment order: 1 KB of codes and 16 scales per

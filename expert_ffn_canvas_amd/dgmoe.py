@@ -22,6 +22,7 @@ DG_ERR_OOM, DG_ERR_HIP, DG_ERR_UNSUPPORTED = -5, -6, -7
 DG_MOE_PACK_WEIGHTS = 0x1
 DG_FWD_ADD_INPUT = 0x1
 DG_FWD_ROUTER_NO_WAIT = 0x2
+DG_FWD_GEMM_NO_WAIT = 0x4
 ABI_VERSION = 2
 DG_DEV_QUEUE_OVERFLOW, DG_DEV_XCD_ROUTER, DG_DEV_XCD_GEMM, DG_DEV_WAIT_TIMEOUT = 0x1, 0x2, 0x4, 0x8
 

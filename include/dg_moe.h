@@ -109,6 +109,13 @@ typedef enum dg_status {
  * path taken when such a wait runs out). The results are bit-identical;
  * only the timing differs. */
 #define DG_FWD_ROUTER_NO_WAIT 0x2u
+/* For tests of the failure path: the down tasks of the fused GEMM launch do
+ * not wait for their tile's gate_up tasks at all, so every one of them takes
+ * the path of a wait that ran out: it writes NaN for its outputs and raises
+ * DG_DEV_WAIT_TIMEOUT in the handle's device status word (which stays set).
+ * Every kernel still ends normally. Ignored where the GEMMs run as two
+ * launches (int4 experts read in place). */
+#define DG_FWD_GEMM_NO_WAIT 0x4u
 
 typedef struct dg_moe_config {
   uint32_t struct_size;   /* = sizeof(dg_moe_config)                                  */

@@ -214,10 +214,11 @@ def to_f32(t):
     return t.detach().float().cpu().numpy()
 
 
-def layer_parity(layer, x, wn, K, eps=synth.RMS_EPS, tokens=None, n_threads=0):
+def layer_parity(layer, x, wn, K, eps=synth.RMS_EPS, tokens=None, n_threads=0, check_state=True):
     """Run the GPU forward (debug) and compare routing, permutation and output with the oracle.
 
-    tokens: indices of tokens whose outputs are compared (None = all). Returns a dict of measurements.
+    tokens: indices of tokens whose outputs are compared (None = all). check_state: also require a clear device
+    status word and the queues the deal gives. Returns a dict of measurements.
     """
     T = x.shape[0]
     dbg = layer.forward_debug(x)
@@ -228,7 +229,8 @@ def layer_parity(layer, x, wn, K, eps=synth.RMS_EPS, tokens=None, n_threads=0):
     gw = dbg["topk_w"].cpu().numpy()
     near = check_routing(gidx, gw, orc, K, T)
     check_permutation(dbg, K, layer.E, T)
-    check_device_state(dbg, K, layer.E, T, layer.D, layer.F, balanced=layer.gemms_fused)
+    if check_state:
+        check_device_state(dbg, K, layer.E, T, layer.D, layer.F, balanced=layer.gemms_fused)
     tok = np.arange(T) if tokens is None else np.asarray(tokens)
     ref = oracle.moe_forward(wn, xn, K, eps, forced=gidx, tokens=tok, n_threads=n_threads)
     gout = to_f32(dbg["out"])[tok]

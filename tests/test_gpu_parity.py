@@ -598,6 +598,35 @@ def test_device_status_word_stays_clear(canvas256):
     layer.close()
 
 
+@pytest.mark.parametrize("experts,act", [("bf16", "bf16"), ("i4g128", "bf16"), ("mxfp4", "bf16"), ("bf16", "f32")])
+def test_down_wait_timeout_reaches_the_host(experts, act):
+    # The fused launch's down tasks forced (from the host) to give up their bounded wait at once: every one
+    # writes NaN for its outputs and raises DG_DEV_WAIT_TIMEOUT, which the host reads back; every kernel ends
+    # normally, another handle is untouched, and a forward of the same handle without the flag is correct
+    # again (the bit stays set: the word is sticky).
+    T, E, K, D, F = 96, 16, 4, 256, 128
+    _say(f"down wait timeout {experts} act={act}")
+    wl = synth.small_workload(T=T, E=E, K=K, D=D, F=F, act=act, router_w=act, experts=experts, seed=33)
+    inp = synth.make_inputs(wl, device="cuda")
+    w, x = inp["layers"][0], inp["x"]
+    adt = _act(wl)
+    forced = _layer(w, T, adt, K=K, pack=True)
+    other = _layer(w, T, adt, K=K, pack=True)
+    sp = torch.cuda.current_stream().cuda_stream
+    out = torch.empty((T, D), dtype=adt, device="cuda")
+    assert dgmoe.dg_moe_forward(forced.handle, x.data_ptr(), out.data_ptr(), T, None, dgmoe.DG_FWD_GEMM_NO_WAIT,
+                                sp) == 0
+    torch.cuda.synchronize()
+    assert not torch.isfinite(out.float()).any(), "every output should be NaN once every down task gave up"
+    r = layer_parity(forced, x, oracle_weights(w), K, check_state=False)  # the same handle, normal forward
+    flags = int(r["dbg"]["dev_flags"].cpu()[0])
+    assert flags == dgmoe.DG_DEV_WAIT_TIMEOUT, f"device status word 0x{flags:x}"
+    r2 = layer_parity(other, x, oracle_weights(w), K)
+    assert int(r2["dbg"]["dev_flags"].cpu()[0]) == 0
+    forced.close()
+    other.close()
+
+
 def test_create_out_of_memory():
     # a workspace larger than the device (max_tokens 2^20 at d_model 16384, d_ff 4096: act and the per-slot
     # outputs alone need 8 * 2^20 * (4096 + 16384) * 2 bytes = 344 GB) is refused with DG_ERR_OOM at create
