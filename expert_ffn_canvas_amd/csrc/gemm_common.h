@@ -144,7 +144,7 @@ __device__ __forceinline__ void fused_tasks(const FusedGemmArgs& f, GateUp gate_
   if (tid == 0) {
     unsigned long long v = 0;
     int n = 0;
-    while (n < f.wait_polls && ((v = atomicAdd(cnt, 0ull)) & 0xffull) < need) {
+    while (((v = atomicAdd(cnt, 0ull)) & 0xffull) < need && n < f.wait_polls) {
       __builtin_amdgcn_s_sleep(8);
       ++n;
     }
