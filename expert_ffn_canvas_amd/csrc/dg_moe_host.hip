@@ -323,10 +323,10 @@ dg_status dg_moe_create(const dg_moe_config* cfg, const dg_moe_weights* w, void*
       c1 = dg::launch_pack_i4(static_cast<const uint8_t*>(w->w_gate_up), w->s_gate_up,
                               static_cast<uint8_t*>(const_cast<void*>(hd->w_gate_up)),
                               const_cast<uint16_t*>(hd->s_gate_up), cfg->n_experts, 2 * cfg->d_ff, cfg->d_model,
-                              stream);
+                              cfg->d_ff / 16, stream);
       c2 = dg::launch_pack_i4(static_cast<const uint8_t*>(w->w_down), w->s_down,
                               static_cast<uint8_t*>(const_cast<void*>(hd->w_down)), const_cast<uint16_t*>(hd->s_down),
-                              cfg->n_experts, cfg->d_model, cfg->d_ff, stream);
+                              cfg->n_experts, cfg->d_model, cfg->d_ff, 1, stream);
       hd->w_packed = 1;
     } else {  // bf16: MFMA fragment order, 1 KB per wave-wide read
       c1 = dg::launch_pack_panels(static_cast<const uint16_t*>(w->w_gate_up),

@@ -301,7 +301,10 @@ __global__ __launch_bounds__(kThreads) void k_down_i4(GemmArgs a) {
 // 128 gi + 32 s + 8 g .. + 7, nibble-ordered so that the exact widening below
 // yields them in natural order (nibble i holds input 2 i for i < 4 and
 // input 2 (i - 4) + 1 for i >= 4). Inputs past K (the short last group) get
-// code 8, which stands for 0. Scales: 16 fp16 per (e, p, gi), row order.
+// code 8, which stands for 0. Scales: those of the two panels one task reads
+// (gate_up: panel q and q + F/16, gate and up; down: panels 2 q and 2 q + 1)
+// side by side, 16 rows x 2 fp16 per (e, pair q, gi), so a lane loads both of
+// its row's scales of a group as one dword.
 // So a wave reads one weight fragment as 1 KB contiguous, and the activation
 // fragments are exactly the bf16 kernels' (same LDS layout and DMA).
 
@@ -325,9 +328,11 @@ __device__ __forceinline__ f16x8 dequant8n(uint32_t v) {
 }
 
 // One thread per (block, lane).
+// pair_stride: panels between the two panels of a pair (R / 32 for gate_up,
+// whose pairs are gate panel q and up panel q; 1 for down, panels 2 q, 2 q + 1).
 __global__ __launch_bounds__(256) void k_pack_i4(const uint8_t* __restrict__ codes, const uint16_t* __restrict__ scales,
                                                  uint8_t* __restrict__ pcodes, uint16_t* __restrict__ pscales, int E,
-                                                 int R, int K) {
+                                                 int R, int K, int pair_stride) {
   const int G = (K + 127) / 128, NP = R / 16;
   const size_t nblk = (size_t)E * NP * G;
   const int lane = threadIdx.x & 63;
@@ -350,31 +355,36 @@ __global__ __launch_bounds__(256) void k_pack_i4(const uint8_t* __restrict__ cod
              (c[7] << 28);
     }
     *reinterpret_cast<u32x4*>(pcodes + (b * 64 + lane) * 16) = o;
-    if (g == 0) pscales[b * 16 + n] = scales[row * G + gi];
+    if (g == 0) {
+      const int p = (int)(ep % NP);
+      const int pair = pair_stride == 1 ? p >> 1 : (p < pair_stride ? p : p - pair_stride);
+      const int slot = pair_stride == 1 ? p & 1 : (p < pair_stride ? 0 : 1);
+      pscales[((((ep / NP) * (NP / 2) + pair) * G + gi) * 16 + n) * 2 + slot] = scales[row * G + gi];
+    }
   }
 }
 
-// Weights of one group for this lane: codes of both panels and their scales.
+// Weights of one group for this lane: codes of both panels and their two
+// scales (fp16, first panel's in the low half).
 struct WGroup {
   u32x4 c0, c1;
-  uint16_t s0, s1;
+  uint32_t s;
 };
 
 // NT: past the caches (an expert in one tile reads its weights once); else
 // normal loads, so that the expert's other tiles find them in L2.
+// Three loads per group: the scale pair as one dword (two 2-byte loads, one
+// per panel, had cost the T = 256 launch 7 us: 87 against 80 us).
 template <bool NT>
-__device__ __forceinline__ void load_wg(const uint8_t* c0, const uint8_t* c1, const uint16_t* s0, const uint16_t* s1,
-                                        int gi, WGroup& w) {
+__device__ __forceinline__ void load_wg(const uint8_t* c0, const uint8_t* c1, const uint32_t* sp, int gi, WGroup& w) {
   if constexpr (NT) {
     w.c0 = ld_stream(reinterpret_cast<const u32x4*>(c0 + (size_t)gi * 1024));
     w.c1 = ld_stream(reinterpret_cast<const u32x4*>(c1 + (size_t)gi * 1024));
-    w.s0 = ld_stream(s0 + gi * 16);
-    w.s1 = ld_stream(s1 + gi * 16);
+    w.s = ld_stream(sp + gi * 16);
   } else {
     w.c0 = *reinterpret_cast<const u32x4*>(c0 + (size_t)gi * 1024);
     w.c1 = *reinterpret_cast<const u32x4*>(c1 + (size_t)gi * 1024);
-    w.s0 = s0[gi * 16];
-    w.s1 = s1[gi * 16];
+    w.s = sp[gi * 16];
   }
 }
 
@@ -403,7 +413,8 @@ __device__ __forceinline__ void mma_i4(const char* stage, int lane, const WGroup
     }
     __builtin_amdgcn_sched_barrier(0);  // widen one sub-step's codes at a time
   }
-  const float f0 = (float)__builtin_bit_cast(_Float16, w.s0), f1 = (float)__builtin_bit_cast(_Float16, w.s1);
+  const float f0 = (float)__builtin_bit_cast(_Float16, (uint16_t)(w.s & 0xffffu));
+  const float f1 = (float)__builtin_bit_cast(_Float16, (uint16_t)(w.s >> 16));
 #pragma unroll
   for (int mt = 0; mt < NMT; ++mt)
 #pragma unroll
@@ -426,7 +437,7 @@ struct I4Tile {
 
 template <int ROWS, int NMT, bool NT>
 __device__ __forceinline__ void issue_i4(char* As, const uint16_t* const (&rowp)[I4Tile<ROWS>::kNI], const uint8_t* c0,
-                                         const uint8_t* c1, const uint16_t* s0, const uint16_t* s1, int j, int K,
+                                         const uint8_t* c1, const uint32_t* sp, int j, int K,
                                          int wave, int lane, WGroup& w) {
   char* st = As + (j % kDepthI4) * I4Tile<ROWS>::kStage;
   const int k0 = j * kKS;
@@ -435,21 +446,21 @@ __device__ __forceinline__ void issue_i4(char* As, const uint16_t* const (&rowp)
   else
     dma_a<NMT, kSegs / 2>(st, rowp, k0, wave, lane);
   __builtin_amdgcn_sched_barrier(0);
-  load_wg<NT>(c0, c1, s0, s1, j, w);
+  load_wg<NT>(c0, c1, sp, j, w);
   __builtin_amdgcn_sched_barrier(0);
 }
 
 // Step i: wait until step i's transfers have landed (those of step i + 1,
-// NMT DMA transfers and 4 weight loads, may still fly; WAIT = 0 for the last
+// NMT DMA transfers and 3 weight loads, may still fly; WAIT = 0 for the last
 // step), publish, issue step i + 2, multiply step i.
 template <int ROWS, int NMT, bool NT, bool ISSUE, int WAIT>
 __device__ __forceinline__ void step_i4(char* As, const uint16_t* const (&rowp)[I4Tile<ROWS>::kNI], const uint8_t* c0,
-                                        const uint8_t* c1, const uint16_t* s0, const uint16_t* s1, int i, int K,
+                                        const uint8_t* c1, const uint32_t* sp, int i, int K,
                                         int wave, int lane, const WGroup& wb, WGroup& wn2,
                                         f32x4 (&acc0)[I4Tile<ROWS>::kMB], f32x4 (&acc1)[I4Tile<ROWS>::kMB]) {
   wait_vmcnt<WAIT>();
   lds_barrier();
-  if (ISSUE) issue_i4<ROWS, NMT, NT>(As, rowp, c0, c1, s0, s1, i + 2, K, wave, lane, wn2);
+  if (ISSUE) issue_i4<ROWS, NMT, NT>(As, rowp, c0, c1, sp, i + 2, K, wave, lane, wn2);
   mma_i4<NMT>(As + (i % kDepthI4) * I4Tile<ROWS>::kStage, lane, wb, acc0, acc1);
 }
 
@@ -457,39 +468,39 @@ __device__ __forceinline__ void step_i4(char* As, const uint16_t* const (&rowp)[
 // two to four groups written out so that every wait count is exact.
 template <int ROWS, int NMT, bool NT>
 __device__ __forceinline__ void loop_i4(char* As, const uint16_t* const (&rowp)[I4Tile<ROWS>::kNI], const uint8_t* c0,
-                                        const uint8_t* c1, const uint16_t* s0, const uint16_t* s1, int K, int tid,
+                                        const uint8_t* c1, const uint32_t* sp, int K, int tid,
                                         f32x4 (&acc0)[I4Tile<ROWS>::kMB], f32x4 (&acc1)[I4Tile<ROWS>::kMB]) {
-  constexpr int kW = NMT + 4;
+  constexpr int kW = NMT + 3;
   const int lane = tid & 63, wave = tid >> 6;
   const int n = (K + kKS - 1) / kKS;
   WGroup w0, w1, w2;
-  issue_i4<ROWS, NMT, NT>(As, rowp, c0, c1, s0, s1, 0, K, wave, lane, w0);
+  issue_i4<ROWS, NMT, NT>(As, rowp, c0, c1, sp, 0, K, wave, lane, w0);
   if (n == 1) {
-    step_i4<ROWS, NMT, NT, false, 0>(As, rowp, c0, c1, s0, s1, 0, K, wave, lane, w0, w2, acc0, acc1);
+    step_i4<ROWS, NMT, NT, false, 0>(As, rowp, c0, c1, sp, 0, K, wave, lane, w0, w2, acc0, acc1);
     return;
   }
-  issue_i4<ROWS, NMT, NT>(As, rowp, c0, c1, s0, s1, 1, K, wave, lane, w1);
+  issue_i4<ROWS, NMT, NT>(As, rowp, c0, c1, sp, 1, K, wave, lane, w1);
   int i = 0;
   for (; i + 5 <= n; i += 3) {
-    step_i4<ROWS, NMT, NT, true, kW>(As, rowp, c0, c1, s0, s1, i, K, wave, lane, w0, w2, acc0, acc1);
-    step_i4<ROWS, NMT, NT, true, kW>(As, rowp, c0, c1, s0, s1, i + 1, K, wave, lane, w1, w0, acc0, acc1);
-    step_i4<ROWS, NMT, NT, true, kW>(As, rowp, c0, c1, s0, s1, i + 2, K, wave, lane, w2, w1, acc0, acc1);
+    step_i4<ROWS, NMT, NT, true, kW>(As, rowp, c0, c1, sp, i, K, wave, lane, w0, w2, acc0, acc1);
+    step_i4<ROWS, NMT, NT, true, kW>(As, rowp, c0, c1, sp, i + 1, K, wave, lane, w1, w0, acc0, acc1);
+    step_i4<ROWS, NMT, NT, true, kW>(As, rowp, c0, c1, sp, i + 2, K, wave, lane, w2, w1, acc0, acc1);
   }
   switch (n - i) {
     case 2:
-      step_i4<ROWS, NMT, NT, false, kW>(As, rowp, c0, c1, s0, s1, i, K, wave, lane, w0, w2, acc0, acc1);
-      step_i4<ROWS, NMT, NT, false, 0>(As, rowp, c0, c1, s0, s1, i + 1, K, wave, lane, w1, w0, acc0, acc1);
+      step_i4<ROWS, NMT, NT, false, kW>(As, rowp, c0, c1, sp, i, K, wave, lane, w0, w2, acc0, acc1);
+      step_i4<ROWS, NMT, NT, false, 0>(As, rowp, c0, c1, sp, i + 1, K, wave, lane, w1, w0, acc0, acc1);
       break;
     case 3:
-      step_i4<ROWS, NMT, NT, true, kW>(As, rowp, c0, c1, s0, s1, i, K, wave, lane, w0, w2, acc0, acc1);
-      step_i4<ROWS, NMT, NT, false, kW>(As, rowp, c0, c1, s0, s1, i + 1, K, wave, lane, w1, w0, acc0, acc1);
-      step_i4<ROWS, NMT, NT, false, 0>(As, rowp, c0, c1, s0, s1, i + 2, K, wave, lane, w2, w1, acc0, acc1);
+      step_i4<ROWS, NMT, NT, true, kW>(As, rowp, c0, c1, sp, i, K, wave, lane, w0, w2, acc0, acc1);
+      step_i4<ROWS, NMT, NT, false, kW>(As, rowp, c0, c1, sp, i + 1, K, wave, lane, w1, w0, acc0, acc1);
+      step_i4<ROWS, NMT, NT, false, 0>(As, rowp, c0, c1, sp, i + 2, K, wave, lane, w2, w1, acc0, acc1);
       break;
     default:  // 4
-      step_i4<ROWS, NMT, NT, true, kW>(As, rowp, c0, c1, s0, s1, i, K, wave, lane, w0, w2, acc0, acc1);
-      step_i4<ROWS, NMT, NT, true, kW>(As, rowp, c0, c1, s0, s1, i + 1, K, wave, lane, w1, w0, acc0, acc1);
-      step_i4<ROWS, NMT, NT, false, kW>(As, rowp, c0, c1, s0, s1, i + 2, K, wave, lane, w2, w1, acc0, acc1);
-      step_i4<ROWS, NMT, NT, false, 0>(As, rowp, c0, c1, s0, s1, i + 3, K, wave, lane, w0, w2, acc0, acc1);
+      step_i4<ROWS, NMT, NT, true, kW>(As, rowp, c0, c1, sp, i, K, wave, lane, w0, w2, acc0, acc1);
+      step_i4<ROWS, NMT, NT, true, kW>(As, rowp, c0, c1, sp, i + 1, K, wave, lane, w1, w0, acc0, acc1);
+      step_i4<ROWS, NMT, NT, false, kW>(As, rowp, c0, c1, sp, i + 2, K, wave, lane, w2, w1, acc0, acc1);
+      step_i4<ROWS, NMT, NT, false, 0>(As, rowp, c0, c1, sp, i + 3, K, wave, lane, w0, w2, acc0, acc1);
       break;
   }
 }
@@ -527,12 +538,12 @@ __device__ __forceinline__ void i4p_body(const GemmArgs& a, const Tile& tl, char
     p1 = p0 + 1;
   }
   const uint8_t* C = static_cast<const uint8_t*>(GATE_UP ? a.w_gate_up : a.w_down);
-  const uint16_t* S = GATE_UP ? a.s_gate_up : a.s_down;
+  const uint32_t* S = reinterpret_cast<const uint32_t*>(GATE_UP ? a.s_gate_up : a.s_down);
   const size_t b0 = ((size_t)tl.e * NP + p0) * G, b1 = ((size_t)tl.e * NP + p1) * G;
   const uint8_t* c0 = C + b0 * 1024 + lane * 16;
   const uint8_t* c1 = C + b1 * 1024 + lane * 16;
-  const uint16_t* s0 = S + b0 * 16 + (lane & 15);
-  const uint16_t* s1 = S + b1 * 16 + (lane & 15);
+  // the scale pair of panels p0, p1 (pair nb * kWaves + wave in both GEMMs)
+  const uint32_t* sp = S + ((size_t)tl.e * (NP / 2) + nb * kWaves + wave) * G * 16 + (lane & 15);
 
   f32x4 acc0[MB], acc1[MB];
 #pragma unroll
@@ -542,15 +553,15 @@ __device__ __forceinline__ void i4p_body(const GemmArgs& a, const Tile& tl, char
   }
   if constexpr (MB == 2) {
     if (nmt == 1)
-      loop_i4<ROWS, 1, NT>(As, rowp, c0, c1, s0, s1, K, tid, acc0, acc1);
+      loop_i4<ROWS, 1, NT>(As, rowp, c0, c1, sp, K, tid, acc0, acc1);
     else
-      loop_i4<ROWS, 2, NT>(As, rowp, c0, c1, s0, s1, K, tid, acc0, acc1);
+      loop_i4<ROWS, 2, NT>(As, rowp, c0, c1, sp, K, tid, acc0, acc1);
   } else {
     switch (nmt) {
-      case 1: loop_i4<ROWS, 1, NT>(As, rowp, c0, c1, s0, s1, K, tid, acc0, acc1); break;
-      case 2: loop_i4<ROWS, 2, NT>(As, rowp, c0, c1, s0, s1, K, tid, acc0, acc1); break;
-      case 3: loop_i4<ROWS, 3, NT>(As, rowp, c0, c1, s0, s1, K, tid, acc0, acc1); break;
-      default: loop_i4<ROWS, 4, NT>(As, rowp, c0, c1, s0, s1, K, tid, acc0, acc1); break;
+      case 1: loop_i4<ROWS, 1, NT>(As, rowp, c0, c1, sp, K, tid, acc0, acc1); break;
+      case 2: loop_i4<ROWS, 2, NT>(As, rowp, c0, c1, sp, K, tid, acc0, acc1); break;
+      case 3: loop_i4<ROWS, 3, NT>(As, rowp, c0, c1, sp, K, tid, acc0, acc1); break;
+      default: loop_i4<ROWS, 4, NT>(As, rowp, c0, c1, sp, K, tid, acc0, acc1); break;
     }
   }
 
@@ -605,8 +616,8 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3, 3))
 }  // namespace
 
 hipError_t launch_pack_i4(const uint8_t* codes, const uint16_t* scales, uint8_t* pcodes, uint16_t* pscales, int E,
-                          int R, int K, hipStream_t stream) {
-  k_pack_i4<<<dim3(4096), dim3(256), 0, stream>>>(codes, scales, pcodes, pscales, E, R, K);
+                          int R, int K, int pair_stride, hipStream_t stream) {
+  k_pack_i4<<<dim3(4096), dim3(256), 0, stream>>>(codes, scales, pcodes, pscales, E, R, K, pair_stride);
   return hipGetLastError();
 }
 

@@ -212,11 +212,13 @@ struct FusedGemmArgs {
 constexpr int kGemmWaitPolls = 1 << 17;
 hipError_t launch_gemm_fused(const FusedGemmArgs& f, int tile_rows, hipStream_t stream, const KernelEvents* ev);
 // Create-time relayout of int4-g128 expert weights (codes [E][R][K/2], scales
-// [E][R][ceil(K/128)]) into fragment order: 1 KB of codes and 16 scales per
-// (expert, 16-row panel, 128-input group), the short last group padded with
-// code 8 (zero).
+// [E][R][ceil(K/128)]) into fragment order: 1 KB of codes per (expert, 16-row
+// panel, 128-input group), the short last group padded with code 8 (zero);
+// the scales of the two panels one task reads side by side, 16 rows x 2 fp16
+// per (expert, panel pair, group). pair_stride: panels between a pair's two
+// (gate_up: F / 16, gate panel q with up panel q; down: 1, panels 2q, 2q + 1).
 hipError_t launch_pack_i4(const uint8_t* codes, const uint16_t* scales, uint8_t* pcodes, uint16_t* pscales, int E,
-                          int R, int K, hipStream_t stream);
+                          int R, int K, int pair_stride, hipStream_t stream);
 // The two int4 products on the caller's row-major layout (borrow mode).
 hipError_t launch_gate_up_i4(const GemmArgs& a, hipStream_t stream, const KernelEvents* ev);
 hipError_t launch_down_i4(const GemmArgs& a, hipStream_t stream, const KernelEvents* ev);

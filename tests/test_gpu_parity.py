@@ -335,6 +335,22 @@ def test_int4_small_tail_group(E, K, T, bias, pack):
     layer_parity(layer, inp["x"], oracle_weights(w), K)
 
 
+@pytest.mark.parametrize("pack", [False, True], ids=["borrow", "pack"])
+def test_int4_long_rows(pack):
+    # d_model 8192: 64 scale groups per gate_up row, more than the packed kernel keeps in LDS, so its gate_up
+    # loads each group's scales with the codes, while its down GEMM (d_ff 192: two groups, the last 64 wide)
+    # keeps them in LDS
+    T, E, K, D, F = 40, 6, 2, 8192, 192
+    _say(f"int4 long rows E={E} K={K} D={D} F={F} T={T} pack={pack}")
+    wl = synth.small_workload(T=T, E=E, K=K, D=D, F=F, experts="i4g128", bias="zipf", seed=71)
+    inp = synth.make_inputs(wl, device="cuda")
+    w = inp["layers"][0]
+    layer = _layer(w, T, torch.bfloat16, K=K, pack=pack)
+    r = layer_parity(layer, inp["x"], oracle_weights(w), K)
+    print(f"err {r['err']:.3e}")
+    layer.close()
+
+
 def test_q8_0():
     wl = synth.WORKLOADS["q8"]
     _say(f"{wl.name} T={wl.T} pack=True")
