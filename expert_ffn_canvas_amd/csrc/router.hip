@@ -593,7 +593,7 @@ hipError_t launch_logits(const RouterArgs& a, hipStream_t stream, const KernelEv
   const int nu = a.Epad / 16;  // 2 .. 16
   void (*k)(RouterArgs);
   if (a.x_f32)  // fp32 x lives in registers: at most two m-tiles
-    k = mt == 1 ? (split == 2 ? pick_logits<true, 1, 3, 2>(nu) : pick_logits<true, 1, 2>(nu))
+    k = mt == 1 ? (split == 2 ? pick_logits<true, 1, 3, 2>(nu) : pick_logits<true, 1, 3>(nu))
                 : pick_logits<true, 2, 1>(nu);
   else  // 16 tokens: one 128-column chunk in flight per wave (32 KB of x stages; with three, 96 KB, the
         // canvas256 router took 12.2 against 10.7 us and the 512-token stack 3 us more per layer: the
